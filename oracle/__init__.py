@@ -1,0 +1,11 @@
+"""CPU oracle for the CLO decode step (test infrastructure; see clo_oracle)."""
+from .clo_oracle import (  # noqa: F401
+    as_f64,
+    attend,
+    decode_layer,
+    decode_unit,
+    group_cosine,
+    reuse_decision,
+    select_topk,
+    token_scores,
+)

@@ -1,0 +1,156 @@
+"""CPU oracle for the CLO decode step -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the package's smoke check and the benchmark's CPU-baseline
+leg may import or call this module.  The product path (the HIP library and its
+binding) never does, and this module imports nothing from the product path.
+
+What it computes, per unit u = (sequence b, KV head kvh) of one layer, with
+g = Hq / Hkv query heads per KV head (query head h -> KV head h // g), all in
+float64 on the exact values of the stored inputs:
+
+  O1  reuse test      c = <q_t, q_prev> / (|q_t| |q_prev|) over the g heads of
+                      the unit taken as one concatenated vector; c = 0 when a
+                      norm is 0; reuse = (c >= tau).
+  O2  on reuse        the selection is the previous step's index set.
+  O3  scoring         s_j = max over the g heads of q_h . K_j, j < N.
+  O4  top-k           the k largest s_j, ties by smaller j; stored ascending.
+  O5  gather          Kc = K[sel], Vc = V[sel] (source does not change values).
+  O6  attention       per head: l_i = q_h . Kc_i / sqrt(d),
+                      p = softmax(l), o_h = sum_i p_i Vc_i.
+
+Sources (CLO per-paper synthesis page, "CLO (2511.14510) -- L3 Per-Paper
+Synthesis"; CLO abstract page on fugumt):
+  * O1: synthesis section 2.1 item 2 -- adjacent decode-step queries have a
+    cosine similarity above 0.8 on most heads, which CLO turns into its cache
+    reuse condition; abstract, feature (1) -- the cache is head-wise and
+    coarse-grained.
+  * O2: abstract, feature (1) -- approximate on-GPU caching; synthesis section
+    5.2 speaks of "cache miss" heads.
+  * O3/O4: synthesis section 2.2 -- only 10% of the KV (top-k = 10%) is moved
+    or cached; section 2.3 table -- accuracy comes from top-k sparse attention.
+  * O5: abstract, features (2) and (3) -- persistent on-GPU heads and
+    zero-copy transfers only change where rows come from.
+  * O6: synthesis section 2.3 table -- attention is top-k sparse attention.
+The pages print no formulas.  Readings taken where they are silent: the
+cosine spans the concatenated query group (one decision per KV head); the
+comparison is inclusive; the group's score is the max over its heads; ties go
+to the smaller index; attention is scaled dot-product softmax attention over
+the selected rows only, with scale 1/sqrt(d).
+
+Every function here is pinned by CPU tests against closed forms, library
+routines for the special cases it reduces to, brute force and invariants.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Dict, Iterable, Optional, Tuple
+
+import numpy as np
+
+F32, BF16 = "f32", "bf16"
+
+
+def as_f64(a, dtype: str) -> np.ndarray:
+    """Exact float64 value of stored elements.
+
+    dtype "f32": IEEE binary32 values; dtype "bf16": 16-bit patterns whose value
+    is the binary32 number with those bits as its upper half.
+    """
+    if dtype == F32:
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == BF16:
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32)
+        return (bits * np.uint32(65536)).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def group_cosine(q_group: np.ndarray, q_prev_group: np.ndarray) -> float:
+    """O1: cosine of the two [g, d] query groups, each read as one g*d vector."""
+    a = np.asarray(q_group, dtype=np.float64).reshape(-1)
+    b = np.asarray(q_prev_group, dtype=np.float64).reshape(-1)
+    dot = float(np.sum(a * b))
+    na = math.sqrt(float(np.sum(a * a)))
+    nb = math.sqrt(float(np.sum(b * b)))
+    if na == 0.0 or nb == 0.0:
+        return 0.0
+    return dot / (na * nb)
+
+
+def reuse_decision(c: float, tau: float) -> bool:
+    """O1: reuse exactly when the cosine reaches the threshold (NaN never does)."""
+    return bool(c >= tau)
+
+
+def token_scores(q_group: np.ndarray, K: np.ndarray) -> np.ndarray:
+    """O3: s_j = max over the group's heads h of sum_i q[h, i] * K[j, i]."""
+    q = np.asarray(q_group, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    per_head = K @ q.T  # [N, g]
+    return per_head.max(axis=1)
+
+
+def select_topk(s: np.ndarray, k: int) -> np.ndarray:
+    """O4: indices of the k largest scores, ties to the smaller index, ascending."""
+    s = np.asarray(s, dtype=np.float64)
+    if not 1 <= k <= s.shape[0]:
+        raise ValueError("k out of range")
+    order = np.argsort(-s, kind="stable")  # score descending, index ascending
+    return np.sort(order[:k]).astype(np.int64)
+
+
+def attend(q_group: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, return_p: bool = False):
+    """O6: softmax(q_h . Kc_i / sqrt(d)) weighted sum of Vc rows, per head h."""
+    q = np.asarray(q_group, dtype=np.float64)
+    Kc = np.asarray(Kc, dtype=np.float64)
+    Vc = np.asarray(Vc, dtype=np.float64)
+    d = q.shape[1]
+    logits = (Kc @ q.T) / math.sqrt(d)  # [k, g]
+    m = logits.max(axis=0, keepdims=True)
+    e = np.exp(logits - m)
+    p = e / e.sum(axis=0, keepdims=True)  # [k, g]
+    out = p.T @ Vc  # [g, d]
+    if return_p:
+        return out, p.T
+    return out
+
+
+def decode_unit(q_group, q_prev_group, K, V, k: int, tau: float,
+                idx_prev: Optional[np.ndarray] = None) -> Dict[str, object]:
+    """O1-O6 for one unit.  q_group/q_prev_group [g, d]; K, V [N, d] (float64)."""
+    c = group_cosine(q_group, q_prev_group)
+    reuse = reuse_decision(c, tau)
+    if reuse:
+        if idx_prev is None:
+            raise ValueError("a reused unit needs the previous selection")
+        sel = np.asarray(idx_prev, dtype=np.int64)
+    else:
+        sel = select_topk(token_scores(q_group, K), k)
+    Kc = np.asarray(K, dtype=np.float64)[sel]
+    Vc = np.asarray(V, dtype=np.float64)[sel]
+    out = attend(q_group, Kc, Vc)
+    return {"cos": c, "reuse": reuse, "idx": sel, "out": out}
+
+
+def decode_layer(q, q_prev, kv_of: Callable[[int, int], Tuple[np.ndarray, np.ndarray]],
+                 hkv: int, k: int, tau: float, dtype: str,
+                 idx_prev: Optional[np.ndarray] = None,
+                 units: Optional[Iterable[Tuple[int, int]]] = None) -> Dict[Tuple[int, int], Dict[str, object]]:
+    """Run decode_unit over (b, kvh) units of one layer.
+
+    q, q_prev: stored [B, Hq, d] arrays of `dtype`; kv_of(b, kvh) returns the
+    stored [N, d] K and V of a unit; idx_prev: [B, Hkv, k] selections of the
+    previous step (needed for reused units).  Returns {(b, kvh): result}.
+    """
+    qf = as_f64(q, dtype)
+    qpf = as_f64(q_prev, dtype)
+    B, Hq, _ = qf.shape
+    g = Hq // hkv
+    if units is None:
+        units = [(b, h) for b in range(B) for h in range(hkv)]
+    res = {}
+    for b, kvh in units:
+        K, V = kv_of(b, kvh)
+        prev = None if idx_prev is None else idx_prev[b, kvh]
+        res[(b, kvh)] = decode_unit(qf[b, kvh * g:(kvh + 1) * g], qpf[b, kvh * g:(kvh + 1) * g],
+                                    as_f64(K, dtype), as_f64(V, dtype), k, tau, prev)
+    return res

@@ -1,0 +1,303 @@
+"""Pins for the CPU oracle: checks against facts fixed outside the oracle itself.
+
+Each pin takes an object `O` exposing the oracle's functions (group_cosine,
+reuse_decision, token_scores, select_topk, attend, decode_unit, decode_layer,
+as_f64), so the same pins run against the real oracle (all must pass) and
+against deliberately broken copies of it (each must fail at least one pin).
+
+Sources of truth used here, none of which is the oracle's own code:
+  * hand-derived closed forms for tiny inputs (values written as exact
+    expressions of e, sqrt and the sigmoid);
+  * library routines for special cases the method reduces to: torch's
+    scaled_dot_product_attention (float64, CPU) for k = N, torch.topk for
+    distinct scores, scipy's cosine distance;
+  * brute force over all k-subsets for tiny selections;
+  * invariants (softmax sums to 1, convex hull, scale and permutation
+    behaviour, k = 1 returns the row).
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+
+
+def sigmoid(x: float) -> float:
+    return 1.0 / (1.0 + math.exp(-x))
+
+
+def close(a, b, tol=1e-9):
+    return np.allclose(np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64), rtol=0, atol=tol)
+
+
+# ---------------------------------------------------------------- cosine / reuse
+def pin_cosine_closed_forms(O):
+    # q = (1,0) against (3,1): 3/sqrt(10); against (1,1): 1/sqrt(2); against (-1,0): -1
+    q = np.array([[1.0, 0.0]])
+    assert close(O.group_cosine(q, np.array([[3.0, 1.0]])), 3 / math.sqrt(10))
+    assert close(O.group_cosine(q, np.array([[1.0, 1.0]])), 1 / math.sqrt(2))
+    assert close(O.group_cosine(q, np.array([[-1.0, 0.0]])), -1.0)
+    assert O.reuse_decision(3 / math.sqrt(10), 0.8) is True
+    assert O.reuse_decision(1 / math.sqrt(2), 0.8) is False
+
+
+def pin_cosine_group_concatenated(O):
+    # q = ((2,0),(0,1)), q_prev = ((1,0),(1,0)): concatenated (2,0,0,1).(1,0,1,0)
+    # = 2, norms sqrt(5) and sqrt(2) -> 2/sqrt(10).  The per-head mean would be
+    # 0.5 and the per-head min 0, so at tau = 0.6 only the concatenated reading hits.
+    q = np.array([[2.0, 0.0], [0.0, 1.0]])
+    qp = np.array([[1.0, 0.0], [1.0, 0.0]])
+    c = O.group_cosine(q, qp)
+    assert close(c, 2 / math.sqrt(10))
+    assert O.reuse_decision(c, 0.6) is True
+
+
+def pin_cosine_invariants(O):
+    rng = np.random.default_rng(1)
+    for _ in range(20):
+        g, d = rng.integers(1, 6), rng.integers(1, 130)
+        a = rng.standard_normal((g, d))
+        b = rng.standard_normal((g, d))
+        c = O.group_cosine(a, b)
+        # scipy's cosine distance on the flattened vectors
+        from scipy.spatial.distance import cosine
+
+        assert close(c, 1.0 - cosine(a.reshape(-1), b.reshape(-1)), 1e-12)
+        # scale invariance and the two extreme cases
+        assert close(O.group_cosine(3.5 * a, 0.25 * b), c, 1e-12)
+        assert close(O.group_cosine(a, 7.0 * a), 1.0, 1e-12)
+        assert close(O.group_cosine(a, -a), -1.0, 1e-12)
+        assert -1.0 - 1e-12 <= c <= 1.0 + 1e-12
+    z = np.zeros((2, 4))
+    assert O.group_cosine(z, np.ones((2, 4))) == 0.0
+
+
+def pin_reuse_threshold(O):
+    # inclusive at equality, never on NaN, +inf forces a miss, -inf a hit
+    assert O.reuse_decision(0.8, 0.8) is True
+    assert O.reuse_decision(0.8 - 1e-12, 0.8) is False
+    assert O.reuse_decision(float("nan"), 0.8) is False
+    assert O.reuse_decision(1.0, float("inf")) is False
+    assert O.reuse_decision(-1.0, float("-inf")) is True
+
+
+# ---------------------------------------------------------------- scoring / top-k
+def pin_t1_selection(O):
+    # g=1, d=2: q=(sqrt2,0), K rows (1,0),(0,1),(-1,0),(2,0): scores sqrt2,0,-sqrt2,2sqrt2
+    q = np.array([[math.sqrt(2), 0.0]])
+    K = np.array([[1.0, 0.0], [0.0, 1.0], [-1.0, 0.0], [2.0, 0.0]])
+    s = O.token_scores(q, K)
+    assert close(s, [math.sqrt(2), 0.0, -math.sqrt(2), 2 * math.sqrt(2)])
+    assert list(O.select_topk(s, 2)) == [0, 3]
+
+
+def pin_t2_group_max(O):
+    # g=2: q_a=(1,0), q_b=(0,1); K=(3,0),(0,2.5),(1.5,1.5),(-1,-1).
+    # max over heads: 3, 2.5, 1.5, -1 -> {0,1}; a sum over heads would give {0,2}.
+    q = np.array([[1.0, 0.0], [0.0, 1.0]])
+    K = np.array([[3.0, 0.0], [0.0, 2.5], [1.5, 1.5], [-1.0, -1.0]])
+    s = O.token_scores(q, K)
+    assert close(s, [3.0, 2.5, 1.5, -1.0])
+    assert list(O.select_topk(s, 2)) == [0, 1]
+
+
+def pin_topk_vs_torch(O):
+    import torch
+
+    rng = np.random.default_rng(2)
+    for n in (1, 7, 64, 1000, 4099):
+        s = rng.standard_normal(n) * 10
+        for k in sorted({1, max(1, n // 10), n // 2 or 1, n}):
+            ref = torch.topk(torch.from_numpy(s), k).indices.numpy()
+            assert list(O.select_topk(s, k)) == sorted(ref.tolist())
+
+
+def pin_topk_bruteforce_with_ties(O):
+    # Enumerate every k-subset; exactly one has each member ahead of each
+    # non-member under (score descending, index ascending).
+    rng = np.random.default_rng(3)
+    for _ in range(60):
+        n = int(rng.integers(1, 8))
+        s = rng.integers(-2, 3, size=n).astype(np.float64)  # many ties
+        k = int(rng.integers(1, n + 1))
+        ahead = lambda i, j: (s[i] > s[j]) or (s[i] == s[j] and i < j)  # noqa: E731
+        good = [S for S in itertools.combinations(range(n), k)
+                if all(ahead(i, j) for i in S for j in range(n) if j not in S)]
+        assert len(good) == 1
+        assert list(O.select_topk(s, k)) == list(good[0])
+
+
+def pin_topk_invariants(O):
+    rng = np.random.default_rng(4)
+    n, k = 500, 50
+    s = rng.standard_normal(n)
+    idx = O.select_topk(s, k)
+    assert len(idx) == k and np.all(np.diff(idx) > 0)
+    mask = np.zeros(n, bool)
+    mask[idx] = True
+    assert s[mask].min() > s[~mask].max()
+    perm = rng.permutation(n)
+    idx_p = O.select_topk(s[perm], k)  # s[perm][i] = s[perm[i]]
+    assert sorted(perm[idx_p].tolist()) == idx.tolist()
+    # scaling the query by a positive factor keeps the selection
+    q = rng.standard_normal((3, 16))
+    K = rng.standard_normal((n, 16))
+    assert list(O.select_topk(O.token_scores(2.5 * q, K), k)) == list(O.select_topk(O.token_scores(q, K), k))
+
+
+# ---------------------------------------------------------------- attention
+def pin_t1_attention(O):
+    # idx {0,3}: logits (1, 2) at d=2 -> p = (1/(1+e), e/(1+e)); V rows (1,0),(0,2)
+    e = math.e
+    q = np.array([[math.sqrt(2), 0.0]])
+    Kc = np.array([[1.0, 0.0], [2.0, 0.0]])
+    Vc = np.array([[1.0, 0.0], [0.0, 2.0]])
+    out, p = O.attend(q, Kc, Vc, return_p=True)
+    assert close(p[0], [1 / (1 + e), e / (1 + e)], 1e-12)
+    assert close(out[0], [1 / (1 + e), 2 * e / (1 + e)], 1e-12)
+    # zero-padded to d=128: logits sqrt2/sqrt128 = 1/8 and 2sqrt2/sqrt128 = 1/4
+    pad = lambda a: np.pad(a, ((0, 0), (0, 126)))  # noqa: E731
+    out, p = O.attend(pad(q), pad(Kc), pad(Vc), return_p=True)
+    p1 = sigmoid(0.125)
+    assert close(p[0], [1 - p1, p1], 1e-12)
+    assert close(out[0, :2], [1 - p1, 2 * p1], 1e-12)
+    assert close(out[0, 2:], 0.0)
+
+
+def pin_t2_attention(O):
+    # Kc = (3,0),(0,2.5); Vc = (1,2),(3,4)
+    # head a logits (3/sqrt d, 0); head b logits (0, 2.5/sqrt d); o = (1,2) + 2 p_1 (1,1)
+    q = np.array([[1.0, 0.0], [0.0, 1.0]])
+    Kc = np.array([[3.0, 0.0], [0.0, 2.5]])
+    Vc = np.array([[1.0, 2.0], [3.0, 4.0]])
+    for d in (2, 128):
+        pad = lambda a: np.pad(a, ((0, 0), (0, d - 2)))  # noqa: E731
+        out = O.attend(pad(q), pad(Kc), pad(Vc))
+        pa1 = sigmoid(-3 / math.sqrt(d))
+        pb1 = sigmoid(2.5 / math.sqrt(d))
+        assert close(out[0, :2], [1 + 2 * pa1, 2 + 2 * pa1], 1e-12)
+        assert close(out[1, :2], [1 + 2 * pb1, 2 + 2 * pb1], 1e-12)
+
+
+def pin_attention_invariants(O):
+    rng = np.random.default_rng(5)
+    for _ in range(10):
+        g, k, d = int(rng.integers(1, 6)), int(rng.integers(1, 300)), int(rng.integers(2, 130))
+        q = rng.standard_normal((g, d)) * 3
+        Kc = rng.standard_normal((k, d))
+        Vc = rng.standard_normal((k, d))
+        out, p = O.attend(q, Kc, Vc, return_p=True)
+        assert p.shape == (g, k)
+        assert np.all(np.abs(p.sum(axis=1) - 1.0) < 1e-12)
+        assert np.all(p >= 0)
+        assert np.all(out <= Vc.max(axis=0) + 1e-12) and np.all(out >= Vc.min(axis=0) - 1e-12)
+        same = np.tile(Vc[:1], (k, 1))
+        assert close(O.attend(q, Kc, same), np.tile(Vc[:1], (g, 1)), 1e-12)
+        assert np.array_equal(O.attend(q, Kc[:1], Vc[:1]), np.tile(Vc[:1], (g, 1)))
+
+
+def _sdpa_dense(q, K, V):
+    """Dense GQA decode attention from torch (float64, CPU): q [B,Hq,d], K,V [B,Hkv,N,d]."""
+    import torch
+    import torch.nn.functional as F
+
+    qt = torch.from_numpy(q)[:, :, None, :]  # [B,Hq,1,d]
+    g = q.shape[1] // K.shape[1]
+    Kt = torch.from_numpy(K).repeat_interleave(g, dim=1).contiguous()
+    Vt = torch.from_numpy(V).repeat_interleave(g, dim=1).contiguous()
+    return F.scaled_dot_product_attention(qt, Kt, Vt)[:, :, 0, :].numpy()
+
+
+def pin_dense_limit_gqa(O):
+    # k = N with every unit missing is plain dense attention (GQA: head h reads KV head h // g)
+    rng = np.random.default_rng(6)
+    for (B, Hq, Hkv, N, d) in [(2, 8, 2, 37, 16), (1, 10, 2, 64, 8), (2, 4, 4, 19, 32)]:
+        q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+        qp = rng.standard_normal((B, Hq, d)).astype(np.float32)
+        K = rng.standard_normal((B, Hkv, N, d)).astype(np.float32) * 2
+        V = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+        res = O.decode_layer(q, qp, lambda b, h: (K[b, h], V[b, h]), Hkv, N, float("inf"), "f32")
+        ref = _sdpa_dense(q.astype(np.float64), K.astype(np.float64), V.astype(np.float64))
+        g = Hq // Hkv
+        for (b, h), r in res.items():
+            assert r["reuse"] is False
+            assert list(r["idx"]) == list(range(N))
+            assert close(r["out"], ref[b, h * g:(h + 1) * g], 1e-10)
+
+
+def pin_sparse_equals_dense_on_selection(O):
+    # top-k attention equals dense attention restricted to the selected tokens
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, N, d, k = 1, 4, 2, 50, 8, 7
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    K = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    res = O.decode_layer(q, q, lambda b, h: (K[b, h], V[b, h]), Hkv, k, float("inf"), "f32")
+    g = Hq // Hkv
+    for (b, h), r in res.items():
+        sel = np.asarray(r["idx"])
+        ref = _sdpa_dense(q[:, h * g:(h + 1) * g].astype(np.float64),
+                          K[:, h:h + 1][:, :, sel].astype(np.float64), V[:, h:h + 1][:, :, sel].astype(np.float64))
+        assert close(r["out"], ref[b], 1e-10)
+        # brute force: the selection is the top-k of the per-token max over the group
+        s = np.max(K[b, h].astype(np.float64) @ q[b, h * g:(h + 1) * g].astype(np.float64).T, axis=1)
+        assert sorted(np.argsort(-s)[:k].tolist()) == sel.tolist()
+
+
+def pin_two_step_reuse(O):
+    # step 0: every unit misses (tau = +inf) with q_prev as the query; step 1:
+    # a hit reuses step 0's selection, a miss selects afresh.
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, N, d, k = 2, 4, 2, 40, 8, 5
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    qp = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    K = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    kv = lambda b, h: (K[b, h], V[b, h])  # noqa: E731
+    s0 = O.decode_layer(qp, qp, kv, Hkv, k, float("inf"), "f32")
+    idx0 = np.stack([np.stack([s0[(b, h)]["idx"] for h in range(Hkv)]) for b in range(B)])
+    hit = O.decode_layer(q, qp, kv, Hkv, k, -1.5, "f32", idx_prev=idx0)
+    miss = O.decode_layer(q, qp, kv, Hkv, k, 1.5, "f32", idx_prev=idx0)
+    g = Hq // Hkv
+    for b in range(B):
+        for h in range(Hkv):
+            qg = q[b, h * g:(h + 1) * g].astype(np.float64)
+            assert hit[(b, h)]["reuse"] is True and list(hit[(b, h)]["idx"]) == list(idx0[b, h])
+            ref = _sdpa_dense(qg[None], K[b:b + 1, h:h + 1][:, :, idx0[b, h]].astype(np.float64),
+                              V[b:b + 1, h:h + 1][:, :, idx0[b, h]].astype(np.float64))
+            assert close(hit[(b, h)]["out"], ref[0], 1e-10)
+            assert miss[(b, h)]["reuse"] is False
+            s = np.max(K[b, h].astype(np.float64) @ qg.T, axis=1)
+            assert list(miss[(b, h)]["idx"]) == sorted(np.argsort(-s)[:k].tolist())
+
+
+def pin_bf16_decoding(O):
+    # IEEE facts about bfloat16 bit patterns
+    bits = np.array([0x3F80, 0xC000, 0x3FC0, 0x0000, 0x8000, 0x7F7F, 0x0001, 0x4049], dtype=np.uint16)
+    want = [1.0, -2.0, 1.5, 0.0, -0.0, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -133, 3.140625]
+    got = O.as_f64(bits, "bf16")
+    assert list(got) == want
+    assert np.signbit(got[4])
+    f = np.array([0.1, -3.25], dtype=np.float32)
+    assert list(O.as_f64(f, "f32")) == [float(np.float32(0.1)), -3.25]
+
+
+ALL_PINS = [
+    pin_cosine_closed_forms,
+    pin_cosine_group_concatenated,
+    pin_cosine_invariants,
+    pin_reuse_threshold,
+    pin_t1_selection,
+    pin_t2_group_max,
+    pin_topk_vs_torch,
+    pin_topk_bruteforce_with_ties,
+    pin_topk_invariants,
+    pin_t1_attention,
+    pin_t2_attention,
+    pin_attention_invariants,
+    pin_dense_limit_gqa,
+    pin_sparse_equals_dense_on_selection,
+    pin_two_step_reuse,
+    pin_bf16_decoding,
+]
