@@ -1,0 +1,189 @@
+/*
+ * clo.h -- C ABI of the CLO decode-step library for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step of CPU-light KV-cache offloading ("CLO: Efficient LLM
+ * Inference System with CPU-Light KVCache Offloading via Algorithm-System
+ * Co-Design", abstract; "CLO (2511.14510) -- L3 Per-Paper Synthesis",
+ * sections 2.1-2.3) for every unit u = (sequence b, KV head kvh) of one layer:
+ *
+ *   A1 reuse test    cosine of the unit's current query group against the
+ *                    previous step's (synthesis 2.1 item 2: adjacent-step
+ *                    queries are highly similar, > 0.8, on most heads; abstract
+ *                    feature (1): head-wise coarse-grained approximate caching).
+ *   A2 scoring       s_j = max over the group's query heads of q_h . K_j.
+ *   A3 top-k         the k highest-scoring tokens (synthesis 2.2: top-k = 10%).
+ *   A4 gather        the selected K/V rows of non-persistent heads are read by
+ *                    the GPU straight from pinned host memory into an HBM cache
+ *                    (abstract feature (3): zero-copy transfer engine; feature
+ *                    (2): persistent heads keep their whole KV on the GPU).
+ *   A5 attention     softmax(q_h . K_sel / sqrt(d)) . V_sel per query head
+ *                    (synthesis 2.3 table: top-k sparse attention).
+ *
+ * A unit whose cosine reaches tau reuses the previous step's selection and
+ * cached rows; A2-A4 run for the other ("miss") units only.  Query head h
+ * belongs to KV head h / g, g = n_q_heads / n_kv_heads.
+ *
+ * Conventions for every entry point:
+ *  - All buffers are caller-owned.  The library allocates nothing, frees
+ *    nothing and keeps no pointer after the call returns.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Buffers must stay alive until the stream work completes.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    non-OK status means nothing was enqueued.  clo_last_error() gives the
+ *    reason (thread-local).  No exception crosses the ABI and nothing aborts.
+ *  - Device buffers must be device memory of the current device; host K/V
+ *    buffers must be pinned host memory that the device can address (e.g.
+ *    hipHostMalloc); pageable host memory is rejected with CLO_E_ARG.  Every
+ *    tensor pointer must be 16-byte aligned.  Where the runtime reports an
+ *    allocation's extent, a tensor that would run past it is rejected.
+ *  - Inputs must be finite; results for NaN/Inf inputs are unspecified (no
+ *    out-of-bounds access happens either way).
+ *  - Calls on distinct buffers and streams may run concurrently.
+ *
+ * Tensor layouts (row-major, element type = shape->dtype unless noted), with
+ * P = number of persistent KV heads (bits set in persistent_mask), H = n_kv_heads - P,
+ * and "slot" = a head's rank among the persistent (or non-persistent) heads in
+ * head order:
+ *   q, q_prev, out   [B, Hq, d]
+ *   k_hbm, v_hbm     [B, P, N, d]   device   full K/V of persistent heads
+ *   k_host, v_host   [B, H, N, d]   pinned   full K/V of non-persistent heads
+ *   k_score          [B, H, N, d]   device   copy of k_host read by scoring
+ *   k_cache, v_cache [B, H, k, d]   device   rows k_host[idx], v_host[idx]
+ *   idx              [B, Hkv, k]    int32    selected token indices, ascending
+ *   reuse            [B, Hkv]       uint8    1 = reuse (hit), 0 = miss
+ *   cos              [B, Hkv]       float    group cosine
+ */
+#ifndef CLO_H
+#define CLO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { CLO_F32 = 0, CLO_BF16 = 1 } clo_dtype;
+
+typedef enum {
+  CLO_OK = 0,
+  CLO_E_ARG = 1,          /* invalid argument (null/misaligned pointer, bad shape, bad memory kind) */
+  CLO_E_UNSUPPORTED = 2,  /* valid but unsupported: head_dim != 128, dtype, group size > 8 */
+  CLO_E_WORKSPACE = 3,    /* workspace missing or smaller than clo_workspace_size() */
+  CLO_E_HIP = 4,          /* the HIP runtime reported an error at launch */
+  CLO_E_TIMEOUT = 5       /* written to clo_sync.error_word when a device-side wait gives up */
+} clo_status;
+
+/* Problem shape of one layer. */
+typedef struct {
+  int32_t batch;       /* B >= 0 (B == 0: nothing to do, returns CLO_OK) */
+  int32_t n_q_heads;   /* Hq, a multiple of n_kv_heads, Hq / Hkv <= 8 */
+  int32_t n_kv_heads;  /* Hkv, 1..64 */
+  int32_t head_dim;    /* d, must be 128 */
+  int64_t context;     /* N >= 1 tokens */
+  int64_t topk;        /* k, 1 <= k <= N (the pages use k = ceil(N / 10)) */
+  float tau;           /* reuse threshold: reuse when cos >= tau; +inf forces every unit to miss */
+  int32_t dtype;       /* clo_dtype of q, q_prev, K, V, caches and out */
+} clo_shape;
+
+/* Where one layer's keys, values, selections and cached rows live. */
+typedef struct {
+  uint64_t persistent_mask;  /* bit h set: KV head h keeps its full K/V in HBM (same for all sequences) */
+  const void* k_hbm;         /* [B, P, N, d] device; may be NULL when P == 0 */
+  const void* v_hbm;
+  const void* k_host;        /* [B, H, N, d] pinned host; may be NULL when H == 0 */
+  const void* v_host;
+  const void* k_score;       /* [B, H, N, d] device copy of k_host, read by scoring */
+  void* k_cache;             /* [B, H, k, d] device, written for miss units, read by attention */
+  void* v_cache;
+  int32_t* idx;              /* [B, Hkv, k] device, written for miss units, read for all units */
+} clo_layer;
+
+/*
+ * Device-side ordering between streams (the pages' GPU-centric
+ * synchronization: abstract, feature (3); synthesis section 2.1 item 3, "UVA
+ * polling" instead of coarse CPU-centric synchronization).  All pointers are
+ * device memory and may be NULL (then that half is skipped).
+ *   wait_flag/wait_value      before its first kernel, the call waits on the
+ *                             GPU until *wait_flag >= wait_value (acquire,
+ *                             agent scope), polling at most spin_limit times
+ *                             (0 = a default of about one second); on time-out
+ *                             it writes CLO_E_TIMEOUT to *error_word (when not
+ *                             NULL) and continues.
+ *   signal_flag/signal_value  after its last kernel, the call stores
+ *                             signal_value to *signal_flag (release, agent scope).
+ */
+typedef struct {
+  const uint32_t* wait_flag;
+  uint32_t wait_value;
+  uint32_t* signal_flag;
+  uint32_t signal_value;
+  uint32_t* error_word;
+  uint32_t spin_limit;
+} clo_sync;
+
+/* Bytes of device workspace the calls below need for `shape` (0 for a bad shape). */
+size_t clo_workspace_size(const clo_shape* shape);
+
+/*
+ * A1 -- reuse test (synthesis 2.1 item 2; abstract feature (1)).
+ * For each unit: c = <q_g, q_prev_g> / (|q_g| |q_prev_g|) over the unit's g
+ * query heads read as one g*d vector (c = 0 when a norm is 0), in fp32;
+ * reuse[u] = (c >= tau).  cos may be NULL.
+ */
+clo_status clo_reuse_test(const clo_shape* shape, const void* q, const void* q_prev,
+                          uint8_t* reuse, float* cos, void* stream);
+
+/*
+ * A2 + A3 -- scoring and exact top-k (synthesis 2.2 and 2.3 table).
+ * For every miss unit (reuse[u] == 0; all units when reuse is NULL): scores
+ * s_j = max_h q_h . K_j accumulated in fp32 over the unit's keys (k_hbm for
+ * persistent heads, k_score otherwise), then idx[u] = the k tokens with the
+ * largest s_j (ties to the smaller index), ascending.  idx of hit units is
+ * left untouched.  ws: device workspace of at least clo_workspace_size() bytes.
+ */
+clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const void* q,
+                           const uint8_t* reuse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * A4 -- gather (abstract features (2) and (3); synthesis 2.1 item 3).
+ * For every miss unit of a non-persistent head: k_cache[u][i] = k_host[u][idx[u][i]]
+ * and v_cache[u][i] = v_host[u][idx[u][i]], read by the GPU directly from pinned
+ * host memory (bit-exact copies).  Persistent heads need no transfer: attention
+ * reads their rows in place.  reuse NULL = all units miss.  sync may be NULL.
+ */
+clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const uint8_t* reuse,
+                         const clo_sync* sync, void* stream);
+
+/*
+ * A5 -- sparse attention over the selected rows, every unit (synthesis 2.3
+ * table).  For query head h of unit u: l_i = q_h . K_sel_i / sqrt(d),
+ * p = softmax(l), out_h = sum_i p_i V_sel_i, accumulated in fp32 and rounded
+ * to dtype.  Rows come from k_cache/v_cache (non-persistent heads) or from
+ * k_hbm/v_hbm at idx (persistent heads).  ws as for clo_topk_select.
+ */
+clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const void* q, void* out,
+                           void* ws, size_t ws_bytes, const clo_sync* sync, void* stream);
+
+/*
+ * A1..A5 -- one whole decode step of one layer on one stream: reuse test,
+ * then scoring, top-k and gather for the miss units, then attention for all
+ * units.  Same buffers and semantics as the calls above; the reuse decisions
+ * never leave the GPU.  cos may be NULL; reuse must not be NULL.
+ */
+clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const void* q,
+                           const void* q_prev, void* out, uint8_t* reuse, float* cos,
+                           void* ws, size_t ws_bytes, const clo_sync* sync, void* stream);
+
+/* Static text for a status code. */
+const char* clo_status_string(clo_status status);
+
+/* Copies the calling thread's message for its last non-OK status into buf
+ * (NUL-terminated, truncated to len) and returns that status. */
+clo_status clo_last_error(char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CLO_H */

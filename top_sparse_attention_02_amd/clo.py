@@ -1,0 +1,215 @@
+"""Python binding of libclo.so: the same entry points as include/clo.h, argument marshalling only.
+
+Every step of the decode path runs in the HIP kernels behind the C ABI; this
+module only turns torch tensors / pinned host buffers into pointers and checks
+the returned status.  Importing it without a built libclo.so raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libclo.so")
+
+CLO_F32, CLO_BF16 = 0, 1
+CLO_OK, CLO_E_ARG, CLO_E_UNSUPPORTED, CLO_E_WORKSPACE, CLO_E_HIP, CLO_E_TIMEOUT = range(6)
+
+# every function include/clo.h declares
+EXPORTS = ("clo_workspace_size", "clo_reuse_test", "clo_topk_select", "clo_gather_kv", "clo_sparse_attn",
+           "clo_decode_step", "clo_status_string", "clo_last_error")
+
+
+class CloError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        super().__init__(f"{func}: status {status} ({msg})")
+        self.status = status
+
+
+class clo_shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("context", ctypes.c_int64), ("topk", ctypes.c_int64),
+                ("tau", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class clo_layer(ctypes.Structure):
+    _fields_ = [("persistent_mask", ctypes.c_uint64), ("k_hbm", ctypes.c_void_p), ("v_hbm", ctypes.c_void_p),
+                ("k_host", ctypes.c_void_p), ("v_host", ctypes.c_void_p), ("k_score", ctypes.c_void_p),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("idx", ctypes.c_void_p)]
+
+
+class clo_sync(ctypes.Structure):
+    _fields_ = [("wait_flag", ctypes.c_void_p), ("wait_value", ctypes.c_uint32),
+                ("signal_flag", ctypes.c_void_p), ("signal_value", ctypes.c_uint32),
+                ("error_word", ctypes.c_void_p), ("spin_limit", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def load():
+    """Load libclo.so; raise ImportError when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libclo.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        P = ctypes.POINTER
+        L.clo_workspace_size.restype = sz
+        L.clo_workspace_size.argtypes = [P(clo_shape)]
+        L.clo_reuse_test.restype = st
+        L.clo_reuse_test.argtypes = [P(clo_shape), vp, vp, vp, vp, vp]
+        L.clo_topk_select.restype = st
+        L.clo_topk_select.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, sz, vp]
+        L.clo_gather_kv.restype = st
+        L.clo_gather_kv.argtypes = [P(clo_shape), P(clo_layer), vp, P(clo_sync), vp]
+        L.clo_sparse_attn.restype = st
+        L.clo_sparse_attn.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, sz, P(clo_sync), vp]
+        L.clo_decode_step.restype = st
+        L.clo_decode_step.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, vp, vp, vp, sz, P(clo_sync), vp]
+        L.clo_status_string.restype = ctypes.c_char_p
+        L.clo_status_string.argtypes = [st]
+        L.clo_last_error.restype = st
+        L.clo_last_error.argtypes = [ctypes.c_char_p, sz]
+        _lib = L
+    return _lib
+
+
+def ptr(x) -> Optional[int]:
+    """Address of a torch tensor, a pinned HostBuffer, an int, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if hasattr(x, "ptr"):
+        return x.ptr
+    raise TypeError(f"cannot take the address of {type(x)}")
+
+
+def nbytes(x, given: Optional[int] = None) -> int:
+    """Size of a workspace: `given` when stated, else the tensor's or buffer's size (0 for a raw address)."""
+    if given is not None:
+        return int(given)
+    if x is None or isinstance(x, int):
+        return 0
+    if hasattr(x, "numel") and hasattr(x, "element_size"):
+        return x.numel() * x.element_size()
+    return int(getattr(x, "nbytes"))
+
+
+def stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def clo_last_error():
+    """(status, message) of the calling thread's last non-OK call."""
+    buf = ctypes.create_string_buffer(512)
+    st = load().clo_last_error(buf, 512)
+    return st, buf.value.decode()
+
+
+def last_error() -> str:
+    return clo_last_error()[1]
+
+
+def _check(status: int, func: str):
+    if status != CLO_OK:
+        raise CloError(status, func, last_error() or load().clo_status_string(status).decode())
+
+
+@dataclass
+class Shape:
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    context: int
+    topk: int
+    tau: float
+    dtype: int
+    head_dim: int = 128
+
+    def c(self) -> clo_shape:
+        return clo_shape(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.context, self.topk,
+                         self.tau, self.dtype)
+
+
+@dataclass
+class Layer:
+    persistent_mask: int = 0
+    k_hbm: object = None
+    v_hbm: object = None
+    k_host: object = None
+    v_host: object = None
+    k_score: object = None
+    k_cache: object = None
+    v_cache: object = None
+    idx: object = None
+
+    def c(self) -> clo_layer:
+        return clo_layer(self.persistent_mask, ptr(self.k_hbm), ptr(self.v_hbm), ptr(self.k_host), ptr(self.v_host),
+                         ptr(self.k_score), ptr(self.k_cache), ptr(self.v_cache), ptr(self.idx))
+
+
+@dataclass
+class Sync:
+    wait_flag: object = None
+    wait_value: int = 0
+    signal_flag: object = None
+    signal_value: int = 0
+    error_word: object = None
+    spin_limit: int = 0
+
+    def c(self) -> clo_sync:
+        return clo_sync(ptr(self.wait_flag), self.wait_value, ptr(self.signal_flag), self.signal_value,
+                        ptr(self.error_word), self.spin_limit)
+
+
+def _sync(s: Optional[Sync]):
+    return ctypes.byref(s.c()) if s is not None else None
+
+
+def clo_workspace_size(shape: Shape) -> int:
+    return int(load().clo_workspace_size(ctypes.byref(shape.c())))
+
+
+def clo_reuse_test(shape: Shape, q, q_prev, reuse, cos=None, stream=None):
+    _check(load().clo_reuse_test(ctypes.byref(shape.c()), ptr(q), ptr(q_prev), ptr(reuse), ptr(cos),
+                                 stream_handle(stream)), "clo_reuse_test")
+
+
+def clo_topk_select(shape: Shape, layer: Layer, q, reuse, ws, stream=None, ws_bytes: Optional[int] = None):
+    _check(load().clo_topk_select(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(q), ptr(reuse), ptr(ws),
+                                  nbytes(ws, ws_bytes), stream_handle(stream)), "clo_topk_select")
+
+
+def clo_gather_kv(shape: Shape, layer: Layer, reuse, sync: Optional[Sync] = None, stream=None):
+    _check(load().clo_gather_kv(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(reuse), _sync(sync),
+                                stream_handle(stream)), "clo_gather_kv")
+
+
+def clo_sparse_attn(shape: Shape, layer: Layer, q, out, ws, sync: Optional[Sync] = None, stream=None,
+                    ws_bytes: Optional[int] = None):
+    _check(load().clo_sparse_attn(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(q), ptr(out), ptr(ws),
+                                  nbytes(ws, ws_bytes), _sync(sync), stream_handle(stream)),
+           "clo_sparse_attn")
+
+
+def clo_decode_step(shape: Shape, layer: Layer, q, q_prev, out, reuse, cos, ws, sync: Optional[Sync] = None,
+                    stream=None, ws_bytes: Optional[int] = None):
+    _check(load().clo_decode_step(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(q), ptr(q_prev), ptr(out),
+                                  ptr(reuse), ptr(cos), ptr(ws), nbytes(ws, ws_bytes), _sync(sync),
+                                  stream_handle(stream)), "clo_decode_step")
+
+
+def clo_status_string(status: int) -> str:
+    return load().clo_status_string(status).decode()

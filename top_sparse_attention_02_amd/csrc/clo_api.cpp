@@ -1,0 +1,419 @@
+// C ABI of the CLO decode-step library: host-side validation, workspace
+// layout and the launch sequence of each entry point.  Declarations and the
+// contract of every call are in include/clo.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/clo.h"
+#include "clo_internal.h"
+
+using namespace clo;
+
+namespace {
+
+thread_local clo_status g_last_status = CLO_OK;
+thread_local char g_last_msg[512] = "";
+
+clo_status fail(clo_status st, const char* fmt, ...) {
+  g_last_status = st;
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_msg, sizeof g_last_msg, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+clo_status ok() {
+  return CLO_OK;
+}
+
+int num_cus() {
+  static thread_local int dev = -1, n = 0;
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (d != dev) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    dev = d;
+  }
+  return n;
+}
+
+size_t esize(int32_t dtype) { return dtype == CLO_F32 ? 4 : 2; }
+
+clo_status check_shape(const clo_shape* s) {
+  if (!s) return fail(CLO_E_ARG, "shape is NULL");
+  if (s->dtype != CLO_F32 && s->dtype != CLO_BF16) return fail(CLO_E_UNSUPPORTED, "dtype %d is not fp32 or bf16", s->dtype);
+  if (s->head_dim != kHeadDim) return fail(CLO_E_UNSUPPORTED, "head_dim %d (only 128 is supported)", s->head_dim);
+  if (s->batch < 0) return fail(CLO_E_ARG, "batch %d < 0", s->batch);
+  if (s->n_kv_heads < 1 || s->n_kv_heads > kMaxKvHeads)
+    return fail(CLO_E_ARG, "n_kv_heads %d outside 1..%d", s->n_kv_heads, kMaxKvHeads);
+  if (s->n_q_heads < 1 || s->n_q_heads % s->n_kv_heads)
+    return fail(CLO_E_ARG, "n_q_heads %d is not a positive multiple of n_kv_heads %d", s->n_q_heads, s->n_kv_heads);
+  if (s->n_q_heads / s->n_kv_heads > kMaxGroup)
+    return fail(CLO_E_UNSUPPORTED, "group size %d > %d", s->n_q_heads / s->n_kv_heads, kMaxGroup);
+  if (s->context < 1 || s->context > (int64_t)INT32_MAX) return fail(CLO_E_ARG, "context %lld out of range", (long long)s->context);
+  if (s->topk < 1 || s->topk > s->context)
+    return fail(CLO_E_ARG, "topk %lld outside 1..context (%lld)", (long long)s->topk, (long long)s->context);
+  return ok();
+}
+
+// Device memory of this process (torch allocations, hipMalloc, managed).
+clo_status check_device(const void* p, size_t bytes, const char* name) {
+  if (!p) return fail(CLO_E_ARG, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) & 15u) return fail(CLO_E_ARG, "%s is not 16-byte aligned", name);
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(CLO_E_ARG, "%s is not memory known to HIP", name);
+  }
+  if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeManaged && at.type != hipMemoryTypeUnified)
+    return fail(CLO_E_ARG, "%s is not device memory (memory type %d)", name, (int)at.type);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) == hipSuccess) {
+    if (static_cast<const char*>(p) + bytes > static_cast<const char*>(base) + size)
+      return fail(CLO_E_ARG, "%s: %zu bytes needed but the allocation ends %zu bytes after it", name, bytes,
+                  (size_t)(static_cast<const char*>(base) + size - static_cast<const char*>(p)));
+  } else {
+    (void)hipGetLastError();
+  }
+  return ok();
+}
+
+// Pinned host memory the device can address; returns its device address.
+clo_status check_host(const void* p, size_t bytes, const char* name, const void** dev) {
+  if (!p) return fail(CLO_E_ARG, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) & 15u) return fail(CLO_E_ARG, "%s is not 16-byte aligned", name);
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(CLO_E_ARG, "%s is not pinned host memory (pageable memory cannot be read by the GPU)", name);
+  }
+  if (at.type == hipMemoryTypeDevice) {
+    *dev = p;  // device-resident copy: allowed, the gather then reads HBM
+    return check_device(p, bytes, name);
+  }
+  if (at.type != hipMemoryTypeHost && at.type != hipMemoryTypeManaged && at.type != hipMemoryTypeUnified)
+    return fail(CLO_E_ARG, "%s is not pinned host memory (memory type %d)", name, (int)at.type);
+  if (!at.devicePointer) return fail(CLO_E_ARG, "%s is not mapped for device access", name);
+  *dev = static_cast<const char*>(at.devicePointer) +
+         (static_cast<const char*>(p) - static_cast<const char*>(at.hostPointer ? at.hostPointer : p));
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(*dev)) == hipSuccess) {
+    if (static_cast<const char*>(*dev) + bytes > static_cast<const char*>(base) + size)
+      return fail(CLO_E_ARG, "%s: %zu bytes needed but the allocation is shorter", name, bytes);
+  } else {
+    (void)hipGetLastError();
+  }
+  return ok();
+}
+
+struct Plan {
+  LayerArgs a;
+  size_t e;     // element bytes
+  int64_t U;    // units per layer
+  int nch_attn;
+};
+
+clo_status make_plan(const clo_shape* s, uint64_t pmask, Plan* p) {
+  clo_status st = check_shape(s);
+  if (st) return st;
+  if (s->n_kv_heads < 64 && (pmask >> s->n_kv_heads))
+    return fail(CLO_E_ARG, "persistent_mask has bits at or above n_kv_heads (%d)", s->n_kv_heads);
+  LayerArgs& a = p->a;
+  memset(&a, 0, sizeof a);
+  a.B = s->batch;
+  a.Hq = s->n_q_heads;
+  a.Hkv = s->n_kv_heads;
+  a.G = s->n_q_heads / s->n_kv_heads;
+  a.N = s->context;
+  a.k = s->topk;
+  a.Np = round_up(s->context, 64);
+  a.tau = s->tau;
+  a.dtype = s->dtype;
+  a.pmask = pmask;
+  int np = 0, nh = 0;
+  for (int h = 0; h < a.Hkv; ++h) {
+    if ((pmask >> h) & 1ull)
+      a.slot[h] = (int8_t)np++;
+    else
+      a.slot[h] = (int8_t)nh++;
+  }
+  a.P = np;
+  a.H = nh;
+  p->e = esize(s->dtype);
+  p->U = (int64_t)a.B * a.Hkv;
+  p->nch_attn = (int)((a.k + kAttnChunk - 1) / kAttnChunk);
+  return ok();
+}
+
+// Workspace layout: counts | list_all | list_host | keys | part, each 256-byte aligned.
+struct WsLayout {
+  size_t counts, list_all, list_host, keys, part, total;
+};
+
+WsLayout ws_layout(const Plan& p) {
+  WsLayout w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return at;
+  };
+  w.counts = take(16);
+  w.list_all = take((size_t)p.U * 4);
+  w.list_host = take((size_t)p.U * 4);
+  w.keys = take((size_t)p.U * (size_t)p.a.Np * 4);
+  w.part = take((size_t)p.U * (size_t)p.nch_attn * (size_t)p.a.G * kPartStride * 4);
+  w.total = off;
+  return w;
+}
+
+clo_status bind_ws(const Plan& p, void* ws, size_t ws_bytes, Workspace* w) {
+  const WsLayout L = ws_layout(p);
+  if (!ws) return fail(CLO_E_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(CLO_E_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < L.total) return fail(CLO_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, L.total);
+  if (check_device(ws, L.total, "workspace")) {
+    char why[sizeof g_last_msg];
+    memcpy(why, g_last_msg, sizeof why);
+    return fail(CLO_E_WORKSPACE, "%s", why);
+  }
+  char* b = static_cast<char*>(ws);
+  w->counts = reinterpret_cast<int32_t*>(b + L.counts);
+  w->list_all = reinterpret_cast<int32_t*>(b + L.list_all);
+  w->list_host = reinterpret_cast<int32_t*>(b + L.list_host);
+  w->keys = reinterpret_cast<uint32_t*>(b + L.keys);
+  w->part = reinterpret_cast<float*>(b + L.part);
+  return ok();
+}
+
+// Buffer sizes in bytes.
+size_t q_bytes(const Plan& p) { return (size_t)p.a.B * p.a.Hq * kHeadDim * p.e; }
+size_t full_bytes(const Plan& p, int heads) { return (size_t)p.a.B * heads * (size_t)p.a.N * kHeadDim * p.e; }
+size_t cache_bytes(const Plan& p) { return (size_t)p.a.B * p.a.H * (size_t)p.a.k * kHeadDim * p.e; }
+size_t idx_bytes(const Plan& p) { return (size_t)p.U * (size_t)p.a.k * 4; }
+
+// Which layer buffers a call reads or writes.
+enum Need : unsigned { NEED_SCORE = 1, NEED_HOST = 2, NEED_CACHE = 4, NEED_HBM_KV = 8, NEED_HBM_K = 16 };
+
+clo_status check_layer(const clo_layer* l, Plan* p, unsigned need) {
+  if (!l) return fail(CLO_E_ARG, "layer is NULL");
+  clo_status st;
+  LayerArgs& a = p->a;
+  if ((st = check_device(l->idx, idx_bytes(*p), "layer.idx"))) return st;
+  a.idx = l->idx;
+  if (a.P > 0 && (need & (NEED_HBM_KV | NEED_HBM_K))) {
+    if ((st = check_device(l->k_hbm, full_bytes(*p, a.P), "layer.k_hbm"))) return st;
+    a.k_hbm = l->k_hbm;
+    if (need & NEED_HBM_KV) {
+      if ((st = check_device(l->v_hbm, full_bytes(*p, a.P), "layer.v_hbm"))) return st;
+      a.v_hbm = l->v_hbm;
+    }
+  }
+  if (a.H > 0) {
+    if (need & NEED_SCORE) {
+      if ((st = check_device(l->k_score, full_bytes(*p, a.H), "layer.k_score"))) return st;
+      a.k_score = l->k_score;
+    }
+    if (need & NEED_HOST) {
+      const void* dk = nullptr;
+      const void* dv = nullptr;
+      if ((st = check_host(l->k_host, full_bytes(*p, a.H), "layer.k_host", &dk))) return st;
+      if ((st = check_host(l->v_host, full_bytes(*p, a.H), "layer.v_host", &dv))) return st;
+      a.k_host = dk;
+      a.v_host = dv;
+    }
+    if (need & NEED_CACHE) {
+      if ((st = check_device(l->k_cache, cache_bytes(*p), "layer.k_cache"))) return st;
+      if ((st = check_device(l->v_cache, cache_bytes(*p), "layer.v_cache"))) return st;
+      a.k_cache = l->k_cache;
+      a.v_cache = l->v_cache;
+    }
+  }
+  return ok();
+}
+
+// Flags and the error word are single 32-bit words (often slices of one
+// tensor), so they need only 4-byte alignment.
+clo_status check_flag_ptr(const void* p, const char* name) {
+  if (!p) return ok();
+  if (reinterpret_cast<uintptr_t>(p) & 3u) return fail(CLO_E_ARG, "%s is not 4-byte aligned", name);
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(CLO_E_ARG, "%s is not memory known to HIP", name);
+  }
+  if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeManaged && at.type != hipMemoryTypeUnified)
+    return fail(CLO_E_ARG, "%s is not device memory", name);
+  return ok();
+}
+
+clo_status check_sync_flags(const clo_sync* sy) {
+  if (!sy) return ok();
+  clo_status st;
+  if ((st = check_flag_ptr(sy->wait_flag, "sync.wait_flag"))) return st;
+  if ((st = check_flag_ptr(sy->signal_flag, "sync.signal_flag"))) return st;
+  if ((st = check_flag_ptr(sy->error_word, "sync.error_word"))) return st;
+  return ok();
+}
+
+clo_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return CLO_OK;
+  return fail(CLO_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+clo_status pre_wait(const clo_sync* sy, hipStream_t s) {
+  if (!sy || !sy->wait_flag) return CLO_OK;
+  const uint32_t limit = sy->spin_limit ? sy->spin_limit : (1u << 22);
+  return hip_status(launch_wait(sy->wait_flag, sy->wait_value, limit, sy->error_word, s), "wait launch");
+}
+
+clo_status post_signal(const clo_sync* sy, hipStream_t s) {
+  if (!sy || !sy->signal_flag) return CLO_OK;
+  return hip_status(launch_signal(sy->signal_flag, sy->signal_value, s), "signal launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t clo_workspace_size(const clo_shape* shape) {
+  Plan p;
+  if (make_plan(shape, 0, &p)) return 0;
+  return ws_layout(p).total;
+}
+
+clo_status clo_reuse_test(const clo_shape* shape, const void* q, const void* q_prev, uint8_t* reuse, float* cos,
+                          void* stream) {
+  Plan p;
+  clo_status st;
+  if ((st = make_plan(shape, 0, &p))) return st;
+  if (p.U == 0) return ok();
+  if ((st = check_device(q, q_bytes(p), "q"))) return st;
+  if ((st = check_device(q_prev, q_bytes(p), "q_prev"))) return st;
+  if ((st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
+  if (cos && (st = check_device(cos, (size_t)p.U * 4, "cos"))) return st;
+  return hip_status(launch_reuse(p.a, q, q_prev, reuse, cos, static_cast<hipStream_t>(stream)), "reuse launch");
+}
+
+clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const void* q, const uint8_t* reuse,
+                           void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  clo_status st;
+  if ((st = make_plan(shape, layer ? layer->persistent_mask : 0, &p))) return st;
+  if (p.U == 0) return ok();
+  Workspace w;
+  if ((st = check_layer(layer, &p, NEED_SCORE | NEED_HBM_K))) return st;
+  if ((st = check_device(q, q_bytes(p), "q"))) return st;
+  if (reuse && (st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
+  if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int cu = num_cus();
+  if ((st = hip_status(launch_compact(p.a, reuse, w, s), "compact launch"))) return st;
+  if ((st = hip_status(launch_score(p.a, q, w, cu, s), "score launch"))) return st;
+  return hip_status(launch_topk(p.a, w, cu, s), "top-k launch");
+}
+
+clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const uint8_t* reuse, const clo_sync* sync,
+                         void* stream) {
+  Plan p;
+  clo_status st;
+  if ((st = make_plan(shape, layer ? layer->persistent_mask : 0, &p))) return st;
+  if ((st = check_sync_flags(sync))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.U == 0 || p.a.H == 0) {
+    if ((st = pre_wait(sync, s))) return st;
+    return post_signal(sync, s);
+  }
+  if ((st = check_layer(layer, &p, NEED_HOST | NEED_CACHE))) return st;
+  if (reuse && (st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
+  if ((st = pre_wait(sync, s))) return st;
+  if ((st = hip_status(launch_gather(p.a, reuse, num_cus(), s), "gather launch"))) return st;
+  return post_signal(sync, s);
+}
+
+clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const void* q, void* out, void* ws,
+                           size_t ws_bytes, const clo_sync* sync, void* stream) {
+  Plan p;
+  clo_status st;
+  if ((st = make_plan(shape, layer ? layer->persistent_mask : 0, &p))) return st;
+  if ((st = check_sync_flags(sync))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.U == 0) {
+    if ((st = pre_wait(sync, s))) return st;
+    return post_signal(sync, s);
+  }
+  Workspace w;
+  if ((st = check_layer(layer, &p, NEED_CACHE | NEED_HBM_KV))) return st;
+  if ((st = check_device(q, q_bytes(p), "q"))) return st;
+  if ((st = check_device(out, q_bytes(p), "out"))) return st;
+  if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
+  if ((st = pre_wait(sync, s))) return st;
+  if ((st = hip_status(launch_attention(p.a, q, out, w, s), "attention launch"))) return st;
+  return post_signal(sync, s);
+}
+
+clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const void* q, const void* q_prev,
+                           void* out, uint8_t* reuse, float* cos, void* ws, size_t ws_bytes, const clo_sync* sync,
+                           void* stream) {
+  Plan p;
+  clo_status st;
+  if ((st = make_plan(shape, layer ? layer->persistent_mask : 0, &p))) return st;
+  if ((st = check_sync_flags(sync))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.U == 0) {
+    if ((st = pre_wait(sync, s))) return st;
+    return post_signal(sync, s);
+  }
+  Workspace w;
+  if ((st = check_layer(layer, &p, NEED_SCORE | NEED_HOST | NEED_CACHE | NEED_HBM_KV))) return st;
+  if ((st = check_device(q, q_bytes(p), "q"))) return st;
+  if ((st = check_device(q_prev, q_bytes(p), "q_prev"))) return st;
+  if ((st = check_device(out, q_bytes(p), "out"))) return st;
+  if ((st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
+  if (cos && (st = check_device(cos, (size_t)p.U * 4, "cos"))) return st;
+  if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
+  const int cu = num_cus();
+  if ((st = pre_wait(sync, s))) return st;
+  if ((st = hip_status(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch"))) return st;
+  if ((st = hip_status(launch_compact(p.a, reuse, w, s), "compact launch"))) return st;
+  if ((st = hip_status(launch_score(p.a, q, w, cu, s), "score launch"))) return st;
+  if ((st = hip_status(launch_topk(p.a, w, cu, s), "top-k launch"))) return st;
+  if (p.a.H > 0 && (st = hip_status(launch_gather(p.a, reuse, cu, s), "gather launch"))) return st;
+  if ((st = hip_status(launch_attention(p.a, q, out, w, s), "attention launch"))) return st;
+  return post_signal(sync, s);
+}
+
+const char* clo_status_string(clo_status status) {
+  switch (status) {
+    case CLO_OK: return "ok";
+    case CLO_E_ARG: return "invalid argument";
+    case CLO_E_UNSUPPORTED: return "unsupported shape or dtype";
+    case CLO_E_WORKSPACE: return "workspace missing or too small";
+    case CLO_E_HIP: return "HIP runtime error";
+    case CLO_E_TIMEOUT: return "device-side wait timed out";
+  }
+  return "unknown status";
+}
+
+clo_status clo_last_error(char* buf, size_t len) {
+  if (buf && len) {
+    strncpy(buf, g_last_msg, len - 1);
+    buf[len - 1] = '\0';
+  }
+  return g_last_status;
+}
+
+}  // extern "C"

@@ -1,0 +1,645 @@
+// HIP kernels of the CLO decode step for gfx950 (MI355X).
+//
+// Steps (CLO abstract features (1)-(3); "CLO (2511.14510) -- L3 Per-Paper
+// Synthesis" sections 2.1-2.3):
+//   reuse_kernel       A1  group cosine of q_t vs q_prev per (sequence, KV head) unit
+//   compact_kernel         device-side list of miss units (no host read-back)
+//   score_kernel       A2  s_j = max_h q_h . K_j over the unit's keys, stored as
+//                          order-preserving uint32 keys
+//   topk_kernel        A3  exact radix select of the k largest keys + stable
+//                          compaction into ascending token indices
+//   gather_kernel      A4  selected K/V rows of non-persistent heads read by the
+//                          GPU straight from pinned host memory into the HBM cache
+//   attn_partial/combine A5 softmax attention over the selected rows, split over
+//                          chunks of rows and merged with the usual max/sum rescale
+//   wait/signal_kernel     device-side flags ordering work between streams
+//
+// Element types: float (fp32) and uint16_t holding bf16 bit patterns.  All
+// arithmetic is fp32.
+#include <math.h>
+
+#include <type_traits>
+
+#include "../../include/clo.h"
+#include "clo_internal.h"
+
+namespace clo {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---------------------------------------------------------------- element access
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  x[0] = bf_lo(u.x); x[1] = bf_hi(u.x); x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
+  x[4] = bf_lo(u.z); x[5] = bf_hi(u.z); x[6] = bf_lo(u.w); x[7] = bf_hi(u.w);
+}
+
+__device__ __forceinline__ void load2(const float* p, float& a, float& b) {
+  const float2 v = *reinterpret_cast<const float2*>(p);
+  a = v.x; b = v.y;
+}
+
+__device__ __forceinline__ void load2(const uint16_t* p, float& a, float& b) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+  a = bf_lo(w); b = bf_hi(w);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = to_bf16(v); }
+
+// Order-preserving map of an fp32 score to uint32 (larger score -> larger key);
+// -0 is folded onto +0 so that equal scores give equal keys.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Sum over the 16 lanes of a row group; the xor butterfly leaves the same
+// bits in every lane of the group.
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 8, 16);
+  x += __shfl_xor(x, 4, 16);
+  x += __shfl_xor(x, 2, 16);
+  x += __shfl_xor(x, 1, 16);
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+template <typename T>
+__device__ __forceinline__ const T* unit_keys(const LayerArgs& a, int b, int h) {
+  const bool pers = (a.pmask >> h) & 1ull;
+  const T* base = static_cast<const T*>(pers ? a.k_hbm : a.k_score);
+  const int64_t heads = pers ? a.P : a.H;
+  return base + ((int64_t)b * heads + a.slot[h]) * a.N * kHeadDim;
+}
+
+// ---------------------------------------------------------------- A1 reuse test
+template <typename T>
+__global__ __launch_bounds__(64) void reuse_kernel(const T* __restrict__ q, const T* __restrict__ qp,
+                                                   uint8_t* __restrict__ reuse, float* __restrict__ cosv,
+                                                   int Hkv, int Hq, int G, float tau) {
+  const int u = blockIdx.x;
+  const int b = u / Hkv, h = u % Hkv;
+  const int64_t off = ((int64_t)b * Hq + (int64_t)h * G) * kHeadDim;  // the group is contiguous
+  const int n8 = G * kHeadDim / 8;
+  float dot = 0.f, na = 0.f, nb = 0.f;
+  for (int i = threadIdx.x; i < n8; i += 64) {
+    float x[8], y[8];
+    load8(q + off + i * 8, x);
+    load8(qp + off + i * 8, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      dot = fmaf(x[e], y[e], dot);
+      na = fmaf(x[e], x[e], na);
+      nb = fmaf(y[e], y[e], nb);
+    }
+  }
+  dot = wave_sum(dot);
+  na = wave_sum(na);
+  nb = wave_sum(nb);
+  if (threadIdx.x == 0) {
+    const float c = (na == 0.f || nb == 0.f) ? 0.f : dot / (sqrtf(na) * sqrtf(nb));
+    if (cosv) cosv[u] = c;
+    reuse[u] = (c >= tau) ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------- miss lists
+__global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict__ reuse, int U, int Hkv,
+                                                       uint64_t pmask, int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ list_all,
+                                                       int32_t* __restrict__ list_host) {
+  __shared__ int wsum[2][16];
+  __shared__ int base[2];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) base[0] = base[1] = 0;
+  __syncthreads();
+  for (int t0 = 0; t0 < U; t0 += 1024) {
+    const int u = t0 + tid;
+    const bool miss = (u < U) && (reuse == nullptr || reuse[u] == 0);
+    const bool host = miss && !((pmask >> (u % Hkv)) & 1ull);
+    const uint64_t bm = __ballot(miss), bh = __ballot(host);
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    if (lane == 0) {
+      wsum[0][w] = __popcll(bm);
+      wsum[1][w] = __popcll(bh);
+    }
+    __syncthreads();
+    int om = base[0] + __popcll(bm & below), oh = base[1] + __popcll(bh & below);
+    for (int i = 0; i < w; ++i) {
+      om += wsum[0][i];
+      oh += wsum[1][i];
+    }
+    if (miss) list_all[om] = u;
+    if (host) list_host[oh] = u;
+    __syncthreads();
+    if (tid == 0) {
+      for (int i = 0; i < 16; ++i) {
+        base[0] += wsum[0][i];
+        base[1] += wsum[1][i];
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    counts[0] = base[0];
+    counts[1] = base[1];
+  }
+}
+
+// ---------------------------------------------------------------- A2 scoring
+// 16 lanes per key row (8 elements each), 4 rows per wave instruction.
+template <typename T, int G>
+__global__ __launch_bounds__(256) void score_kernel(LayerArgs a, const T* __restrict__ q,
+                                                    const int32_t* __restrict__ list,
+                                                    const int32_t* __restrict__ counts,
+                                                    uint32_t* __restrict__ keys) {
+  constexpr int UNR = 8;
+  constexpr int kRowsPerWave = kScoreChunk / 4;
+  const int nch = (int)((a.N + kScoreChunk - 1) / kScoreChunk);
+  const int64_t items = (int64_t)counts[0] * nch;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & 15, rg = lane >> 4;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int u = list[it / nch];
+    const int c = (int)(it % nch);
+    const int b = u / a.Hkv, h = u % a.Hkv;
+    const T* kb = unit_keys<T>(a, b, h);
+    float qv[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) load8(q + ((int64_t)b * a.Hq + (int64_t)h * G + g) * kHeadDim + sub * 8, qv[g]);
+    uint32_t* kout = keys + (int64_t)u * a.Np;
+    const int64_t r_begin = (int64_t)c * kScoreChunk + (int64_t)wave * kRowsPerWave;
+    for (int r = 0; r < kRowsPerWave; r += 4 * UNR) {
+      float kx[UNR][8];
+      int64_t row[UNR];
+#pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        row[j] = r_begin + r + j * 4 + rg;
+        const int64_t rr = row[j] < a.N ? row[j] : a.N - 1;
+        load8(kb + rr * kHeadDim + sub * 8, kx[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        float best = kNegInf;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s = fmaf(qv[g][e], kx[j][e], s);
+          best = fmaxf(best, sum16(s));
+        }
+        if (sub == 0 && row[j] < a.N) kout[row[j]] = score_key(best);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- A3 top-k
+// One 1024-thread block per miss unit: four 8-bit radix passes (MSB first)
+// find the k-th largest key T and how many keys equal to T are taken; then a
+// block-wide scan writes the winners in ascending index order (keys > T, plus
+// the first `need` keys == T by index).
+__global__ __launch_bounds__(1024) void topk_kernel(LayerArgs a, const int32_t* __restrict__ list,
+                                                    const int32_t* __restrict__ counts,
+                                                    const uint32_t* __restrict__ keys) {
+  __shared__ uint32_t hist[16][256];
+  __shared__ uint32_t tot[256];
+  __shared__ uint32_t s_prefix, s_mask, s_rem, s_base_gt, s_base_eq;
+  __shared__ uint32_t s_wgt[16], s_weq[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_units = counts[0];
+  const int64_t N = a.N;
+  for (int it = blockIdx.x; it < n_units; it += gridDim.x) {
+    const int u = list[it];
+    const uint32_t* kk = keys + (int64_t)u * a.Np;
+    int32_t* out = a.idx + (int64_t)u * a.k;
+    if (tid == 0) {
+      s_prefix = 0u;
+      s_mask = 0u;
+      s_rem = (uint32_t)a.k;
+    }
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int i = tid; i < 16 * 256; i += 1024) (&hist[0][0])[i] = 0u;
+      __syncthreads();
+      const uint32_t prefix = s_prefix, mask = s_mask;
+      for (int64_t i = (int64_t)tid * 4; i < N; i += 4096) {
+        const uint4 v = *reinterpret_cast<const uint4*>(kk + i);
+        const uint32_t kv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (i + e < N && (kv[e] & mask) == prefix) atomicAdd(&hist[wave][(kv[e] >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 256) {
+        uint32_t s = 0;
+        for (int w = 0; w < 16; ++w) s += hist[w][tid];
+        tot[tid] = s;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t rem = s_rem;
+        uint32_t acc = 0;
+        int dg = 255;
+        for (; dg > 0; --dg) {
+          if (acc + tot[dg] >= rem) break;
+          acc += tot[dg];
+        }
+        s_rem = rem - acc;
+        s_prefix = prefix | ((uint32_t)dg << shift);
+        s_mask = mask | (255u << shift);
+      }
+      __syncthreads();
+    }
+    const uint32_t T = s_prefix, need = s_rem;
+    if (tid == 0) {
+      s_base_gt = 0u;
+      s_base_eq = 0u;
+    }
+    __syncthreads();
+    for (int64_t t0 = 0; t0 < N; t0 += 4096) {
+      const int64_t i = t0 + (int64_t)tid * 4;
+      uint32_t kv[4] = {0u, 0u, 0u, 0u};
+      if (i < N) {
+        const uint4 v = *reinterpret_cast<const uint4*>(kk + i);
+        kv[0] = v.x; kv[1] = v.y; kv[2] = v.z; kv[3] = v.w;
+      }
+      bool gt[4], eq[4];
+      uint32_t cg = 0, ce = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gt[e] = (i + e < N) && kv[e] > T;
+        eq[e] = (i + e < N) && kv[e] == T;
+        cg += gt[e];
+        ce += eq[e];
+      }
+      uint32_t xg = cg, xe = ce;
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t yg = __shfl_up(xg, off, 64), ye = __shfl_up(xe, off, 64);
+        if (lane >= off) {
+          xg += yg;
+          xe += ye;
+        }
+      }
+      if (lane == 63) {
+        s_wgt[wave] = xg;
+        s_weq[wave] = xe;
+      }
+      __syncthreads();
+      uint32_t pg = s_base_gt + xg - cg, pe = s_base_eq + xe - ce;
+      for (int w = 0; w < wave; ++w) {
+        pg += s_wgt[w];
+        pe += s_weq[w];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (gt[e]) {
+          const uint32_t pos = pg + (pe < need ? pe : need);
+          if (pos < (uint32_t)a.k) out[pos] = (int32_t)(i + e);
+          ++pg;
+        } else if (eq[e]) {
+          if (pe < need && pg + pe < (uint32_t)a.k) out[pg + pe] = (int32_t)(i + e);
+          ++pe;
+        }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        for (int w = 0; w < 16; ++w) {
+          s_base_gt += s_wgt[w];
+          s_base_eq += s_weq[w];
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------- A4 gather
+// Rows of d elements are moved as 16-byte pieces: LPR lanes per row.  The
+// loads from pinned host memory are issued UNR rows deep per lane before any
+// store so that many reads are in flight on the host link.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t* __restrict__ reuse) {
+  constexpr int RB = kHeadDim * (int)sizeof(T);  // row bytes
+  constexpr int LPR = RB / 16;
+  constexpr int RPI = 256 / LPR;
+  constexpr int UNR = 8;
+  const int nch = (int)((a.k + kGatherChunk - 1) / kGatherChunk);
+  const int64_t items = (int64_t)a.B * a.Hkv * nch;
+  const int sub = threadIdx.x % LPR, rl = threadIdx.x / LPR;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int u = (int)(it / nch);
+    const int c = (int)(it % nch);
+    const int b = u / a.Hkv, h = u % a.Hkv;
+    if ((a.pmask >> h) & 1ull) continue;
+    if (reuse && reuse[u]) continue;
+    const int64_t slot = (int64_t)b * a.H + a.slot[h];
+    const char* ks = static_cast<const char*>(a.k_host) + slot * a.N * RB;
+    const char* vs = static_cast<const char*>(a.v_host) + slot * a.N * RB;
+    char* kd = static_cast<char*>(a.k_cache) + slot * a.k * RB;
+    char* vd = static_cast<char*>(a.v_cache) + slot * a.k * RB;
+    const int32_t* ix = a.idx + (int64_t)u * a.k;
+    const int64_t r0 = (int64_t)c * kGatherChunk;
+    for (int r = 0; r < kGatherChunk; r += RPI * UNR) {
+      uint4 kx[UNR], vx[UNR];
+      int64_t row[UNR];
+#pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        row[j] = r0 + r + j * RPI + rl;
+        if (row[j] < a.k) {
+          int64_t src = ix[row[j]];
+          src = src < 0 ? 0 : (src >= a.N ? a.N - 1 : src);
+          kx[j] = *reinterpret_cast<const uint4*>(ks + src * RB + sub * 16);
+          vx[j] = *reinterpret_cast<const uint4*>(vs + src * RB + sub * 16);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        if (row[j] < a.k) {
+          *reinterpret_cast<uint4*>(kd + row[j] * RB + sub * 16) = kx[j];
+          *reinterpret_cast<uint4*>(vd + row[j] * RB + sub * 16) = vx[j];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- A5 attention
+// Work item = (unit, chunk of kAttnChunk selected rows).  Phase 1: logits of
+// every (head, row) into LDS; phase 2: per-head max and exp-sum; phase 3:
+// p-weighted V sum, one column pair per lane.  The partial (o, m, l) of each
+// chunk is merged by attn_combine_kernel.
+template <typename T, int G>
+__global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T* __restrict__ q,
+                                                           float* __restrict__ part, int nch) {
+  __shared__ float lg[G][kAttnChunk];
+  __shared__ float red[4][G][kHeadDim];
+  __shared__ float sm[G], sl[G];
+  const int u = blockIdx.x / nch, c = blockIdx.x % nch;
+  const int b = u / a.Hkv, h = u % a.Hkv;
+  const bool pers = (a.pmask >> h) & 1ull;
+  const int64_t r0 = (int64_t)c * kAttnChunk;
+  const int nrows = (int)((a.k - r0) < kAttnChunk ? (a.k - r0) : kAttnChunk);
+  const int32_t* ix = a.idx + (int64_t)u * a.k + r0;
+  const T* kbase;
+  const T* vbase;
+  if (pers) {
+    const int64_t s = ((int64_t)b * a.P + a.slot[h]) * a.N * kHeadDim;
+    kbase = static_cast<const T*>(a.k_hbm) + s;
+    vbase = static_cast<const T*>(a.v_hbm) + s;
+  } else {
+    const int64_t s = (((int64_t)b * a.H + a.slot[h]) * a.k + r0) * kHeadDim;
+    kbase = static_cast<const T*>(a.k_cache) + s;
+    vbase = static_cast<const T*>(a.v_cache) + s;
+  }
+  auto row_of = [&](int i) -> int64_t {
+    if (!pers) return i;
+    int64_t r = ix[i];
+    return r < 0 ? 0 : (r >= a.N ? a.N - 1 : r);
+  };
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane & 15, rg = lane >> 4;
+  const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
+
+  // phase 1: logits
+  {
+    float qv[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) load8(q + ((int64_t)b * a.Hq + (int64_t)h * G + g) * kHeadDim + sub * 8, qv[g]);
+    for (int j = 0; j < kAttnChunk / 16; ++j) {
+      const int i = j * 16 + wave * 4 + rg;
+      if (i < nrows) {
+        float kx[8];
+        load8(kbase + row_of(i) * kHeadDim + sub * 8, kx);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s = fmaf(qv[g][e], kx[e], s);
+          s = sum16(s);
+          if (sub == 0) lg[g][i] = s * scale;
+        }
+      } else if (sub == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) lg[g][i] = kNegInf;
+      }
+    }
+  }
+  __syncthreads();
+  // phase 2: softmax statistics per head
+  for (int g = wave; g < G; g += 4) {
+    float m = kNegInf;
+    for (int i = lane; i < kAttnChunk; i += 64) m = fmaxf(m, lg[g][i]);
+    m = wave_max(m);
+    float s = 0.f;
+    for (int i = lane; i < kAttnChunk; i += 64) {
+      const float p = (i < nrows) ? expf(lg[g][i] - m) : 0.f;
+      lg[g][i] = p;
+      s += p;
+    }
+    s = wave_sum(s);
+    if (lane == 0) {
+      sm[g] = m;
+      sl[g] = s;
+    }
+  }
+  __syncthreads();
+  // phase 3: p-weighted sum of V rows; wave w takes rows [64w, 64w + 64)
+  {
+    float acc[G][2];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g][0] = acc[g][1] = 0.f;
+    const int i_end = min(nrows, wave * 64 + 64);
+    for (int i = wave * 64; i < i_end; ++i) {
+      float v0, v1;
+      load2(vbase + row_of(i) * kHeadDim + 2 * lane, v0, v1);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p = lg[g][i];
+        acc[g][0] = fmaf(p, v0, acc[g][0]);
+        acc[g][1] = fmaf(p, v1, acc[g][1]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      red[wave][g][2 * lane] = acc[g][0];
+      red[wave][g][2 * lane + 1] = acc[g][1];
+    }
+  }
+  __syncthreads();
+  float* dst = part + ((int64_t)u * nch + c) * G * kPartStride;
+  for (int t = tid; t < G * kHeadDim; t += 256) {
+    const int g = t / kHeadDim, col = t % kHeadDim;
+    dst[g * kPartStride + col] = (red[0][g][col] + red[1][g][col]) + (red[2][g][col] + red[3][g][col]);
+  }
+  if (tid < G) {
+    dst[tid * kPartStride + kHeadDim] = sm[tid];
+    dst[tid * kPartStride + kHeadDim + 1] = sl[tid];
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(128) void attn_combine_kernel(LayerArgs a, const float* __restrict__ part, int nch,
+                                                           T* __restrict__ out) {
+  const int G = a.G;
+  const int u = blockIdx.x / G, g = blockIdx.x % G;
+  const int b = u / a.Hkv, h = u % a.Hkv;
+  const int col = threadIdx.x;
+  const float* p = part + ((int64_t)u * nch * G + g) * kPartStride;
+  const int64_t cstride = (int64_t)G * kPartStride;
+  float M = kNegInf;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, p[c * cstride + kHeadDim]);
+  float L = 0.f, O = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const float w = expf(p[c * cstride + kHeadDim] - M);
+    L = fmaf(p[c * cstride + kHeadDim + 1], w, L);
+    O = fmaf(p[c * cstride + col], w, O);
+  }
+  store_out(out + ((int64_t)b * a.Hq + (int64_t)h * G + g) * kHeadDim + col, O / L);
+}
+
+// ---------------------------------------------------------------- device-side flags
+__global__ __launch_bounds__(64) void wait_kernel(const uint32_t* flag, uint32_t value, uint32_t limit,
+                                                  uint32_t* error_word) {
+  if (threadIdx.x != 0) return;
+  uint32_t n = 0;
+  while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < value) {
+    if (++n >= limit) {
+      if (error_word) __hip_atomic_store(error_word, (uint32_t)CLO_E_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+__global__ __launch_bounds__(64) void signal_kernel(uint32_t* flag, uint32_t value) {
+  if (threadIdx.x == 0) __hip_atomic_store(flag, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename F>
+hipError_t dispatch_group(int G, F&& f) {
+  switch (G) {
+    case 1: return f(std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 3: return f(std::integral_constant<int, 3>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+    case 5: return f(std::integral_constant<int, 5>{});
+    case 6: return f(std::integral_constant<int, 6>{});
+    case 7: return f(std::integral_constant<int, 7>{});
+    case 8: return f(std::integral_constant<int, 8>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+inline int grid_cap(int64_t items, int64_t cap) { return (int)(items < cap ? (items > 0 ? items : 1) : cap); }
+
+}  // namespace
+
+hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, uint8_t* reuse, float* cos,
+                        hipStream_t s) {
+  const int U = a.B * a.Hkv;
+  if (a.dtype == CLO_F32)
+    reuse_kernel<float><<<U, 64, 0, s>>>(static_cast<const float*>(q), static_cast<const float*>(q_prev), reuse,
+                                         cos, a.Hkv, a.Hq, a.G, a.tau);
+  else
+    reuse_kernel<uint16_t><<<U, 64, 0, s>>>(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(q_prev),
+                                            reuse, cos, a.Hkv, a.Hq, a.G, a.tau);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, hipStream_t s) {
+  compact_kernel<<<1, 1024, 0, s>>>(reuse, a.B * a.Hkv, a.Hkv, a.pmask, w.counts, w.list_all, w.list_host);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const LayerArgs& a, const void* q, const Workspace& w, int num_cu, hipStream_t s) {
+  const int64_t nch = (a.N + kScoreChunk - 1) / kScoreChunk;
+  const int grid = grid_cap((int64_t)a.B * a.Hkv * nch, (int64_t)num_cu * 8);
+  return dispatch_group(a.G, [&](auto gc) {
+    constexpr int G = decltype(gc)::value;
+    if (a.dtype == CLO_F32)
+      score_kernel<float, G><<<grid, 256, 0, s>>>(a, static_cast<const float*>(q), w.list_all, w.counts, w.keys);
+    else
+      score_kernel<uint16_t, G><<<grid, 256, 0, s>>>(a, static_cast<const uint16_t*>(q), w.list_all, w.counts,
+                                                     w.keys);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_topk(const LayerArgs& a, const Workspace& w, int num_cu, hipStream_t s) {
+  const int grid = grid_cap((int64_t)a.B * a.Hkv, (int64_t)num_cu * 2);
+  topk_kernel<<<grid, 1024, 0, s>>>(a, w.list_all, w.counts, w.keys);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, int num_cu, hipStream_t s) {
+  const int64_t nch = (a.k + kGatherChunk - 1) / kGatherChunk;
+  const int grid = grid_cap((int64_t)a.B * a.Hkv * nch, (int64_t)num_cu * 8);
+  if (a.dtype == CLO_F32)
+    gather_kernel<float><<<grid, 256, 0, s>>>(a, reuse);
+  else
+    gather_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const LayerArgs& a, const void* q, void* out, const Workspace& w, hipStream_t s) {
+  const int nch = (int)((a.k + kAttnChunk - 1) / kAttnChunk);
+  const int64_t U = (int64_t)a.B * a.Hkv;
+  hipError_t e = dispatch_group(a.G, [&](auto gc) {
+    constexpr int G = decltype(gc)::value;
+    if (a.dtype == CLO_F32)
+      attn_partial_kernel<float, G><<<(unsigned)(U * nch), 256, 0, s>>>(a, static_cast<const float*>(q), w.part, nch);
+    else
+      attn_partial_kernel<uint16_t, G><<<(unsigned)(U * nch), 256, 0, s>>>(a, static_cast<const uint16_t*>(q), w.part,
+                                                                           nch);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
+  if (a.dtype == CLO_F32)
+    attn_combine_kernel<float><<<(unsigned)(U * a.G), 128, 0, s>>>(a, w.part, nch, static_cast<float*>(out));
+  else
+    attn_combine_kernel<uint16_t><<<(unsigned)(U * a.G), 128, 0, s>>>(a, w.part, nch, static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_wait(const uint32_t* flag, uint32_t value, uint32_t spin_limit, uint32_t* error_word,
+                       hipStream_t s) {
+  wait_kernel<<<1, 64, 0, s>>>(flag, value, spin_limit, error_word);
+  return hipGetLastError();
+}
+
+hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s) {
+  signal_kernel<<<1, 64, 0, s>>>(flag, value);
+  return hipGetLastError();
+}
+
+}  // namespace clo

@@ -1,0 +1,154 @@
+"""Device/pinned buffers of one layer in the library's layout, and loading synthetic workloads into them.
+
+`LayerBuffers` allocates every tensor a decode step reads or writes (device
+memory from torch, K/V of non-persistent heads in pinned host memory) in the
+row-major layouts include/clo.h documents.  `load_layer` fills them from a
+seeded `gen.Problem`; `decode_step` drives the two-step protocol: step 0 (cold,
+every unit misses, q_prev as the query) and step 1 (the steady decode step).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import clo
+from .hip_host import HostBuffer, copy_h2d, hipHostMallocMapped
+
+HEAD_DIM = 128
+
+
+def torch_dtype(dtype: str):
+    return torch.float32 if dtype == "f32" else torch.bfloat16
+
+
+def clo_dtype(dtype: str) -> int:
+    return clo.CLO_F32 if dtype == "f32" else clo.CLO_BF16
+
+
+def elem_bytes(dtype: str) -> int:
+    return 4 if dtype == "f32" else 2
+
+
+class LayerBuffers:
+    """All buffers of one layer for batch B, Hq/Hkv heads, context N and top-k k."""
+
+    def __init__(self, batch: int, hq: int, hkv: int, context: int, topk: int, dtype: str, persistent_mask: int,
+                 tau: float, device: str = "cuda", host_flags: int = hipHostMallocMapped,
+                 host_kv: Optional[tuple] = None, score_kv: Optional[torch.Tensor] = None):
+        self.B, self.Hq, self.Hkv, self.N, self.k = batch, hq, hkv, context, topk
+        self.dtype, self.tau, self.mask = dtype, tau, persistent_mask
+        self.P = bin(persistent_mask).count("1")
+        self.H = hkv - self.P
+        tdt = torch_dtype(dtype)
+        d = HEAD_DIM
+        dev = torch.device(device)
+        self.q = torch.zeros(batch, hq, d, dtype=tdt, device=dev)
+        self.q_prev = torch.zeros_like(self.q)
+        self.out = torch.zeros_like(self.q)
+        self.reuse = torch.zeros(batch, hkv, dtype=torch.uint8, device=dev)
+        self.cos = torch.zeros(batch, hkv, dtype=torch.float32, device=dev)
+        self.idx = torch.zeros(batch, hkv, topk, dtype=torch.int32, device=dev)
+        self.k_hbm = self.v_hbm = None
+        if self.P:
+            self.k_hbm = torch.empty(batch, self.P, context, d, dtype=tdt, device=dev)
+            self.v_hbm = torch.empty_like(self.k_hbm)
+        self.k_host = self.v_host = self.k_score = self.k_cache = self.v_cache = None
+        if self.H:
+            nb = batch * self.H * context * d * elem_bytes(dtype)
+            if host_kv is not None:
+                self.k_host, self.v_host = host_kv
+            else:
+                self.k_host = HostBuffer(nb, host_flags)
+                self.v_host = HostBuffer(nb, host_flags)
+            self.k_score = score_kv if score_kv is not None else torch.empty(batch, self.H, context, d, dtype=tdt,
+                                                                             device=dev)
+            self.k_cache = torch.zeros(batch, self.H, topk, d, dtype=tdt, device=dev)
+            self.v_cache = torch.zeros_like(self.k_cache)
+        self.shape = clo.Shape(batch, hq, hkv, context, topk, tau, clo_dtype(dtype))
+        ws = clo.clo_workspace_size(self.shape)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+
+    # ----------------------------------------------------------------- views
+    def layer(self) -> clo.Layer:
+        return clo.Layer(self.mask, self.k_hbm, self.v_hbm, self.k_host, self.v_host, self.k_score, self.k_cache,
+                         self.v_cache, self.idx)
+
+    def shape_with(self, tau: float) -> clo.Shape:
+        s = clo.Shape(**self.shape.__dict__)
+        s.tau = tau
+        return s
+
+    def slot(self, kvh: int) -> int:
+        """Rank of KV head kvh among the persistent or the non-persistent heads."""
+        pers = (self.mask >> kvh) & 1
+        return sum(1 for h in range(kvh) if ((self.mask >> h) & 1) == pers)
+
+    def is_persistent(self, kvh: int) -> bool:
+        return bool((self.mask >> kvh) & 1)
+
+    def host_view(self, which: str, b: int, kvh: int) -> np.ndarray:
+        """numpy view [N, d] of a non-persistent unit's pinned K or V."""
+        buf = self.k_host if which == "k" else self.v_host
+        npdt = np.float32 if self.dtype == "f32" else np.uint16
+        unit = self.N * HEAD_DIM * elem_bytes(self.dtype)
+        off = (b * self.H + self.slot(kvh)) * unit
+        return buf.numpy(npdt, (self.N, HEAD_DIM), offset=off)
+
+    # ----------------------------------------------------------------- steps
+    def decode_step(self, q, q_prev, tau: float, stream=None, sync=None):
+        clo.clo_decode_step(self.shape_with(tau), self.layer(), q, q_prev, self.out, self.reuse, self.cos, self.ws,
+                            sync=sync, stream=stream)
+
+    def step0(self, stream=None):
+        """Cold step: every unit misses and selects with q_prev as its query."""
+        self.decode_step(self.q_prev, self.q_prev, math.inf, stream)
+
+    def step1(self, stream=None):
+        """Steady decode step: q_t against q_prev with the real threshold."""
+        self.decode_step(self.q, self.q_prev, self.tau, stream)
+
+
+def stored_tensor(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    return t.to(device)
+
+
+def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads: Optional[int] = None,
+               log=None) -> LayerBuffers:
+    """Allocate (unless given) and fill the buffers of one layer of `problem`."""
+    p = problem
+    mask = p.persistent_mask_bits(layer)
+    if bufs is None:
+        bufs = LayerBuffers(p.batch, p.hq, p.hkv, p.context, p.topk, p.dtype, mask, p.tau)
+    assert bufs.mask == mask
+    bufs.q.copy_(stored_tensor(p.q(layer), p.dtype))
+    bufs.q_prev.copy_(stored_tensor(p.q_prev(layer), p.dtype))
+    eb = elem_bytes(p.dtype)
+    unit_bytes = p.context * HEAD_DIM * eb
+    staging = None
+    for b in range(p.batch):
+        for kvh in range(p.hkv):
+            if bufs.is_persistent(kvh):
+                if staging is None:
+                    staging = HostBuffer(unit_bytes)
+                s = bufs.slot(kvh)
+                for which, dst in (("k", bufs.k_hbm), ("v", bufs.v_hbm)):
+                    p.fill(which, layer, b, kvh, staging.ptr, threads)
+                    copy_h2d(dst[b, s].data_ptr(), staging.ptr, unit_bytes)
+            else:
+                off = (b * bufs.H + bufs.slot(kvh)) * unit_bytes
+                p.fill("k", layer, b, kvh, bufs.k_host.ptr + off, threads)
+                p.fill("v", layer, b, kvh, bufs.v_host.ptr + off, threads)
+        if log:
+            log(f"  generated sequence {b + 1}/{p.batch}")
+    if bufs.H:
+        copy_h2d(bufs.k_score.data_ptr(), bufs.k_host.ptr, bufs.B * bufs.H * unit_bytes)
+    if staging is not None:
+        staging.close()
+    torch.cuda.synchronize()
+    return bufs
