@@ -1,0 +1,318 @@
+"""Decode-step benchmark of the CLO hot path on one MI355X.
+
+Default workload: the Llama3-8B decode-layer shape at batch 64 -- 32 query / 8
+KV heads, d = 128, bf16, context 131072, top-k 13108 (10%), 80% of (sequence,
+KV head) units with query cosine in [0.801, 0.98] (reuse hits) and 20% in
+[0.2, 0.6] (misses), every KV head offloaded to pinned host memory.  One step =
+the steady decode step (step 1): reuse test, scoring + top-k + zero-copy host
+gather for the miss units, sparse attention for all units.
+
+Prints one JSON line: steps/s, ms/step, the dominant kernel's roofline (host
+gather against the host link; scoring against HBM is reported beside it), the
+measured host-link reference, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn decode steps/s (Llama3-8B shape, B=64); HBM & host-link GB/s vs peak"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+HEAD_DIM = 128
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3])
+    ap.add_argument("--step", type=int, default=1, choices=[0, 1], help="1 = steady step (headline), 0 = cold")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the host-link reference probes")
+    ap.add_argument("--cpu-sample-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB device-to-device copy first (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(bufs, reuse, step_kind):
+    """Bytes the method must move in one step (no scores, histograms, q or idx).
+
+    HBM: M * N * d * b (scoring) + M_p * k * 2 d b (persistent miss rows)
+         + M_np * k * 2 d b (cache writes) + H * k * 2 d b (rows of hit units)
+    host: M_np * k * 2 d b
+    """
+    import numpy as np
+
+    b = 4 if bufs.dtype == "f32" else 2
+    miss = ~reuse.astype(bool)
+    pers = np.array([bufs.is_persistent(h) for h in range(bufs.Hkv)])[None, :].repeat(bufs.B, 0)
+    M = int(miss.sum())
+    M_p = int((miss & pers).sum())
+    M_np = M - M_p
+    H = int((~miss).sum())
+    row2 = bufs.k * 2 * HEAD_DIM * b
+    score = M * bufs.N * HEAD_DIM * b
+    hbm = score + M_p * row2 + M_np * row2 + H * row2
+    host = M_np * row2
+    flops = M * 2 * (bufs.Hq // bufs.Hkv) * HEAD_DIM * bufs.N + bufs.B * bufs.Hkv * 4 * (bufs.Hq // bufs.Hkv) * HEAD_DIM * bufs.k
+    return dict(misses=M, misses_persistent=M_p, misses_host=M_np, hits=H, hbm_bytes=hbm, host_bytes=host,
+                score_bytes=score, attn_bytes=bufs.B * bufs.Hkv * row2, flops=flops)
+
+
+def probe_host_link(torch, nbytes=1 << 30):
+    """Measured host-link reference: SDMA memcpy of pinned memory, and the gather
+    kernel streaming contiguous rows (identity index) from pinned memory."""
+    from top_sparse_attention_02_amd import clo
+    from top_sparse_attention_02_amd.hip_host import HostBuffer, copy_async
+
+    res = {}
+    hb = HostBuffer(nbytes)
+    hb.numpy("u1")[:] = 1
+    dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for i in range(4):
+        e0.record()
+        copy_async(dev.data_ptr(), hb.ptr, nbytes, s.cuda_stream)
+        e1.record()
+        e1.synchronize()
+        if i:
+            times.append(e0.elapsed_time(e1) / 1e3)
+    res["memcpy_h2d_gbs"] = nbytes / min(times) / 1e9
+    # zero-copy streaming read: one unit whose k = N rows are all selected in order
+    rows = nbytes // (2 * HEAD_DIM * 2)  # K and V halves
+    kv = HostBuffer(2 * rows * HEAD_DIM * 2)
+    kv.numpy("u1")[:] = 1
+    idx = torch.arange(rows, dtype=torch.int32, device="cuda").view(1, 1, rows)
+    cache = torch.empty(2, rows, HEAD_DIM, dtype=torch.bfloat16, device="cuda")
+    shape = clo.Shape(1, 1, 1, rows, rows, math.inf, clo.CLO_BF16)
+    layer = clo.Layer(0, None, None, kv.ptr, kv.ptr + rows * HEAD_DIM * 2, None, cache[0], cache[1], idx)
+    times = []
+    for i in range(4):
+        e0.record()
+        clo.clo_gather_kv(shape, layer, None)
+        e1.record()
+        e1.synchronize()
+        if i:
+            times.append(e0.elapsed_time(e1) / 1e3)
+    res["zero_copy_stream_gbs"] = 2 * rows * HEAD_DIM * 2 / min(times) / 1e9
+    res["h_meas_gbs"] = max(res["memcpy_h2d_gbs"], res["zero_copy_stream_gbs"])
+    del dev, cache, idx
+    kv.close()
+    hb.close()
+    return res
+
+
+def cpu_baseline(p, bufs, budget_s, step_kind):
+    """The CPU oracle, as it is, on a bounded sample of the step's units, scaled to steps/s.
+
+    Inputs are the generated ones only: the oracle classifies units with its own
+    cosine test and, for a reused unit, first makes its own previous selection
+    (untimed) from q_prev."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    qf, qpf = oracle.as_f64(p.q(0), p.dtype), oracle.as_f64(p.q_prev(0), p.dtype)
+    g = p.g
+    tau = p.tau if step_kind == 1 else math.inf
+    query = qf if step_kind == 1 else qpf
+    units = [(b, h) for b in range(p.batch) for h in range(p.hkv)]
+    hit_u = [u for u in units
+             if oracle.reuse_decision(oracle.group_cosine(query[u[0], u[1] * g:(u[1] + 1) * g],
+                                                          qpf[u[0], u[1] * g:(u[1] + 1) * g]), tau)]
+    miss_u = [u for u in units if u not in set(hit_u)]
+
+    def kv_stored(b, h):
+        if bufs.is_persistent(h):
+            return p.kv("k", 0, b, h), p.kv("v", 0, b, h)
+        return bufs.host_view("k", b, h), bufs.host_view("v", b, h)
+
+    def run(u, reused):
+        b, h = u
+        K, V = kv_stored(b, h)
+        qg, qpg = query[b, h * g:(h + 1) * g], qpf[b, h * g:(h + 1) * g]
+        prev = None
+        if reused:  # the previous step's selection, made by the oracle itself (untimed)
+            prev = oracle.select_topk(oracle.token_scores(qpg, oracle.as_f64(K, p.dtype)), p.topk)
+        t = time.perf_counter()
+        oracle.decode_unit(qg, qpg, oracle.as_f64(K, p.dtype), oracle.as_f64(V, p.dtype), p.topk, tau, prev)
+        return time.perf_counter() - t
+
+    t_miss, t_hit = [], []
+    spent = 0.0
+    i = 0
+    while spent < budget_s and (i < len(miss_u) or i < len(hit_u)):
+        if i < len(miss_u):
+            t_miss.append(run(miss_u[i], False))
+            spent += t_miss[-1]
+        if i < len(hit_u):
+            t_hit.append(run(hit_u[i], True))
+            spent += t_hit[-1]
+        i += 1
+    est = (np.mean(t_miss) if t_miss else 0.0) * len(miss_u) + (np.mean(t_hit) if t_hit else 0.0) * len(hit_u)
+    return {"value": round(1.0 / est, 6) if est > 0 else None, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(t_miss)} miss + {len(t_hit)} reuse units of the {len(units)}-unit step "
+                      f"({spent:.1f} s of oracle time), fp64 numpy oracle, per-unit mean times scaled to the "
+                      f"step's {len(miss_u)} miss / {len(hit_u)} reuse units",
+            "seconds_per_step_est": round(est, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
+              f"multi-GPU exchange: units shard by sequence or KV head, one process per GPU).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import gen
+    from top_sparse_attention_02_amd import clo, workload
+
+    torch.cuda.set_device(0)
+    clo.load()
+    p = gen.config(args.config)
+    log(f"config {args.config}: B={p.batch} Hq={p.hq} Hkv={p.hkv} N={p.context} k={p.topk} {p.dtype} "
+        f"persistent={p.persistent_mask_bits(0):#x}")
+    t0 = time.time()
+    bufs = workload.load_layer(p, 0, log=log if p.batch >= 16 else None)
+    log(f"inputs generated and resident ({time.time() - t0:.1f} s)")
+
+    probe = None
+    if not args.no_probe:
+        probe = probe_host_link(torch)
+        log(f"host link: memcpy {probe['memcpy_h2d_gbs']:.1f} GB/s, zero-copy stream "
+            f"{probe['zero_copy_stream_gbs']:.1f} GB/s")
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy done: 1 GiB read + 1 GiB written")
+
+    bufs.step0()
+    torch.cuda.synchronize()
+    step = bufs.step1 if args.step == 1 else bufs.step0
+    tau = p.tau if args.step == 1 else math.inf
+    query = bufs.q if args.step == 1 else bufs.q_prev
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K fused decode steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    reuse = bufs.reuse.cpu().numpy()
+    alg = algorithmic_bytes(bufs, reuse, args.step)
+
+    # per-phase times: the same kernels through the separate entry points, events between them
+    shape, layer = bufs.shape_with(tau), bufs.layer()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev[i][0].record()
+        clo.clo_reuse_test(shape, query, bufs.q_prev, bufs.reuse, bufs.cos)
+        ev[i][1].record()
+        clo.clo_topk_select(shape, layer, query, bufs.reuse, bufs.ws)
+        ev[i][2].record()
+        clo.clo_gather_kv(shape, layer, bufs.reuse)
+        ev[i][3].record()
+        clo.clo_sparse_attn(shape, layer, query, bufs.out, bufs.ws)
+        ev[i][4].record()
+    torch.cuda.synchronize()
+    names = ["reuse_test", "score_topk", "gather", "attention"]
+    phases = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+              for j, n in enumerate(names)}
+
+    gather_s = phases["gather"] / 1e3
+    host_gbs = alg["host_bytes"] / gather_s / 1e9 if alg["host_bytes"] else 0.0
+    score_s = phases["score_topk"] / 1e3
+    score_gbs = alg["score_bytes"] / score_s / 1e9 if alg["score_bytes"] else 0.0
+    attn_gbs = alg["attn_bytes"] / (phases["attention"] / 1e3) / 1e9
+    step_s = ms_per_step / 1e3
+    if alg["host_bytes"]:
+        roofline = {"bound": "host-link", "kernel": "gather_kernel", "achieved": round(host_gbs, 2),
+                    "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s", "frac": round(host_gbs / HOST_LINK_PEAK_GBS, 4),
+                    "traffic": None, "bytes_per_launch": alg["host_bytes"],
+                    "launch_ms": round(phases["gather"], 4)}
+        if probe:
+            roofline["peak_measured"] = round(probe["h_meas_gbs"], 2)
+            roofline["frac_measured"] = round(host_gbs / probe["h_meas_gbs"], 4)
+    else:
+        roofline = {"bound": "hbm", "kernel": "score+topk", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+
+    result = {
+        "metric": METRIC,
+        "value": round(1.0 / step_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic (seeded N(0,1) keys/values and queries; no model weights)",
+        "config": {"workload": f"config {args.config}: " + {
+            1: "one layer, B=1, 32Q/8KV, d=128, N=4096, fp32, top-k 410, all heads persistent",
+            2: "Llama3-8B layer, B=16, 32Q/8KV, d=128, N=32768, bf16, top-k 3277, 2/8 heads persistent",
+            3: "Llama3-8B layer, B=64, 32Q/8KV, d=128, N=131072, bf16, top-k 13108, all heads host-resident",
+        }[args.config] + (", steady step (80/20 reuse)" if args.step == 1 else ", cold step (all miss)"),
+            "batch": p.batch, "q_heads": p.hq, "kv_heads": p.hkv, "head_dim": HEAD_DIM, "context": p.context,
+            "topk": p.topk, "tau": p.tau, "step": args.step},
+        "roofline": roofline,
+        "roofline_score": {"bound": "hbm", "kernel": "compact+score+topk", "achieved": round(score_gbs, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
+                           "bytes_per_launch": alg["score_bytes"]},
+        "attention_hbm_gbs": round(attn_gbs, 1),
+        "step_hbm_gbs": round(alg["hbm_bytes"] / step_s / 1e9, 1),
+        "step_host_gbs": round(alg["host_bytes"] / step_s / 1e9, 2),
+        "phases_ms": {k: round(v, 4) for k, v in phases.items()},
+        "units": {k: alg[k] for k in ("misses", "misses_persistent", "misses_host", "hits")},
+        "host_link_probe": {k: round(v, 2) for k, v in probe.items()} if probe else None,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample of units")
+        result["cpu_baseline"] = cpu_baseline(p, bufs, args.cpu_sample_seconds, args.step)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
