@@ -143,15 +143,8 @@ clo_status make_plan(const clo_shape* s, uint64_t pmask, Plan* p) {
   a.tau = s->tau;
   a.dtype = s->dtype;
   a.pmask = pmask;
-  int np = 0, nh = 0;
-  for (int h = 0; h < a.Hkv; ++h) {
-    if ((pmask >> h) & 1ull)
-      a.slot[h] = (int8_t)np++;
-    else
-      a.slot[h] = (int8_t)nh++;
-  }
-  a.P = np;
-  a.H = nh;
+  a.P = __builtin_popcountll(pmask);
+  a.H = a.Hkv - a.P;
   p->e = esize(s->dtype);
   p->U = (int64_t)a.B * a.Hkv;
   p->nch_attn = (int)((a.k + kAttnChunk - 1) / kAttnChunk);

@@ -31,7 +31,6 @@ struct LayerArgs {
   void* k_cache;
   void* v_cache;
   int32_t* idx;
-  int8_t slot[kMaxKvHeads];  // rank of head h among persistent / non-persistent heads
 };
 
 struct Workspace {

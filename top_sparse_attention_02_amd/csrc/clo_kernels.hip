@@ -28,6 +28,8 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------- element access
 __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
   const float4 a = *reinterpret_cast<const float4*>(p);
@@ -93,12 +95,18 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Rank of KV head h among the heads of its kind (persistent or not), in head order.
+__device__ __forceinline__ int head_slot(uint64_t pmask, int h) {
+  const uint64_t below = pmask & ((1ull << h) - 1ull);
+  return ((pmask >> h) & 1ull) ? __popcll(below) : h - __popcll(below);
+}
+
 template <typename T>
 __device__ __forceinline__ const T* unit_keys(const LayerArgs& a, int b, int h) {
   const bool pers = (a.pmask >> h) & 1ull;
   const T* base = static_cast<const T*>(pers ? a.k_hbm : a.k_score);
   const int64_t heads = pers ? a.P : a.H;
-  return base + ((int64_t)b * heads + a.slot[h]) * a.N * kHeadDim;
+  return base + ((int64_t)b * heads + head_slot(a.pmask, h)) * a.N * kHeadDim;
 }
 
 // ---------------------------------------------------------------- A1 reuse test
@@ -218,6 +226,83 @@ __global__ __launch_bounds__(256) void score_kernel(LayerArgs a, const T* __rest
           best = fmaxf(best, sum16(s));
         }
         if (sub == 0 && row[j] < a.N) kout[row[j]] = score_key(best);
+      }
+    }
+  }
+}
+
+// bf16 scoring on the matrix cores: per wave, S[16 x 16] = Qpad[16 x 128] . K^T[128 x 16]
+// with v_mfma_f32_16x16x32_bf16 (four k-steps of 32).  Rows of Qpad are the
+// unit's g query heads (zero rows past g); columns are 16 consecutive keys.
+// Lane l supplies row/column l % 16 and the k-slice (l / 16) of each k-step for
+// both operands, so every key row is read straight from HBM as 16-byte pieces;
+// the dot product only needs A and B to share that k-slice mapping.  The
+// result S[i][j] lands in lane j + 16 * (i / 4), register i % 4: lanes 0-15
+// hold heads 0-3 of key j, lanes 16-31 heads 4-7.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int G>
+__global__ __launch_bounds__(256) void score_mfma_kernel(LayerArgs a, const uint16_t* __restrict__ q,
+                                                         const int32_t* __restrict__ list,
+                                                         const int32_t* __restrict__ counts,
+                                                         uint32_t* __restrict__ keys) {
+  constexpr int TILES = 4;                         // 16-key tiles per wave iteration
+  constexpr int kKeysPerWave = kScoreChunk / 4;    // 512
+  static_assert(G <= 8, "group of at most 8 query heads");
+  const int nch = (int)((a.N + kScoreChunk - 1) / kScoreChunk);
+  const int64_t items = (int64_t)counts[0] * nch;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, ks = lane >> 4;       // tile column / k-slice of this lane
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int u = list[it / nch];
+    const int c = (int)(it % nch);
+    const int b = u / a.Hkv, h = u % a.Hkv;
+    const uint16_t* kb = unit_keys<uint16_t>(a, b, h);
+    bf16x8 qa[4];
+    {
+      const int head = col;  // row of Qpad
+      const uint16_t* qh = q + ((int64_t)b * a.Hq + (int64_t)h * G + (head < G ? head : 0)) * kHeadDim;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 w = *reinterpret_cast<const u32x4*>(qh + s * 32 + ks * 8);
+        if (head >= G) w = u32x4{0u, 0u, 0u, 0u};
+        qa[s] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+    uint32_t* kout = keys + (int64_t)u * a.Np;
+    const int64_t w_begin = (int64_t)c * kScoreChunk + (int64_t)wave * kKeysPerWave;
+    for (int t0 = 0; t0 < kKeysPerWave; t0 += 16 * TILES) {
+      if (w_begin + t0 >= a.N) break;  // uniform per wave
+      u32x4 kbuf[TILES][4];
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        int64_t row = w_begin + t0 + t * 16 + col;
+        row = row < a.N ? row : a.N - 1;
+        const uint16_t* kr = kb + row * kHeadDim + ks * 8;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kbuf[t][s] = *reinterpret_cast<const u32x4*>(kr + s * 32);
+      }
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8, kbuf[t][s]), acc, 0, 0, 0);
+        // max over the unit's heads: rows 0..min(G,4)-1 here, rows 4..G-1 in lane + 16
+        float m = acc[0];
+        if (G > 1) m = fmaxf(m, acc[1]);
+        if (G > 2) m = fmaxf(m, acc[2]);
+        if (G > 3) m = fmaxf(m, acc[3]);
+        if (G > 4) {
+          float m2 = acc[0];
+          if (G > 5) m2 = fmaxf(m2, acc[1]);
+          if (G > 6) m2 = fmaxf(m2, acc[2]);
+          if (G > 7) m2 = fmaxf(m2, acc[3]);
+          m = fmaxf(m, __shfl_down(m2, 16, 64));
+        }
+        const int64_t key = w_begin + t0 + t * 16 + col;
+        if (lane < 16 && key < a.N) kout[key] = score_key(m);
       }
     }
   }
@@ -362,31 +447,32 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
     const int b = u / a.Hkv, h = u % a.Hkv;
     if ((a.pmask >> h) & 1ull) continue;
     if (reuse && reuse[u]) continue;
-    const int64_t slot = (int64_t)b * a.H + a.slot[h];
+    const int64_t slot = (int64_t)b * a.H + head_slot(a.pmask, h);
     const char* ks = static_cast<const char*>(a.k_host) + slot * a.N * RB;
     const char* vs = static_cast<const char*>(a.v_host) + slot * a.N * RB;
     char* kd = static_cast<char*>(a.k_cache) + slot * a.k * RB;
     char* vd = static_cast<char*>(a.v_cache) + slot * a.k * RB;
     const int32_t* ix = a.idx + (int64_t)u * a.k;
     const int64_t r0 = (int64_t)c * kGatherChunk;
-    for (int r = 0; r < kGatherChunk; r += RPI * UNR) {
-      uint4 kx[UNR], vx[UNR];
-      int64_t row[UNR];
+    const int64_t r_end = (r0 + kGatherChunk < a.k) ? r0 + kGatherChunk : a.k;
+    for (int64_t rb = r0; rb < r_end; rb += RPI * UNR) {
+      // rows past the end re-read the last row (in bounds) and are not stored
+      u32x4 kx[UNR], vx[UNR];
 #pragma unroll
       for (int j = 0; j < UNR; ++j) {
-        row[j] = r0 + r + j * RPI + rl;
-        if (row[j] < a.k) {
-          int64_t src = ix[row[j]];
-          src = src < 0 ? 0 : (src >= a.N ? a.N - 1 : src);
-          kx[j] = *reinterpret_cast<const uint4*>(ks + src * RB + sub * 16);
-          vx[j] = *reinterpret_cast<const uint4*>(vs + src * RB + sub * 16);
-        }
+        int64_t row = rb + j * RPI + rl;
+        row = row < r_end ? row : r_end - 1;
+        int64_t src = ix[row];
+        src = src < 0 ? 0 : (src >= a.N ? a.N - 1 : src);
+        kx[j] = *reinterpret_cast<const u32x4*>(ks + src * RB + sub * 16);
+        vx[j] = *reinterpret_cast<const u32x4*>(vs + src * RB + sub * 16);
       }
 #pragma unroll
       for (int j = 0; j < UNR; ++j) {
-        if (row[j] < a.k) {
-          *reinterpret_cast<uint4*>(kd + row[j] * RB + sub * 16) = kx[j];
-          *reinterpret_cast<uint4*>(vd + row[j] * RB + sub * 16) = vx[j];
+        const int64_t row = rb + j * RPI + rl;
+        if (row < r_end) {
+          *reinterpret_cast<u32x4*>(kd + row * RB + sub * 16) = kx[j];
+          *reinterpret_cast<u32x4*>(vd + row * RB + sub * 16) = vx[j];
         }
       }
     }
@@ -413,11 +499,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
   const T* kbase;
   const T* vbase;
   if (pers) {
-    const int64_t s = ((int64_t)b * a.P + a.slot[h]) * a.N * kHeadDim;
+    const int64_t s = ((int64_t)b * a.P + head_slot(a.pmask, h)) * a.N * kHeadDim;
     kbase = static_cast<const T*>(a.k_hbm) + s;
     vbase = static_cast<const T*>(a.v_hbm) + s;
   } else {
-    const int64_t s = (((int64_t)b * a.H + a.slot[h]) * a.k + r0) * kHeadDim;
+    const int64_t s = (((int64_t)b * a.H + head_slot(a.pmask, h)) * a.k + r0) * kHeadDim;
     kbase = static_cast<const T*>(a.k_cache) + s;
     vbase = static_cast<const T*>(a.v_cache) + s;
   }
@@ -583,14 +669,13 @@ hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Worksp
 
 hipError_t launch_score(const LayerArgs& a, const void* q, const Workspace& w, int num_cu, hipStream_t s) {
   const int64_t nch = (a.N + kScoreChunk - 1) / kScoreChunk;
-  const int grid = grid_cap((int64_t)a.B * a.Hkv * nch, (int64_t)num_cu * 8);
+  const int grid = grid_cap((int64_t)a.B * a.Hkv * nch, (int64_t)num_cu * 32);
   return dispatch_group(a.G, [&](auto gc) {
     constexpr int G = decltype(gc)::value;
     if (a.dtype == CLO_F32)
       score_kernel<float, G><<<grid, 256, 0, s>>>(a, static_cast<const float*>(q), w.list_all, w.counts, w.keys);
     else
-      score_kernel<uint16_t, G><<<grid, 256, 0, s>>>(a, static_cast<const uint16_t*>(q), w.list_all, w.counts,
-                                                     w.keys);
+      score_mfma_kernel<G><<<grid, 256, 0, s>>>(a, static_cast<const uint16_t*>(q), w.list_all, w.counts, w.keys);
     return hipGetLastError();
   });
 }
