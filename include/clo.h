@@ -24,8 +24,9 @@
  * belongs to KV head h / g, g = n_q_heads / n_kv_heads.
  *
  * Conventions for every entry point:
- *  - All buffers are caller-owned.  The library allocates nothing, frees
- *    nothing and keeps no pointer after the call returns.
+ *  - All buffers are caller-owned.  The library allocates no memory, frees
+ *    nothing and keeps no pointer after the call returns (the only state it
+ *    keeps is clo_decode_step's helper streams and events, see there).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  Buffers must stay alive until the stream work completes.
  *  - Arguments are validated on the host before anything is launched; a
@@ -166,10 +167,21 @@ clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const
                            void* ws, size_t ws_bytes, const clo_sync* sync, void* stream);
 
 /*
- * A1..A5 -- one whole decode step of one layer on one stream: reuse test,
- * then scoring, top-k and gather for the miss units, then attention for all
- * units.  Same buffers and semantics as the calls above; the reuse decisions
- * never leave the GPU.  cos may be NULL; reuse must not be NULL.
+ * A1..A5 -- one whole decode step of one layer: reuse test, then scoring,
+ * top-k and gather for the miss units, then attention for all units.  Same
+ * buffers and semantics as the calls above; the reuse decisions never leave
+ * the GPU.  cos may be NULL; reuse must not be NULL.
+ *
+ * When the layer has offloaded heads, the step overlaps its HBM work with the
+ * host gather: units are split into ranges; `stream` scores and selects range
+ * after range, a helper stream gathers each range once its top-k is done, and
+ * a second helper stream attends the reuse units and then each gathered range.
+ * The two helper streams (default priority, non-blocking) and their events are
+ * created by the library on first use per device and kept until the process
+ * ends; they hold no user data.  All ordering is done on the GPU with events;
+ * the call is ordered after earlier work on `stream`, and later work on
+ * `stream` is ordered after all of the step.  Concurrent calls on one device
+ * share the helper streams (their work then runs one after another).
  */
 clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const void* q,
                            const void* q_prev, void* out, uint8_t* reuse, float* cos,

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/clo.h"
 #include "clo_internal.h"
@@ -151,9 +152,9 @@ clo_status make_plan(const clo_shape* s, uint64_t pmask, Plan* p) {
   return ok();
 }
 
-// Workspace layout: counts | list_all | list_host | keys | part, each 256-byte aligned.
+// Workspace layout: meta | list_all | list_host | list_hit | keys | part, each 256-byte aligned.
 struct WsLayout {
-  size_t counts, list_all, list_host, keys, part, total;
+  size_t meta, list_all, list_host, list_hit, keys, part, total;
 };
 
 WsLayout ws_layout(const Plan& p) {
@@ -164,9 +165,10 @@ WsLayout ws_layout(const Plan& p) {
     off += (size_t)round_up((int64_t)bytes, 256);
     return at;
   };
-  w.counts = take(16);
+  w.meta = take(kMetaInts * 4);
   w.list_all = take((size_t)p.U * 4);
   w.list_host = take((size_t)p.U * 4);
+  w.list_hit = take((size_t)p.U * 4);
   w.keys = take((size_t)p.U * (size_t)p.a.Np * 4);
   w.part = take((size_t)p.U * (size_t)p.nch_attn * (size_t)p.a.G * kPartStride * 4);
   w.total = off;
@@ -184,11 +186,59 @@ clo_status bind_ws(const Plan& p, void* ws, size_t ws_bytes, Workspace* w) {
     return fail(CLO_E_WORKSPACE, "%s", why);
   }
   char* b = static_cast<char*>(ws);
-  w->counts = reinterpret_cast<int32_t*>(b + L.counts);
+  w->meta = reinterpret_cast<int32_t*>(b + L.meta);
   w->list_all = reinterpret_cast<int32_t*>(b + L.list_all);
   w->list_host = reinterpret_cast<int32_t*>(b + L.list_host);
+  w->list_hit = reinterpret_cast<int32_t*>(b + L.list_hit);
   w->keys = reinterpret_cast<uint32_t*>(b + L.keys);
   w->part = reinterpret_cast<float*>(b + L.part);
+  return ok();
+}
+
+Span span_all_misses(const Workspace& w) { return Span{w.list_all, w.meta + kMetaZero, w.meta + kMetaCountAll}; }
+Span span_hits(const Workspace& w) { return Span{w.list_hit, w.meta + kMetaZero, w.meta + kMetaCountHit}; }
+Span span_range(const Workspace& w, int r) {
+  return Span{w.list_all, w.meta + kMetaOffAll + r, w.meta + kMetaOffAll + r + 1};
+}
+Span span_host_range(const Workspace& w, int r) {
+  return Span{w.list_host, w.meta + kMetaOffHost + r, w.meta + kMetaOffHost + r + 1};
+}
+constexpr Span kAllUnits{nullptr, nullptr, nullptr};
+
+// Per-device helper streams and events of the overlapped decode step, created
+// on first use and kept for the life of the process.  They hold no user data.
+struct DeviceQueues {
+  std::mutex mu;  // one decode step enqueues at a time per device
+  bool ready = false;
+  hipStream_t gather = nullptr;  // host gathers, one unit range after another
+  hipStream_t attend = nullptr;  // attention: reuse units first, then each range's misses
+  hipEvent_t ev_attn = nullptr;
+  hipEvent_t ev_topk[kMaxRanges] = {}, ev_gather[kMaxRanges] = {};
+};
+
+DeviceQueues g_queues[64];
+std::mutex g_queues_init;
+
+clo_status device_queues(DeviceQueues** out) {
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) {
+    (void)hipGetLastError();
+    return fail(CLO_E_HIP, "no current HIP device");
+  }
+  DeviceQueues& q = g_queues[d];
+  std::lock_guard<std::mutex> lk(g_queues_init);
+  if (!q.ready) {
+    hipError_t e = hipStreamCreateWithFlags(&q.gather, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&q.attend, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&q.ev_attn, hipEventDisableTiming);
+    for (int r = 0; r < kMaxRanges && e == hipSuccess; ++r) {
+      e = hipEventCreateWithFlags(&q.ev_topk[r], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&q.ev_gather[r], hipEventDisableTiming);
+    }
+    if (e != hipSuccess) return fail(CLO_E_HIP, "creating helper streams/events: %s", hipGetErrorString(e));
+    q.ready = true;
+  }
+  *out = &q;
   return ok();
 }
 
@@ -314,9 +364,9 @@ clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int cu = num_cus();
-  if ((st = hip_status(launch_compact(p.a, reuse, w, s), "compact launch"))) return st;
-  if ((st = hip_status(launch_score(p.a, q, w, cu, s), "score launch"))) return st;
-  return hip_status(launch_topk(p.a, w, cu, s), "top-k launch");
+  if ((st = hip_status(launch_compact(p.a, reuse, w, 1, s), "compact launch"))) return st;
+  if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w.keys, cu, s), "score launch"))) return st;
+  return hip_status(launch_topk(p.a, span_all_misses(w), p.U, w.keys, cu, s), "top-k launch");
 }
 
 clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const uint8_t* reuse, const clo_sync* sync,
@@ -333,7 +383,7 @@ clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const u
   if ((st = check_layer(layer, &p, NEED_HOST | NEED_CACHE))) return st;
   if (reuse && (st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
   if ((st = pre_wait(sync, s))) return st;
-  if ((st = hip_status(launch_gather(p.a, reuse, num_cus(), s), "gather launch"))) return st;
+  if ((st = hip_status(launch_gather(p.a, reuse, kAllUnits, p.U, kGatherBlocksAlone, s), "gather launch"))) return st;
   return post_signal(sync, s);
 }
 
@@ -354,9 +404,71 @@ clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const
   if ((st = check_device(out, q_bytes(p), "out"))) return st;
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
   if ((st = pre_wait(sync, s))) return st;
-  if ((st = hip_status(launch_attention(p.a, q, out, w, s), "attention launch"))) return st;
+  if ((st = hip_status(launch_attn_partial(p.a, q, w.part, kAllUnits, p.U, s), "attention launch"))) return st;
+  if ((st = hip_status(launch_attn_combine(p.a, w.part, out, s), "attention combine launch"))) return st;
   return post_signal(sync, s);
 }
+
+namespace {
+
+// Decode step for layers without offloaded heads: one stream, nothing to overlap.
+clo_status step_in_order(const Plan& p, const Workspace& w, const void* q, const void* q_prev, void* out,
+                         uint8_t* reuse, float* cos, hipStream_t s) {
+  clo_status st;
+  const int cu = num_cus();
+  if ((st = hip_status(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch"))) return st;
+  if ((st = hip_status(launch_compact(p.a, reuse, w, 1, s), "compact launch"))) return st;
+  if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w.keys, cu, s), "score launch"))) return st;
+  if ((st = hip_status(launch_topk(p.a, span_all_misses(w), p.U, w.keys, cu, s), "top-k launch"))) return st;
+  if ((st = hip_status(launch_attn_partial(p.a, q, w.part, kAllUnits, p.U, s), "attention launch"))) return st;
+  return hip_status(launch_attn_combine(p.a, w.part, out, s), "attention combine launch");
+}
+
+// Decode step with offloaded heads.  Units are split into R ranges.  The
+// caller's stream scores and selects range after range; the gather stream
+// starts each range's host reads as soon as its top-k is done; the attention
+// stream first attends the reuse units (which need nothing new) and then each
+// range's miss units once their rows have arrived.  Events order the streams
+// on the GPU; the host never waits.  The caller's stream finally waits for the
+// attention stream, so the call is ordered like a single-stream call.
+clo_status step_overlapped(const Plan& p, const Workspace& w, const void* q, const void* q_prev, void* out,
+                           uint8_t* reuse, float* cos, hipStream_t s) {
+  DeviceQueues* dq = nullptr;
+  clo_status st;
+  if ((st = device_queues(&dq))) return st;
+  std::lock_guard<std::mutex> lk(dq->mu);
+  const int cu = num_cus();
+  const int R = (int)(p.U < 8 ? p.U : 8);
+  const int64_t per = (p.U + R - 1) / R + 1;  // bound on the units of one range
+  hipStream_t gs = dq->gather, as = dq->attend;
+#define CLO_TRY(expr, what) \
+  if ((st = hip_status((expr), (what)))) return st
+  CLO_TRY(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch");
+  CLO_TRY(launch_compact(p.a, reuse, w, R, s), "compact launch");
+  for (int r = 0; r < R; ++r) {
+    CLO_TRY(launch_score(p.a, q, span_range(w, r), per, w.keys, cu, s), "score launch");
+    CLO_TRY(launch_topk(p.a, span_range(w, r), per, w.keys, cu, s), "top-k launch");
+    CLO_TRY(hipEventRecord(dq->ev_topk[r], s), "event record");
+    CLO_TRY(hipStreamWaitEvent(gs, dq->ev_topk[r], 0), "stream wait");
+    if (r == 0) {
+      // reuse units need no new rows; start them once the first range is selected,
+      // so that their many short blocks do not delay the first top-k
+      CLO_TRY(hipStreamWaitEvent(as, dq->ev_topk[0], 0), "stream wait");
+      CLO_TRY(launch_attn_partial(p.a, q, w.part, span_hits(w), p.U, as), "attention launch");
+    }
+    CLO_TRY(launch_gather(p.a, reuse, span_host_range(w, r), per, kGatherBlocksOverlapped, gs), "gather launch");
+    CLO_TRY(hipEventRecord(dq->ev_gather[r], gs), "event record");
+    CLO_TRY(hipStreamWaitEvent(as, dq->ev_gather[r], 0), "stream wait");
+    CLO_TRY(launch_attn_partial(p.a, q, w.part, span_range(w, r), per, as), "attention launch");
+  }
+  CLO_TRY(launch_attn_combine(p.a, w.part, out, as), "attention combine launch");
+  CLO_TRY(hipEventRecord(dq->ev_attn, as), "event record");
+  CLO_TRY(hipStreamWaitEvent(s, dq->ev_attn, 0), "stream wait");
+#undef CLO_TRY
+  return ok();
+}
+
+}  // namespace
 
 clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const void* q, const void* q_prev,
                            void* out, uint8_t* reuse, float* cos, void* ws, size_t ws_bytes, const clo_sync* sync,
@@ -378,14 +490,10 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
   if ((st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
   if (cos && (st = check_device(cos, (size_t)p.U * 4, "cos"))) return st;
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
-  const int cu = num_cus();
   if ((st = pre_wait(sync, s))) return st;
-  if ((st = hip_status(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch"))) return st;
-  if ((st = hip_status(launch_compact(p.a, reuse, w, s), "compact launch"))) return st;
-  if ((st = hip_status(launch_score(p.a, q, w, cu, s), "score launch"))) return st;
-  if ((st = hip_status(launch_topk(p.a, w, cu, s), "top-k launch"))) return st;
-  if (p.a.H > 0 && (st = hip_status(launch_gather(p.a, reuse, cu, s), "gather launch"))) return st;
-  if ((st = hip_status(launch_attention(p.a, q, out, w, s), "attention launch"))) return st;
+  st = p.a.H > 0 ? step_overlapped(p, w, q, q_prev, out, reuse, cos, s)
+                 : step_in_order(p, w, q, q_prev, out, reuse, cos, s);
+  if (st) return st;
   return post_signal(sync, s);
 }
 

@@ -16,6 +16,15 @@ constexpr int kGatherChunk = 512;   // rows gathered by one work item
 constexpr int kAttnChunk = 256;     // selected rows attended by one work item
 constexpr int kPartStride = kHeadDim + 2;  // floats per (chunk, head) partial: o[d], m, l
 
+// Gather grid.  Each 4-wave block keeps 8 rows x 2 (K, V) x 16 B per lane in
+// flight (32 KiB per block); the host link saturates with far fewer bytes in
+// flight than 32 blocks provide.  More blocks fill the memory request queues
+// with slow host reads and stall HBM kernels running beside the gather
+// (measured on MI355X: 256 blocks -> 14.8 ms per config-3 step, 32 -> 13.2 ms,
+// with the gather alone unchanged at ~12.2 ms).
+constexpr int kGatherBlocksOverlapped = 32;
+constexpr int kGatherBlocksAlone = 64;
+
 // Everything a kernel needs to address one layer's buffers.
 struct LayerArgs {
   int32_t B, Hq, Hkv, G, P, H;
@@ -33,12 +42,35 @@ struct LayerArgs {
   int32_t* idx;
 };
 
+// Unit ranges of one decode step: units are split into R contiguous ranges
+// (unit u belongs to range u * R / U) so that the gather of one range can run
+// while the next range is scored.
+constexpr int kMaxRanges = 16;
+
+// Layout of the int32 "meta" block at the start of the workspace.
+constexpr int kMetaCountAll = 0;   // miss units
+constexpr int kMetaCountHost = 1;  // miss units of non-persistent heads
+constexpr int kMetaCountHit = 2;   // reuse units
+constexpr int kMetaZero = 4;       // always 0
+constexpr int kMetaOffAll = 16;    // [R + 1] first position of each range in list_all
+constexpr int kMetaOffHost = 40;   // [R + 1] first position of each range in list_host
+constexpr int kMetaInts = 64;
+
 struct Workspace {
-  int32_t* counts;     // [0] miss units, [1] miss units of non-persistent heads
+  int32_t* meta;       // counts and range offsets (layout above)
   int32_t* list_all;   // [U] miss units, ascending
   int32_t* list_host;  // [U] miss units of non-persistent heads, ascending
+  int32_t* list_hit;   // [U] reuse units, ascending
   uint32_t* keys;      // [U][Np] order-preserving score keys
   float* part;         // [U][nch][G][kPartStride] attention partials
+};
+
+// A device-side list of units: list[*lo .. *hi).  list == nullptr means "all
+// units" (and, for the gather, "skip reuse units and persistent heads").
+struct Span {
+  const int32_t* list;
+  const int32_t* lo;
+  const int32_t* hi;
 };
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -46,11 +78,19 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // Launchers: enqueue on `s`; return the HIP error of the launch.
 hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, uint8_t* reuse, float* cos,
                         hipStream_t s);
-hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, hipStream_t s);
-hipError_t launch_score(const LayerArgs& a, const void* q, const Workspace& w, int num_cu, hipStream_t s);
-hipError_t launch_topk(const LayerArgs& a, const Workspace& w, int num_cu, hipStream_t s);
-hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, int num_cu, hipStream_t s);
-hipError_t launch_attention(const LayerArgs& a, const void* q, void* out, const Workspace& w, hipStream_t s);
+// max_units: an upper bound on the span's length, used to size the grid.
+hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, int ranges, hipStream_t s);
+hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_units, uint32_t* keys, int num_cu,
+                        hipStream_t s);
+hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uint32_t* keys, int num_cu,
+                       hipStream_t s);
+// max_blocks bounds the grid: the host link saturates with a few hundred
+// waves in flight, and a smaller grid leaves the CUs to concurrent kernels.
+hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, Span sp, int64_t max_units, int max_blocks,
+                         hipStream_t s);
+hipError_t launch_attn_partial(const LayerArgs& a, const void* q, float* part, Span sp, int64_t max_units,
+                               hipStream_t s);
+hipError_t launch_attn_combine(const LayerArgs& a, const float* part, void* out, hipStream_t s);
 hipError_t launch_wait(const uint32_t* flag, uint32_t value, uint32_t spin_limit, uint32_t* error_word,
                        hipStream_t s);
 hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s);

@@ -140,60 +140,89 @@ __global__ __launch_bounds__(64) void reuse_kernel(const T* __restrict__ q, cons
   }
 }
 
-// ---------------------------------------------------------------- miss lists
+// ---------------------------------------------------------------- unit lists
+// One block scans the reuse flags in unit order into three ascending lists
+// (miss units, miss units of non-persistent heads, reuse units) and the first
+// list position of each of the R unit ranges; nothing is read back by the host.
 __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict__ reuse, int U, int Hkv,
-                                                       uint64_t pmask, int32_t* __restrict__ counts,
+                                                       uint64_t pmask, int R, int32_t* __restrict__ meta,
                                                        int32_t* __restrict__ list_all,
-                                                       int32_t* __restrict__ list_host) {
-  __shared__ int wsum[2][16];
-  __shared__ int base[2];
+                                                       int32_t* __restrict__ list_host,
+                                                       int32_t* __restrict__ list_hit) {
+  __shared__ int wsum[3][16];
+  __shared__ int base[3];
+  __shared__ int rcount[2][kMaxRanges];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (tid == 0) base[0] = base[1] = 0;
+  if (tid < 3) base[tid] = 0;
+  if (tid < 2 * kMaxRanges) (&rcount[0][0])[tid] = 0;
   __syncthreads();
   for (int t0 = 0; t0 < U; t0 += 1024) {
     const int u = t0 + tid;
-    const bool miss = (u < U) && (reuse == nullptr || reuse[u] == 0);
+    const bool valid = u < U;
+    const bool miss = valid && (reuse == nullptr || reuse[u] == 0);
     const bool host = miss && !((pmask >> (u % Hkv)) & 1ull);
-    const uint64_t bm = __ballot(miss), bh = __ballot(host);
+    const bool hit = valid && !miss;
+    if (miss) {
+      const int r = (int)((int64_t)u * R / U);
+      atomicAdd(&rcount[0][r], 1);
+      if (host) atomicAdd(&rcount[1][r], 1);
+    }
+    const uint64_t bm = __ballot(miss), bh = __ballot(host), bt = __ballot(hit);
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
     if (lane == 0) {
       wsum[0][w] = __popcll(bm);
       wsum[1][w] = __popcll(bh);
+      wsum[2][w] = __popcll(bt);
     }
     __syncthreads();
     int om = base[0] + __popcll(bm & below), oh = base[1] + __popcll(bh & below);
+    int ot = base[2] + __popcll(bt & below);
     for (int i = 0; i < w; ++i) {
       om += wsum[0][i];
       oh += wsum[1][i];
+      ot += wsum[2][i];
     }
     if (miss) list_all[om] = u;
     if (host) list_host[oh] = u;
+    if (hit) list_hit[ot] = u;
     __syncthreads();
     if (tid == 0) {
       for (int i = 0; i < 16; ++i) {
         base[0] += wsum[0][i];
         base[1] += wsum[1][i];
+        base[2] += wsum[2][i];
       }
     }
     __syncthreads();
   }
   if (tid == 0) {
-    counts[0] = base[0];
-    counts[1] = base[1];
+    meta[kMetaCountAll] = base[0];
+    meta[kMetaCountHost] = base[1];
+    meta[kMetaCountHit] = base[2];
+    meta[kMetaZero] = 0;
+    int oa = 0, oh = 0;
+    for (int r = 0; r < R; ++r) {
+      meta[kMetaOffAll + r] = oa;
+      meta[kMetaOffHost + r] = oh;
+      oa += rcount[0][r];
+      oh += rcount[1][r];
+    }
+    meta[kMetaOffAll + R] = oa;
+    meta[kMetaOffHost + R] = oh;
   }
 }
 
 // ---------------------------------------------------------------- A2 scoring
 // 16 lanes per key row (8 elements each), 4 rows per wave instruction.
 template <typename T, int G>
-__global__ __launch_bounds__(256) void score_kernel(LayerArgs a, const T* __restrict__ q,
-                                                    const int32_t* __restrict__ list,
-                                                    const int32_t* __restrict__ counts,
+__global__ __launch_bounds__(256) void score_kernel(LayerArgs a, const T* __restrict__ q, Span sp,
                                                     uint32_t* __restrict__ keys) {
   constexpr int UNR = 8;
   constexpr int kRowsPerWave = kScoreChunk / 4;
   const int nch = (int)((a.N + kScoreChunk - 1) / kScoreChunk);
-  const int64_t items = (int64_t)counts[0] * nch;
+  const int lo = *sp.lo;
+  const int64_t items = (int64_t)(*sp.hi - lo) * nch;
+  const int32_t* list = sp.list + lo;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane & 15, rg = lane >> 4;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
@@ -243,15 +272,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int G>
-__global__ __launch_bounds__(256) void score_mfma_kernel(LayerArgs a, const uint16_t* __restrict__ q,
-                                                         const int32_t* __restrict__ list,
-                                                         const int32_t* __restrict__ counts,
+__global__ __launch_bounds__(256) void score_mfma_kernel(LayerArgs a, const uint16_t* __restrict__ q, Span sp,
                                                          uint32_t* __restrict__ keys) {
   constexpr int TILES = 4;                         // 16-key tiles per wave iteration
   constexpr int kKeysPerWave = kScoreChunk / 4;    // 512
   static_assert(G <= 8, "group of at most 8 query heads");
   const int nch = (int)((a.N + kScoreChunk - 1) / kScoreChunk);
-  const int64_t items = (int64_t)counts[0] * nch;
+  const int lo = *sp.lo;
+  const int64_t items = (int64_t)(*sp.hi - lo) * nch;
+  const int32_t* list = sp.list + lo;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, ks = lane >> 4;       // tile column / k-slice of this lane
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
@@ -313,15 +342,15 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(LayerArgs a, const uint
 // find the k-th largest key T and how many keys equal to T are taken; then a
 // block-wide scan writes the winners in ascending index order (keys > T, plus
 // the first `need` keys == T by index).
-__global__ __launch_bounds__(1024) void topk_kernel(LayerArgs a, const int32_t* __restrict__ list,
-                                                    const int32_t* __restrict__ counts,
-                                                    const uint32_t* __restrict__ keys) {
+__global__ __launch_bounds__(1024) void topk_kernel(LayerArgs a, Span sp, const uint32_t* __restrict__ keys) {
   __shared__ uint32_t hist[16][256];
   __shared__ uint32_t tot[256];
   __shared__ uint32_t s_prefix, s_mask, s_rem, s_base_gt, s_base_eq;
   __shared__ uint32_t s_wgt[16], s_weq[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_units = counts[0];
+  const int lo = *sp.lo;
+  const int n_units = *sp.hi - lo;
+  const int32_t* list = sp.list + lo;
   const int64_t N = a.N;
   for (int it = blockIdx.x; it < n_units; it += gridDim.x) {
     const int u = list[it];
@@ -433,20 +462,21 @@ __global__ __launch_bounds__(1024) void topk_kernel(LayerArgs a, const int32_t* 
 // loads from pinned host memory are issued UNR rows deep per lane before any
 // store so that many reads are in flight on the host link.
 template <typename T>
-__global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t* __restrict__ reuse) {
+__global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp) {
   constexpr int RB = kHeadDim * (int)sizeof(T);  // row bytes
   constexpr int LPR = RB / 16;
   constexpr int RPI = 256 / LPR;
   constexpr int UNR = 8;
   const int nch = (int)((a.k + kGatherChunk - 1) / kGatherChunk);
-  const int64_t items = (int64_t)a.B * a.Hkv * nch;
+  const int lo = sp.list ? *sp.lo : 0;
+  const int64_t n_units = sp.list ? (int64_t)(*sp.hi - lo) : (int64_t)a.B * a.Hkv;
+  const int64_t items = n_units * nch;
   const int sub = threadIdx.x % LPR, rl = threadIdx.x / LPR;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int u = (int)(it / nch);
+    const int u = sp.list ? sp.list[lo + it / nch] : (int)(it / nch);
     const int c = (int)(it % nch);
     const int b = u / a.Hkv, h = u % a.Hkv;
-    if ((a.pmask >> h) & 1ull) continue;
-    if (reuse && reuse[u]) continue;
+    if (!sp.list && (((a.pmask >> h) & 1ull) || (reuse && reuse[u]))) continue;
     const int64_t slot = (int64_t)b * a.H + head_slot(a.pmask, h);
     const char* ks = static_cast<const char*>(a.k_host) + slot * a.N * RB;
     const char* vs = static_cast<const char*>(a.v_host) + slot * a.N * RB;
@@ -486,11 +516,19 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
 // chunk is merged by attn_combine_kernel.
 template <typename T, int G>
 __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T* __restrict__ q,
-                                                           float* __restrict__ part, int nch) {
+                                                           float* __restrict__ part, int nch, Span sp) {
   __shared__ float lg[G][kAttnChunk];
   __shared__ float red[4][G][kHeadDim];
   __shared__ float sm[G], sl[G];
-  const int u = blockIdx.x / nch, c = blockIdx.x % nch;
+  int u;
+  if (sp.list) {
+    const int lo = *sp.lo;
+    if ((int64_t)blockIdx.x >= (int64_t)(*sp.hi - lo) * nch) return;  // whole block
+    u = sp.list[lo + blockIdx.x / nch];
+  } else {
+    u = blockIdx.x / nch;
+  }
+  const int c = blockIdx.x % nch;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const bool pers = (a.pmask >> h) & 1ull;
   const int64_t r0 = (int64_t)c * kAttnChunk;
@@ -662,57 +700,65 @@ hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, u
   return hipGetLastError();
 }
 
-hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, hipStream_t s) {
-  compact_kernel<<<1, 1024, 0, s>>>(reuse, a.B * a.Hkv, a.Hkv, a.pmask, w.counts, w.list_all, w.list_host);
+hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, int ranges, hipStream_t s) {
+  compact_kernel<<<1, 1024, 0, s>>>(reuse, a.B * a.Hkv, a.Hkv, a.pmask, ranges, w.meta, w.list_all, w.list_host,
+                                    w.list_hit);
   return hipGetLastError();
 }
 
-hipError_t launch_score(const LayerArgs& a, const void* q, const Workspace& w, int num_cu, hipStream_t s) {
+hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_units, uint32_t* keys, int num_cu,
+                        hipStream_t s) {
   const int64_t nch = (a.N + kScoreChunk - 1) / kScoreChunk;
-  const int grid = grid_cap((int64_t)a.B * a.Hkv * nch, (int64_t)num_cu * 32);
+  const int grid = grid_cap(max_units * nch, (int64_t)num_cu * 32);
   return dispatch_group(a.G, [&](auto gc) {
     constexpr int G = decltype(gc)::value;
     if (a.dtype == CLO_F32)
-      score_kernel<float, G><<<grid, 256, 0, s>>>(a, static_cast<const float*>(q), w.list_all, w.counts, w.keys);
+      score_kernel<float, G><<<grid, 256, 0, s>>>(a, static_cast<const float*>(q), sp, keys);
     else
-      score_mfma_kernel<G><<<grid, 256, 0, s>>>(a, static_cast<const uint16_t*>(q), w.list_all, w.counts, w.keys);
+      score_mfma_kernel<G><<<grid, 256, 0, s>>>(a, static_cast<const uint16_t*>(q), sp, keys);
     return hipGetLastError();
   });
 }
 
-hipError_t launch_topk(const LayerArgs& a, const Workspace& w, int num_cu, hipStream_t s) {
-  const int grid = grid_cap((int64_t)a.B * a.Hkv, (int64_t)num_cu * 2);
-  topk_kernel<<<grid, 1024, 0, s>>>(a, w.list_all, w.counts, w.keys);
+hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uint32_t* keys, int num_cu,
+                       hipStream_t s) {
+  const int grid = grid_cap(max_units, (int64_t)num_cu * 2);
+  topk_kernel<<<grid, 1024, 0, s>>>(a, sp, keys);
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, int num_cu, hipStream_t s) {
+hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, Span sp, int64_t max_units, int max_blocks,
+                         hipStream_t s) {
   const int64_t nch = (a.k + kGatherChunk - 1) / kGatherChunk;
-  const int grid = grid_cap((int64_t)a.B * a.Hkv * nch, (int64_t)num_cu * 8);
+  const int grid = grid_cap(max_units * nch, (int64_t)max_blocks);
   if (a.dtype == CLO_F32)
-    gather_kernel<float><<<grid, 256, 0, s>>>(a, reuse);
+    gather_kernel<float><<<grid, 256, 0, s>>>(a, reuse, sp);
   else
-    gather_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse);
+    gather_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse, sp);
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const LayerArgs& a, const void* q, void* out, const Workspace& w, hipStream_t s) {
+hipError_t launch_attn_partial(const LayerArgs& a, const void* q, float* part, Span sp, int64_t max_units,
+                               hipStream_t s) {
   const int nch = (int)((a.k + kAttnChunk - 1) / kAttnChunk);
-  const int64_t U = (int64_t)a.B * a.Hkv;
-  hipError_t e = dispatch_group(a.G, [&](auto gc) {
+  const unsigned grid = (unsigned)(max_units > 0 ? max_units * nch : 1);
+  return dispatch_group(a.G, [&](auto gc) {
     constexpr int G = decltype(gc)::value;
     if (a.dtype == CLO_F32)
-      attn_partial_kernel<float, G><<<(unsigned)(U * nch), 256, 0, s>>>(a, static_cast<const float*>(q), w.part, nch);
+      attn_partial_kernel<float, G><<<grid, 256, 0, s>>>(a, static_cast<const float*>(q), part, nch, sp);
     else
-      attn_partial_kernel<uint16_t, G><<<(unsigned)(U * nch), 256, 0, s>>>(a, static_cast<const uint16_t*>(q), w.part,
-                                                                           nch);
+      attn_partial_kernel<uint16_t, G><<<grid, 256, 0, s>>>(a, static_cast<const uint16_t*>(q), part, nch, sp);
     return hipGetLastError();
   });
-  if (e != hipSuccess) return e;
+}
+
+hipError_t launch_attn_combine(const LayerArgs& a, const float* part, void* out, hipStream_t s) {
+  const int nch = (int)((a.k + kAttnChunk - 1) / kAttnChunk);
+  const unsigned grid = (unsigned)((int64_t)a.B * a.Hkv * a.G);
   if (a.dtype == CLO_F32)
-    attn_combine_kernel<float><<<(unsigned)(U * a.G), 128, 0, s>>>(a, w.part, nch, static_cast<float*>(out));
+    attn_combine_kernel<float><<<grid, 128, 0, s>>>(a, part, nch, static_cast<float*>(out));
   else
-    attn_combine_kernel<uint16_t><<<(unsigned)(U * a.G), 128, 0, s>>>(a, w.part, nch, static_cast<uint16_t*>(out));
+    attn_combine_kernel<uint16_t><<<grid, 128, 0, s>>>(a, part, nch, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
