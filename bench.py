@@ -39,7 +39,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3])
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--data-layers", type=int, default=0,
+                    help="configs 4-5: distinct K/V layer buffers, reused cyclically over the 48 layers")
     ap.add_argument("--step", type=int, default=1, choices=[0, 1], help="1 = steady step (headline), 0 = cold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the host-link reference probes")
@@ -49,29 +51,40 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(bufs, reuse, step_kind):
-    """Bytes the method must move in one step (no scores, histograms, q or idx).
+def algorithmic_bytes(layers):
+    """Bytes the method must move in one step over the given layers (no scores,
+    histograms, q or idx), from each layer's reuse flags after the step.
 
     HBM: M * N * d * b (scoring) + M_p * k * 2 d b (persistent miss rows)
-         + M_np * k * 2 d b (cache writes) + H * k * 2 d b (rows of hit units)
+         + M_np * k * 2 d b (cache writes) + H * k * 2 d b (rows of reuse units)
     host: M_np * k * 2 d b
     """
     import numpy as np
 
-    b = 4 if bufs.dtype == "f32" else 2
-    miss = ~reuse.astype(bool)
-    pers = np.array([bufs.is_persistent(h) for h in range(bufs.Hkv)])[None, :].repeat(bufs.B, 0)
-    M = int(miss.sum())
-    M_p = int((miss & pers).sum())
-    M_np = M - M_p
-    H = int((~miss).sum())
-    row2 = bufs.k * 2 * HEAD_DIM * b
-    score = M * bufs.N * HEAD_DIM * b
-    hbm = score + M_p * row2 + M_np * row2 + H * row2
-    host = M_np * row2
-    flops = M * 2 * (bufs.Hq // bufs.Hkv) * HEAD_DIM * bufs.N + bufs.B * bufs.Hkv * 4 * (bufs.Hq // bufs.Hkv) * HEAD_DIM * bufs.k
-    return dict(misses=M, misses_persistent=M_p, misses_host=M_np, hits=H, hbm_bytes=hbm, host_bytes=host,
-                score_bytes=score, attn_bytes=bufs.B * bufs.Hkv * row2, flops=flops)
+    tot = dict(misses=0, misses_persistent=0, misses_host=0, hits=0, hbm_bytes=0, host_bytes=0, score_bytes=0,
+               attn_bytes=0, flops=0)
+    for bufs in layers:
+        b = 4 if bufs.dtype == "f32" else 2
+        reuse = bufs.reuse.cpu().numpy()
+        miss = ~reuse.astype(bool)
+        pers = np.array([bufs.is_persistent(h) for h in range(bufs.Hkv)])[None, :].repeat(bufs.B, 0)
+        M = int(miss.sum())
+        M_p = int((miss & pers).sum())
+        M_np = M - M_p
+        H = int((~miss).sum())
+        g = bufs.Hq // bufs.Hkv
+        row2 = bufs.k * 2 * HEAD_DIM * b
+        score = M * bufs.N * HEAD_DIM * b
+        tot["misses"] += M
+        tot["misses_persistent"] += M_p
+        tot["misses_host"] += M_np
+        tot["hits"] += H
+        tot["score_bytes"] += score
+        tot["hbm_bytes"] += score + M_p * row2 + M_np * row2 + H * row2
+        tot["host_bytes"] += M_np * row2
+        tot["attn_bytes"] += bufs.B * bufs.Hkv * row2
+        tot["flops"] += M * 2 * g * HEAD_DIM * bufs.N + bufs.B * bufs.Hkv * 4 * g * HEAD_DIM * bufs.k
+    return tot
 
 
 def probe_host_link(torch, nbytes=1 << 30):
@@ -119,7 +132,7 @@ def probe_host_link(torch, nbytes=1 << 30):
     return res
 
 
-def cpu_baseline(p, bufs, budget_s, step_kind):
+def cpu_baseline(p, layers, budget_s, step_kind):
     """The CPU oracle, as it is, on a bounded sample of the step's units, scaled to steps/s.
 
     Inputs are the generated ones only: the oracle classifies units with its own
@@ -135,24 +148,33 @@ def cpu_baseline(p, bufs, budget_s, step_kind):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    qf, qpf = oracle.as_f64(p.q(0), p.dtype), oracle.as_f64(p.q_prev(0), p.dtype)
     g = p.g
     tau = p.tau if step_kind == 1 else math.inf
-    query = qf if step_kind == 1 else qpf
-    units = [(b, h) for b in range(p.batch) for h in range(p.hkv)]
-    hit_u = [u for u in units
-             if oracle.reuse_decision(oracle.group_cosine(query[u[0], u[1] * g:(u[1] + 1) * g],
-                                                          qpf[u[0], u[1] * g:(u[1] + 1) * g]), tau)]
-    miss_u = [u for u in units if u not in set(hit_u)]
+    miss_u, hit_u = [], []
+    qs = {}
+    for l in range(p.layers):
+        qf, qpf = oracle.as_f64(p.q(l), p.dtype), oracle.as_f64(p.q_prev(l), p.dtype)
+        query = qf if step_kind == 1 else qpf
+        qs[l] = (query, qpf)
+        for b in range(p.batch):
+            for h in range(p.hkv):
+                c = oracle.group_cosine(query[b, h * g:(h + 1) * g], qpf[b, h * g:(h + 1) * g])
+                (hit_u if oracle.reuse_decision(c, tau) else miss_u).append((l, b, h))
+    # sample evenly over the step
+    rng = np.random.default_rng(0)
+    miss_s = [miss_u[i] for i in rng.permutation(len(miss_u))]
+    hit_s = [hit_u[i] for i in rng.permutation(len(hit_u))]
 
-    def kv_stored(b, h):
+    def kv_stored(l, b, h):
+        bufs = layers[l]
         if bufs.is_persistent(h):
-            return p.kv("k", 0, b, h), p.kv("v", 0, b, h)
+            return p.kv("k", l, b, h), p.kv("v", l, b, h)
         return bufs.host_view("k", b, h), bufs.host_view("v", b, h)
 
     def run(u, reused):
-        b, h = u
-        K, V = kv_stored(b, h)
+        l, b, h = u
+        K, V = kv_stored(l, b, h)
+        query, qpf = qs[l]
         qg, qpg = query[b, h * g:(h + 1) * g], qpf[b, h * g:(h + 1) * g]
         prev = None
         if reused:  # the previous step's selection, made by the oracle itself (untimed)
@@ -164,20 +186,62 @@ def cpu_baseline(p, bufs, budget_s, step_kind):
     t_miss, t_hit = [], []
     spent = 0.0
     i = 0
-    while spent < budget_s and (i < len(miss_u) or i < len(hit_u)):
-        if i < len(miss_u):
-            t_miss.append(run(miss_u[i], False))
+    while spent < budget_s and (i < len(miss_s) or i < len(hit_s)):
+        if i < len(miss_s):
+            t_miss.append(run(miss_s[i], False))
             spent += t_miss[-1]
-        if i < len(hit_u):
-            t_hit.append(run(hit_u[i], True))
+        if i < len(hit_s):
+            t_hit.append(run(hit_s[i], True))
             spent += t_hit[-1]
         i += 1
     est = (np.mean(t_miss) if t_miss else 0.0) * len(miss_u) + (np.mean(t_hit) if t_hit else 0.0) * len(hit_u)
     return {"value": round(1.0 / est, 6) if est > 0 else None, "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(t_miss)} miss + {len(t_hit)} reuse units of the {len(units)}-unit step "
+            "sample": f"{len(t_miss)} miss + {len(t_hit)} reuse units of the {len(miss_u) + len(hit_u)}-unit step "
                       f"({spent:.1f} s of oracle time), fp64 numpy oracle, per-unit mean times scaled to the "
                       f"step's {len(miss_u)} miss / {len(hit_u)} reuse units",
             "seconds_per_step_est": round(est, 3)}
+
+
+WORKLOADS = {
+    1: "one layer, B=1, 32Q/8KV, d=128, N=4096, fp32, top-k 410, all heads persistent",
+    2: "Llama3-8B layer, B=16, 32Q/8KV, d=128, N=32768, bf16, top-k 3277, 2/8 heads persistent",
+    3: "Llama3-8B layer, B=64, 32Q/8KV, d=128, N=131072, bf16, top-k 13108, all heads host-resident",
+    4: "Qwen2.5-14B, 48 layers, B=8, 40Q/8KV, d=128, N=262144, bf16, top-k 26215, ~47% of (layer, KV head) "
+       "slots persistent",
+    5: "Qwen2.5-14B, 48 layers, B=1, 40Q/8KV, d=128, N=524288, bf16, top-k 52429, ~47% of (layer, KV head) "
+       "slots persistent",
+}
+
+
+def phase_times(torch, clo, layers, step_kind, passes):
+    """Per-phase GPU times (ms per step): the step's kernels through the separate
+    entry points, in order on one stream, with events between them."""
+    import numpy as np
+
+    names = ["reuse_test", "score_topk", "gather", "attention"]
+    acc = {n: [] for n in names}
+    torch.cuda.synchronize()
+    for _ in range(passes):
+        evs = []
+        for bufs in layers:
+            tau = bufs.tau if step_kind == 1 else math.inf
+            query = bufs.q if step_kind == 1 else bufs.q_prev
+            shape, layer = bufs.shape_with(tau), bufs.layer()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            ev[0].record()
+            clo.clo_reuse_test(shape, query, bufs.q_prev, bufs.reuse, bufs.cos)
+            ev[1].record()
+            clo.clo_topk_select(shape, layer, query, bufs.reuse, bufs.ws)
+            ev[2].record()
+            clo.clo_gather_kv(shape, layer, bufs.reuse)
+            ev[3].record()
+            clo.clo_sparse_attn(shape, layer, query, bufs.out, bufs.ws)
+            ev[4].record()
+            evs.append(ev)
+        torch.cuda.synchronize()
+        for j, n in enumerate(names):
+            acc[n].append(sum(ev[j].elapsed_time(ev[j + 1]) for ev in evs))
+    return {n: float(np.mean(v)) for n, v in acc.items()}
 
 
 def main():
@@ -186,7 +250,6 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
               f"multi-GPU exchange: units shard by sequence or KV head, one process per GPU).", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
     import gen
@@ -194,11 +257,18 @@ def main():
 
     torch.cuda.set_device(0)
     clo.load()
-    p = gen.config(args.config)
-    log(f"config {args.config}: B={p.batch} Hq={p.hq} Hkv={p.hkv} N={p.context} k={p.topk} {p.dtype} "
-        f"persistent={p.persistent_mask_bits(0):#x}")
+    overrides = {}
+    if args.config in (4, 5):
+        overrides["data_layers"] = args.data_layers or (8 if args.config == 4 else 16)
+    p = gen.config(args.config, **overrides)
+    multi = p.layers > 1
+    log(f"config {args.config}: L={p.layers} B={p.batch} Hq={p.hq} Hkv={p.hkv} N={p.context} k={p.topk} "
+        f"{p.dtype} data layers={p.data_layers or p.layers}")
     t0 = time.time()
-    bufs = workload.load_layer(p, 0, log=log if p.batch >= 16 else None)
+    if multi:
+        layers = workload.load_layers(p, log=log)
+    else:
+        layers = [workload.load_layer(p, 0, log=log if p.batch >= 16 else None)]
     log(f"inputs generated and resident ({time.time() - t0:.1f} s)")
 
     probe = None
@@ -216,16 +286,19 @@ def main():
         del src, dst
         log("calibration copy done: 1 GiB read + 1 GiB written")
 
-    bufs.step0()
+    if multi:
+        loop = workload.LayerLoop(layers)
+        loop.step(cold=True)
+        step = (lambda: loop.step()) if args.step == 1 else (lambda: loop.step(cold=True))
+    else:
+        layers[0].step0()
+        step = layers[0].step1 if args.step == 1 else layers[0].step0
     torch.cuda.synchronize()
-    step = bufs.step1 if args.step == 1 else bufs.step0
-    tau = p.tau if args.step == 1 else math.inf
-    query = bufs.q if args.step == 1 else bufs.q_prev
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K fused decode steps
+    # timed region: K whole decode steps (all layers)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -235,29 +308,12 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    if multi:
+        loop.check()
     ms_per_step = e0.elapsed_time(e1) / args.steps
-    reuse = bufs.reuse.cpu().numpy()
-    alg = algorithmic_bytes(bufs, reuse, args.step)
+    alg = algorithmic_bytes(layers)
 
-    # per-phase times: the same kernels through the separate entry points, events between them
-    shape, layer = bufs.shape_with(tau), bufs.layer()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        ev[i][0].record()
-        clo.clo_reuse_test(shape, query, bufs.q_prev, bufs.reuse, bufs.cos)
-        ev[i][1].record()
-        clo.clo_topk_select(shape, layer, query, bufs.reuse, bufs.ws)
-        ev[i][2].record()
-        clo.clo_gather_kv(shape, layer, bufs.reuse)
-        ev[i][3].record()
-        clo.clo_sparse_attn(shape, layer, query, bufs.out, bufs.ws)
-        ev[i][4].record()
-    torch.cuda.synchronize()
-    names = ["reuse_test", "score_topk", "gather", "attention"]
-    phases = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
-              for j, n in enumerate(names)}
-
+    phases = phase_times(torch, clo, layers, args.step, passes=args.steps if not multi else 2)
     gather_s = phases["gather"] / 1e3
     host_gbs = alg["host_bytes"] / gather_s / 1e9 if alg["host_bytes"] else 0.0
     score_s = phases["score_topk"] / 1e3
@@ -267,14 +323,15 @@ def main():
     if alg["host_bytes"]:
         roofline = {"bound": "host-link", "kernel": "gather_kernel", "achieved": round(host_gbs, 2),
                     "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s", "frac": round(host_gbs / HOST_LINK_PEAK_GBS, 4),
-                    "traffic": None, "bytes_per_launch": alg["host_bytes"],
-                    "launch_ms": round(phases["gather"], 4)}
+                    "traffic": None, "bytes_per_launch": alg["host_bytes"] // len(layers),
+                    "launch_ms": round(phases["gather"] / len(layers), 4)}
         if probe:
             roofline["peak_measured"] = round(probe["h_meas_gbs"], 2)
             roofline["frac_measured"] = round(host_gbs / probe["h_meas_gbs"], 4)
     else:
-        roofline = {"bound": "hbm", "kernel": "score+topk", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+        roofline = {"bound": "hbm", "kernel": "attn_partial_kernel", "achieved": round(attn_gbs, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": None}
 
     result = {
         "metric": METRIC,
@@ -289,17 +346,15 @@ def main():
         "vs_baseline": None,
         "dtype": p.dtype,
         "data": "synthetic (seeded N(0,1) keys/values and queries; no model weights)",
-        "config": {"workload": f"config {args.config}: " + {
-            1: "one layer, B=1, 32Q/8KV, d=128, N=4096, fp32, top-k 410, all heads persistent",
-            2: "Llama3-8B layer, B=16, 32Q/8KV, d=128, N=32768, bf16, top-k 3277, 2/8 heads persistent",
-            3: "Llama3-8B layer, B=64, 32Q/8KV, d=128, N=131072, bf16, top-k 13108, all heads host-resident",
-        }[args.config] + (", steady step (80/20 reuse)" if args.step == 1 else ", cold step (all miss)"),
-            "batch": p.batch, "q_heads": p.hq, "kv_heads": p.hkv, "head_dim": HEAD_DIM, "context": p.context,
-            "topk": p.topk, "tau": p.tau, "step": args.step},
+        "config": {"workload": f"config {args.config}: " + WORKLOADS[args.config] +
+                   (", steady step (80/20 reuse)" if args.step == 1 else ", cold step (all miss)"),
+                   "layers": p.layers, "batch": p.batch, "q_heads": p.hq, "kv_heads": p.hkv, "head_dim": HEAD_DIM,
+                   "context": p.context, "topk": p.topk, "tau": p.tau, "step": args.step,
+                   "data_layers": p.data_layers or p.layers},
         "roofline": roofline,
         "roofline_score": {"bound": "hbm", "kernel": "compact+score+topk", "achieved": round(score_gbs, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
-                           "bytes_per_launch": alg["score_bytes"]},
+                           "bytes_per_step": alg["score_bytes"]},
         "attention_hbm_gbs": round(attn_gbs, 1),
         "step_hbm_gbs": round(alg["hbm_bytes"] / step_s / 1e9, 1),
         "step_host_gbs": round(alg["host_bytes"] / step_s / 1e9, 2),
@@ -308,9 +363,11 @@ def main():
         "host_link_probe": {k: round(v, 2) for k, v in probe.items()} if probe else None,
         "wall_s": round(wall, 3),
     }
+    if multi:
+        result["layer_steps_per_s"] = round(p.layers / step_s, 2)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of units")
-        result["cpu_baseline"] = cpu_baseline(p, bufs, args.cpu_sample_seconds, args.step)
+        result["cpu_baseline"] = cpu_baseline(p, layers, args.cpu_sample_seconds, args.step)
     print(json.dumps(result), flush=True)
 
 

@@ -369,6 +369,7 @@ def config(cfg: int, **overrides) -> Problem:
         p["topk"] = topk_count(p["context"])
     if "persistent" not in p:
         L, H = p["layers"], p["hkv"]
+        period = p.get("data_layers") or L  # aliased layers share data, so they share the mask
         if cfg == 1:
             p["persistent"] = np.ones((L, H), dtype=bool)
         elif cfg == 2:
@@ -377,5 +378,6 @@ def config(cfg: int, **overrides) -> Problem:
             p["persistent"] = np.zeros((L, H), dtype=bool)
         else:
             # ~47.6% of (layer, KV head) slots keep their full KV in HBM
-            p["persistent"] = _persistent_slots(seed, L, H, int(round(0.476 * L * H)))
+            base = _persistent_slots(seed, period, H, int(round(0.476 * period * H)))
+            p["persistent"] = np.stack([base[l % period] for l in range(L)])
     return Problem(**p)

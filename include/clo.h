@@ -103,8 +103,10 @@ typedef struct {
 /*
  * Device-side ordering between streams (the pages' GPU-centric
  * synchronization: abstract, feature (3); synthesis section 2.1 item 3, "UVA
- * polling" instead of coarse CPU-centric synchronization).  All pointers are
- * device memory and may be NULL (then that half is skipped).
+ * polling" instead of coarse CPU-centric synchronization).  Every entry point
+ * takes one (NULL = none).  All pointers are device memory and may be NULL
+ * (then that half is skipped).  A producer's signal must be enqueued (in host
+ * order) before the consumer's wait, as with events.
  *   wait_flag/wait_value      before its first kernel, the call waits on the
  *                             GPU until *wait_flag >= wait_value (acquire,
  *                             agent scope), polling at most spin_limit times
@@ -130,10 +132,10 @@ size_t clo_workspace_size(const clo_shape* shape);
  * A1 -- reuse test (synthesis 2.1 item 2; abstract feature (1)).
  * For each unit: c = <q_g, q_prev_g> / (|q_g| |q_prev_g|) over the unit's g
  * query heads read as one g*d vector (c = 0 when a norm is 0), in fp32;
- * reuse[u] = (c >= tau).  cos may be NULL.
+ * reuse[u] = (c >= tau).  cos and sync may be NULL.
  */
 clo_status clo_reuse_test(const clo_shape* shape, const void* q, const void* q_prev,
-                          uint8_t* reuse, float* cos, void* stream);
+                          uint8_t* reuse, float* cos, const clo_sync* sync, void* stream);
 
 /*
  * A2 + A3 -- scoring and exact top-k (synthesis 2.2 and 2.3 table).
@@ -142,9 +144,11 @@ clo_status clo_reuse_test(const clo_shape* shape, const void* q, const void* q_p
  * persistent heads, k_score otherwise), then idx[u] = the k tokens with the
  * largest s_j (ties to the smaller index), ascending.  idx of hit units is
  * left untouched.  ws: device workspace of at least clo_workspace_size() bytes.
+ * sync may be NULL.
  */
 clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const void* q,
-                           const uint8_t* reuse, void* ws, size_t ws_bytes, void* stream);
+                           const uint8_t* reuse, void* ws, size_t ws_bytes, const clo_sync* sync,
+                           void* stream);
 
 /*
  * A4 -- gather (abstract features (2) and (3); synthesis 2.1 item 3).

@@ -1,0 +1,137 @@
+"""Multi-layer decode step (layer-ahead selection and gather on their own streams,
+ordered by device flags) and the device-side wait/signal protocol."""
+import math
+
+import numpy as np
+import pytest
+
+import gen
+from tests.gpu_common import compare, log, oracle_steps, snapshot
+from tests.margins import enforce_margins
+
+pytestmark = pytest.mark.gpu
+
+
+def multi_layer_problem():
+    return gen.Problem(name="layers", layers=6, data_layers=3, batch=2, hq=10, hkv=2, d=128, context=3000,
+                       topk=300, dtype="bf16", tau=0.8, seed=0x5EED0200, qprev_model="target_cos", low_frac=0.5,
+                       heavy_frac=0.005,
+                       persistent=np.array([[1, 0], [0, 0], [0, 1], [1, 0], [0, 0], [0, 1]], dtype=bool))
+
+
+def enforce_all_layers(p):
+    # aliased layers score the same keys with different queries: repeat until no layer resamples
+    for _ in range(10):
+        snap = {k: dict(v) for k, v in p.k_resample.items()}
+        for l in range(p.layers):
+            enforce_margins(p, l)
+        if {k: dict(v) for k, v in p.k_resample.items()} == snap:
+            return p
+    raise RuntimeError("margins did not settle")
+
+
+def test_layer_loop_matches_sequential_and_oracle(need_gpu):
+    import torch
+
+    from top_sparse_attention_02_amd import workload
+
+    p = enforce_all_layers(multi_layer_problem())
+    layers = workload.load_layers(p)
+    loop = workload.LayerLoop(layers)
+    log("[case layer loop] cold step")
+    loop.step(cold=True)
+    torch.cuda.synchronize()
+    loop.check()
+    a0 = [snapshot(b) for b in layers]
+    log("[case layer loop] steady step")
+    loop.step()
+    torch.cuda.synchronize()
+    loop.check()
+    a1 = [snapshot(b) for b in layers]
+    # the same steps, layer by layer on one stream with the fused entry point
+    for b in layers:
+        b.step0()
+    b0 = [snapshot(b) for b in layers]
+    for b in layers:
+        b.step1()
+    b1 = [snapshot(b) for b in layers]
+    for l in range(p.layers):
+        for key in a0[l]:
+            assert np.array_equal(a0[l][key], b0[l][key]), (l, key)
+            assert np.array_equal(a1[l][key], b1[l][key]), (l, key)
+    # and the oracle, layer by layer
+    for l in range(p.layers):
+        r0, r1, kv = oracle_steps(p, l)
+        compare(p, layers[l], a0[l], r0, kv, f"layer {l} step0")
+        compare(p, layers[l], a1[l], r1, kv, f"layer {l} step1")
+
+
+def test_consumer_sees_rows_written_before_the_flag(need_gpu):
+    """Delay the producer (gather) on its stream; the consumer (attention) must still
+    read the freshly gathered rows because it waits for the producer's flag."""
+    import torch
+
+    from top_sparse_attention_02_amd import clo, workload
+    from tests.gpu_common import small_problem
+
+    p = small_problem("delay", batch=2, hq=8, hkv=2, context=4000, topk=400, dtype="bf16", persistent=[0, 0],
+                      qprev_model="independent")
+    enforce_margins(p, 0)
+    bufs = workload.load_layer(p, 0)
+    bufs.step0()
+    torch.cuda.synchronize()
+    ref = snapshot(bufs)
+    # wipe the cache and output, then redo gather + attention on two streams
+    bufs.k_cache.zero_()
+    bufs.v_cache.zero_()
+    bufs.out.zero_()
+    flag = torch.zeros(2, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    shape, layer = bufs.shape_with(math.inf), bufs.layer()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(sp):
+        torch.cuda._sleep(50_000_000)  # tens of milliseconds before the producer starts
+    clo.clo_gather_kv(shape, layer, None, sync=clo.Sync(signal_flag=flag[0], signal_value=7), stream=sp)
+    clo.clo_sparse_attn(shape, layer, bufs.q_prev, bufs.out, bufs.ws,
+                        sync=clo.Sync(wait_flag=flag[0], wait_value=7, error_word=err), stream=sc)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = snapshot(bufs)
+    assert np.array_equal(got["k_cache"], ref["k_cache"])
+    assert np.array_equal(got["out"], ref["out"])
+
+
+def test_never_signalled_flag_times_out_without_hanging(need_gpu):
+    import torch
+
+    from top_sparse_attention_02_amd import clo, workload
+    from tests.gpu_common import small_problem
+
+    p = small_problem("timeout", batch=1, hq=4, hkv=1, context=500, topk=50, dtype="f32", persistent=[0])
+    bufs = workload.load_layer(p, 0)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    clo.clo_gather_kv(bufs.shape_with(math.inf), bufs.layer(), None,
+                      sync=clo.Sync(wait_flag=flag[0], wait_value=1, error_word=err, spin_limit=2000))
+    torch.cuda.synchronize()
+    assert int(err.item()) == clo.CLO_E_TIMEOUT
+
+
+def test_already_signalled_flag_does_not_wait(need_gpu):
+    import time
+
+    import torch
+
+    from top_sparse_attention_02_amd import clo
+
+    flag = torch.full((1,), 5, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    shape = clo.Shape(0, 4, 1, 10, 1, 0.8, clo.CLO_F32)  # empty batch: only the wait and the signal run
+    t = time.perf_counter()
+    clo.clo_gather_kv(shape, clo.Layer(), None,
+                      sync=clo.Sync(wait_flag=flag[0], wait_value=5, signal_flag=flag[0], signal_value=9,
+                                    error_word=err))
+    torch.cuda.synchronize()
+    assert time.perf_counter() - t < 0.5
+    assert int(err.item()) == 0 and int(flag.item()) == 9

@@ -60,9 +60,9 @@ def load():
         L.clo_workspace_size.restype = sz
         L.clo_workspace_size.argtypes = [P(clo_shape)]
         L.clo_reuse_test.restype = st
-        L.clo_reuse_test.argtypes = [P(clo_shape), vp, vp, vp, vp, vp]
+        L.clo_reuse_test.argtypes = [P(clo_shape), vp, vp, vp, vp, P(clo_sync), vp]
         L.clo_topk_select.restype = st
-        L.clo_topk_select.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, sz, vp]
+        L.clo_topk_select.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, sz, P(clo_sync), vp]
         L.clo_gather_kv.restype = st
         L.clo_gather_kv.argtypes = [P(clo_shape), P(clo_layer), vp, P(clo_sync), vp]
         L.clo_sparse_attn.restype = st
@@ -182,14 +182,15 @@ def clo_workspace_size(shape: Shape) -> int:
     return int(load().clo_workspace_size(ctypes.byref(shape.c())))
 
 
-def clo_reuse_test(shape: Shape, q, q_prev, reuse, cos=None, stream=None):
-    _check(load().clo_reuse_test(ctypes.byref(shape.c()), ptr(q), ptr(q_prev), ptr(reuse), ptr(cos),
+def clo_reuse_test(shape: Shape, q, q_prev, reuse, cos=None, sync: Optional[Sync] = None, stream=None):
+    _check(load().clo_reuse_test(ctypes.byref(shape.c()), ptr(q), ptr(q_prev), ptr(reuse), ptr(cos), _sync(sync),
                                  stream_handle(stream)), "clo_reuse_test")
 
 
-def clo_topk_select(shape: Shape, layer: Layer, q, reuse, ws, stream=None, ws_bytes: Optional[int] = None):
+def clo_topk_select(shape: Shape, layer: Layer, q, reuse, ws, sync: Optional[Sync] = None, stream=None,
+                    ws_bytes: Optional[int] = None):
     _check(load().clo_topk_select(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(q), ptr(reuse), ptr(ws),
-                                  nbytes(ws, ws_bytes), stream_handle(stream)), "clo_topk_select")
+                                  nbytes(ws, ws_bytes), _sync(sync), stream_handle(stream)), "clo_topk_select")
 
 
 def clo_gather_kv(shape: Shape, layer: Layer, reuse, sync: Optional[Sync] = None, stream=None):

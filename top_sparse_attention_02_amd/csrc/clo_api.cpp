@@ -339,34 +339,47 @@ size_t clo_workspace_size(const clo_shape* shape) {
 }
 
 clo_status clo_reuse_test(const clo_shape* shape, const void* q, const void* q_prev, uint8_t* reuse, float* cos,
-                          void* stream) {
+                          const clo_sync* sync, void* stream) {
   Plan p;
   clo_status st;
   if ((st = make_plan(shape, 0, &p))) return st;
-  if (p.U == 0) return ok();
+  if ((st = check_sync_flags(sync))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.U == 0) {
+    if ((st = pre_wait(sync, s))) return st;
+    return post_signal(sync, s);
+  }
   if ((st = check_device(q, q_bytes(p), "q"))) return st;
   if ((st = check_device(q_prev, q_bytes(p), "q_prev"))) return st;
   if ((st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
   if (cos && (st = check_device(cos, (size_t)p.U * 4, "cos"))) return st;
-  return hip_status(launch_reuse(p.a, q, q_prev, reuse, cos, static_cast<hipStream_t>(stream)), "reuse launch");
+  if ((st = pre_wait(sync, s))) return st;
+  if ((st = hip_status(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch"))) return st;
+  return post_signal(sync, s);
 }
 
 clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const void* q, const uint8_t* reuse,
-                           void* ws, size_t ws_bytes, void* stream) {
+                           void* ws, size_t ws_bytes, const clo_sync* sync, void* stream) {
   Plan p;
   clo_status st;
   if ((st = make_plan(shape, layer ? layer->persistent_mask : 0, &p))) return st;
-  if (p.U == 0) return ok();
+  if ((st = check_sync_flags(sync))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.U == 0) {
+    if ((st = pre_wait(sync, s))) return st;
+    return post_signal(sync, s);
+  }
   Workspace w;
   if ((st = check_layer(layer, &p, NEED_SCORE | NEED_HBM_K))) return st;
   if ((st = check_device(q, q_bytes(p), "q"))) return st;
   if (reuse && (st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const int cu = num_cus();
+  if ((st = pre_wait(sync, s))) return st;
   if ((st = hip_status(launch_compact(p.a, reuse, w, 1, s), "compact launch"))) return st;
   if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w.keys, cu, s), "score launch"))) return st;
-  return hip_status(launch_topk(p.a, span_all_misses(w), p.U, w.keys, cu, s), "top-k launch");
+  if ((st = hip_status(launch_topk(p.a, span_all_misses(w), p.U, w.keys, cu, s), "top-k launch"))) return st;
+  return post_signal(sync, s);
 }
 
 clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const uint8_t* reuse, const clo_sync* sync,

@@ -37,7 +37,7 @@ class LayerBuffers:
 
     def __init__(self, batch: int, hq: int, hkv: int, context: int, topk: int, dtype: str, persistent_mask: int,
                  tau: float, device: str = "cuda", host_flags: int = hipHostMallocMapped,
-                 host_kv: Optional[tuple] = None, score_kv: Optional[torch.Tensor] = None):
+                 share: Optional["LayerBuffers"] = None):
         self.B, self.Hq, self.Hkv, self.N, self.k = batch, hq, hkv, context, topk
         self.dtype, self.tau, self.mask = dtype, tau, persistent_mask
         self.P = bin(persistent_mask).count("1")
@@ -51,20 +51,26 @@ class LayerBuffers:
         self.reuse = torch.zeros(batch, hkv, dtype=torch.uint8, device=dev)
         self.cos = torch.zeros(batch, hkv, dtype=torch.float32, device=dev)
         self.idx = torch.zeros(batch, hkv, topk, dtype=torch.int32, device=dev)
-        self.k_hbm = self.v_hbm = None
-        if self.P:
-            self.k_hbm = torch.empty(batch, self.P, context, d, dtype=tdt, device=dev)
-            self.v_hbm = torch.empty_like(self.k_hbm)
-        self.k_host = self.v_host = self.k_score = self.k_cache = self.v_cache = None
-        if self.H:
-            nb = batch * self.H * context * d * elem_bytes(dtype)
-            if host_kv is not None:
-                self.k_host, self.v_host = host_kv
-            else:
+        # inputs (full K/V): shared with `share` when layers alias the same data
+        self.shared = share is not None
+        if share is not None:
+            assert share.mask == persistent_mask and share.N == context and share.B == batch
+            self.k_hbm, self.v_hbm = share.k_hbm, share.v_hbm
+            self.k_host, self.v_host, self.k_score = share.k_host, share.v_host, share.k_score
+        else:
+            self.k_hbm = self.v_hbm = None
+            if self.P:
+                self.k_hbm = torch.empty(batch, self.P, context, d, dtype=tdt, device=dev)
+                self.v_hbm = torch.empty_like(self.k_hbm)
+            self.k_host = self.v_host = self.k_score = None
+            if self.H:
+                nb = batch * self.H * context * d * elem_bytes(dtype)
                 self.k_host = HostBuffer(nb, host_flags)
                 self.v_host = HostBuffer(nb, host_flags)
-            self.k_score = score_kv if score_kv is not None else torch.empty(batch, self.H, context, d, dtype=tdt,
-                                                                             device=dev)
+                self.k_score = torch.empty(batch, self.H, context, d, dtype=tdt, device=dev)
+        # outputs and per-layer state
+        self.k_cache = self.v_cache = None
+        if self.H:
             self.k_cache = torch.zeros(batch, self.H, topk, d, dtype=tdt, device=dev)
             self.v_cache = torch.zeros_like(self.k_cache)
         self.shape = clo.Shape(batch, hq, hkv, context, topk, tau, clo_dtype(dtype))
@@ -119,15 +125,20 @@ def stored_tensor(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
 
 
 def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads: Optional[int] = None,
-               log=None) -> LayerBuffers:
-    """Allocate (unless given) and fill the buffers of one layer of `problem`."""
+               log=None, share: Optional[LayerBuffers] = None) -> LayerBuffers:
+    """Allocate (unless given) and fill the buffers of one layer of `problem`.
+
+    With `share`, the layer reuses that layer's K/V buffers (aliased data) and
+    only its queries are loaded."""
     p = problem
     mask = p.persistent_mask_bits(layer)
     if bufs is None:
-        bufs = LayerBuffers(p.batch, p.hq, p.hkv, p.context, p.topk, p.dtype, mask, p.tau)
+        bufs = LayerBuffers(p.batch, p.hq, p.hkv, p.context, p.topk, p.dtype, mask, p.tau, share=share)
     assert bufs.mask == mask
     bufs.q.copy_(stored_tensor(p.q(layer), p.dtype))
     bufs.q_prev.copy_(stored_tensor(p.q_prev(layer), p.dtype))
+    if bufs.shared:
+        return bufs
     eb = elem_bytes(p.dtype)
     unit_bytes = p.context * HEAD_DIM * eb
     staging = None
@@ -152,3 +163,82 @@ def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads
         staging.close()
     torch.cuda.synchronize()
     return bufs
+
+
+def load_layers(problem, log=None, threads: Optional[int] = None):
+    """Buffers of every layer; layers with the same data layer share their K/V."""
+    first = {}
+    layers = []
+    for l in range(problem.layers):
+        dl = problem.data_layer(l)
+        bufs = load_layer(problem, l, threads=threads, share=first.get(dl))
+        first.setdefault(dl, bufs)
+        layers.append(bufs)
+        if log:
+            log(f"  layer {l + 1}/{problem.layers} ready (data layer {dl})")
+    torch.cuda.synchronize()
+    return layers
+
+
+class LayerLoop:
+    """A multi-layer decode step on three streams ordered only by device flags.
+
+    select: reuse test, scoring and top-k of layer l, then flag sel[l] = epoch;
+    gather: waits for sel[l], reads layer l's selected rows from host memory,
+            then flag gat[l] = epoch;
+    attend: waits for gat[l], attention of layer l, then flag att[l] = epoch.
+    The select stream of the next step waits for att[l] of this step before
+    overwriting layer l's selections.  Selection and gathering of layer l+1
+    therefore run while layer l is attended (one-layer-ahead prefetch and
+    beyond); the host never waits inside a step.
+    """
+
+    def __init__(self, layers, spin_limit: int = 0):
+        self.layers = layers
+        L = len(layers)
+        dev = layers[0].q.device
+        self.flags = torch.zeros(3, L, dtype=torch.int32, device=dev)
+        self.error = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.s_select = torch.cuda.Stream(device=dev)
+        self.s_gather = torch.cuda.Stream(device=dev)
+        self.s_attend = torch.cuda.Stream(device=dev)
+        self.epoch = 0
+        self.spin_limit = spin_limit
+
+    def _flag(self, kind: int, l: int):
+        return self.flags[kind, l]
+
+    def step(self, cold: bool = False):
+        """Enqueue one decode step over all layers (cold: every unit misses)."""
+        # the loop's streams start after work already queued on the current stream
+        cur = torch.cuda.current_stream()
+        for st in (self.s_select, self.s_gather, self.s_attend):
+            st.wait_stream(cur)
+        self.epoch += 1
+        e = self.epoch
+        sp = self.spin_limit
+        for l, b in enumerate(self.layers):
+            tau = math.inf if cold else b.tau
+            q = b.q_prev if cold else b.q
+            shape, layer = b.shape_with(tau), b.layer()
+            after_prev = clo.Sync(wait_flag=self._flag(2, l), wait_value=e - 1, error_word=self.error,
+                                  spin_limit=sp) if e > 1 else None
+            clo.clo_reuse_test(shape, q, b.q_prev, b.reuse, b.cos, sync=after_prev, stream=self.s_select)
+            clo.clo_topk_select(shape, layer, q, b.reuse, b.ws,
+                                sync=clo.Sync(signal_flag=self._flag(0, l), signal_value=e), stream=self.s_select)
+            clo.clo_gather_kv(shape, layer, b.reuse,
+                              sync=clo.Sync(wait_flag=self._flag(0, l), wait_value=e, signal_flag=self._flag(1, l),
+                                            signal_value=e, error_word=self.error, spin_limit=sp),
+                              stream=self.s_gather)
+            clo.clo_sparse_attn(shape, layer, q, b.out, b.ws,
+                                sync=clo.Sync(wait_flag=self._flag(1, l), wait_value=e, signal_flag=self._flag(2, l),
+                                              signal_value=e, error_word=self.error, spin_limit=sp),
+                                stream=self.s_attend)
+        # the caller's stream continues after the last attention
+        cur.wait_stream(self.s_attend)
+
+    def check(self):
+        """Raise if any device-side wait timed out (call after a synchronize)."""
+        v = int(self.error.item())
+        if v:
+            raise RuntimeError(f"device-side wait failed with status {v} ({clo.clo_status_string(v)})")
