@@ -265,12 +265,17 @@ class Problem:
         return np.sort(smallest_by_key(derive_key(self.seed, TAG_HEAVY, dl, b), self.context, m))
 
     def _row_scale(self, layer: int, b: int) -> Optional[np.ndarray]:
-        rows = self.heavy_rows(layer, b)
-        if rows.size == 0:
-            return None
-        s = np.ones(self.context, dtype=np.float32)
-        s[rows] = self.heavy_scale
-        return s
+        key = (self.data_layer(layer), b)
+        cache = self.__dict__.setdefault("_scale_cache", {})
+        if key not in cache:
+            rows = self.heavy_rows(layer, b)
+            if rows.size == 0:
+                cache[key] = None
+            else:
+                s = np.ones(self.context, dtype=np.float32)
+                s[rows] = self.heavy_scale
+                cache[key] = s
+        return cache[key]
 
     def fill(self, which: str, layer: int, b: int, kvh: int, out_ptr: int, threads: Optional[int] = None):
         """Write the [N, d] K or V block of one unit to raw memory at out_ptr."""
@@ -300,6 +305,21 @@ class Problem:
         out = np.empty((self.context, self.d), dtype=storage_dtype(self.dtype))
         self.fill(which, layer, b, kvh, out.ctypes.data)
         return out
+
+    def k_row_draw(self, layer: int, b: int, kvh: int, row: int, rnd: int) -> np.ndarray:
+        """Stored values of key row `row` of a unit as drawn in resample round `rnd`."""
+        dl = self.data_layer(layer)
+        vals = normal_stream(derive_key(self.seed, TAG_K, dl, b, kvh, rnd), self.d, first=row * self.d)
+        scale = self._row_scale(layer, b)
+        if scale is not None:
+            vals = vals * float(scale[row])
+        return round_to(vals, self.dtype)
+
+    def k_row_round(self, layer: int, b: int, kvh: int, row: int) -> int:
+        return self.k_resample.get((self.data_layer(layer), b, kvh), {}).get(int(row), 0)
+
+    def set_k_row_round(self, layer: int, b: int, kvh: int, row: int, rnd: int) -> None:
+        self.k_resample.setdefault((self.data_layer(layer), b, kvh), {})[int(row)] = int(rnd)
 
     def resample_k_rows(self, layer: int, b: int, kvh: int, rows) -> None:
         """Give the listed key rows of a unit a fresh draw (next resample round)."""

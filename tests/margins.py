@@ -26,23 +26,67 @@ def gamma(d: int) -> float:
     return d * u / (1 - d * u)
 
 
+def score_delta(qgs, K: np.ndarray) -> float:
+    """delta_u for the queries that score a unit."""
+    m = 0.0
+    for qg in qgs:
+        m = max(m, float((np.abs(K) @ np.abs(qg).T).max()))
+    return max(1e-2, 4 * gamma(qgs[0].shape[1]) * m)
+
+
+def boundaries(qgs, K: np.ndarray, ranks):
+    """For each query: its scores and the midpoints between the r-th and (r+1)-th largest score."""
+    out = []
+    for qg in qgs:
+        s = oracle.token_scores(qg, K)
+        order = np.argsort(-s, kind="stable")
+        ts = [0.5 * (s[order[r - 1]] + s[order[r]]) for r in ranks if 1 <= r < s.shape[0]]
+        out.append((s, ts))
+    return out
+
+
 def near_boundary_rows(qg: np.ndarray, K: np.ndarray, ranks) -> set:
-    s = oracle.token_scores(qg, K)
-    n = s.shape[0]
-    absdot = np.abs(K) @ np.abs(qg).T  # [N, g]
-    delta = max(1e-2, 4 * gamma(qg.shape[1]) * float(absdot.max()))
-    order = np.argsort(-s, kind="stable")
+    """Rows whose score lies within delta_u of a rank boundary (for one query)."""
+    delta = score_delta([qg], K)
+    (s, ts), = boundaries([qg], K, ranks)
     bad = set()
-    for r in ranks:
-        if r < 1 or r >= n:
-            continue
-        t = 0.5 * (s[order[r - 1]] + s[order[r]])
+    for t in ts:
         bad |= set(np.nonzero(np.abs(s - t) < delta)[0].tolist())
     return bad
 
 
+def _redraw_keeping_sides(p, layer, b, h, K, qgs, row, bounds, delta, max_tries=4000):
+    """Draw new rounds of one key row until, for every query and boundary, its score
+    is on the same side as before and at least delta away."""
+    sides = [[s[row] > t for t in ts] for s, ts in bounds]
+    rnd = p.k_row_round(layer, b, h, row)
+    for _ in range(max_tries):
+        rnd += 1
+        cand = oracle.as_f64(p.k_row_draw(layer, b, h, row, rnd), p.dtype)
+        ok = True
+        for qg, (s, ts), sd in zip(qgs, bounds, sides):
+            sc = float(np.max(qg @ cand))
+            for t, above in zip(ts, sd):
+                if (sc > t + delta) if above else (sc < t - delta):
+                    continue
+                ok = False
+                break
+            if not ok:
+                break
+        if ok:
+            p.set_k_row_round(layer, b, h, row, rnd)
+            K[row] = cand
+            return
+    raise RuntimeError(f"no redraw of key row {row} keeps its side")
+
+
 def enforce_margins(problem, layer: int, units=None, extra_ranks=(), max_rounds: int = 40, tau=None):
-    """Resample q_prev / key rows of the listed (b, kvh) units until every decision has a margin."""
+    """Redraw q_prev / key rows of the listed (b, kvh) units until every decision has a margin.
+
+    A key within delta_u of a rank boundary is redrawn until it lands on the same
+    side of every boundary, at least delta_u away: the number of keys above each
+    boundary is unchanged, so the boundaries stay where they are and the band
+    around them empties."""
     p = problem
     tau = p.tau if tau is None else tau
     g = p.g
@@ -63,14 +107,24 @@ def enforce_margins(problem, layer: int, units=None, extra_ranks=(), max_rounds:
         raise RuntimeError("cosine margins not reached")
     ranks = [p.topk, *extra_ranks]
     for b, h in units:
+        qgs = [qp[b, h * g:(h + 1) * g], q[b, h * g:(h + 1) * g]]
+        K = oracle.as_f64(p.kv("k", layer, b, h), p.dtype)
         for _ in range(max_rounds):
-            K = oracle.as_f64(p.kv("k", layer, b, h), p.dtype)
+            delta = score_delta(qgs, K)
+            bounds = boundaries(qgs, K, ranks)
             bad = set()
-            for qq in (qp, q):
-                bad |= near_boundary_rows(qq[b, h * g:(h + 1) * g], K, ranks)
+            for s, ts in bounds:
+                for t in ts:
+                    bad |= set(np.nonzero(np.abs(s - t) < delta)[0].tolist())
+                # a key between two boundaries of one query (the k-th key when ranks k-1
+                # and k are both guarded) stays; its neighbours are moved away instead
+                if len(ts) > 1:
+                    lo_t, hi_t = min(ts), max(ts)
+                    bad -= set(np.nonzero((s > lo_t) & (s < hi_t))[0].tolist())
             if not bad:
                 break
-            p.resample_k_rows(layer, b, h, sorted(bad))
+            for row in sorted(bad):
+                _redraw_keeping_sides(p, layer, b, h, K, qgs, row, bounds, delta)
         else:
             raise RuntimeError(f"score margins not reached for unit {(b, h)}")
     return p

@@ -31,6 +31,10 @@ CASES = {
                     qprev_model="independent"),
     # more than one score chunk per unit and a top-k spanning several 4096-key tiles
     "bf16_g4_long": dict(batch=1, hq=8, hkv=2, context=20000, topk=2000, dtype="bf16", persistent=[0, 1]),
+    # long context: the multi-block top-k (17 chunks of 16384 keys, ragged last chunk)
+    "bf16_g5_multiblock": dict(batch=1, hq=10, hkv=2, context=270000, topk=27000, dtype="bf16",
+                               persistent=[0, 1], heavy_frac=0.005),
+    "f32_g4_multiblock": dict(batch=2, hq=8, hkv=2, context=262145, topk=26215, dtype="f32", persistent=[1, 0]),
 }
 
 
@@ -73,12 +77,14 @@ def test_dense_limit_equals_full_attention(need_gpu):
     assert err < 1e-4
 
 
-def test_ties_go_to_the_smaller_index(need_gpu):
-    """Duplicate the k-th key into two low-scoring rows (one before it): exact ties on both sides."""
+@pytest.mark.parametrize("context", [3000, 300000])
+def test_ties_go_to_the_smaller_index(need_gpu, context):
+    """Duplicate the k-th key into two low-scoring rows (one before it): exact ties on both sides
+    (single-block top-k at N = 3000, multi-block across chunks at N = 300000)."""
     from top_sparse_attention_02_amd import workload
 
-    p = small_problem("ties", batch=1, hq=4, hkv=2, context=3000, topk=300, dtype="bf16", persistent=[0, 1],
-                      qprev_model="independent")
+    p = small_problem(f"ties{context}", batch=1, hq=4, hkv=2, context=context, topk=context // 10, dtype="bf16",
+                      persistent=[0, 1], qprev_model="independent")
     enforce_margins(p, 0, extra_ranks=(p.topk - 1,))
     bufs = workload.load_layer(p, 0)
     qp = oracle.as_f64(p.q_prev(0), "bf16")

@@ -56,8 +56,24 @@ constexpr int kMetaOffAll = 16;    // [R + 1] first position of each range in li
 constexpr int kMetaOffHost = 40;   // [R + 1] first position of each range in list_host
 constexpr int kMetaInts = 64;
 
+// Multi-block top-k: each unit's keys are split into chunks of kTopkChunk keys,
+// one 256-thread block per chunk.
+constexpr int kTopkChunk = 16384;
+
+// Per-unit radix-select state in the workspace.
+struct TopkState {
+  uint32_t prefix;  // digits of the k-th largest key found so far
+  uint32_t mask;    // bits of prefix already fixed
+  uint32_t rem;     // how many keys still to take among those matching prefix
+  uint32_t done;    // chunk blocks finished in the current pass
+};
+
 struct Workspace {
   int32_t* meta;       // counts and range offsets (layout above)
+  uint32_t* ghist;     // [U][256] per-unit radix histogram of the current pass
+  TopkState* tstate;   // [U]
+  uint32_t* tcount;    // [U][cmax][2] per-chunk counts of keys > T and == T
+  int32_t cmax;        // chunks per unit (ceil(N / kTopkChunk))
   int32_t* list_all;   // [U] miss units, ascending
   int32_t* list_host;  // [U] miss units of non-persistent heads, ascending
   int32_t* list_hit;   // [U] reuse units, ascending
@@ -82,7 +98,7 @@ hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, u
 hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, int ranges, hipStream_t s);
 hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_units, uint32_t* keys, int num_cu,
                         hipStream_t s);
-hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uint32_t* keys, int num_cu,
+hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uint32_t* keys, const Workspace& w,
                        hipStream_t s);
 // max_blocks bounds the grid: the host link saturates with a few hundred
 // waves in flight, and a smaller grid leaves the CUs to concurrent kernels.

@@ -338,11 +338,126 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(LayerArgs a, const uint
 }
 
 // ---------------------------------------------------------------- A3 top-k
-// One 1024-thread block per miss unit: four 8-bit radix passes (MSB first)
-// find the k-th largest key T and how many keys equal to T are taken; then a
-// block-wide scan writes the winners in ascending index order (keys > T, plus
-// the first `need` keys == T by index).
-__global__ __launch_bounds__(1024) void topk_kernel(LayerArgs a, Span sp, const uint32_t* __restrict__ keys) {
+// Exact radix select over each miss unit's order-preserving score keys, spread
+// over chunk blocks so that a unit with a long context is selected by many CUs:
+//   topk_init_kernel   per unit: zero the global histogram, prefix = 0, rem = k
+//   topk_pass_kernel   x4, 8 bits each, MSB first: every chunk block builds an
+//                      LDS histogram of its keys that match the prefix so far and
+//                      adds it to the unit's global histogram; the last block to
+//                      finish (atomic counter) picks the digit holding the
+//                      rem-th largest key, extends the prefix and clears the
+//                      histogram.  After four passes prefix = T, the k-th largest
+//                      key, and rem = how many keys equal to T are taken.
+//   topk_count_kernel  per chunk: keys > T and keys == T
+//   topk_write_kernel  per chunk: offsets from the counts of earlier chunks, then
+//                      a block scan writes the winners (keys > T, and the first
+//                      rem keys == T by index) in ascending index order.
+constexpr int kTopkThreads = 256;
+// Contexts of at least this many chunks (N >= 262144) take the multi-block
+// path; shorter ones a single block per unit (fewer launches, and the many
+// units of short-context batches already fill the GPU).
+constexpr int kTopkMultiMin = 16;
+constexpr int kTopkUnroll = 4;     // 16-byte key loads in flight per thread
+
+struct UnitChunk {
+  int u, c;
+  bool valid;
+};
+
+__device__ __forceinline__ UnitChunk unit_chunk(const Span& sp, int cmax) {
+  const int lo = *sp.lo;
+  const int64_t n = (int64_t)(*sp.hi - lo) * cmax;
+  UnitChunk r{0, 0, false};
+  if ((int64_t)blockIdx.x >= n) return r;
+  r.u = sp.list[lo + blockIdx.x / cmax];
+  r.c = blockIdx.x % cmax;
+  r.valid = true;
+  return r;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_init_kernel(LayerArgs a, Span sp, uint32_t* __restrict__ ghist,
+                                                                 TopkState* __restrict__ st) {
+  const int lo = *sp.lo;
+  if ((int)blockIdx.x >= *sp.hi - lo) return;
+  const int u = sp.list[lo + blockIdx.x];
+  ghist[(int64_t)u * 256 + threadIdx.x] = 0u;
+  if (threadIdx.x == 0) st[u] = TopkState{0u, 0u, (uint32_t)a.k, 0u};
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_pass_kernel(LayerArgs a, Span sp,
+                                                                 const uint32_t* __restrict__ keys,
+                                                                 uint32_t* __restrict__ ghist,
+                                                                 TopkState* __restrict__ st, int cmax, int shift) {
+  __shared__ uint32_t hist[kTopkThreads / 64][256];
+  __shared__ uint32_t tot[256];
+  __shared__ int s_last;
+  const UnitChunk uc = unit_chunk(sp, cmax);
+  if (!uc.valid) return;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int64_t N = a.N;
+  const int64_t c0 = (int64_t)uc.c * kTopkChunk;
+  const int64_t c1 = (c0 + kTopkChunk < N) ? c0 + kTopkChunk : N;
+  const uint32_t* kk = keys + (int64_t)uc.u * a.Np;
+  const uint32_t prefix = st[uc.u].prefix, mask = st[uc.u].mask;
+  for (int i = tid; i < (kTopkThreads / 64) * 256; i += kTopkThreads) (&hist[0][0])[i] = 0u;
+  __syncthreads();
+  constexpr int kStep = kTopkThreads * 4;
+  for (int64_t base = c0 + (int64_t)tid * 4; base < c1; base += (int64_t)kStep * kTopkUnroll) {
+    u32x4 v[kTopkUnroll];
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j) {
+      const int64_t i = base + (int64_t)j * kStep;
+      v[j] = i < c1 ? *reinterpret_cast<const u32x4*>(kk + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kv = v[j][e];
+        if (base + (int64_t)j * kStep + e < c1 && (kv & mask) == prefix)
+          atomicAdd(&hist[wave][(kv >> shift) & 255u], 1u);
+      }
+  }
+  __syncthreads();
+  {
+    uint32_t sum = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / 64; ++w) sum += hist[w][tid];
+    if (sum) atomicAdd(&ghist[(int64_t)uc.u * 256 + tid], sum);
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int nchunks = (int)((N + kTopkChunk - 1) / kTopkChunk);
+    s_last = atomicAdd(&st[uc.u].done, 1u) == (uint32_t)(nchunks - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // last block of this unit: every other block's histogram is in ghist
+  __threadfence();
+  uint32_t* gh = ghist + (int64_t)uc.u * 256;
+  tot[tid] = __hip_atomic_load(gh + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  gh[tid] = 0u;
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t rem = st[uc.u].rem;
+    uint32_t acc = 0;
+    int dg = 255;
+    for (; dg > 0; --dg) {
+      if (acc + tot[dg] >= rem) break;
+      acc += tot[dg];
+    }
+    st[uc.u] = TopkState{prefix | ((uint32_t)dg << shift), mask | (255u << shift), rem - acc, 0u};
+  }
+}
+
+// Short contexts: one 1024-thread block per miss unit runs the four passes and
+// the compaction itself (one launch; many units keep many CUs busy).
+constexpr int kUnitThreads = 1024;
+constexpr int kUnitPerThread = 16;
+
+__global__ __launch_bounds__(kUnitThreads) void topk_unit_kernel(LayerArgs a, Span sp,
+                                                                 const uint32_t* __restrict__ keys) {
   __shared__ uint32_t hist[16][256];
   __shared__ uint32_t tot[256];
   __shared__ uint32_t s_prefix, s_mask, s_rem, s_base_gt, s_base_eq;
@@ -363,21 +478,31 @@ __global__ __launch_bounds__(1024) void topk_kernel(LayerArgs a, Span sp, const 
     }
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      for (int i = tid; i < 16 * 256; i += 1024) (&hist[0][0])[i] = 0u;
+      for (int i = tid; i < 16 * 256; i += kUnitThreads) (&hist[0][0])[i] = 0u;
       __syncthreads();
       const uint32_t prefix = s_prefix, mask = s_mask;
-      for (int64_t i = (int64_t)tid * 4; i < N; i += 4096) {
-        const uint4 v = *reinterpret_cast<const uint4*>(kk + i);
-        const uint32_t kv[4] = {v.x, v.y, v.z, v.w};
+      constexpr int kStep = kUnitThreads * 4;
+      for (int64_t base = (int64_t)tid * 4; base < N; base += (int64_t)kStep * kTopkUnroll) {
+        u32x4 v[kTopkUnroll];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (i + e < N && (kv[e] & mask) == prefix) atomicAdd(&hist[wave][(kv[e] >> shift) & 255u], 1u);
+        for (int j = 0; j < kTopkUnroll; ++j) {
+          const int64_t i = base + (int64_t)j * kStep;
+          v[j] = i < N ? *reinterpret_cast<const u32x4*>(kk + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < kTopkUnroll; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t kv = v[j][e];
+            if (base + (int64_t)j * kStep + e < N && (kv & mask) == prefix)
+              atomicAdd(&hist[wave][(kv >> shift) & 255u], 1u);
+          }
       }
       __syncthreads();
       if (tid < 256) {
-        uint32_t s = 0;
-        for (int w = 0; w < 16; ++w) s += hist[w][tid];
-        tot[tid] = s;
+        uint32_t sum = 0;
+        for (int w = 0; w < 16; ++w) sum += hist[w][tid];
+        tot[tid] = sum;
       }
       __syncthreads();
       if (tid == 0) {
@@ -400,22 +525,22 @@ __global__ __launch_bounds__(1024) void topk_kernel(LayerArgs a, Span sp, const 
       s_base_eq = 0u;
     }
     __syncthreads();
-    for (int64_t t0 = 0; t0 < N; t0 += 4096) {
-      const int64_t i = t0 + (int64_t)tid * 4;
-      uint32_t kv[4] = {0u, 0u, 0u, 0u};
-      if (i < N) {
-        const uint4 v = *reinterpret_cast<const uint4*>(kk + i);
-        kv[0] = v.x; kv[1] = v.y; kv[2] = v.z; kv[3] = v.w;
-      }
-      bool gt[4], eq[4];
+    constexpr int kTile = kUnitThreads * kUnitPerThread;
+    for (int64_t t0 = 0; t0 < N; t0 += kTile) {
+      const int64_t i0 = t0 + (int64_t)tid * kUnitPerThread;
+      u32x4 v[kUnitPerThread / 4];
+#pragma unroll
+      for (int j = 0; j < kUnitPerThread / 4; ++j)
+        v[j] = (i0 + 4 * j < N) ? *reinterpret_cast<const u32x4*>(kk + i0 + 4 * j) : u32x4{0u, 0u, 0u, 0u};
       uint32_t cg = 0, ce = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gt[e] = (i + e < N) && kv[e] > T;
-        eq[e] = (i + e < N) && kv[e] == T;
-        cg += gt[e];
-        ce += eq[e];
-      }
+      for (int j = 0; j < kUnitPerThread / 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool valid = i0 + 4 * j + e < N;
+          cg += (valid && v[j][e] > T);
+          ce += (valid && v[j][e] == T);
+        }
       uint32_t xg = cg, xe = ce;
       for (int off = 1; off < 64; off <<= 1) {
         const uint32_t yg = __shfl_up(xg, off, 64), ye = __shfl_up(xe, off, 64);
@@ -435,16 +560,21 @@ __global__ __launch_bounds__(1024) void topk_kernel(LayerArgs a, Span sp, const 
         pe += s_weq[w];
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (gt[e]) {
-          const uint32_t pos = pg + (pe < need ? pe : need);
-          if (pos < (uint32_t)a.k) out[pos] = (int32_t)(i + e);
-          ++pg;
-        } else if (eq[e]) {
-          if (pe < need && pg + pe < (uint32_t)a.k) out[pg + pe] = (int32_t)(i + e);
-          ++pe;
+      for (int j = 0; j < kUnitPerThread / 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t i = i0 + 4 * j + e;
+          if (i >= N) continue;
+          const uint32_t kv = v[j][e];
+          if (kv > T) {
+            const uint32_t pos = pg + (pe < need ? pe : need);
+            if (pos < (uint32_t)a.k) out[pos] = (int32_t)i;
+            ++pg;
+          } else if (kv == T) {
+            if (pe < need && pg + pe < (uint32_t)a.k) out[pg + pe] = (int32_t)i;
+            ++pe;
+          }
         }
-      }
       __syncthreads();
       if (tid == 0) {
         for (int w = 0; w < 16; ++w) {
@@ -454,6 +584,135 @@ __global__ __launch_bounds__(1024) void topk_kernel(LayerArgs a, Span sp, const 
       }
       __syncthreads();
     }
+  }
+}
+
+// Block-wide exclusive scan of two counts (keys > T, keys == T) of each thread.
+__device__ __forceinline__ void scan2(uint32_t cg, uint32_t ce, uint32_t* s_wg, uint32_t* s_we, uint32_t& eg,
+                                      uint32_t& ee, uint32_t& tg, uint32_t& te) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t xg = cg, xe = ce;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t yg = __shfl_up(xg, off, 64), ye = __shfl_up(xe, off, 64);
+    if (lane >= off) {
+      xg += yg;
+      xe += ye;
+    }
+  }
+  if (lane == 63) {
+    s_wg[wave] = xg;
+    s_we[wave] = xe;
+  }
+  __syncthreads();
+  eg = xg - cg;
+  ee = xe - ce;
+  tg = 0;
+  te = 0;
+  for (int w = 0; w < kTopkThreads / 64; ++w) {
+    if (w < wave) {
+      eg += s_wg[w];
+      ee += s_we[w];
+    }
+    tg += s_wg[w];
+    te += s_we[w];
+  }
+  __syncthreads();
+}
+
+constexpr int kTopkPerThread = 16;  // consecutive keys per thread per tile in count / write
+
+__global__ __launch_bounds__(kTopkThreads) void topk_count_kernel(LayerArgs a, Span sp,
+                                                                  const uint32_t* __restrict__ keys,
+                                                                  const TopkState* __restrict__ st,
+                                                                  uint32_t* __restrict__ tcount, int cmax) {
+  __shared__ uint32_t s_wg[kTopkThreads / 64], s_we[kTopkThreads / 64];
+  const UnitChunk uc = unit_chunk(sp, cmax);
+  if (!uc.valid) return;
+  const int64_t N = a.N;
+  const int64_t c0 = (int64_t)uc.c * kTopkChunk;
+  const int64_t c1 = (c0 + kTopkChunk < N) ? c0 + kTopkChunk : N;
+  const uint32_t* kk = keys + (int64_t)uc.u * a.Np;
+  const uint32_t T = st[uc.u].prefix;
+  uint32_t cg = 0, ce = 0;
+  for (int64_t base = c0 + (int64_t)threadIdx.x * 4; base < c1; base += (int64_t)kTopkThreads * 4 * kTopkUnroll) {
+    u32x4 v[kTopkUnroll];
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j) {
+      const int64_t i = base + (int64_t)j * kTopkThreads * 4;
+      v[j] = i < c1 ? *reinterpret_cast<const u32x4*>(kk + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = base + (int64_t)j * kTopkThreads * 4 + e < c1;
+        cg += valid && v[j][e] > T;
+        ce += valid && v[j][e] == T;
+      }
+  }
+  uint32_t eg, ee, tg, te;
+  scan2(cg, ce, s_wg, s_we, eg, ee, tg, te);
+  if (threadIdx.x == 0) {
+    tcount[((int64_t)uc.u * cmax + uc.c) * 2] = tg;
+    tcount[((int64_t)uc.u * cmax + uc.c) * 2 + 1] = te;
+  }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_write_kernel(LayerArgs a, Span sp,
+                                                                  const uint32_t* __restrict__ keys,
+                                                                  const TopkState* __restrict__ st,
+                                                                  const uint32_t* __restrict__ tcount, int cmax) {
+  __shared__ uint32_t s_wg[kTopkThreads / 64], s_we[kTopkThreads / 64];
+  const UnitChunk uc = unit_chunk(sp, cmax);
+  if (!uc.valid) return;
+  const int64_t N = a.N;
+  const int64_t c0 = (int64_t)uc.c * kTopkChunk;
+  const int64_t c1 = (c0 + kTopkChunk < N) ? c0 + kTopkChunk : N;
+  const uint32_t* kk = keys + (int64_t)uc.u * a.Np;
+  int32_t* out = a.idx + (int64_t)uc.u * a.k;
+  const uint32_t T = st[uc.u].prefix, need = st[uc.u].rem;
+  uint32_t base_g = 0, base_e = 0;
+  for (int c = 0; c < uc.c; ++c) {
+    base_g += tcount[((int64_t)uc.u * cmax + c) * 2];
+    base_e += tcount[((int64_t)uc.u * cmax + c) * 2 + 1];
+  }
+  constexpr int kTile = kTopkThreads * kTopkPerThread;
+  for (int64_t t0 = c0; t0 < c1; t0 += kTile) {
+    const int64_t i0 = t0 + (int64_t)threadIdx.x * kTopkPerThread;
+    u32x4 v[kTopkPerThread / 4];
+#pragma unroll
+    for (int j = 0; j < kTopkPerThread / 4; ++j)
+      v[j] = (i0 + 4 * j < c1) ? *reinterpret_cast<const u32x4*>(kk + i0 + 4 * j) : u32x4{0u, 0u, 0u, 0u};
+    uint32_t cg = 0, ce = 0;
+#pragma unroll
+    for (int j = 0; j < kTopkPerThread / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = i0 + 4 * j + e < c1;
+        cg += valid && v[j][e] > T;
+        ce += valid && v[j][e] == T;
+      }
+    uint32_t eg, ee, tg, te;
+    scan2(cg, ce, s_wg, s_we, eg, ee, tg, te);
+    uint32_t pg = base_g + eg, pe = base_e + ee;
+#pragma unroll
+    for (int j = 0; j < kTopkPerThread / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t i = i0 + 4 * j + e;
+        if (i >= c1) continue;
+        const uint32_t kv = v[j][e];
+        if (kv > T) {
+          const uint32_t pos = pg + (pe < need ? pe : need);
+          if (pos < (uint32_t)a.k) out[pos] = (int32_t)i;
+          ++pg;
+        } else if (kv == T) {
+          if (pe < need && pg + pe < (uint32_t)a.k) out[pg + pe] = (int32_t)i;
+          ++pe;
+        }
+      }
+    base_g += tg;
+    base_e += te;
   }
 }
 
@@ -512,8 +771,43 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
 // ---------------------------------------------------------------- A5 attention
 // Work item = (unit, chunk of kAttnChunk selected rows).  Phase 1: logits of
 // every (head, row) into LDS; phase 2: per-head max and exp-sum; phase 3:
-// p-weighted V sum, one column pair per lane.  The partial (o, m, l) of each
-// chunk is merged by attn_combine_kernel.
+// p-weighted V sum.  In phases 1 and 3 a row is read by 16 lanes, 16 bytes
+// each (bf16: 8 elements; fp32: 8 elements = two 16-byte pieces), 4 rows per
+// wave instruction, and each lane issues kAttnBatch rows' loads before it
+// uses any of them.  The partial (o, m, l) of each chunk is merged by
+// attn_combine_kernel.
+constexpr int kAttnBatch = 8;
+
+template <typename T>
+struct Row8;  // raw 8 elements of a row as loaded
+template <>
+struct Row8<uint16_t> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void unpack(float (&x)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf_lo(w[i]);
+      x[2 * i + 1] = bf_hi(w[i]);
+    }
+  }
+};
+template <>
+struct Row8<float> {
+  u32x4 w0, w1;
+  __device__ __forceinline__ void load(const float* p) {
+    w0 = *reinterpret_cast<const u32x4*>(p);
+    w1 = *reinterpret_cast<const u32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void unpack(float (&x)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = __uint_as_float(w0[i]);
+      x[4 + i] = __uint_as_float(w1[i]);
+    }
+  }
+};
+
 template <typename T, int G>
 __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T* __restrict__ q,
                                                            float* __restrict__ part, int nch, Span sp) {
@@ -545,6 +839,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
     kbase = static_cast<const T*>(a.k_cache) + s;
     vbase = static_cast<const T*>(a.v_cache) + s;
   }
+  // row of the source tensor holding selected row i (< nrows) of this chunk
   auto row_of = [&](int i) -> int64_t {
     if (!pers) return i;
     int64_t r = ix[i];
@@ -553,28 +848,35 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane & 15, rg = lane >> 4;
   const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
+  // this lane's rows: wave w owns rows [64 w, 64 w + 64); row group rg takes every 4th
+  const int row_base = wave * 64 + rg;
 
   // phase 1: logits
   {
     float qv[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g) load8(q + ((int64_t)b * a.Hq + (int64_t)h * G + g) * kHeadDim + sub * 8, qv[g]);
-    for (int j = 0; j < kAttnChunk / 16; ++j) {
-      const int i = j * 16 + wave * 4 + rg;
-      if (i < nrows) {
+#pragma unroll
+    for (int j0 = 0; j0 < 16; j0 += kAttnBatch) {
+      Row8<T> kr[kAttnBatch];
+#pragma unroll
+      for (int j = 0; j < kAttnBatch; ++j) {
+        const int i = row_base + 4 * (j0 + j);
+        kr[j].load(kbase + row_of(i < nrows ? i : nrows - 1) * kHeadDim + sub * 8);
+      }
+#pragma unroll
+      for (int j = 0; j < kAttnBatch; ++j) {
+        const int i = row_base + 4 * (j0 + j);
         float kx[8];
-        load8(kbase + row_of(i) * kHeadDim + sub * 8, kx);
+        kr[j].unpack(kx);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float s = 0.f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) s = fmaf(qv[g][e], kx[e], s);
           s = sum16(s);
-          if (sub == 0) lg[g][i] = s * scale;
+          if (sub == 0) lg[g][i] = (i < nrows) ? s * scale : kNegInf;
         }
-      } else if (sub == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) lg[g][i] = kNegInf;
       }
     }
   }
@@ -597,26 +899,49 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
     }
   }
   __syncthreads();
-  // phase 3: p-weighted sum of V rows; wave w takes rows [64w, 64w + 64)
+  // phase 3: p-weighted sum of V rows, columns 8 sub .. 8 sub + 7 in this lane
   {
-    float acc[G][2];
+    float acc[G][8];
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g][0] = acc[g][1] = 0.f;
-    const int i_end = min(nrows, wave * 64 + 64);
-    for (int i = wave * 64; i < i_end; ++i) {
-      float v0, v1;
-      load2(vbase + row_of(i) * kHeadDim + 2 * lane, v0, v1);
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float p = lg[g][i];
-        acc[g][0] = fmaf(p, v0, acc[g][0]);
-        acc[g][1] = fmaf(p, v1, acc[g][1]);
+      for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+#pragma unroll
+    for (int j0 = 0; j0 < 16; j0 += kAttnBatch) {
+      Row8<T> vr[kAttnBatch];
+#pragma unroll
+      for (int j = 0; j < kAttnBatch; ++j) {
+        const int i = row_base + 4 * (j0 + j);
+        vr[j].load(vbase + row_of(i < nrows ? i : nrows - 1) * kHeadDim + sub * 8);
+      }
+#pragma unroll
+      for (int j = 0; j < kAttnBatch; ++j) {
+        const int i = row_base + 4 * (j0 + j);
+        float vx[8];
+        vr[j].unpack(vx);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float p = lg[g][i];  // 0 past the last valid row
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p, vx[e], acc[g][e]);
+        }
       }
     }
+    // sum the four row groups of the wave (lanes sub, sub + 16, sub + 32, sub + 48)
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      red[wave][g][2 * lane] = acc[g][0];
-      red[wave][g][2 * lane + 1] = acc[g][1];
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = acc[g][e];
+        x += __shfl_xor(x, 16, 64);
+        x += __shfl_xor(x, 32, 64);
+        acc[g][e] = x;
+      }
+    if (rg == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[wave][g][sub * 8 + e] = acc[g][e];
     }
   }
   __syncthreads();
@@ -631,6 +956,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
   }
 }
 
+// Merge the chunk partials of one (unit, head): one thread per output column,
+// online max/sum rescaling over the chunks, kAttnBatch chunks' partials loaded
+// before any is used.
 template <typename T>
 __global__ __launch_bounds__(128) void attn_combine_kernel(LayerArgs a, const float* __restrict__ part, int nch,
                                                            T* __restrict__ out) {
@@ -640,13 +968,25 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(LayerArgs a, const fl
   const int col = threadIdx.x;
   const float* p = part + ((int64_t)u * nch * G + g) * kPartStride;
   const int64_t cstride = (int64_t)G * kPartStride;
-  float M = kNegInf;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, p[c * cstride + kHeadDim]);
-  float L = 0.f, O = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const float w = expf(p[c * cstride + kHeadDim] - M);
-    L = fmaf(p[c * cstride + kHeadDim + 1], w, L);
-    O = fmaf(p[c * cstride + col], w, O);
+  float M = kNegInf, L = 0.f, O = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += kAttnBatch) {
+    float m[kAttnBatch], l[kAttnBatch], o[kAttnBatch];
+#pragma unroll
+    for (int j = 0; j < kAttnBatch; ++j) {
+      const int c = c0 + j < nch ? c0 + j : nch - 1;
+      m[j] = p[c * cstride + kHeadDim];
+      l[j] = p[c * cstride + kHeadDim + 1];
+      o[j] = p[c * cstride + col];
+    }
+#pragma unroll
+    for (int j = 0; j < kAttnBatch; ++j) {
+      if (c0 + j >= nch) break;
+      const float Mn = fmaxf(M, m[j]);
+      const float sa = expf(M - Mn), sb = expf(m[j] - Mn);
+      L = L * sa + l[j] * sb;
+      O = O * sa + o[j] * sb;
+      M = Mn;
+    }
   }
   store_out(out + ((int64_t)b * a.Hq + (int64_t)h * G + g) * kHeadDim + col, O / L);
 }
@@ -720,10 +1060,22 @@ hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_
   });
 }
 
-hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uint32_t* keys, int num_cu,
+hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uint32_t* keys, const Workspace& w,
                        hipStream_t s) {
-  const int grid = grid_cap(max_units, (int64_t)num_cu * 2);
-  topk_kernel<<<grid, 1024, 0, s>>>(a, sp, keys);
+  const int cmax = w.cmax;
+  if (cmax < kTopkMultiMin) {
+    const int grid = grid_cap(max_units, 4096);
+    topk_unit_kernel<<<grid, kUnitThreads, 0, s>>>(a, sp, keys);
+    return hipGetLastError();
+  }
+  const int64_t grid = max_units * cmax;
+  const unsigned ug = (unsigned)(max_units > 0 ? max_units : 1);
+  const unsigned cg = (unsigned)(grid > 0 ? grid : 1);
+  topk_init_kernel<<<ug, kTopkThreads, 0, s>>>(a, sp, w.ghist, w.tstate);
+  for (int pass = 0; pass < 4; ++pass)
+    topk_pass_kernel<<<cg, kTopkThreads, 0, s>>>(a, sp, keys, w.ghist, w.tstate, cmax, 24 - 8 * pass);
+  topk_count_kernel<<<cg, kTopkThreads, 0, s>>>(a, sp, keys, w.tstate, w.tcount, cmax);
+  topk_write_kernel<<<cg, kTopkThreads, 0, s>>>(a, sp, keys, w.tstate, w.tcount, cmax);
   return hipGetLastError();
 }
 
