@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the host-link reference probes")
     ap.add_argument("--cpu-sample-seconds", type=float, default=10.0)
+    ap.add_argument("--host-memory", choices=["mapped", "coherent", "noncoherent"], default="mapped",
+                    help="pinned host memory kind for offloaded K/V (hipHostMalloc flags)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device-to-device copy first (reference for HBM byte counters)")
     return ap.parse_args()
@@ -116,10 +118,11 @@ def probe_host_link(torch, nbytes=1 << 30):
     cache = torch.empty(2, rows, HEAD_DIM, dtype=torch.bfloat16, device="cuda")
     shape = clo.Shape(1, 1, 1, rows, rows, math.inf, clo.CLO_BF16)
     layer = clo.Layer(0, None, None, kv.ptr, kv.ptr + rows * HEAD_DIM * 2, None, cache[0], cache[1], idx)
+    pws = torch.empty(clo.clo_workspace_size(shape), dtype=torch.uint8, device="cuda")
     times = []
     for i in range(4):
         e0.record()
-        clo.clo_gather_kv(shape, layer, None)
+        clo.clo_gather_kv(shape, layer, None, pws)
         e1.record()
         e1.synchronize()
         if i:
@@ -233,7 +236,7 @@ def phase_times(torch, clo, layers, step_kind, passes):
             ev[1].record()
             clo.clo_topk_select(shape, layer, query, bufs.reuse, bufs.ws)
             ev[2].record()
-            clo.clo_gather_kv(shape, layer, bufs.reuse)
+            clo.clo_gather_kv(shape, layer, bufs.reuse, bufs.ws)
             ev[3].record()
             clo.clo_sparse_attn(shape, layer, query, bufs.out, bufs.ws)
             ev[4].record()
@@ -264,11 +267,16 @@ def main():
     multi = p.layers > 1
     log(f"config {args.config}: L={p.layers} B={p.batch} Hq={p.hq} Hkv={p.hkv} N={p.context} k={p.topk} "
         f"{p.dtype} data layers={p.data_layers or p.layers}")
+    from top_sparse_attention_02_amd import hip_host
+
+    flags = {"mapped": hip_host.hipHostMallocMapped,
+             "coherent": hip_host.hipHostMallocMapped | hip_host.hipHostMallocCoherent,
+             "noncoherent": hip_host.hipHostMallocMapped | hip_host.hipHostMallocNonCoherent}[args.host_memory]
     t0 = time.time()
     if multi:
-        layers = workload.load_layers(p, log=log)
+        layers = workload.load_layers(p, log=log, host_flags=flags)
     else:
-        layers = [workload.load_layer(p, 0, log=log if p.batch >= 16 else None)]
+        layers = [workload.load_layer(p, 0, log=log if p.batch >= 16 else None, host_flags=flags)]
     log(f"inputs generated and resident ({time.time() - t0:.1f} s)")
 
     probe = None
@@ -350,7 +358,7 @@ def main():
                    (", steady step (80/20 reuse)" if args.step == 1 else ", cold step (all miss)"),
                    "layers": p.layers, "batch": p.batch, "q_heads": p.hq, "kv_heads": p.hkv, "head_dim": HEAD_DIM,
                    "context": p.context, "topk": p.topk, "tau": p.tau, "step": args.step,
-                   "data_layers": p.data_layers or p.layers},
+                   "data_layers": p.data_layers or p.layers, "host_memory": args.host_memory},
         "roofline": roofline,
         "roofline_score": {"bound": "hbm", "kernel": "compact+score+topk", "achieved": round(score_gbs, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),

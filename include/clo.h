@@ -155,10 +155,12 @@ clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const
  * For every miss unit of a non-persistent head: k_cache[u][i] = k_host[u][idx[u][i]]
  * and v_cache[u][i] = v_host[u][idx[u][i]], read by the GPU directly from pinned
  * host memory (bit-exact copies).  Persistent heads need no transfer: attention
- * reads their rows in place.  reuse NULL = all units miss.  sync may be NULL.
+ * reads their rows in place.  reuse NULL = all units miss.  ws: device workspace
+ * as for clo_topk_select (the gather's blocks take work from a counter in it;
+ * calls that share one workspace must not overlap).  sync may be NULL.
  */
 clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const uint8_t* reuse,
-                         const clo_sync* sync, void* stream);
+                         void* ws, size_t ws_bytes, const clo_sync* sync, void* stream);
 
 /*
  * A5 -- sparse attention over the selected rows, every unit (synthesis 2.3

@@ -92,7 +92,7 @@ def test_consumer_sees_rows_written_before_the_flag(need_gpu):
     torch.cuda.synchronize()
     with torch.cuda.stream(sp):
         torch.cuda._sleep(50_000_000)  # tens of milliseconds before the producer starts
-    clo.clo_gather_kv(shape, layer, None, sync=clo.Sync(signal_flag=flag[0], signal_value=7), stream=sp)
+    clo.clo_gather_kv(shape, layer, None, bufs.ws, sync=clo.Sync(signal_flag=flag[0], signal_value=7), stream=sp)
     clo.clo_sparse_attn(shape, layer, bufs.q_prev, bufs.out, bufs.ws,
                         sync=clo.Sync(wait_flag=flag[0], wait_value=7, error_word=err), stream=sc)
     torch.cuda.synchronize()
@@ -112,7 +112,7 @@ def test_never_signalled_flag_times_out_without_hanging(need_gpu):
     bufs = workload.load_layer(p, 0)
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    clo.clo_gather_kv(bufs.shape_with(math.inf), bufs.layer(), None,
+    clo.clo_gather_kv(bufs.shape_with(math.inf), bufs.layer(), None, bufs.ws,
                       sync=clo.Sync(wait_flag=flag[0], wait_value=1, error_word=err, spin_limit=2000))
     torch.cuda.synchronize()
     assert int(err.item()) == clo.CLO_E_TIMEOUT
@@ -129,7 +129,7 @@ def test_already_signalled_flag_does_not_wait(need_gpu):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     shape = clo.Shape(0, 4, 1, 10, 1, 0.8, clo.CLO_F32)  # empty batch: only the wait and the signal run
     t = time.perf_counter()
-    clo.clo_gather_kv(shape, clo.Layer(), None,
+    clo.clo_gather_kv(shape, clo.Layer(), None, None,
                       sync=clo.Sync(wait_flag=flag[0], wait_value=5, signal_flag=flag[0], signal_value=9,
                                     error_word=err))
     torch.cuda.synchronize()

@@ -135,7 +135,7 @@ def test_standalone_entry_points_equal_fused_step(need_gpu):
     layer = bufs.layer()
     clo.clo_reuse_test(shape, bufs.q, bufs.q_prev, bufs.reuse, bufs.cos)
     clo.clo_topk_select(shape, layer, bufs.q, bufs.reuse, bufs.ws)
-    clo.clo_gather_kv(shape, layer, bufs.reuse)
+    clo.clo_gather_kv(shape, layer, bufs.reuse, bufs.ws)
     clo.clo_sparse_attn(shape, layer, bufs.q, bufs.out, bufs.ws)
     split = snapshot(bufs)
     for key in fused:
@@ -161,7 +161,7 @@ def test_zero_copy_gather_equals_hbm_gather(need_gpu):
     bufs.v_cache.zero_()
     layer = bufs.layer()
     layer.k_host, layer.v_host = k_dev, v_dev
-    clo.clo_gather_kv(bufs.shape_with(math.inf), layer, None)
+    clo.clo_gather_kv(bufs.shape_with(math.inf), layer, None, bufs.ws)
     dev = snapshot(bufs)
     assert np.array_equal(host["k_cache"], dev["k_cache"])
     assert np.array_equal(host["v_cache"], dev["v_cache"])

@@ -64,7 +64,7 @@ def load():
         L.clo_topk_select.restype = st
         L.clo_topk_select.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, sz, P(clo_sync), vp]
         L.clo_gather_kv.restype = st
-        L.clo_gather_kv.argtypes = [P(clo_shape), P(clo_layer), vp, P(clo_sync), vp]
+        L.clo_gather_kv.argtypes = [P(clo_shape), P(clo_layer), vp, vp, sz, P(clo_sync), vp]
         L.clo_sparse_attn.restype = st
         L.clo_sparse_attn.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, sz, P(clo_sync), vp]
         L.clo_decode_step.restype = st
@@ -193,9 +193,10 @@ def clo_topk_select(shape: Shape, layer: Layer, q, reuse, ws, sync: Optional[Syn
                                   nbytes(ws, ws_bytes), _sync(sync), stream_handle(stream)), "clo_topk_select")
 
 
-def clo_gather_kv(shape: Shape, layer: Layer, reuse, sync: Optional[Sync] = None, stream=None):
-    _check(load().clo_gather_kv(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(reuse), _sync(sync),
-                                stream_handle(stream)), "clo_gather_kv")
+def clo_gather_kv(shape: Shape, layer: Layer, reuse, ws, sync: Optional[Sync] = None, stream=None,
+                  ws_bytes: Optional[int] = None):
+    _check(load().clo_gather_kv(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(reuse), ptr(ws),
+                                nbytes(ws, ws_bytes), _sync(sync), stream_handle(stream)), "clo_gather_kv")
 
 
 def clo_sparse_attn(shape: Shape, layer: Layer, q, out, ws, sync: Optional[Sync] = None, stream=None,

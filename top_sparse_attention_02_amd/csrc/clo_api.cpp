@@ -392,8 +392,8 @@ clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const
   return post_signal(sync, s);
 }
 
-clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const uint8_t* reuse, const clo_sync* sync,
-                         void* stream) {
+clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const uint8_t* reuse, void* ws,
+                         size_t ws_bytes, const clo_sync* sync, void* stream) {
   Plan p;
   clo_status st;
   if ((st = make_plan(shape, layer ? layer->persistent_mask : 0, &p))) return st;
@@ -403,10 +403,15 @@ clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const u
     if ((st = pre_wait(sync, s))) return st;
     return post_signal(sync, s);
   }
+  Workspace w;
   if ((st = check_layer(layer, &p, NEED_HOST | NEED_CACHE))) return st;
   if (reuse && (st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
+  if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
+  uint32_t* counter = reinterpret_cast<uint32_t*>(w.meta + kMetaGather);
   if ((st = pre_wait(sync, s))) return st;
-  if ((st = hip_status(launch_gather(p.a, reuse, kAllUnits, p.U, kGatherBlocksAlone, s), "gather launch"))) return st;
+  if ((st = hip_status(launch_zero(counter, s), "gather counter launch"))) return st;
+  if ((st = hip_status(launch_gather(p.a, reuse, kAllUnits, p.U, kGatherBlocksAlone, counter, s), "gather launch")))
+    return st;
   return post_signal(sync, s);
 }
 
@@ -479,7 +484,9 @@ clo_status step_overlapped(const Plan& p, const Workspace& w, const void* q, con
       CLO_TRY(hipStreamWaitEvent(as, dq->ev_topk[0], 0), "stream wait");
       CLO_TRY(launch_attn_partial(p.a, q, w.part, span_hits(w), p.U, as), "attention launch");
     }
-    CLO_TRY(launch_gather(p.a, reuse, span_host_range(w, r), per, kGatherBlocksOverlapped, gs), "gather launch");
+    CLO_TRY(launch_gather(p.a, reuse, span_host_range(w, r), per, kGatherBlocksOverlapped,
+                          reinterpret_cast<uint32_t*>(w.meta + kMetaGather + r), gs),
+            "gather launch");
     CLO_TRY(hipEventRecord(dq->ev_gather[r], gs), "event record");
     CLO_TRY(hipStreamWaitEvent(as, dq->ev_gather[r], 0), "stream wait");
     CLO_TRY(launch_attn_partial(p.a, q, w.part, span_range(w, r), per, as), "attention launch");

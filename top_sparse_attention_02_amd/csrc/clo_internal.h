@@ -12,7 +12,7 @@ constexpr int kMaxKvHeads = 64;   // width of the persistent mask
 
 // Work decomposition (rows / keys per work item).
 constexpr int kScoreChunk = 2048;   // keys scored by one work item
-constexpr int kGatherChunk = 512;   // rows gathered by one work item
+constexpr int kGatherChunk = 256;   // rows gathered by one work item
 constexpr int kAttnChunk = 256;     // selected rows attended by one work item
 constexpr int kPartStride = kHeadDim + 2;  // floats per (chunk, head) partial: o[d], m, l
 
@@ -54,7 +54,8 @@ constexpr int kMetaCountHit = 2;   // reuse units
 constexpr int kMetaZero = 4;       // always 0
 constexpr int kMetaOffAll = 16;    // [R + 1] first position of each range in list_all
 constexpr int kMetaOffHost = 40;   // [R + 1] first position of each range in list_host
-constexpr int kMetaInts = 64;
+constexpr int kMetaGather = 64;    // [kMaxRanges] work counters of the range gathers
+constexpr int kMetaInts = 96;
 
 // Multi-block top-k: each unit's keys are split into chunks of kTopkChunk keys,
 // one 256-thread block per chunk.
@@ -102,8 +103,11 @@ hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uin
                        hipStream_t s);
 // max_blocks bounds the grid: the host link saturates with a few hundred
 // waves in flight, and a smaller grid leaves the CUs to concurrent kernels.
+// Blocks take work items from *counter (zero at launch) so that blocks that
+// start late, behind other streams' work, simply take fewer items.
 hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, Span sp, int64_t max_units, int max_blocks,
-                         hipStream_t s);
+                         uint32_t* counter, hipStream_t s);
+hipError_t launch_zero(uint32_t* word, hipStream_t s);
 hipError_t launch_attn_partial(const LayerArgs& a, const void* q, float* part, Span sp, int64_t max_units,
                                hipStream_t s);
 hipError_t launch_attn_combine(const LayerArgs& a, const float* part, void* out, hipStream_t s);

@@ -195,6 +195,7 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
     }
     __syncthreads();
   }
+  if (tid < kMaxRanges) meta[kMetaGather + tid] = 0;
   if (tid == 0) {
     meta[kMetaCountAll] = base[0];
     meta[kMetaCountHost] = base[1];
@@ -721,17 +722,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_write_kernel(LayerArgs a, S
 // loads from pinned host memory are issued UNR rows deep per lane before any
 // store so that many reads are in flight on the host link.
 template <typename T>
-__global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp) {
+__global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp,
+                                                     uint32_t* __restrict__ counter) {
   constexpr int RB = kHeadDim * (int)sizeof(T);  // row bytes
   constexpr int LPR = RB / 16;
   constexpr int RPI = 256 / LPR;
   constexpr int UNR = 8;
+  __shared__ uint32_t s_item;
   const int nch = (int)((a.k + kGatherChunk - 1) / kGatherChunk);
   const int lo = sp.list ? *sp.lo : 0;
   const int64_t n_units = sp.list ? (int64_t)(*sp.hi - lo) : (int64_t)a.B * a.Hkv;
   const int64_t items = n_units * nch;
   const int sub = threadIdx.x % LPR, rl = threadIdx.x / LPR;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(counter, 1u);
+    __syncthreads();
+    const int64_t it = s_item;
+    __syncthreads();
+    if (it >= items) break;  // uniform per block
     const int u = sp.list ? sp.list[lo + it / nch] : (int)(it / nch);
     const int c = (int)(it % nch);
     const int b = u / a.Hkv, h = u % a.Hkv;
@@ -766,6 +774,10 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
       }
     }
   }
+}
+
+__global__ void zero_kernel(uint32_t* word) {
+  if (threadIdx.x == 0) *word = 0u;
 }
 
 // ---------------------------------------------------------------- A5 attention
@@ -1080,13 +1092,18 @@ hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uin
 }
 
 hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, Span sp, int64_t max_units, int max_blocks,
-                         hipStream_t s) {
+                         uint32_t* counter, hipStream_t s) {
   const int64_t nch = (a.k + kGatherChunk - 1) / kGatherChunk;
   const int grid = grid_cap(max_units * nch, (int64_t)max_blocks);
   if (a.dtype == CLO_F32)
-    gather_kernel<float><<<grid, 256, 0, s>>>(a, reuse, sp);
+    gather_kernel<float><<<grid, 256, 0, s>>>(a, reuse, sp, counter);
   else
-    gather_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse, sp);
+    gather_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse, sp, counter);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(uint32_t* word, hipStream_t s) {
+  zero_kernel<<<1, 64, 0, s>>>(word);
   return hipGetLastError();
 }
 

@@ -125,7 +125,7 @@ def stored_tensor(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
 
 
 def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads: Optional[int] = None,
-               log=None, share: Optional[LayerBuffers] = None) -> LayerBuffers:
+               log=None, share: Optional[LayerBuffers] = None, host_flags: int = hipHostMallocMapped) -> LayerBuffers:
     """Allocate (unless given) and fill the buffers of one layer of `problem`.
 
     With `share`, the layer reuses that layer's K/V buffers (aliased data) and
@@ -133,7 +133,8 @@ def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads
     p = problem
     mask = p.persistent_mask_bits(layer)
     if bufs is None:
-        bufs = LayerBuffers(p.batch, p.hq, p.hkv, p.context, p.topk, p.dtype, mask, p.tau, share=share)
+        bufs = LayerBuffers(p.batch, p.hq, p.hkv, p.context, p.topk, p.dtype, mask, p.tau, share=share,
+                            host_flags=host_flags)
     assert bufs.mask == mask
     bufs.q.copy_(stored_tensor(p.q(layer), p.dtype))
     bufs.q_prev.copy_(stored_tensor(p.q_prev(layer), p.dtype))
@@ -165,13 +166,13 @@ def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads
     return bufs
 
 
-def load_layers(problem, log=None, threads: Optional[int] = None):
+def load_layers(problem, log=None, threads: Optional[int] = None, host_flags: int = hipHostMallocMapped):
     """Buffers of every layer; layers with the same data layer share their K/V."""
     first = {}
     layers = []
     for l in range(problem.layers):
         dl = problem.data_layer(l)
-        bufs = load_layer(problem, l, threads=threads, share=first.get(dl))
+        bufs = load_layer(problem, l, threads=threads, share=first.get(dl), host_flags=host_flags)
         first.setdefault(dl, bufs)
         layers.append(bufs)
         if log:
@@ -226,7 +227,7 @@ class LayerLoop:
             clo.clo_reuse_test(shape, q, b.q_prev, b.reuse, b.cos, sync=after_prev, stream=self.s_select)
             clo.clo_topk_select(shape, layer, q, b.reuse, b.ws,
                                 sync=clo.Sync(signal_flag=self._flag(0, l), signal_value=e), stream=self.s_select)
-            clo.clo_gather_kv(shape, layer, b.reuse,
+            clo.clo_gather_kv(shape, layer, b.reuse, b.ws,
                               sync=clo.Sync(wait_flag=self._flag(0, l), wait_value=e, signal_flag=self._flag(1, l),
                                             signal_value=e, error_word=self.error, spin_limit=sp),
                               stream=self.s_gather)
