@@ -89,6 +89,30 @@ def algorithmic_bytes(layers):
     return tot
 
 
+def profiled_traffic(kernel: str, cfg: int):
+    """HBM/host traffic of a kernel from a committed rocprofv3 counter record, or None.
+
+    The record (profiles/<kernel>_traffic__*.json) stores the sha256 of the kernel
+    source it was measured on; once the source changes the figure no longer
+    applies and None is reported."""
+    import glob
+    import hashlib
+
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic__*.json"))):
+        try:
+            rec = json.load(open(path))
+        except (OSError, ValueError):
+            continue
+        if rec.get("kernel") != kernel or not rec.get("workload", "").startswith(f"config {cfg} "):
+            continue
+        src = os.path.join(ROOT, rec["source"])
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+            return None
+        rec["path"] = os.path.relpath(path, ROOT)
+        return rec
+    return None
+
+
 def probe_host_link(torch, nbytes=1 << 30):
     """Measured host-link reference: SDMA memcpy of pinned memory, and the gather
     kernel streaming contiguous rows (identity index) from pinned memory."""
@@ -333,6 +357,13 @@ def main():
                     "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s", "frac": round(host_gbs / HOST_LINK_PEAK_GBS, 4),
                     "traffic": None, "bytes_per_launch": alg["host_bytes"] // len(layers),
                     "launch_ms": round(phases["gather"] / len(layers), 4)}
+        rec = profiled_traffic("gather_kernel", args.config) if not multi and args.step == 1 else None
+        if rec:
+            roofline["traffic"] = rec["traffic_bytes_per_launch"]
+            roofline["traffic_detail"] = {"read_bytes": rec["read_bytes_per_launch"],
+                                          "write_bytes": rec["write_bytes_per_launch"],
+                                          "fetch_scale": rec["fetch_scale"], "write_scale": rec["write_scale"],
+                                          "source": rec["path"]}
         if probe:
             roofline["peak_measured"] = round(probe["h_meas_gbs"], 2)
             roofline["frac_measured"] = round(host_gbs / probe["h_meas_gbs"], 4)
