@@ -214,6 +214,7 @@ Span span_host_range(const Workspace& w, int r) {
   return Span{w.list_host, w.meta + kMetaOffHost + r, w.meta + kMetaOffHost + r + 1};
 }
 constexpr Span kAllUnits{nullptr, nullptr, nullptr};
+uint32_t* score_counter(const Workspace& w, int r) { return reinterpret_cast<uint32_t*>(w.meta + kMetaScore + r); }
 
 // Per-device helper streams and events of the overlapped decode step, created
 // on first use and kept for the life of the process.  They hold no user data.
@@ -387,7 +388,7 @@ clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const
   const int cu = num_cus();
   if ((st = pre_wait(sync, s))) return st;
   if ((st = hip_status(launch_compact(p.a, reuse, w, 1, s), "compact launch"))) return st;
-  if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w.keys, cu, s), "score launch"))) return st;
+  if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w.keys, score_counter(w, 0), cu, s), "score launch"))) return st;
   if ((st = hip_status(launch_topk(p.a, span_all_misses(w), p.U, w.keys, w, s), "top-k launch"))) return st;
   return post_signal(sync, s);
 }
@@ -446,7 +447,7 @@ clo_status step_in_order(const Plan& p, const Workspace& w, const void* q, const
   const int cu = num_cus();
   if ((st = hip_status(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch"))) return st;
   if ((st = hip_status(launch_compact(p.a, reuse, w, 1, s), "compact launch"))) return st;
-  if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w.keys, cu, s), "score launch"))) return st;
+  if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w.keys, score_counter(w, 0), cu, s), "score launch"))) return st;
   if ((st = hip_status(launch_topk(p.a, span_all_misses(w), p.U, w.keys, w, s), "top-k launch"))) return st;
   if ((st = hip_status(launch_attn_partial(p.a, q, w.part, kAllUnits, p.U, s), "attention launch"))) return st;
   return hip_status(launch_attn_combine(p.a, w.part, out, s), "attention combine launch");
@@ -474,7 +475,7 @@ clo_status step_overlapped(const Plan& p, const Workspace& w, const void* q, con
   CLO_TRY(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch");
   CLO_TRY(launch_compact(p.a, reuse, w, R, s), "compact launch");
   for (int r = 0; r < R; ++r) {
-    CLO_TRY(launch_score(p.a, q, span_range(w, r), per, w.keys, cu, s), "score launch");
+    CLO_TRY(launch_score(p.a, q, span_range(w, r), per, w.keys, score_counter(w, r), cu, s), "score launch");
     CLO_TRY(launch_topk(p.a, span_range(w, r), per, w.keys, w, s), "top-k launch");
     CLO_TRY(hipEventRecord(dq->ev_topk[r], s), "event record");
     CLO_TRY(hipStreamWaitEvent(gs, dq->ev_topk[r], 0), "stream wait");

@@ -55,6 +55,7 @@ constexpr int kMetaZero = 4;       // always 0
 constexpr int kMetaOffAll = 16;    // [R + 1] first position of each range in list_all
 constexpr int kMetaOffHost = 40;   // [R + 1] first position of each range in list_host
 constexpr int kMetaGather = 64;    // [kMaxRanges] work counters of the range gathers
+constexpr int kMetaScore = 80;     // [kMaxRanges] work counters of the range scorings
 constexpr int kMetaInts = 96;
 
 // Multi-block top-k: each unit's keys are split into chunks of kTopkChunk keys,
@@ -97,8 +98,9 @@ hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, u
                         hipStream_t s);
 // max_units: an upper bound on the span's length, used to size the grid.
 hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, int ranges, hipStream_t s);
-hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_units, uint32_t* keys, int num_cu,
-                        hipStream_t s);
+// counter: zero at launch (the compact kernel clears the range counters).
+hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_units, uint32_t* keys,
+                        uint32_t* counter, int num_cu, hipStream_t s);
 hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uint32_t* keys, const Workspace& w,
                        hipStream_t s);
 // max_blocks bounds the grid: the host link saturates with a few hundred

@@ -195,7 +195,10 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
     }
     __syncthreads();
   }
-  if (tid < kMaxRanges) meta[kMetaGather + tid] = 0;
+  if (tid < kMaxRanges) {
+    meta[kMetaGather + tid] = 0;
+    meta[kMetaScore + tid] = 0;
+  }
   if (tid == 0) {
     meta[kMetaCountAll] = base[0];
     meta[kMetaCountHost] = base[1];
@@ -272,25 +275,39 @@ __global__ __launch_bounds__(256) void score_kernel(LayerArgs a, const T* __rest
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Blocks are persistent and take items of kScoreItem keys (kScoreItem / 4 per
+// wave) from a device counter, so that the last round of work is short and no
+// block idles behind a slow one; the query operand is reloaded only when the
+// unit changes.
+constexpr int kScoreItem = 1024;
+
 template <int G>
 __global__ __launch_bounds__(256) void score_mfma_kernel(LayerArgs a, const uint16_t* __restrict__ q, Span sp,
-                                                         uint32_t* __restrict__ keys) {
-  constexpr int TILES = 4;                         // 16-key tiles per wave iteration
-  constexpr int kKeysPerWave = kScoreChunk / 4;    // 512
+                                                         uint32_t* __restrict__ keys, uint32_t* __restrict__ counter) {
+  constexpr int TILES = 8;                         // 16-key tiles per wave iteration (128 keys)
+  constexpr int kKeysPerWave = kScoreItem / 4;     // 256
   static_assert(G <= 8, "group of at most 8 query heads");
-  const int nch = (int)((a.N + kScoreChunk - 1) / kScoreChunk);
+  __shared__ uint32_t s_item;
+  const int nch = (int)((a.N + kScoreItem - 1) / kScoreItem);
   const int lo = *sp.lo;
   const int64_t items = (int64_t)(*sp.hi - lo) * nch;
   const int32_t* list = sp.list + lo;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, ks = lane >> 4;       // tile column / k-slice of this lane
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+  int cur_u = -1;
+  bf16x8 qa[4];
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(counter, 1u);
+    __syncthreads();
+    const int64_t it = s_item;
+    __syncthreads();
+    if (it >= items) break;  // uniform per block
     const int u = list[it / nch];
     const int c = (int)(it % nch);
     const int b = u / a.Hkv, h = u % a.Hkv;
     const uint16_t* kb = unit_keys<uint16_t>(a, b, h);
-    bf16x8 qa[4];
-    {
+    if (u != cur_u) {
+      cur_u = u;
       const int head = col;  // row of Qpad
       const uint16_t* qh = q + ((int64_t)b * a.Hq + (int64_t)h * G + (head < G ? head : 0)) * kHeadDim;
 #pragma unroll
@@ -301,7 +318,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(LayerArgs a, const uint
       }
     }
     uint32_t* kout = keys + (int64_t)u * a.Np;
-    const int64_t w_begin = (int64_t)c * kScoreChunk + (int64_t)wave * kKeysPerWave;
+    const int64_t w_begin = (int64_t)c * kScoreItem + (int64_t)wave * kKeysPerWave;
     for (int t0 = 0; t0 < kKeysPerWave; t0 += 16 * TILES) {
       if (w_begin + t0 >= a.N) break;  // uniform per wave
       u32x4 kbuf[TILES][4];
@@ -313,6 +330,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(LayerArgs a, const uint
 #pragma unroll
         for (int s = 0; s < 4; ++s) kbuf[t][s] = *reinterpret_cast<const u32x4*>(kr + s * 32);
       }
+      float mt[TILES];  // tile maxima, valid in lanes 0..15 (lane = key within the tile)
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -331,8 +349,20 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(LayerArgs a, const uint
           if (G > 7) m2 = fmaxf(m2, acc[3]);
           m = fmaxf(m, __shfl_down(m2, 16, 64));
         }
-        const int64_t key = w_begin + t0 + t * 16 + col;
-        if (lane < 16 && key < a.N) kout[key] = score_key(m);
+        mt[t] = m;
+      }
+      // lane L of the wave takes key L of each 4-tile group: one 256-byte store
+      // per group instead of four 64-byte ones
+#pragma unroll
+      for (int t4 = 0; t4 < TILES; t4 += 4) {
+        float v = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float x = __shfl(mt[t4 + t], col, 64);
+          if (ks == t) v = x;
+        }
+        const int64_t key = w_begin + t0 + t4 * 16 + lane;
+        if (key < a.N) kout[key] = score_key(v);
       }
     }
   }
@@ -1058,16 +1088,21 @@ hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Worksp
   return hipGetLastError();
 }
 
-hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_units, uint32_t* keys, int num_cu,
-                        hipStream_t s) {
-  const int64_t nch = (a.N + kScoreChunk - 1) / kScoreChunk;
-  const int grid = grid_cap(max_units * nch, (int64_t)num_cu * 32);
+hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_units, uint32_t* keys,
+                        uint32_t* counter, int num_cu, hipStream_t s) {
   return dispatch_group(a.G, [&](auto gc) {
     constexpr int G = decltype(gc)::value;
-    if (a.dtype == CLO_F32)
+    if (a.dtype == CLO_F32) {
+      const int64_t nch = (a.N + kScoreChunk - 1) / kScoreChunk;
+      const int grid = grid_cap(max_units * nch, (int64_t)num_cu * 32);
       score_kernel<float, G><<<grid, 256, 0, s>>>(a, static_cast<const float*>(q), sp, keys);
-    else
-      score_mfma_kernel<G><<<grid, 256, 0, s>>>(a, static_cast<const uint16_t*>(q), sp, keys);
+    } else {
+      // persistent: two blocks (eight waves) per CU keep enough 16-byte loads in
+      // flight to stream K; more blocks only add contention
+      const int64_t nch = (a.N + kScoreItem - 1) / kScoreItem;
+      const int grid = grid_cap(max_units * nch, (int64_t)num_cu * 2);
+      score_mfma_kernel<G><<<grid, 256, 0, s>>>(a, static_cast<const uint16_t*>(q), sp, keys, counter);
+    }
     return hipGetLastError();
   });
 }
