@@ -16,14 +16,24 @@ constexpr int kGatherChunk = 256;   // rows gathered by one work item
 constexpr int kAttnChunk = 256;     // selected rows attended by one work item
 constexpr int kPartStride = kHeadDim + 2;  // floats per (chunk, head) partial: o[d], m, l
 
-// Gather grid.  Each 4-wave block keeps 8 rows x 2 (K, V) x 16 B per lane in
-// flight (32 KiB per block); the host link saturates with far fewer bytes in
-// flight than 32 blocks provide.  More blocks fill the memory request queues
-// with slow host reads and stall HBM kernels running beside the gather
-// (measured on MI355X: 256 blocks -> 14.8 ms per config-3 step, 32 -> 13.2 ms,
-// with the gather alone unchanged at ~12.2 ms).
+// Gather grid and depth.  Each 4-wave block keeps kGatherUnroll rows x 2 (K, V)
+// x 16 B per lane in flight.  The host link saturates with about 256-512 KiB of
+// reads in flight; beyond that the extra slow host reads only fill the memory
+// request queues and stall HBM kernels running beside the gather.  Measured on
+// MI355X (1 M random 256-byte rows from pinned memory, with an HBM scoring
+// kernel and a pointer chase on other streams):
+//   in flight   gather alone   scoring beside it   pointer chase beside it
+//   4096 KiB    56.1 GB/s      8-24x slower        18x slower
+//    512 KiB    56.8 GB/s      1.3-1.5x            1.5x
+//    384 KiB    56.7 GB/s      1.2-1.35x           1.3x   (24 blocks x 2 rows)
+//    128 KiB    49.4 GB/s      1.1-1.3x            1.2x
+// The overlapped single-layer step is bound by the gather alone and takes 32
+// blocks (512 KiB); a standalone gather usually runs beside the selection and
+// attention of other layers and takes 24 (384 KiB): on the 48-layer loop at
+// 512K context, 24 blocks gave 23.8 ms per step against 25.2 ms with 32.
+constexpr int kGatherUnroll = 2;
 constexpr int kGatherBlocksOverlapped = 32;
-constexpr int kGatherBlocksAlone = 64;
+constexpr int kGatherBlocksAlone = 24;
 
 // Everything a kernel needs to address one layer's buffers.
 struct LayerArgs {

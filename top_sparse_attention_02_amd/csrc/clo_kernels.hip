@@ -750,15 +750,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_write_kernel(LayerArgs a, S
 // ---------------------------------------------------------------- A4 gather
 // Rows of d elements are moved as 16-byte pieces: LPR lanes per row.  The
 // loads from pinned host memory are issued UNR rows deep per lane before any
-// store so that many reads are in flight on the host link.
+// store; grid x UNR sets the bytes in flight on the host link.
 template <typename T>
 __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp,
                                                      uint32_t* __restrict__ counter) {
   constexpr int RB = kHeadDim * (int)sizeof(T);  // row bytes
   constexpr int LPR = RB / 16;
   constexpr int RPI = 256 / LPR;
-  constexpr int UNR = 8;
+  constexpr int UNR = kGatherUnroll;
+  static_assert(kGatherChunk == 256, "one index per thread");
   __shared__ uint32_t s_item;
+  __shared__ int32_t s_src[kGatherChunk];  // the item's source rows, clamped into [0, N)
   const int nch = (int)((a.k + kGatherChunk - 1) / kGatherChunk);
   const int lo = sp.list ? *sp.lo : 0;
   const int64_t n_units = sp.list ? (int64_t)(*sp.hi - lo) : (int64_t)a.B * a.Hkv;
@@ -782,6 +784,13 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
     const int32_t* ix = a.idx + (int64_t)u * a.k;
     const int64_t r0 = (int64_t)c * kGatherChunk;
     const int64_t r_end = (r0 + kGatherChunk < a.k) ? r0 + kGatherChunk : a.k;
+    // the item's indices in one coalesced load, so that the host reads below
+    // do not wait on an index load each time
+    if (r0 + threadIdx.x < r_end) {
+      const int32_t src = ix[r0 + threadIdx.x];
+      s_src[threadIdx.x] = src < 0 ? 0 : (src >= a.N ? (int32_t)(a.N - 1) : src);
+    }
+    __syncthreads();
     for (int64_t rb = r0; rb < r_end; rb += RPI * UNR) {
       // rows past the end re-read the last row (in bounds) and are not stored
       u32x4 kx[UNR], vx[UNR];
@@ -789,8 +798,7 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
       for (int j = 0; j < UNR; ++j) {
         int64_t row = rb + j * RPI + rl;
         row = row < r_end ? row : r_end - 1;
-        int64_t src = ix[row];
-        src = src < 0 ? 0 : (src >= a.N ? a.N - 1 : src);
+        const int64_t src = s_src[row - r0];
         kx[j] = *reinterpret_cast<const u32x4*>(ks + src * RB + sub * 16);
         vx[j] = *reinterpret_cast<const u32x4*>(vs + src * RB + sub * 16);
       }
