@@ -152,10 +152,10 @@ clo_status make_plan(const clo_shape* s, uint64_t pmask, Plan* p) {
   return ok();
 }
 
-// Workspace layout: meta | list_all | list_host | list_hit | ghist | tstate | tcount | keys | part,
+// Workspace layout: meta | list_all | list_host | list_hit | h0 | h1 | tstate | chist | keys | part,
 // each 256-byte aligned.
 struct WsLayout {
-  size_t meta, list_all, list_host, list_hit, ghist, tstate, tcount, keys, part, total;
+  size_t meta, list_all, list_host, list_hit, h0, h1, tstate, chist, keys, part, total;
   int cmax;
 };
 
@@ -172,9 +172,10 @@ WsLayout ws_layout(const Plan& p) {
   w.list_host = take((size_t)p.U * 4);
   w.list_hit = take((size_t)p.U * 4);
   w.cmax = (int)((p.a.N + kTopkChunk - 1) / kTopkChunk);
-  w.ghist = take((size_t)p.U * 256 * 4);
+  w.h0 = take((size_t)p.U * 256 * 4);
+  w.h1 = take((size_t)p.U * 256 * 4);
   w.tstate = take((size_t)p.U * sizeof(TopkState));
-  w.tcount = take((size_t)p.U * (size_t)w.cmax * 2 * 4);
+  w.chist = take((size_t)p.U * (size_t)w.cmax * kChunkHist * 4);
   w.keys = take((size_t)p.U * (size_t)p.a.Np * 4);
   w.part = take((size_t)p.U * (size_t)p.nch_attn * (size_t)p.a.G * kPartStride * 4);
   w.total = off;
@@ -196,9 +197,10 @@ clo_status bind_ws(const Plan& p, void* ws, size_t ws_bytes, Workspace* w) {
   w->list_all = reinterpret_cast<int32_t*>(b + L.list_all);
   w->list_host = reinterpret_cast<int32_t*>(b + L.list_host);
   w->list_hit = reinterpret_cast<int32_t*>(b + L.list_hit);
-  w->ghist = reinterpret_cast<uint32_t*>(b + L.ghist);
+  w->h0 = reinterpret_cast<uint32_t*>(b + L.h0);
+  w->h1 = reinterpret_cast<uint32_t*>(b + L.h1);
   w->tstate = reinterpret_cast<TopkState*>(b + L.tstate);
-  w->tcount = reinterpret_cast<uint32_t*>(b + L.tcount);
+  w->chist = reinterpret_cast<uint32_t*>(b + L.chist);
   w->cmax = L.cmax;
   w->keys = reinterpret_cast<uint32_t*>(b + L.keys);
   w->part = reinterpret_cast<float*>(b + L.part);
@@ -388,7 +390,7 @@ clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const
   const int cu = num_cus();
   if ((st = pre_wait(sync, s))) return st;
   if ((st = hip_status(launch_compact(p.a, reuse, w, 1, s), "compact launch"))) return st;
-  if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w.keys, score_counter(w, 0), cu, s), "score launch"))) return st;
+  if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w, score_counter(w, 0), cu, s), "score launch"))) return st;
   if ((st = hip_status(launch_topk(p.a, span_all_misses(w), p.U, w.keys, w, s), "top-k launch"))) return st;
   return post_signal(sync, s);
 }
@@ -447,7 +449,7 @@ clo_status step_in_order(const Plan& p, const Workspace& w, const void* q, const
   const int cu = num_cus();
   if ((st = hip_status(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch"))) return st;
   if ((st = hip_status(launch_compact(p.a, reuse, w, 1, s), "compact launch"))) return st;
-  if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w.keys, score_counter(w, 0), cu, s), "score launch"))) return st;
+  if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w, score_counter(w, 0), cu, s), "score launch"))) return st;
   if ((st = hip_status(launch_topk(p.a, span_all_misses(w), p.U, w.keys, w, s), "top-k launch"))) return st;
   if ((st = hip_status(launch_attn_partial(p.a, q, w.part, kAllUnits, p.U, s), "attention launch"))) return st;
   return hip_status(launch_attn_combine(p.a, w.part, out, s), "attention combine launch");
@@ -475,7 +477,7 @@ clo_status step_overlapped(const Plan& p, const Workspace& w, const void* q, con
   CLO_TRY(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch");
   CLO_TRY(launch_compact(p.a, reuse, w, R, s), "compact launch");
   for (int r = 0; r < R; ++r) {
-    CLO_TRY(launch_score(p.a, q, span_range(w, r), per, w.keys, score_counter(w, r), cu, s), "score launch");
+    CLO_TRY(launch_score(p.a, q, span_range(w, r), per, w, score_counter(w, r), cu, s), "score launch");
     CLO_TRY(launch_topk(p.a, span_range(w, r), per, w.keys, w, s), "top-k launch");
     CLO_TRY(hipEventRecord(dq->ev_topk[r], s), "event record");
     CLO_TRY(hipStreamWaitEvent(gs, dq->ev_topk[r], 0), "stream wait");

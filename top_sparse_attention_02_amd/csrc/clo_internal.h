@@ -80,11 +80,16 @@ struct TopkState {
   uint32_t done;    // chunk blocks finished in the current pass
 };
 
+// Per chunk of the digit-4 pass: 256 bins of the chunk's keys that match the
+// 24-bit prefix, and the count of its keys above that prefix.
+constexpr int kChunkHist = 257;
+
 struct Workspace {
   int32_t* meta;       // counts and range offsets (layout above)
-  uint32_t* ghist;     // [U][256] per-unit radix histogram of the current pass
+  uint32_t* h0;        // [U][256] per-unit radix histograms (digits 1 and 3)
+  uint32_t* h1;        // [U][256] (digits 2 and 4)
   TopkState* tstate;   // [U]
-  uint32_t* tcount;    // [U][cmax][2] per-chunk counts of keys > T and == T
+  uint32_t* chist;     // [U][cmax][kChunkHist] per-chunk digit-4 histograms
   int32_t cmax;        // chunks per unit (ceil(N / kTopkChunk))
   int32_t* list_all;   // [U] miss units, ascending
   int32_t* list_host;  // [U] miss units of non-persistent heads, ascending
@@ -109,7 +114,9 @@ hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, u
 // max_units: an upper bound on the span's length, used to size the grid.
 hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, int ranges, hipStream_t s);
 // counter: zero at launch (the compact kernel clears the range counters).
-hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_units, uint32_t* keys,
+// Writes w.keys and the digit-1 histograms of the span's units (cleared by the
+// compact kernel).
+hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_units, const Workspace& w,
                         uint32_t* counter, int num_cu, hipStream_t s);
 hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uint32_t* keys, const Workspace& w,
                        hipStream_t s);

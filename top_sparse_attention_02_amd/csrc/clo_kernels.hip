@@ -153,7 +153,7 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
                                                        uint64_t pmask, int R, int32_t* __restrict__ meta,
                                                        int32_t* __restrict__ list_all,
                                                        int32_t* __restrict__ list_host,
-                                                       int32_t* __restrict__ list_hit) {
+                                                       int32_t* __restrict__ list_hit, uint32_t* __restrict__ h0) {
   __shared__ int wsum[3][16];
   __shared__ int base[3];
   __shared__ int rcount[2][kMaxRanges];
@@ -187,7 +187,12 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
       oh += wsum[1][i];
       ot += wsum[2][i];
     }
-    if (miss) list_all[om] = u;
+    if (miss) {
+      list_all[om] = u;
+      // digit-1 histogram of the unit's top-k, filled by the scoring kernel
+      u32x4* hz = reinterpret_cast<u32x4*>(h0 + (int64_t)u * 256);
+      for (int i = 0; i < 64; ++i) hz[i] = u32x4{0u, 0u, 0u, 0u};
+    }
     if (host) list_host[oh] = u;
     if (hit) list_hit[ot] = u;
     __syncthreads();
@@ -222,11 +227,42 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
 }
 
 // ---------------------------------------------------------------- A2 scoring
+// Both scoring kernels also count digit 1 (the top 8 bits) of every key they
+// produce in per-wave LDS histograms, which score_item_done adds to the unit's
+// global histogram H0 at the end of each work item; the block that takes a
+// unit's first item also clears the unit's H1 and resets its radix state
+// (nothing reads either before the top-k kernels that follow).
+__device__ __forceinline__ void score_item_done(uint32_t (*s_h)[256], int u, int c, int64_t k,
+                                                uint32_t* __restrict__ h0, uint32_t* __restrict__ h1,
+                                                TopkState* __restrict__ st) {
+  __syncthreads();
+  const int t = threadIdx.x;  // 256 threads, one bin each
+  const uint32_t sum = s_h[0][t] + s_h[1][t] + s_h[2][t] + s_h[3][t];
+  s_h[0][t] = 0u;
+  s_h[1][t] = 0u;
+  s_h[2][t] = 0u;
+  s_h[3][t] = 0u;
+  if (sum) atomicAdd(h0 + (int64_t)u * 256 + t, sum);
+  if (c == 0) {
+    h1[(int64_t)u * 256 + t] = 0u;
+    if (t == 0) st[u] = TopkState{0u, 0u, (uint32_t)k, 0u};
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void clear_score_hist(uint32_t (*s_h)[256]) {
+  for (int i = threadIdx.x; i < 4 * 256; i += 256) (&s_h[0][0])[i] = 0u;
+  __syncthreads();
+}
+
 // 16 lanes per key row (8 elements each), 4 rows per wave instruction.
 template <typename T, int G>
 __global__ __launch_bounds__(256) void score_kernel(LayerArgs a, const T* __restrict__ q, Span sp,
-                                                    uint32_t* __restrict__ keys) {
+                                                    uint32_t* __restrict__ keys, uint32_t* __restrict__ h0,
+                                                    uint32_t* __restrict__ h1, TopkState* __restrict__ st) {
   constexpr int UNR = 8;
+  __shared__ uint32_t s_h[4][256];
+  clear_score_hist(s_h);
   constexpr int kRowsPerWave = kScoreChunk / 4;
   const int nch = (int)((a.N + kScoreChunk - 1) / kScoreChunk);
   const int lo = *sp.lo;
@@ -263,9 +299,14 @@ __global__ __launch_bounds__(256) void score_kernel(LayerArgs a, const T* __rest
           for (int e = 0; e < 8; ++e) s = fmaf(qv[g][e], kx[j][e], s);
           best = fmaxf(best, sum16(s));
         }
-        if (sub == 0 && row[j] < a.N) kout[row[j]] = score_key(best);
+        if (sub == 0 && row[j] < a.N) {
+          const uint32_t sk = score_key(best);
+          kout[row[j]] = sk;
+          atomicAdd(&s_h[wave][sk >> 24], 1u);
+        }
       }
     }
+    score_item_done(s_h, u, c, a.k, h0, h1, st);
   }
 }
 
@@ -288,11 +329,15 @@ constexpr int kScoreItem = 1024;
 
 template <int G>
 __global__ __launch_bounds__(256) void score_mfma_kernel(LayerArgs a, const uint16_t* __restrict__ q, Span sp,
-                                                         uint32_t* __restrict__ keys, uint32_t* __restrict__ counter) {
+                                                         uint32_t* __restrict__ keys, uint32_t* __restrict__ counter,
+                                                         uint32_t* __restrict__ h0, uint32_t* __restrict__ h1,
+                                                         TopkState* __restrict__ st) {
   constexpr int TILES = 8;                         // 16-key tiles per wave iteration (128 keys)
   constexpr int kKeysPerWave = kScoreItem / 4;     // 256
   static_assert(G <= 8, "group of at most 8 query heads");
   __shared__ uint32_t s_item;
+  __shared__ uint32_t s_h[4][256];
+  clear_score_hist(s_h);
   const int nch = (int)((a.N + kScoreItem - 1) / kScoreItem);
   const int lo = *sp.lo;
   const int64_t items = (int64_t)(*sp.hi - lo) * nch;
@@ -367,27 +412,43 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(LayerArgs a, const uint
           if (ks == t) v = x;
         }
         const int64_t key = w_begin + t0 + t4 * 16 + lane;
-        if (key < a.N) kout[key] = score_key(v);
+        if (key < a.N) {
+          const uint32_t sk = score_key(v);
+          kout[key] = sk;
+          atomicAdd(&s_h[wave][sk >> 24], 1u);
+        }
       }
     }
+    score_item_done(s_h, u, c, a.k, h0, h1, st);
   }
 }
 
 // ---------------------------------------------------------------- A3 top-k
-// Exact radix select over each miss unit's order-preserving score keys, spread
-// over chunk blocks so that a unit with a long context is selected by many CUs:
-//   topk_init_kernel   per unit: zero the global histogram, prefix = 0, rem = k
-//   topk_pass_kernel   x4, 8 bits each, MSB first: every chunk block builds an
-//                      LDS histogram of its keys that match the prefix so far and
-//                      adds it to the unit's global histogram; the last block to
-//                      finish (atomic counter) picks the digit holding the
-//                      rem-th largest key, extends the prefix and clears the
-//                      histogram.  After four passes prefix = T, the k-th largest
-//                      key, and rem = how many keys equal to T are taken.
-//   topk_count_kernel  per chunk: keys > T and keys == T
-//   topk_write_kernel  per chunk: offsets from the counts of earlier chunks, then
-//                      a block scan writes the winners (keys > T, and the first
-//                      rem keys == T by index) in ascending index order.
+// Exact radix select over each miss unit's order-preserving score keys, four
+// 8-bit digits from the most significant one.  For a digit position, a
+// histogram of the keys that match the digits fixed so far gives the digit of
+// the k-th largest key (pick_digit); after four digits, T = the k-th largest key
+// and `rem` = how many keys equal to T are taken (the first rem by index, the
+// tie rule).  The winners (keys > T, then those rem keys == T) are written in
+// ascending index order.
+//
+//   scoring          digit 1 histogram of every miss unit (H0), built in LDS
+//                    while the keys are produced and added per work item
+//   single block     contexts of fewer than kTopkMultiMin chunks: one 1024-
+//   (topk_unit)      thread block per unit takes digit 1 from H0 and runs
+//                    digits 2-4 and the write itself
+//   multi block      one 256-thread block per chunk of kTopkChunk keys:
+//   (topk_pass x3)   digit 2 (every block takes digit 1 from H0 first), digit 3,
+//                    digit 4; each block adds its LDS histogram to the unit's
+//                    global one, and the last block of the unit to finish (an
+//                    atomic done count) picks the digit.  The digit-4 pass also
+//                    stores each chunk's own histogram and count of keys above
+//                    the 24-bit prefix, from which every chunk's output offset
+//                    follows once T is known.
+//   (topk_write)     per chunk: offset from the earlier chunks' histograms,
+//                    then a block scan writes the winners.
+// H0 is cleared by the compaction kernel; H1 and the per-unit state by the
+// scoring block that takes a unit's first work item.
 constexpr int kTopkThreads = 256;
 // Contexts of at least this many chunks (N >= 131072) take the multi-block
 // path; shorter ones a single block per unit (fewer launches, and the many
@@ -396,6 +457,39 @@ constexpr int kTopkThreads = 256;
 // 0.84 ms; 128 units at N = 32768 in 0.29 ms (single block) vs 0.31 ms.
 constexpr int kTopkMultiMin = 8;
 constexpr int kTopkUnroll = 4;     // 16-byte key loads in flight per thread
+
+// One full wave: the digit d whose bin holds the rem-th largest of the counted
+// keys (bins scanned from 255 down) and `above` = the count in bins above d.
+// Lane l reads bins 4l..4l+3 of h (LDS); every lane returns the same values.
+// If fewer than rem keys were counted, d = 0 (cannot happen for valid counts).
+__device__ __forceinline__ void pick_digit(const uint32_t* h, uint32_t rem, uint32_t& digit, uint32_t& above) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t b0 = h[4 * lane], b1 = h[4 * lane + 1], b2 = h[4 * lane + 2], b3 = h[4 * lane + 3];
+  const uint32_t s = b0 + b1 + b2 + b3;
+  uint32_t S = s;  // keys in bins >= 4 lane
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(S, off, 64);
+    if (lane + off < 64) S += y;
+  }
+  // S does not increase with the lane, so the lanes with S >= rem are 0..L
+  const uint64_t m = __ballot(S >= rem);
+  const int L = m ? 63 - __builtin_clzll(m) : 0;
+  uint32_t acc = __shfl(S - s, L, 64);
+  const uint32_t c3 = __shfl(b3, L, 64), c2 = __shfl(b2, L, 64), c1 = __shfl(b1, L, 64);
+  uint32_t d = 4u * (uint32_t)L;
+  if (acc + c3 >= rem) {
+    d += 3;
+  } else if ((acc += c3) + c2 >= rem) {
+    d += 2;
+  } else if ((acc += c2) + c1 >= rem) {
+    d += 1;
+  } else {
+    acc += c1;
+  }
+  digit = d;
+  above = acc;
+}
 
 struct UnitChunk {
   int u, c;
@@ -413,21 +507,41 @@ __device__ __forceinline__ UnitChunk unit_chunk(const Span& sp, int cmax) {
   return r;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_init_kernel(LayerArgs a, Span sp, uint32_t* __restrict__ ghist,
-                                                                 TopkState* __restrict__ st) {
-  const int lo = *sp.lo;
-  if ((int)blockIdx.x >= *sp.hi - lo) return;
-  const int u = sp.list[lo + blockIdx.x];
-  ghist[(int64_t)u * 256 + threadIdx.x] = 0u;
-  if (threadIdx.x == 0) st[u] = TopkState{0u, 0u, (uint32_t)a.k, 0u};
+// Block-wide sums of two per-thread counts (256 threads); every thread gets both.
+__device__ __forceinline__ void block_sum2(uint32_t x, uint32_t y, uint32_t* s_x, uint32_t* s_y, uint32_t& tx,
+                                           uint32_t& ty) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    x += __shfl_xor(x, off, 64);
+    y += __shfl_xor(y, off, 64);
+  }
+  if (lane == 0) {
+    s_x[wave] = x;
+    s_y[wave] = y;
+  }
+  __syncthreads();
+  tx = 0;
+  ty = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / 64; ++w) {
+    tx += s_x[w];
+    ty += s_y[w];
+  }
+  __syncthreads();
 }
 
+// Digit pass over one chunk of one unit (shift 16, 8 or 0).  Histograms: digit 2
+// and digit 4 accumulate in H1, digit 3 in H0 (which the digit-2 pass clears
+// once every block has read digit 1 from it).
 __global__ __launch_bounds__(kTopkThreads) void topk_pass_kernel(LayerArgs a, Span sp,
                                                                  const uint32_t* __restrict__ keys,
-                                                                 uint32_t* __restrict__ ghist,
-                                                                 TopkState* __restrict__ st, int cmax, int shift) {
+                                                                 uint32_t* __restrict__ h0, uint32_t* __restrict__ h1,
+                                                                 TopkState* __restrict__ st,
+                                                                 uint32_t* __restrict__ chist, int cmax, int shift) {
   __shared__ uint32_t hist[kTopkThreads / 64][256];
   __shared__ uint32_t tot[256];
+  __shared__ uint32_t s_prefix, s_mask, s_rem, s_x[4], s_y[4];
   __shared__ int s_last;
   const UnitChunk uc = unit_chunk(sp, cmax);
   if (!uc.valid) return;
@@ -436,9 +550,31 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pass_kernel(LayerArgs a, Sp
   const int64_t c0 = (int64_t)uc.c * kTopkChunk;
   const int64_t c1 = (c0 + kTopkChunk < N) ? c0 + kTopkChunk : N;
   const uint32_t* kk = keys + (int64_t)uc.u * a.Np;
-  const uint32_t prefix = st[uc.u].prefix, mask = st[uc.u].mask;
+  uint32_t* h0u = h0 + (int64_t)uc.u * 256;
+  uint32_t* h1u = h1 + (int64_t)uc.u * 256;
+  uint32_t* acc_h = shift == 8 ? h0u : h1u;
+  if (shift == 16) {
+    // digit 1 from the scoring histogram
+    tot[tid] = h0u[tid];
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t d, above;
+      pick_digit(tot, (uint32_t)a.k, d, above);
+      if (tid == 0) {
+        s_prefix = d << 24;
+        s_mask = 0xFF000000u;
+        s_rem = (uint32_t)a.k - above;
+      }
+    }
+  } else if (tid == 0) {
+    s_prefix = st[uc.u].prefix;
+    s_mask = st[uc.u].mask;
+    s_rem = st[uc.u].rem;
+  }
   for (int i = tid; i < (kTopkThreads / 64) * 256; i += kTopkThreads) (&hist[0][0])[i] = 0u;
   __syncthreads();
+  const uint32_t prefix = s_prefix, mask = s_mask;
+  uint32_t gt = 0;  // digit-4 pass: keys whose fixed 24 bits exceed the prefix
   constexpr int kStep = kTopkThreads * 4;
   for (int64_t base = c0 + (int64_t)tid * 4; base < c1; base += (int64_t)kStep * kTopkUnroll) {
     u32x4 v[kTopkUnroll];
@@ -452,22 +588,27 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pass_kernel(LayerArgs a, Sp
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t kv = v[j][e];
-        if (base + (int64_t)j * kStep + e < c1 && (kv & mask) == prefix)
-          atomicAdd(&hist[wave][(kv >> shift) & 255u], 1u);
+        const bool valid = base + (int64_t)j * kStep + e < c1;
+        if (valid && (kv & mask) == prefix) atomicAdd(&hist[wave][(kv >> shift) & 255u], 1u);
+        gt += valid && (kv & mask) > prefix;
       }
   }
   __syncthreads();
   {
-    uint32_t sum = 0;
-#pragma unroll
-    for (int w = 0; w < kTopkThreads / 64; ++w) sum += hist[w][tid];
-    if (sum) atomicAdd(&ghist[(int64_t)uc.u * 256 + tid], sum);
+    const uint32_t sum = hist[0][tid] + hist[1][tid] + hist[2][tid] + hist[3][tid];
+    if (sum) atomicAdd(&acc_h[tid], sum);
+    if (shift == 0) chist[((int64_t)uc.u * cmax + uc.c) * kChunkHist + tid] = sum;
+  }
+  if (shift == 0) {
+    uint32_t g, unused;
+    block_sum2(gt, 0u, s_x, s_y, g, unused);
+    if (tid == 0) chist[((int64_t)uc.u * cmax + uc.c) * kChunkHist + 256] = g;
   }
   // Device-scope atomics are performed at the device's point of coherence; once
   // this thread's adds are acknowledged they are visible to every block, so
   // waiting for the acknowledgements before the done count suffices.  (A
   // __threadfence here would write back and invalidate the whole L2 of this
-  // XCD in every block of every pass.)
+  // XCD in every block.)
   wait_vm_acks();
   __syncthreads();
   if (tid == 0) {
@@ -478,29 +619,27 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pass_kernel(LayerArgs a, Sp
   if (!s_last) return;
   // last block of this unit: every other block's adds were acknowledged before
   // its done increment; the totals are read with device-scope atomic loads
-  uint32_t* gh = ghist + (int64_t)uc.u * 256;
-  tot[tid] = __hip_atomic_load(gh + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  gh[tid] = 0u;
+  tot[tid] = __hip_atomic_load(acc_h + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  acc_h[tid] = 0u;
+  if (shift == 16) h0u[tid] = 0u;  // every block has read digit 1 from it
   __syncthreads();
-  if (tid == 0) {
-    const uint32_t rem = st[uc.u].rem;
-    uint32_t acc = 0;
-    int dg = 255;
-    for (; dg > 0; --dg) {
-      if (acc + tot[dg] >= rem) break;
-      acc += tot[dg];
-    }
-    st[uc.u] = TopkState{prefix | ((uint32_t)dg << shift), mask | (255u << shift), rem - acc, 0u};
+  if (wave == 0) {
+    uint32_t d, above;
+    pick_digit(tot, s_rem, d, above);
+    if (tid == 0)
+      st[uc.u] = TopkState{prefix | (d << shift), mask | (255u << shift), s_rem - above, 0u};
   }
 }
 
-// Short contexts: one 1024-thread block per miss unit runs the four passes and
-// the compaction itself (one launch; many units keep many CUs busy).
+// Short contexts: one 1024-thread block per miss unit takes digit 1 from H0
+// and runs digits 2-4 and the compaction itself (one launch; many units keep
+// many CUs busy).
 constexpr int kUnitThreads = 1024;
 constexpr int kUnitPerThread = 16;
 
 __global__ __launch_bounds__(kUnitThreads) void topk_unit_kernel(LayerArgs a, Span sp,
-                                                                 const uint32_t* __restrict__ keys) {
+                                                                 const uint32_t* __restrict__ keys,
+                                                                 const uint32_t* __restrict__ h0) {
   __shared__ uint32_t hist[16][256];
   __shared__ uint32_t tot[256];
   __shared__ uint32_t s_prefix, s_mask, s_rem, s_base_gt, s_base_eq;
@@ -514,13 +653,18 @@ __global__ __launch_bounds__(kUnitThreads) void topk_unit_kernel(LayerArgs a, Sp
     const int u = list[it];
     const uint32_t* kk = keys + (int64_t)u * a.Np;
     int32_t* out = a.idx + (int64_t)u * a.k;
-    if (tid == 0) {
-      s_prefix = 0u;
-      s_mask = 0u;
-      s_rem = (uint32_t)a.k;
+    if (tid < 256) tot[tid] = h0[(int64_t)u * 256 + tid];
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t d, above;
+      pick_digit(tot, (uint32_t)a.k, d, above);
+      if (tid == 0) {
+        s_prefix = d << 24;
+        s_mask = 0xFF000000u;
+        s_rem = (uint32_t)a.k - above;
+      }
     }
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
+    for (int shift = 16; shift >= 0; shift -= 8) {
       for (int i = tid; i < 16 * 256; i += kUnitThreads) (&hist[0][0])[i] = 0u;
       __syncthreads();
       const uint32_t prefix = s_prefix, mask = s_mask;
@@ -548,17 +692,14 @@ __global__ __launch_bounds__(kUnitThreads) void topk_unit_kernel(LayerArgs a, Sp
         tot[tid] = sum;
       }
       __syncthreads();
-      if (tid == 0) {
-        const uint32_t rem = s_rem;
-        uint32_t acc = 0;
-        int dg = 255;
-        for (; dg > 0; --dg) {
-          if (acc + tot[dg] >= rem) break;
-          acc += tot[dg];
+      if (wave == 0) {
+        uint32_t d, above;
+        pick_digit(tot, s_rem, d, above);
+        if (tid == 0) {
+          s_rem -= above;
+          s_prefix = prefix | (d << shift);
+          s_mask = mask | (255u << shift);
         }
-        s_rem = rem - acc;
-        s_prefix = prefix | ((uint32_t)dg << shift);
-        s_mask = mask | (255u << shift);
       }
       __syncthreads();
     }
@@ -662,66 +803,40 @@ __device__ __forceinline__ void scan2(uint32_t cg, uint32_t ce, uint32_t* s_wg, 
   __syncthreads();
 }
 
-constexpr int kTopkPerThread = 16;  // consecutive keys per thread per tile in count / write
-
-__global__ __launch_bounds__(kTopkThreads) void topk_count_kernel(LayerArgs a, Span sp,
-                                                                  const uint32_t* __restrict__ keys,
-                                                                  const TopkState* __restrict__ st,
-                                                                  uint32_t* __restrict__ tcount, int cmax) {
-  __shared__ uint32_t s_wg[kTopkThreads / 64], s_we[kTopkThreads / 64];
-  const UnitChunk uc = unit_chunk(sp, cmax);
-  if (!uc.valid) return;
-  const int64_t N = a.N;
-  const int64_t c0 = (int64_t)uc.c * kTopkChunk;
-  const int64_t c1 = (c0 + kTopkChunk < N) ? c0 + kTopkChunk : N;
-  const uint32_t* kk = keys + (int64_t)uc.u * a.Np;
-  const uint32_t T = st[uc.u].prefix;
-  uint32_t cg = 0, ce = 0;
-  for (int64_t base = c0 + (int64_t)threadIdx.x * 4; base < c1; base += (int64_t)kTopkThreads * 4 * kTopkUnroll) {
-    u32x4 v[kTopkUnroll];
-#pragma unroll
-    for (int j = 0; j < kTopkUnroll; ++j) {
-      const int64_t i = base + (int64_t)j * kTopkThreads * 4;
-      v[j] = i < c1 ? *reinterpret_cast<const u32x4*>(kk + i) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < kTopkUnroll; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool valid = base + (int64_t)j * kTopkThreads * 4 + e < c1;
-        cg += valid && v[j][e] > T;
-        ce += valid && v[j][e] == T;
-      }
-  }
-  uint32_t eg, ee, tg, te;
-  scan2(cg, ce, s_wg, s_we, eg, ee, tg, te);
-  if (threadIdx.x == 0) {
-    tcount[((int64_t)uc.u * cmax + uc.c) * 2] = tg;
-    tcount[((int64_t)uc.u * cmax + uc.c) * 2 + 1] = te;
-  }
-}
+constexpr int kTopkPerThread = 16;  // consecutive keys per thread per tile in the write
 
 __global__ __launch_bounds__(kTopkThreads) void topk_write_kernel(LayerArgs a, Span sp,
                                                                   const uint32_t* __restrict__ keys,
                                                                   const TopkState* __restrict__ st,
-                                                                  const uint32_t* __restrict__ tcount, int cmax) {
+                                                                  const uint32_t* __restrict__ chist, int cmax) {
   __shared__ uint32_t s_wg[kTopkThreads / 64], s_we[kTopkThreads / 64];
   const UnitChunk uc = unit_chunk(sp, cmax);
   if (!uc.valid) return;
+  const int tid = threadIdx.x;
   const int64_t N = a.N;
   const int64_t c0 = (int64_t)uc.c * kTopkChunk;
   const int64_t c1 = (c0 + kTopkChunk < N) ? c0 + kTopkChunk : N;
   const uint32_t* kk = keys + (int64_t)uc.u * a.Np;
   int32_t* out = a.idx + (int64_t)uc.u * a.k;
   const uint32_t T = st[uc.u].prefix, need = st[uc.u].rem;
-  uint32_t base_g = 0, base_e = 0;
-  for (int c = 0; c < uc.c; ++c) {
-    base_g += tcount[((int64_t)uc.u * cmax + c) * 2];
-    base_e += tcount[((int64_t)uc.u * cmax + c) * 2 + 1];
+  const uint32_t D = T & 255u;
+  // winners before this chunk: each earlier chunk's keys above the 24-bit
+  // prefix of T, plus its digit-4 bins above D (> T) and at D (== T)
+  uint32_t base_g, base_e;
+  {
+    uint32_t sg = 0, se = 0;
+    const uint32_t* ch = chist + (int64_t)uc.u * cmax * kChunkHist;
+    for (int c = 0; c < uc.c; ++c) {
+      const uint32_t v = ch[(int64_t)c * kChunkHist + tid];
+      sg += (uint32_t)tid > D ? v : 0u;
+      se += (uint32_t)tid == D ? v : 0u;
+      if (tid == 0) sg += ch[(int64_t)c * kChunkHist + 256];
+    }
+    block_sum2(sg, se, s_wg, s_we, base_g, base_e);
   }
   constexpr int kTile = kTopkThreads * kTopkPerThread;
   for (int64_t t0 = c0; t0 < c1; t0 += kTile) {
-    const int64_t i0 = t0 + (int64_t)threadIdx.x * kTopkPerThread;
+    const int64_t i0 = t0 + (int64_t)tid * kTopkPerThread;
     u32x4 v[kTopkPerThread / 4];
 #pragma unroll
     for (int j = 0; j < kTopkPerThread / 4; ++j)
@@ -1104,24 +1219,26 @@ hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, u
 
 hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, int ranges, hipStream_t s) {
   compact_kernel<<<1, 1024, 0, s>>>(reuse, a.B * a.Hkv, a.Hkv, a.pmask, ranges, w.meta, w.list_all, w.list_host,
-                                    w.list_hit);
+                                    w.list_hit, w.h0);
   return hipGetLastError();
 }
 
-hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_units, uint32_t* keys,
+hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_units, const Workspace& w,
                         uint32_t* counter, int num_cu, hipStream_t s) {
+  uint32_t* keys = w.keys;
   return dispatch_group(a.G, [&](auto gc) {
     constexpr int G = decltype(gc)::value;
     if (a.dtype == CLO_F32) {
       const int64_t nch = (a.N + kScoreChunk - 1) / kScoreChunk;
       const int grid = grid_cap(max_units * nch, (int64_t)num_cu * 32);
-      score_kernel<float, G><<<grid, 256, 0, s>>>(a, static_cast<const float*>(q), sp, keys);
+      score_kernel<float, G><<<grid, 256, 0, s>>>(a, static_cast<const float*>(q), sp, keys, w.h0, w.h1, w.tstate);
     } else {
       // persistent: two blocks (eight waves) per CU keep enough 16-byte loads in
       // flight to stream K; more blocks only add contention
       const int64_t nch = (a.N + kScoreItem - 1) / kScoreItem;
       const int grid = grid_cap(max_units * nch, (int64_t)num_cu * 2);
-      score_mfma_kernel<G><<<grid, 256, 0, s>>>(a, static_cast<const uint16_t*>(q), sp, keys, counter);
+      score_mfma_kernel<G><<<grid, 256, 0, s>>>(a, static_cast<const uint16_t*>(q), sp, keys, counter, w.h0, w.h1,
+                                                 w.tstate);
     }
     return hipGetLastError();
   });
@@ -1132,17 +1249,14 @@ hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uin
   const int cmax = w.cmax;
   if (cmax < kTopkMultiMin) {
     const int grid = grid_cap(max_units, 4096);
-    topk_unit_kernel<<<grid, kUnitThreads, 0, s>>>(a, sp, keys);
+    topk_unit_kernel<<<grid, kUnitThreads, 0, s>>>(a, sp, keys, w.h0);
     return hipGetLastError();
   }
   const int64_t grid = max_units * cmax;
-  const unsigned ug = (unsigned)(max_units > 0 ? max_units : 1);
   const unsigned cg = (unsigned)(grid > 0 ? grid : 1);
-  topk_init_kernel<<<ug, kTopkThreads, 0, s>>>(a, sp, w.ghist, w.tstate);
-  for (int pass = 0; pass < 4; ++pass)
-    topk_pass_kernel<<<cg, kTopkThreads, 0, s>>>(a, sp, keys, w.ghist, w.tstate, cmax, 24 - 8 * pass);
-  topk_count_kernel<<<cg, kTopkThreads, 0, s>>>(a, sp, keys, w.tstate, w.tcount, cmax);
-  topk_write_kernel<<<cg, kTopkThreads, 0, s>>>(a, sp, keys, w.tstate, w.tcount, cmax);
+  for (int shift = 16; shift >= 0; shift -= 8)
+    topk_pass_kernel<<<cg, kTopkThreads, 0, s>>>(a, sp, keys, w.h0, w.h1, w.tstate, w.chist, cmax, shift);
+  topk_write_kernel<<<cg, kTopkThreads, 0, s>>>(a, sp, keys, w.tstate, w.chist, cmax);
   return hipGetLastError();
 }
 
