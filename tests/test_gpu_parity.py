@@ -35,6 +35,8 @@ CASES = {
     "bf16_g5_multiblock": dict(batch=1, hq=10, hkv=2, context=270000, topk=27000, dtype="bf16",
                                persistent=[0, 1], heavy_frac=0.005),
     "f32_g4_multiblock": dict(batch=2, hq=8, hkv=2, context=262145, topk=26215, dtype="f32", persistent=[1, 0]),
+    # 24 attention chunks, merged by two chunk groups
+    "bf16_g4_two_groups": dict(batch=2, hq=8, hkv=2, context=60001, topk=6001, dtype="bf16", persistent=[1, 0]),
     # either side of the switch between the single-block and the multi-block top-k
     # (7 chunks of 16384 keys; 7 chunks and one key)
     "bf16_g4_single_at_switch": dict(batch=1, hq=8, hkv=2, context=114688, topk=11469, dtype="bf16",

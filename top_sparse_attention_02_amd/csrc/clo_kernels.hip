@@ -1133,31 +1133,37 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
   }
 }
 
-// Merge the chunk partials of one (unit, head): one thread per output column,
-// online max/sum rescaling over the chunks, kAttnBatch chunks' partials loaded
-// before any is used.
-template <typename T>
-__global__ __launch_bounds__(128) void attn_combine_kernel(LayerArgs a, const float* __restrict__ part, int nch,
-                                                           T* __restrict__ out) {
+// Merge the chunk partials of one (unit, head) with the usual max/sum
+// rescaling.  S groups of 128 threads (one per output column) each merge a
+// contiguous run of the chunks, kAttnBatch chunks' partials loaded before any is
+// used; group 0 then merges the S group results from LDS.  Long selections
+// (many chunks, few units) take S up to 8, so that no single thread walks
+// hundreds of chunks one load latency after another.
+template <typename T, int S>
+__global__ __launch_bounds__(128 * S) void attn_combine_kernel(LayerArgs a, const float* __restrict__ part, int nch,
+                                                               T* __restrict__ out) {
+  __shared__ float sM[S], sL[S], sO[S][kHeadDim];
   const int G = a.G;
   const int u = blockIdx.x / G, g = blockIdx.x % G;
   const int b = u / a.Hkv, h = u % a.Hkv;
-  const int col = threadIdx.x;
+  const int grp = threadIdx.x / kHeadDim, col = threadIdx.x % kHeadDim;
+  const int per = (nch + S - 1) / S;
+  const int cb = grp * per, ce = (cb + per < nch) ? cb + per : nch;
   const float* p = part + ((int64_t)u * nch * G + g) * kPartStride;
   const int64_t cstride = (int64_t)G * kPartStride;
   float M = kNegInf, L = 0.f, O = 0.f;
-  for (int c0 = 0; c0 < nch; c0 += kAttnBatch) {
+  for (int c0 = cb; c0 < ce; c0 += kAttnBatch) {
     float m[kAttnBatch], l[kAttnBatch], o[kAttnBatch];
 #pragma unroll
     for (int j = 0; j < kAttnBatch; ++j) {
-      const int c = c0 + j < nch ? c0 + j : nch - 1;
+      const int c = c0 + j < ce ? c0 + j : ce - 1;
       m[j] = p[c * cstride + kHeadDim];
       l[j] = p[c * cstride + kHeadDim + 1];
       o[j] = p[c * cstride + col];
     }
 #pragma unroll
     for (int j = 0; j < kAttnBatch; ++j) {
-      if (c0 + j >= nch) break;
+      if (c0 + j >= ce) break;
       const float Mn = fmaxf(M, m[j]);
       const float sa = expf(M - Mn), sb = expf(m[j] - Mn);
       L = L * sa + l[j] * sb;
@@ -1165,7 +1171,29 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(LayerArgs a, const fl
       M = Mn;
     }
   }
-  store_out(out + ((int64_t)b * a.Hq + (int64_t)h * G + g) * kHeadDim + col, O / L);
+  if (S == 1) {
+    store_out(out + ((int64_t)b * a.Hq + (int64_t)h * G + g) * kHeadDim + col, O / L);
+    return;
+  }
+  if (col == 0) {
+    sM[grp] = M;
+    sL[grp] = L;
+  }
+  sO[grp][col] = O;
+  __syncthreads();
+  if (grp != 0) return;
+  // group 0 holds at least one chunk, so Mx is finite; empty groups (M = -inf) weigh 0
+  float Mx = sM[0];
+#pragma unroll
+  for (int i = 1; i < S; ++i) Mx = fmaxf(Mx, sM[i]);
+  float Lt = 0.f, Ot = 0.f;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const float w = expf(sM[i] - Mx);
+    Lt += sL[i] * w;
+    Ot += sO[i][col] * w;
+  }
+  store_out(out + ((int64_t)b * a.Hq + (int64_t)h * G + g) * kHeadDim + col, Ot / Lt);
 }
 
 // ---------------------------------------------------------------- device-side flags
@@ -1293,10 +1321,21 @@ hipError_t launch_attn_partial(const LayerArgs& a, const void* q, float* part, S
 hipError_t launch_attn_combine(const LayerArgs& a, const float* part, void* out, hipStream_t s) {
   const int nch = (int)((a.k + kAttnChunk - 1) / kAttnChunk);
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hkv * a.G);
-  if (a.dtype == CLO_F32)
-    attn_combine_kernel<float><<<grid, 128, 0, s>>>(a, part, nch, static_cast<float*>(out));
-  else
-    attn_combine_kernel<uint16_t><<<grid, 128, 0, s>>>(a, part, nch, static_cast<uint16_t*>(out));
+  // chunk groups: about 16 or more chunks each
+  const int S = nch > 64 ? 8 : nch > 32 ? 4 : nch > 16 ? 2 : 1;
+  auto go = [&](auto sc) {
+    constexpr int SG = decltype(sc)::value;
+    if (a.dtype == CLO_F32)
+      attn_combine_kernel<float, SG><<<grid, 128 * SG, 0, s>>>(a, part, nch, static_cast<float*>(out));
+    else
+      attn_combine_kernel<uint16_t, SG><<<grid, 128 * SG, 0, s>>>(a, part, nch, static_cast<uint16_t*>(out));
+  };
+  switch (S) {
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    default: go(std::integral_constant<int, 8>{}); break;
+  }
   return hipGetLastError();
 }
 
