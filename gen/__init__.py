@@ -30,7 +30,7 @@ _lib = None
 MASK64 = (1 << 64) - 1
 
 # tensor tags for key derivation
-TAG_Q, TAG_QPREV, TAG_K, TAG_V, TAG_HEAVY, TAG_PERSIST, TAG_LOW, TAG_COS = range(1, 9)
+TAG_Q, TAG_QPREV, TAG_K, TAG_V, TAG_HEAVY, TAG_PERSIST, TAG_LOW, TAG_COS, TAG_WALK = range(1, 10)
 
 F32, BF16 = "f32", "bf16"
 
@@ -167,6 +167,7 @@ class Problem:
     data_layers: Optional[int] = None  # K/V of layer l are those of layer l % data_layers
     k_resample: Dict[Tuple[int, int, int], Dict[int, int]] = field(default_factory=dict)
     qprev_round: Dict[Tuple[int, int, int], int] = field(default_factory=dict)
+    walk_round: Dict[Tuple[int, int, int, int], int] = field(default_factory=dict)
 
     def __post_init__(self):
         assert self.hq % self.hkv == 0
@@ -255,6 +256,53 @@ class Problem:
                 else:
                     raise ValueError(self.qprev_model)
         return round_to(out, self.dtype)
+
+    # ---- many decode steps ----------------------------------------------
+    def walk_cos(self, layer: int, b: int, kvh: int, t: int) -> float:
+        """Target cosine between a unit's query groups at steps t-1 and t: the
+        80/20 model drawn afresh per (unit, step) -- "low" with probability
+        low_frac, uniform in the class's range."""
+        u = uniform_stream(derive_key(self.seed, TAG_WALK, layer, b, kvh, t), 2)
+        lo, hi = self.low_range if u[0] < self.low_frac else self.high_range
+        return float(lo + (hi - lo) * u[1])
+
+    def q_walk(self, layer: int, t: int) -> np.ndarray:
+        """Query at decode step t of a multi-step run, stored dtype, [B, Hq, d].
+
+        Step 0 is q(layer); step t turns each unit's concatenated query group of
+        step t-1 (its stored values) by the target cosine walk_cos towards a fresh
+        direction orthogonal to it, keeping its norm."""
+        cache = self.__dict__.setdefault("_walk_cache", {})
+        if (layer, t) in cache:
+            return cache[(layer, t)]
+        if t == 0:
+            out = self.q(layer)
+        else:
+            prev = stored_to_f64(self.q_walk(layer, t - 1), self.dtype)
+            res = np.empty_like(prev)
+            g, d = self.g, self.d
+            for b in range(self.batch):
+                for kvh in range(self.hkv):
+                    c = self.walk_cos(layer, b, kvh, t)
+                    r = self.walk_round.get((layer, b, kvh, t), 0)
+                    qg = prev[b, kvh * g:(kvh + 1) * g].reshape(-1)
+                    qn = np.sqrt(np.dot(qg, qg))
+                    qhat = qg / qn
+                    n = normal_stream(derive_key(self.seed, TAG_WALK, layer, b, kvh, t, r + 1), g * d)
+                    w = n - np.dot(n, qhat) * qhat
+                    w /= np.sqrt(np.dot(w, w))
+                    res[b, kvh * g:(kvh + 1) * g] = (qn * (c * qhat + math.sqrt(1 - c * c) * w)).reshape(g, d)
+            out = round_to(res, self.dtype)
+        cache[(layer, t)] = out
+        return out
+
+    def resample_walk(self, layer: int, b: int, kvh: int, t: int) -> None:
+        """Fresh direction for a unit's step-t query (later steps follow from it)."""
+        key = (layer, b, kvh, t)
+        self.walk_round[key] = self.walk_round.get(key, 0) + 1
+        cache = self.__dict__.get("_walk_cache", {})
+        for k in [k for k in cache if k[0] == layer and k[1] >= t]:
+            del cache[k]
 
     # ---- keys and values -----------------------------------------------
     def heavy_rows(self, layer: int, b: int) -> np.ndarray:

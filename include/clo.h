@@ -43,12 +43,12 @@
  *
  * Tensor layouts (row-major, element type = shape->dtype unless noted), with
  * P = number of persistent KV heads (bits set in persistent_mask), H = n_kv_heads - P,
- * and "slot" = a head's rank among the persistent (or non-persistent) heads in
- * head order:
+ * C = shape->capacity (or N when 0), and "slot" = a head's rank among the
+ * persistent (or non-persistent) heads in head order:
  *   q, q_prev, out   [B, Hq, d]
- *   k_hbm, v_hbm     [B, P, N, d]   device   full K/V of persistent heads
- *   k_host, v_host   [B, H, N, d]   pinned   full K/V of non-persistent heads
- *   k_score          [B, H, N, d]   device   copy of k_host read by scoring
+ *   k_hbm, v_hbm     [B, P, C, d]   device   full K/V of persistent heads (rows < N used)
+ *   k_host, v_host   [B, H, C, d]   pinned   full K/V of non-persistent heads
+ *   k_score          [B, H, C, d]   device   copy of k_host read by scoring
  *   k_cache, v_cache [B, H, k, d]   device   rows k_host[idx], v_host[idx]
  *   idx              [B, Hkv, k]    int32    selected token indices, ascending
  *   reuse            [B, Hkv]       uint8    1 = reuse (hit), 0 = miss
@@ -85,16 +85,20 @@ typedef struct {
   int64_t topk;        /* k, 1 <= k <= N (the pages use k = ceil(N / 10)) */
   float tau;           /* reuse threshold: reuse when cos >= tau; +inf forces every unit to miss */
   int32_t dtype;       /* clo_dtype of q, q_prev, K, V, caches and out */
+  int64_t capacity;    /* rows allocated per (sequence, head) in k_hbm, v_hbm, k_host, v_host and
+                          k_score: the row stride of those tensors.  0 = context.  A context that
+                          grows during decoding (clo_append_kv) keeps capacity fixed and raises
+                          context; only rows 0..context-1 are read. */
 } clo_shape;
 
 /* Where one layer's keys, values, selections and cached rows live. */
 typedef struct {
   uint64_t persistent_mask;  /* bit h set: KV head h keeps its full K/V in HBM (same for all sequences) */
-  const void* k_hbm;         /* [B, P, N, d] device; may be NULL when P == 0 */
+  const void* k_hbm;         /* [B, P, C, d] device; may be NULL when P == 0 */
   const void* v_hbm;
-  const void* k_host;        /* [B, H, N, d] pinned host; may be NULL when H == 0 */
+  const void* k_host;        /* [B, H, C, d] pinned host; may be NULL when H == 0 */
   const void* v_host;
-  const void* k_score;       /* [B, H, N, d] device copy of k_host, read by scoring */
+  const void* k_score;       /* [B, H, C, d] device copy of k_host, read by scoring */
   void* k_cache;             /* [B, H, k, d] device, written for miss units, read by attention */
   void* v_cache;
   int32_t* idx;              /* [B, Hkv, k] device, written for miss units, read for all units */
@@ -192,6 +196,34 @@ clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const
 clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const void* q,
                            const void* q_prev, void* out, uint8_t* reuse, float* cos,
                            void* ws, size_t ws_bytes, const clo_sync* sync, void* stream);
+
+/*
+ * Multi-step decoding with a growing context -- appending the decoded token
+ * (synthesis section 5.6 on incremental offloading: new KV goes to host memory
+ * as it is produced; abstract feature (3): the GPU moves KV without CPU work).
+ * Writes k_new[b][h] and v_new[b][h] ([B, Hkv, d] device, dtype of the shape)
+ * as row `position` of every (sequence, KV head): into k_hbm/v_hbm for
+ * persistent heads; for the others into k_host/v_host, stored by the GPU
+ * straight into pinned host memory, and into the k_score copy.  Requires
+ * 0 <= position < capacity (CLO_E_ARG otherwise); shape->context is not used
+ * beyond validation and the row is visible to later calls on the same stream
+ * (a decode step with context = position + 1 reads it).  k_cache, v_cache and
+ * idx are not touched.  sync may be NULL.
+ */
+clo_status clo_append_kv(const clo_shape* shape, const clo_layer* layer, const void* k_new, const void* v_new,
+                         int64_t position, const clo_sync* sync, void* stream);
+
+/*
+ * Reference queries for the reuse test across many steps (synthesis section
+ * 2.1 item 2; the pages leave open which earlier query a step is compared
+ * with).  For every unit with reuse[u] == 0 (all units when reuse is NULL),
+ * copies the unit's g query heads of q into q_ref ([B, Hq, d], device, dtype
+ * of the shape); reuse units keep their reference.  Passing q_ref as q_prev to
+ * the next step then compares each unit with the query of its last refresh
+ * instead of the previous step's query.  sync may be NULL.
+ */
+clo_status clo_update_reference(const clo_shape* shape, const void* q, const uint8_t* reuse, void* q_ref,
+                                const clo_sync* sync, void* stream);
 
 /* Static text for a status code. */
 const char* clo_status_string(clo_status status);

@@ -3,6 +3,7 @@ from .clo_oracle import (  # noqa: F401
     as_f64,
     attend,
     decode_layer,
+    decode_steps_unit,
     decode_unit,
     group_cosine,
     reuse_decision,

@@ -31,11 +31,18 @@ Synthesis"; CLO abstract page on fugumt):
   * O5: abstract, features (2) and (3) -- persistent on-GPU heads and
     zero-copy transfers only change where rows come from.
   * O6: synthesis section 2.3 table -- attention is top-k sparse attention.
+  * Multi-step decoding (decode_steps_unit): synthesis section 2.1 item 2 --
+    the similarity is between adjacent decode steps; section 5.6 -- the
+    context grows by the decoded token and new KV is offloaded incrementally.
 The pages print no formulas.  Readings taken where they are silent: the
 cosine spans the concatenated query group (one decision per KV head); the
 comparison is inclusive; the group's score is the max over its heads; ties go
 to the smaller index; attention is scaled dot-product softmax attention over
-the selected rows only, with scale 1/sqrt(d).
+the selected rows only, with scale 1/sqrt(d).  Over many steps: step 0 is a
+cold step (every unit selects); before step t >= 1 one token is appended, so
+step t sees n0 + t keys; k stays fixed; the reuse test compares with either the
+previous step's query ("previous") or the query of the unit's last miss
+("refresh") -- the pages do not say which earlier query is meant.
 
 Every function here is pinned by CPU tests against closed forms, library
 routines for the special cases it reduces to, brute force and invariants.
@@ -154,3 +161,31 @@ def decode_layer(q, q_prev, kv_of: Callable[[int, int], Tuple[np.ndarray, np.nda
         res[(b, kvh)] = decode_unit(qf[b, kvh * g:(kvh + 1) * g], qpf[b, kvh * g:(kvh + 1) * g],
                                     as_f64(K, dtype), as_f64(V, dtype), k, tau, prev)
     return res
+
+
+def decode_steps_unit(queries, K, V, n0: int, k: int, tau: float, policy: str = "previous"):
+    """O1-O6 for one unit over len(queries) decode steps with a growing context.
+
+    queries: the unit's [g, d] query groups q_0, q_1, ... (float64); K, V: the
+    unit's [n0 + T, d] rows (float64), row n0 + t - 1 being the token appended
+    before step t.  Step 0 runs on the first n0 rows with every unit missing
+    (a cold start); step t >= 1 runs on the first n0 + t rows, its reuse test
+    against the reference query, a hit keeping the previous step's selection.
+    The reference is q_{t-1} ("previous") or the query of the unit's last miss
+    ("refresh").  Returns one decode_unit result per step.
+    """
+    if policy not in ("previous", "refresh"):
+        raise ValueError(policy)
+    results = []
+    ref = sel = None
+    for t, qg in enumerate(queries):
+        n = n0 + t
+        if t == 0:
+            r = decode_unit(qg, qg, K[:n], V[:n], k, math.inf)
+        else:
+            r = decode_unit(qg, ref, K[:n], V[:n], k, tau, sel)
+        sel = r["idx"]
+        if policy == "previous" or not r["reuse"]:
+            ref = qg
+        results.append(r)
+    return results

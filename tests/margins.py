@@ -128,3 +128,98 @@ def enforce_margins(problem, layer: int, units=None, extra_ranks=(), max_rounds:
         else:
             raise RuntimeError(f"score margins not reached for unit {(b, h)}")
     return p
+
+
+def _redraw_keeping_sides_pairs(p, layer, b, h, K, pairs, row, bounds, delta, max_tries=2000):
+    """_redraw_keeping_sides for queries that each score only a prefix of the rows
+    (pairs of query group and row count); a row past a prefix is free there.
+
+    With many queries a key that sits above some boundaries and below others (a
+    heavy hitter) rarely finds a draw on the same side of all of them; then the
+    first draw at least delta away from every boundary is taken, on either side.
+    The boundaries may then move by one rank, and the caller checks again."""
+    sides = [[s[row] > t for t in ts] if row < n else None for (s, ts), (_, n) in zip(bounds, pairs)]
+    rnd = p.k_row_round(layer, b, h, row)
+    for keep_sides in (True, False):
+        for _ in range(max_tries):
+            rnd += 1
+            cand = oracle.as_f64(p.k_row_draw(layer, b, h, row, rnd), p.dtype)
+            ok = True
+            for (qg, n), (s, ts), sd in zip(pairs, bounds, sides):
+                if sd is None:
+                    continue
+                sc = float(np.max(qg @ cand))
+                for t, above in zip(ts, sd):
+                    if keep_sides:
+                        good = (sc > t + delta) if above else (sc < t - delta)
+                    else:
+                        good = abs(sc - t) >= delta
+                    if not good:
+                        ok = False
+                        break
+                if not ok:
+                    break
+            if ok:
+                p.set_k_row_round(layer, b, h, row, rnd)
+                K[row] = cand
+                return
+    raise RuntimeError(f"no redraw of key row {row} clears the boundaries")
+
+
+def enforce_walk_margins(problem, layer: int, steps: int, tau=None, max_rounds: int = 40):
+    """Margins for a multi-step run over a growing context (steps 0..steps; step t
+    sees the first context - steps + t key rows and queries with p.q_walk(layer, t)).
+
+    Cosines: step by step, a unit's step-t query is redrawn while its cosine with
+    the previous step's query or with the query of its last miss under the
+    refresh policy lies within 1e-4 of tau (so both reference policies decide
+    with a margin).  Scores: as enforce_margins, for every step's query over the
+    rows present at that step."""
+    p = problem
+    tau = p.tau if tau is None else tau
+    g = p.g
+    n0 = p.context - steps
+    units = [(b, h) for b in range(p.batch) for h in range(p.hkv)]
+    last_miss = {u: 0 for u in units}
+    qf = lambda t: oracle.as_f64(p.q_walk(layer, t), p.dtype)  # noqa: E731
+    for t in range(1, steps + 1):
+        for _ in range(max_rounds):
+            qt, qp = qf(t), qf(t - 1)
+            redo = []
+            for b, h in units:
+                sl = slice(h * g, (h + 1) * g)
+                qr = qf(last_miss[(b, h)])[b, sl]
+                c1 = oracle.group_cosine(qt[b, sl], qp[b, sl])
+                c2 = oracle.group_cosine(qt[b, sl], qr)
+                if abs(c1 - tau) < COS_MARGIN or abs(c2 - tau) < COS_MARGIN:
+                    redo.append((b, h))
+            if not redo:
+                break
+            for b, h in redo:
+                p.resample_walk(layer, b, h, t)
+        else:
+            raise RuntimeError(f"cosine margins not reached at step {t}")
+        qt = qf(t)
+        for b, h in units:
+            sl = slice(h * g, (h + 1) * g)
+            if oracle.group_cosine(qt[b, sl], qf(last_miss[(b, h)])[b, sl]) < tau:
+                last_miss[(b, h)] = t
+    qs = [qf(t) for t in range(steps + 1)]
+    for b, h in units:
+        sl = slice(h * g, (h + 1) * g)
+        pairs = [(qs[t][b, sl], n0 + t) for t in range(steps + 1)]
+        K = oracle.as_f64(p.kv("k", layer, b, h), p.dtype)
+        for _ in range(max_rounds):
+            delta = score_delta([q for q, _ in pairs], K)
+            bounds = [boundaries([q], K[:n], [p.topk])[0] for q, n in pairs]
+            bad = set()
+            for s, ts in bounds:
+                for t in ts:
+                    bad |= set(np.nonzero(np.abs(s - t) < delta)[0].tolist())
+            if not bad:
+                break
+            for row in sorted(bad):
+                _redraw_keeping_sides_pairs(p, layer, b, h, K, pairs, row, bounds, delta)
+        else:
+            raise RuntimeError(f"score margins not reached for unit {(b, h)}")
+    return p

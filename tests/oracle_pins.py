@@ -272,6 +272,79 @@ def pin_two_step_reuse(O):
             assert list(miss[(b, h)]["idx"]) == sorted(np.argsort(-s)[:k].tolist())
 
 
+# ---------------------------------------------------------------- many steps, growing context
+# A 2-D unit (g = 1, d = 2) whose query turns by 30 degrees per step, with three
+# initial key rows and one appended before each step, tau = 0.8.  cos(q_t, q_{t-1})
+# = cos 30 = 0.866 always hits; against the query of the last miss, step 2 sees
+# cos 60 = 0.5 and misses, step 3 sees cos 30 again and hits.
+_S3 = math.sqrt(3.0)
+_WALK_Q = [np.array([[1.0, 0.0]]), np.array([[_S3 / 2, 0.5]]), np.array([[0.5, _S3 / 2]]), np.array([[0.0, 1.0]])]
+_WALK_K = np.array([[1.0, 0.0], [0.0, 1.0], [-1.0, 0.0], [0.5, 0.5], [0.0, 2.0], [-1.0, -1.0]])
+_WALK_V = np.array([[1.0, 0.0], [0.0, 1.0], [5.0, 5.0], [7.0, 7.0], [2.0, 3.0], [9.0, 9.0]])
+
+
+def pin_multistep_reference_policies_k1(O):
+    # k = 1: the output is the selected V row.  Step 0 (rows 0-2, q = (1,0)) selects
+    # row 0.  "previous" hits every step and keeps row 0.  "refresh" misses at step 2,
+    # where the scores of rows 0-4 are 1/2, sqrt3/2, -1/2, (1+sqrt3)/4, sqrt3: the
+    # row appended before step 2 wins; step 3 hits and keeps it.
+    prev = O.decode_steps_unit(_WALK_Q, _WALK_K, _WALK_V, 3, 1, 0.8, "previous")
+    ref = O.decode_steps_unit(_WALK_Q, _WALK_K, _WALK_V, 3, 1, 0.8, "refresh")
+    assert [r["reuse"] for r in prev] == [False, True, True, True]
+    assert [r["reuse"] for r in ref] == [False, True, False, True]
+    assert [list(r["idx"]) for r in prev] == [[0], [0], [0], [0]]
+    assert [list(r["idx"]) for r in ref] == [[0], [0], [4], [4]]
+    for r in prev:
+        assert close(r["out"], [[1.0, 0.0]])
+    for r, want in zip(ref, ([1.0, 0.0], [1.0, 0.0], [2.0, 3.0], [2.0, 3.0])):
+        assert close(r["out"], [want])
+    assert close([r["cos"] for r in ref[1:]], [_S3 / 2, 0.5, _S3 / 2])
+
+
+def pin_multistep_reference_policies_k2(O):
+    # k = 2 (scale 1/sqrt2): with two rows a, b the weights are sigma((l_a - l_b)/sqrt2).
+    r2 = math.sqrt(2.0)
+    prev = O.decode_steps_unit(_WALK_Q, _WALK_K, _WALK_V, 3, 2, 0.8, "previous")
+    ref = O.decode_steps_unit(_WALK_Q, _WALK_K, _WALK_V, 3, 2, 0.8, "refresh")
+    assert [list(r["idx"]) for r in prev] == [[0, 1]] * 4
+    assert [list(r["idx"]) for r in ref] == [[0, 1], [0, 1], [1, 4], [1, 4]]
+    # rows 0 and 1 (V = (1,0), (0,1)): o = (p0, 1 - p0), p0 = sigma((q.r0 - q.r1)/sqrt2)
+    for t, diff in enumerate((1.0, _S3 / 2 - 0.5, 0.5 - _S3 / 2, -1.0)):
+        p0 = sigmoid(diff / r2)
+        assert close(prev[t]["out"], [[p0, 1 - p0]])
+    # refresh, steps 2 and 3: rows 1 and 4 (V = (0,1), (2,3)): o = (2 p4, p1 + 3 p4)
+    for t, (l1, l4) in ((2, (_S3 / 2, _S3)), (3, (1.0, 2.0))):
+        p1 = sigmoid((l1 - l4) / r2)
+        p4 = 1 - p1
+        assert close(ref[t]["out"], [[2 * p4, p1 + 3 * p4]])
+
+
+def pin_multistep_limits(O):
+    # tau = +inf: every step selects afresh over the keys present at that step
+    # (brute force) and attends them (torch SDPA); tau = -1.5: every later step
+    # keeps step 0's selection and attends it with its own query.
+    rng = np.random.default_rng(11)
+    g, d, n0, T, k = 3, 16, 40, 5, 6
+    K = rng.standard_normal((n0 + T, d))
+    V = rng.standard_normal((n0 + T, d))
+    qs = [rng.standard_normal((g, d)) for _ in range(T + 1)]
+    for policy in ("previous", "refresh"):
+        fresh = O.decode_steps_unit(qs, K, V, n0, k, float("inf"), policy)
+        keep = O.decode_steps_unit(qs, K, V, n0, k, -1.5, policy)
+        s0 = np.max(K[:n0] @ qs[0].T, axis=1)
+        sel0 = sorted(np.argsort(-s0)[:k].tolist())
+        for t in range(T + 1):
+            s = np.max(K[:n0 + t] @ qs[t].T, axis=1)
+            sel = sorted(np.argsort(-s)[:k].tolist())
+            assert fresh[t]["reuse"] is False and list(fresh[t]["idx"]) == sel
+            ref = _sdpa_dense(qs[t][None], K[None, None, sel], V[None, None, sel])
+            assert close(fresh[t]["out"], ref[0], 1e-10)
+            assert list(keep[t]["idx"]) == sel0
+            assert keep[t]["reuse"] is (t > 0)
+            ref = _sdpa_dense(qs[t][None], K[None, None, sel0], V[None, None, sel0])
+            assert close(keep[t]["out"], ref[0], 1e-10)
+
+
 def pin_bf16_decoding(O):
     # IEEE facts about bfloat16 bit patterns
     bits = np.array([0x3F80, 0xC000, 0x3FC0, 0x0000, 0x8000, 0x7F7F, 0x0001, 0x4049], dtype=np.uint16)
@@ -299,5 +372,8 @@ ALL_PINS = [
     pin_dense_limit_gqa,
     pin_sparse_equals_dense_on_selection,
     pin_two_step_reuse,
+    pin_multistep_reference_policies_k1,
+    pin_multistep_reference_policies_k2,
+    pin_multistep_limits,
     pin_bf16_decoding,
 ]

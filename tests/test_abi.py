@@ -101,3 +101,26 @@ def test_status_strings():
     for st in range(6):
         assert clo.clo_status_string(st)
     assert clo.clo_status_string(99) == "unknown status"
+
+
+def test_capacity_below_context_rejected():
+    with pytest.raises(clo.CloError) as e:
+        clo.clo_decode_step(shape(capacity=999), clo.Layer(), 16, 16, 16, 16, None, 256, stream=0)
+    assert e.value.status == clo.CLO_E_ARG and "capacity" in str(e.value)
+    # a capacity above the context sizes the workspace no differently (keys follow the context)
+    assert clo.clo_workspace_size(shape(capacity=4000)) == clo.clo_workspace_size(shape())
+
+
+def test_append_position_outside_capacity_rejected():
+    for pos in (-1, 1000, 5000):
+        cap = 0 if pos != 5000 else 4000
+        with pytest.raises(clo.CloError) as e:
+            clo.clo_append_kv(shape(capacity=cap), clo.Layer(), 16, 16, pos, stream=0)
+        assert e.value.status == clo.CLO_E_ARG and "position" in str(e.value)
+
+
+def test_update_reference_null_pointers_rejected():
+    with pytest.raises(clo.CloError) as e:
+        clo.clo_update_reference(shape(), None, None, None, stream=0)
+    assert e.value.status == clo.CLO_E_ARG and "q is NULL" in str(e.value)
+    clo.clo_update_reference(shape(batch=0), None, None, None, stream=0)

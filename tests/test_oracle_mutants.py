@@ -41,10 +41,32 @@ def _ns(**over):
                                              k, tau, None if idx_prev is None else idx_prev[b, h])
         return res
 
+    def decode_steps_unit(queries, K, V, n0, k, tau, policy="previous", grow=1, lag=0, rules=None):
+        # rules maps a policy to when the reference is replaced: "previous" every
+        # step, "refresh" on a miss, "never" only at the cold step
+        rule = (rules or {}).get(policy, policy)
+        results, ref, sel = [], None, None
+        for t, qg in enumerate(queries):
+            n = n0 + grow * t - (lag if t else 0)
+            if t == 0:
+                r = ns.decode_unit(qg, qg, K[:n], V[:n], k, math.inf)
+            else:
+                r = ns.decode_unit(qg, ref, K[:n], V[:n], k, tau, sel)
+            sel = r["idx"]
+            if t == 0 or rule == "previous" or (rule == "refresh" and not r["reuse"]):
+                ref = qg
+            results.append(r)
+        return results
+
     if "decode_unit" not in over:
         ns.decode_unit = decode_unit
     if "decode_layer" not in over:
         ns.decode_layer = decode_layer
+    steps_kw = over.get("steps_kw")
+    if steps_kw is not None:
+        ns.decode_steps_unit = lambda *a, **kw: decode_steps_unit(*a, **{**kw, **steps_kw})
+    elif "decode_steps_unit" not in over:
+        ns.decode_steps_unit = decode_steps_unit
     if "head_of" in over:
         ns.decode_layer = lambda *a, **kw: decode_layer(*a, head_of=over["head_of"], **kw)
     return ns
@@ -125,6 +147,13 @@ MUTANTS = {
     "topk_smallest": dict(select_topk=m_smallest_k),
     "gqa_head_modulo": dict(head_of=m_head_modulo),
     "bf16_decoded_as_int": dict(as_f64=m_bf16_low_half),
+    # many steps: the context does not grow, grows one step late, or the
+    # reference is kept / replaced at the wrong steps
+    "steps_context_fixed": dict(steps_kw=dict(grow=0)),
+    "steps_context_one_late": dict(steps_kw=dict(lag=1)),
+    "steps_refresh_never_updates": dict(steps_kw=dict(rules={"refresh": "never"})),
+    "steps_refresh_as_previous": dict(steps_kw=dict(rules={"refresh": "previous"})),
+    "steps_previous_as_refresh": dict(steps_kw=dict(rules={"previous": "refresh"})),
 }
 
 

@@ -18,7 +18,7 @@ CLO_OK, CLO_E_ARG, CLO_E_UNSUPPORTED, CLO_E_WORKSPACE, CLO_E_HIP, CLO_E_TIMEOUT 
 
 # every function include/clo.h declares
 EXPORTS = ("clo_workspace_size", "clo_reuse_test", "clo_topk_select", "clo_gather_kv", "clo_sparse_attn",
-           "clo_decode_step", "clo_status_string", "clo_last_error")
+           "clo_decode_step", "clo_append_kv", "clo_update_reference", "clo_status_string", "clo_last_error")
 
 
 class CloError(RuntimeError):
@@ -30,7 +30,7 @@ class CloError(RuntimeError):
 class clo_shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("context", ctypes.c_int64), ("topk", ctypes.c_int64),
-                ("tau", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("tau", ctypes.c_float), ("dtype", ctypes.c_int32), ("capacity", ctypes.c_int64)]
 
 
 class clo_layer(ctypes.Structure):
@@ -69,6 +69,10 @@ def load():
         L.clo_sparse_attn.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, sz, P(clo_sync), vp]
         L.clo_decode_step.restype = st
         L.clo_decode_step.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, vp, vp, vp, sz, P(clo_sync), vp]
+        L.clo_append_kv.restype = st
+        L.clo_append_kv.argtypes = [P(clo_shape), P(clo_layer), vp, vp, ctypes.c_int64, P(clo_sync), vp]
+        L.clo_update_reference.restype = st
+        L.clo_update_reference.argtypes = [P(clo_shape), vp, vp, vp, P(clo_sync), vp]
         L.clo_status_string.restype = ctypes.c_char_p
         L.clo_status_string.argtypes = [st]
         L.clo_last_error.restype = st
@@ -137,10 +141,11 @@ class Shape:
     tau: float
     dtype: int
     head_dim: int = 128
+    capacity: int = 0  # rows allocated per (sequence, head); 0 = context
 
     def c(self) -> clo_shape:
         return clo_shape(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.context, self.topk,
-                         self.tau, self.dtype)
+                         self.tau, self.dtype, self.capacity)
 
 
 @dataclass
@@ -211,6 +216,17 @@ def clo_decode_step(shape: Shape, layer: Layer, q, q_prev, out, reuse, cos, ws, 
     _check(load().clo_decode_step(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(q), ptr(q_prev), ptr(out),
                                   ptr(reuse), ptr(cos), ptr(ws), nbytes(ws, ws_bytes), _sync(sync),
                                   stream_handle(stream)), "clo_decode_step")
+
+
+def clo_append_kv(shape: Shape, layer: Layer, k_new, v_new, position: int, sync: Optional[Sync] = None,
+                  stream=None):
+    _check(load().clo_append_kv(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(k_new), ptr(v_new),
+                                int(position), _sync(sync), stream_handle(stream)), "clo_append_kv")
+
+
+def clo_update_reference(shape: Shape, q, reuse, q_ref, sync: Optional[Sync] = None, stream=None):
+    _check(load().clo_update_reference(ctypes.byref(shape.c()), ptr(q), ptr(reuse), ptr(q_ref), _sync(sync),
+                                       stream_handle(stream)), "clo_update_reference")
 
 
 def clo_status_string(status: int) -> str:

@@ -65,6 +65,9 @@ clo_status check_shape(const clo_shape* s) {
   if (s->context < 1 || s->context > (int64_t)INT32_MAX) return fail(CLO_E_ARG, "context %lld out of range", (long long)s->context);
   if (s->topk < 1 || s->topk > s->context)
     return fail(CLO_E_ARG, "topk %lld outside 1..context (%lld)", (long long)s->topk, (long long)s->context);
+  if (s->capacity != 0 && (s->capacity < s->context || s->capacity > (int64_t)INT32_MAX))
+    return fail(CLO_E_ARG, "capacity %lld outside context (%lld)..2^31-1", (long long)s->capacity,
+                (long long)s->context);
   return ok();
 }
 
@@ -139,6 +142,7 @@ clo_status make_plan(const clo_shape* s, uint64_t pmask, Plan* p) {
   a.Hkv = s->n_kv_heads;
   a.G = s->n_q_heads / s->n_kv_heads;
   a.N = s->context;
+  a.C = s->capacity ? s->capacity : s->context;
   a.k = s->topk;
   a.Np = round_up(s->context, 64);
   a.tau = s->tau;
@@ -257,19 +261,21 @@ clo_status device_queues(DeviceQueues** out) {
 
 // Buffer sizes in bytes.
 size_t q_bytes(const Plan& p) { return (size_t)p.a.B * p.a.Hq * kHeadDim * p.e; }
-size_t full_bytes(const Plan& p, int heads) { return (size_t)p.a.B * heads * (size_t)p.a.N * kHeadDim * p.e; }
+size_t full_bytes(const Plan& p, int heads) { return (size_t)p.a.B * heads * (size_t)p.a.C * kHeadDim * p.e; }
 size_t cache_bytes(const Plan& p) { return (size_t)p.a.B * p.a.H * (size_t)p.a.k * kHeadDim * p.e; }
 size_t idx_bytes(const Plan& p) { return (size_t)p.U * (size_t)p.a.k * 4; }
 
 // Which layer buffers a call reads or writes.
-enum Need : unsigned { NEED_SCORE = 1, NEED_HOST = 2, NEED_CACHE = 4, NEED_HBM_KV = 8, NEED_HBM_K = 16 };
+enum Need : unsigned { NEED_SCORE = 1, NEED_HOST = 2, NEED_CACHE = 4, NEED_HBM_KV = 8, NEED_HBM_K = 16, NEED_IDX = 32 };
 
 clo_status check_layer(const clo_layer* l, Plan* p, unsigned need) {
   if (!l) return fail(CLO_E_ARG, "layer is NULL");
   clo_status st;
   LayerArgs& a = p->a;
-  if ((st = check_device(l->idx, idx_bytes(*p), "layer.idx"))) return st;
-  a.idx = l->idx;
+  if (need & NEED_IDX) {
+    if ((st = check_device(l->idx, idx_bytes(*p), "layer.idx"))) return st;
+    a.idx = l->idx;
+  }
   if (a.P > 0 && (need & (NEED_HBM_KV | NEED_HBM_K))) {
     if ((st = check_device(l->k_hbm, full_bytes(*p, a.P), "layer.k_hbm"))) return st;
     a.k_hbm = l->k_hbm;
@@ -383,7 +389,7 @@ clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const
     return post_signal(sync, s);
   }
   Workspace w;
-  if ((st = check_layer(layer, &p, NEED_SCORE | NEED_HBM_K))) return st;
+  if ((st = check_layer(layer, &p, NEED_IDX | NEED_SCORE | NEED_HBM_K))) return st;
   if ((st = check_device(q, q_bytes(p), "q"))) return st;
   if (reuse && (st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
@@ -407,7 +413,7 @@ clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const u
     return post_signal(sync, s);
   }
   Workspace w;
-  if ((st = check_layer(layer, &p, NEED_HOST | NEED_CACHE))) return st;
+  if ((st = check_layer(layer, &p, NEED_IDX | NEED_HOST | NEED_CACHE))) return st;
   if (reuse && (st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
   uint32_t* counter = reinterpret_cast<uint32_t*>(w.meta + kMetaGather);
@@ -430,7 +436,7 @@ clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const
     return post_signal(sync, s);
   }
   Workspace w;
-  if ((st = check_layer(layer, &p, NEED_CACHE | NEED_HBM_KV))) return st;
+  if ((st = check_layer(layer, &p, NEED_IDX | NEED_CACHE | NEED_HBM_KV))) return st;
   if ((st = check_device(q, q_bytes(p), "q"))) return st;
   if ((st = check_device(out, q_bytes(p), "out"))) return st;
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
@@ -516,7 +522,7 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
     return post_signal(sync, s);
   }
   Workspace w;
-  if ((st = check_layer(layer, &p, NEED_SCORE | NEED_HOST | NEED_CACHE | NEED_HBM_KV))) return st;
+  if ((st = check_layer(layer, &p, NEED_IDX | NEED_SCORE | NEED_HOST | NEED_CACHE | NEED_HBM_KV))) return st;
   if ((st = check_device(q, q_bytes(p), "q"))) return st;
   if ((st = check_device(q_prev, q_bytes(p), "q_prev"))) return st;
   if ((st = check_device(out, q_bytes(p), "out"))) return st;
@@ -527,6 +533,52 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
   st = p.a.H > 0 ? step_overlapped(p, w, q, q_prev, out, reuse, cos, s)
                  : step_in_order(p, w, q, q_prev, out, reuse, cos, s);
   if (st) return st;
+  return post_signal(sync, s);
+}
+
+clo_status clo_append_kv(const clo_shape* shape, const clo_layer* layer, const void* k_new, const void* v_new,
+                         int64_t position, const clo_sync* sync, void* stream) {
+  Plan p;
+  clo_status st;
+  if ((st = make_plan(shape, layer ? layer->persistent_mask : 0, &p))) return st;
+  if ((st = check_sync_flags(sync))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (position < 0 || position >= p.a.C)
+    return fail(CLO_E_ARG, "position %lld outside 0..capacity-1 (%lld)", (long long)position, (long long)p.a.C);
+  if (p.U == 0) {
+    if ((st = pre_wait(sync, s))) return st;
+    return post_signal(sync, s);
+  }
+  if ((st = check_layer(layer, &p, NEED_SCORE | NEED_HOST | NEED_HBM_KV))) return st;
+  const size_t row_bytes = (size_t)p.U * kHeadDim * p.e;
+  if ((st = check_device(k_new, row_bytes, "k_new"))) return st;
+  if ((st = check_device(v_new, row_bytes, "v_new"))) return st;
+  if ((st = pre_wait(sync, s))) return st;
+  const LayerArgs& a = p.a;
+  if ((st = hip_status(launch_append(a, k_new, v_new, position, const_cast<void*>(a.k_hbm), const_cast<void*>(a.v_hbm),
+                                     const_cast<void*>(a.k_host), const_cast<void*>(a.v_host),
+                                     const_cast<void*>(a.k_score), s),
+                       "append launch")))
+    return st;
+  return post_signal(sync, s);
+}
+
+clo_status clo_update_reference(const clo_shape* shape, const void* q, const uint8_t* reuse, void* q_ref,
+                                const clo_sync* sync, void* stream) {
+  Plan p;
+  clo_status st;
+  if ((st = make_plan(shape, 0, &p))) return st;
+  if ((st = check_sync_flags(sync))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.U == 0) {
+    if ((st = pre_wait(sync, s))) return st;
+    return post_signal(sync, s);
+  }
+  if ((st = check_device(q, q_bytes(p), "q"))) return st;
+  if ((st = check_device(q_ref, q_bytes(p), "q_ref"))) return st;
+  if (reuse && (st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
+  if ((st = pre_wait(sync, s))) return st;
+  if ((st = hip_status(launch_update_reference(p.a, q, reuse, q_ref, s), "reference launch"))) return st;
   return post_signal(sync, s);
 }
 

@@ -39,6 +39,7 @@ constexpr int kGatherBlocksAlone = 24;
 struct LayerArgs {
   int32_t B, Hq, Hkv, G, P, H;
   int64_t N, k, Np;  // Np: padded key-row stride of the score workspace
+  int64_t C;         // rows allocated per (sequence, head) in the full K/V tensors (>= N)
   float tau;
   int32_t dtype;
   uint64_t pmask;
@@ -130,6 +131,10 @@ hipError_t launch_zero(uint32_t* word, hipStream_t s);
 hipError_t launch_attn_partial(const LayerArgs& a, const void* q, float* part, Span sp, int64_t max_units,
                                hipStream_t s);
 hipError_t launch_attn_combine(const LayerArgs& a, const float* part, void* out, hipStream_t s);
+hipError_t launch_append(const LayerArgs& a, const void* k_new, const void* v_new, int64_t position,
+                         void* k_hbm, void* v_hbm, void* k_host, void* v_host, void* k_score, hipStream_t s);
+hipError_t launch_update_reference(const LayerArgs& a, const void* q, const uint8_t* reuse, void* q_ref,
+                                   hipStream_t s);
 hipError_t launch_wait(const uint32_t* flag, uint32_t value, uint32_t spin_limit, uint32_t* error_word,
                        hipStream_t s);
 hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s);

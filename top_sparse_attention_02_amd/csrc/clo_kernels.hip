@@ -111,7 +111,7 @@ __device__ __forceinline__ const T* unit_keys(const LayerArgs& a, int b, int h) 
   const bool pers = (a.pmask >> h) & 1ull;
   const T* base = static_cast<const T*>(pers ? a.k_hbm : a.k_score);
   const int64_t heads = pers ? a.P : a.H;
-  return base + ((int64_t)b * heads + head_slot(a.pmask, h)) * a.N * kHeadDim;
+  return base + ((int64_t)b * heads + head_slot(a.pmask, h)) * a.C * kHeadDim;
 }
 
 // ---------------------------------------------------------------- A1 reuse test
@@ -938,8 +938,8 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
     const int b = u / a.Hkv, h = u % a.Hkv;
     if (!sp.list && (((a.pmask >> h) & 1ull) || (reuse && reuse[u]))) continue;
     const int64_t slot = (int64_t)b * a.H + head_slot(a.pmask, h);
-    const char* ks = static_cast<const char*>(a.k_host) + slot * a.N * RB;
-    const char* vs = static_cast<const char*>(a.v_host) + slot * a.N * RB;
+    const char* ks = static_cast<const char*>(a.k_host) + slot * a.C * RB;
+    const char* vs = static_cast<const char*>(a.v_host) + slot * a.C * RB;
     char* kd = static_cast<char*>(a.k_cache) + slot * a.k * RB;
     char* vd = static_cast<char*>(a.v_cache) + slot * a.k * RB;
     const int32_t* ix = a.idx + (int64_t)u * a.k;
@@ -1042,7 +1042,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
   const T* kbase;
   const T* vbase;
   if (pers) {
-    const int64_t s = ((int64_t)b * a.P + head_slot(a.pmask, h)) * a.N * kHeadDim;
+    const int64_t s = ((int64_t)b * a.P + head_slot(a.pmask, h)) * a.C * kHeadDim;
     kbase = static_cast<const T*>(a.k_hbm) + s;
     vbase = static_cast<const T*>(a.v_hbm) + s;
   } else {
@@ -1230,6 +1230,49 @@ __global__ __launch_bounds__(128 * S) void attn_combine_kernel(LayerArgs a, cons
   store_out(out + ((int64_t)b * a.Hq + (int64_t)h * G + g) * kHeadDim + col, Ot / Lt);
 }
 
+// ---------------------------------------------------------------- growing context
+// Row `position` of every (sequence, KV head) from k_new / v_new [B, Hkv, d]:
+// one 64-lane wave per unit, 16-byte pieces (bf16: 16 lanes per row; fp32: 32).
+// Offloaded heads' rows are stored by the GPU straight into pinned host memory
+// and into the HBM score copy.
+template <typename T>
+__global__ __launch_bounds__(64) void append_kernel(LayerArgs a, const T* __restrict__ k_new,
+                                                   const T* __restrict__ v_new, int64_t position, T* k_hbm,
+                                                   T* v_hbm, T* k_host, T* v_host, T* k_score) {
+  constexpr int kPieces = kHeadDim * (int)sizeof(T) / 16;  // 16-byte pieces per row
+  const int u = blockIdx.x;
+  const int b = u / a.Hkv, h = u % a.Hkv;
+  const bool pers = (a.pmask >> h) & 1ull;
+  const int64_t rows = pers ? a.P : a.H;
+  const int64_t dst = (((int64_t)b * rows + head_slot(a.pmask, h)) * a.C + position) * kHeadDim;
+  const int64_t src = (int64_t)u * kHeadDim;
+  for (int i = threadIdx.x; i < kPieces; i += 64) {
+    const u32x4 kv = reinterpret_cast<const u32x4*>(k_new + src)[i];
+    const u32x4 vv = reinterpret_cast<const u32x4*>(v_new + src)[i];
+    if (pers) {
+      reinterpret_cast<u32x4*>(k_hbm + dst)[i] = kv;
+      reinterpret_cast<u32x4*>(v_hbm + dst)[i] = vv;
+    } else {
+      reinterpret_cast<u32x4*>(k_host + dst)[i] = kv;
+      reinterpret_cast<u32x4*>(v_host + dst)[i] = vv;
+      reinterpret_cast<u32x4*>(k_score + dst)[i] = kv;
+    }
+  }
+}
+
+// q_ref[unit] = q[unit] for every miss unit (the unit's g heads, contiguous).
+template <typename T>
+__global__ __launch_bounds__(64) void update_reference_kernel(const T* __restrict__ q,
+                                                              const uint8_t* __restrict__ reuse, T* q_ref,
+                                                              int G) {
+  const int u = blockIdx.x;
+  if (reuse && reuse[u]) return;
+  const int64_t n = (int64_t)G * kHeadDim * (int)sizeof(T) / 16;  // 16-byte pieces of the unit
+  const u32x4* src = reinterpret_cast<const u32x4*>(q + (int64_t)u * G * kHeadDim);
+  u32x4* dst = reinterpret_cast<u32x4*>(q_ref + (int64_t)u * G * kHeadDim);
+  for (int64_t i = threadIdx.x; i < n; i += 64) dst[i] = src[i];
+}
+
 // ---------------------------------------------------------------- device-side flags
 __global__ __launch_bounds__(64) void wait_kernel(const uint32_t* flag, uint32_t value, uint32_t limit,
                                                   uint32_t* error_word) {
@@ -1370,6 +1413,34 @@ hipError_t launch_attn_combine(const LayerArgs& a, const float* part, void* out,
     case 4: go(std::integral_constant<int, 4>{}); break;
     default: go(std::integral_constant<int, 8>{}); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const LayerArgs& a, const void* k_new, const void* v_new, int64_t position,
+                         void* k_hbm, void* v_hbm, void* k_host, void* v_host, void* k_score, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)a.B * a.Hkv);
+  if (a.dtype == CLO_F32)
+    append_kernel<float><<<grid, 64, 0, s>>>(a, static_cast<const float*>(k_new), static_cast<const float*>(v_new),
+                                             position, static_cast<float*>(k_hbm), static_cast<float*>(v_hbm),
+                                             static_cast<float*>(k_host), static_cast<float*>(v_host),
+                                             static_cast<float*>(k_score));
+  else
+    append_kernel<uint16_t><<<grid, 64, 0, s>>>(
+        a, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), position,
+        static_cast<uint16_t*>(k_hbm), static_cast<uint16_t*>(v_hbm), static_cast<uint16_t*>(k_host),
+        static_cast<uint16_t*>(v_host), static_cast<uint16_t*>(k_score));
+  return hipGetLastError();
+}
+
+hipError_t launch_update_reference(const LayerArgs& a, const void* q, const uint8_t* reuse, void* q_ref,
+                                   hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)a.B * a.Hkv);
+  if (a.dtype == CLO_F32)
+    update_reference_kernel<float><<<grid, 64, 0, s>>>(static_cast<const float*>(q), reuse,
+                                                       static_cast<float*>(q_ref), a.G);
+  else
+    update_reference_kernel<uint16_t><<<grid, 64, 0, s>>>(static_cast<const uint16_t*>(q), reuse,
+                                                          static_cast<uint16_t*>(q_ref), a.G);
   return hipGetLastError();
 }
 

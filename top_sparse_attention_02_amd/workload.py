@@ -243,3 +243,82 @@ class LayerLoop:
         v = int(self.error.item())
         if v:
             raise RuntimeError(f"device-side wait failed with status {v} ({clo.clo_status_string(v)})")
+
+
+def host_rows_tensor(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Stored rows (fp32, or bf16 bit patterns) from pinned or pageable memory -> device tensor."""
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a.view(np.int16) if dtype == "bf16" else a)
+    if dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    return t.to(device)
+
+
+class GrowingRun:
+    """Multi-step decoding of one layer over a growing context.
+
+    The layer's buffers hold capacity C = problem.context rows per (sequence,
+    head).  The run starts with the first n0 = C - steps rows (the rows after
+    them are cleared) and before step t >= 1 appends row n0 + t - 1 of every
+    unit with clo_append_kv, so step t decodes over n0 + t rows.  Step 0 is a
+    cold step (every unit misses, q_0 as its own reference); step t >= 1
+    compares q_t = problem.q_walk(layer, t) with the reference: the previous
+    step's query ("previous") or the query of the unit's last miss ("refresh",
+    kept on the GPU by clo_update_reference).
+    """
+
+    def __init__(self, problem, layer: int, steps: int, policy: str = "previous",
+                 host_flags: int = hipHostMallocMapped):
+        if policy not in ("previous", "refresh"):
+            raise ValueError(policy)
+        p = problem
+        self.p, self.layer, self.steps, self.policy = p, layer, steps, policy
+        self.C = p.context
+        self.n0 = p.context - steps
+        assert self.n0 >= p.topk
+        b = self.bufs = load_layer(p, layer, host_flags=host_flags)
+        dev = b.q.device
+        tdt = torch_dtype(p.dtype)
+        n0 = self.n0
+        # the rows appended during the run, [steps, B, Hkv, d], taken from the loaded
+        # buffers; the buffers then hold only the first n0 rows
+        self.k_new = torch.zeros(steps, b.B, b.Hkv, HEAD_DIM, dtype=tdt, device=dev)
+        self.v_new = torch.zeros_like(self.k_new)
+        for h in range(b.Hkv):
+            s = b.slot(h)
+            if b.is_persistent(h):
+                self.k_new[:, :, h] = b.k_hbm[:, s, n0:].transpose(0, 1)
+                self.v_new[:, :, h] = b.v_hbm[:, s, n0:].transpose(0, 1)
+                b.k_hbm[:, s, n0:] = 0
+                b.v_hbm[:, s, n0:] = 0
+            else:
+                self.k_new[:, :, h] = b.k_score[:, s, n0:].transpose(0, 1)
+                b.k_score[:, s, n0:] = 0
+                for bb in range(b.B):
+                    self.v_new[:, bb, h] = host_rows_tensor(b.host_view("v", bb, h)[n0:], p.dtype, dev)
+                    b.host_view("k", bb, h)[n0:] = 0
+                    b.host_view("v", bb, h)[n0:] = 0
+        self.qs = torch.stack([stored_tensor(p.q_walk(layer, t), p.dtype, dev) for t in range(steps + 1)])
+        self.q_ref = torch.zeros_like(b.q)
+        torch.cuda.synchronize()
+
+    def shape(self, t: int, tau: float) -> clo.Shape:
+        s = clo.Shape(**self.bufs.shape.__dict__)
+        s.context, s.capacity, s.tau = self.n0 + t, self.C, tau
+        return s
+
+    def step(self, t: int, stream=None):
+        """Enqueue step t (steps run in order 0, 1, ..., steps)."""
+        b = self.bufs
+        q = self.qs[t]
+        if t == 0:
+            s = self.shape(0, math.inf)
+            clo.clo_decode_step(s, b.layer(), q, q, b.out, b.reuse, b.cos, b.ws, stream=stream)
+            clo.clo_update_reference(s, q, None, self.q_ref, stream=stream)
+            return
+        s = self.shape(t, b.tau)
+        clo.clo_append_kv(s, b.layer(), self.k_new[t - 1], self.v_new[t - 1], self.n0 + t - 1, stream=stream)
+        ref = self.qs[t - 1] if self.policy == "previous" else self.q_ref
+        clo.clo_decode_step(s, b.layer(), q, ref, b.out, b.reuse, b.cos, b.ws, stream=stream)
+        if self.policy == "refresh":
+            clo.clo_update_reference(s, q, b.reuse, self.q_ref, stream=stream)
