@@ -50,6 +50,10 @@ def parse():
                     help="pinned host memory kind for offloaded K/V (hipHostMalloc flags)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device-to-device copy first (reference for HBM byte counters)")
+    ap.add_argument("--growing", type=int, default=0, metavar="T",
+                    help="configs 1-3: T decode steps over a context that grows by one appended token per "
+                         "step, under both reference policies (previous step's query / query at the last "
+                         "miss): step time, hit rate, host bytes and drift from a fresh top-k step")
     return ap.parse_args()
 
 
@@ -287,6 +291,74 @@ def phase_times(torch, clo, layers, step_kind, passes):
     return {n: float(np.mean(v)) for n, v in acc.items()}
 
 
+def growing_bench(torch, clo, workload, gen, cfg: int, steps: int) -> dict:
+    """T steps over a growing context (the workload's context plus one appended
+    token per step; k fixed at the workload's top-k), per reference policy.
+
+    Timed per step (HIP events around the step's calls: append, decode, reference
+    update).  Drift: after the timed pass, each step's output against a fresh
+    top-k step (tau = +inf) at the same context with the same query, normwise per
+    (sequence, query head): max_i |o_i - f_i| / max_i |f_i|."""
+    import numpy as np
+
+    base = gen.config(cfg)
+    n0 = base.context
+    p = gen.config(cfg, context=n0 + steps, topk=base.topk)
+    log(f"growing context: N0={n0}, {steps} appended tokens, k={p.topk}; generating inputs")
+    t0 = time.time()
+    run = workload.GrowingRun(p, 0, steps, "previous")
+    b = run.bufs
+    fresh = workload.LayerBuffers(p.batch, p.hq, p.hkv, p.context, p.topk, p.dtype, b.mask, p.tau, share=b)
+    log(f"inputs ready ({time.time() - t0:.1f} s)")
+    eb = 4 if p.dtype == "f32" else 2
+    host = np.array([not b.is_persistent(h) for h in range(b.Hkv)])[None, :]
+    res = {}
+    for policy in ("previous", "refresh"):
+        run.reset(policy)
+        outs = torch.empty((steps + 1,) + tuple(b.out.shape), dtype=b.out.dtype, device=b.out.device)
+        reuse = torch.empty((steps + 1,) + tuple(b.reuse.shape), dtype=torch.uint8, device=b.out.device)
+        run.step(0)
+        torch.cuda.synchronize()
+        evs = []
+        for t in range(1, steps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run.step(t)
+            e1.record()
+            outs[t].copy_(b.out)
+            reuse[t].copy_(b.reuse)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(z) for a, z in evs])
+        drift_mean, drift_max = [], []
+        for t in range(1, steps + 1):
+            clo.clo_decode_step(run.shape(t, math.inf), fresh.layer(), run.qs[t], run.qs[t], fresh.out, fresh.reuse,
+                                fresh.cos, fresh.ws)
+            f = fresh.out.float()
+            err = (outs[t].float() - f).abs().amax(-1) / f.abs().amax(-1).clamp_min(1e-30)
+            drift_mean.append(float(err.mean()))
+            drift_max.append(float(err.max()))
+        torch.cuda.synchronize()
+        r = reuse[1:].cpu().numpy().astype(bool)
+        host_misses = (~r & host).sum(axis=(1, 2))
+        host_bytes = host_misses * p.topk * 2 * HEAD_DIM * eb
+        res[policy] = {
+            "steps_per_s": round(1000.0 / float(ms.mean()), 3),
+            "ms_per_step": round(float(ms.mean()), 4),
+            "ms_per_step_min_max": [round(float(ms.min()), 4), round(float(ms.max()), 4)],
+            "hit_rate": round(float(r.mean()), 4),
+            "hit_rate_per_step": [round(float(x), 4) for x in r.mean(axis=(1, 2))],
+            "host_gb_per_step": round(float(host_bytes.mean()) / 1e9, 4),
+            "host_gbs": round(float(host_bytes.sum()) / (float(ms.sum()) / 1e3) / 1e9, 2),
+            "drift_mean": round(float(np.mean(drift_mean)), 5),
+            "drift_max": round(float(np.max(drift_max)), 5),
+            "drift_mean_per_step": [round(x, 5) for x in drift_mean],
+        }
+        log(f"{policy}: {res[policy]['steps_per_s']} steps/s, hit rate {res[policy]['hit_rate']}, "
+            f"drift mean {res[policy]['drift_mean']}")
+    return {"n0": n0, "steps": steps, "topk": p.topk, "policies": res}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -300,6 +372,21 @@ def main():
 
     torch.cuda.set_device(0)
     clo.load()
+    if args.growing:
+        if args.config not in (1, 2, 3):
+            print("--growing runs a single-layer workload (configs 1-3)", file=sys.stderr)
+            sys.exit(2)
+        g = growing_bench(torch, clo, workload, gen, args.config, args.growing)
+        prev = g["policies"]["previous"]
+        print(json.dumps({
+            "metric": "sparse-attn decode steps/s over a growing context (one appended token per step)",
+            "value": prev["steps_per_s"], "unit": "steps/s", "n_gpus": 1, "steps": args.growing, "warmup": 1,
+            "ms_per_step": prev["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": gen.config(args.config).dtype, "data": "synthetic (seeded; query walk with the 80/20 cosine model)",
+            "config": {"workload": f"config {args.config}: " + WORKLOADS[args.config] +
+                       f", {args.growing} decode steps with one appended token each, reference = previous query"},
+            "growing": g}), flush=True)
+        return
     overrides = {}
     if args.config in (4, 5):
         overrides["data_layers"] = args.data_layers or (8 if args.config == 4 else 16)

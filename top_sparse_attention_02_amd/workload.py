@@ -289,17 +289,33 @@ class GrowingRun:
             if b.is_persistent(h):
                 self.k_new[:, :, h] = b.k_hbm[:, s, n0:].transpose(0, 1)
                 self.v_new[:, :, h] = b.v_hbm[:, s, n0:].transpose(0, 1)
+            else:
+                self.k_new[:, :, h] = b.k_score[:, s, n0:].transpose(0, 1)
+                for bb in range(b.B):
+                    self.v_new[:, bb, h] = host_rows_tensor(b.host_view("v", bb, h)[n0:], p.dtype, dev)
+        self.qs = torch.stack([stored_tensor(p.q_walk(layer, t), p.dtype, dev) for t in range(steps + 1)])
+        self.q_ref = torch.zeros_like(b.q)
+        self.reset()
+
+    def reset(self, policy: Optional[str] = None):
+        """Clear the rows the run appends, so that it can start again (optionally
+        with another reference policy)."""
+        if policy is not None:
+            if policy not in ("previous", "refresh"):
+                raise ValueError(policy)
+            self.policy = policy
+        b, n0 = self.bufs, self.n0
+        torch.cuda.synchronize()
+        for h in range(b.Hkv):
+            s = b.slot(h)
+            if b.is_persistent(h):
                 b.k_hbm[:, s, n0:] = 0
                 b.v_hbm[:, s, n0:] = 0
             else:
-                self.k_new[:, :, h] = b.k_score[:, s, n0:].transpose(0, 1)
                 b.k_score[:, s, n0:] = 0
                 for bb in range(b.B):
-                    self.v_new[:, bb, h] = host_rows_tensor(b.host_view("v", bb, h)[n0:], p.dtype, dev)
                     b.host_view("k", bb, h)[n0:] = 0
                     b.host_view("v", bb, h)[n0:] = 0
-        self.qs = torch.stack([stored_tensor(p.q_walk(layer, t), p.dtype, dev) for t in range(steps + 1)])
-        self.q_ref = torch.zeros_like(b.q)
         torch.cuda.synchronize()
 
     def shape(self, t: int, tau: float) -> clo.Shape:
