@@ -50,6 +50,13 @@ def parse():
                     help="pinned host memory kind for offloaded K/V (hipHostMalloc flags)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device-to-device copy first (reference for HBM byte counters)")
+    ap.add_argument("--volatile", type=float, default=0.0, metavar="F",
+                    help="head-dependent similarity: a fraction F of the (layer, KV head) slots draw the low "
+                         "cosine class with probability 0.6, the others less often (20%% low overall)")
+    ap.add_argument("--plan-persistent", action="store_true",
+                    help="choose the persistent heads from profiling (mean reuse-test cosine per slot on "
+                         "separately seeded instances, lowest first) instead of the seeded draw; same count")
+    ap.add_argument("--profile-instances", type=int, default=8)
     ap.add_argument("--growing", type=int, default=0, metavar="T",
                     help="configs 1-3: T decode steps over a context that grows by one appended token per "
                          "step, under both reference policies (previous step's query / query at the last "
@@ -359,6 +366,45 @@ def growing_bench(torch, clo, workload, gen, cfg: int, steps: int) -> dict:
     return {"n0": n0, "steps": steps, "topk": p.topk, "policies": res}
 
 
+def profile_and_plan(torch, clo, gen, cfg: int, overrides: dict, instances: int) -> dict:
+    """Profiling-based persistent heads: run the reuse test (on the GPU, through
+    the C ABI) on `instances` separately seeded copies of the workload that share
+    its volatile slots, average each (data layer, KV head) slot's cosine, and let
+    clo_plan_persistent mark the slots with the lowest mean as persistent -- as
+    many as the seeded draw has."""
+    import numpy as np
+
+    from top_sparse_attention_02_amd import workload
+
+    base = gen.config(cfg, **overrides)
+    L, H = base.layers, base.hkv
+    period = base.data_layers or L
+    n = int(base.persistent[:period].sum())
+    sums = np.zeros((period, H))
+    counts = np.zeros((period, H))
+    for i in range(instances):
+        pi = gen.config(cfg, **{**overrides, "seed": base.seed + 7919 * (i + 1), "slot_seed": base.seed})
+        shape = clo.Shape(pi.batch, pi.hq, pi.hkv, pi.context, pi.topk, pi.tau, workload.clo_dtype(pi.dtype))
+        cos = torch.zeros(pi.batch, H, dtype=torch.float32, device="cuda")
+        reuse = torch.zeros(pi.batch, H, dtype=torch.uint8, device="cuda")
+        for l in range(L):
+            q = workload.stored_tensor(pi.q(l), pi.dtype)
+            qp = workload.stored_tensor(pi.q_prev(l), pi.dtype)
+            clo.clo_reuse_test(shape, q, qp, reuse, cos)
+            sums[l % period] += cos.sum(0).cpu().numpy()
+            counts[l % period] += pi.batch
+    s_hat = (sums / counts).astype(np.float32)
+    masks = clo.clo_plan_persistent(s_hat, n)
+    plan = np.array([[(m >> h) & 1 for h in range(H)] for m in masks], dtype=bool)
+    vol = base.volatile_slots()[:period]
+    log(f"profiled {instances} instances: {n} persistent slots, {int((plan & vol).sum())} of {int(vol.sum())} "
+        f"volatile slots among them (seeded draw: {int((base.persistent[:period] & vol).sum())})")
+    return {"persistent": np.stack([plan[l % period] for l in range(L)]), "n_persistent_slots": n,
+            "profile_instances": instances, "volatile_slots": int(vol.sum()),
+            "volatile_persistent_planned": int((plan & vol).sum()),
+            "volatile_persistent_seeded": int((base.persistent[:period] & vol).sum())}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -390,6 +436,12 @@ def main():
     overrides = {}
     if args.config in (4, 5):
         overrides["data_layers"] = args.data_layers or (8 if args.config == 4 else 16)
+    if args.volatile:
+        overrides["volatile_frac"] = args.volatile
+    plan = None
+    if args.plan_persistent:
+        plan = profile_and_plan(torch, clo, gen, args.config, overrides, args.profile_instances)
+        overrides["persistent"] = plan["persistent"]
     p = gen.config(args.config, **overrides)
     multi = p.layers > 1
     log(f"config {args.config}: L={p.layers} B={p.batch} Hq={p.hq} Hkv={p.hkv} N={p.context} k={p.topk} "
@@ -489,11 +541,15 @@ def main():
         "dtype": p.dtype,
         "data": "synthetic (seeded N(0,1) keys/values and queries; no model weights)",
         "config": {"workload": f"config {args.config}: " + WORKLOADS[args.config] +
-                   (", steady step (80/20 reuse)" if args.step == 1 else ", cold step (all miss)"),
+                   (", steady step (80/20 reuse)" if args.step == 1 else ", cold step (all miss)") +
+                   (f", {args.volatile:.0%} volatile (layer, KV head) slots" if args.volatile else "") +
+                   (", persistent heads from profiling" if plan else ""),
                    "layers": p.layers, "batch": p.batch, "q_heads": p.hq, "kv_heads": p.hkv, "head_dim": HEAD_DIM,
                    "context": p.context, "topk": p.topk, "tau": p.tau, "step": args.step,
                    "data_layers": p.data_layers or p.layers, "host_memory": args.host_memory},
         "roofline": roofline,
+        "persistent_plan": None if plan is None else {k: v for k, v in plan.items() if k != "persistent"},
+        "volatile_frac": args.volatile,
         "roofline_score": score_roofline(score_gbs, alg, args, multi),
         "attention_hbm_gbs": round(attn_gbs, 1),
         "step_hbm_gbs": round(alg["hbm_bytes"] / step_s / 1e9, 1),

@@ -30,7 +30,7 @@ _lib = None
 MASK64 = (1 << 64) - 1
 
 # tensor tags for key derivation
-TAG_Q, TAG_QPREV, TAG_K, TAG_V, TAG_HEAVY, TAG_PERSIST, TAG_LOW, TAG_COS, TAG_WALK = range(1, 10)
+TAG_Q, TAG_QPREV, TAG_K, TAG_V, TAG_HEAVY, TAG_PERSIST, TAG_LOW, TAG_COS, TAG_WALK, TAG_VOLATILE = range(1, 11)
 
 F32, BF16 = "f32", "bf16"
 
@@ -165,6 +165,12 @@ class Problem:
     low_range: Tuple[float, float] = (0.2, 0.6)
     high_range: Tuple[float, float] = (0.801, 0.98)
     data_layers: Optional[int] = None  # K/V of layer l are those of layer l % data_layers
+    # head-dependent similarity: a fraction of the (data layer, KV head) slots are
+    # "volatile" -- their units draw the low cosine class with probability
+    # volatile_low, the other slots less often, so that low_frac holds overall
+    volatile_frac: float = 0.0
+    volatile_low: float = 0.6
+    slot_seed: Optional[int] = None  # seed of the volatile-slot draw (default: seed)
     k_resample: Dict[Tuple[int, int, int], Dict[int, int]] = field(default_factory=dict)
     qprev_round: Dict[Tuple[int, int, int], int] = field(default_factory=dict)
     walk_round: Dict[Tuple[int, int, int, int], int] = field(default_factory=dict)
@@ -212,8 +218,40 @@ class Problem:
         """Current-step query, stored dtype, [B, Hq, d]."""
         return round_to(self.q_f64(layer), self.dtype)
 
+    def volatile_slots(self) -> np.ndarray:
+        """bool [layers, hkv]: the volatile (layer, KV head) slots, periodic over the
+        data layers like the persistent mask."""
+        if "_volatile" not in self.__dict__:
+            period = self.data_layers or self.layers
+            n = int(round(self.volatile_frac * period * self.hkv))
+            seed = self.slot_seed if self.slot_seed is not None else self.seed
+            base = np.zeros(period * self.hkv, dtype=bool)
+            base[smallest_by_key(derive_key(seed, TAG_VOLATILE), period * self.hkv, n)] = True
+            base = base.reshape(period, self.hkv)
+            self.__dict__["_volatile"] = np.stack([base[l % period] for l in range(self.layers)])
+        return self.__dict__["_volatile"]
+
+    def low_probability(self, layer: int, kvh: int) -> float:
+        """P(low cosine class) of a unit of this slot under the volatile-slot model."""
+        if self.volatile_slots()[layer, kvh]:
+            return self.volatile_low
+        v = self.volatile_frac
+        return max(0.0, (self.low_frac - v * self.volatile_low) / (1.0 - v))
+
     def cos_target(self, layer: int, b: int, kvh: int) -> float:
-        """Target group cosine of a unit under the 80/20 correlation model."""
+        """Target group cosine of a unit under the 80/20 correlation model (exactly
+        round(low_frac * units) low units; with volatile slots, each unit low with
+        its slot's probability)."""
+        if self._cos_targets is None and self.volatile_frac > 0:
+            U = self.layers * self.batch * self.hkv
+            u = uniform_stream(derive_key(self.seed, TAG_COS), U)
+            w = uniform_stream(derive_key(self.seed, TAG_LOW), U)
+            t = np.empty(U)
+            for i in range(U):
+                l, h = i // (self.batch * self.hkv), i % self.hkv
+                lo, hi = self.low_range if w[i] < self.low_probability(l, h) else self.high_range
+                t[i] = lo + (hi - lo) * u[i]
+            self._cos_targets = t
         if self._cos_targets is None:
             U = self.layers * self.batch * self.hkv
             n_low = int(round(self.low_frac * U))

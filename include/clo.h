@@ -19,7 +19,7 @@
  *   A5 attention     softmax(q_h . K_sel / sqrt(d)) . V_sel per query head
  *                    (synthesis 2.3 table: top-k sparse attention).
  *
- * A unit whose cosine reaches tau reuses the previous step's selection and
+ * A unit whose cosine reaches tau (its head's tau_heads entry when given) reuses the previous step's selection and
  * cached rows; A2-A4 run for the other ("miss") units only.  Query head h
  * belongs to KV head h / g, g = n_q_heads / n_kv_heads.
  *
@@ -89,6 +89,10 @@ typedef struct {
                           k_score: the row stride of those tensors.  0 = context.  A context that
                           grows during decoding (clo_append_kv) keeps capacity fixed and raises
                           context; only rows 0..context-1 are read. */
+  const float* tau_heads;  /* per-head thresholds (synthesis sections 3.1 and 5.3: profiling sets a
+                              threshold per head): host array [n_kv_heads], read during the call;
+                              unit (b, h) reuses when cos >= tau_heads[h].  NULL = tau for every
+                              head. */
 } clo_shape;
 
 /* Where one layer's keys, values, selections and cached rows live. */
@@ -224,6 +228,21 @@ clo_status clo_append_kv(const clo_shape* shape, const clo_layer* layer, const v
  */
 clo_status clo_update_reference(const clo_shape* shape, const void* q, const uint8_t* reuse, void* q_ref,
                                 const clo_sync* sync, void* stream);
+
+/*
+ * Profiling-based choice of persistent heads (synthesis section 3.1 attack
+ * point 6 and section 5.3: offline profiling fixes each head's mean adjacent-
+ * step query similarity and the number of persistent heads).  s_hat is a host
+ * array [n_layers, n_kv_heads] of per-(layer, KV head) mean cosines; the
+ * n_persist slots with the lowest s_hat (the heads that miss most, whose
+ * transfers a persistent copy saves) become persistent, ties to the lower
+ * (layer, head) index.  Writes masks[l] (bit h = KV head h persistent) for
+ * every layer.  Host only: launches nothing.  CLO_E_ARG for NULL pointers,
+ * n_kv_heads outside 1..64, n_persist outside 0..n_layers*n_kv_heads or a NaN
+ * in s_hat.
+ */
+clo_status clo_plan_persistent(const float* s_hat, int32_t n_layers, int32_t n_kv_heads, int32_t n_persist,
+                               uint64_t* masks);
 
 /* Static text for a status code. */
 const char* clo_status_string(clo_status status);

@@ -6,6 +6,7 @@ from .clo_oracle import (  # noqa: F401
     decode_steps_unit,
     decode_unit,
     group_cosine,
+    plan_persistent,
     reuse_decision,
     select_topk,
     token_scores,

@@ -31,6 +31,10 @@ Synthesis"; CLO abstract page on fugumt):
   * O5: abstract, features (2) and (3) -- persistent on-GPU heads and
     zero-copy transfers only change where rows come from.
   * O6: synthesis section 2.3 table -- attention is top-k sparse attention.
+  * Per-head thresholds and the persistent-head choice (decode_layer with one
+    tau per KV head, plan_persistent): synthesis section 3.1 attack point 6
+    and section 5.3 -- offline profiling fixes each head's mean similarity,
+    its threshold and the number of persistent heads.
   * Multi-step decoding (decode_steps_unit): synthesis section 2.1 item 2 --
     the similarity is between adjacent decode steps; section 5.6 -- the
     context grows by the decoded token and new KV is offloaded incrementally.
@@ -139,14 +143,15 @@ def decode_unit(q_group, q_prev_group, K, V, k: int, tau: float,
 
 
 def decode_layer(q, q_prev, kv_of: Callable[[int, int], Tuple[np.ndarray, np.ndarray]],
-                 hkv: int, k: int, tau: float, dtype: str,
+                 hkv: int, k: int, tau, dtype: str,
                  idx_prev: Optional[np.ndarray] = None,
                  units: Optional[Iterable[Tuple[int, int]]] = None) -> Dict[Tuple[int, int], Dict[str, object]]:
     """Run decode_unit over (b, kvh) units of one layer.
 
     q, q_prev: stored [B, Hq, d] arrays of `dtype`; kv_of(b, kvh) returns the
     stored [N, d] K and V of a unit; idx_prev: [B, Hkv, k] selections of the
-    previous step (needed for reused units).  Returns {(b, kvh): result}.
+    previous step (needed for reused units); tau: one threshold, or one per KV
+    head (per-head thresholds).  Returns {(b, kvh): result}.
     """
     qf = as_f64(q, dtype)
     qpf = as_f64(q_prev, dtype)
@@ -158,8 +163,9 @@ def decode_layer(q, q_prev, kv_of: Callable[[int, int], Tuple[np.ndarray, np.nda
     for b, kvh in units:
         K, V = kv_of(b, kvh)
         prev = None if idx_prev is None else idx_prev[b, kvh]
+        tau_u = float(tau[kvh]) if np.ndim(tau) else float(tau)
         res[(b, kvh)] = decode_unit(qf[b, kvh * g:(kvh + 1) * g], qpf[b, kvh * g:(kvh + 1) * g],
-                                    as_f64(K, dtype), as_f64(V, dtype), k, tau, prev)
+                                    as_f64(K, dtype), as_f64(V, dtype), k, tau_u, prev)
     return res
 
 
@@ -189,3 +195,20 @@ def decode_steps_unit(queries, K, V, n0: int, k: int, tau: float, policy: str = 
             ref = qg
         results.append(r)
     return results
+
+
+def plan_persistent(s_hat, n_persist: int):
+    """Persistent-head masks from profiled similarities.
+
+    s_hat: [L, Hkv] mean adjacent-step cosine of each (layer, KV head) slot.  The
+    n_persist slots with the lowest s_hat are persistent -- they miss most, so a
+    persistent copy saves the most transfers; equal values go to the lower
+    (layer, head) index.  Returns one bit mask per layer.
+    """
+    s = np.asarray(s_hat, dtype=np.float64)
+    L, H = s.shape
+    order = sorted(range(L * H), key=lambda i: (s.reshape(-1)[i], i))
+    masks = [0] * L
+    for i in order[:n_persist]:
+        masks[i // H] |= 1 << (i % H)
+    return masks

@@ -345,6 +345,50 @@ def pin_multistep_limits(O):
             assert close(keep[t]["out"], ref[0], 1e-10)
 
 
+# ---------------------------------------------------------------- per-head thresholds, persistent choice
+def pin_per_head_thresholds(O):
+    # two KV heads whose groups have the same cosine 3/sqrt(10) = 0.9487 with the
+    # previous query: thresholds (0.9, 0.95) make the first a hit and the second a
+    # miss; equal thresholds behave like the single threshold.
+    B, Hkv, g, d, N, k = 1, 2, 1, 2, 4, 2
+    q = np.array([[[1.0, 0.0], [1.0, 0.0]]], dtype=np.float32)
+    qp = np.array([[[3.0, 1.0], [3.0, 1.0]]], dtype=np.float32)
+    K = np.array([[1.0, 0.0], [0.0, 1.0], [-1.0, 0.0], [2.0, 0.0]], dtype=np.float32)
+    V = np.array([[1.0, 0.0], [0.0, 1.0], [5.0, 5.0], [0.0, 2.0]], dtype=np.float32)
+    kv = lambda b, h: (K, V)  # noqa: E731
+    idx_prev = np.array([[[1, 2], [1, 2]]])
+    r = O.decode_layer(q, qp, kv, Hkv, k, [0.9, 0.95], "f32", idx_prev=idx_prev)
+    assert r[(0, 0)]["reuse"] is True and list(r[(0, 0)]["idx"]) == [1, 2]
+    assert r[(0, 1)]["reuse"] is False and list(r[(0, 1)]["idx"]) == [0, 3]
+    for t in (0.9, 0.95):
+        a = O.decode_layer(q, qp, kv, Hkv, k, [t, t], "f32", idx_prev=idx_prev)
+        b = O.decode_layer(q, qp, kv, Hkv, k, t, "f32", idx_prev=idx_prev)
+        for u in a:
+            assert a[u]["reuse"] == b[u]["reuse"] and list(a[u]["idx"]) == list(b[u]["idx"])
+
+
+def pin_plan_persistent(O):
+    # closed form: 2 layers x 3 heads; the three lowest similarities are slots
+    # (1,0)=0.1, (0,2)=0.2 and the tie 0.5 between (0,1) and (1,2) goes to (0,1)
+    s = np.array([[0.9, 0.5, 0.2], [0.1, 0.7, 0.5]])
+    assert O.plan_persistent(s, 0) == [0, 0]
+    assert O.plan_persistent(s, 3) == [0b110, 0b001]
+    assert O.plan_persistent(s, 6) == [0b111, 0b111]
+    # brute force: among all subsets of the same size, the chosen one has the
+    # smallest total similarity, and with ties the lexicographically first slots
+    rng = np.random.default_rng(12)
+    for _ in range(30):
+        L, H = rng.integers(1, 4), rng.integers(1, 4)
+        s = rng.integers(0, 4, size=(L, H)).astype(np.float64) / 4  # many ties
+        n = int(rng.integers(0, L * H + 1))
+        masks = O.plan_persistent(s, n)
+        chosen = sorted(l * H + h for l in range(L) for h in range(H) if masks[l] >> h & 1)
+        assert len(chosen) == n
+        flat = s.reshape(-1)
+        best = min(itertools.combinations(range(L * H), n), key=lambda c: (sum(flat[list(c)]), c))
+        assert chosen == list(best)
+
+
 def pin_bf16_decoding(O):
     # IEEE facts about bfloat16 bit patterns
     bits = np.array([0x3F80, 0xC000, 0x3FC0, 0x0000, 0x8000, 0x7F7F, 0x0001, 0x4049], dtype=np.uint16)
@@ -375,5 +419,7 @@ ALL_PINS = [
     pin_multistep_reference_policies_k1,
     pin_multistep_reference_policies_k2,
     pin_multistep_limits,
+    pin_per_head_thresholds,
+    pin_plan_persistent,
     pin_bf16_decoding,
 ]

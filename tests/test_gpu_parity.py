@@ -173,3 +173,35 @@ def test_zero_copy_gather_equals_hbm_gather(need_gpu):
     dev = snapshot(bufs)
     assert np.array_equal(host["k_cache"], dev["k_cache"])
     assert np.array_equal(host["v_cache"], dev["v_cache"])
+
+
+def test_per_head_thresholds(need_gpu):
+    """Each KV head decides with its own threshold (host array in the shape)."""
+    from top_sparse_attention_02_amd import workload
+
+    p = small_problem("tau_heads", batch=3, hq=16, hkv=4, context=3000, topk=300, dtype="bf16",
+                      persistent=[1, 0, 0, 1], qprev_model="target_cos", low_frac=0.3)
+    taus = [0.3, 0.8, 0.95, 0.5]
+    # margins against each head's own threshold
+    for h, t in enumerate(taus):
+        enforce_margins(p, 0, units=[(b, h) for b in range(p.batch)], tau=t)
+    log(f"[case tau_heads] thresholds {taus}")
+    bufs = workload.load_layer(p, 0)
+    bufs.shape.tau_heads = taus
+    bufs.step0()
+    got0 = snapshot(bufs)
+    bufs.step1()
+    got1 = snapshot(bufs)
+    r0, _, kv = oracle_steps(p, 0)
+    idx0 = np.zeros((p.batch, p.hkv, p.topk), dtype=np.int64)
+    for (b, h), r in r0.items():
+        idx0[b, h] = r["idx"]
+    r1 = oracle.decode_layer(p.q(0), p.q_prev(0), kv, p.hkv, p.topk, taus, p.dtype, idx_prev=idx0)
+    compare(p, bufs, got0, r0, kv, "step0")
+    compare(p, bufs, got1, r1, kv, "step1")
+    # the thresholds change decisions: a unit's outcome follows its own head's tau
+    c = got1["cos"]
+    for b in range(p.batch):
+        for h in range(p.hkv):
+            assert bool(got1["reuse"][b, h]) == (c[b, h] >= taus[h])
+    assert len({bool(x) for x in got1["reuse"].reshape(-1)}) == 2

@@ -28,7 +28,8 @@ def _ns(**over):
         return {"cos": c, "reuse": reuse, "idx": sel,
                 "out": ns.attend(q_group, np.asarray(K, float)[sel], np.asarray(V, float)[sel])}
 
-    def decode_layer(q, q_prev, kv_of, hkv, k, tau, dtype, idx_prev=None, units=None, head_of=None):
+    def decode_layer(q, q_prev, kv_of, hkv, k, tau, dtype, idx_prev=None, units=None, head_of=None,
+                     tau_of=None):
         qf, qpf = ns.as_f64(q, dtype), ns.as_f64(q_prev, dtype)
         B, Hq, _ = qf.shape
         g = Hq // hkv
@@ -37,8 +38,9 @@ def _ns(**over):
             for h in range(hkv):
                 heads = head_of(h, g, hkv, Hq) if head_of else list(range(h * g, (h + 1) * g))
                 K, V = kv_of(b, h)
+                t = (tau_of or (lambda tau, h: float(tau[h]) if np.ndim(tau) else float(tau)))(tau, h)
                 res[(b, h)] = ns.decode_unit(qf[b, heads], qpf[b, heads], ns.as_f64(K, dtype), ns.as_f64(V, dtype),
-                                             k, tau, None if idx_prev is None else idx_prev[b, h])
+                                             k, t, None if idx_prev is None else idx_prev[b, h])
         return res
 
     def decode_steps_unit(queries, K, V, n0, k, tau, policy="previous", grow=1, lag=0, rules=None):
@@ -69,6 +71,10 @@ def _ns(**over):
         ns.decode_steps_unit = decode_steps_unit
     if "head_of" in over:
         ns.decode_layer = lambda *a, **kw: decode_layer(*a, head_of=over["head_of"], **kw)
+    if "tau_of" in over:
+        ns.decode_layer = lambda *a, **kw: decode_layer(*a, tau_of=over["tau_of"], **kw)
+    if "plan_persistent" not in over:
+        ns.plan_persistent = base.plan_persistent
     return ns
 
 
@@ -134,6 +140,20 @@ def m_cos_no_prev_norm(a, b):
     return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(a)))
 
 
+def m_plan_highest_first(s_hat, n):
+    return base.plan_persistent(-np.asarray(s_hat, float), n)
+
+
+def m_plan_ties_to_higher_index(s_hat, n):
+    s = np.asarray(s_hat, float)
+    L, H = s.shape
+    order = sorted(range(L * H), key=lambda i: (s.reshape(-1)[i], -i))
+    masks = [0] * L
+    for i in order[:n]:
+        masks[i // H] |= 1 << (i % H)
+    return masks
+
+
 MUTANTS = {
     "score_sum_over_heads": dict(token_scores=m_sum_over_heads),
     "cosine_mean_of_heads": dict(group_cosine=m_mean_head_cosine),
@@ -149,6 +169,10 @@ MUTANTS = {
     "bf16_decoded_as_int": dict(as_f64=m_bf16_low_half),
     # many steps: the context does not grow, grows one step late, or the
     # reference is kept / replaced at the wrong steps
+    "tau_heads_ignored": dict(tau_of=lambda tau, h: float(np.max(tau)) if np.ndim(tau) else float(tau)),
+    "tau_heads_reversed": dict(tau_of=lambda tau, h: float(tau[::-1][h]) if np.ndim(tau) else float(tau)),
+    "plan_highest_similarity": dict(plan_persistent=m_plan_highest_first),
+    "plan_ties_to_higher_index": dict(plan_persistent=m_plan_ties_to_higher_index),
     "steps_context_fixed": dict(steps_kw=dict(grow=0)),
     "steps_context_one_late": dict(steps_kw=dict(lag=1)),
     "steps_refresh_never_updates": dict(steps_kw=dict(rules={"refresh": "never"})),

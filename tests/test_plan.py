@@ -1,0 +1,42 @@
+"""clo_plan_persistent (host-only, no GPU) against the oracle's plan_persistent."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from top_sparse_attention_02_amd import clo
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_plan_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    L, H = int(rng.integers(1, 50)), int(rng.integers(1, 9))
+    # coarse values: many ties, exactly representable in float32
+    s = (rng.integers(0, 16, size=(L, H)) / 16).astype(np.float32)
+    n = int(rng.integers(0, L * H + 1))
+    assert clo.clo_plan_persistent(s, n) == oracle.plan_persistent(s, n)
+
+
+def test_plan_config_sized():
+    # 48 layers x 8 KV heads, 183 persistent slots (47.6%)
+    rng = np.random.default_rng(3)
+    s = rng.uniform(0.2, 1.0, size=(48, 8)).astype(np.float32)
+    masks = clo.clo_plan_persistent(s, 183)
+    assert masks == oracle.plan_persistent(s, 183)
+    assert sum(bin(m).count("1") for m in masks) == 183
+
+
+@pytest.mark.parametrize("n", [-1, 17])
+def test_plan_rejects_bad_counts(n):
+    with pytest.raises(clo.CloError) as e:
+        clo.clo_plan_persistent(np.zeros((2, 8), np.float32), n)
+    assert e.value.status == clo.CLO_E_ARG
+
+
+def test_plan_rejects_nan():
+    s = np.zeros((2, 4), np.float32)
+    s[1, 2] = math.nan
+    with pytest.raises(clo.CloError) as e:
+        clo.clo_plan_persistent(s, 3)
+    assert e.value.status == clo.CLO_E_ARG and "NaN" in str(e.value)

@@ -9,7 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
-from typing import Optional
+from typing import Optional, Sequence
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libclo.so")
 
@@ -18,7 +18,8 @@ CLO_OK, CLO_E_ARG, CLO_E_UNSUPPORTED, CLO_E_WORKSPACE, CLO_E_HIP, CLO_E_TIMEOUT 
 
 # every function include/clo.h declares
 EXPORTS = ("clo_workspace_size", "clo_reuse_test", "clo_topk_select", "clo_gather_kv", "clo_sparse_attn",
-           "clo_decode_step", "clo_append_kv", "clo_update_reference", "clo_status_string", "clo_last_error")
+           "clo_decode_step", "clo_append_kv", "clo_update_reference", "clo_plan_persistent", "clo_status_string",
+           "clo_last_error")
 
 
 class CloError(RuntimeError):
@@ -30,7 +31,8 @@ class CloError(RuntimeError):
 class clo_shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("context", ctypes.c_int64), ("topk", ctypes.c_int64),
-                ("tau", ctypes.c_float), ("dtype", ctypes.c_int32), ("capacity", ctypes.c_int64)]
+                ("tau", ctypes.c_float), ("dtype", ctypes.c_int32), ("capacity", ctypes.c_int64),
+                ("tau_heads", ctypes.POINTER(ctypes.c_float))]
 
 
 class clo_layer(ctypes.Structure):
@@ -73,6 +75,8 @@ def load():
         L.clo_append_kv.argtypes = [P(clo_shape), P(clo_layer), vp, vp, ctypes.c_int64, P(clo_sync), vp]
         L.clo_update_reference.restype = st
         L.clo_update_reference.argtypes = [P(clo_shape), vp, vp, vp, P(clo_sync), vp]
+        L.clo_plan_persistent.restype = st
+        L.clo_plan_persistent.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
         L.clo_status_string.restype = ctypes.c_char_p
         L.clo_status_string.argtypes = [st]
         L.clo_last_error.restype = st
@@ -142,10 +146,17 @@ class Shape:
     dtype: int
     head_dim: int = 128
     capacity: int = 0  # rows allocated per (sequence, head); 0 = context
+    tau_heads: Optional[Sequence[float]] = None  # per-KV-head thresholds; None = tau for every head
 
     def c(self) -> clo_shape:
-        return clo_shape(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.context, self.topk,
-                         self.tau, self.dtype, self.capacity)
+        th = None
+        if self.tau_heads is not None:
+            th = (ctypes.c_float * len(self.tau_heads))(*[float(x) for x in self.tau_heads])
+        cs = clo_shape(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.context, self.topk,
+                       self.tau, self.dtype, self.capacity,
+                       ctypes.cast(th, ctypes.POINTER(ctypes.c_float)) if th is not None else None)
+        cs._tau_heads = th  # keeps the array alive while the struct is in use
+        return cs
 
 
 @dataclass
@@ -227,6 +238,18 @@ def clo_append_kv(shape: Shape, layer: Layer, k_new, v_new, position: int, sync:
 def clo_update_reference(shape: Shape, q, reuse, q_ref, sync: Optional[Sync] = None, stream=None):
     _check(load().clo_update_reference(ctypes.byref(shape.c()), ptr(q), ptr(reuse), ptr(q_ref), _sync(sync),
                                        stream_handle(stream)), "clo_update_reference")
+
+
+def clo_plan_persistent(s_hat, n_persist: int):
+    """Persistent-head masks from per-(layer, KV head) mean similarities s_hat [L, Hkv] (host)."""
+    import numpy as np
+
+    a = np.ascontiguousarray(np.asarray(s_hat, dtype=np.float32))
+    L, H = a.shape
+    masks = (ctypes.c_uint64 * max(L, 1))()
+    _check(load().clo_plan_persistent(a.ctypes.data, L, H, int(n_persist), ctypes.cast(masks, ctypes.c_void_p)),
+           "clo_plan_persistent")
+    return [int(masks[i]) for i in range(L)]
 
 
 def clo_status_string(status: int) -> str:

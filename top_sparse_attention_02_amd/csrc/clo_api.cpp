@@ -1,3 +1,5 @@
+#include <algorithm>
+#include <vector>
 // C ABI of the CLO decode-step library: host-side validation, workspace
 // layout and the launch sequence of each entry point.  Declarations and the
 // contract of every call are in include/clo.h.
@@ -146,6 +148,7 @@ clo_status make_plan(const clo_shape* s, uint64_t pmask, Plan* p) {
   a.k = s->topk;
   a.Np = round_up(s->context, 64);
   a.tau = s->tau;
+  for (int h = 0; h < kMaxKvHeads; ++h) a.tau_h[h] = (s->tau_heads && h < s->n_kv_heads) ? s->tau_heads[h] : s->tau;
   a.dtype = s->dtype;
   a.pmask = pmask;
   a.P = __builtin_popcountll(pmask);
@@ -580,6 +583,30 @@ clo_status clo_update_reference(const clo_shape* shape, const void* q, const uin
   if ((st = pre_wait(sync, s))) return st;
   if ((st = hip_status(launch_update_reference(p.a, q, reuse, q_ref, s), "reference launch"))) return st;
   return post_signal(sync, s);
+}
+
+clo_status clo_plan_persistent(const float* s_hat, int32_t n_layers, int32_t n_kv_heads, int32_t n_persist,
+                               uint64_t* masks) {
+  if (!s_hat || !masks) return fail(CLO_E_ARG, "s_hat or masks is NULL");
+  if (n_layers < 0) return fail(CLO_E_ARG, "n_layers %d < 0", n_layers);
+  if (n_kv_heads < 1 || n_kv_heads > kMaxKvHeads)
+    return fail(CLO_E_ARG, "n_kv_heads %d outside 1..%d", n_kv_heads, kMaxKvHeads);
+  const int64_t slots = (int64_t)n_layers * n_kv_heads;
+  if (n_persist < 0 || n_persist > slots)
+    return fail(CLO_E_ARG, "n_persist %d outside 0..%lld", n_persist, (long long)slots);
+  std::vector<int64_t> order((size_t)slots);
+  for (int64_t i = 0; i < slots; ++i) {
+    if (std::isnan(s_hat[i])) return fail(CLO_E_ARG, "s_hat[%lld] is NaN", (long long)i);
+    order[(size_t)i] = i;
+  }
+  // lowest mean similarity first; equal values keep the lower slot index first
+  std::stable_sort(order.begin(), order.end(), [&](int64_t x, int64_t y) { return s_hat[x] < s_hat[y]; });
+  for (int l = 0; l < n_layers; ++l) masks[l] = 0;
+  for (int i = 0; i < n_persist; ++i) {
+    const int64_t slot = order[(size_t)i];
+    masks[slot / n_kv_heads] |= 1ull << (slot % n_kv_heads);
+  }
+  return ok();
 }
 
 const char* clo_status_string(clo_status status) {

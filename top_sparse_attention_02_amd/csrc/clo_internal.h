@@ -41,6 +41,7 @@ struct LayerArgs {
   int64_t N, k, Np;  // Np: padded key-row stride of the score workspace
   int64_t C;         // rows allocated per (sequence, head) in the full K/V tensors (>= N)
   float tau;
+  float tau_h[kMaxKvHeads];  // threshold of each KV head (tau when none are given)
   int32_t dtype;
   uint64_t pmask;
   const void* k_hbm;

@@ -115,10 +115,14 @@ __device__ __forceinline__ const T* unit_keys(const LayerArgs& a, int b, int h) 
 }
 
 // ---------------------------------------------------------------- A1 reuse test
+struct HeadTau {
+  float t[kMaxKvHeads];
+};
+
 template <typename T>
 __global__ __launch_bounds__(64) void reuse_kernel(const T* __restrict__ q, const T* __restrict__ qp,
                                                    uint8_t* __restrict__ reuse, float* __restrict__ cosv,
-                                                   int Hkv, int Hq, int G, float tau) {
+                                                   int Hkv, int Hq, int G, HeadTau tau) {
   const int u = blockIdx.x;
   const int b = u / Hkv, h = u % Hkv;
   const int64_t off = ((int64_t)b * Hq + (int64_t)h * G) * kHeadDim;  // the group is contiguous
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(64) void reuse_kernel(const T* __restrict__ q, cons
   if (threadIdx.x == 0) {
     const float c = (na == 0.f || nb == 0.f) ? 0.f : dot / (sqrtf(na) * sqrtf(nb));
     if (cosv) cosv[u] = c;
-    reuse[u] = (c >= tau) ? 1 : 0;
+    reuse[u] = (c >= tau.t[h]) ? 1 : 0;
   }
 }
 
@@ -1313,12 +1317,14 @@ inline int grid_cap(int64_t items, int64_t cap) { return (int)(items < cap ? (it
 hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, uint8_t* reuse, float* cos,
                         hipStream_t s) {
   const int U = a.B * a.Hkv;
+  HeadTau th;
+  for (int h = 0; h < kMaxKvHeads; ++h) th.t[h] = a.tau_h[h];
   if (a.dtype == CLO_F32)
     reuse_kernel<float><<<U, 64, 0, s>>>(static_cast<const float*>(q), static_cast<const float*>(q_prev), reuse,
-                                         cos, a.Hkv, a.Hq, a.G, a.tau);
+                                         cos, a.Hkv, a.Hq, a.G, th);
   else
     reuse_kernel<uint16_t><<<U, 64, 0, s>>>(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(q_prev),
-                                            reuse, cos, a.Hkv, a.Hq, a.G, a.tau);
+                                            reuse, cos, a.Hkv, a.Hq, a.G, th);
   return hipGetLastError();
 }
 

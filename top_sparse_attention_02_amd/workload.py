@@ -83,8 +83,12 @@ class LayerBuffers:
                          self.v_cache, self.idx)
 
     def shape_with(self, tau: float) -> clo.Shape:
+        """The layer's shape with threshold tau (+inf: every unit misses, whatever
+        the per-head thresholds)."""
         s = clo.Shape(**self.shape.__dict__)
         s.tau = tau
+        if math.isinf(tau):
+            s.tau_heads = None
         return s
 
     def slot(self, kvh: int) -> int:
