@@ -57,6 +57,12 @@ def parse():
                     help="choose the persistent heads from profiling (mean reuse-test cosine per slot on "
                          "separately seeded instances, lowest first) instead of the seeded draw; same count")
     ap.add_argument("--profile-instances", type=int, default=8)
+    ap.add_argument("--host-kv", choices=["native", "int8"], default="native",
+                    help="format of the offloaded K/V in host memory: the step's dtype, or int8 rows with one "
+                         "power-of-two scale per row (half the host-link bytes of bf16; dequantized exactly "
+                         "by the gather)")
+    ap.add_argument("--no-compare-native", action="store_true",
+                    help="int8 host KV, configs 1-3: skip the output comparison against the native format")
     ap.add_argument("--growing", type=int, default=0, metavar="T",
                     help="configs 1-3: T decode steps over a context that grows by one appended token per "
                          "step, under both reference policies (previous step's query / query at the last "
@@ -70,7 +76,8 @@ def algorithmic_bytes(layers):
 
     HBM: M * N * d * b (scoring) + M_p * k * 2 d b (persistent miss rows)
          + M_np * k * 2 d b (cache writes) + H * k * 2 d b (rows of reuse units)
-    host: M_np * k * 2 d b
+    host: M_np * k * 2 d b_host (b_host = 1 for the int8 host format, whose row
+          exponents come from HBM: + M_np * k * 2 bytes there)
     """
     import numpy as np
 
@@ -93,8 +100,10 @@ def algorithmic_bytes(layers):
         tot["misses_host"] += M_np
         tot["hits"] += H
         tot["score_bytes"] += score
-        tot["hbm_bytes"] += score + M_p * row2 + M_np * row2 + H * row2
-        tot["host_bytes"] += M_np * row2
+        q8 = getattr(bufs, "host_format", 0) == 1
+        host_row2 = bufs.k * 2 * HEAD_DIM * (1 if q8 else b)
+        tot["hbm_bytes"] += score + M_p * row2 + M_np * row2 + H * row2 + (M_np * bufs.k * 2 if q8 else 0)
+        tot["host_bytes"] += M_np * host_row2
         tot["attn_bytes"] += bufs.B * bufs.Hkv * row2
         tot["flops"] += M * 2 * g * HEAD_DIM * bufs.N + bufs.B * bufs.Hkv * 4 * g * HEAD_DIM * bufs.k
     return tot
@@ -405,6 +414,25 @@ def profile_and_plan(torch, clo, gen, cfg: int, overrides: dict, instances: int)
             "volatile_persistent_seeded": int((base.persistent[:period] & vol).sum())}
 
 
+def compare_native(torch, workload, p, q8_layer, step_kind: int, flags) -> dict:
+    """Output of the int8-host-KV step against the same step with native host
+    rows (the same inputs loaded a second time): normwise relative deviation per
+    (sequence, query head), max_i |o_i - n_i| / max_i |n_i|, and how many
+    selections differ (none can: scoring reads the exact keys in both)."""
+    nat = workload.load_layer(p, 0, host_flags=flags)
+    for bufs in (nat, q8_layer):
+        bufs.step0()
+        if step_kind == 1:
+            bufs.step1()
+    torch.cuda.synchronize()
+    o, n = q8_layer.out.float(), nat.out.float()
+    dev = (o - n).abs().amax(-1) / n.abs().amax(-1).clamp_min(1e-30)
+    res = {"out_dev_mean": float(dev.mean()), "out_dev_max": float(dev.max()),
+           "selections_equal": bool(torch.equal(q8_layer.idx, nat.idx))}
+    del nat
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -452,10 +480,12 @@ def main():
              "coherent": hip_host.hipHostMallocMapped | hip_host.hipHostMallocCoherent,
              "noncoherent": hip_host.hipHostMallocMapped | hip_host.hipHostMallocNonCoherent}[args.host_memory]
     t0 = time.time()
+    host_format = clo.CLO_HOST_INT8 if args.host_kv == "int8" else clo.CLO_HOST_NATIVE
     if multi:
-        layers = workload.load_layers(p, log=log, host_flags=flags)
+        layers = workload.load_layers(p, log=log, host_flags=flags, host_format=host_format)
     else:
-        layers = [workload.load_layer(p, 0, log=log if p.batch >= 16 else None, host_flags=flags)]
+        layers = [workload.load_layer(p, 0, log=log if p.batch >= 16 else None, host_flags=flags,
+                                      host_format=host_format)]
     log(f"inputs generated and resident ({time.time() - t0:.1f} s)")
 
     probe = None
@@ -500,6 +530,11 @@ def main():
     ms_per_step = e0.elapsed_time(e1) / args.steps
     alg = algorithmic_bytes(layers)
 
+    quant = None
+    if host_format == clo.CLO_HOST_INT8 and not multi and not args.no_compare_native:
+        quant = compare_native(torch, workload, p, layers[0], args.step, flags)
+        log(f"int8 host KV vs native: output deviation mean {quant['out_dev_mean']:.2e}, "
+            f"max {quant['out_dev_max']:.2e}")
     phases = phase_times(torch, clo, layers, args.step, passes=args.steps if not multi else 2)
     gather_s = phases["gather"] / 1e3
     host_gbs = alg["host_bytes"] / gather_s / 1e9 if alg["host_bytes"] else 0.0
@@ -543,12 +578,15 @@ def main():
         "config": {"workload": f"config {args.config}: " + WORKLOADS[args.config] +
                    (", steady step (80/20 reuse)" if args.step == 1 else ", cold step (all miss)") +
                    (f", {args.volatile:.0%} volatile (layer, KV head) slots" if args.volatile else "") +
-                   (", persistent heads from profiling" if plan else ""),
+                   (", persistent heads from profiling" if plan else "") +
+                   (", int8 host KV (power-of-two row scales)" if args.host_kv == "int8" else ""),
                    "layers": p.layers, "batch": p.batch, "q_heads": p.hq, "kv_heads": p.hkv, "head_dim": HEAD_DIM,
                    "context": p.context, "topk": p.topk, "tau": p.tau, "step": args.step,
                    "data_layers": p.data_layers or p.layers, "host_memory": args.host_memory},
         "roofline": roofline,
         "persistent_plan": None if plan is None else {k: v for k, v in plan.items() if k != "persistent"},
+        "host_kv": args.host_kv,
+        "host_kv_vs_native": quant,
         "volatile_frac": args.volatile,
         "roofline_score": score_roofline(score_gbs, alg, args, multi),
         "attention_hbm_gbs": round(attn_gbs, 1),

@@ -35,7 +35,7 @@
  *  - Device buffers must be device memory of the current device; host K/V
  *    buffers must be pinned host memory that the device can address (e.g.
  *    hipHostMalloc); pageable host memory is rejected with CLO_E_ARG.  Every
- *    tensor pointer must be 16-byte aligned.  Where the runtime reports an
+ *    tensor pointer must be 16-byte aligned (int8 exponent arrays: any byte).  Where the runtime reports an
  *    allocation's extent, a tensor that would run past it is rejected.
  *  - Inputs must be finite; results for NaN/Inf inputs are unspecified (no
  *    out-of-bounds access happens either way).
@@ -47,7 +47,8 @@
  * persistent (or non-persistent) heads in head order:
  *   q, q_prev, out   [B, Hq, d]
  *   k_hbm, v_hbm     [B, P, C, d]   device   full K/V of persistent heads (rows < N used)
- *   k_host, v_host   [B, H, C, d]   pinned   full K/V of non-persistent heads
+ *   k_host, v_host   [B, H, C, d]   pinned   full K/V of non-persistent heads (int8 when
+ *                                            layer->host_format is CLO_HOST_INT8)
  *   k_score          [B, H, C, d]   device   copy of k_host read by scoring
  *   k_cache, v_cache [B, H, k, d]   device   rows k_host[idx], v_host[idx]
  *   idx              [B, Hkv, k]    int32    selected token indices, ascending
@@ -65,6 +66,17 @@ extern "C" {
 #endif
 
 typedef enum { CLO_F32 = 0, CLO_BF16 = 1 } clo_dtype;
+
+/* Element format of the offloaded K/V in host memory (clo_layer.host_format).
+ *   CLO_HOST_NATIVE  rows in the shape's dtype (the pages' format)
+ *   CLO_HOST_INT8    quantized rows: 128 int8 values q_i per row and one scale
+ *                    exponent e per row (int8, kept in device memory); the row's
+ *                    values are q_i * 2^e.  A row x is quantized as: m = max|x_i|;
+ *                    e = the smallest integer with m <= 127 * 2^e (e = 0 when m = 0),
+ *                    raised to -120 if smaller; q_i = x_i * 2^-e rounded to the
+ *                    nearest integer, ties to even.  q_i * 2^e is exact in bf16 and
+ *                    fp32, so dequantized rows are exact. */
+typedef enum { CLO_HOST_NATIVE = 0, CLO_HOST_INT8 = 1 } clo_host_format;
 
 typedef enum {
   CLO_OK = 0,
@@ -100,12 +112,15 @@ typedef struct {
   uint64_t persistent_mask;  /* bit h set: KV head h keeps its full K/V in HBM (same for all sequences) */
   const void* k_hbm;         /* [B, P, C, d] device; may be NULL when P == 0 */
   const void* v_hbm;
-  const void* k_host;        /* [B, H, C, d] pinned host; may be NULL when H == 0 */
+  const void* k_host;        /* [B, H, C, d] pinned host (dtype, or int8); may be NULL when H == 0 */
   const void* v_host;
   const void* k_score;       /* [B, H, C, d] device copy of k_host, read by scoring */
   void* k_cache;             /* [B, H, k, d] device, written for miss units, read by attention */
   void* v_cache;
   int32_t* idx;              /* [B, Hkv, k] device, written for miss units, read for all units */
+  int32_t host_format;       /* clo_host_format of k_host / v_host (0 = the shape's dtype) */
+  const int8_t* k_host_exp;  /* CLO_HOST_INT8: [B, H, C] device, row scale exponents of k_host */
+  const int8_t* v_host_exp;  /*                [B, H, C] device, of v_host */
 } clo_layer;
 
 /*
@@ -162,7 +177,8 @@ clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const
  * A4 -- gather (abstract features (2) and (3); synthesis 2.1 item 3).
  * For every miss unit of a non-persistent head: k_cache[u][i] = k_host[u][idx[u][i]]
  * and v_cache[u][i] = v_host[u][idx[u][i]], read by the GPU directly from pinned
- * host memory (bit-exact copies).  Persistent heads need no transfer: attention
+ * host memory (bit-exact copies; with CLO_HOST_INT8 the rows are dequantized
+ * exactly, q_i * 2^e, on the way into the cache).  Persistent heads need no transfer: attention
  * reads their rows in place.  reuse NULL = all units miss.  ws: device workspace
  * as for clo_topk_select (the gather's blocks take work from a counter in it;
  * calls that share one workspace must not overlap).  sync may be NULL.
@@ -208,7 +224,9 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
  * Writes k_new[b][h] and v_new[b][h] ([B, Hkv, d] device, dtype of the shape)
  * as row `position` of every (sequence, KV head): into k_hbm/v_hbm for
  * persistent heads; for the others into k_host/v_host, stored by the GPU
- * straight into pinned host memory, and into the k_score copy.  Requires
+ * straight into pinned host memory (quantized first when the layer's
+ * host_format is CLO_HOST_INT8, its exponents into k_host_exp/v_host_exp), and
+ * into the k_score copy.  Requires
  * 0 <= position < capacity (CLO_E_ARG otherwise); shape->context is not used
  * beyond validation and the row is visible to later calls on the same stream
  * (a decode step with context = position + 1 reads it).  k_cache, v_cache and
@@ -243,6 +261,17 @@ clo_status clo_update_reference(const clo_shape* shape, const void* q, const uin
  */
 clo_status clo_plan_persistent(const float* s_hat, int32_t n_layers, int32_t n_kv_heads, int32_t n_persist,
                                uint64_t* masks);
+
+/*
+ * Quantize rows for an int8 host copy (CLO_HOST_INT8; quantized offloaded KV,
+ * synthesis sections 3.3 and 5.6 on cutting the bytes that cross the host link).
+ * Reads n_rows rows of 128 elements of `dtype` from src (device), writes their
+ * int8 values to dst (device or pinned host memory, [n_rows, 128]) and their
+ * scale exponents to dst_exp (device, [n_rows]), by the rule documented at
+ * clo_host_format.  Finite inputs only.  sync may be NULL.
+ */
+clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int8_t* dst_exp,
+                             const clo_sync* sync, void* stream);
 
 /* Static text for a status code. */
 const char* clo_status_string(clo_status status);

@@ -4,9 +4,12 @@ from .clo_oracle import (  # noqa: F401
     attend,
     decode_layer,
     decode_steps_unit,
+    dequantize_row,
     decode_unit,
     group_cosine,
     plan_persistent,
+    quantize_row,
+    quantized_rows,
     reuse_decision,
     select_topk,
     token_scores,

@@ -35,6 +35,11 @@ Synthesis"; CLO abstract page on fugumt):
     tau per KV head, plan_persistent): synthesis section 3.1 attack point 6
     and section 5.3 -- offline profiling fixes each head's mean similarity,
     its threshold and the number of persistent heads.
+  * Quantized host KV (quantize_row, dequantize_row): synthesis sections 3.3
+    and 5.6 -- fewer bytes across the host link; the format (int8 values, one
+    power-of-two scale per row) is this implementation's choice, written out
+    at quantize_row.  Scoring keeps the exact keys; attention of offloaded
+    heads reads the dequantized rows (decode_unit's K_attn / V_attn).
   * Multi-step decoding (decode_steps_unit): synthesis section 2.1 item 2 --
     the similarity is between adjacent decode steps; section 5.6 -- the
     context grows by the decoded token and new KV is offloaded incrementally.
@@ -126,8 +131,11 @@ def attend(q_group: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, return_p: bool =
 
 
 def decode_unit(q_group, q_prev_group, K, V, k: int, tau: float,
-                idx_prev: Optional[np.ndarray] = None) -> Dict[str, object]:
-    """O1-O6 for one unit.  q_group/q_prev_group [g, d]; K, V [N, d] (float64)."""
+                idx_prev: Optional[np.ndarray] = None, K_attn=None, V_attn=None) -> Dict[str, object]:
+    """O1-O6 for one unit.  q_group/q_prev_group [g, d]; K, V [N, d] (float64).
+
+    K_attn / V_attn: the rows attention reads, when they differ from the keys
+    that are scored (a quantized host copy); default K and V."""
     c = group_cosine(q_group, q_prev_group)
     reuse = reuse_decision(c, tau)
     if reuse:
@@ -136,8 +144,8 @@ def decode_unit(q_group, q_prev_group, K, V, k: int, tau: float,
         sel = np.asarray(idx_prev, dtype=np.int64)
     else:
         sel = select_topk(token_scores(q_group, K), k)
-    Kc = np.asarray(K, dtype=np.float64)[sel]
-    Vc = np.asarray(V, dtype=np.float64)[sel]
+    Kc = np.asarray(K if K_attn is None else K_attn, dtype=np.float64)[sel]
+    Vc = np.asarray(V if V_attn is None else V_attn, dtype=np.float64)[sel]
     out = attend(q_group, Kc, Vc)
     return {"cos": c, "reuse": reuse, "idx": sel, "out": out}
 
@@ -145,13 +153,16 @@ def decode_unit(q_group, q_prev_group, K, V, k: int, tau: float,
 def decode_layer(q, q_prev, kv_of: Callable[[int, int], Tuple[np.ndarray, np.ndarray]],
                  hkv: int, k: int, tau, dtype: str,
                  idx_prev: Optional[np.ndarray] = None,
-                 units: Optional[Iterable[Tuple[int, int]]] = None) -> Dict[Tuple[int, int], Dict[str, object]]:
+                 units: Optional[Iterable[Tuple[int, int]]] = None,
+                 attn_kv_of=None) -> Dict[Tuple[int, int], Dict[str, object]]:
     """Run decode_unit over (b, kvh) units of one layer.
 
     q, q_prev: stored [B, Hq, d] arrays of `dtype`; kv_of(b, kvh) returns the
     stored [N, d] K and V of a unit; idx_prev: [B, Hkv, k] selections of the
     previous step (needed for reused units); tau: one threshold, or one per KV
-    head (per-head thresholds).  Returns {(b, kvh): result}.
+    head (per-head thresholds); attn_kv_of(b, kvh): float64 rows attention reads
+    instead of the stored K and V (None for a unit = the stored rows).
+    Returns {(b, kvh): result}.
     """
     qf = as_f64(q, dtype)
     qpf = as_f64(q_prev, dtype)
@@ -164,8 +175,10 @@ def decode_layer(q, q_prev, kv_of: Callable[[int, int], Tuple[np.ndarray, np.nda
         K, V = kv_of(b, kvh)
         prev = None if idx_prev is None else idx_prev[b, kvh]
         tau_u = float(tau[kvh]) if np.ndim(tau) else float(tau)
+        ka = attn_kv_of(b, kvh) if attn_kv_of else None
         res[(b, kvh)] = decode_unit(qf[b, kvh * g:(kvh + 1) * g], qpf[b, kvh * g:(kvh + 1) * g],
-                                    as_f64(K, dtype), as_f64(V, dtype), k, tau_u, prev)
+                                    as_f64(K, dtype), as_f64(V, dtype), k, tau_u, prev,
+                                    *(ka if ka is not None else (None, None)))
     return res
 
 
@@ -212,3 +225,39 @@ def plan_persistent(s_hat, n_persist: int):
     for i in order[:n_persist]:
         masks[i // H] |= 1 << (i % H)
     return masks
+
+
+QUANT_MIN_EXP = -120
+
+
+def quantize_row(x):
+    """Int8 host format of one row: (q, e) with x ~ q * 2^e.
+
+    m = max |x_i|; e = the smallest integer with m <= 127 * 2^e (0 for a zero
+    row), raised to -120 if smaller; q_i = x_i * 2^-e rounded to the nearest
+    integer, ties to even (|q_i| <= 127 by the choice of e).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m = float(np.max(np.abs(x))) if x.size else 0.0
+    if m == 0.0:
+        return np.zeros(x.shape, dtype=np.int64), 0
+    e = math.frexp(m)[1] - 1 - 6  # floor(log2 m) - 6
+    if m > 127.0 * 2.0 ** e:
+        e += 1
+    e = max(e, QUANT_MIN_EXP)
+    q = np.rint(x * 2.0 ** -e).astype(np.int64)
+    return q, e
+
+
+def dequantize_row(q, e: int) -> np.ndarray:
+    """q_i * 2^e (exact in float64, and in bf16 and fp32 since |q_i| <= 127)."""
+    return np.asarray(q, dtype=np.float64) * 2.0 ** e
+
+
+def quantized_rows(X) -> np.ndarray:
+    """Every row of X [n, d] through quantize_row and dequantize_row."""
+    X = np.asarray(X, dtype=np.float64)
+    out = np.empty_like(X)
+    for i in range(X.shape[0]):
+        out[i] = dequantize_row(*quantize_row(X[i]))
+    return out

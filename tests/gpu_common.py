@@ -73,8 +73,11 @@ def oracle_steps(p: gen.Problem, layer: int, units=None):
     return r0, r1, kv
 
 
-def compare(p: gen.Problem, bufs, got, ref, kv, step: str, units=None, check_cos=None):
-    """Assert GPU outputs of one step equal the oracle's (decisions and indices bit-exact)."""
+def compare(p: gen.Problem, bufs, got, ref, kv, step: str, units=None, check_cos=None, cache_of=None):
+    """Assert GPU outputs of one step equal the oracle's (decisions and indices bit-exact).
+
+    cache_of(b, kvh): the float64 rows a miss unit's cache must hold (default: the
+    stored K and V, bit for bit)."""
     g = p.g
     check_cos = (step == "step1") if check_cos is None else check_cos
     tol = TOL[p.dtype]
@@ -89,10 +92,17 @@ def compare(p: gen.Problem, bufs, got, ref, kv, step: str, units=None, check_cos
             extra = sorted(set(gi.tolist()) - set(r["idx"].tolist()))[:5]
             raise AssertionError(f"{where}: idx differs (missing {missing}, extra {extra})")
         if not bufs.is_persistent(h) and not r["reuse"]:
-            K, V = kv(b, h)
             s = bufs.slot(h)
-            assert np.array_equal(got["k_cache"][b, s], K[r["idx"]]), f"{where}: K cache rows differ"
-            assert np.array_equal(got["v_cache"][b, s], V[r["idx"]]), f"{where}: V cache rows differ"
+            if cache_of is not None:
+                Kq, Vq = cache_of(b, h)
+                assert np.array_equal(oracle.as_f64(got["k_cache"][b, s], p.dtype), Kq[r["idx"]]), \
+                    f"{where}: K cache rows differ from the dequantized rows"
+                assert np.array_equal(oracle.as_f64(got["v_cache"][b, s], p.dtype), Vq[r["idx"]]), \
+                    f"{where}: V cache rows differ from the dequantized rows"
+            else:
+                K, V = kv(b, h)
+                assert np.array_equal(got["k_cache"][b, s], K[r["idx"]]), f"{where}: K cache rows differ"
+                assert np.array_equal(got["v_cache"][b, s], V[r["idx"]]), f"{where}: V cache rows differ"
         o = got["out"][b, h * g:(h + 1) * g]
         ro = r["out"]
         err = np.abs(o - ro).max(axis=1) / np.maximum(np.abs(ro).max(axis=1), 1e-30)

@@ -389,6 +389,44 @@ def pin_plan_persistent(O):
         assert chosen == list(best)
 
 
+# ---------------------------------------------------------------- int8 host format
+def pin_quantize_closed_forms(O):
+    # m = 1: 127 * 2^-7 = 0.99 < 1 <= 127 * 2^-6 = 1.98, so e = -6 and q = x * 64
+    q, e = O.quantize_row([1.0, -0.5, 0.25, 0.0])
+    assert e == -6 and list(q) == [64, -32, 16, 0]
+    # m exactly 127 * 2^-6 stays at e = -6 (q = 127); the next float up needs e = -5
+    q, e = O.quantize_row([127 * 2.0 ** -6, 1.0])
+    assert e == -6 and list(q) == [127, 64]
+    q, e = O.quantize_row([np.nextafter(127 * 2.0 ** -6, 2.0), 1.0])
+    assert e == -5 and list(q) == [64, 32]
+    # halves round to even: with e = -1 (m = 63.5) x = 0.75 -> 1.5 -> 2, x = 1.25 -> 2.5 -> 2, -0.25 -> -0.5 -> 0
+    q, e = O.quantize_row([63.5, 0.75, 1.25, -0.25])
+    assert e == -1 and list(q) == [127, 2, 2, 0]
+    # zero rows and the smallest exponent
+    q, e = O.quantize_row([0.0, 0.0])
+    assert e == 0 and list(q) == [0, 0]
+    q, e = O.quantize_row([2.0 ** -130, -(2.0 ** -125)])
+    assert e == -120 and list(q) == [0, 0]
+    assert list(O.dequantize_row([64, -32, 16], -6)) == [1.0, -0.5, 0.25]
+
+
+def pin_quantize_invariants(O):
+    rng = np.random.default_rng(13)
+    for _ in range(200):
+        x = rng.standard_normal(128) * 2.0 ** rng.integers(-20, 20)
+        q, e = O.quantize_row(x)
+        m = np.max(np.abs(x))
+        assert np.max(np.abs(q)) <= 127 and m <= 127 * 2.0 ** e and not m <= 127 * 2.0 ** (e - 1)
+        xd = O.dequantize_row(q, e)
+        assert np.max(np.abs(xd - x)) <= 2.0 ** (e - 1)  # round to nearest
+        # every dequantized value fits bfloat16 exactly (at most 8 significant bits)
+        mant = np.abs(xd[xd != 0]) / 2.0 ** np.floor(np.log2(np.abs(xd[xd != 0])))
+        assert np.all(mant * 128 == np.round(mant * 128))
+        # scaling by a power of two shifts e and keeps q
+        q2, e2 = O.quantize_row(x * 8.0)
+        assert e2 == e + 3 and list(q2) == list(q)
+
+
 def pin_bf16_decoding(O):
     # IEEE facts about bfloat16 bit patterns
     bits = np.array([0x3F80, 0xC000, 0x3FC0, 0x0000, 0x8000, 0x7F7F, 0x0001, 0x4049], dtype=np.uint16)
@@ -421,5 +459,7 @@ ALL_PINS = [
     pin_multistep_limits,
     pin_per_head_thresholds,
     pin_plan_persistent,
+    pin_quantize_closed_forms,
+    pin_quantize_invariants,
     pin_bf16_decoding,
 ]

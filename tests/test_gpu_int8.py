@@ -1,0 +1,164 @@
+"""Int8 host KV (CLO_HOST_INT8) on the GPU against the oracle.
+
+Rows quantize to int8 values with one power-of-two scale per row; the gather
+dequantizes them exactly into the HBM cache.  Quantized values and exponents,
+selections and cache rows must equal the oracle's bit for bit; outputs (the
+oracle attending the dequantized rows of offloaded heads) within the usual
+tolerances."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_common import compare, log, small_problem, snapshot, to_numpy
+from tests.margins import enforce_margins, enforce_walk_margins
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(rng, n, dtype):
+    x = rng.standard_normal((n, 128)) * 2.0 ** rng.integers(-30, 30, size=(n, 1)).astype(np.float64)
+    x[0] = 0.0                                     # zero row
+    x[1] = rng.standard_normal(128) * 2.0 ** -125  # below the smallest exponent
+    x[2, :] = 0.0
+    x[2, 5] = 127 * 2.0 ** -6                      # exactly at an exponent boundary
+    if dtype == "f32":
+        return x.astype(np.float32)
+    b = x.astype(np.float32).view(np.uint32)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)  # bf16 patterns, RNE
+
+
+@pytest.mark.parametrize("where", ["host", "device"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_rows_match_oracle(need_gpu, dtype, where):
+    import torch
+
+    from top_sparse_attention_02_amd import clo, workload
+    from top_sparse_attention_02_amd.hip_host import HostBuffer
+
+    rng = np.random.default_rng(21)
+    n = 1000
+    x = _rows(rng, n, dtype)
+    src = workload.host_rows_tensor(x, dtype)
+    exp = torch.zeros(n, dtype=torch.int8, device="cuda")
+    if where == "host":
+        host = HostBuffer(n * 128)
+        clo.clo_quantize_rows(src, n, workload.clo_dtype(dtype), host.ptr, exp)
+        torch.cuda.synchronize()
+        q = host.numpy(np.int8, (n, 128)).copy()
+    else:
+        dst = torch.zeros(n, 128, dtype=torch.int8, device="cuda")
+        clo.clo_quantize_rows(src, n, workload.clo_dtype(dtype), dst, exp)
+        q = dst.cpu().numpy()
+    e = exp.cpu().numpy()
+    xf = oracle.as_f64(x, dtype)
+    for i in range(n):
+        rq, re = oracle.quantize_row(xf[i])
+        assert e[i] == re and np.array_equal(q[i].astype(np.int64), rq), f"row {i}"
+
+
+def _int8_problem(name, **kw):
+    return small_problem(name, **kw)
+
+
+CASES = {
+    "bf16_g4_mixed": dict(batch=2, hq=8, hkv=2, context=3000, topk=300, dtype="bf16", persistent=[1, 0],
+                          heavy_frac=0.005),
+    "f32_g5_host": dict(batch=2, hq=10, hkv=2, context=2500, topk=250, dtype="f32", persistent=[0, 0]),
+}
+
+
+def _cache_of(p, kvs, layer=0):
+    memo = {}
+
+    def f(b, h):
+        if (b, h) not in memo:
+            K, V = kvs(b, h)
+            memo[(b, h)] = (oracle.quantized_rows(oracle.as_f64(K, p.dtype)),
+                            oracle.quantized_rows(oracle.as_f64(V, p.dtype)))
+        return memo[(b, h)]
+    return f
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_int8_host_decode_matches_oracle(need_gpu, name):
+    from top_sparse_attention_02_amd import clo, workload
+
+    p = _int8_problem("int8_" + name, **CASES[name])
+    enforce_margins(p, 0)
+    log(f"[case int8 {name}] B={p.batch} Hq={p.hq} Hkv={p.hkv} N={p.context} k={p.topk} {p.dtype}")
+    bufs = workload.load_layer(p, 0, host_format=clo.CLO_HOST_INT8)
+    bufs.step0()
+    got0 = snapshot(bufs)
+    bufs.step1()
+    got1 = snapshot(bufs)
+    memo = {}
+
+    def kv(b, h):
+        if (b, h) not in memo:
+            memo[(b, h)] = (p.kv("k", 0, b, h), p.kv("v", 0, b, h))
+        return memo[(b, h)]
+
+    cache_of = _cache_of(p, kv)
+    attn = lambda b, h: None if bufs.is_persistent(h) else cache_of(b, h)  # noqa: E731
+    qp, q = p.q_prev(0), p.q(0)
+    r0 = oracle.decode_layer(qp, qp, kv, p.hkv, p.topk, math.inf, p.dtype, attn_kv_of=attn)
+    idx0 = np.zeros((p.batch, p.hkv, p.topk), dtype=np.int64)
+    for (b, h), r in r0.items():
+        idx0[b, h] = r["idx"]
+    r1 = oracle.decode_layer(q, qp, kv, p.hkv, p.topk, p.tau, p.dtype, idx_prev=idx0, attn_kv_of=attn)
+    compare(p, bufs, got0, r0, kv, "step0", cache_of=cache_of)
+    compare(p, bufs, got1, r1, kv, "step1", cache_of=cache_of)
+
+
+def test_int8_growing_context(need_gpu):
+    from top_sparse_attention_02_amd import clo, workload
+
+    steps = 5
+    p = _int8_problem("int8_growing", batch=2, hq=8, hkv=2, context=3000 + steps, topk=300, dtype="bf16",
+                      persistent=[0, 1], low_frac=0.2)
+    enforce_walk_margins(p, 0, steps)
+    log(f"[case int8 growing] N={p.context - steps}+{steps}")
+    run = workload.GrowingRun(p, 0, steps, "refresh", host_format=clo.CLO_HOST_INT8)
+    g, n0 = p.g, p.context - steps
+    kvs = {(b, h): (p.kv("k", 0, b, h), p.kv("v", 0, b, h)) for b in range(p.batch) for h in range(p.hkv)}
+    kv = lambda b, h: kvs[(b, h)]  # noqa: E731
+    cache_of = _cache_of(p, kv)
+    qs = [oracle.as_f64(p.q_walk(0, t), p.dtype) for t in range(steps + 1)]
+    ref = {}
+    for (b, h), (K, V) in kvs.items():
+        Ka, Va = cache_of(b, h) if not run.bufs.is_persistent(h) else (oracle.as_f64(K, p.dtype),
+                                                                      oracle.as_f64(V, p.dtype))
+        sl = slice(h * g, (h + 1) * g)
+        # scoring reads the exact keys, attention the (dequantized) rows of the host copy
+        res, r_ref, sel = [], None, None
+        for t in range(steps + 1):
+            n = n0 + t
+            Kf, Vf = oracle.as_f64(K, p.dtype)[:n], oracle.as_f64(V, p.dtype)[:n]
+            if t == 0:
+                r = oracle.decode_unit(qs[0][b, sl], qs[0][b, sl], Kf, Vf, p.topk, math.inf, None, Ka[:n], Va[:n])
+            else:
+                r = oracle.decode_unit(qs[t][b, sl], r_ref, Kf, Vf, p.topk, p.tau, sel, Ka[:n], Va[:n])
+            sel = r["idx"]
+            if not r["reuse"]:
+                r_ref = qs[t][b, sl]
+            res.append(r)
+        ref[(b, h)] = res
+    for t in range(steps + 1):
+        run.step(t)
+        got = snapshot(run.bufs)
+        compare(p, run.bufs, got, {u: r[t] for u, r in ref.items()}, kv, f"step{t}", check_cos=t > 0,
+                cache_of=cache_of)
+    # the appended rows were quantized on the GPU into pinned memory, exponents into HBM
+    b = run.bufs
+    for (bb, h), (K, V) in kvs.items():
+        if b.is_persistent(h):
+            continue
+        s = b.slot(h)
+        for which, X, exps in (("k", K, b.k_exp), ("v", V, b.v_exp)):
+            hv = b.host_view(which, bb, h)
+            ex = exps[bb, s].cpu().numpy()
+            for row in range(n0, p.context):
+                rq, re = oracle.quantize_row(oracle.as_f64(X[row], p.dtype))
+                assert ex[row] == re and np.array_equal(hv[row].astype(np.int64), rq), (which, bb, h, row)

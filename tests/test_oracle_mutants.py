@@ -73,8 +73,9 @@ def _ns(**over):
         ns.decode_layer = lambda *a, **kw: decode_layer(*a, head_of=over["head_of"], **kw)
     if "tau_of" in over:
         ns.decode_layer = lambda *a, **kw: decode_layer(*a, tau_of=over["tau_of"], **kw)
-    if "plan_persistent" not in over:
-        ns.plan_persistent = base.plan_persistent
+    for name in ("plan_persistent", "quantize_row", "dequantize_row"):
+        if name not in over:
+            setattr(ns, name, getattr(base, name))
     return ns
 
 
@@ -154,6 +155,23 @@ def m_plan_ties_to_higher_index(s_hat, n):
     return masks
 
 
+def m_quant_floor(x):
+    q, e = base.quantize_row(x)
+    return np.floor(np.asarray(x, float) * 2.0 ** -e).astype(np.int64), e
+
+
+def m_quant_exponent_low(x):
+    q, e = base.quantize_row(x)
+    e -= 1
+    return np.clip(np.rint(np.asarray(x, float) * 2.0 ** -e), -127, 127).astype(np.int64), e
+
+
+def m_quant_half_away(x):
+    q, e = base.quantize_row(x)
+    y = np.asarray(x, float) * 2.0 ** -e
+    return (np.sign(y) * np.floor(np.abs(y) + 0.5)).astype(np.int64), e
+
+
 MUTANTS = {
     "score_sum_over_heads": dict(token_scores=m_sum_over_heads),
     "cosine_mean_of_heads": dict(group_cosine=m_mean_head_cosine),
@@ -173,6 +191,10 @@ MUTANTS = {
     "tau_heads_reversed": dict(tau_of=lambda tau, h: float(tau[::-1][h]) if np.ndim(tau) else float(tau)),
     "plan_highest_similarity": dict(plan_persistent=m_plan_highest_first),
     "plan_ties_to_higher_index": dict(plan_persistent=m_plan_ties_to_higher_index),
+    "quant_floor": dict(quantize_row=m_quant_floor),
+    "quant_exponent_low": dict(quantize_row=m_quant_exponent_low),
+    "quant_ties_away": dict(quantize_row=m_quant_half_away),
+    "dequant_wrong_sign_exponent": dict(dequantize_row=lambda q, e: np.asarray(q, float) * 2.0 ** -e),
     "steps_context_fixed": dict(steps_kw=dict(grow=0)),
     "steps_context_one_late": dict(steps_kw=dict(lag=1)),
     "steps_refresh_never_updates": dict(steps_kw=dict(rules={"refresh": "never"})),

@@ -14,12 +14,13 @@ from typing import Optional, Sequence
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libclo.so")
 
 CLO_F32, CLO_BF16 = 0, 1
+CLO_HOST_NATIVE, CLO_HOST_INT8 = 0, 1
 CLO_OK, CLO_E_ARG, CLO_E_UNSUPPORTED, CLO_E_WORKSPACE, CLO_E_HIP, CLO_E_TIMEOUT = range(6)
 
 # every function include/clo.h declares
 EXPORTS = ("clo_workspace_size", "clo_reuse_test", "clo_topk_select", "clo_gather_kv", "clo_sparse_attn",
-           "clo_decode_step", "clo_append_kv", "clo_update_reference", "clo_plan_persistent", "clo_status_string",
-           "clo_last_error")
+           "clo_decode_step", "clo_append_kv", "clo_update_reference", "clo_plan_persistent", "clo_quantize_rows",
+           "clo_status_string", "clo_last_error")
 
 
 class CloError(RuntimeError):
@@ -38,7 +39,8 @@ class clo_shape(ctypes.Structure):
 class clo_layer(ctypes.Structure):
     _fields_ = [("persistent_mask", ctypes.c_uint64), ("k_hbm", ctypes.c_void_p), ("v_hbm", ctypes.c_void_p),
                 ("k_host", ctypes.c_void_p), ("v_host", ctypes.c_void_p), ("k_score", ctypes.c_void_p),
-                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("idx", ctypes.c_void_p)]
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("idx", ctypes.c_void_p),
+                ("host_format", ctypes.c_int32), ("k_host_exp", ctypes.c_void_p), ("v_host_exp", ctypes.c_void_p)]
 
 
 class clo_sync(ctypes.Structure):
@@ -75,6 +77,8 @@ def load():
         L.clo_append_kv.argtypes = [P(clo_shape), P(clo_layer), vp, vp, ctypes.c_int64, P(clo_sync), vp]
         L.clo_update_reference.restype = st
         L.clo_update_reference.argtypes = [P(clo_shape), vp, vp, vp, P(clo_sync), vp]
+        L.clo_quantize_rows.restype = st
+        L.clo_quantize_rows.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, P(clo_sync), vp]
         L.clo_plan_persistent.restype = st
         L.clo_plan_persistent.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
         L.clo_status_string.restype = ctypes.c_char_p
@@ -170,10 +174,14 @@ class Layer:
     k_cache: object = None
     v_cache: object = None
     idx: object = None
+    host_format: int = 0  # CLO_HOST_NATIVE or CLO_HOST_INT8
+    k_host_exp: object = None
+    v_host_exp: object = None
 
     def c(self) -> clo_layer:
         return clo_layer(self.persistent_mask, ptr(self.k_hbm), ptr(self.v_hbm), ptr(self.k_host), ptr(self.v_host),
-                         ptr(self.k_score), ptr(self.k_cache), ptr(self.v_cache), ptr(self.idx))
+                         ptr(self.k_score), ptr(self.k_cache), ptr(self.v_cache), ptr(self.idx), self.host_format,
+                         ptr(self.k_host_exp), ptr(self.v_host_exp))
 
 
 @dataclass
@@ -238,6 +246,11 @@ def clo_append_kv(shape: Shape, layer: Layer, k_new, v_new, position: int, sync:
 def clo_update_reference(shape: Shape, q, reuse, q_ref, sync: Optional[Sync] = None, stream=None):
     _check(load().clo_update_reference(ctypes.byref(shape.c()), ptr(q), ptr(reuse), ptr(q_ref), _sync(sync),
                                        stream_handle(stream)), "clo_update_reference")
+
+
+def clo_quantize_rows(src, n_rows: int, dtype: int, dst, dst_exp, sync: Optional[Sync] = None, stream=None):
+    _check(load().clo_quantize_rows(ptr(src), int(n_rows), int(dtype), ptr(dst), ptr(dst_exp), _sync(sync),
+                                    stream_handle(stream)), "clo_quantize_rows")
 
 
 def clo_plan_persistent(s_hat, n_persist: int):

@@ -74,9 +74,10 @@ clo_status check_shape(const clo_shape* s) {
 }
 
 // Device memory of this process (torch allocations, hipMalloc, managed).
-clo_status check_device(const void* p, size_t bytes, const char* name) {
+clo_status check_device(const void* p, size_t bytes, const char* name, uintptr_t align = 16) {
   if (!p) return fail(CLO_E_ARG, "%s is NULL", name);
-  if (reinterpret_cast<uintptr_t>(p) & 15u) return fail(CLO_E_ARG, "%s is not 16-byte aligned", name);
+  if (reinterpret_cast<uintptr_t>(p) & (align - 1))
+    return fail(CLO_E_ARG, "%s is not %zu-byte aligned", name, (size_t)align);
   hipPointerAttribute_t at;
   if (hipPointerGetAttributes(&at, p) != hipSuccess) {
     (void)hipGetLastError();
@@ -295,10 +296,21 @@ clo_status check_layer(const clo_layer* l, Plan* p, unsigned need) {
     if (need & NEED_HOST) {
       const void* dk = nullptr;
       const void* dv = nullptr;
-      if ((st = check_host(l->k_host, full_bytes(*p, a.H), "layer.k_host", &dk))) return st;
-      if ((st = check_host(l->v_host, full_bytes(*p, a.H), "layer.v_host", &dv))) return st;
+      if (l->host_format != CLO_HOST_NATIVE && l->host_format != CLO_HOST_INT8)
+        return fail(CLO_E_ARG, "layer.host_format %d is not a clo_host_format", l->host_format);
+      a.host_fmt = l->host_format;
+      const size_t rows = (size_t)a.B * a.H * (size_t)a.C;
+      const size_t hb = a.host_fmt == CLO_HOST_INT8 ? rows * kHeadDim : full_bytes(*p, a.H);
+      if ((st = check_host(l->k_host, hb, "layer.k_host", &dk))) return st;
+      if ((st = check_host(l->v_host, hb, "layer.v_host", &dv))) return st;
       a.k_host = dk;
       a.v_host = dv;
+      if (a.host_fmt == CLO_HOST_INT8) {
+        if ((st = check_device(l->k_host_exp, rows, "layer.k_host_exp", 1))) return st;
+        if ((st = check_device(l->v_host_exp, rows, "layer.v_host_exp", 1))) return st;
+        a.k_exp = l->k_host_exp;
+        a.v_exp = l->v_host_exp;
+      }
     }
     if (need & NEED_CACHE) {
       if ((st = check_device(l->k_cache, cache_bytes(*p), "layer.k_cache"))) return st;
@@ -607,6 +619,29 @@ clo_status clo_plan_persistent(const float* s_hat, int32_t n_layers, int32_t n_k
     masks[slot / n_kv_heads] |= 1ull << (slot % n_kv_heads);
   }
   return ok();
+}
+
+clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int8_t* dst_exp,
+                             const clo_sync* sync, void* stream) {
+  clo_status st;
+  if (dtype != CLO_F32 && dtype != CLO_BF16) return fail(CLO_E_UNSUPPORTED, "dtype %d is not fp32 or bf16", dtype);
+  if (n_rows < 0) return fail(CLO_E_ARG, "n_rows %lld < 0", (long long)n_rows);
+  if ((st = check_sync_flags(sync))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_rows == 0) {
+    if ((st = pre_wait(sync, s))) return st;
+    return post_signal(sync, s);
+  }
+  const size_t e = dtype == CLO_F32 ? 4 : 2;
+  if ((st = check_device(src, (size_t)n_rows * kHeadDim * e, "src"))) return st;
+  const void* d = nullptr;
+  if ((st = check_host(dst, (size_t)n_rows * kHeadDim, "dst", &d))) return st;  // device memory passes too
+  if ((st = check_device(dst_exp, (size_t)n_rows, "dst_exp", 1))) return st;
+  if ((st = pre_wait(sync, s))) return st;
+  if ((st = hip_status(launch_quantize_rows(src, n_rows, dtype, static_cast<int8_t*>(const_cast<void*>(d)), dst_exp, s),
+                       "quantize launch")))
+    return st;
+  return post_signal(sync, s);
 }
 
 const char* clo_status_string(clo_status status) {

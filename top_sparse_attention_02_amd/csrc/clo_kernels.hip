@@ -979,6 +979,160 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
   }
 }
 
+// Int8 host rows (CLO_HOST_INT8): 128 bytes per row, 8 lanes of 16 values each;
+// the row's exponent e (device memory) turns q into q * 2^e, exact in T.  The
+// rest is the native kernel's scheme: items of 256 rows from a counter, the
+// item's source rows and exponents preloaded into LDS, 2 rows of K and V deep
+// per lane.
+__device__ __forceinline__ float pow2f(int e) { return __int_as_float((e + 127) << 23); }  // -126 <= e <= 127
+
+template <typename T>
+__device__ __forceinline__ void store_deq16(T* dst, u32x4 w, float scale);
+template <>
+__device__ __forceinline__ void store_deq16<uint16_t>(uint16_t* dst, u32x4 w, float scale) {
+  u32x4 o[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = w[i];
+    // four signed bytes -> exact products q * 2^e -> bf16 (exact: q has 7 bits)
+    const float f0 = (float)(int8_t)(x & 0xFFu) * scale, f1 = (float)(int8_t)((x >> 8) & 0xFFu) * scale;
+    const float f2 = (float)(int8_t)((x >> 16) & 0xFFu) * scale, f3 = (float)(int8_t)(x >> 24) * scale;
+    o[i / 2][(i % 2) * 2] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+    o[i / 2][(i % 2) * 2 + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
+  }
+  reinterpret_cast<u32x4*>(dst)[0] = o[0];
+  reinterpret_cast<u32x4*>(dst)[1] = o[1];
+}
+template <>
+__device__ __forceinline__ void store_deq16<float>(float* dst, u32x4 w, float scale) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = w[i];
+    u32x4 o;
+    o[0] = __float_as_uint((float)(int8_t)(x & 0xFFu) * scale);
+    o[1] = __float_as_uint((float)(int8_t)((x >> 8) & 0xFFu) * scale);
+    o[2] = __float_as_uint((float)(int8_t)((x >> 16) & 0xFFu) * scale);
+    o[3] = __float_as_uint((float)(int8_t)(x >> 24) * scale);
+    reinterpret_cast<u32x4*>(dst)[i] = o;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gather_q8_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp,
+                                                        uint32_t* __restrict__ counter) {
+  constexpr int LPR = kHeadDim / 16;  // lanes per int8 row
+  constexpr int RPI = 256 / LPR;
+  constexpr int UNR = kGatherUnroll;
+  __shared__ uint32_t s_item;
+  __shared__ int32_t s_src[kGatherChunk];
+  __shared__ float s_sk[kGatherChunk], s_sv[kGatherChunk];  // 2^e of the item's K and V rows
+  const int nch = (int)((a.k + kGatherChunk - 1) / kGatherChunk);
+  const int lo = sp.list ? *sp.lo : 0;
+  const int64_t n_units = sp.list ? (int64_t)(*sp.hi - lo) : (int64_t)a.B * a.Hkv;
+  const int64_t items = n_units * nch;
+  const int sub = threadIdx.x % LPR, rl = threadIdx.x / LPR;
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(counter, 1u);
+    __syncthreads();
+    const int64_t it = s_item;
+    __syncthreads();
+    if (it >= items) break;  // uniform per block
+    const int u = sp.list ? sp.list[lo + it / nch] : (int)(it / nch);
+    const int c = (int)(it % nch);
+    const int b = u / a.Hkv, h = u % a.Hkv;
+    if (!sp.list && (((a.pmask >> h) & 1ull) || (reuse && reuse[u]))) continue;
+    const int64_t slot = (int64_t)b * a.H + head_slot(a.pmask, h);
+    const char* ks = static_cast<const char*>(a.k_host) + slot * a.C * kHeadDim;
+    const char* vs = static_cast<const char*>(a.v_host) + slot * a.C * kHeadDim;
+    T* kd = static_cast<T*>(a.k_cache) + slot * a.k * kHeadDim;
+    T* vd = static_cast<T*>(a.v_cache) + slot * a.k * kHeadDim;
+    const int32_t* ix = a.idx + (int64_t)u * a.k;
+    const int64_t r0 = (int64_t)c * kGatherChunk;
+    const int64_t r_end = (r0 + kGatherChunk < a.k) ? r0 + kGatherChunk : a.k;
+    if (r0 + threadIdx.x < r_end) {
+      int32_t src = ix[r0 + threadIdx.x];
+      src = src < 0 ? 0 : (src >= a.N ? (int32_t)(a.N - 1) : src);
+      s_src[threadIdx.x] = src;
+      s_sk[threadIdx.x] = pow2f(a.k_exp[slot * a.C + src]);
+      s_sv[threadIdx.x] = pow2f(a.v_exp[slot * a.C + src]);
+    }
+    __syncthreads();
+    for (int64_t rb = r0; rb < r_end; rb += RPI * UNR) {
+      u32x4 kx[UNR], vx[UNR];
+#pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        int64_t row = rb + j * RPI + rl;
+        row = row < r_end ? row : r_end - 1;
+        const int64_t src = s_src[row - r0];
+        kx[j] = *reinterpret_cast<const u32x4*>(ks + src * kHeadDim + sub * 16);
+        vx[j] = *reinterpret_cast<const u32x4*>(vs + src * kHeadDim + sub * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        const int64_t row = rb + j * RPI + rl;
+        if (row < r_end) {
+          store_deq16<T>(kd + row * kHeadDim + sub * 16, kx[j], s_sk[row - r0]);
+          store_deq16<T>(vd + row * kHeadDim + sub * 16, vx[j], s_sv[row - r0]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- int8 quantization
+// Row quantization of the int8 host format by one wave: lane l holds elements
+// 2l and 2l+1.  m = max|x|; e = the smallest integer with m <= 127 * 2^e (0 for a
+// zero row), at least kQuantMinExp; q = x * 2^-e rounded to nearest even.
+__device__ __forceinline__ int quant_exponent(float m) {
+  if (m == 0.f) return 0;
+  int E;
+  frexpf(m, &E);  // m = f * 2^E, 0.5 <= f < 1
+  int e = E - 1 - 6;
+  if (m > ldexpf(127.f, e)) e += 1;
+  return e < kQuantMinExp ? kQuantMinExp : e;
+}
+
+__device__ __forceinline__ uint32_t quant_pair(float x0, float x1, int e) {
+  const float inv = ldexpf(1.f, -e);  // exact power of two
+  const int q0 = (int)rintf(x0 * inv), q1 = (int)rintf(x1 * inv);
+  return (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8);
+}
+
+template <typename T>
+__device__ __forceinline__ void load_pair(const T* row, int lane, float& x0, float& x1);
+template <>
+__device__ __forceinline__ void load_pair<uint16_t>(const uint16_t* row, int lane, float& x0, float& x1) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(row)[lane];
+  x0 = bf_lo(w);
+  x1 = bf_hi(w);
+}
+template <>
+__device__ __forceinline__ void load_pair<float>(const float* row, int lane, float& x0, float& x1) {
+  const float2 v = reinterpret_cast<const float2*>(row)[lane];
+  x0 = v.x;
+  x1 = v.y;
+}
+
+// Quantizes one row held by a wave and stores 2 bytes per lane plus the exponent.
+template <typename T>
+__device__ __forceinline__ void quantize_row_wave(const T* row, int8_t* dst, int8_t* dst_exp) {
+  const int lane = threadIdx.x & 63;
+  float x0, x1;
+  load_pair<T>(row, lane, x0, x1);
+  const float m = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+  const int e = quant_exponent(m);
+  reinterpret_cast<uint16_t*>(dst)[lane] = (uint16_t)quant_pair(x0, x1, e);
+  if (lane == 0) *dst_exp = (int8_t)e;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict__ src, int64_t n_rows, int8_t* dst,
+                                                            int8_t* __restrict__ dst_exp) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;  // whole wave
+  quantize_row_wave<T>(src + row * kHeadDim, dst + row * kHeadDim, dst_exp + row);
+}
+
 __global__ void zero_kernel(uint32_t* word) {
   if (threadIdx.x == 0) *word = 0u;
 }
@@ -1250,6 +1404,15 @@ __global__ __launch_bounds__(64) void append_kernel(LayerArgs a, const T* __rest
   const int64_t rows = pers ? a.P : a.H;
   const int64_t dst = (((int64_t)b * rows + head_slot(a.pmask, h)) * a.C + position) * kHeadDim;
   const int64_t src = (int64_t)u * kHeadDim;
+  if (!pers && a.host_fmt == CLO_HOST_INT8) {
+    // the int8 host copy gets the quantized row, the score copy the exact one
+    const int64_t er = dst / kHeadDim;
+    quantize_row_wave<T>(k_new + src, reinterpret_cast<int8_t*>(k_host) + dst, const_cast<int8_t*>(a.k_exp) + er);
+    quantize_row_wave<T>(v_new + src, reinterpret_cast<int8_t*>(v_host) + dst, const_cast<int8_t*>(a.v_exp) + er);
+    for (int i = threadIdx.x; i < kPieces; i += 64)
+      reinterpret_cast<u32x4*>(k_score + dst)[i] = reinterpret_cast<const u32x4*>(k_new + src)[i];
+    return;
+  }
   for (int i = threadIdx.x; i < kPieces; i += 64) {
     const u32x4 kv = reinterpret_cast<const u32x4*>(k_new + src)[i];
     const u32x4 vv = reinterpret_cast<const u32x4*>(v_new + src)[i];
@@ -1375,10 +1538,28 @@ hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, Span sp, int6
                          uint32_t* counter, hipStream_t s) {
   const int64_t nch = (a.k + kGatherChunk - 1) / kGatherChunk;
   const int grid = grid_cap(max_units * nch, (int64_t)max_blocks);
-  if (a.dtype == CLO_F32)
+  if (a.host_fmt == CLO_HOST_INT8) {
+    if (a.dtype == CLO_F32)
+      gather_q8_kernel<float><<<grid, 256, 0, s>>>(a, reuse, sp, counter);
+    else
+      gather_q8_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse, sp, counter);
+  } else if (a.dtype == CLO_F32) {
     gather_kernel<float><<<grid, 256, 0, s>>>(a, reuse, sp, counter);
-  else
+  } else {
     gather_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse, sp, counter);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int8_t* dst_exp,
+                                hipStream_t s) {
+  const int64_t blocks = (n_rows + 3) / 4;
+  if (blocks <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)blocks;
+  if (dtype == CLO_F32)
+    quantize_rows_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(src), n_rows, dst, dst_exp);
+  else
+    quantize_rows_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), n_rows, dst, dst_exp);
   return hipGetLastError();
 }
 

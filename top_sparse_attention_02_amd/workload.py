@@ -37,9 +37,10 @@ class LayerBuffers:
 
     def __init__(self, batch: int, hq: int, hkv: int, context: int, topk: int, dtype: str, persistent_mask: int,
                  tau: float, device: str = "cuda", host_flags: int = hipHostMallocMapped,
-                 share: Optional["LayerBuffers"] = None):
+                 share: Optional["LayerBuffers"] = None, host_format: int = clo.CLO_HOST_NATIVE):
         self.B, self.Hq, self.Hkv, self.N, self.k = batch, hq, hkv, context, topk
         self.dtype, self.tau, self.mask = dtype, tau, persistent_mask
+        self.host_format = host_format
         self.P = bin(persistent_mask).count("1")
         self.H = hkv - self.P
         tdt = torch_dtype(dtype)
@@ -53,10 +54,12 @@ class LayerBuffers:
         self.idx = torch.zeros(batch, hkv, topk, dtype=torch.int32, device=dev)
         # inputs (full K/V): shared with `share` when layers alias the same data
         self.shared = share is not None
+        self.k_exp = self.v_exp = None
         if share is not None:
             assert share.mask == persistent_mask and share.N == context and share.B == batch
             self.k_hbm, self.v_hbm = share.k_hbm, share.v_hbm
             self.k_host, self.v_host, self.k_score = share.k_host, share.v_host, share.k_score
+            self.host_format, self.k_exp, self.v_exp = share.host_format, share.k_exp, share.v_exp
         else:
             self.k_hbm = self.v_hbm = None
             if self.P:
@@ -64,10 +67,14 @@ class LayerBuffers:
                 self.v_hbm = torch.empty_like(self.k_hbm)
             self.k_host = self.v_host = self.k_score = None
             if self.H:
-                nb = batch * self.H * context * d * elem_bytes(dtype)
+                hb = 1 if host_format == clo.CLO_HOST_INT8 else elem_bytes(dtype)
+                nb = batch * self.H * context * d * hb
                 self.k_host = HostBuffer(nb, host_flags)
                 self.v_host = HostBuffer(nb, host_flags)
                 self.k_score = torch.empty(batch, self.H, context, d, dtype=tdt, device=dev)
+                if host_format == clo.CLO_HOST_INT8:
+                    self.k_exp = torch.zeros(batch, self.H, context, dtype=torch.int8, device=dev)
+                    self.v_exp = torch.zeros_like(self.k_exp)
         # outputs and per-layer state
         self.k_cache = self.v_cache = None
         if self.H:
@@ -80,7 +87,7 @@ class LayerBuffers:
     # ----------------------------------------------------------------- views
     def layer(self) -> clo.Layer:
         return clo.Layer(self.mask, self.k_hbm, self.v_hbm, self.k_host, self.v_host, self.k_score, self.k_cache,
-                         self.v_cache, self.idx)
+                         self.v_cache, self.idx, self.host_format, self.k_exp, self.v_exp)
 
     def shape_with(self, tau: float) -> clo.Shape:
         """The layer's shape with threshold tau (+inf: every unit misses, whatever
@@ -100,10 +107,13 @@ class LayerBuffers:
         return bool((self.mask >> kvh) & 1)
 
     def host_view(self, which: str, b: int, kvh: int) -> np.ndarray:
-        """numpy view [N, d] of a non-persistent unit's pinned K or V."""
+        """numpy view [N, d] of a non-persistent unit's pinned K or V (int8 for the int8 host format)."""
         buf = self.k_host if which == "k" else self.v_host
-        npdt = np.float32 if self.dtype == "f32" else np.uint16
-        unit = self.N * HEAD_DIM * elem_bytes(self.dtype)
+        if self.host_format == clo.CLO_HOST_INT8:
+            npdt, eb = np.int8, 1
+        else:
+            npdt, eb = (np.float32 if self.dtype == "f32" else np.uint16), elem_bytes(self.dtype)
+        unit = self.N * HEAD_DIM * eb
         off = (b * self.H + self.slot(kvh)) * unit
         return buf.numpy(npdt, (self.N, HEAD_DIM), offset=off)
 
@@ -129,16 +139,18 @@ def stored_tensor(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
 
 
 def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads: Optional[int] = None,
-               log=None, share: Optional[LayerBuffers] = None, host_flags: int = hipHostMallocMapped) -> LayerBuffers:
+               log=None, share: Optional[LayerBuffers] = None, host_flags: int = hipHostMallocMapped,
+               host_format: int = clo.CLO_HOST_NATIVE) -> LayerBuffers:
     """Allocate (unless given) and fill the buffers of one layer of `problem`.
 
     With `share`, the layer reuses that layer's K/V buffers (aliased data) and
-    only its queries are loaded."""
+    only its queries are loaded.  With the int8 host format the offloaded rows
+    are quantized by clo_quantize_rows on the GPU straight into pinned memory."""
     p = problem
     mask = p.persistent_mask_bits(layer)
     if bufs is None:
         bufs = LayerBuffers(p.batch, p.hq, p.hkv, p.context, p.topk, p.dtype, mask, p.tau, share=share,
-                            host_flags=host_flags)
+                            host_flags=host_flags, host_format=host_format)
     assert bufs.mask == mask
     bufs.q.copy_(stored_tensor(p.q(layer), p.dtype))
     bufs.q_prev.copy_(stored_tensor(p.q_prev(layer), p.dtype))
@@ -147,8 +159,24 @@ def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads
     eb = elem_bytes(p.dtype)
     unit_bytes = p.context * HEAD_DIM * eb
     staging = None
+    q8 = bufs.host_format == clo.CLO_HOST_INT8
+    dev_stage = torch.empty(p.context, HEAD_DIM, dtype=torch_dtype(p.dtype), device=bufs.q.device) if q8 else None
     for b in range(p.batch):
         for kvh in range(p.hkv):
+            if q8 and not bufs.is_persistent(kvh):
+                if staging is None:
+                    staging = HostBuffer(unit_bytes)
+                s = bufs.slot(kvh)
+                off = (b * bufs.H + s) * p.context * HEAD_DIM  # int8 bytes
+                for which, exp in (("k", bufs.k_exp), ("v", bufs.v_exp)):
+                    p.fill(which, layer, b, kvh, staging.ptr, threads)
+                    copy_h2d(dev_stage.data_ptr(), staging.ptr, unit_bytes)
+                    if which == "k":
+                        bufs.k_score[b, s].copy_(dev_stage)
+                    buf = bufs.k_host if which == "k" else bufs.v_host
+                    clo.clo_quantize_rows(dev_stage, p.context, clo_dtype(p.dtype), buf.ptr + off, exp[b, s])
+                torch.cuda.synchronize()
+                continue
             if bufs.is_persistent(kvh):
                 if staging is None:
                     staging = HostBuffer(unit_bytes)
@@ -162,7 +190,7 @@ def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads
                 p.fill("v", layer, b, kvh, bufs.v_host.ptr + off, threads)
         if log:
             log(f"  generated sequence {b + 1}/{p.batch}")
-    if bufs.H:
+    if bufs.H and not q8:
         copy_h2d(bufs.k_score.data_ptr(), bufs.k_host.ptr, bufs.B * bufs.H * unit_bytes)
     if staging is not None:
         staging.close()
@@ -170,13 +198,15 @@ def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads
     return bufs
 
 
-def load_layers(problem, log=None, threads: Optional[int] = None, host_flags: int = hipHostMallocMapped):
+def load_layers(problem, log=None, threads: Optional[int] = None, host_flags: int = hipHostMallocMapped,
+                host_format: int = clo.CLO_HOST_NATIVE):
     """Buffers of every layer; layers with the same data layer share their K/V."""
     first = {}
     layers = []
     for l in range(problem.layers):
         dl = problem.data_layer(l)
-        bufs = load_layer(problem, l, threads=threads, share=first.get(dl), host_flags=host_flags)
+        bufs = load_layer(problem, l, threads=threads, share=first.get(dl), host_flags=host_flags,
+                          host_format=host_format)
         first.setdefault(dl, bufs)
         layers.append(bufs)
         if log:
@@ -272,7 +302,7 @@ class GrowingRun:
     """
 
     def __init__(self, problem, layer: int, steps: int, policy: str = "previous",
-                 host_flags: int = hipHostMallocMapped):
+                 host_flags: int = hipHostMallocMapped, host_format: int = clo.CLO_HOST_NATIVE):
         if policy not in ("previous", "refresh"):
             raise ValueError(policy)
         p = problem
@@ -280,7 +310,7 @@ class GrowingRun:
         self.C = p.context
         self.n0 = p.context - steps
         assert self.n0 >= p.topk
-        b = self.bufs = load_layer(p, layer, host_flags=host_flags)
+        b = self.bufs = load_layer(p, layer, host_flags=host_flags, host_format=host_format)
         dev = b.q.device
         tdt = torch_dtype(p.dtype)
         n0 = self.n0
@@ -296,7 +326,7 @@ class GrowingRun:
             else:
                 self.k_new[:, :, h] = b.k_score[:, s, n0:].transpose(0, 1)
                 for bb in range(b.B):
-                    self.v_new[:, bb, h] = host_rows_tensor(b.host_view("v", bb, h)[n0:], p.dtype, dev)
+                    self.v_new[:, bb, h] = host_rows_tensor(p.kv("v", layer, bb, h)[n0:], p.dtype, dev)
         self.qs = torch.stack([stored_tensor(p.q_walk(layer, t), p.dtype, dev) for t in range(steps + 1)])
         self.q_ref = torch.zeros_like(b.q)
         self.reset()
