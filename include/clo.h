@@ -47,8 +47,9 @@
  * persistent (or non-persistent) heads in head order:
  *   q, q_prev, out   [B, Hq, d]
  *   k_hbm, v_hbm     [B, P, C, d]   device   full K/V of persistent heads (rows < N used)
- *   k_host, v_host   [B, H, C, d]   pinned   full K/V of non-persistent heads (int8 when
- *                                            layer->host_format is CLO_HOST_INT8)
+ *   k_host, v_host   [B, H, C, d]   pinned   full K/V of non-persistent heads; with
+ *                                            CLO_HOST_INT8: k_host [B, H, C, 2, d] int8
+ *                                            (K row, V row per token), v_host unused
  *   k_score          [B, H, C, d]   device   copy of k_host read by scoring
  *   k_cache, v_cache [B, H, k, d]   device   rows k_host[idx], v_host[idx]
  *   idx              [B, Hkv, k]    int32    selected token indices, ascending
@@ -71,7 +72,10 @@ typedef enum { CLO_F32 = 0, CLO_BF16 = 1 } clo_dtype;
  *   CLO_HOST_NATIVE  rows in the shape's dtype (the pages' format)
  *   CLO_HOST_INT8    quantized rows: 128 int8 values q_i per row and one scale
  *                    exponent e per row (int8, kept in device memory); the row's
- *                    values are q_i * 2^e.  A row x is quantized as: m = max|x_i|;
+ *                    values are q_i * 2^e.  A token's K and V rows are stored
+ *                    together as one 256-byte record (K values, then V values)
+ *                    in k_host, so that the GPU reads a selected token with one
+ *                    256-byte request; v_host is not used.  A row x is quantized as: m = max|x_i|;
  *                    e = the smallest integer with m <= 127 * 2^e (e = 0 when m = 0),
  *                    raised to -120 if smaller; q_i = x_i * 2^-e rounded to the
  *                    nearest integer, ties to even.  q_i * 2^e is exact in bf16 and
@@ -266,12 +270,14 @@ clo_status clo_plan_persistent(const float* s_hat, int32_t n_layers, int32_t n_k
  * Quantize rows for an int8 host copy (CLO_HOST_INT8; quantized offloaded KV,
  * synthesis sections 3.3 and 5.6 on cutting the bytes that cross the host link).
  * Reads n_rows rows of 128 elements of `dtype` from src (device), writes their
- * int8 values to dst (device or pinned host memory, [n_rows, 128]) and their
- * scale exponents to dst_exp (device, [n_rows]), by the rule documented at
- * clo_host_format.  Finite inputs only.  sync may be NULL.
+ * int8 values to dst (device or pinned host memory; row r at dst + r *
+ * dst_stride bytes, dst_stride >= 128 and a multiple of 16: 256 fills the K or V
+ * half of CLO_HOST_INT8 records) and their scale exponents to dst_exp (device,
+ * [n_rows]), by the rule documented at clo_host_format.  Finite inputs only.
+ * sync may be NULL.
  */
-clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int8_t* dst_exp,
-                             const clo_sync* sync, void* stream);
+clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int64_t dst_stride,
+                             int8_t* dst_exp, const clo_sync* sync, void* stream);
 
 /* Static text for a status code. */
 const char* clo_status_string(clo_status status);

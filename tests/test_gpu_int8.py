@@ -29,7 +29,7 @@ def _rows(rng, n, dtype):
     return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)  # bf16 patterns, RNE
 
 
-@pytest.mark.parametrize("where", ["host", "device"])
+@pytest.mark.parametrize("where", ["host", "device", "host_records"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_quantize_rows_match_oracle(need_gpu, dtype, where):
     import torch
@@ -47,6 +47,15 @@ def test_quantize_rows_match_oracle(need_gpu, dtype, where):
         clo.clo_quantize_rows(src, n, workload.clo_dtype(dtype), host.ptr, exp)
         torch.cuda.synchronize()
         q = host.numpy(np.int8, (n, 128)).copy()
+    elif where == "host_records":
+        # the V half of 256-byte records: rows 256 bytes apart, K halves untouched
+        host = HostBuffer(n * 256)
+        host.numpy(np.int8, (n * 256,))[:] = 99
+        clo.clo_quantize_rows(src, n, workload.clo_dtype(dtype), host.ptr + 128, exp, dst_stride=256)
+        torch.cuda.synchronize()
+        rec = host.numpy(np.int8, (n, 2, 128))
+        assert np.all(rec[:, 0] == 99)
+        q = rec[:, 1].copy()
     else:
         dst = torch.zeros(n, 128, dtype=torch.int8, device="cuda")
         clo.clo_quantize_rows(src, n, workload.clo_dtype(dtype), dst, exp)

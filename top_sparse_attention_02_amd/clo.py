@@ -78,7 +78,7 @@ def load():
         L.clo_update_reference.restype = st
         L.clo_update_reference.argtypes = [P(clo_shape), vp, vp, vp, P(clo_sync), vp]
         L.clo_quantize_rows.restype = st
-        L.clo_quantize_rows.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, P(clo_sync), vp]
+        L.clo_quantize_rows.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int64, vp, P(clo_sync), vp]
         L.clo_plan_persistent.restype = st
         L.clo_plan_persistent.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
         L.clo_status_string.restype = ctypes.c_char_p
@@ -248,9 +248,10 @@ def clo_update_reference(shape: Shape, q, reuse, q_ref, sync: Optional[Sync] = N
                                        stream_handle(stream)), "clo_update_reference")
 
 
-def clo_quantize_rows(src, n_rows: int, dtype: int, dst, dst_exp, sync: Optional[Sync] = None, stream=None):
-    _check(load().clo_quantize_rows(ptr(src), int(n_rows), int(dtype), ptr(dst), ptr(dst_exp), _sync(sync),
-                                    stream_handle(stream)), "clo_quantize_rows")
+def clo_quantize_rows(src, n_rows: int, dtype: int, dst, dst_exp, dst_stride: int = 128, sync: Optional[Sync] = None,
+                      stream=None):
+    _check(load().clo_quantize_rows(ptr(src), int(n_rows), int(dtype), ptr(dst), int(dst_stride), ptr(dst_exp),
+                                    _sync(sync), stream_handle(stream)), "clo_quantize_rows")
 
 
 def clo_plan_persistent(s_hat, n_persist: int):

@@ -300,9 +300,13 @@ clo_status check_layer(const clo_layer* l, Plan* p, unsigned need) {
         return fail(CLO_E_ARG, "layer.host_format %d is not a clo_host_format", l->host_format);
       a.host_fmt = l->host_format;
       const size_t rows = (size_t)a.B * a.H * (size_t)a.C;
-      const size_t hb = a.host_fmt == CLO_HOST_INT8 ? rows * kHeadDim : full_bytes(*p, a.H);
-      if ((st = check_host(l->k_host, hb, "layer.k_host", &dk))) return st;
-      if ((st = check_host(l->v_host, hb, "layer.v_host", &dv))) return st;
+      if (a.host_fmt == CLO_HOST_INT8) {
+        // one 256-byte record (K values, then V values) per token; v_host unused
+        if ((st = check_host(l->k_host, rows * 2 * kHeadDim, "layer.k_host", &dk))) return st;
+      } else {
+        if ((st = check_host(l->k_host, full_bytes(*p, a.H), "layer.k_host", &dk))) return st;
+        if ((st = check_host(l->v_host, full_bytes(*p, a.H), "layer.v_host", &dv))) return st;
+      }
       a.k_host = dk;
       a.v_host = dv;
       if (a.host_fmt == CLO_HOST_INT8) {
@@ -621,11 +625,13 @@ clo_status clo_plan_persistent(const float* s_hat, int32_t n_layers, int32_t n_k
   return ok();
 }
 
-clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int8_t* dst_exp,
-                             const clo_sync* sync, void* stream) {
+clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int64_t dst_stride,
+                             int8_t* dst_exp, const clo_sync* sync, void* stream) {
   clo_status st;
   if (dtype != CLO_F32 && dtype != CLO_BF16) return fail(CLO_E_UNSUPPORTED, "dtype %d is not fp32 or bf16", dtype);
   if (n_rows < 0) return fail(CLO_E_ARG, "n_rows %lld < 0", (long long)n_rows);
+  if (dst_stride < kHeadDim || dst_stride % 16)
+    return fail(CLO_E_ARG, "dst_stride %lld is not a multiple of 16 of at least 128", (long long)dst_stride);
   if ((st = check_sync_flags(sync))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (n_rows == 0) {
@@ -635,10 +641,11 @@ clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int
   const size_t e = dtype == CLO_F32 ? 4 : 2;
   if ((st = check_device(src, (size_t)n_rows * kHeadDim * e, "src"))) return st;
   const void* d = nullptr;
-  if ((st = check_host(dst, (size_t)n_rows * kHeadDim, "dst", &d))) return st;  // device memory passes too
+  if ((st = check_host(dst, (size_t)(n_rows - 1) * dst_stride + kHeadDim, "dst", &d))) return st;  // or device
   if ((st = check_device(dst_exp, (size_t)n_rows, "dst_exp", 1))) return st;
   if ((st = pre_wait(sync, s))) return st;
-  if ((st = hip_status(launch_quantize_rows(src, n_rows, dtype, static_cast<int8_t*>(const_cast<void*>(d)), dst_exp, s),
+  if ((st = hip_status(launch_quantize_rows(src, n_rows, dtype, static_cast<int8_t*>(const_cast<void*>(d)), dst_stride,
+                                            dst_exp, s),
                        "quantize launch")))
     return st;
   return post_signal(sync, s);

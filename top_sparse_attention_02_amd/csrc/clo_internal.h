@@ -141,8 +141,8 @@ hipError_t launch_append(const LayerArgs& a, const void* k_new, const void* v_ne
                          void* k_hbm, void* v_hbm, void* k_host, void* v_host, void* k_score, hipStream_t s);
 hipError_t launch_update_reference(const LayerArgs& a, const void* q, const uint8_t* reuse, void* q_ref,
                                    hipStream_t s);
-hipError_t launch_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int8_t* dst_exp,
-                                hipStream_t s);
+hipError_t launch_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int64_t stride,
+                                int8_t* dst_exp, hipStream_t s);
 hipError_t launch_wait(const uint32_t* flag, uint32_t value, uint32_t spin_limit, uint32_t* error_word,
                        hipStream_t s);
 hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s);

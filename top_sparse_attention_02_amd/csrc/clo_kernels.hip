@@ -1020,17 +1020,21 @@ __device__ __forceinline__ void store_deq16<float>(float* dst, u32x4 w, float sc
 template <typename T>
 __global__ __launch_bounds__(256) void gather_q8_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp,
                                                         uint32_t* __restrict__ counter) {
-  constexpr int LPR = kHeadDim / 16;  // lanes per int8 row
+  // one 256-byte record per token: lanes 0-7 of a row group read its K values,
+  // lanes 8-15 its V values, in a single 16-lane load
+  constexpr int kRec = 2 * kHeadDim;  // record bytes
+  constexpr int LPR = kRec / 16;      // 16 lanes per token
   constexpr int RPI = 256 / LPR;
-  constexpr int UNR = kGatherUnroll;
+  constexpr int UNR = 2 * kGatherUnroll;  // same bytes in flight as the native kernel
   __shared__ uint32_t s_item;
   __shared__ int32_t s_src[kGatherChunk];
-  __shared__ float s_sk[kGatherChunk], s_sv[kGatherChunk];  // 2^e of the item's K and V rows
+  __shared__ float s_sc[2][kGatherChunk];  // 2^e of the item's K and V rows
   const int nch = (int)((a.k + kGatherChunk - 1) / kGatherChunk);
   const int lo = sp.list ? *sp.lo : 0;
   const int64_t n_units = sp.list ? (int64_t)(*sp.hi - lo) : (int64_t)a.B * a.Hkv;
   const int64_t items = n_units * nch;
   const int sub = threadIdx.x % LPR, rl = threadIdx.x / LPR;
+  const int half = sub >> 3, piece = sub & 7;  // 0 = K, 1 = V; 16-value piece of the row
   for (;;) {
     if (threadIdx.x == 0) s_item = atomicAdd(counter, 1u);
     __syncthreads();
@@ -1042,10 +1046,8 @@ __global__ __launch_bounds__(256) void gather_q8_kernel(LayerArgs a, const uint8
     const int b = u / a.Hkv, h = u % a.Hkv;
     if (!sp.list && (((a.pmask >> h) & 1ull) || (reuse && reuse[u]))) continue;
     const int64_t slot = (int64_t)b * a.H + head_slot(a.pmask, h);
-    const char* ks = static_cast<const char*>(a.k_host) + slot * a.C * kHeadDim;
-    const char* vs = static_cast<const char*>(a.v_host) + slot * a.C * kHeadDim;
-    T* kd = static_cast<T*>(a.k_cache) + slot * a.k * kHeadDim;
-    T* vd = static_cast<T*>(a.v_cache) + slot * a.k * kHeadDim;
+    const char* rec = static_cast<const char*>(a.k_host) + slot * a.C * kRec;
+    T* dst = static_cast<T*>(half ? a.v_cache : a.k_cache) + slot * a.k * kHeadDim;
     const int32_t* ix = a.idx + (int64_t)u * a.k;
     const int64_t r0 = (int64_t)c * kGatherChunk;
     const int64_t r_end = (r0 + kGatherChunk < a.k) ? r0 + kGatherChunk : a.k;
@@ -1053,27 +1055,22 @@ __global__ __launch_bounds__(256) void gather_q8_kernel(LayerArgs a, const uint8
       int32_t src = ix[r0 + threadIdx.x];
       src = src < 0 ? 0 : (src >= a.N ? (int32_t)(a.N - 1) : src);
       s_src[threadIdx.x] = src;
-      s_sk[threadIdx.x] = pow2f(a.k_exp[slot * a.C + src]);
-      s_sv[threadIdx.x] = pow2f(a.v_exp[slot * a.C + src]);
+      s_sc[0][threadIdx.x] = pow2f(a.k_exp[slot * a.C + src]);
+      s_sc[1][threadIdx.x] = pow2f(a.v_exp[slot * a.C + src]);
     }
     __syncthreads();
     for (int64_t rb = r0; rb < r_end; rb += RPI * UNR) {
-      u32x4 kx[UNR], vx[UNR];
+      u32x4 x[UNR];
 #pragma unroll
       for (int j = 0; j < UNR; ++j) {
         int64_t row = rb + j * RPI + rl;
         row = row < r_end ? row : r_end - 1;
-        const int64_t src = s_src[row - r0];
-        kx[j] = *reinterpret_cast<const u32x4*>(ks + src * kHeadDim + sub * 16);
-        vx[j] = *reinterpret_cast<const u32x4*>(vs + src * kHeadDim + sub * 16);
+        x[j] = *reinterpret_cast<const u32x4*>(rec + (int64_t)s_src[row - r0] * kRec + sub * 16);
       }
 #pragma unroll
       for (int j = 0; j < UNR; ++j) {
         const int64_t row = rb + j * RPI + rl;
-        if (row < r_end) {
-          store_deq16<T>(kd + row * kHeadDim + sub * 16, kx[j], s_sk[row - r0]);
-          store_deq16<T>(vd + row * kHeadDim + sub * 16, vx[j], s_sv[row - r0]);
-        }
+        if (row < r_end) store_deq16<T>(dst + row * kHeadDim + piece * 16, x[j], s_sc[half][row - r0]);
       }
     }
   }
@@ -1127,10 +1124,10 @@ __device__ __forceinline__ void quantize_row_wave(const T* row, int8_t* dst, int
 
 template <typename T>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict__ src, int64_t n_rows, int8_t* dst,
-                                                            int8_t* __restrict__ dst_exp) {
+                                                            int64_t stride, int8_t* __restrict__ dst_exp) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n_rows) return;  // whole wave
-  quantize_row_wave<T>(src + row * kHeadDim, dst + row * kHeadDim, dst_exp + row);
+  quantize_row_wave<T>(src + row * kHeadDim, dst + row * stride, dst_exp + row);
 }
 
 __global__ void zero_kernel(uint32_t* word) {
@@ -1406,9 +1403,10 @@ __global__ __launch_bounds__(64) void append_kernel(LayerArgs a, const T* __rest
   const int64_t src = (int64_t)u * kHeadDim;
   if (!pers && a.host_fmt == CLO_HOST_INT8) {
     // the int8 host copy gets the quantized row, the score copy the exact one
-    const int64_t er = dst / kHeadDim;
-    quantize_row_wave<T>(k_new + src, reinterpret_cast<int8_t*>(k_host) + dst, const_cast<int8_t*>(a.k_exp) + er);
-    quantize_row_wave<T>(v_new + src, reinterpret_cast<int8_t*>(v_host) + dst, const_cast<int8_t*>(a.v_exp) + er);
+    const int64_t er = dst / kHeadDim;                          // the token's row index
+    int8_t* record = reinterpret_cast<int8_t*>(k_host) + er * 2 * kHeadDim;  // K values, then V values
+    quantize_row_wave<T>(k_new + src, record, const_cast<int8_t*>(a.k_exp) + er);
+    quantize_row_wave<T>(v_new + src, record + kHeadDim, const_cast<int8_t*>(a.v_exp) + er);
     for (int i = threadIdx.x; i < kPieces; i += 64)
       reinterpret_cast<u32x4*>(k_score + dst)[i] = reinterpret_cast<const u32x4*>(k_new + src)[i];
     return;
@@ -1551,15 +1549,16 @@ hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, Span sp, int6
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int8_t* dst_exp,
-                                hipStream_t s) {
+hipError_t launch_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int64_t stride,
+                                int8_t* dst_exp, hipStream_t s) {
   const int64_t blocks = (n_rows + 3) / 4;
   if (blocks <= 0) return hipSuccess;
   const unsigned grid = (unsigned)blocks;
   if (dtype == CLO_F32)
-    quantize_rows_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(src), n_rows, dst, dst_exp);
+    quantize_rows_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(src), n_rows, dst, stride, dst_exp);
   else
-    quantize_rows_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), n_rows, dst, dst_exp);
+    quantize_rows_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), n_rows, dst, stride,
+                                                        dst_exp);
   return hipGetLastError();
 }
 

@@ -67,10 +67,13 @@ class LayerBuffers:
                 self.v_hbm = torch.empty_like(self.k_hbm)
             self.k_host = self.v_host = self.k_score = None
             if self.H:
-                hb = 1 if host_format == clo.CLO_HOST_INT8 else elem_bytes(dtype)
-                nb = batch * self.H * context * d * hb
-                self.k_host = HostBuffer(nb, host_flags)
-                self.v_host = HostBuffer(nb, host_flags)
+                if host_format == clo.CLO_HOST_INT8:
+                    # one 256-byte record per token: int8 K values, then int8 V values
+                    self.k_host = HostBuffer(batch * self.H * context * 2 * d, host_flags)
+                else:
+                    nb = batch * self.H * context * d * elem_bytes(dtype)
+                    self.k_host = HostBuffer(nb, host_flags)
+                    self.v_host = HostBuffer(nb, host_flags)
                 self.k_score = torch.empty(batch, self.H, context, d, dtype=tdt, device=dev)
                 if host_format == clo.CLO_HOST_INT8:
                     self.k_exp = torch.zeros(batch, self.H, context, dtype=torch.int8, device=dev)
@@ -108,11 +111,13 @@ class LayerBuffers:
 
     def host_view(self, which: str, b: int, kvh: int) -> np.ndarray:
         """numpy view [N, d] of a non-persistent unit's pinned K or V (int8 for the int8 host format)."""
-        buf = self.k_host if which == "k" else self.v_host
         if self.host_format == clo.CLO_HOST_INT8:
-            npdt, eb = np.int8, 1
-        else:
-            npdt, eb = (np.float32 if self.dtype == "f32" else np.uint16), elem_bytes(self.dtype)
+            unit = self.N * 2 * HEAD_DIM
+            off = (b * self.H + self.slot(kvh)) * unit
+            rec = self.k_host.numpy(np.int8, (self.N, 2, HEAD_DIM), offset=off)
+            return rec[:, 0 if which == "k" else 1, :]
+        buf = self.k_host if which == "k" else self.v_host
+        npdt, eb = (np.float32 if self.dtype == "f32" else np.uint16), elem_bytes(self.dtype)
         unit = self.N * HEAD_DIM * eb
         off = (b * self.H + self.slot(kvh)) * unit
         return buf.numpy(npdt, (self.N, HEAD_DIM), offset=off)
@@ -167,14 +172,14 @@ def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads
                 if staging is None:
                     staging = HostBuffer(unit_bytes)
                 s = bufs.slot(kvh)
-                off = (b * bufs.H + s) * p.context * HEAD_DIM  # int8 bytes
-                for which, exp in (("k", bufs.k_exp), ("v", bufs.v_exp)):
+                rec = bufs.k_host.ptr + (b * bufs.H + s) * p.context * 2 * HEAD_DIM  # the unit's records
+                for which, exp, half in (("k", bufs.k_exp, 0), ("v", bufs.v_exp, HEAD_DIM)):
                     p.fill(which, layer, b, kvh, staging.ptr, threads)
                     copy_h2d(dev_stage.data_ptr(), staging.ptr, unit_bytes)
                     if which == "k":
                         bufs.k_score[b, s].copy_(dev_stage)
-                    buf = bufs.k_host if which == "k" else bufs.v_host
-                    clo.clo_quantize_rows(dev_stage, p.context, clo_dtype(p.dtype), buf.ptr + off, exp[b, s])
+                    clo.clo_quantize_rows(dev_stage, p.context, clo_dtype(p.dtype), rec + half, exp[b, s],
+                                          dst_stride=2 * HEAD_DIM)
                 torch.cuda.synchronize()
                 continue
             if bufs.is_persistent(kvh):
