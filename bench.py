@@ -61,6 +61,9 @@ def parse():
                     help="format of the offloaded K/V in host memory: the step's dtype, or int8 rows with one "
                          "power-of-two scale per row (half the host-link bytes of bf16; dequantized exactly "
                          "by the gather)")
+    ap.add_argument("--block-size", type=int, default=0, metavar="B",
+                    help="select blocks of B consecutive tokens instead of tokens (top-k a multiple of B: "
+                         "k is rounded down to one)")
     ap.add_argument("--no-compare-native", action="store_true",
                     help="int8 host KV, configs 1-3: skip the output comparison against the native format")
     ap.add_argument("--growing", type=int, default=0, metavar="T",
@@ -414,6 +417,27 @@ def profile_and_plan(torch, clo, gen, cfg: int, overrides: dict, instances: int)
             "volatile_persistent_seeded": int((base.persistent[:period] & vol).sum())}
 
 
+def compare_tokens(torch, bufs, step_kind: int) -> dict:
+    """Block selection against token selection on the same layer: the same step
+    with block_size 1, normwise output deviation per (sequence, query head) and
+    the fraction of the block-selected tokens that token selection also takes."""
+    out_b = bufs.out.float().clone()
+    idx_b = bufs.idx.clone()
+    bs = bufs.shape.block_size
+    bufs.set_block_size(0)
+    bufs.step0()
+    if step_kind == 1:
+        bufs.step1()
+    torch.cuda.synchronize()
+    n = bufs.out.float()
+    dev = (out_b - n).abs().amax(-1) / n.abs().amax(-1).clamp_min(1e-30)
+    ib, it = idx_b.cpu().numpy(), bufs.idx.cpu().numpy()
+    overlap = float(sum(len(set(ib[b, h]) & set(it[b, h])) for b in range(ib.shape[0]) for h in range(ib.shape[1]))
+                    / ib.size)
+    bufs.set_block_size(bs)
+    return {"out_dev_mean": float(dev.mean()), "out_dev_max": float(dev.max()), "selection_overlap": overlap}
+
+
 def compare_native(torch, workload, p, q8_layer, step_kind: int, flags) -> dict:
     """Output of the int8-host-KV step against the same step with native host
     rows (the same inputs loaded a second time): normwise relative deviation per
@@ -466,6 +490,8 @@ def main():
         overrides["data_layers"] = args.data_layers or (8 if args.config == 4 else 16)
     if args.volatile:
         overrides["volatile_frac"] = args.volatile
+    if args.block_size > 1:
+        overrides["topk"] = gen.config(args.config).topk // args.block_size * args.block_size
     plan = None
     if args.plan_persistent:
         plan = profile_and_plan(torch, clo, gen, args.config, overrides, args.profile_instances)
@@ -503,6 +529,9 @@ def main():
         del src, dst
         log("calibration copy done: 1 GiB read + 1 GiB written")
 
+    if args.block_size > 1:
+        for bufs in layers:
+            bufs.set_block_size(args.block_size)
     if multi:
         loop = workload.LayerLoop(layers)
         loop.step(cold=True)
@@ -530,6 +559,11 @@ def main():
     ms_per_step = e0.elapsed_time(e1) / args.steps
     alg = algorithmic_bytes(layers)
 
+    blocks = None
+    if args.block_size > 1 and not multi:
+        blocks = compare_tokens(torch, layers[0], args.step)
+        log(f"blocks of {args.block_size} vs tokens: output deviation mean {blocks['out_dev_mean']:.3f}, "
+            f"selection overlap {blocks['selection_overlap']:.3f}")
     quant = None
     if host_format == clo.CLO_HOST_INT8 and not multi and not args.no_compare_native:
         quant = compare_native(torch, workload, p, layers[0], args.step, flags)
@@ -579,12 +613,15 @@ def main():
                    (", steady step (80/20 reuse)" if args.step == 1 else ", cold step (all miss)") +
                    (f", {args.volatile:.0%} volatile (layer, KV head) slots" if args.volatile else "") +
                    (", persistent heads from profiling" if plan else "") +
-                   (", int8 host KV (power-of-two row scales)" if args.host_kv == "int8" else ""),
+                   (", int8 host KV (power-of-two row scales)" if args.host_kv == "int8" else "") +
+                   (f", selection in blocks of {args.block_size} tokens, k={p.topk}" if args.block_size > 1 else ""),
                    "layers": p.layers, "batch": p.batch, "q_heads": p.hq, "kv_heads": p.hkv, "head_dim": HEAD_DIM,
                    "context": p.context, "topk": p.topk, "tau": p.tau, "step": args.step,
                    "data_layers": p.data_layers or p.layers, "host_memory": args.host_memory},
         "roofline": roofline,
         "persistent_plan": None if plan is None else {k: v for k, v in plan.items() if k != "persistent"},
+        "block_size": args.block_size or 1,
+        "blocks_vs_tokens": blocks,
         "host_kv": args.host_kv,
         "host_kv_vs_native": quant,
         "volatile_frac": args.volatile,

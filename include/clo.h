@@ -109,6 +109,13 @@ typedef struct {
                               threshold per head): host array [n_kv_heads], read during the call;
                               unit (b, h) reuses when cos >= tau_heads[h].  NULL = tau for every
                               head. */
+  int32_t block_size;  /* selection granularity (synthesis section 3.3: per-head selection fragments
+                          host transfers; selecting token blocks keeps them contiguous).  0 or 1 =
+                          tokens.  B > 1: the context is cut into floor(N / B) full blocks of B
+                          consecutive tokens (a partial tail block is not selectable), a block
+                          scores the max of its tokens' scores, the k / B best blocks are taken
+                          (ties to the lower block) and idx lists their tokens ascending.  Needs
+                          topk a multiple of B and at most floor(N / B) * B. */
 } clo_shape;
 
 /* Where one layer's keys, values, selections and cached rows live. */
@@ -169,7 +176,8 @@ clo_status clo_reuse_test(const clo_shape* shape, const void* q, const void* q_p
  * For every miss unit (reuse[u] == 0; all units when reuse is NULL): scores
  * s_j = max_h q_h . K_j accumulated in fp32 over the unit's keys (k_hbm for
  * persistent heads, k_score otherwise), then idx[u] = the k tokens with the
- * largest s_j (ties to the smaller index), ascending.  idx of hit units is
+ * largest s_j (ties to the smaller index), ascending (with shape->block_size
+ * > 1: the tokens of the k / block_size best blocks).  idx of hit units is
  * left untouched.  ws: device workspace of at least clo_workspace_size() bytes.
  * sync may be NULL.
  */

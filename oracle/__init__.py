@@ -11,6 +11,7 @@ from .clo_oracle import (  # noqa: F401
     quantize_row,
     quantized_rows,
     reuse_decision,
+    select_blocks,
     select_topk,
     token_scores,
 )

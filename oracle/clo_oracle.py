@@ -35,6 +35,10 @@ Synthesis"; CLO abstract page on fugumt):
     tau per KV head, plan_persistent): synthesis section 3.1 attack point 6
     and section 5.3 -- offline profiling fixes each head's mean similarity,
     its threshold and the number of persistent heads.
+  * Block-granular selection (select_blocks): synthesis section 3.3 -- per-head
+    token selection fragments host transfers; selecting blocks of consecutive
+    tokens keeps them contiguous.  The block score (max of its tokens' scores)
+    and the full-blocks-only rule are this implementation's reading.
   * Quantized host KV (quantize_row, dequantize_row): synthesis sections 3.3
     and 5.6 -- fewer bytes across the host link; the format (int8 values, one
     power-of-two scale per row) is this implementation's choice, written out
@@ -131,11 +135,13 @@ def attend(q_group: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, return_p: bool =
 
 
 def decode_unit(q_group, q_prev_group, K, V, k: int, tau: float,
-                idx_prev: Optional[np.ndarray] = None, K_attn=None, V_attn=None) -> Dict[str, object]:
+                idx_prev: Optional[np.ndarray] = None, K_attn=None, V_attn=None,
+                block_size: int = 1) -> Dict[str, object]:
     """O1-O6 for one unit.  q_group/q_prev_group [g, d]; K, V [N, d] (float64).
 
     K_attn / V_attn: the rows attention reads, when they differ from the keys
-    that are scored (a quantized host copy); default K and V."""
+    that are scored (a quantized host copy); default K and V.  block_size > 1
+    selects token blocks (select_blocks) instead of tokens."""
     c = group_cosine(q_group, q_prev_group)
     reuse = reuse_decision(c, tau)
     if reuse:
@@ -143,7 +149,8 @@ def decode_unit(q_group, q_prev_group, K, V, k: int, tau: float,
             raise ValueError("a reused unit needs the previous selection")
         sel = np.asarray(idx_prev, dtype=np.int64)
     else:
-        sel = select_topk(token_scores(q_group, K), k)
+        s = token_scores(q_group, K)
+        sel = select_topk(s, k) if block_size <= 1 else select_blocks(s, k, block_size)
     Kc = np.asarray(K if K_attn is None else K_attn, dtype=np.float64)[sel]
     Vc = np.asarray(V if V_attn is None else V_attn, dtype=np.float64)[sel]
     out = attend(q_group, Kc, Vc)
@@ -154,7 +161,7 @@ def decode_layer(q, q_prev, kv_of: Callable[[int, int], Tuple[np.ndarray, np.nda
                  hkv: int, k: int, tau, dtype: str,
                  idx_prev: Optional[np.ndarray] = None,
                  units: Optional[Iterable[Tuple[int, int]]] = None,
-                 attn_kv_of=None) -> Dict[Tuple[int, int], Dict[str, object]]:
+                 attn_kv_of=None, block_size: int = 1) -> Dict[Tuple[int, int], Dict[str, object]]:
     """Run decode_unit over (b, kvh) units of one layer.
 
     q, q_prev: stored [B, Hq, d] arrays of `dtype`; kv_of(b, kvh) returns the
@@ -178,7 +185,7 @@ def decode_layer(q, q_prev, kv_of: Callable[[int, int], Tuple[np.ndarray, np.nda
         ka = attn_kv_of(b, kvh) if attn_kv_of else None
         res[(b, kvh)] = decode_unit(qf[b, kvh * g:(kvh + 1) * g], qpf[b, kvh * g:(kvh + 1) * g],
                                     as_f64(K, dtype), as_f64(V, dtype), k, tau_u, prev,
-                                    *(ka if ka is not None else (None, None)))
+                                    *(ka if ka is not None else (None, None)), block_size=block_size)
     return res
 
 
@@ -261,3 +268,20 @@ def quantized_rows(X) -> np.ndarray:
     for i in range(X.shape[0]):
         out[i] = dequantize_row(*quantize_row(X[i]))
     return out
+
+
+def select_blocks(s: np.ndarray, k: int, block_size: int) -> np.ndarray:
+    """Top-k over blocks of `block_size` consecutive tokens.
+
+    The floor(N / block_size) full blocks score the max of their tokens' scores
+    (a partial tail block is not selectable); the k / block_size best blocks
+    (ties by smaller block index) are taken and their tokens returned
+    ascending.  k must be a multiple of block_size.
+    """
+    s = np.asarray(s, dtype=np.float64)
+    if k % block_size:
+        raise ValueError("k must be a multiple of the block size")
+    nb = s.shape[0] // block_size
+    bscore = s[:nb * block_size].reshape(nb, block_size).max(axis=1)
+    blocks = np.sort(select_topk(bscore, k // block_size))
+    return (blocks[:, None] * block_size + np.arange(block_size)[None, :]).reshape(-1)

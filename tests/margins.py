@@ -223,3 +223,41 @@ def enforce_walk_margins(problem, layer: int, steps: int, tau=None, max_rounds: 
         else:
             raise RuntimeError(f"score margins not reached for unit {(b, h)}")
     return p
+
+
+def enforce_block_margins(problem, layer: int, block_size: int, units=None, max_rounds: int = 40):
+    """Margins for block selection: for each query that scores a unit (q_prev at
+    step 0, q_t at step 1), t = the midpoint between the (k/B)-th and (k/B+1)-th
+    largest block maxima (full blocks of B tokens); every token of the full blocks
+    within delta_u of t is redrawn on its side of t.  A block's max is above t
+    exactly when one of its tokens is, so the chosen blocks stay and the band
+    around t empties."""
+    p = problem
+    g = p.g
+    if units is None:
+        units = [(b, h) for b in range(p.batch) for h in range(p.hkv)]
+    q = oracle.as_f64(p.q(layer), p.dtype)
+    qp = oracle.as_f64(p.q_prev(layer), p.dtype)
+    kb = p.topk // block_size
+    for b, h in units:
+        qgs = [qp[b, h * g:(h + 1) * g], q[b, h * g:(h + 1) * g]]
+        K = oracle.as_f64(p.kv("k", layer, b, h), p.dtype)
+        nb = K.shape[0] // block_size
+        if nb <= kb:
+            continue
+        for _ in range(max_rounds):
+            delta = score_delta(qgs, K)
+            bounds, bad = [], set()
+            for qg in qgs:
+                s = oracle.token_scores(qg, K)
+                bm = np.sort(s[:nb * block_size].reshape(nb, block_size).max(axis=1))[::-1]
+                t = 0.5 * (bm[kb - 1] + bm[kb])
+                bounds.append((s, [t]))
+                bad |= set(np.nonzero(np.abs(s[:nb * block_size] - t) < delta)[0].tolist())
+            if not bad:
+                break
+            for row in sorted(bad):
+                _redraw_keeping_sides(p, layer, b, h, K, qgs, row, bounds, delta)
+        else:
+            raise RuntimeError(f"block margins not reached for unit {(b, h)}")
+    return p

@@ -427,6 +427,42 @@ def pin_quantize_invariants(O):
         assert e2 == e + 3 and list(q2) == list(q)
 
 
+# ---------------------------------------------------------------- block selection
+def pin_select_blocks_closed_form(O):
+    # blocks of 2 over 9 tokens: (0.1, 0.9) -> 0.9, (0.2, 0.3) -> 0.3, (0.8, 0.85) -> 0.85,
+    # (0.0, 0.05) -> 0.05; token 8 (0.7) is a partial tail block and never taken.  The two
+    # best blocks are 0 and 2; token-level top-4 would be tokens 1, 4, 5, 8.
+    s = np.array([0.1, 0.9, 0.2, 0.3, 0.8, 0.85, 0.0, 0.05, 0.7])
+    assert list(O.select_blocks(s, 4, 2)) == [0, 1, 4, 5]
+    assert list(O.select_topk(s, 4)) == [1, 4, 5, 8]
+    # equal block scores go to the lower block
+    assert list(O.select_blocks(np.array([0.5, 0.0, 0.0, 0.5, 0.5, 0.0]), 2, 2)) == [0, 1]
+    # blocks of 3 over 7 tokens: (1, 5, 2) -> 5, (9, 0, 0) -> 9; the tail token 6 never counts
+    assert list(O.select_blocks(np.array([1.0, 5.0, 2.0, 9.0, 0.0, 0.0, 99.0]), 3, 3)) == [3, 4, 5]
+
+
+def pin_select_blocks_invariants(O):
+    rng = np.random.default_rng(14)
+    for _ in range(50):
+        bs = int(rng.integers(1, 9))
+        n = int(rng.integers(bs, 200))
+        nb = n // bs
+        kb = int(rng.integers(1, nb + 1))
+        s = rng.integers(0, 6, size=n).astype(np.float64)  # many ties
+        sel = O.select_blocks(s, kb * bs, bs)
+        assert len(sel) == kb * bs and np.all(np.diff(sel) > 0) and sel.max() < nb * bs
+        blocks = sorted(set((sel // bs).tolist()))
+        assert len(blocks) == kb and all(set(range(b * bs, b * bs + bs)) <= set(sel.tolist()) for b in blocks)
+        bmax = s[:nb * bs].reshape(nb, bs).max(axis=1)
+        chosen = set(blocks)
+        for b in range(nb):
+            for c in chosen:
+                if b not in chosen:
+                    assert bmax[c] > bmax[b] or (bmax[c] == bmax[b] and c < b)
+        if bs == 1:
+            assert list(sel) == list(O.select_topk(s, kb))
+
+
 def pin_bf16_decoding(O):
     # IEEE facts about bfloat16 bit patterns
     bits = np.array([0x3F80, 0xC000, 0x3FC0, 0x0000, 0x8000, 0x7F7F, 0x0001, 0x4049], dtype=np.uint16)
@@ -461,5 +497,7 @@ ALL_PINS = [
     pin_plan_persistent,
     pin_quantize_closed_forms,
     pin_quantize_invariants,
+    pin_select_blocks_closed_form,
+    pin_select_blocks_invariants,
     pin_bf16_decoding,
 ]

@@ -205,3 +205,42 @@ def test_per_head_thresholds(need_gpu):
         for h in range(p.hkv):
             assert bool(got1["reuse"][b, h]) == (c[b, h] >= taus[h])
     assert len({bool(x) for x in got1["reuse"].reshape(-1)}) == 2
+
+
+@pytest.mark.parametrize("bs,dtype", [(16, "bf16"), (64, "f32"), (3, "bf16")])
+def test_block_selection(need_gpu, bs, dtype):
+    """Token blocks as the selection unit (full blocks only, ragged tail ignored)."""
+    from tests.margins import enforce_block_margins
+    from top_sparse_attention_02_amd import workload
+
+    p = small_problem(f"blocks_{bs}_{dtype}", batch=2, hq=8, hkv=2, context=5007, topk=40 * bs, dtype=dtype,
+                      persistent=[0, 1])
+    enforce_margins(p, 0)
+    enforce_block_margins(p, 0, bs)
+    log(f"[case blocks {bs} {dtype}] N={p.context} k={p.topk}")
+    bufs = workload.load_layer(p, 0)
+    bufs.set_block_size(bs)
+    bufs.step0()
+    got0 = snapshot(bufs)
+    bufs.step1()
+    got1 = snapshot(bufs)
+    memo = {}
+
+    def kv(b, h):
+        if (b, h) not in memo:
+            memo[(b, h)] = (p.kv("k", 0, b, h), p.kv("v", 0, b, h))
+        return memo[(b, h)]
+
+    qp, q = p.q_prev(0), p.q(0)
+    r0 = oracle.decode_layer(qp, qp, kv, p.hkv, p.topk, math.inf, p.dtype, block_size=bs)
+    idx0 = np.zeros((p.batch, p.hkv, p.topk), dtype=np.int64)
+    for (b, h), r in r0.items():
+        idx0[b, h] = r["idx"]
+    r1 = oracle.decode_layer(q, qp, kv, p.hkv, p.topk, p.tau, p.dtype, idx_prev=idx0, block_size=bs)
+    compare(p, bufs, got0, r0, kv, "step0")
+    compare(p, bufs, got1, r1, kv, "step1")
+    # every selection is whole blocks
+    for b in range(p.batch):
+        for h in range(p.hkv):
+            sel = got1["idx"][b, h]
+            assert np.all(sel.reshape(-1, bs) == (sel.reshape(-1, bs)[:, :1] + np.arange(bs)))

@@ -73,7 +73,7 @@ def _ns(**over):
         ns.decode_layer = lambda *a, **kw: decode_layer(*a, head_of=over["head_of"], **kw)
     if "tau_of" in over:
         ns.decode_layer = lambda *a, **kw: decode_layer(*a, tau_of=over["tau_of"], **kw)
-    for name in ("plan_persistent", "quantize_row", "dequantize_row"):
+    for name in ("plan_persistent", "quantize_row", "dequantize_row", "select_blocks"):
         if name not in over:
             setattr(ns, name, getattr(base, name))
     return ns
@@ -172,6 +172,33 @@ def m_quant_half_away(x):
     return (np.sign(y) * np.floor(np.abs(y) + 0.5)).astype(np.int64), e
 
 
+def m_blocks_sum(s, k, bs):
+    s = np.asarray(s, float)
+    nb = s.shape[0] // bs
+    bsum = s[:nb * bs].reshape(nb, bs).sum(axis=1)
+    blocks = np.sort(base.select_topk(bsum, k // bs))
+    return (blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
+
+
+def m_blocks_tail_selectable(s, k, bs):
+    s = np.asarray(s, float)
+    nb = -(-s.shape[0] // bs)
+    pad = np.concatenate([s, np.full(nb * bs - s.shape[0], -np.inf)])
+    bmax = pad.reshape(nb, bs).max(axis=1)
+    blocks = np.sort(base.select_topk(bmax, k // bs))
+    out = (blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
+    return out
+
+
+def m_blocks_ties_high(s, k, bs):
+    s = np.asarray(s, float)
+    nb = s.shape[0] // bs
+    bmax = s[:nb * bs].reshape(nb, bs).max(axis=1)
+    order = np.lexsort((-np.arange(nb), -bmax))[:k // bs]
+    blocks = np.sort(order)
+    return (blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
+
+
 MUTANTS = {
     "score_sum_over_heads": dict(token_scores=m_sum_over_heads),
     "cosine_mean_of_heads": dict(group_cosine=m_mean_head_cosine),
@@ -195,6 +222,9 @@ MUTANTS = {
     "quant_exponent_low": dict(quantize_row=m_quant_exponent_low),
     "quant_ties_away": dict(quantize_row=m_quant_half_away),
     "dequant_wrong_sign_exponent": dict(dequantize_row=lambda q, e: np.asarray(q, float) * 2.0 ** -e),
+    "blocks_scored_by_sum": dict(select_blocks=m_blocks_sum),
+    "blocks_tail_selectable": dict(select_blocks=m_blocks_tail_selectable),
+    "blocks_ties_to_higher": dict(select_blocks=m_blocks_ties_high),
     "steps_context_fixed": dict(steps_kw=dict(grow=0)),
     "steps_context_one_late": dict(steps_kw=dict(lag=1)),
     "steps_refresh_never_updates": dict(steps_kw=dict(rules={"refresh": "never"})),

@@ -33,7 +33,7 @@ class clo_shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("context", ctypes.c_int64), ("topk", ctypes.c_int64),
                 ("tau", ctypes.c_float), ("dtype", ctypes.c_int32), ("capacity", ctypes.c_int64),
-                ("tau_heads", ctypes.POINTER(ctypes.c_float))]
+                ("tau_heads", ctypes.POINTER(ctypes.c_float)), ("block_size", ctypes.c_int32)]
 
 
 class clo_layer(ctypes.Structure):
@@ -151,6 +151,7 @@ class Shape:
     head_dim: int = 128
     capacity: int = 0  # rows allocated per (sequence, head); 0 = context
     tau_heads: Optional[Sequence[float]] = None  # per-KV-head thresholds; None = tau for every head
+    block_size: int = 0  # selection granularity in tokens (0/1 = single tokens)
 
     def c(self) -> clo_shape:
         th = None
@@ -158,7 +159,8 @@ class Shape:
             th = (ctypes.c_float * len(self.tau_heads))(*[float(x) for x in self.tau_heads])
         cs = clo_shape(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.context, self.topk,
                        self.tau, self.dtype, self.capacity,
-                       ctypes.cast(th, ctypes.POINTER(ctypes.c_float)) if th is not None else None)
+                       ctypes.cast(th, ctypes.POINTER(ctypes.c_float)) if th is not None else None,
+                       int(self.block_size))
         cs._tau_heads = th  # keeps the array alive while the struct is in use
         return cs
 

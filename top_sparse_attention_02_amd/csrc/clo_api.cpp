@@ -67,6 +67,14 @@ clo_status check_shape(const clo_shape* s) {
   if (s->context < 1 || s->context > (int64_t)INT32_MAX) return fail(CLO_E_ARG, "context %lld out of range", (long long)s->context);
   if (s->topk < 1 || s->topk > s->context)
     return fail(CLO_E_ARG, "topk %lld outside 1..context (%lld)", (long long)s->topk, (long long)s->context);
+  if (s->block_size < 0 || s->block_size > 65536) return fail(CLO_E_ARG, "block_size %d outside 0..65536", s->block_size);
+  if (s->block_size > 1) {
+    if (s->topk % s->block_size)
+      return fail(CLO_E_ARG, "topk %lld is not a multiple of block_size %d", (long long)s->topk, s->block_size);
+    if (s->topk > s->context / s->block_size * s->block_size)
+      return fail(CLO_E_ARG, "topk %lld exceeds the %lld tokens of the full blocks", (long long)s->topk,
+                  (long long)(s->context / s->block_size * s->block_size));
+  }
   if (s->capacity != 0 && (s->capacity < s->context || s->capacity > (int64_t)INT32_MAX))
     return fail(CLO_E_ARG, "capacity %lld outside context (%lld)..2^31-1", (long long)s->capacity,
                 (long long)s->context);
@@ -146,6 +154,7 @@ clo_status make_plan(const clo_shape* s, uint64_t pmask, Plan* p) {
   a.G = s->n_q_heads / s->n_kv_heads;
   a.N = s->context;
   a.C = s->capacity ? s->capacity : s->context;
+  a.bs = s->block_size > 1 ? s->block_size : 1;
   a.k = s->topk;
   a.Np = round_up(s->context, 64);
   a.tau = s->tau;
@@ -163,7 +172,8 @@ clo_status make_plan(const clo_shape* s, uint64_t pmask, Plan* p) {
 // Workspace layout: meta | list_all | list_host | list_hit | h0 | h1 | tstate | chist | keys | part,
 // each 256-byte aligned.
 struct WsLayout {
-  size_t meta, list_all, list_host, list_hit, h0, h1, tstate, chist, keys, part, total;
+  size_t meta, list_all, list_host, list_hit, h0, h1, tstate, chist, keys, part, bkeys, h0b, bidx, total;
+  int64_t npb;
   int cmax;
 };
 
@@ -186,6 +196,14 @@ WsLayout ws_layout(const Plan& p) {
   w.chist = take((size_t)p.U * (size_t)w.cmax * kChunkHist * 4);
   w.keys = take((size_t)p.U * (size_t)p.a.Np * 4);
   w.part = take((size_t)p.U * (size_t)p.nch_attn * (size_t)p.a.G * kPartStride * 4);
+  w.bkeys = w.h0b = w.bidx = 0;
+  w.npb = 0;
+  if (p.a.bs > 1) {  // block selection
+    w.npb = round_up(p.a.N / p.a.bs, 64);
+    w.bkeys = take((size_t)p.U * (size_t)w.npb * 4);
+    w.h0b = take((size_t)p.U * 256 * 4);
+    w.bidx = take((size_t)p.U * (size_t)(p.a.k / p.a.bs) * 4);
+  }
   w.total = off;
   return w;
 }
@@ -212,6 +230,10 @@ clo_status bind_ws(const Plan& p, void* ws, size_t ws_bytes, Workspace* w) {
   w->cmax = L.cmax;
   w->keys = reinterpret_cast<uint32_t*>(b + L.keys);
   w->part = reinterpret_cast<float*>(b + L.part);
+  w->bkeys = p.a.bs > 1 ? reinterpret_cast<uint32_t*>(b + L.bkeys) : nullptr;
+  w->h0b = p.a.bs > 1 ? reinterpret_cast<uint32_t*>(b + L.h0b) : nullptr;
+  w->bidx = p.a.bs > 1 ? reinterpret_cast<int32_t*>(b + L.bidx) : nullptr;
+  w->npb = L.npb;
   return ok();
 }
 
@@ -416,7 +438,7 @@ clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const
   if ((st = pre_wait(sync, s))) return st;
   if ((st = hip_status(launch_compact(p.a, reuse, w, 1, s), "compact launch"))) return st;
   if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w, score_counter(w, 0), cu, s), "score launch"))) return st;
-  if ((st = hip_status(launch_topk(p.a, span_all_misses(w), p.U, w.keys, w, s), "top-k launch"))) return st;
+  if ((st = hip_status(launch_select(p.a, span_all_misses(w), p.U, w, s), "top-k launch"))) return st;
   return post_signal(sync, s);
 }
 
@@ -475,7 +497,7 @@ clo_status step_in_order(const Plan& p, const Workspace& w, const void* q, const
   if ((st = hip_status(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch"))) return st;
   if ((st = hip_status(launch_compact(p.a, reuse, w, 1, s), "compact launch"))) return st;
   if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w, score_counter(w, 0), cu, s), "score launch"))) return st;
-  if ((st = hip_status(launch_topk(p.a, span_all_misses(w), p.U, w.keys, w, s), "top-k launch"))) return st;
+  if ((st = hip_status(launch_select(p.a, span_all_misses(w), p.U, w, s), "top-k launch"))) return st;
   if ((st = hip_status(launch_attn_partial(p.a, q, w.part, kAllUnits, p.U, s), "attention launch"))) return st;
   return hip_status(launch_attn_combine(p.a, w.part, out, s), "attention combine launch");
 }
@@ -503,7 +525,7 @@ clo_status step_overlapped(const Plan& p, const Workspace& w, const void* q, con
   CLO_TRY(launch_compact(p.a, reuse, w, R, s), "compact launch");
   for (int r = 0; r < R; ++r) {
     CLO_TRY(launch_score(p.a, q, span_range(w, r), per, w, score_counter(w, r), cu, s), "score launch");
-    CLO_TRY(launch_topk(p.a, span_range(w, r), per, w.keys, w, s), "top-k launch");
+    CLO_TRY(launch_select(p.a, span_range(w, r), per, w, s), "top-k launch");
     CLO_TRY(hipEventRecord(dq->ev_topk[r], s), "event record");
     CLO_TRY(hipStreamWaitEvent(gs, dq->ev_topk[r], 0), "stream wait");
     if (r == 0) {

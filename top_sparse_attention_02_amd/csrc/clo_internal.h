@@ -52,6 +52,7 @@ struct LayerArgs {
   void* k_cache;
   void* v_cache;
   int32_t* idx;
+  int32_t bs;            // selection block size (1 = tokens)
   int32_t host_fmt;      // CLO_HOST_NATIVE or CLO_HOST_INT8
   const int8_t* k_exp;   // CLO_HOST_INT8: [B, H, C] row exponents of k_host / v_host
   const int8_t* v_exp;
@@ -102,6 +103,10 @@ struct Workspace {
   int32_t* list_host;  // [U] miss units of non-persistent heads, ascending
   int32_t* list_hit;   // [U] reuse units, ascending
   uint32_t* keys;      // [U][Np] order-preserving score keys
+  uint32_t* bkeys;     // block selection: [U][Npb] block keys (max of their tokens' keys)
+  uint32_t* h0b;       // block selection: [U][256] digit-1 histograms of the block keys
+  int32_t* bidx;       // block selection: [U][k / bs] selected blocks, ascending
+  int64_t npb;         // block selection: padded row stride of bkeys
   float* part;         // [U][nch][G][kPartStride] attention partials
 };
 
@@ -127,6 +132,8 @@ hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_
                         uint32_t* counter, int num_cu, hipStream_t s);
 hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uint32_t* keys, const Workspace& w,
                        hipStream_t s);
+// Top-k of tokens, or of token blocks when a.bs > 1, into a.idx (ascending tokens).
+hipError_t launch_select(const LayerArgs& a, Span sp, int64_t max_units, const Workspace& w, hipStream_t s);
 // max_blocks bounds the grid: the host link saturates with a few hundred
 // waves in flight, and a smaller grid leaves the CUs to concurrent kernels.
 // Blocks take work items from *counter (zero at launch) so that blocks that

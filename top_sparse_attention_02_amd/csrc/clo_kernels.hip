@@ -157,7 +157,8 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
                                                        uint64_t pmask, int R, int32_t* __restrict__ meta,
                                                        int32_t* __restrict__ list_all,
                                                        int32_t* __restrict__ list_host,
-                                                       int32_t* __restrict__ list_hit, uint32_t* __restrict__ h0) {
+                                                       int32_t* __restrict__ list_hit, uint32_t* __restrict__ h0,
+                                                       uint32_t* __restrict__ h0b) {
   __shared__ int wsum[3][16];
   __shared__ int base[3];
   __shared__ int rcount[2][kMaxRanges];
@@ -196,6 +197,10 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
       // digit-1 histogram of the unit's top-k, filled by the scoring kernel
       u32x4* hz = reinterpret_cast<u32x4*>(h0 + (int64_t)u * 256);
       for (int i = 0; i < 64; ++i) hz[i] = u32x4{0u, 0u, 0u, 0u};
+      if (h0b) {
+        hz = reinterpret_cast<u32x4*>(h0b + (int64_t)u * 256);
+        for (int i = 0; i < 64; ++i) hz[i] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
     if (host) list_host[oh] = u;
     if (hit) list_hit[ot] = u;
@@ -912,6 +917,64 @@ __global__ __launch_bounds__(kTopkThreads) void topk_write_kernel(LayerArgs a, S
   }
 }
 
+// ---------------------------------------------------------------- A3 top-k over token blocks
+// Block b of a unit covers tokens b*bs .. b*bs+bs-1 (full blocks only); its key is
+// the largest of its tokens' keys (= the key of its best score).  Each CTA takes
+// kBlockKeysPerCta blocks of one unit, writes their keys, counts their digit 1
+// into the unit's block histogram (h0b, cleared by the compact kernel), and the
+// CTA with the unit's first chunk clears h1 and resets the radix state: the top-k
+// kernels then select among the block keys as they do among token keys.
+constexpr int kBlockKeysPerCta = 4096;
+
+__global__ __launch_bounds__(256) void block_keys_kernel(LayerArgs a, Span sp, const uint32_t* __restrict__ keys,
+                                                         uint32_t* __restrict__ bkeys, int64_t nb, int64_t npb,
+                                                         int cmaxb, uint32_t* __restrict__ h0b,
+                                                         uint32_t* __restrict__ h1, TopkState* __restrict__ st,
+                                                         int64_t kb) {
+  __shared__ uint32_t s_h[4][256];
+  const UnitChunk uc = unit_chunk(sp, cmaxb);
+  if (!uc.valid) return;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int i = tid; i < 4 * 256; i += 256) (&s_h[0][0])[i] = 0u;
+  __syncthreads();
+  const uint32_t* kk = keys + (int64_t)uc.u * a.Np;
+  uint32_t* bo = bkeys + (int64_t)uc.u * npb;
+  const int64_t j0 = (int64_t)uc.c * kBlockKeysPerCta;
+  const int64_t j1 = (j0 + kBlockKeysPerCta < nb) ? j0 + kBlockKeysPerCta : nb;
+  for (int64_t j = j0 + tid; j < j1; j += 256) {
+    const uint32_t* t = kk + j * a.bs;
+    uint32_t m = 0u;
+    if ((a.bs & 3) == 0) {
+      for (int i = 0; i < a.bs; i += 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(t + i);
+        m = max(max(m, max(v[0], v[1])), max(v[2], v[3]));
+      }
+    } else {
+      for (int i = 0; i < a.bs; ++i) m = max(m, t[i]);
+    }
+    bo[j] = m;
+    atomicAdd(&s_h[wave][m >> 24], 1u);
+  }
+  __syncthreads();
+  const uint32_t sum = s_h[0][tid] + s_h[1][tid] + s_h[2][tid] + s_h[3][tid];
+  if (sum) atomicAdd(h0b + (int64_t)uc.u * 256 + tid, sum);
+  if (uc.c == 0) {
+    h1[(int64_t)uc.u * 256 + tid] = 0u;
+    if (tid == 0) st[uc.u] = TopkState{0u, 0u, (uint32_t)kb, 0u};
+  }
+}
+
+// idx[u][i] = the i-th token of the unit's selected blocks (blocks ascending).
+__global__ __launch_bounds__(256) void expand_blocks_kernel(LayerArgs a, Span sp, const int32_t* __restrict__ bidx,
+                                                            int64_t kb, int cmaxe) {
+  const UnitChunk uc = unit_chunk(sp, cmaxe);
+  if (!uc.valid) return;
+  const int64_t i0 = (int64_t)uc.c * 1024;
+  const int64_t i1 = (i0 + 1024 < a.k) ? i0 + 1024 : a.k;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += 256)
+    a.idx[(int64_t)uc.u * a.k + i] = bidx[(int64_t)uc.u * kb + i / a.bs] * a.bs + (int32_t)(i % a.bs);
+}
+
 // ---------------------------------------------------------------- A4 gather
 // Rows of d elements are moved as 16-byte pieces: LPR lanes per row.  The
 // loads from pinned host memory are issued UNR rows deep per lane before any
@@ -1491,7 +1554,7 @@ hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, u
 
 hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, int ranges, hipStream_t s) {
   compact_kernel<<<1, 1024, 0, s>>>(reuse, a.B * a.Hkv, a.Hkv, a.pmask, ranges, w.meta, w.list_all, w.list_host,
-                                    w.list_hit, w.h0);
+                                    w.list_hit, w.h0, a.bs > 1 ? w.h0b : nullptr);
   return hipGetLastError();
 }
 
@@ -1529,6 +1592,31 @@ hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uin
   for (int shift = 16; shift >= 0; shift -= 8)
     topk_pass_kernel<<<cg, kTopkThreads, 0, s>>>(a, sp, keys, w.h0, w.h1, w.tstate, w.chist, cmax, shift);
   topk_write_kernel<<<cg, kTopkThreads, 0, s>>>(a, sp, keys, w.tstate, w.chist, cmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const LayerArgs& a, Span sp, int64_t max_units, const Workspace& w, hipStream_t s) {
+  if (a.bs <= 1) return launch_topk(a, sp, max_units, w.keys, w, s);
+  const int64_t nb = a.N / a.bs, kb = a.k / a.bs;
+  LayerArgs ab = a;  // the blocks as the "tokens" of a top-k
+  ab.N = nb;
+  ab.k = kb;
+  ab.Np = w.npb;
+  ab.idx = w.bidx;
+  ab.bs = 1;
+  Workspace wb = w;
+  wb.h0 = w.h0b;
+  wb.keys = w.bkeys;
+  wb.cmax = (int32_t)((nb + kTopkChunk - 1) / kTopkChunk);
+  const int cmaxb = (int)((nb + kBlockKeysPerCta - 1) / kBlockKeysPerCta);
+  const unsigned g1 = (unsigned)(max_units * cmaxb > 0 ? max_units * cmaxb : 1);
+  block_keys_kernel<<<g1, 256, 0, s>>>(a, sp, w.keys, w.bkeys, nb, w.npb, cmaxb, w.h0b, w.h1, w.tstate, kb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = launch_topk(ab, sp, max_units, w.bkeys, wb, s)) != hipSuccess) return e;
+  const int cmaxe = (int)((a.k + 1023) / 1024);
+  const unsigned g2 = (unsigned)(max_units * cmaxe > 0 ? max_units * cmaxe : 1);
+  expand_blocks_kernel<<<g2, 256, 0, s>>>(a, sp, w.bidx, kb, cmaxe);
   return hipGetLastError();
 }
 

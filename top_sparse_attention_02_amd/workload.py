@@ -87,6 +87,13 @@ class LayerBuffers:
         ws = clo.clo_workspace_size(self.shape)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
 
+    def set_block_size(self, block_size: int):
+        """Select token blocks of this size (0/1 = tokens); grows the workspace when needed."""
+        self.shape.block_size = block_size
+        need = clo.clo_workspace_size(self.shape)
+        if need > self.ws.numel():
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.ws.device)
+
     # ----------------------------------------------------------------- views
     def layer(self) -> clo.Layer:
         return clo.Layer(self.mask, self.k_hbm, self.v_hbm, self.k_host, self.v_host, self.k_score, self.k_cache,
