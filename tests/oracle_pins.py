@@ -13,12 +13,18 @@ Sources of truth used here, none of which is the oracle's own code:
     distinct scores, scipy's cosine distance;
   * brute force over all k-subsets for tiny selections;
   * invariants (softmax sums to 1, convex hull, scale and permutation
-    behaviour, k = 1 returns the row).
+    behaviour, k = 1 returns the row);
+  * the worked examples stored as text under tests/golden/ (each file names
+    the passage of the pages it follows and how its values were derived).
 """
 from __future__ import annotations
 
+import ast
 import itertools
+import json
 import math
+import operator
+import os
 
 import numpy as np
 
@@ -474,6 +480,111 @@ def pin_bf16_decoding(O):
     assert list(O.as_f64(f, "f32")) == [float(np.float32(0.1)), -3.25]
 
 
+# ---------------------------------------------------------------- worked examples (tests/golden)
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+_BINOPS = {ast.Add: operator.add, ast.Sub: operator.sub, ast.Mult: operator.mul, ast.Div: operator.truediv,
+           ast.Pow: operator.pow}
+_FUNCS = {"sqrt": math.sqrt, "exp": math.exp, "sigmoid": sigmoid}
+
+
+def golden_value(x):
+    """A fixture number: a JSON number, or a closed form written as text over
+    + - * / **, sqrt, exp, sigmoid and inf (evaluated here, nothing else is
+    allowed)."""
+    if isinstance(x, (int, float)) and not isinstance(x, bool):
+        return float(x)
+    if isinstance(x, list):
+        return [golden_value(v) for v in x]
+
+    def ev(n):
+        if isinstance(n, ast.Expression):
+            return ev(n.body)
+        if isinstance(n, ast.Constant) and isinstance(n.value, (int, float)):
+            return float(n.value)
+        if isinstance(n, ast.Name) and n.id == "inf":
+            return math.inf
+        if isinstance(n, ast.BinOp) and type(n.op) in _BINOPS:
+            return _BINOPS[type(n.op)](ev(n.left), ev(n.right))
+        if isinstance(n, ast.UnaryOp) and isinstance(n.op, (ast.USub, ast.UAdd)):
+            v = ev(n.operand)
+            return -v if isinstance(n.op, ast.USub) else v
+        if (isinstance(n, ast.Call) and isinstance(n.func, ast.Name) and n.func.id in _FUNCS
+                and len(n.args) == 1 and not n.keywords):
+            return _FUNCS[n.func.id](ev(n.args[0]))
+        raise ValueError(f"not a closed form: {x!r}")
+
+    return ev(ast.parse(str(x), mode="eval"))
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN_DIR, name)) as f:
+        return json.load(f)
+
+
+def golden_array(x):
+    return np.array(golden_value(x), dtype=np.float64)
+
+
+def pin_golden_reuse(O):
+    for c in golden("reuse_test.json")["cases"]:
+        cos = O.group_cosine(golden_array(c["q"]), golden_array(c["q_prev"]))
+        assert close(cos, golden_value(c["cos"]), 1e-12), c
+        assert O.reuse_decision(cos, golden_value(c["tau"])) is c["reuse"], c
+
+
+def pin_golden_selection(O):
+    fx = golden("selection.json")
+    for c in fx["cases"]:
+        s = O.token_scores(golden_array(c["q"]), golden_array(c["K"]))
+        assert close(s, golden_array(c["scores"]), 1e-12), c["name"]
+        assert list(O.select_topk(s, c["k"])) == c["idx"], c["name"]
+    for c in fx["block_cases"]:
+        assert list(O.select_blocks(golden_array(c["scores"]), c["k"], c["block_size"])) == c["idx"], c
+
+
+def pin_golden_attention(O):
+    for c in golden("attention.json")["cases"]:
+        d = c["d"]
+        pad = lambda a: np.pad(golden_array(a), ((0, 0), (0, d - len(a[0]))))  # noqa: E731
+        out, p = O.attend(pad(c["q"]), pad(c["Kc"]), pad(c["Vc"]), return_p=True)
+        assert close(p, golden_array(c["p"]), 1e-12), c["name"]
+        w = len(c["out"][0])
+        assert close(out[:, :w], golden_array(c["out"]), 1e-12), c["name"]
+        assert close(out[:, w:], 0.0), c["name"]
+
+
+def pin_golden_decode_step(O):
+    fx = golden("decode_step.json")
+    K, V = golden_array(fx["K"]), golden_array(fx["V"])
+    for c in fx["cases"]:
+        r = O.decode_unit(golden_array(c["q"]), golden_array(c["q_prev"]), K, V, fx["k"], golden_value(c["tau"]),
+                          idx_prev=np.array(c["idx_prev"]))
+        assert close(r["cos"], golden_value(c["cos"]), 1e-12), c["name"]
+        assert r["reuse"] is c["reuse"] and list(r["idx"]) == c["idx"], c["name"]
+        assert close(r["out"], golden_array(c["out"]), 1e-12), c["name"]
+
+
+def pin_golden_growing_context(O):
+    fx = golden("growing_context.json")
+    qs = [golden_array(q) for q in fx["queries"]]
+    K, V = golden_array(fx["K"]), golden_array(fx["V"])
+    for policy, want in fx["policies"].items():
+        res = O.decode_steps_unit(qs, K, V, fx["n0"], fx["k"], golden_value(fx["tau"]), policy)
+        assert [r["reuse"] for r in res] == want["reuse"], policy
+        assert [list(r["idx"]) for r in res] == want["idx"], policy
+        assert close([r["cos"] for r in res], golden_array(want["cos"]), 1e-12), policy
+        for r, o in zip(res, want["out"]):
+            assert close(r["out"], golden_array(o), 1e-12), policy
+
+
+def pin_golden_int8_rows(O):
+    for c in golden("int8_rows.json")["cases"]:
+        x = golden_array(c["x"])
+        q, e = O.quantize_row(x)
+        assert e == c["e"] and list(q) == c["q"], c
+        assert list(O.dequantize_row(q, e)) == [v * 2.0 ** c["e"] for v in c["q"]], c
+
+
 ALL_PINS = [
     pin_cosine_closed_forms,
     pin_cosine_group_concatenated,
@@ -500,4 +611,10 @@ ALL_PINS = [
     pin_select_blocks_closed_form,
     pin_select_blocks_invariants,
     pin_bf16_decoding,
+    pin_golden_reuse,
+    pin_golden_selection,
+    pin_golden_attention,
+    pin_golden_decode_step,
+    pin_golden_growing_context,
+    pin_golden_int8_rows,
 ]
