@@ -80,6 +80,10 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 // their maxima (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 __device__ __forceinline__ void wait_vm_acks() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until this wave's LDS operations have completed: s_waitcnt lgkmcnt(0),
+// vmcnt and expcnt left at their maxima (63 and 7).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Sum over the 16 lanes of a row group; the xor butterfly leaves the same
 // bits in every lane of the group.
 __device__ __forceinline__ float sum16(float x) {
@@ -371,8 +375,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int col = lane & 15, ks = lane >> 4;       // tile column / k-slice of this lane
   int cur_u = -1, prev_c = 0;
   bf16x8 qa[4];
+  if (threadIdx.x == 0) s_item = atomicAdd(counter, 1u);
   for (;;) {
-    if (threadIdx.x == 0) s_item = atomicAdd(counter, 1u);
     __syncthreads();
     const int64_t it = s_item;
     // every wave is past the previous item: add its histogram to the unit's
@@ -405,6 +409,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     // compiler from issuing them early
     uint32_t pend[TILES / 4];
     bool have_pend = false;
+    // the next item is claimed once the last key loads of this one are issued:
+    // the counter's round trip then overlaps the item's tail, while a claim at
+    // the item's start would hold work back from blocks that run out earlier
+    uint32_t next_item = 0;
+    bool claimed = false;
 #pragma unroll
     for (int t0 = 0; t0 < kKeysPerWave; t0 += 16 * TILES) {
       if (w_begin + t0 >= a.N) break;  // uniform per wave
@@ -416,6 +425,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         const uint16_t* kr = kb + row * kHeadDim + ks * 8;
 #pragma unroll
         for (int s = 0; s < 4; ++s) kbuf[t][s] = *reinterpret_cast<const u32x4*>(kr + s * 32);
+      }
+      if (t0 + 16 * TILES >= kKeysPerWave && threadIdx.x == 0) {
+        next_item = atomicAdd(counter, 1u);
+        claimed = true;
       }
       if (have_pend) {
 #pragma unroll
@@ -463,6 +476,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
       for (int i = 0; i < TILES / 4; ++i) atomicAdd(&s_h[wave][pend[i]], 1u);
     }
+    // read at the top of the next iteration, after the barrier there; every
+    // wave read the current value before the barrier that follows the flush
+    if (threadIdx.x == 0) s_item = claimed ? next_item : atomicAdd(counter, 1u);
+    // the LDS writes of this item (s_item, the digit counts) complete before the
+    // barrier at the loop top: hipcc (ROCm 7.2, gfx950) emits that barrier on
+    // this back edge without the LDS wait its fence implies, and other waves
+    // then read the previous item number
+    wait_lds();
   }
 }
 
@@ -1309,6 +1330,14 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
       }
     }
   }
+  // the first batch of V rows is requested now, so that its loads are in flight
+  // across the softmax phase
+  Row8<T> vpre[kAttnBatch];
+#pragma unroll
+  for (int j = 0; j < kAttnBatch; ++j) {
+    const int i = row_base + 4 * j;
+    vpre[j].load(vbase + row_of(i < nrows ? i : nrows - 1) * kHeadDim + sub * 8);
+  }
   __syncthreads();
   // phase 2: softmax statistics per head
   for (int g = wave; g < G; g += 4) {
@@ -1341,7 +1370,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
 #pragma unroll
       for (int j = 0; j < kAttnBatch; ++j) {
         const int i = row_base + 4 * (j0 + j);
-        vr[j].load(vbase + row_of(i < nrows ? i : nrows - 1) * kHeadDim + sub * 8);
+        if (j0 == 0)
+          vr[j] = vpre[j];
+        else
+          vr[j].load(vbase + row_of(i < nrows ? i : nrows - 1) * kHeadDim + sub * 8);
       }
 #pragma unroll
       for (int j = 0; j < kAttnBatch; ++j) {
