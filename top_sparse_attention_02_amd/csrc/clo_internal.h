@@ -61,9 +61,12 @@ struct LayerArgs {
 constexpr int kQuantMinExp = -120;  // smallest row exponent of the int8 host format
 
 // Unit ranges of one decode step: units are split into R contiguous ranges
-// (unit u belongs to range u * R / U) so that the gather of one range can run
-// while the next range is scored.
+// [first[r], first[r + 1]) so that the gather of one range can run while the
+// next range is scored.
 constexpr int kMaxRanges = 16;
+struct RangeBounds {
+  int32_t first[kMaxRanges + 1];  // first unit of each range; first[R] = U
+};
 
 // Layout of the int32 "meta" block at the start of the workspace.
 constexpr int kMetaCountAll = 0;   // miss units
@@ -124,7 +127,8 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, uint8_t* reuse, float* cos,
                         hipStream_t s);
 // max_units: an upper bound on the span's length, used to size the grid.
-hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, int ranges, hipStream_t s);
+hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, int ranges,
+                          const RangeBounds& bounds, hipStream_t s);
 // counter: zero at launch (the compact kernel clears the range counters).
 // Writes w.keys and the digit-1 histograms of the span's units (cleared by the
 // compact kernel).
@@ -143,7 +147,9 @@ hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, Span sp, int6
 hipError_t launch_zero(uint32_t* word, hipStream_t s);
 hipError_t launch_attn_partial(const LayerArgs& a, const void* q, float* part, Span sp, int64_t max_units,
                                hipStream_t s);
-hipError_t launch_attn_combine(const LayerArgs& a, const float* part, void* out, hipStream_t s);
+// Output rows of the span's units (all units when sp.list == nullptr).
+hipError_t launch_attn_combine(const LayerArgs& a, const float* part, void* out, Span sp, int64_t max_units,
+                               hipStream_t s);
 hipError_t launch_append(const LayerArgs& a, const void* k_new, const void* v_new, int64_t position,
                          void* k_hbm, void* v_hbm, void* k_host, void* v_host, void* k_score, hipStream_t s);
 hipError_t launch_update_reference(const LayerArgs& a, const void* q, const uint8_t* reuse, void* q_ref,

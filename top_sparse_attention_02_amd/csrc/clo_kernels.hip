@@ -158,7 +158,8 @@ __global__ __launch_bounds__(64) void reuse_kernel(const T* __restrict__ q, cons
 // (miss units, miss units of non-persistent heads, reuse units) and the first
 // list position of each of the R unit ranges; nothing is read back by the host.
 __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict__ reuse, int U, int Hkv,
-                                                       uint64_t pmask, int R, int32_t* __restrict__ meta,
+                                                       uint64_t pmask, int R, RangeBounds rb,
+                                                       int32_t* __restrict__ meta,
                                                        int32_t* __restrict__ list_all,
                                                        int32_t* __restrict__ list_host,
                                                        int32_t* __restrict__ list_hit, uint32_t* __restrict__ h0,
@@ -177,7 +178,8 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
     const bool host = miss && !((pmask >> (u % Hkv)) & 1ull);
     const bool hit = valid && !miss;
     if (miss) {
-      const int r = (int)((int64_t)u * R / U);
+      int r = 0;
+      while (r + 1 < R && u >= rb.first[r + 1]) ++r;
       atomicAdd(&rcount[0][r], 1);
       if (host) atomicAdd(&rcount[1][r], 1);
     }
@@ -1425,10 +1427,16 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
 // hundreds of chunks one load latency after another.
 template <typename T, int S>
 __global__ __launch_bounds__(128 * S) void attn_combine_kernel(LayerArgs a, const float* __restrict__ part, int nch,
-                                                               T* __restrict__ out) {
+                                                               Span sp, T* __restrict__ out) {
   __shared__ float sM[S], sL[S], sO[S][kHeadDim];
   const int G = a.G;
-  const int u = blockIdx.x / G, g = blockIdx.x % G;
+  const int i = blockIdx.x / G, g = blockIdx.x % G;
+  int u = i;
+  if (sp.list) {
+    const int lo = *sp.lo;
+    if (i >= *sp.hi - lo) return;  // uniform per block
+    u = sp.list[lo + i];
+  }
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int grp = threadIdx.x / kHeadDim, col = threadIdx.x % kHeadDim;
   const int per = (nch + S - 1) / S;
@@ -1584,9 +1592,10 @@ hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, u
   return hipGetLastError();
 }
 
-hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, int ranges, hipStream_t s) {
-  compact_kernel<<<1, 1024, 0, s>>>(reuse, a.B * a.Hkv, a.Hkv, a.pmask, ranges, w.meta, w.list_all, w.list_host,
-                                    w.list_hit, w.h0, a.bs > 1 ? w.h0b : nullptr);
+hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, int ranges,
+                          const RangeBounds& bounds, hipStream_t s) {
+  compact_kernel<<<1, 1024, 0, s>>>(reuse, a.B * a.Hkv, a.Hkv, a.pmask, ranges, bounds, w.meta, w.list_all,
+                                    w.list_host, w.list_hit, w.h0, a.bs > 1 ? w.h0b : nullptr);
   return hipGetLastError();
 }
 
@@ -1701,17 +1710,20 @@ hipError_t launch_attn_partial(const LayerArgs& a, const void* q, float* part, S
   });
 }
 
-hipError_t launch_attn_combine(const LayerArgs& a, const float* part, void* out, hipStream_t s) {
+hipError_t launch_attn_combine(const LayerArgs& a, const float* part, void* out, Span sp, int64_t max_units,
+                               hipStream_t s) {
   const int nch = (int)((a.k + kAttnChunk - 1) / kAttnChunk);
-  const unsigned grid = (unsigned)((int64_t)a.B * a.Hkv * a.G);
+  const int64_t units = sp.list ? max_units : (int64_t)a.B * a.Hkv;
+  if (units <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)(units * a.G);
   // chunk groups: about 16 or more chunks each
   const int S = nch > 64 ? 8 : nch > 32 ? 4 : nch > 16 ? 2 : 1;
   auto go = [&](auto sc) {
     constexpr int SG = decltype(sc)::value;
     if (a.dtype == CLO_F32)
-      attn_combine_kernel<float, SG><<<grid, 128 * SG, 0, s>>>(a, part, nch, static_cast<float*>(out));
+      attn_combine_kernel<float, SG><<<grid, 128 * SG, 0, s>>>(a, part, nch, sp, static_cast<float*>(out));
     else
-      attn_combine_kernel<uint16_t, SG><<<grid, 128 * SG, 0, s>>>(a, part, nch, static_cast<uint16_t*>(out));
+      attn_combine_kernel<uint16_t, SG><<<grid, 128 * SG, 0, s>>>(a, part, nch, sp, static_cast<uint16_t*>(out));
   };
   switch (S) {
     case 1: go(std::integral_constant<int, 1>{}); break;
