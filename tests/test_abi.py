@@ -68,6 +68,8 @@ def test_workspace_size():
     (dict(topk=0), clo.CLO_E_ARG),
     (dict(context=0, topk=0), clo.CLO_E_ARG),
     (dict(batch=-1), clo.CLO_E_ARG),
+    # units x 256-key chunks beyond 31 bits (grids and work counters)
+    (dict(batch=2 ** 20, n_q_heads=64, n_kv_heads=64, context=8192, topk=100), clo.CLO_E_ARG),
 ])
 def test_bad_shapes_rejected_before_launch(kw, status):
     with pytest.raises(clo.CloError) as e:

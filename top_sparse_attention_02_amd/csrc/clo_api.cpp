@@ -166,6 +166,10 @@ clo_status make_plan(const clo_shape* s, uint64_t pmask, Plan* p) {
   p->e = esize(s->dtype);
   p->U = (int64_t)a.B * a.Hkv;
   p->nch_attn = (int)((a.k + kAttnChunk - 1) / kAttnChunk);
+  // every grid and work-item count (at most units x 256-key chunks) fits in 31 bits
+  if (p->U * ((a.N + 255) / 256) > (int64_t)INT32_MAX)
+    return fail(CLO_E_ARG, "batch x n_kv_heads x context/256 = %lld exceeds 2^31-1",
+                (long long)(p->U * ((a.N + 255) / 256)));
   return ok();
 }
 
