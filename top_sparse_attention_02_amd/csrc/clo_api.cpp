@@ -470,7 +470,9 @@ clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const u
   uint32_t* counter = reinterpret_cast<uint32_t*>(w.meta + kMetaGather);
   if ((st = pre_wait(sync, s))) return st;
   if ((st = hip_status(launch_zero(counter, s), "gather counter launch"))) return st;
-  if ((st = hip_status(launch_gather(p.a, reuse, kAllUnits, p.U, kGatherBlocksAlone, counter, s), "gather launch")))
+  if ((st = hip_status(launch_gather(p.a, reuse, kAllUnits, p.U,
+                                     p.a.host_fmt == CLO_HOST_INT8 ? kGatherBlocksAloneQ8 : kGatherBlocksAlone,
+                                     counter, s), "gather launch")))
     return st;
   return post_signal(sync, s);
 }

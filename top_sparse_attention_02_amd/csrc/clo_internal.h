@@ -34,6 +34,13 @@ constexpr int kPartStride = kHeadDim + 2;  // floats per (chunk, head) partial: 
 constexpr int kGatherUnroll = 2;
 constexpr int kGatherBlocksOverlapped = 32;
 constexpr int kGatherBlocksAlone = 24;
+// The int8 gather moves half the host bytes per row and writes twice as many
+// to HBM, and its items wait on two dependent index and exponent loads before
+// any host read: it needs more blocks to keep the link busy.  Measured on
+// MI355X with 24 / 32 / 40 blocks: the standalone gather at 512 x 13108 rows
+// 52.7 / 55.2 / 56.3 GB/s; the 48-layer loop at B=8, N=262144 19.6 / 20.7 /
+// 21.6 steps/s, and at B=1, N=524288 76.5 / 77.9 / 73.8.
+constexpr int kGatherBlocksAloneQ8 = 32;
 
 // Everything a kernel needs to address one layer's buffers.
 struct LayerArgs {
