@@ -471,7 +471,7 @@ clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const u
   if ((st = pre_wait(sync, s))) return st;
   if ((st = hip_status(launch_zero(counter, s), "gather counter launch"))) return st;
   if ((st = hip_status(launch_gather(p.a, reuse, kAllUnits, p.U,
-                                     p.a.host_fmt == CLO_HOST_INT8 ? kGatherBlocksAloneQ8 : kGatherBlocksAlone,
+                                     p.U >= kGatherWideUnits ? kGatherBlocksAloneWide : kGatherBlocksAlone,
                                      counter, s), "gather launch")))
     return st;
   return post_signal(sync, s);

@@ -28,19 +28,20 @@ constexpr int kPartStride = kHeadDim + 2;  // floats per (chunk, head) partial: 
 //    384 KiB    56.7 GB/s      1.2-1.35x           1.3x   (24 blocks x 2 rows)
 //    128 KiB    49.4 GB/s      1.1-1.3x            1.2x
 // The overlapped single-layer step is bound by the gather alone and takes 32
-// blocks (512 KiB); a standalone gather usually runs beside the selection and
-// attention of other layers and takes 24 (384 KiB): on the 48-layer loop at
-// 512K context, 24 blocks gave 23.8 ms per step against 25.2 ms with 32.
+// blocks (512 KiB).  A standalone gather (one layer of the 48-layer loop, or
+// a phase of its own) takes 32 blocks, or 40 for layers of 64 units or more:
+// there the gather outweighs the selection it slows.  48-layer loop, steps/s
+// with 24 / 32 / 40 blocks:
+//   B=8, N=262144 (64 units)     native 11.7 / 12.0 / 12.3   int8 19.6 / 20.7 / 21.6
+//   B=1, N=524288 (8 units)      native 46.7 / 46.8 / 44.8   int8 76.5 / 77.9 / 73.8
+// The int8 gather alone (512 x 13108 rows) reads 52.7 / 55.2 / 56.3 GB/s: its
+// items wait on index and exponent loads before any host read, and its rows
+// carry half the host bytes.
 constexpr int kGatherUnroll = 2;
 constexpr int kGatherBlocksOverlapped = 32;
-constexpr int kGatherBlocksAlone = 24;
-// The int8 gather moves half the host bytes per row and writes twice as many
-// to HBM, and its items wait on two dependent index and exponent loads before
-// any host read: it needs more blocks to keep the link busy.  Measured on
-// MI355X with 24 / 32 / 40 blocks: the standalone gather at 512 x 13108 rows
-// 52.7 / 55.2 / 56.3 GB/s; the 48-layer loop at B=8, N=262144 19.6 / 20.7 /
-// 21.6 steps/s, and at B=1, N=524288 76.5 / 77.9 / 73.8.
-constexpr int kGatherBlocksAloneQ8 = 32;
+constexpr int kGatherBlocksAlone = 32;
+constexpr int kGatherBlocksAloneWide = 40;  // layers of at least kGatherWideUnits units
+constexpr int kGatherWideUnits = 64;
 
 // Everything a kernel needs to address one layer's buffers.
 struct LayerArgs {
