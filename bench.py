@@ -66,6 +66,8 @@ def parse():
                          "k is rounded down to one)")
     ap.add_argument("--no-compare-native", action="store_true",
                     help="int8 host KV, configs 1-3: skip the output comparison against the native format")
+    ap.add_argument("--select-streams", type=int, default=1, metavar="S",
+                    help="48-layer loop: streams the layers' selections alternate between")
     ap.add_argument("--growing", type=int, default=0, metavar="T",
                     help="configs 1-3: T decode steps over a context that grows by one appended token per "
                          "step, under both reference policies (previous step's query / query at the last "
@@ -533,7 +535,7 @@ def main():
         for bufs in layers:
             bufs.set_block_size(args.block_size)
     if multi:
-        loop = workload.LayerLoop(layers)
+        loop = workload.LayerLoop(layers, select_streams=args.select_streams)
         loop.step(cold=True)
         step = (lambda: loop.step()) if args.step == 1 else (lambda: loop.step(cold=True))
     else:
@@ -617,7 +619,8 @@ def main():
                    (f", selection in blocks of {args.block_size} tokens, k={p.topk}" if args.block_size > 1 else ""),
                    "layers": p.layers, "batch": p.batch, "q_heads": p.hq, "kv_heads": p.hkv, "head_dim": HEAD_DIM,
                    "context": p.context, "topk": p.topk, "tau": p.tau, "step": args.step,
-                   "data_layers": p.data_layers or p.layers, "host_memory": args.host_memory},
+                   "data_layers": p.data_layers or p.layers, "host_memory": args.host_memory,
+                   **({"select_streams": args.select_streams} if multi else {})},
         "roofline": roofline,
         "persistent_plan": None if plan is None else {k: v for k, v in plan.items() if k != "persistent"},
         "block_size": args.block_size or 1,

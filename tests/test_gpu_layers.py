@@ -30,15 +30,16 @@ def enforce_all_layers(p):
     raise RuntimeError("margins did not settle")
 
 
-def test_layer_loop_matches_sequential_and_oracle(need_gpu):
+@pytest.mark.parametrize("select_streams", [1, 2, 3])
+def test_layer_loop_matches_sequential_and_oracle(need_gpu, select_streams):
     import torch
 
     from top_sparse_attention_02_amd import workload
 
     p = enforce_all_layers(multi_layer_problem())
     layers = workload.load_layers(p)
-    loop = workload.LayerLoop(layers)
-    log("[case layer loop] cold step")
+    loop = workload.LayerLoop(layers, select_streams=select_streams)
+    log(f"[case layer loop, {select_streams} select streams] cold step")
     loop.step(cold=True)
     torch.cuda.synchronize()
     loop.check()

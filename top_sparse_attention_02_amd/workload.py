@@ -228,25 +228,32 @@ def load_layers(problem, log=None, threads: Optional[int] = None, host_flags: in
 
 
 class LayerLoop:
-    """A multi-layer decode step on three streams ordered only by device flags.
+    """A multi-layer decode step on streams ordered only by device flags.
 
     select: reuse test, scoring and top-k of layer l, then flag sel[l] = epoch;
+            with select_streams > 1 the layers alternate between that many
+            streams (slower on MI355X: at B=1, N=524288 two streams gave 38.9
+            against 46.6 steps/s and at B=8, N=262144 10.3 against 12.2, the
+            concurrent scorings and top-k passes slowing each other and the
+            gather more than the overlap gains);
     gather: waits for sel[l], reads layer l's selected rows from host memory,
             then flag gat[l] = epoch;
     attend: waits for gat[l], attention of layer l, then flag att[l] = epoch.
-    The select stream of the next step waits for att[l] of this step before
-    overwriting layer l's selections.  Selection and gathering of layer l+1
-    therefore run while layer l is attended (one-layer-ahead prefetch and
-    beyond); the host never waits inside a step.
+    The selection of layer l in the next step waits for att[l] of this step
+    before overwriting layer l's selections.  Selection and gathering of layer
+    l+1 therefore run while layer l is attended (one-layer-ahead prefetch and
+    beyond); the host never waits inside a step.  Every layer has its own
+    workspace, selections and cache, so selections on different streams share
+    only read-only inputs.
     """
 
-    def __init__(self, layers, spin_limit: int = 0):
+    def __init__(self, layers, spin_limit: int = 0, select_streams: int = 1):
         self.layers = layers
         L = len(layers)
         dev = layers[0].q.device
         self.flags = torch.zeros(3, L, dtype=torch.int32, device=dev)
         self.error = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.s_select = torch.cuda.Stream(device=dev)
+        self.s_selects = [torch.cuda.Stream(device=dev) for _ in range(max(1, select_streams))]
         self.s_gather = torch.cuda.Stream(device=dev)
         self.s_attend = torch.cuda.Stream(device=dev)
         self.epoch = 0
@@ -259,7 +266,7 @@ class LayerLoop:
         """Enqueue one decode step over all layers (cold: every unit misses)."""
         # the loop's streams start after work already queued on the current stream
         cur = torch.cuda.current_stream()
-        for st in (self.s_select, self.s_gather, self.s_attend):
+        for st in (*self.s_selects, self.s_gather, self.s_attend):
             st.wait_stream(cur)
         self.epoch += 1
         e = self.epoch
@@ -270,9 +277,10 @@ class LayerLoop:
             shape, layer = b.shape_with(tau), b.layer()
             after_prev = clo.Sync(wait_flag=self._flag(2, l), wait_value=e - 1, error_word=self.error,
                                   spin_limit=sp) if e > 1 else None
-            clo.clo_reuse_test(shape, q, b.q_prev, b.reuse, b.cos, sync=after_prev, stream=self.s_select)
+            s_sel = self.s_selects[l % len(self.s_selects)]
+            clo.clo_reuse_test(shape, q, b.q_prev, b.reuse, b.cos, sync=after_prev, stream=s_sel)
             clo.clo_topk_select(shape, layer, q, b.reuse, b.ws,
-                                sync=clo.Sync(signal_flag=self._flag(0, l), signal_value=e), stream=self.s_select)
+                                sync=clo.Sync(signal_flag=self._flag(0, l), signal_value=e), stream=s_sel)
             clo.clo_gather_kv(shape, layer, b.reuse, b.ws,
                               sync=clo.Sync(wait_flag=self._flag(0, l), wait_value=e, signal_flag=self._flag(1, l),
                                             signal_value=e, error_word=self.error, spin_limit=sp),
