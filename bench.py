@@ -138,7 +138,7 @@ def profiled_traffic(kernel: str, cfg: int):
     return None
 
 
-def score_roofline(score_gbs: float, alg: dict, args, multi: bool) -> dict:
+def score_roofline(score_gbs: float, alg: dict, args, multi: bool, hbm_probe=None) -> dict:
     """The scoring pass against HBM peak: live, as the whole clo_topk_select call
     (compaction, scoring and top-k, timed with events), and, where a committed
     kernel-trace record for this workload and source exists, the scoring kernel
@@ -151,7 +151,38 @@ def score_roofline(score_gbs: float, alg: dict, args, multi: bool) -> dict:
         out["kernel_only"] = {"kernel": "score_mfma_kernel", "achieved": round(gbs, 1),
                               "frac": round(gbs / HBM_PEAK_GBS, 4), "mean_us": rec["mean_us"],
                               "traffic": rec["traffic_bytes_per_launch"], "source": rec["path"]}
+        if hbm_probe:
+            out["kernel_only"]["frac_measured"] = round(gbs / hbm_probe["read_gbs"], 4)
+    if hbm_probe:
+        out["peak_measured"] = round(hbm_probe["read_gbs"], 1)
+        out["frac_measured"] = round(score_gbs / hbm_probe["read_gbs"], 4)
     return out
+
+
+def probe_hbm_read(torch, nbytes=4 << 30):
+    """Measured HBM read ceiling: a plain streaming read (16-byte loads, nothing
+    computed, almost nothing written) over a 4 GiB buffer, far larger than the
+    256 MB MALL; best of a few grid sizes."""
+    from top_sparse_attention_02_amd import clo
+
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = (0.0, 0)
+    for blocks in (512, 1024, 2048, 4096):
+        times = []
+        for i in range(4):
+            e0.record()
+            clo.clo_stream_read(buf, nbytes, blocks, sink)
+            e1.record()
+            e1.synchronize()
+            if i:
+                times.append(e0.elapsed_time(e1) / 1e3)
+        gbs = nbytes / min(times) / 1e9
+        if gbs > best[0]:
+            best = (gbs, blocks)
+    del buf, sink
+    return {"read_gbs": best[0], "blocks": best[1], "bytes": nbytes}
 
 
 def probe_host_link(torch, nbytes=1 << 30):
@@ -522,6 +553,11 @@ def main():
         log(f"host link: memcpy {probe['memcpy_h2d_gbs']:.1f} GB/s, zero-copy stream "
             f"{probe['zero_copy_stream_gbs']:.1f} GB/s")
 
+    hbm_probe = None
+    if not args.no_probe:
+        hbm_probe = probe_hbm_read(torch)
+        log(f"HBM read ceiling: {hbm_probe['read_gbs']:.0f} GB/s ({hbm_probe['blocks']} blocks)")
+
     if args.calibrate_copy:
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -597,6 +633,9 @@ def main():
         roofline = {"bound": "hbm", "kernel": "attn_partial_kernel", "achieved": round(attn_gbs, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                     "traffic": None}
+        if hbm_probe:
+            roofline["peak_measured"] = round(hbm_probe["read_gbs"], 1)
+            roofline["frac_measured"] = round(attn_gbs / hbm_probe["read_gbs"], 4)
 
     result = {
         "metric": METRIC,
@@ -628,13 +667,16 @@ def main():
         "host_kv": args.host_kv,
         "host_kv_vs_native": quant,
         "volatile_frac": args.volatile,
-        "roofline_score": score_roofline(score_gbs, alg, args, multi),
+        "roofline_score": score_roofline(score_gbs, alg, args, multi, hbm_probe),
         "attention_hbm_gbs": round(attn_gbs, 1),
+        "attention_frac_measured": round(attn_gbs / hbm_probe["read_gbs"], 4) if hbm_probe else None,
         "step_hbm_gbs": round(alg["hbm_bytes"] / step_s / 1e9, 1),
         "step_host_gbs": round(alg["host_bytes"] / step_s / 1e9, 2),
         "phases_ms": {k: round(v, 4) for k, v in phases.items()},
         "units": {k: alg[k] for k in ("misses", "misses_persistent", "misses_host", "hits")},
         "host_link_probe": {k: round(v, 2) for k, v in probe.items()} if probe else None,
+        "hbm_read_probe": ({"read_gbs": round(hbm_probe["read_gbs"], 1), "blocks": hbm_probe["blocks"],
+                            "bytes": hbm_probe["bytes"]} if hbm_probe else None),
         "wall_s": round(wall, 3),
     }
     if multi:

@@ -186,6 +186,19 @@ clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const
                            void* stream);
 
 /*
+ * A1 + A2 + A3 in one call -- clo_reuse_test followed by clo_topk_select(reuse),
+ * with the same arguments, outputs and errors as the two calls (reuse and cos
+ * written for every unit, idx for the miss units).  For pipelines that gather
+ * and attend on other streams (one-layer-ahead prefetch, synthesis 5.6): on
+ * layers of at most 64 units (batch x KV heads) the reuse test, the unit lists
+ * and the wait on sync->wait_flag take one launch instead of three.  sync may be NULL (its
+ * wait precedes the reuse test, its signal follows the top-k).
+ */
+clo_status clo_reuse_select(const clo_shape* shape, const clo_layer* layer, const void* q,
+                            const void* q_prev, uint8_t* reuse, float* cos, void* ws, size_t ws_bytes,
+                            const clo_sync* sync, void* stream);
+
+/*
  * A4 -- gather (abstract features (2) and (3); synthesis 2.1 item 3).
  * For every miss unit of a non-persistent head: k_cache[u][i] = k_host[u][idx[u][i]]
  * and v_cache[u][i] = v_host[u][idx[u][i]], read by the GPU directly from pinned
@@ -286,6 +299,16 @@ clo_status clo_plan_persistent(const float* s_hat, int32_t n_layers, int32_t n_k
  */
 clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int64_t dst_stride,
                              int8_t* dst_exp, const clo_sync* sync, void* stream);
+
+/*
+ * Measurement helper (no step of the method): reads `bytes` (a multiple of 16)
+ * of device memory at src (16-byte aligned) with `blocks` blocks of 256
+ * threads, 16-byte loads, and leaves *sink (device, 4 bytes) unchanged except
+ * with probability 2^-32.  Timed around its launch it gives the HBM read
+ * ceiling against which the HBM-bound kernels (scoring, attention) are
+ * reported, as the pinned->device copy gives the host link's.
+ */
+clo_status clo_stream_read(const void* src, size_t bytes, int32_t blocks, uint32_t* sink, void* stream);
 
 /* Static text for a status code. */
 const char* clo_status_string(clo_status status);

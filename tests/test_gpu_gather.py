@@ -1,0 +1,75 @@
+"""GPU: the standalone gather (clo_gather_kv) on layers of few and of many units.
+
+The gather is a bitwise copy, k_cache[u][i] = k_host[u][idx[u][i]] (and the same
+for V), for every miss unit of an offloaded head; persistent heads and reuse
+units are left alone.  Without a unit list the kernel lists the units it serves
+in LDS up to 2048 units and skips unit by unit beyond that, so both sides of
+that bound are run, each twice in a row on one workspace: once with the work
+counter reset by a launch of its own (no sync) and once by the wait kernel of
+a sync whose flag is already set.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def _gather_case(batch, hkv, persistent_heads, context, topk, seed):
+    import torch
+
+    from top_sparse_attention_02_amd import clo
+    from top_sparse_attention_02_amd.hip_host import HostBuffer
+
+    rng = np.random.default_rng(seed)
+    pmask = sum(1 << h for h in persistent_heads)
+    off_heads = [h for h in range(hkv) if h not in persistent_heads]
+    H = len(off_heads)
+    shape = clo.Shape(batch, hkv, hkv, context, topk, 0.8, clo.CLO_BF16)
+    k_host = HostBuffer(batch * H * context * D * 2)
+    v_host = HostBuffer(batch * H * context * D * 2)
+    kh = k_host.numpy("u2", (batch, H, context, D))
+    vh = v_host.numpy("u2", (batch, H, context, D))
+    kh[:] = rng.integers(0, 1 << 16, size=kh.shape, dtype=np.uint16)
+    vh[:] = rng.integers(0, 1 << 16, size=vh.shape, dtype=np.uint16)
+    idx = np.stack([np.sort(rng.choice(context, size=topk, replace=False)) for _ in range(batch * hkv)])
+    idx = idx.reshape(batch, hkv, topk).astype(np.int32)
+    idx_d = torch.from_numpy(idx).cuda()
+    sentinel = 0x7F7F
+    k_cache = torch.full((batch, H, topk, D), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    v_cache = torch.full((batch, H, topk, D), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    layer = clo.Layer(pmask, None, None, k_host.ptr, v_host.ptr, None, k_cache, v_cache, idx_d)
+    ws = torch.empty(clo.clo_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    flag = torch.ones(1, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    expect_k = np.full((batch, H, topk, D), sentinel, dtype=np.uint16)
+    expect_v = expect_k.copy()
+    for call in range(2):
+        reuse = (rng.random((batch, hkv)) < 0.5).astype(np.uint8)
+        reuse_d = torch.from_numpy(reuse).cuda()
+        sync = None if call == 0 else clo.Sync(wait_flag=flag, wait_value=1, error_word=err)
+        clo.clo_gather_kv(shape, layer, reuse_d, ws, sync=sync)
+        torch.cuda.synchronize()
+        for b in range(batch):
+            for s, h in enumerate(off_heads):
+                if not reuse[b, h]:
+                    expect_k[b, s] = kh[b, s, idx[b, h]]
+                    expect_v[b, s] = vh[b, s, idx[b, h]]
+        got_k = k_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+        got_v = v_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got_k, expect_k), f"K cache rows differ after call {call}"
+        assert np.array_equal(got_v, expect_v), f"V cache rows differ after call {call}"
+        assert int(err.item()) == 0
+    k_host.close()
+    v_host.close()
+
+
+@pytest.mark.parametrize("batch,hkv,persistent,context,topk", [
+    (3, 8, [1, 6], 700, 300),     # 24 units: listed in LDS; 2 items per unit with a ragged tail
+    (257, 8, [0, 5], 40, 7),      # 2056 units: more than the LDS list holds
+    (1, 8, [], 5000, 513),        # one sequence, every head offloaded, 3 items per unit
+])
+def test_standalone_gather_copies_selected_rows(need_gpu, batch, hkv, persistent, context, topk):
+    print(f"gather case B={batch} Hkv={hkv} persistent={persistent} N={context} k={topk}", flush=True)
+    _gather_case(batch, hkv, persistent, context, topk, seed=batch * 1000 + context)

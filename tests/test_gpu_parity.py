@@ -150,6 +150,40 @@ def test_standalone_entry_points_equal_fused_step(need_gpu):
         assert np.array_equal(fused[key], split[key]), key
 
 
+@pytest.mark.parametrize("batch,hkv,persistent", [(2, 4, [1, 0, 0, 1]), (9, 8, [0, 1, 0, 0, 0, 0, 1, 0])])
+def test_reuse_select_equals_fused_step(need_gpu, batch, hkv, persistent):
+    """clo_reuse_select (reuse test + top-k in one call; one fused launch for the reuse
+    test and unit lists up to 64 units, separate launches above) + gather + attention
+    == clo_decode_step, bit for bit; its wait on an already-set flag passes through."""
+    import torch
+
+    from top_sparse_attention_02_amd import clo, workload
+
+    p = small_problem(f"rsel{batch}", batch=batch, hq=2 * hkv, hkv=hkv, context=2100, topk=210, dtype="bf16",
+                      persistent=persistent)
+    enforce_margins(p, 0)
+    bufs = workload.load_layer(p, 0)
+    bufs.step0()
+    bufs.step1()
+    fused = snapshot(bufs)
+    bufs.step0()
+    shape = bufs.shape_with(p.tau)
+    layer = bufs.layer()
+    flag = torch.full((1,), 3, dtype=torch.int32, device="cuda")
+    sig = torch.zeros(1, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bufs.cos.fill_(-7.0)
+    clo.clo_reuse_select(shape, layer, bufs.q, bufs.q_prev, bufs.reuse, bufs.cos, bufs.ws,
+                         sync=clo.Sync(wait_flag=flag, wait_value=3, error_word=err, signal_flag=sig,
+                                       signal_value=5))
+    clo.clo_gather_kv(shape, layer, bufs.reuse, bufs.ws)
+    clo.clo_sparse_attn(shape, layer, bufs.q, bufs.out, bufs.ws)
+    split = snapshot(bufs)
+    assert int(err.item()) == 0 and int(sig.item()) == 5
+    for key in fused:
+        assert np.array_equal(fused[key], split[key]), key
+
+
 def test_zero_copy_gather_equals_hbm_gather(need_gpu):
     """The gather reads the same bytes from pinned host memory as from an HBM copy."""
     import torch

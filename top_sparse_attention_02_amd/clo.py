@@ -18,9 +18,9 @@ CLO_HOST_NATIVE, CLO_HOST_INT8 = 0, 1
 CLO_OK, CLO_E_ARG, CLO_E_UNSUPPORTED, CLO_E_WORKSPACE, CLO_E_HIP, CLO_E_TIMEOUT = range(6)
 
 # every function include/clo.h declares
-EXPORTS = ("clo_workspace_size", "clo_reuse_test", "clo_topk_select", "clo_gather_kv", "clo_sparse_attn",
-           "clo_decode_step", "clo_append_kv", "clo_update_reference", "clo_plan_persistent", "clo_quantize_rows",
-           "clo_status_string", "clo_last_error")
+EXPORTS = ("clo_workspace_size", "clo_reuse_test", "clo_topk_select", "clo_reuse_select", "clo_gather_kv",
+           "clo_sparse_attn", "clo_decode_step", "clo_append_kv", "clo_update_reference", "clo_plan_persistent", "clo_quantize_rows",
+           "clo_stream_read", "clo_status_string", "clo_last_error")
 
 
 class CloError(RuntimeError):
@@ -67,6 +67,8 @@ def load():
         L.clo_reuse_test.argtypes = [P(clo_shape), vp, vp, vp, vp, P(clo_sync), vp]
         L.clo_topk_select.restype = st
         L.clo_topk_select.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, sz, P(clo_sync), vp]
+        L.clo_reuse_select.restype = st
+        L.clo_reuse_select.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, vp, vp, sz, P(clo_sync), vp]
         L.clo_gather_kv.restype = st
         L.clo_gather_kv.argtypes = [P(clo_shape), P(clo_layer), vp, vp, sz, P(clo_sync), vp]
         L.clo_sparse_attn.restype = st
@@ -79,6 +81,8 @@ def load():
         L.clo_update_reference.argtypes = [P(clo_shape), vp, vp, vp, P(clo_sync), vp]
         L.clo_quantize_rows.restype = st
         L.clo_quantize_rows.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int64, vp, P(clo_sync), vp]
+        L.clo_stream_read.restype = st
+        L.clo_stream_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int32, vp, vp]
         L.clo_plan_persistent.restype = st
         L.clo_plan_persistent.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
         L.clo_status_string.restype = ctypes.c_char_p
@@ -219,6 +223,13 @@ def clo_topk_select(shape: Shape, layer: Layer, q, reuse, ws, sync: Optional[Syn
                                   nbytes(ws, ws_bytes), _sync(sync), stream_handle(stream)), "clo_topk_select")
 
 
+def clo_reuse_select(shape: Shape, layer: Layer, q, q_prev, reuse, cos, ws, sync: Optional[Sync] = None,
+                     stream=None, ws_bytes: Optional[int] = None):
+    _check(load().clo_reuse_select(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(q), ptr(q_prev), ptr(reuse),
+                                   ptr(cos), ptr(ws), nbytes(ws, ws_bytes), _sync(sync), stream_handle(stream)),
+           "clo_reuse_select")
+
+
 def clo_gather_kv(shape: Shape, layer: Layer, reuse, ws, sync: Optional[Sync] = None, stream=None,
                   ws_bytes: Optional[int] = None):
     _check(load().clo_gather_kv(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(reuse), ptr(ws),
@@ -254,6 +265,12 @@ def clo_quantize_rows(src, n_rows: int, dtype: int, dst, dst_exp, dst_stride: in
                       stream=None):
     _check(load().clo_quantize_rows(ptr(src), int(n_rows), int(dtype), ptr(dst), int(dst_stride), ptr(dst_exp),
                                     _sync(sync), stream_handle(stream)), "clo_quantize_rows")
+
+
+def clo_stream_read(src, nbytes_: int, blocks: int, sink, stream=None):
+    """Measurement helper: stream-read nbytes_ of device memory (HBM read ceiling)."""
+    _check(load().clo_stream_read(ptr(src), int(nbytes_), int(blocks), ptr(sink), stream_handle(stream)),
+           "clo_stream_read")
 
 
 def clo_plan_persistent(s_hat, n_persist: int):

@@ -387,10 +387,13 @@ clo_status hip_status(hipError_t e, const char* what) {
   return fail(CLO_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-clo_status pre_wait(const clo_sync* sy, hipStream_t s) {
-  if (!sy || !sy->wait_flag) return CLO_OK;
+// zero_word (may be NULL): a work counter the next kernel needs at zero; it is
+// cleared by the wait kernel, or by a launch of its own when there is no wait
+clo_status pre_wait(const clo_sync* sy, hipStream_t s, uint32_t* zero_word = nullptr) {
+  if (!sy || !sy->wait_flag)
+    return zero_word ? hip_status(launch_zero(zero_word, s), "counter reset launch") : CLO_OK;
   const uint32_t limit = sy->spin_limit ? sy->spin_limit : (1u << 22);
-  return hip_status(launch_wait(sy->wait_flag, sy->wait_value, limit, sy->error_word, s), "wait launch");
+  return hip_status(launch_wait(sy->wait_flag, sy->wait_value, limit, sy->error_word, zero_word, s), "wait launch");
 }
 
 clo_status post_signal(const clo_sync* sy, hipStream_t s) {
@@ -452,6 +455,44 @@ clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const
   return post_signal(sync, s);
 }
 
+clo_status clo_reuse_select(const clo_shape* shape, const clo_layer* layer, const void* q, const void* q_prev,
+                            uint8_t* reuse, float* cos, void* ws, size_t ws_bytes, const clo_sync* sync,
+                            void* stream) {
+  Plan p;
+  clo_status st;
+  if ((st = make_plan(shape, layer ? layer->persistent_mask : 0, &p))) return st;
+  if ((st = check_sync_flags(sync))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.U == 0) {
+    if ((st = pre_wait(sync, s))) return st;
+    return post_signal(sync, s);
+  }
+  Workspace w;
+  if ((st = check_layer(layer, &p, NEED_IDX | NEED_SCORE | NEED_HBM_K))) return st;
+  if ((st = check_device(q, q_bytes(p), "q"))) return st;
+  if ((st = check_device(q_prev, q_bytes(p), "q_prev"))) return st;
+  if ((st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
+  if (cos && (st = check_device(cos, (size_t)p.U * 4, "cos"))) return st;
+  if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
+  const int cu = num_cus();
+  if (p.U <= kFusedReuseUnits) {
+    const bool wait = sync && sync->wait_flag;
+    const uint32_t limit = wait && sync->spin_limit ? sync->spin_limit : (1u << 22);
+    if ((st = hip_status(launch_reuse_compact(p.a, q, q_prev, reuse, cos, w, wait ? sync->wait_flag : nullptr,
+                                              wait ? sync->wait_value : 0u, limit,
+                                              wait ? sync->error_word : nullptr, s),
+                         "reuse test launch")))
+      return st;
+  } else {
+    if ((st = pre_wait(sync, s))) return st;
+    if ((st = hip_status(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch"))) return st;
+    if ((st = hip_status(launch_compact(p.a, reuse, w, 1, one_range(p), s), "compact launch"))) return st;
+  }
+  if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w, score_counter(w, 0), cu, s), "score launch"))) return st;
+  if ((st = hip_status(launch_select(p.a, span_all_misses(w), p.U, w, s), "top-k launch"))) return st;
+  return post_signal(sync, s);
+}
+
 clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const uint8_t* reuse, void* ws,
                          size_t ws_bytes, const clo_sync* sync, void* stream) {
   Plan p;
@@ -468,8 +509,7 @@ clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const u
   if (reuse && (st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
   uint32_t* counter = reinterpret_cast<uint32_t*>(w.meta + kMetaGather);
-  if ((st = pre_wait(sync, s))) return st;
-  if ((st = hip_status(launch_zero(counter, s), "gather counter launch"))) return st;
+  if ((st = pre_wait(sync, s, counter))) return st;
   if ((st = hip_status(launch_gather(p.a, reuse, kAllUnits, p.U,
                                      p.U >= kGatherWideUnits ? kGatherBlocksAloneWide : kGatherBlocksAlone,
                                      counter, s), "gather launch")))
@@ -506,8 +546,14 @@ clo_status step_in_order(const Plan& p, const Workspace& w, const void* q, const
                          uint8_t* reuse, float* cos, hipStream_t s) {
   clo_status st;
   const int cu = num_cus();
-  if ((st = hip_status(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch"))) return st;
-  if ((st = hip_status(launch_compact(p.a, reuse, w, 1, one_range(p), s), "compact launch"))) return st;
+  if (p.U <= kFusedReuseUnits) {
+    if ((st = hip_status(launch_reuse_compact(p.a, q, q_prev, reuse, cos, w, nullptr, 0u, 0u, nullptr, s),
+                         "reuse test launch")))
+      return st;
+  } else {
+    if ((st = hip_status(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch"))) return st;
+    if ((st = hip_status(launch_compact(p.a, reuse, w, 1, one_range(p), s), "compact launch"))) return st;
+  }
   if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w, score_counter(w, 0), cu, s), "score launch"))) return st;
   if ((st = hip_status(launch_select(p.a, span_all_misses(w), p.U, w, s), "top-k launch"))) return st;
   if ((st = hip_status(launch_attn_partial(p.a, q, w.part, kAllUnits, p.U, s), "attention launch"))) return st;
@@ -667,6 +713,17 @@ clo_status clo_plan_persistent(const float* s_hat, int32_t n_layers, int32_t n_k
     masks[slot / n_kv_heads] |= 1ull << (slot % n_kv_heads);
   }
   return ok();
+}
+
+clo_status clo_stream_read(const void* src, size_t bytes, int32_t blocks, uint32_t* sink, void* stream) {
+  if (bytes % 16) return fail(CLO_E_ARG, "bytes %zu is not a multiple of 16", bytes);
+  if (blocks < 1 || blocks > (1 << 20)) return fail(CLO_E_ARG, "blocks %d is not in [1, 2^20]", (int)blocks);
+  if (bytes == 0) return ok();
+  clo_status st;
+  if ((st = check_device(src, bytes, "src"))) return st;
+  if ((st = check_device(sink, 4, "sink", 4))) return st;
+  return hip_status(launch_stream_read(src, (int64_t)(bytes / 16), blocks, sink, static_cast<hipStream_t>(stream)),
+                    "stream read launch");
 }
 
 clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int64_t dst_stride,

@@ -71,6 +71,10 @@ constexpr int kQuantMinExp = -120;  // smallest row exponent of the int8 host fo
 // Unit ranges of one decode step: units are split into R contiguous ranges
 // [first[r], first[r + 1]) so that the gather of one range can run while the
 // next range is scored.
+// Layers of at most this many units take the reuse test and the unit lists in
+// one single-block launch (16 waves, at most 4 units each; wider layers keep a
+// wave per unit in a launch of its own).
+constexpr int kFusedReuseUnits = 64;
 constexpr int kMaxRanges = 16;
 struct RangeBounds {
   int32_t first[kMaxRanges + 1];  // first unit of each range; first[R] = U
@@ -134,6 +138,11 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // Launchers: enqueue on `s`; return the HIP error of the launch.
 hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, uint8_t* reuse, float* cos,
                         hipStream_t s);
+// Reuse test + unit lists (one range) in one block, after an optional wait on
+// a device flag; layers of at most kFusedReuseUnits units.
+hipError_t launch_reuse_compact(const LayerArgs& a, const void* q, const void* q_prev, uint8_t* reuse, float* cos,
+                                const Workspace& w, const uint32_t* wait_flag, uint32_t wait_value, uint32_t limit,
+                                uint32_t* error_word, hipStream_t s);
 // max_units: an upper bound on the span's length, used to size the grid.
 hipError_t launch_compact(const LayerArgs& a, const uint8_t* reuse, const Workspace& w, int ranges,
                           const RangeBounds& bounds, hipStream_t s);
@@ -153,6 +162,7 @@ hipError_t launch_select(const LayerArgs& a, Span sp, int64_t max_units, const W
 hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, Span sp, int64_t max_units, int max_blocks,
                          uint32_t* counter, hipStream_t s);
 hipError_t launch_zero(uint32_t* word, hipStream_t s);
+hipError_t launch_stream_read(const void* src, int64_t n16, int blocks, uint32_t* sink, hipStream_t s);
 hipError_t launch_attn_partial(const LayerArgs& a, const void* q, float* part, Span sp, int64_t max_units,
                                hipStream_t s);
 // Output rows of the span's units (all units when sp.list == nullptr).
@@ -165,7 +175,7 @@ hipError_t launch_update_reference(const LayerArgs& a, const void* q, const uint
 hipError_t launch_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int64_t stride,
                                 int8_t* dst_exp, hipStream_t s);
 hipError_t launch_wait(const uint32_t* flag, uint32_t value, uint32_t spin_limit, uint32_t* error_word,
-                       hipStream_t s);
+                       uint32_t* zero_word, hipStream_t s);
 hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s);
 
 }  // namespace clo

@@ -123,16 +123,17 @@ struct HeadTau {
   float t[kMaxKvHeads];
 };
 
+// Cosine of unit u's concatenated query group against the previous step's,
+// by one wave (fp32 dot and norms); valid in every lane.
 template <typename T>
-__global__ __launch_bounds__(64) void reuse_kernel(const T* __restrict__ q, const T* __restrict__ qp,
-                                                   uint8_t* __restrict__ reuse, float* __restrict__ cosv,
-                                                   int Hkv, int Hq, int G, HeadTau tau) {
-  const int u = blockIdx.x;
+__device__ __forceinline__ float group_cosine(const T* __restrict__ q, const T* __restrict__ qp, int u, int Hkv,
+                                              int Hq, int G) {
+  const int lane = threadIdx.x & 63;
   const int b = u / Hkv, h = u % Hkv;
   const int64_t off = ((int64_t)b * Hq + (int64_t)h * G) * kHeadDim;  // the group is contiguous
   const int n8 = G * kHeadDim / 8;
   float dot = 0.f, na = 0.f, nb = 0.f;
-  for (int i = threadIdx.x; i < n8; i += 64) {
+  for (int i = lane; i < n8; i += 64) {
     float x[8], y[8];
     load8(q + off + i * 8, x);
     load8(qp + off + i * 8, y);
@@ -146,10 +147,18 @@ __global__ __launch_bounds__(64) void reuse_kernel(const T* __restrict__ q, cons
   dot = wave_sum(dot);
   na = wave_sum(na);
   nb = wave_sum(nb);
+  return (na == 0.f || nb == 0.f) ? 0.f : dot / (sqrtf(na) * sqrtf(nb));
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void reuse_kernel(const T* __restrict__ q, const T* __restrict__ qp,
+                                                   uint8_t* __restrict__ reuse, float* __restrict__ cosv,
+                                                   int Hkv, int Hq, int G, HeadTau tau) {
+  const int u = blockIdx.x;
+  const float c = group_cosine(q, qp, u, Hkv, Hq, G);
   if (threadIdx.x == 0) {
-    const float c = (na == 0.f || nb == 0.f) ? 0.f : dot / (sqrtf(na) * sqrtf(nb));
     if (cosv) cosv[u] = c;
-    reuse[u] = (c >= tau.t[h]) ? 1 : 0;
+    reuse[u] = (c >= tau.t[u % Hkv]) ? 1 : 0;
   }
 }
 
@@ -157,13 +166,11 @@ __global__ __launch_bounds__(64) void reuse_kernel(const T* __restrict__ q, cons
 // One block scans the reuse flags in unit order into three ascending lists
 // (miss units, miss units of non-persistent heads, reuse units) and the first
 // list position of each of the R unit ranges; nothing is read back by the host.
-__global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict__ reuse, int U, int Hkv,
-                                                       uint64_t pmask, int R, RangeBounds rb,
-                                                       int32_t* __restrict__ meta,
-                                                       int32_t* __restrict__ list_all,
-                                                       int32_t* __restrict__ list_host,
-                                                       int32_t* __restrict__ list_hit, uint32_t* __restrict__ h0,
-                                                       uint32_t* __restrict__ h0b) {
+template <typename MissF>
+__device__ void compact_units(MissF is_miss, int U, int Hkv, uint64_t pmask, int R, const RangeBounds& rb,
+                              int32_t* __restrict__ meta, int32_t* __restrict__ list_all,
+                              int32_t* __restrict__ list_host, int32_t* __restrict__ list_hit,
+                              uint32_t* __restrict__ h0, uint32_t* __restrict__ h0b) {
   __shared__ int wsum[3][16];
   __shared__ int base[3];
   __shared__ int rcount[2][kMaxRanges];
@@ -174,7 +181,7 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
   for (int t0 = 0; t0 < U; t0 += 1024) {
     const int u = t0 + tid;
     const bool valid = u < U;
-    const bool miss = valid && (reuse == nullptr || reuse[u] == 0);
+    const bool miss = valid && is_miss(u);
     const bool host = miss && !((pmask >> (u % Hkv)) & 1ull);
     const bool hit = valid && !miss;
     if (miss) {
@@ -239,6 +246,66 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
     meta[kMetaOffAll + R] = oa;
     meta[kMetaOffHost + R] = oh;
   }
+}
+
+
+__global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict__ reuse, int U, int Hkv,
+                                                       uint64_t pmask, int R, RangeBounds rb,
+                                                       int32_t* __restrict__ meta,
+                                                       int32_t* __restrict__ list_all,
+                                                       int32_t* __restrict__ list_host,
+                                                       int32_t* __restrict__ list_hit, uint32_t* __restrict__ h0,
+                                                       uint32_t* __restrict__ h0b) {
+  compact_units([&](int u) { return reuse == nullptr || reuse[u] == 0; }, U, Hkv, pmask, R, rb, meta, list_all,
+                list_host, list_hit, h0, h0b);
+}
+
+// Reuse test and unit lists of a layer of at most kFusedReuseUnits units in one
+// block: after an optional bounded wait on a device flag (as wait_kernel), the
+// 16 waves compute the units' cosines, keep the decisions in LDS and compact
+// them.  Three launches of a few microseconds each become one, which matters
+// on a select stream whose every launch waits behind other streams' memory
+// traffic.
+template <typename T>
+__global__ __launch_bounds__(1024) void reuse_compact_kernel(const T* __restrict__ q, const T* __restrict__ qp,
+                                                             uint8_t* __restrict__ reuse, float* __restrict__ cosv,
+                                                             int Hkv, int Hq, int G, HeadTau tau, int U,
+                                                             uint64_t pmask, int32_t* __restrict__ meta,
+                                                             int32_t* __restrict__ list_all,
+                                                             int32_t* __restrict__ list_host,
+                                                             int32_t* __restrict__ list_hit,
+                                                             uint32_t* __restrict__ h0, uint32_t* __restrict__ h0b,
+                                                             const uint32_t* wait_flag, uint32_t wait_value,
+                                                             uint32_t limit, uint32_t* error_word) {
+  __shared__ uint8_t s_reuse[kFusedReuseUnits];
+  static_assert(kFusedReuseUnits <= 1024, "one unit per thread in the compaction");
+  if (wait_flag && threadIdx.x == 0) {
+    uint32_t n = 0;
+    while (__hip_atomic_load(wait_flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < wait_value) {
+      if (++n >= limit) {
+        if (error_word)
+          __hip_atomic_store(error_word, (uint32_t)CLO_E_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int u = wave; u < U; u += 16) {
+    const float c = group_cosine(q, qp, u, Hkv, Hq, G);
+    if (lane == 0) {
+      const uint8_t r = (c >= tau.t[u % Hkv]) ? 1 : 0;
+      if (cosv) cosv[u] = c;
+      reuse[u] = r;
+      s_reuse[u] = r;
+    }
+  }
+  __syncthreads();
+  RangeBounds rb{};
+  rb.first[1] = U;
+  compact_units([&](int u) { return s_reuse[u] == 0; }, U, Hkv, pmask, 1, rb, meta, list_all, list_host, list_hit,
+                h0, h0b);
 }
 
 // ---------------------------------------------------------------- A2 scoring
@@ -999,6 +1066,33 @@ __global__ __launch_bounds__(256) void expand_blocks_kernel(LayerArgs a, Span sp
 }
 
 // ---------------------------------------------------------------- A4 gather
+// Without a unit list (the standalone gather) every block first lists the units
+// it serves -- offloaded heads that miss, ascending -- in LDS, so that the work
+// counter runs over their items only instead of handing out (and skipping) the
+// items of reuse and persistent units one claim at a time.  Layers of more than
+// kGatherListCap units keep the skipping scheme.
+constexpr int kGatherListCap = 2048;
+
+__device__ __forceinline__ int list_gather_units(const LayerArgs& a, const uint8_t* __restrict__ reuse, int U,
+                                                 int32_t* s_units, uint32_t* s_wcnt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int total = 0;
+  for (int base = 0; base < U; base += 256) {
+    const int u = base + (int)threadIdx.x;
+    bool f = false;
+    if (u < U) f = !((a.pmask >> (u % a.Hkv)) & 1ull) && !(reuse && reuse[u]);
+    const uint64_t m = __ballot(f);
+    if (lane == 0) s_wcnt[wave] = (uint32_t)__popcll(m);
+    __syncthreads();
+    int off = total;
+    for (int w = 0; w < wave; ++w) off += (int)s_wcnt[w];
+    if (f) s_units[off + __popcll(m & ((1ull << lane) - 1ull))] = u;
+    total += (int)(s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3]);
+    __syncthreads();
+  }
+  return total;
+}
+
 // Rows of d elements are moved as 16-byte pieces: LPR lanes per row.  The
 // loads from pinned host memory are issued UNR rows deep per lane before any
 // store; grid x UNR sets the bytes in flight on the host link.
@@ -1012,9 +1106,14 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
   static_assert(kGatherChunk == 256, "one index per thread");
   __shared__ uint32_t s_item;
   __shared__ int32_t s_src[kGatherChunk];  // the item's source rows, clamped into [0, N)
+  __shared__ int32_t s_units[kGatherListCap];
+  __shared__ uint32_t s_wcnt[4];
   const int nch = (int)((a.k + kGatherChunk - 1) / kGatherChunk);
   const int lo = sp.list ? *sp.lo : 0;
-  const int64_t n_units = sp.list ? (int64_t)(*sp.hi - lo) : (int64_t)a.B * a.Hkv;
+  const int U = a.B * a.Hkv;
+  const bool listed = !sp.list && U <= kGatherListCap;
+  const int64_t n_units = sp.list ? (int64_t)(*sp.hi - lo)
+                                  : (listed ? (int64_t)list_gather_units(a, reuse, U, s_units, s_wcnt) : (int64_t)U);
   const int64_t items = n_units * nch;
   const int sub = threadIdx.x % LPR, rl = threadIdx.x / LPR;
   for (;;) {
@@ -1023,10 +1122,10 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
     const int64_t it = s_item;
     __syncthreads();
     if (it >= items) break;  // uniform per block
-    const int u = sp.list ? sp.list[lo + it / nch] : (int)(it / nch);
+    const int u = sp.list ? sp.list[lo + it / nch] : (listed ? s_units[it / nch] : (int)(it / nch));
     const int c = (int)(it % nch);
     const int b = u / a.Hkv, h = u % a.Hkv;
-    if (!sp.list && (((a.pmask >> h) & 1ull) || (reuse && reuse[u]))) continue;
+    if (!sp.list && !listed && (((a.pmask >> h) & 1ull) || (reuse && reuse[u]))) continue;
     const int64_t slot = (int64_t)b * a.H + head_slot(a.pmask, h);
     const char* ks = static_cast<const char*>(a.k_host) + slot * a.C * RB;
     const char* vs = static_cast<const char*>(a.v_host) + slot * a.C * RB;
@@ -1115,9 +1214,14 @@ __global__ __launch_bounds__(256) void gather_q8_kernel(LayerArgs a, const uint8
   __shared__ uint32_t s_item;
   __shared__ int32_t s_src[kGatherChunk];
   __shared__ float s_sc[2][kGatherChunk];  // 2^e of the item's K and V rows
+  __shared__ int32_t s_units[kGatherListCap];
+  __shared__ uint32_t s_wcnt[4];
   const int nch = (int)((a.k + kGatherChunk - 1) / kGatherChunk);
   const int lo = sp.list ? *sp.lo : 0;
-  const int64_t n_units = sp.list ? (int64_t)(*sp.hi - lo) : (int64_t)a.B * a.Hkv;
+  const int U = a.B * a.Hkv;
+  const bool listed = !sp.list && U <= kGatherListCap;
+  const int64_t n_units = sp.list ? (int64_t)(*sp.hi - lo)
+                                  : (listed ? (int64_t)list_gather_units(a, reuse, U, s_units, s_wcnt) : (int64_t)U);
   const int64_t items = n_units * nch;
   const int sub = threadIdx.x % LPR, rl = threadIdx.x / LPR;
   const int half = sub >> 3, piece = sub & 7;  // 0 = K, 1 = V; 16-value piece of the row
@@ -1127,10 +1231,10 @@ __global__ __launch_bounds__(256) void gather_q8_kernel(LayerArgs a, const uint8
     const int64_t it = s_item;
     __syncthreads();
     if (it >= items) break;  // uniform per block
-    const int u = sp.list ? sp.list[lo + it / nch] : (int)(it / nch);
+    const int u = sp.list ? sp.list[lo + it / nch] : (listed ? s_units[it / nch] : (int)(it / nch));
     const int c = (int)(it % nch);
     const int b = u / a.Hkv, h = u % a.Hkv;
-    if (!sp.list && (((a.pmask >> h) & 1ull) || (reuse && reuse[u]))) continue;
+    if (!sp.list && !listed && (((a.pmask >> h) & 1ull) || (reuse && reuse[u]))) continue;
     const int64_t slot = (int64_t)b * a.H + head_slot(a.pmask, h);
     const char* rec = static_cast<const char*>(a.k_host) + slot * a.C * kRec;
     T* dst = static_cast<T*>(half ? a.v_cache : a.k_cache) + slot * a.k * kHeadDim;
@@ -1542,8 +1646,10 @@ __global__ __launch_bounds__(64) void update_reference_kernel(const T* __restric
 }
 
 // ---------------------------------------------------------------- device-side flags
+// zero_word (may be NULL): a work counter of the kernel that follows on the
+// stream, cleared here so that the wait and the reset take one launch
 __global__ __launch_bounds__(64) void wait_kernel(const uint32_t* flag, uint32_t value, uint32_t limit,
-                                                  uint32_t* error_word) {
+                                                  uint32_t* error_word, uint32_t* zero_word) {
   if (threadIdx.x != 0) return;
   uint32_t n = 0;
   while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < value) {
@@ -1553,10 +1659,35 @@ __global__ __launch_bounds__(64) void wait_kernel(const uint32_t* flag, uint32_t
     }
     __builtin_amdgcn_s_sleep(8);
   }
+  if (zero_word) *zero_word = 0u;
 }
 
 __global__ __launch_bounds__(64) void signal_kernel(uint32_t* flag, uint32_t value) {
   if (threadIdx.x == 0) __hip_atomic_store(flag, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------- measurement
+// Streaming read of n16 16-byte words: the HBM read ceiling that the scoring
+// and attention kernels are compared with.  Each thread keeps 8 loads in
+// flight; the xor of everything read is stored only if it equals `never`, so
+// the loads cannot be dropped and almost nothing is written.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ p, int64_t n16, uint32_t never,
+                                                          uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t x = 0;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4 w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = p[i + j * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x ^= w[j][0] ^ w[j][1] ^ w[j][2] ^ w[j][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 w = p[i];
+    x ^= w[0] ^ w[1] ^ w[2] ^ w[3];
+  }
+  if (x == never) sink[0] = x;
 }
 
 template <typename F>
@@ -1589,6 +1720,28 @@ hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, u
   else
     reuse_kernel<uint16_t><<<U, 64, 0, s>>>(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(q_prev),
                                             reuse, cos, a.Hkv, a.Hq, a.G, th);
+  return hipGetLastError();
+}
+
+hipError_t launch_reuse_compact(const LayerArgs& a, const void* q, const void* q_prev, uint8_t* reuse, float* cos,
+                                const Workspace& w, const uint32_t* wait_flag, uint32_t wait_value, uint32_t limit,
+                                uint32_t* error_word, hipStream_t s) {
+  const int U = a.B * a.Hkv;
+  if (U > kFusedReuseUnits) return hipErrorInvalidValue;
+  HeadTau th;
+  for (int h = 0; h < kMaxKvHeads; ++h) th.t[h] = a.tau_h[h];
+  uint32_t* h0b = a.bs > 1 ? w.h0b : nullptr;
+  if (a.dtype == CLO_F32)
+    reuse_compact_kernel<float><<<1, 1024, 0, s>>>(static_cast<const float*>(q), static_cast<const float*>(q_prev),
+                                                   reuse, cos, a.Hkv, a.Hq, a.G, th, U, a.pmask, w.meta, w.list_all,
+                                                   w.list_host, w.list_hit, w.h0, h0b, wait_flag, wait_value, limit,
+                                                   error_word);
+  else
+    reuse_compact_kernel<uint16_t><<<1, 1024, 0, s>>>(static_cast<const uint16_t*>(q),
+                                                      static_cast<const uint16_t*>(q_prev), reuse, cos, a.Hkv, a.Hq,
+                                                      a.G, th, U, a.pmask, w.meta, w.list_all, w.list_host,
+                                                      w.list_hit, w.h0, h0b, wait_flag, wait_value, limit,
+                                                      error_word);
   return hipGetLastError();
 }
 
@@ -1691,6 +1844,11 @@ hipError_t launch_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, 
   return hipGetLastError();
 }
 
+hipError_t launch_stream_read(const void* src, int64_t n16, int blocks, uint32_t* sink, hipStream_t s) {
+  stream_read_kernel<<<blocks, 256, 0, s>>>(static_cast<const u32x4*>(src), n16, 0x9E3779B9u, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_zero(uint32_t* word, hipStream_t s) {
   zero_kernel<<<1, 64, 0, s>>>(word);
   return hipGetLastError();
@@ -1763,8 +1921,8 @@ hipError_t launch_update_reference(const LayerArgs& a, const void* q, const uint
 }
 
 hipError_t launch_wait(const uint32_t* flag, uint32_t value, uint32_t spin_limit, uint32_t* error_word,
-                       hipStream_t s) {
-  wait_kernel<<<1, 64, 0, s>>>(flag, value, spin_limit, error_word);
+                       uint32_t* zero_word, hipStream_t s) {
+  wait_kernel<<<1, 64, 0, s>>>(flag, value, spin_limit, error_word, zero_word);
   return hipGetLastError();
 }
 

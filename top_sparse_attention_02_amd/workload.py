@@ -230,7 +230,8 @@ def load_layers(problem, log=None, threads: Optional[int] = None, host_flags: in
 class LayerLoop:
     """A multi-layer decode step on streams ordered only by device flags.
 
-    select: reuse test, scoring and top-k of layer l, then flag sel[l] = epoch;
+    select: reuse test, scoring and top-k of layer l (one clo_reuse_select), then
+            flag sel[l] = epoch;
             with select_streams > 1 the layers alternate between that many
             streams (slower on MI355X: at B=1, N=524288 two streams gave 38.9
             against 46.6 steps/s and at B=8, N=262144 10.3 against 12.2, the
@@ -275,12 +276,13 @@ class LayerLoop:
             tau = math.inf if cold else b.tau
             q = b.q_prev if cold else b.q
             shape, layer = b.shape_with(tau), b.layer()
-            after_prev = clo.Sync(wait_flag=self._flag(2, l), wait_value=e - 1, error_word=self.error,
-                                  spin_limit=sp) if e > 1 else None
+            # waits for the previous step's attention of this layer, signals sel[l]
+            sel_sync = clo.Sync(signal_flag=self._flag(0, l), signal_value=e)
+            if e > 1:
+                sel_sync = clo.Sync(wait_flag=self._flag(2, l), wait_value=e - 1, error_word=self.error,
+                                    spin_limit=sp, signal_flag=self._flag(0, l), signal_value=e)
             s_sel = self.s_selects[l % len(self.s_selects)]
-            clo.clo_reuse_test(shape, q, b.q_prev, b.reuse, b.cos, sync=after_prev, stream=s_sel)
-            clo.clo_topk_select(shape, layer, q, b.reuse, b.ws,
-                                sync=clo.Sync(signal_flag=self._flag(0, l), signal_value=e), stream=s_sel)
+            clo.clo_reuse_select(shape, layer, q, b.q_prev, b.reuse, b.cos, b.ws, sync=sel_sync, stream=s_sel)
             clo.clo_gather_kv(shape, layer, b.reuse, b.ws,
                               sync=clo.Sync(wait_flag=self._flag(0, l), wait_value=e, signal_flag=self._flag(1, l),
                                             signal_value=e, error_word=self.error, spin_limit=sp),
