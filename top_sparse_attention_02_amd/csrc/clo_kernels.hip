@@ -1408,7 +1408,50 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
   const int row_base = wave * 64 + rg;
 
   // phase 1: logits
-  {
+  if constexpr (sizeof(T) == 2) {
+    // bf16: on the matrix cores, as in scoring.  Wave w takes its 64 rows as four
+    // 16-row tiles: D[head][row] = sum over 128 dims of Q[head] K[row], A = the
+    // unit's G query heads padded to 16 rows, B = 16 rows x 32 dims per k-step,
+    // each lane loading 16-byte pieces of its row straight into B registers.
+    // D leaves heads 4 (lane / 16) .. + 3 of row (lane % 16) in each lane.
+    const int col = lane & 15, ks = lane >> 4;
+    bf16x8 qa[4];
+    {
+      const uint16_t* qh = reinterpret_cast<const uint16_t*>(q) +
+                           ((int64_t)b * a.Hq + (int64_t)h * G + (col < G ? col : 0)) * kHeadDim;
+      const uint32_t keep = col < G ? ~0u : 0u;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(qh + s4 * 32 + ks * 8);
+        qa[s4] = __builtin_bit_cast(bf16x8, w & keep);
+      }
+    }
+    const T* kb16 = kbase;
+#pragma unroll
+    for (int t0 = 0; t0 < 4; t0 += 2) {
+      u32x4 kt[2][4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int i = wave * 64 + (t0 + t) * 16 + col;
+        const T* kr = kb16 + row_of(i < nrows ? i : nrows - 1) * kHeadDim + ks * 8;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) kt[t][s4] = *reinterpret_cast<const u32x4*>(kr + s4 * 32);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s4], __builtin_bit_cast(bf16x8, kt[t][s4]), acc, 0, 0, 0);
+        const int i = wave * 64 + (t0 + t) * 16 + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int g = ks * 4 + r;
+          if (g < G) lg[g][i] = (i < nrows) ? acc[r] * scale : kNegInf;
+        }
+      }
+    }
+  } else {
     float qv[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g) load8(q + ((int64_t)b * a.Hq + (int64_t)h * G + g) * kHeadDim + sub * 8, qv[g]);
