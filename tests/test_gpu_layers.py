@@ -119,6 +119,36 @@ def test_never_signalled_flag_times_out_without_hanging(need_gpu):
     assert int(err.item()) == clo.CLO_E_TIMEOUT
 
 
+def test_reuse_select_wait_times_out_without_hanging(need_gpu):
+    """The wait folded into clo_reuse_select's single-block launch is bounded too: a flag
+    that is never set (tiny spin limit) ends in CLO_E_TIMEOUT, and the selection still
+    runs, equal to the oracle's."""
+    import torch
+
+    import oracle
+    from top_sparse_attention_02_amd import clo, workload
+    from tests.gpu_common import small_problem
+
+    p = small_problem("rsel_timeout", batch=1, hq=4, hkv=2, context=600, topk=60, dtype="f32", persistent=[1, 0])
+    enforce_margins(p, 0)
+    bufs = workload.load_layer(p, 0)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sig = torch.zeros(1, dtype=torch.int32, device="cuda")
+    clo.clo_reuse_select(bufs.shape_with(math.inf), bufs.layer(), bufs.q_prev, bufs.q_prev, bufs.reuse, bufs.cos,
+                         bufs.ws, sync=clo.Sync(wait_flag=flag[0], wait_value=1, error_word=err, spin_limit=2000,
+                                                signal_flag=sig[0], signal_value=4))
+    torch.cuda.synchronize()
+    assert int(err.item()) == clo.CLO_E_TIMEOUT
+    assert int(sig.item()) == 4
+    qp = p.q_prev(0)
+    for h in range(p.hkv):
+        ref = oracle.decode_unit(qp[0, h * 2:(h + 1) * 2], qp[0, h * 2:(h + 1) * 2],
+                                 oracle.as_f64(p.kv("k", 0, 0, h), "f32"), oracle.as_f64(p.kv("v", 0, 0, h), "f32"),
+                                 p.topk, math.inf)
+        assert np.array_equal(bufs.idx[0, h].cpu().numpy(), ref["idx"])
+
+
 def test_already_signalled_flag_does_not_wait(need_gpu):
     import time
 
