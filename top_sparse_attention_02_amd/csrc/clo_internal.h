@@ -28,18 +28,21 @@ constexpr int kPartStride = kHeadDim + 2;  // floats per (chunk, head) partial: 
 //    384 KiB    56.7 GB/s      1.2-1.35x           1.3x   (24 blocks x 2 rows)
 //    128 KiB    49.4 GB/s      1.1-1.3x            1.2x
 // The overlapped single-layer step is bound by the gather alone and takes 32
-// blocks (512 KiB).  A standalone gather (one layer of the 48-layer loop, or
-// a phase of its own) takes 32 blocks, or 40 for layers of 64 units or more:
-// there the gather outweighs the selection it slows.  48-layer loop, steps/s
-// with 24 / 32 / 40 blocks:
-//   B=8, N=262144 (64 units)     native 11.7 / 12.0 / 12.3   int8 19.6 / 20.7 / 21.6
-//   B=1, N=524288 (8 units)      native 46.7 / 46.8 / 44.8   int8 76.5 / 77.9 / 73.8
-// The int8 gather alone (512 x 13108 rows) reads 52.7 / 55.2 / 56.3 GB/s: its
-// items wait on index and exponent loads before any host read, and its rows
-// carry half the host bytes.
+// blocks (512 KiB; 24 blocks: 12.40 -> 13.19 ms at B=64, N=131072).  A
+// standalone gather (one layer of the 48-layer loop, or a phase of its own)
+// takes 24 blocks, or 40 for layers of 64 units or more.  Beside the gather,
+// the select stream of the 48-layer loop is the longer one, and fewer host
+// reads in flight slow its kernels less.  ms per 48-layer step with the
+// standalone gather at 16 / 20 / 24 / 32 / 40 blocks:
+//   B=1, N=524288 (8 units)    native 19.38 / 19.20 / 19.12 / 20.46 / 21.61
+//                              int8   11.71 / 11.31 / 11.26 / 12.19 / 12.76
+// and B=8, N=262144 (64 units) 77.9 with 24, 32 or 40 blocks.
+// The int8 gather alone (512 x 13108 rows) reads 52.7 / 55.2 / 56.3 GB/s with
+// 24 / 32 / 40 blocks: its items wait on index and exponent loads before any
+// host read, and its rows carry half the host bytes.
 constexpr int kGatherUnroll = 2;
 constexpr int kGatherBlocksOverlapped = 32;
-constexpr int kGatherBlocksAlone = 32;
+constexpr int kGatherBlocksAlone = 24;
 constexpr int kGatherBlocksAloneWide = 40;  // layers of at least kGatherWideUnits units
 constexpr int kGatherWideUnits = 64;
 
