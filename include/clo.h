@@ -229,9 +229,10 @@ clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const
  *
  * When the layer has offloaded heads, the step overlaps its HBM work with the
  * host gather: units are split into ranges; `stream` scores and selects range
- * after range, a helper stream gathers each range once its top-k is done, and
- * a second helper stream attends the reuse units and then each gathered range.
- * The two helper streams (default priority, non-blocking) and their events are
+ * after range, two helper streams gather the even and the odd ranges, each
+ * once its top-k is done, and a third attends the reuse units and then each
+ * gathered range.  The helper streams (default priority, non-blocking) and
+ * their events are
  * created by the library on first use per device and kept until the process
  * ends; they hold no user data.  All ordering is done on the GPU with events;
  * the call is ordered after earlier work on `stream`, and later work on

@@ -263,7 +263,8 @@ uint32_t* score_counter(const Workspace& w, int r) { return reinterpret_cast<uin
 struct DeviceQueues {
   std::mutex mu;  // one decode step enqueues at a time per device
   bool ready = false;
-  hipStream_t gather = nullptr;  // host gathers, one unit range after another
+  hipStream_t gather = nullptr;   // host gathers of the even unit ranges
+  hipStream_t gather2 = nullptr;  // and of the odd ones
   hipStream_t attend = nullptr;  // attention: reuse units first, then each range's misses
   hipEvent_t ev_attn = nullptr;
   hipEvent_t ev_topk[kMaxRanges] = {}, ev_gather[kMaxRanges] = {};
@@ -282,6 +283,7 @@ clo_status device_queues(DeviceQueues** out) {
   std::lock_guard<std::mutex> lk(g_queues_init);
   if (!q.ready) {
     hipError_t e = hipStreamCreateWithFlags(&q.gather, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&q.gather2, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&q.attend, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&q.ev_attn, hipEventDisableTiming);
     for (int r = 0; r < kMaxRanges && e == hipSuccess; ++r) {
@@ -594,11 +596,15 @@ clo_status step_overlapped(const Plan& p, const Workspace& w, const void* q, con
     CLO_TRY(launch_score(p.a, q, span_range(w, r), per, w, score_counter(w, r), cu, s), "score launch");
     CLO_TRY(launch_select(p.a, span_range(w, r), per, w, s), "top-k launch");
     CLO_TRY(hipEventRecord(dq->ev_topk[r], s), "event record");
-    CLO_TRY(hipStreamWaitEvent(gs, dq->ev_topk[r], 0), "stream wait");
+    // ranges alternate between two gather streams, so that one range's host
+    // reads start while the previous range's last items finish instead of
+    // after a launch gap (~12 us each)
+    hipStream_t gsr = (r & 1) ? dq->gather2 : gs;
+    CLO_TRY(hipStreamWaitEvent(gsr, dq->ev_topk[r], 0), "stream wait");
     CLO_TRY(launch_gather(p.a, reuse, span_host_range(w, r), per, kGatherBlocksOverlapped,
-                          reinterpret_cast<uint32_t*>(w.meta + kMetaGather + r), gs),
+                          reinterpret_cast<uint32_t*>(w.meta + kMetaGather + r), gsr),
             "gather launch");
-    CLO_TRY(hipEventRecord(dq->ev_gather[r], gs), "event record");
+    CLO_TRY(hipEventRecord(dq->ev_gather[r], gsr), "event record");
   }
   // reuse units need no new rows; they are attended once the first range is
   // selected, so that their many short blocks do not delay the first top-k
