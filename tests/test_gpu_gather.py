@@ -73,3 +73,24 @@ def _gather_case(batch, hkv, persistent_heads, context, topk, seed):
 def test_standalone_gather_copies_selected_rows(need_gpu, batch, hkv, persistent, context, topk):
     print(f"gather case B={batch} Hkv={hkv} persistent={persistent} N={context} k={topk}", flush=True)
     _gather_case(batch, hkv, persistent, context, topk, seed=batch * 1000 + context)
+
+
+def test_stream_read_probe_reads_without_writing(need_gpu):
+    """clo_stream_read (the HBM read-ceiling probe) runs over a buffer and leaves the sink
+    alone unless the xor of everything read equals its sentinel; argument errors are
+    rejected on the host."""
+    import torch
+
+    from top_sparse_attention_02_amd import clo
+
+    buf = torch.arange(1 << 20, dtype=torch.int32, device="cuda")  # words < 2^20: no xor equals the sentinel
+    sink = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
+    clo.clo_stream_read(buf, buf.numel() * 4, 64, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 12345
+    with pytest.raises(clo.CloError):
+        clo.clo_stream_read(buf, 100, 64, sink)  # not a multiple of 16
+    with pytest.raises(clo.CloError):
+        clo.clo_stream_read(buf[1:], 16, 64, sink)  # not 16-byte aligned
+    with pytest.raises(clo.CloError):
+        clo.clo_stream_read(buf, 16, 0, sink)  # no blocks
