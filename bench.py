@@ -592,6 +592,16 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    # a second pass of K steps with an event after every step, for the per-step
+    # median and minimum (kept out of the timed region above: at tens of
+    # microseconds per step the extra events would show in it)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record()
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     if multi:
         loop.check()
     ms_per_step = e0.elapsed_time(e1) / args.steps
@@ -645,6 +655,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 4),
+        "ms_per_step_min": round(per_step[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
