@@ -629,7 +629,9 @@ def main():
                     "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s", "frac": round(host_gbs / HOST_LINK_PEAK_GBS, 4),
                     "traffic": None, "bytes_per_launch": alg["host_bytes"] // len(layers),
                     "launch_ms": round(phases["gather"] / len(layers), 4)}
-        rec = profiled_traffic("gather_kernel", args.config) if not multi and args.step == 1 else None
+        # the committed record covers the native-format token gather of the steady step only
+        same_launch = not multi and args.step == 1 and args.host_kv == "native" and args.block_size <= 1
+        rec = profiled_traffic("gather_kernel", args.config) if same_launch else None
         if rec:
             roofline["traffic"] = rec["traffic_bytes_per_launch"]
             roofline["traffic_detail"] = {"read_bytes": rec["read_bytes_per_launch"],

@@ -28,11 +28,12 @@ constexpr int kPartStride = kHeadDim + 2;  // floats per (chunk, head) partial: 
 //    384 KiB    56.7 GB/s      1.2-1.35x           1.3x   (24 blocks x 2 rows)
 //    128 KiB    49.4 GB/s      1.1-1.3x            1.2x
 // The overlapped single-layer step is bound by the gather alone.  Its unit
-// ranges alternate between two gather streams of 16 blocks each (512 KiB in
+// ranges alternate between two gather streams of 20 blocks each (640 KiB in
 // flight while both run).  ms per step, one stream of 32 / 24 blocks, two of
-// 32 / 24 / 16: B=64, N=131072 12.41 / 13.19, 12.86 / 13.01 / 12.34; B=16,
-// N=32768 3.13 / -, 3.26 / 3.28 / 3.03; B=64 with int8 host KV 6.65 / -,
-// 6.98 / 7.10 / 6.57.  A
+// 32 / 24 / 20 / 16: B=64, N=131072 12.41 / 13.19, 12.86 / 13.10 / 12.37 /
+// 12.39; B=16, N=32768 3.13 / -, 3.26 / 3.28 / - / 3.03; B=64 with int8 host
+// KV 6.65 / -, 6.98 / 7.28 / 6.48 / 6.60 (two streams of 24 fall off a cliff:
+// more host reads in flight than the link needs slow every HBM kernel).  A
 // standalone gather (one layer of the 48-layer loop, or a phase of its own)
 // takes 24 blocks, or 40 for layers of 64 units or more.  Beside the gather,
 // the select stream of the 48-layer loop is the longer one, and fewer host
@@ -45,7 +46,7 @@ constexpr int kPartStride = kHeadDim + 2;  // floats per (chunk, head) partial: 
 // 24 / 32 / 40 blocks: its items wait on index and exponent loads before any
 // host read, and its rows carry half the host bytes.
 constexpr int kGatherUnroll = 2;
-constexpr int kGatherBlocksOverlapped = 16;  // per gather stream
+constexpr int kGatherBlocksOverlapped = 20;  // per gather stream
 constexpr int kGatherBlocksAlone = 24;
 constexpr int kGatherBlocksAloneWide = 40;  // layers of at least kGatherWideUnits units
 constexpr int kGatherWideUnits = 64;
