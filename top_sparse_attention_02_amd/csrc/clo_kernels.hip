@@ -589,7 +589,10 @@ constexpr int kTopkThreads = 256;
 // 102 units at N = 131072 select in 0.81 ms (multi-block, with scoring) vs
 // 0.84 ms; 128 units at N = 32768 in 0.29 ms (single block) vs 0.31 ms.
 constexpr int kTopkMultiMin = 8;
-constexpr int kTopkUnroll = 4;     // 16-byte key loads in flight per thread
+constexpr int kTopkUnroll = 4;     // 16-byte key loads in flight per thread (single-block kernel)
+// the multi-block digit passes issue all of a chunk's loads at once (16 per
+// thread): beside the host gather every round trip to memory is slow
+constexpr int kTopkPassUnroll = kTopkChunk / (kTopkThreads * 4);
 
 // One full wave: the digit d whose bin holds the rem-th largest of the counted
 // keys (bins scanned from 255 down) and `above` = the count in bins above d.
@@ -709,15 +712,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pass_kernel(LayerArgs a, Sp
   const uint32_t prefix = s_prefix, mask = s_mask;
   uint32_t gt = 0;  // digit-4 pass: keys whose fixed 24 bits exceed the prefix
   constexpr int kStep = kTopkThreads * 4;
-  for (int64_t base = c0 + (int64_t)tid * 4; base < c1; base += (int64_t)kStep * kTopkUnroll) {
-    u32x4 v[kTopkUnroll];
+  for (int64_t base = c0 + (int64_t)tid * 4; base < c1; base += (int64_t)kStep * kTopkPassUnroll) {
+    u32x4 v[kTopkPassUnroll];
 #pragma unroll
-    for (int j = 0; j < kTopkUnroll; ++j) {
+    for (int j = 0; j < kTopkPassUnroll; ++j) {
       const int64_t i = base + (int64_t)j * kStep;
       v[j] = i < c1 ? *reinterpret_cast<const u32x4*>(kk + i) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int j = 0; j < kTopkUnroll; ++j)
+    for (int j = 0; j < kTopkPassUnroll; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t kv = v[j][e];
@@ -953,35 +956,59 @@ __global__ __launch_bounds__(kTopkThreads) void topk_write_kernel(LayerArgs a, S
   int32_t* out = a.idx + (int64_t)uc.u * a.k;
   const uint32_t T = st[uc.u].prefix, need = st[uc.u].rem;
   const uint32_t D = T & 255u;
+  // the chunk's keys are requested first (16 loads per thread), then the
+  // earlier chunks' histograms 8 chunks at a time: beside the host gather
+  // every round trip to memory is slow, and this kernel used to make one per
+  // earlier chunk and one per tile
+  constexpr int kTile = kTopkThreads * kTopkPerThread;
+  constexpr int kTiles = kTopkChunk / kTile;
+  static_assert(kTopkChunk % kTile == 0, "whole tiles per chunk");
+  u32x4 v[kTiles][kTopkPerThread / 4];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    const int64_t i0 = c0 + (int64_t)t * kTile + (int64_t)tid * kTopkPerThread;
+#pragma unroll
+    for (int j = 0; j < kTopkPerThread / 4; ++j)
+      v[t][j] = (i0 + 4 * j < c1) ? *reinterpret_cast<const u32x4*>(kk + i0 + 4 * j) : u32x4{0u, 0u, 0u, 0u};
+  }
   // winners before this chunk: each earlier chunk's keys above the 24-bit
   // prefix of T, plus its digit-4 bins above D (> T) and at D (== T)
   uint32_t base_g, base_e;
   {
     uint32_t sg = 0, se = 0;
     const uint32_t* ch = chist + (int64_t)uc.u * cmax * kChunkHist;
-    for (int c = 0; c < uc.c; ++c) {
-      const uint32_t v = ch[(int64_t)c * kChunkHist + tid];
-      sg += (uint32_t)tid > D ? v : 0u;
-      se += (uint32_t)tid == D ? v : 0u;
-      if (tid == 0) sg += ch[(int64_t)c * kChunkHist + 256];
+    constexpr int kBatch = 8;
+    for (int cb = 0; cb < uc.c; cb += kBatch) {
+      uint32_t x[kBatch], y[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int c = cb + q < uc.c ? cb + q : uc.c - 1;  // in range; counted below only if cb + q < uc.c
+        x[q] = ch[(int64_t)c * kChunkHist + tid];
+        y[q] = tid == 0 ? ch[(int64_t)c * kChunkHist + 256] : 0u;
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        if (cb + q < uc.c) {
+          sg += ((uint32_t)tid > D ? x[q] : 0u) + y[q];
+          se += (uint32_t)tid == D ? x[q] : 0u;
+        }
+      }
     }
     block_sum2(sg, se, s_wg, s_we, base_g, base_e);
   }
-  constexpr int kTile = kTopkThreads * kTopkPerThread;
-  for (int64_t t0 = c0; t0 < c1; t0 += kTile) {
-    const int64_t i0 = t0 + (int64_t)tid * kTopkPerThread;
-    u32x4 v[kTopkPerThread / 4];
 #pragma unroll
-    for (int j = 0; j < kTopkPerThread / 4; ++j)
-      v[j] = (i0 + 4 * j < c1) ? *reinterpret_cast<const u32x4*>(kk + i0 + 4 * j) : u32x4{0u, 0u, 0u, 0u};
+  for (int t = 0; t < kTiles; ++t) {
+    const int64_t t0 = c0 + (int64_t)t * kTile;
+    if (t0 >= c1) break;  // uniform per block
+    const int64_t i0 = t0 + (int64_t)tid * kTopkPerThread;
     uint32_t cg = 0, ce = 0;
 #pragma unroll
     for (int j = 0; j < kTopkPerThread / 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool valid = i0 + 4 * j + e < c1;
-        cg += valid && v[j][e] > T;
-        ce += valid && v[j][e] == T;
+        cg += valid && v[t][j][e] > T;
+        ce += valid && v[t][j][e] == T;
       }
     uint32_t eg, ee, tg, te;
     scan2(cg, ce, s_wg, s_we, eg, ee, tg, te);
@@ -992,7 +1019,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_write_kernel(LayerArgs a, S
       for (int e = 0; e < 4; ++e) {
         const int64_t i = i0 + 4 * j + e;
         if (i >= c1) continue;
-        const uint32_t kv = v[j][e];
+        const uint32_t kv = v[t][j][e];
         if (kv > T) {
           const uint32_t pos = pg + (pe < need ? pe : need);
           if (pos < (uint32_t)a.k) out[pos] = (int32_t)i;
