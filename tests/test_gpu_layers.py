@@ -67,6 +67,33 @@ def test_layer_loop_matches_sequential_and_oracle(need_gpu, select_streams):
         compare(p, layers[l], a1[l], r1, kv, f"layer {l} step1")
 
 
+def test_layer_loop_int8_host_kv_matches_sequential(need_gpu):
+    """The three-stream loop over layers whose offloaded KV is int8 in host memory (the
+    dequantizing gather, its in-LDS unit list and the fused reuse-select launch) equals
+    the fused step run layer after layer on one stream, bit for bit."""
+    import torch
+
+    from top_sparse_attention_02_amd import clo, workload
+
+    p = enforce_all_layers(multi_layer_problem())
+    layers = workload.load_layers(p, host_format=clo.CLO_HOST_INT8)
+    loop = workload.LayerLoop(layers)
+    log("[case layer loop, int8 host KV] cold + steady step")
+    loop.step(cold=True)
+    loop.step()
+    torch.cuda.synchronize()
+    loop.check()
+    a1 = [snapshot(b) for b in layers]
+    for b in layers:
+        b.step0()
+    for b in layers:
+        b.step1()
+    b1 = [snapshot(b) for b in layers]
+    for l in range(p.layers):
+        for key in a1[l]:
+            assert np.array_equal(a1[l][key], b1[l][key]), (l, key)
+
+
 def test_consumer_sees_rows_written_before_the_flag(need_gpu):
     """Delay the producer (gather) on its stream; the consumer (attention) must still
     read the freshly gathered rows because it waits for the producer's flag."""

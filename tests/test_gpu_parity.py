@@ -278,3 +278,15 @@ def test_block_selection(need_gpu, bs, dtype):
         for h in range(p.hkv):
             sel = got1["idx"][b, h]
             assert np.all(sel.reshape(-1, bs) == (sel.reshape(-1, bs)[:, :1] + np.arange(bs)))
+    # step 1 again through clo_reuse_select (its single-block reuse test and unit
+    # lists clear the block-key histograms), the gather and attention: bit for bit
+    from top_sparse_attention_02_amd import clo
+
+    bufs.step0()
+    shape, layer = bufs.shape_with(p.tau), bufs.layer()
+    clo.clo_reuse_select(shape, layer, bufs.q, bufs.q_prev, bufs.reuse, bufs.cos, bufs.ws)
+    clo.clo_gather_kv(shape, layer, bufs.reuse, bufs.ws)
+    clo.clo_sparse_attn(shape, layer, bufs.q, bufs.out, bufs.ws)
+    split = snapshot(bufs)
+    for key in got1:
+        assert np.array_equal(got1[key], split[key]), key
