@@ -68,6 +68,9 @@ def parse():
                     help="int8 host KV, configs 1-3: skip the output comparison against the native format")
     ap.add_argument("--select-streams", type=int, default=1, metavar="S",
                     help="48-layer loop: streams the layers' selections alternate between")
+    ap.add_argument("--graph", action="store_true",
+                    help="single-layer configs: capture one step into a HIP graph and time its replays "
+                         "(launch-bound small steps)")
     ap.add_argument("--growing", type=int, default=0, metavar="T",
                     help="configs 1-3: T decode steps over a context that grows by one appended token per "
                          "step, under both reference policies (previous step's query / query at the last "
@@ -578,6 +581,13 @@ def main():
         layers[0].step0()
         step = layers[0].step1 if args.step == 1 else layers[0].step0
     torch.cuda.synchronize()
+    if args.graph:
+        if multi:
+            print("--graph is for single-layer configs (the 48-layer loop waits on device flags)", file=sys.stderr)
+            sys.exit(2)
+        graph = workload.capture_step(step)
+        step = graph.replay
+        log("step captured into a HIP graph; timing its replays")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -673,6 +683,7 @@ def main():
                    "layers": p.layers, "batch": p.batch, "q_heads": p.hq, "kv_heads": p.hkv, "head_dim": HEAD_DIM,
                    "context": p.context, "topk": p.topk, "tau": p.tau, "step": args.step,
                    "data_layers": p.data_layers or p.layers, "host_memory": args.host_memory,
+                   **({"graph": True} if args.graph else {}),
                    **({"select_streams": args.select_streams} if multi else {})},
         "roofline": roofline,
         "persistent_plan": None if plan is None else {k: v for k, v in plan.items() if k != "persistent"},

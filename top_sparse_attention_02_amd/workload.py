@@ -143,6 +143,28 @@ class LayerBuffers:
         self.decode_step(self.q, self.q_prev, self.tau, stream)
 
 
+def capture_step(step) -> "torch.cuda.CUDAGraph":
+    """Capture one call of `step` (a function that enqueues a whole decode step on
+    the current stream, e.g. LayerBuffers.step1) into a HIP graph; replay() then
+    launches all of its kernels at once.  The library records no memset or copy,
+    synchronizes nothing and orders its helper streams with events, so the step
+    captures whole; validation runs on the host at capture time only, and the
+    buffers must stay where they were when captured."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # one eager call first: the library creates its helper streams outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    # relaxed: the host-side pointer checks of the library's entry points
+    # (hipPointerGetAttributes) run during the capture, and they enqueue nothing
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        step()
+    torch.cuda.synchronize()
+    return g
+
+
 def stored_tensor(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(a))
     if dtype == "bf16":
