@@ -67,6 +67,7 @@ def _gather_case(batch, hkv, persistent_heads, context, topk, seed):
 
 @pytest.mark.parametrize("batch,hkv,persistent,context,topk", [
     (3, 8, [1, 6], 700, 300),     # 24 units: listed in LDS; 2 items per unit with a ragged tail
+    (256, 8, [3], 40, 9),         # 2048 units: exactly what the LDS list holds
     (257, 8, [0, 5], 40, 7),      # 2056 units: more than the LDS list holds
     (1, 8, [], 5000, 513),        # one sequence, every head offloaded, 3 items per unit
 ])

@@ -150,7 +150,8 @@ def test_standalone_entry_points_equal_fused_step(need_gpu):
         assert np.array_equal(fused[key], split[key]), key
 
 
-@pytest.mark.parametrize("batch,hkv,persistent", [(2, 4, [1, 0, 0, 1]), (9, 8, [0, 1, 0, 0, 0, 0, 1, 0])])
+@pytest.mark.parametrize("batch,hkv,persistent", [(2, 4, [1, 0, 0, 1]), (8, 8, [0, 0, 1, 0, 0, 0, 0, 1]),
+                                                  (9, 8, [0, 1, 0, 0, 0, 0, 1, 0])])
 def test_reuse_select_equals_fused_step(need_gpu, batch, hkv, persistent):
     """clo_reuse_select (reuse test + top-k in one call; one fused launch for the reuse
     test and unit lists up to 64 units, separate launches above) + gather + attention
