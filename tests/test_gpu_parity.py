@@ -155,7 +155,8 @@ def test_standalone_entry_points_equal_fused_step(need_gpu):
 def test_reuse_select_equals_fused_step(need_gpu, batch, hkv, persistent):
     """clo_reuse_select (reuse test + top-k in one call; one fused launch for the reuse
     test and unit lists up to 64 units, separate launches above) + gather + attention
-    == clo_decode_step, bit for bit; its wait on an already-set flag passes through."""
+    == clo_decode_step, bit for bit, at 8, 64 and 72 units (either side of the 64-unit
+    bound); its wait on an already-set flag passes through."""
     import torch
 
     from top_sparse_attention_02_amd import clo, workload
