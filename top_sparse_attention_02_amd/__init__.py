@@ -14,6 +14,7 @@ from .clo import (  # noqa: F401
     clo_decode_step,
     clo_gather_kv,
     clo_last_error,
+    clo_reuse_select,
     clo_reuse_test,
     clo_sparse_attn,
     clo_status_string,
