@@ -307,7 +307,10 @@ clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int
  * threads, 16-byte loads, and leaves *sink (device, 4 bytes) unchanged except
  * with probability 2^-32.  Timed around its launch it gives the HBM read
  * ceiling against which the HBM-bound kernels (scoring, attention) are
- * reported, as the pinned->device copy gives the host link's.
+ * reported, as the pinned->device copy gives the host link's.  Asynchronous
+ * on `stream`; bytes == 0 launches nothing.  CLO_E_ARG for a size that is not
+ * a multiple of 16, blocks outside 1..2^20, or a src / sink that is NULL,
+ * misaligned, not device memory or shorter than the size.
  */
 clo_status clo_stream_read(const void* src, size_t bytes, int32_t blocks, uint32_t* sink, void* stream);
 
