@@ -234,12 +234,13 @@ def probe_host_link(torch, nbytes=1 << 30):
     return res
 
 
-def cpu_baseline(p, layers, budget_s, step_kind):
+def cpu_baseline(p, layers, budget_s, step_kind, one_thread=False):
     """The CPU oracle, as it is, on a bounded sample of the step's units, scaled to steps/s.
 
     Inputs are the generated ones only: the oracle classifies units with its own
     cosine test and, for a reused unit, first makes its own previous selection
-    (untimed) from q_prev."""
+    (untimed) from q_prev.  one_thread: also time a second sample with the BLAS
+    pool limited to one thread (the small workloads)."""
     import numpy as np
 
     import oracle
@@ -285,23 +286,37 @@ def cpu_baseline(p, layers, budget_s, step_kind):
         oracle.decode_unit(qg, qpg, oracle.as_f64(K, p.dtype), oracle.as_f64(V, p.dtype), p.topk, tau, prev)
         return time.perf_counter() - t
 
-    t_miss, t_hit = [], []
-    spent = 0.0
-    i = 0
-    while spent < budget_s and (i < len(miss_s) or i < len(hit_s)):
-        if i < len(miss_s):
-            t_miss.append(run(miss_s[i], False))
-            spent += t_miss[-1]
-        if i < len(hit_s):
-            t_hit.append(run(hit_s[i], True))
-            spent += t_hit[-1]
-        i += 1
-    est = (np.mean(t_miss) if t_miss else 0.0) * len(miss_u) + (np.mean(t_hit) if t_hit else 0.0) * len(hit_u)
-    return {"value": round(1.0 / est, 6) if est > 0 else None, "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(t_miss)} miss + {len(t_hit)} reuse units of the {len(miss_u) + len(hit_u)}-unit step "
-                      f"({spent:.1f} s of oracle time), fp64 numpy oracle, per-unit mean times scaled to the "
-                      f"step's {len(miss_u)} miss / {len(hit_u)} reuse units",
-            "seconds_per_step_est": round(est, 3)}
+    def sample(budget):
+        t_miss, t_hit = [], []
+        spent = 0.0
+        i = 0
+        while spent < budget and (i < len(miss_s) or i < len(hit_s)):
+            if i < len(miss_s):
+                t_miss.append(run(miss_s[i], False))
+                spent += t_miss[-1]
+            if i < len(hit_s):
+                t_hit.append(run(hit_s[i], True))
+                spent += t_hit[-1]
+            i += 1
+        est = (np.mean(t_miss) if t_miss else 0.0) * len(miss_u) + (np.mean(t_hit) if t_hit else 0.0) * len(hit_u)
+        return est, len(t_miss), len(t_hit), spent
+
+    est, n_miss, n_hit, spent = sample(budget_s)
+    out = {"value": round(1.0 / est, 6) if est > 0 else None, "unit": "steps/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n_miss} miss + {n_hit} reuse units of the {len(miss_u) + len(hit_u)}-unit step "
+                     f"({spent:.1f} s of oracle time), fp64 numpy oracle, per-unit mean times scaled to the "
+                     f"step's {len(miss_u)} miss / {len(hit_u)} reuse units",
+           "seconds_per_step_est": round(est, 3)}
+    if one_thread:
+        try:
+            from threadpoolctl import threadpool_limits
+        except ImportError:
+            return out
+        with threadpool_limits(limits=1):
+            est1, n_miss1, n_hit1, spent1 = sample(budget_s / 2)
+        out["value_1thread"] = round(1.0 / est1, 6) if est1 > 0 else None
+        out["sample_1thread"] = f"{n_miss1} miss + {n_hit1} reuse units ({spent1:.1f} s), BLAS limited to 1 thread"
+    return out
 
 
 WORKLOADS = {
@@ -708,7 +723,8 @@ def main():
         result["layer_steps_per_s"] = round(p.layers / step_s, 2)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of units")
-        result["cpu_baseline"] = cpu_baseline(p, layers, args.cpu_sample_seconds, args.step)
+        result["cpu_baseline"] = cpu_baseline(p, layers, args.cpu_sample_seconds, args.step,
+                                              one_thread=args.config in (1, 2))
     print(json.dumps(result), flush=True)
 
 
