@@ -150,6 +150,38 @@ def test_standalone_entry_points_equal_fused_step(need_gpu):
         assert np.array_equal(fused[key], split[key]), key
 
 
+@pytest.mark.parametrize("name,kw", [
+    # config-1 shape: 8 units, 2 attention chunks
+    ("inorder_f32", dict(batch=1, hq=32, hkv=8, context=4096, topk=410, dtype="f32", persistent=[1] * 8)),
+    # 12 chunks per unit, bf16, group 5
+    ("inorder_bf16", dict(batch=2, hq=10, hkv=2, context=30000, topk=3000, dtype="bf16", persistent=[1, 1])),
+    # 70 units: the reuse test and unit lists in launches of their own
+    ("inorder_wide", dict(batch=35, hq=4, hkv=2, context=700, topk=70, dtype="bf16", persistent=[1, 1])),
+])
+def test_in_order_step_equals_separate_calls(need_gpu, name, kw):
+    """Layers without offloaded heads run the whole step in order on one stream (the reuse
+    test and unit lists in one launch up to 64 units).  Its outputs equal a separate
+    clo_sparse_attn call's bit for bit, and both steps the oracle's."""
+    from top_sparse_attention_02_amd import clo, workload
+
+    p = small_problem(name, **kw)
+    enforce_margins(p, 0)
+    bufs = workload.load_layer(p, 0)
+    log(f"[case {name}] U={p.batch * p.hkv} k={p.topk}")
+    bufs.step0()
+    got0 = snapshot(bufs)
+    bufs.step1()
+    fused = snapshot(bufs)
+    shape, layer = bufs.shape_with(p.tau), bufs.layer()
+    bufs.out.zero_()
+    clo.clo_sparse_attn(shape, layer, bufs.q, bufs.out, bufs.ws)
+    split = snapshot(bufs)
+    assert np.array_equal(fused["out"], split["out"])
+    r0, r1, kv = oracle_steps(p, 0)
+    compare(p, bufs, got0, r0, kv, "step0")
+    compare(p, bufs, fused, r1, kv, "step1")
+
+
 @pytest.mark.parametrize("batch,hkv,persistent", [(2, 4, [1, 0, 0, 1]), (8, 8, [0, 0, 1, 0, 0, 0, 0, 1]),
                                                   (9, 8, [0, 1, 0, 0, 0, 0, 1, 0])])
 def test_reuse_select_equals_fused_step(need_gpu, batch, hkv, persistent):
