@@ -105,12 +105,15 @@ typedef struct {
                           k_score: the row stride of those tensors.  0 = context.  A context that
                           grows during decoding (clo_append_kv) keeps capacity fixed and raises
                           context; only rows 0..context-1 are read. */
-  const float* tau_heads;  /* per-head thresholds (synthesis sections 3.1 and 5.3: profiling sets a
-                              threshold per head): host array [n_kv_heads], read during the call;
-                              unit (b, h) reuses when cos >= tau_heads[h].  NULL = tau for every
-                              head. */
-  int32_t block_size;  /* selection granularity (synthesis section 3.3: per-head selection fragments
-                          host transfers; selecting token blocks keeps them contiguous).  0 or 1 =
+  const float* tau_heads;  /* per-head thresholds (synthesis section 3.3, attack point 6, and
+                              section 5.3: profiling sets a threshold per head): host array
+                              of exactly n_kv_heads floats (the library reads that many; a
+                              shorter array is read past its end), read during the call;
+                              unit (b, h) reuses when cos >= tau_heads[h].  NULL = tau for
+                              every head. */
+  int32_t block_size;  /* selection granularity (KV-cache offloading article: pillar 2, PulseInfer
+                          paragraph -- per-head selection fragments host transfers; pillar 3,
+                          block-sparse recall -- whole blocks keep each recall one transfer).  0 or 1 =
                           tokens.  B > 1: the context is cut into floor(N / B) full blocks of B
                           consecutive tokens (a partial tail block is not selectable), a block
                           scores the max of its tokens' scores, the k / B best blocks are taken
@@ -245,7 +248,7 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
 
 /*
  * Multi-step decoding with a growing context -- appending the decoded token
- * (synthesis section 5.6 on incremental offloading: new KV goes to host memory
+ * (synthesis section 5.7 on incremental offloading: new KV goes to host memory
  * as it is produced; abstract feature (3): the GPU moves KV without CPU work).
  * Writes k_new[b][h] and v_new[b][h] ([B, Hkv, d] device, dtype of the shape)
  * as row `position` of every (sequence, KV head): into k_hbm/v_hbm for
@@ -274,7 +277,7 @@ clo_status clo_update_reference(const clo_shape* shape, const void* q, const uin
                                 const clo_sync* sync, void* stream);
 
 /*
- * Profiling-based choice of persistent heads (synthesis section 3.1 attack
+ * Profiling-based choice of persistent heads (synthesis section 3.3 attack
  * point 6 and section 5.3: offline profiling fixes each head's mean adjacent-
  * step query similarity and the number of persistent heads).  s_hat is a host
  * array [n_layers, n_kv_heads] of per-(layer, KV head) mean cosines; the
@@ -290,7 +293,8 @@ clo_status clo_plan_persistent(const float* s_hat, int32_t n_layers, int32_t n_k
 
 /*
  * Quantize rows for an int8 host copy (CLO_HOST_INT8; quantized offloaded KV,
- * synthesis sections 3.3 and 5.6 on cutting the bytes that cross the host link).
+ * KV-cache offloading article, pillar 3, quantized offloading: fewer bytes cross
+ * the host link and the GPU dequantizes).
  * Reads n_rows rows of 128 elements of `dtype` from src (device), writes their
  * int8 values to dst (device or pinned host memory; row r at dst + r *
  * dst_stride bytes, dst_stride >= 128 and a multiple of 16: 256 fills the K or V

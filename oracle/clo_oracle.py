@@ -32,21 +32,25 @@ Synthesis"; CLO abstract page on fugumt):
     zero-copy transfers only change where rows come from.
   * O6: synthesis section 2.3 table -- attention is top-k sparse attention.
   * Per-head thresholds and the persistent-head choice (decode_layer with one
-    tau per KV head, plan_persistent): synthesis section 3.1 attack point 6
+    tau per KV head, plan_persistent): synthesis section 3.3, attack point 6,
     and section 5.3 -- offline profiling fixes each head's mean similarity,
-    its threshold and the number of persistent heads.
-  * Block-granular selection (select_blocks): synthesis section 3.3 -- per-head
-    token selection fragments host transfers; selecting blocks of consecutive
-    tokens keeps them contiguous.  The block score (max of its tokens' scores)
-    and the full-blocks-only rule are this implementation's reading.
-  * Quantized host KV (quantize_row, dequantize_row): synthesis sections 3.3
-    and 5.6 -- fewer bytes across the host link; the format (int8 values, one
+    the number of persistent heads, and (section 5.3) a threshold per head.
+  * Block-granular selection (select_blocks, decode_unit's block_size): the
+    KV-cache offloading article ("KV Cache Offloading 完全拆解"), pillar 2,
+    its PulseInfer paragraph (per-head sparse selection breaks the recall into
+    many small PCIe transfers), and pillar 3, subsection "搬运量:从全量到分块
+    稀疏" (recall whole blocks so that each recall is one transfer).  The block
+    score (max of its tokens' scores) and the full-blocks-only rule are this
+    implementation's reading.
+  * Quantized host KV (quantize_row, dequantize_row, quantized_rows): the same
+    article, pillar 3, subsection "量化卸载" (quantize the offloaded KV, move
+    fewer bytes, dequantize on the GPU).  The format (int8 values, one
     power-of-two scale per row) is this implementation's choice, written out
     at quantize_row.  Scoring keeps the exact keys; attention of offloaded
     heads reads the dequantized rows (decode_unit's K_attn / V_attn).
   * Multi-step decoding (decode_steps_unit): synthesis section 2.1 item 2 --
-    the similarity is between adjacent decode steps; section 5.6 -- the
-    context grows by the decoded token and new KV is offloaded incrementally.
+    the similarity is between adjacent decode steps; section 5.7 -- a KV cache
+    that keeps growing, offloaded incrementally.
 The pages print no formulas.  Readings taken where they are silent: the
 cosine spans the concatenated query group (one decision per KV head); the
 comparison is inclusive; the group's score is the max over its heads; ties go

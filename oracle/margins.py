@@ -1,5 +1,9 @@
 """Decision margins that make bit-exact parity of reuse decisions and top-k sets well posed.
 
+Test infrastructure, as the rest of this package: only the tests, the smoke
+check and the benchmark's CPU baseline use it; it adjusts seeded inputs with
+the oracle's own arithmetic and never with the GPU path.
+
 The GPU accumulates in fp32 and the oracle in fp64, so a score within rounding
 error of the k-th/(k+1)-th boundary, or a cosine within rounding error of tau,
 could flip a decision.  Before a parity comparison, the inputs are adjusted with
@@ -16,7 +20,7 @@ from __future__ import annotations
 
 import numpy as np
 
-import oracle
+from . import clo_oracle as oracle
 
 COS_MARGIN = 1e-4
 

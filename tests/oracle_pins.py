@@ -433,6 +433,23 @@ def pin_quantize_invariants(O):
         assert e2 == e + 3 and list(q2) == list(q)
 
 
+def pin_quantized_rows_closed_form(O):
+    # quantized_rows works row by row: row 0 (max 1) gets e = -6, so 0.3 becomes
+    # rint(19.2) / 64 = 19/64; row 1 (max 100) gets e = 0, so 0.3 becomes 0.  A
+    # column-wise or transposed rule would give column 1 (max 0.3, e = -8) the
+    # value rint(76.8) / 256 = 77/256 in both rows.
+    X = np.array([[1.0, 0.3, 0.0, -0.5], [100.0, 0.3, -7.0, 0.0]])
+    got = O.quantized_rows(X)
+    assert got.shape == X.shape
+    want = np.array([[1.0, 19 / 64, 0.0, -0.5], [100.0, 0.0, -7.0, 0.0]])
+    assert np.array_equal(got, want)
+    # rows that each fit their own scale come back unchanged (row 0: e = 0, row 1:
+    # e = -16, values 64 * 2^-16 and -16 * 2^-16); one scale per column would
+    # flush 2^-10 to 0 next to 64
+    Y = np.array([[64.0, -32.0, 16.0], [2.0 ** -10, 0.0, -(2.0 ** -12)]])
+    assert np.array_equal(O.quantized_rows(Y), Y)
+
+
 # ---------------------------------------------------------------- block selection
 def pin_select_blocks_closed_form(O):
     # blocks of 2 over 9 tokens: (0.1, 0.9) -> 0.9, (0.2, 0.3) -> 0.3, (0.8, 0.85) -> 0.85,
@@ -467,6 +484,76 @@ def pin_select_blocks_invariants(O):
                     assert bmax[c] > bmax[b] or (bmax[c] == bmax[b] and c < b)
         if bs == 1:
             assert list(sel) == list(O.select_topk(s, kb))
+
+
+# ---------------------------------------------------------------- attention rows apart from scored keys, blocks in a layer
+# T1's unit: q = (sqrt2, 0); exact keys (1,0), (0,1), (-1,0), (2,0) score sqrt2, 0,
+# -sqrt2, 2 sqrt2, so k = 2 selects rows {0, 3}.  Attention reads other rows:
+# K_attn has the selected rows halved, (0.5,0) and (1,0) (logits 1/2 and 1 at
+# d = 2, weights sigma(-1/2) and sigma(1/2)), and a large row 1, (5,0), that the
+# exact keys never select (scoring K_attn would take {1, 3}); V_attn rows 0 and 3
+# are (10,0) and (0,20).
+_T1_Q = np.array([[math.sqrt(2.0), 0.0]])
+_T1_K = np.array([[1.0, 0.0], [0.0, 1.0], [-1.0, 0.0], [2.0, 0.0]])
+_T1_V = np.array([[1.0, 0.0], [0.0, 1.0], [5.0, 5.0], [0.0, 2.0]])
+_T1_KA = np.array([[0.5, 0.0], [5.0, 0.0], [-0.5, 0.0], [1.0, 0.0]])
+_T1_VA = np.array([[10.0, 0.0], [3.0, 3.0], [7.0, 7.0], [0.0, 20.0]])
+_T1_OUT_A = [10 * sigmoid(-0.5), 20 * sigmoid(0.5)]
+
+
+def pin_decode_unit_attn_rows(O):
+    r = O.decode_unit(_T1_Q, _T1_Q, _T1_K, _T1_V, 2, math.inf, K_attn=_T1_KA, V_attn=_T1_VA)
+    assert r["reuse"] is False and list(r["idx"]) == [0, 3]
+    assert close(r["out"], [_T1_OUT_A], 1e-12)
+    # without separate rows: T1's own attention, weights sigma(-1) and sigma(1) on V rows (1,0), (0,2)
+    r = O.decode_unit(_T1_Q, _T1_Q, _T1_K, _T1_V, 2, math.inf)
+    assert close(r["out"], [[sigmoid(-1.0), 2 * sigmoid(1.0)]], 1e-12)
+    # a reused unit attends its previous selection in the separate rows too
+    r = O.decode_unit(_T1_Q, _T1_Q, _T1_K, _T1_V, 2, -1.5, idx_prev=np.array([0, 3]), K_attn=_T1_KA,
+                      V_attn=_T1_VA)
+    assert r["reuse"] is True and close(r["out"], [_T1_OUT_A], 1e-12)
+
+
+def pin_decode_layer_attn_rows(O):
+    # a layer of two units (B = 1, Hkv = 2, g = 1, fp32, q = (1, 0) exact) on T1's
+    # keys: scores 1, 0, -1, 2 select {0, 3} in both.  attn_kv_of gives unit (0, 1)
+    # the separate rows and leaves unit (0, 0) alone.  Unit (0, 0): logits 1/sqrt2,
+    # 2/sqrt2 on V rows (1,0), (0,2); unit (0, 1): logits (1/2)/sqrt2, 1/sqrt2 on
+    # V_attn rows (10,0), (0,20).
+    q = np.array([[[1.0, 0.0], [1.0, 0.0]]], dtype=np.float32)
+    K32, V32 = _T1_K.astype(np.float32), _T1_V.astype(np.float32)
+    res = O.decode_layer(q, q, lambda b, h: (K32, V32), 2, 2, math.inf, "f32",
+                         attn_kv_of=lambda b, h: (_T1_KA, _T1_VA) if h == 1 else None)
+    assert list(res[(0, 0)]["idx"]) == [0, 3] and list(res[(0, 1)]["idx"]) == [0, 3]
+    p = sigmoid(1 / math.sqrt(2.0))
+    assert close(res[(0, 0)]["out"], [[1 - p, 2 * p]], 1e-12)
+    p = sigmoid(0.5 / math.sqrt(2.0))
+    assert close(res[(0, 1)]["out"], [[10 * (1 - p), 20 * p]], 1e-12)
+
+
+def pin_decode_layer_blocks(O):
+    # B = 1, Hkv = 2, g = 1, d = 2, N = 5, k = 2, blocks of 2 (token 4 is a tail
+    # block, never selectable); values exact in fp32.
+    # unit 0: q = (1, 0); scores 1/8, 7/8, 3/4, 13/16, 3 -> blocks 7/8, 13/16 ->
+    #   block 0 = tokens {0, 1} (token top-2 would be {1, 4}); logits (1/8, 7/8)/sqrt2
+    #   on V rows (1,0), (0,1): o = (1 - p, p), p = sigma((3/4)/sqrt2).
+    # unit 1: q = (0, 1); scores 1/4, 1/8, 1/2, 3/8, 9 -> blocks 1/4, 1/2 -> block 1 =
+    #   tokens {2, 3} (token top-2: {2, 4}); logits (1/2, 3/8)/sqrt2 on V rows (2,0),
+    #   (0,2): o = (2 p2, 2 (1 - p2)), p2 = sigma((1/8)/sqrt2).
+    q = np.array([[[1.0, 0.0], [0.0, 1.0]]], dtype=np.float32)
+    K = {0: np.array([[0.125, 0], [0.875, 0], [0.75, 0], [0.8125, 0], [3.0, 0]], dtype=np.float32),
+         1: np.array([[0, 0.25], [0, 0.125], [0, 0.5], [0, 0.375], [0, 9.0]], dtype=np.float32)}
+    V = {0: np.array([[1, 0], [0, 1], [4, 4], [6, 6], [8, 8]], dtype=np.float32),
+         1: np.array([[1, 0], [0, 1], [2, 0], [0, 2], [5, 5]], dtype=np.float32)}
+    kv = lambda b, h: (K[h], V[h])  # noqa: E731
+    res = O.decode_layer(q, q, kv, 2, 2, math.inf, "f32", block_size=2)
+    assert list(res[(0, 0)]["idx"]) == [0, 1] and list(res[(0, 1)]["idx"]) == [2, 3]
+    p = sigmoid(0.75 / math.sqrt(2.0))
+    assert close(res[(0, 0)]["out"], [[1 - p, p]], 1e-12)
+    p2 = sigmoid(0.125 / math.sqrt(2.0))
+    assert close(res[(0, 1)]["out"], [[2 * p2, 2 * (1 - p2)]], 1e-12)
+    tok = O.decode_layer(q, q, kv, 2, 2, math.inf, "f32")
+    assert list(tok[(0, 0)]["idx"]) == [1, 4] and list(tok[(0, 1)]["idx"]) == [2, 4]
 
 
 def pin_bf16_decoding(O):
@@ -608,8 +695,12 @@ ALL_PINS = [
     pin_plan_persistent,
     pin_quantize_closed_forms,
     pin_quantize_invariants,
+    pin_quantized_rows_closed_form,
     pin_select_blocks_closed_form,
     pin_select_blocks_invariants,
+    pin_decode_unit_attn_rows,
+    pin_decode_layer_attn_rows,
+    pin_decode_layer_blocks,
     pin_bf16_decoding,
     pin_golden_reuse,
     pin_golden_selection,

@@ -16,7 +16,7 @@ import pytest
 import gen
 import oracle
 from tests.gpu_common import compare, log, snapshot
-from tests.margins import enforce_margins
+from oracle.margins import enforce_margins
 
 pytestmark = pytest.mark.gpu
 
@@ -64,7 +64,7 @@ def sample_units(p, layer, n_miss, n_hit, seed=0):
 def enforce_cos_all(p, layer):
     """Cosine margins on every unit of a layer (only q_prev redraws; cheap)."""
     all_units = [(b, h) for b in range(p.batch) for h in range(p.hkv)]
-    from tests import margins
+    from oracle import margins
 
     g = p.g
     for _ in range(20):

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from tests.gpu_common import log, small_problem, snapshot
-from tests.margins import enforce_margins
+from oracle.margins import enforce_margins
 
 pytestmark = pytest.mark.gpu
 

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from tests.gpu_common import compare, log, small_problem, snapshot, to_numpy
-from tests.margins import enforce_margins, enforce_walk_margins
+from oracle.margins import enforce_margins, enforce_walk_margins
 
 pytestmark = pytest.mark.gpu
 

@@ -7,7 +7,7 @@ import pytest
 
 import gen
 from tests.gpu_common import compare, log, oracle_steps, snapshot
-from tests.margins import enforce_margins
+from oracle.margins import enforce_margins
 
 pytestmark = pytest.mark.gpu
 

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from tests.gpu_common import log, run_and_check, small_problem, snapshot, compare, oracle_steps
-from tests.margins import enforce_margins
+from oracle.margins import enforce_margins
 
 pytestmark = pytest.mark.gpu
 
@@ -278,7 +278,7 @@ def test_per_head_thresholds(need_gpu):
 @pytest.mark.parametrize("bs,dtype", [(16, "bf16"), (64, "f32"), (3, "bf16")])
 def test_block_selection(need_gpu, bs, dtype):
     """Token blocks as the selection unit (full blocks only, ragged tail ignored)."""
-    from tests.margins import enforce_block_margins
+    from oracle.margins import enforce_block_margins
     from top_sparse_attention_02_amd import workload
 
     p = small_problem(f"blocks_{bs}_{dtype}", batch=2, hq=8, hkv=2, context=5007, topk=40 * bs, dtype=dtype,

@@ -1,251 +1,132 @@
-"""Plant plausible mistakes in copies of the oracle; each must fail at least one pin.
+"""Plant plausible mistakes in the oracle's own source; each must fail at least one pin.
 
-This shows the pins are strong enough to catch a dropped term, a wrong sign or
-index, or a transposed operand anywhere in the oracle's arithmetic.
+Every mutant is a fresh copy of oracle/clo_oracle.py, executed as a module of
+its own after one or more text edits (each edit site must occur exactly once),
+or with one function replaced.  The oracle's functions look each other up in
+their module, so a mutant goes through the real decode_unit, decode_layer and
+decode_steps_unit: a dropped term, a wrong sign or index, or a transposed
+operand anywhere in the arithmetic, or in the way those compositions route
+their arguments, must be caught by the pins.
 """
-import math
+import os
 import types
 
 import numpy as np
 import pytest
 
-import oracle
 from oracle import clo_oracle as base
 from tests.oracle_pins import ALL_PINS
 
-
-def _ns(**over):
-    ns = types.SimpleNamespace(**{n: getattr(base, n) for n in (
-        "as_f64", "group_cosine", "reuse_decision", "token_scores", "select_topk",
-        "attend", "decode_unit", "decode_layer")})
-    for k, v in over.items():
-        setattr(ns, k, v)
-    # decode_unit/decode_layer must route through the (possibly mutated) namespace
-    def decode_unit(q_group, q_prev_group, K, V, k, tau, idx_prev=None):
-        c = ns.group_cosine(q_group, q_prev_group)
-        reuse = ns.reuse_decision(c, tau)
-        sel = np.asarray(idx_prev) if reuse else ns.select_topk(ns.token_scores(q_group, K), k)
-        return {"cos": c, "reuse": reuse, "idx": sel,
-                "out": ns.attend(q_group, np.asarray(K, float)[sel], np.asarray(V, float)[sel])}
-
-    def decode_layer(q, q_prev, kv_of, hkv, k, tau, dtype, idx_prev=None, units=None, head_of=None,
-                     tau_of=None):
-        qf, qpf = ns.as_f64(q, dtype), ns.as_f64(q_prev, dtype)
-        B, Hq, _ = qf.shape
-        g = Hq // hkv
-        res = {}
-        for b in range(B):
-            for h in range(hkv):
-                heads = head_of(h, g, hkv, Hq) if head_of else list(range(h * g, (h + 1) * g))
-                K, V = kv_of(b, h)
-                t = (tau_of or (lambda tau, h: float(tau[h]) if np.ndim(tau) else float(tau)))(tau, h)
-                res[(b, h)] = ns.decode_unit(qf[b, heads], qpf[b, heads], ns.as_f64(K, dtype), ns.as_f64(V, dtype),
-                                             k, t, None if idx_prev is None else idx_prev[b, h])
-        return res
-
-    def decode_steps_unit(queries, K, V, n0, k, tau, policy="previous", grow=1, lag=0, rules=None):
-        # rules maps a policy to when the reference is replaced: "previous" every
-        # step, "refresh" on a miss, "never" only at the cold step
-        rule = (rules or {}).get(policy, policy)
-        results, ref, sel = [], None, None
-        for t, qg in enumerate(queries):
-            n = n0 + grow * t - (lag if t else 0)
-            if t == 0:
-                r = ns.decode_unit(qg, qg, K[:n], V[:n], k, math.inf)
-            else:
-                r = ns.decode_unit(qg, ref, K[:n], V[:n], k, tau, sel)
-            sel = r["idx"]
-            if t == 0 or rule == "previous" or (rule == "refresh" and not r["reuse"]):
-                ref = qg
-            results.append(r)
-        return results
-
-    if "decode_unit" not in over:
-        ns.decode_unit = decode_unit
-    if "decode_layer" not in over:
-        ns.decode_layer = decode_layer
-    steps_kw = over.get("steps_kw")
-    if steps_kw is not None:
-        ns.decode_steps_unit = lambda *a, **kw: decode_steps_unit(*a, **{**kw, **steps_kw})
-    elif "decode_steps_unit" not in over:
-        ns.decode_steps_unit = decode_steps_unit
-    if "head_of" in over:
-        ns.decode_layer = lambda *a, **kw: decode_layer(*a, head_of=over["head_of"], **kw)
-    if "tau_of" in over:
-        ns.decode_layer = lambda *a, **kw: decode_layer(*a, tau_of=over["tau_of"], **kw)
-    for name in ("plan_persistent", "quantize_row", "dequantize_row", "select_blocks"):
-        if name not in over:
-            setattr(ns, name, getattr(base, name))
-    return ns
+SRC_PATH = base.__file__
+with open(SRC_PATH, encoding="utf-8") as _f:
+    SRC = _f.read()
 
 
-def m_sum_over_heads(q_group, K):
-    return (np.asarray(K, float) @ np.asarray(q_group, float).T).sum(axis=1)
+def mutant_module(edits=(), funcs=None, name="clo_oracle_mutant"):
+    """A copy of the oracle with text edits [(old, new), ...] and function replacements."""
+    src = SRC
+    for old, new in edits:
+        n = src.count(old)
+        assert n == 1, f"mutation site {old!r} occurs {n} times in {os.path.basename(SRC_PATH)}"
+        src = src.replace(old, new)
+    mod = types.ModuleType(name)
+    mod.__file__ = SRC_PATH
+    exec(compile(src, f"<{name}>", "exec"), mod.__dict__)
+    for fname, f in (funcs or {}).items():
+        assert hasattr(mod, fname), fname
+        setattr(mod, fname, f)
+    return mod
 
 
 def m_mean_head_cosine(a, b):
     a, b = np.asarray(a, float), np.asarray(b, float)
-    cs = [base.group_cosine(a[i:i + 1], b[i:i + 1]) for i in range(a.shape[0])]
-    return float(np.mean(cs))
+    return float(np.mean([base.group_cosine(a[i:i + 1], b[i:i + 1]) for i in range(a.shape[0])]))
 
 
-def m_strict_reuse(c, tau):
-    return bool(c > tau)
-
-
-def m_no_scale(q_group, Kc, Vc, return_p=False):
-    q = np.asarray(q_group, float)
-    return base.attend(q * math.sqrt(q.shape[1]), Kc, Vc, return_p)
-
-
-def m_softmax_wrong_axis(q_group, Kc, Vc, return_p=False):
-    q, Kc, Vc = (np.asarray(x, float) for x in (q_group, Kc, Vc))
-    lg = (Kc @ q.T) / math.sqrt(q.shape[1])
-    e = np.exp(lg - lg.max(axis=1, keepdims=True))
-    p = e / e.sum(axis=1, keepdims=True)
-    out = p.T @ Vc
-    return (out, p.T) if return_p else out
-
-
-def m_values_from_keys(q_group, Kc, Vc, return_p=False):
-    return base.attend(q_group, Kc, Kc, return_p)
-
-
-def m_ties_to_larger_index(s, k):
-    s = np.asarray(s, float)
-    n = s.shape[0]
-    order = np.lexsort((-np.arange(n), -s))
-    return np.sort(order[:k])
-
-
-def m_unsorted_topk(s, k):
-    return np.argsort(-np.asarray(s, float), kind="stable")[:k]
-
-
-def m_smallest_k(s, k):
-    return base.select_topk(-np.asarray(s, float), k)
-
-
-def m_head_modulo(h, g, hkv, hq):
-    return [x for x in range(hq) if x % hkv == h]
-
-
-def m_bf16_low_half(a, dtype):
-    if dtype == "bf16":
-        return np.asarray(a, np.uint16).astype(np.float64)
-    return base.as_f64(a, dtype)
-
-
-def m_cos_no_prev_norm(a, b):
-    a, b = np.asarray(a, float).reshape(-1), np.asarray(b, float).reshape(-1)
-    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(a)))
-
-
-def m_plan_highest_first(s_hat, n):
-    return base.plan_persistent(-np.asarray(s_hat, float), n)
-
-
-def m_plan_ties_to_higher_index(s_hat, n):
-    s = np.asarray(s_hat, float)
-    L, H = s.shape
-    order = sorted(range(L * H), key=lambda i: (s.reshape(-1)[i], -i))
-    masks = [0] * L
-    for i in order[:n]:
-        masks[i // H] |= 1 << (i % H)
-    return masks
-
-
-def m_quant_floor(x):
-    q, e = base.quantize_row(x)
-    return np.floor(np.asarray(x, float) * 2.0 ** -e).astype(np.int64), e
-
-
-def m_quant_exponent_low(x):
-    q, e = base.quantize_row(x)
-    e -= 1
-    return np.clip(np.rint(np.asarray(x, float) * 2.0 ** -e), -127, 127).astype(np.int64), e
-
-
-def m_quant_half_away(x):
-    q, e = base.quantize_row(x)
-    y = np.asarray(x, float) * 2.0 ** -e
-    return (np.sign(y) * np.floor(np.abs(y) + 0.5)).astype(np.int64), e
-
-
-def m_blocks_sum(s, k, bs):
-    s = np.asarray(s, float)
-    nb = s.shape[0] // bs
-    bsum = s[:nb * bs].reshape(nb, bs).sum(axis=1)
-    blocks = np.sort(base.select_topk(bsum, k // bs))
-    return (blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
-
-
-def m_blocks_tail_selectable(s, k, bs):
-    s = np.asarray(s, float)
-    nb = -(-s.shape[0] // bs)
-    pad = np.concatenate([s, np.full(nb * bs - s.shape[0], -np.inf)])
-    bmax = pad.reshape(nb, bs).max(axis=1)
-    blocks = np.sort(base.select_topk(bmax, k // bs))
-    out = (blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
-    return out
-
-
-def m_blocks_ties_high(s, k, bs):
-    s = np.asarray(s, float)
-    nb = s.shape[0] // bs
-    bmax = s[:nb * bs].reshape(nb, bs).max(axis=1)
-    order = np.lexsort((-np.arange(nb), -bmax))[:k // bs]
-    blocks = np.sort(order)
-    return (blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
-
+E = lambda old, new: dict(edits=[(old, new)])  # noqa: E731
 
 MUTANTS = {
-    "score_sum_over_heads": dict(token_scores=m_sum_over_heads),
-    "cosine_mean_of_heads": dict(group_cosine=m_mean_head_cosine),
-    "cosine_wrong_norm": dict(group_cosine=m_cos_no_prev_norm),
-    "reuse_strict": dict(reuse_decision=m_strict_reuse),
-    "attention_no_scale": dict(attend=m_no_scale),
-    "softmax_over_heads": dict(attend=m_softmax_wrong_axis),
-    "values_from_keys": dict(attend=m_values_from_keys),
-    "ties_to_larger_index": dict(select_topk=m_ties_to_larger_index),
-    "topk_unsorted": dict(select_topk=m_unsorted_topk),
-    "topk_smallest": dict(select_topk=m_smallest_k),
-    "gqa_head_modulo": dict(head_of=m_head_modulo),
-    "bf16_decoded_as_int": dict(as_f64=m_bf16_low_half),
+    # reuse test
+    "cosine_mean_of_heads": dict(funcs=dict(group_cosine=m_mean_head_cosine)),
+    "cosine_wrong_norm": E("nb = math.sqrt(float(np.sum(b * b)))", "nb = math.sqrt(float(np.sum(a * a)))"),
+    "reuse_strict": E("return bool(c >= tau)", "return bool(c > tau)"),
+    # scoring and top-k
+    "score_sum_over_heads": E("return per_head.max(axis=1)", "return per_head.sum(axis=1)"),
+    "ties_to_larger_index": E('order = np.argsort(-s, kind="stable")',
+                              'order = s.shape[0] - 1 - np.argsort(-s[::-1], kind="stable")'),
+    "topk_unsorted": E("return np.sort(order[:k]).astype(np.int64)", "return order[:k].astype(np.int64)"),
+    "topk_smallest": E('order = np.argsort(-s, kind="stable")', 'order = np.argsort(s, kind="stable")'),
+    # attention
+    "attention_no_scale": E("logits = (Kc @ q.T) / math.sqrt(d)", "logits = Kc @ q.T"),
+    "softmax_over_heads": dict(edits=[("m = logits.max(axis=0, keepdims=True)", "m = logits.max(axis=1, keepdims=True)"),
+                                      ("p = e / e.sum(axis=0, keepdims=True)", "p = e / e.sum(axis=1, keepdims=True)")]),
+    "values_from_keys": E("out = p.T @ Vc", "out = p.T @ Kc"),
+    # bf16 decoding
+    "bf16_decoded_as_int": E("return (bits * np.uint32(65536)).view(np.float32).astype(np.float64)",
+                             "return bits.astype(np.float64)"),
+    # one unit: rows attention reads apart from the scored keys, block selection
+    "attend_scored_keys": E("Kc = np.asarray(K if K_attn is None else K_attn, dtype=np.float64)[sel]",
+                            "Kc = np.asarray(K, dtype=np.float64)[sel]"),
+    "attend_exact_values": E("Vc = np.asarray(V if V_attn is None else V_attn, dtype=np.float64)[sel]",
+                             "Vc = np.asarray(V, dtype=np.float64)[sel]"),
+    "score_attention_rows": E("s = token_scores(q_group, K)", "s = token_scores(q_group, K if K_attn is None else K_attn)"),
+    "unit_ignores_block_size": E("sel = select_topk(s, k) if block_size <= 1 else select_blocks(s, k, block_size)",
+                                 "sel = select_topk(s, k)"),
+    # one layer: GQA grouping, thresholds, previous selections, routing of the unit's arguments
+    "gqa_head_modulo": E("decode_unit(qf[b, kvh * g:(kvh + 1) * g], qpf[b, kvh * g:(kvh + 1) * g],",
+                         "decode_unit(qf[b, kvh::hkv], qpf[b, kvh::hkv],"),
+    "tau_heads_ignored": E("tau_u = float(tau[kvh]) if np.ndim(tau) else float(tau)", "tau_u = float(np.max(tau))"),
+    "tau_heads_reversed": E("tau_u = float(tau[kvh]) if np.ndim(tau) else float(tau)",
+                            "tau_u = float(tau[::-1][kvh]) if np.ndim(tau) else float(tau)"),
+    "previous_selection_of_head_0": E("prev = None if idx_prev is None else idx_prev[b, kvh]",
+                                      "prev = None if idx_prev is None else idx_prev[b, 0]"),
+    "layer_ignores_attention_rows": E("ka = attn_kv_of(b, kvh) if attn_kv_of else None", "ka = None"),
+    "layer_ignores_block_size": E("*(ka if ka is not None else (None, None)), block_size=block_size)",
+                                  "*(ka if ka is not None else (None, None)))"),
+    # persistent-head planning
+    "plan_highest_similarity": E("key=lambda i: (s.reshape(-1)[i], i)", "key=lambda i: (-s.reshape(-1)[i], i)"),
+    "plan_ties_to_higher_index": E("key=lambda i: (s.reshape(-1)[i], i)", "key=lambda i: (s.reshape(-1)[i], -i)"),
+    # int8 rows
+    "quant_floor": E("q = np.rint(x * 2.0 ** -e).astype(np.int64)", "q = np.floor(x * 2.0 ** -e).astype(np.int64)"),
+    "quant_exponent_low": E("e = max(e, QUANT_MIN_EXP)", "e = max(e, QUANT_MIN_EXP) - 1"),
+    "quant_ties_away": E("q = np.rint(x * 2.0 ** -e).astype(np.int64)",
+                         "q = (np.sign(x) * np.floor(np.abs(x * 2.0 ** -e) + 0.5)).astype(np.int64)"),
+    "dequant_wrong_sign_exponent": E("return np.asarray(q, dtype=np.float64) * 2.0 ** e",
+                                     "return np.asarray(q, dtype=np.float64) * 2.0 ** -e"),
+    "quantized_rows_by_column": E("    for i in range(X.shape[0]):\n        out[i] = dequantize_row(*quantize_row(X[i]))",
+                                  "    for i in range(X.shape[1]):\n        out[:, i] = dequantize_row(*quantize_row(X[:, i]))"),
+    # block selection
+    "blocks_scored_by_sum": E("bscore = s[:nb * block_size].reshape(nb, block_size).max(axis=1)",
+                              "bscore = s[:nb * block_size].reshape(nb, block_size).sum(axis=1)"),
+    "blocks_tail_selectable": dict(edits=[
+        ("nb = s.shape[0] // block_size", "nb = -(-s.shape[0] // block_size)"),
+        ("bscore = s[:nb * block_size].reshape(nb, block_size).max(axis=1)",
+         "bscore = np.concatenate([s, np.full(nb * block_size - s.shape[0], -np.inf)]).reshape(nb, block_size).max(axis=1)")]),
+    "blocks_ties_to_higher": E("blocks = np.sort(select_topk(bscore, k // block_size))",
+                               "blocks = np.sort(nb - 1 - select_topk(bscore[::-1], k // block_size))"),
     # many steps: the context does not grow, grows one step late, or the
     # reference is kept / replaced at the wrong steps
-    "tau_heads_ignored": dict(tau_of=lambda tau, h: float(np.max(tau)) if np.ndim(tau) else float(tau)),
-    "tau_heads_reversed": dict(tau_of=lambda tau, h: float(tau[::-1][h]) if np.ndim(tau) else float(tau)),
-    "plan_highest_similarity": dict(plan_persistent=m_plan_highest_first),
-    "plan_ties_to_higher_index": dict(plan_persistent=m_plan_ties_to_higher_index),
-    "quant_floor": dict(quantize_row=m_quant_floor),
-    "quant_exponent_low": dict(quantize_row=m_quant_exponent_low),
-    "quant_ties_away": dict(quantize_row=m_quant_half_away),
-    "dequant_wrong_sign_exponent": dict(dequantize_row=lambda q, e: np.asarray(q, float) * 2.0 ** -e),
-    "blocks_scored_by_sum": dict(select_blocks=m_blocks_sum),
-    "blocks_tail_selectable": dict(select_blocks=m_blocks_tail_selectable),
-    "blocks_ties_to_higher": dict(select_blocks=m_blocks_ties_high),
-    "steps_context_fixed": dict(steps_kw=dict(grow=0)),
-    "steps_context_one_late": dict(steps_kw=dict(lag=1)),
-    "steps_refresh_never_updates": dict(steps_kw=dict(rules={"refresh": "never"})),
-    "steps_refresh_as_previous": dict(steps_kw=dict(rules={"refresh": "previous"})),
-    "steps_previous_as_refresh": dict(steps_kw=dict(rules={"previous": "refresh"})),
+    "steps_context_fixed": E("n = n0 + t", "n = n0"),
+    "steps_context_one_late": E("n = n0 + t", "n = n0 + max(t - 1, 0)"),
+    "steps_refresh_never_updates": E('if policy == "previous" or not r["reuse"]:', 'if policy == "previous" or t == 0:'),
+    "steps_refresh_as_previous": E('if policy == "previous" or not r["reuse"]:', "if True:"),
+    "steps_previous_as_refresh": E('if policy == "previous" or not r["reuse"]:', 'if not r["reuse"]:'),
 }
 
 
-def test_unmutated_namespace_passes():
-    ns = _ns()
+def test_unmutated_copy_passes():
+    mod = mutant_module()
     for pin in ALL_PINS:
-        pin(ns)
+        pin(mod)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name):
-    ns = _ns(**MUTANTS[name])
+    mod = mutant_module(name=f"mutant_{name}", **MUTANTS[name])
     failed = []
     for pin in ALL_PINS:
         try:
-            pin(ns)
+            pin(mod)
         except Exception:
             failed.append(pin.__name__)
     assert failed, f"mutant {name} passed every pin"

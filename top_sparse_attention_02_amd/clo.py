@@ -160,6 +160,9 @@ class Shape:
     def c(self) -> clo_shape:
         th = None
         if self.tau_heads is not None:
+            if len(self.tau_heads) != self.n_kv_heads:
+                # the library reads exactly n_kv_heads thresholds from the array
+                raise ValueError(f"tau_heads has {len(self.tau_heads)} entries, n_kv_heads is {self.n_kv_heads}")
             th = (ctypes.c_float * len(self.tau_heads))(*[float(x) for x in self.tau_heads])
         cs = clo_shape(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.context, self.topk,
                        self.tau, self.dtype, self.capacity,
