@@ -88,7 +88,9 @@ typedef enum {
   CLO_E_UNSUPPORTED = 2,  /* valid but unsupported: head_dim != 128, dtype, group size > 8 */
   CLO_E_WORKSPACE = 3,    /* workspace missing or smaller than clo_workspace_size() */
   CLO_E_HIP = 4,          /* the HIP runtime reported an error at launch */
-  CLO_E_TIMEOUT = 5       /* written to clo_sync.error_word when a device-side wait gives up */
+  CLO_E_TIMEOUT = 5,      /* written to clo_sync.error_word when a device-side wait gives up */
+  CLO_E_INDEX = 6         /* written to clo_sync.error_word when a kernel meets a selected index
+                             outside 0..context-1 (the read is clamped into range) */
 } clo_status;
 
 /* Problem shape of one layer. */
@@ -152,6 +154,14 @@ typedef struct {
  *                             NULL) and continues.
  *   signal_flag/signal_value  after its last kernel, the call stores
  *                             signal_value to *signal_flag (release, agent scope).
+ *   error_word                asynchronous errors of the call's kernels: a
+ *                             timed-out wait (CLO_E_TIMEOUT) or a selected index
+ *                             outside 0..context-1 met by the gather or by
+ *                             attention over persistent heads (CLO_E_INDEX; the
+ *                             kernel reads the nearest row in range instead and
+ *                             finishes normally).  Only a zero word is written,
+ *                             so the first error stays; the caller clears it.
+ *                             NULL = such errors are not reported.
  */
 typedef struct {
   const uint32_t* wait_flag;
@@ -206,7 +216,9 @@ clo_status clo_reuse_select(const clo_shape* shape, const clo_layer* layer, cons
  * For every miss unit of a non-persistent head: k_cache[u][i] = k_host[u][idx[u][i]]
  * and v_cache[u][i] = v_host[u][idx[u][i]], read by the GPU directly from pinned
  * host memory (bit-exact copies; with CLO_HOST_INT8 the rows are dequantized
- * exactly, q_i * 2^e, on the way into the cache).  Persistent heads need no transfer: attention
+ * exactly, q_i * 2^e, on the way into the cache).  An idx entry outside
+ * 0..context-1 (a corrupt caller selection) is reported as CLO_E_INDEX in
+ * sync->error_word and the row nearest to it is copied.  Persistent heads need no transfer: attention
  * reads their rows in place.  reuse NULL = all units miss.  ws: device workspace
  * as for clo_topk_select (the gather's blocks take work from a counter in it;
  * calls that share one workspace must not overlap).  sync may be NULL.
@@ -219,7 +231,9 @@ clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const u
  * table).  For query head h of unit u: l_i = q_h . K_sel_i / sqrt(d),
  * p = softmax(l), out_h = sum_i p_i V_sel_i, accumulated in fp32 and rounded
  * to dtype.  Rows come from k_cache/v_cache (non-persistent heads) or from
- * k_hbm/v_hbm at idx (persistent heads).  ws as for clo_topk_select.
+ * k_hbm/v_hbm at idx (persistent heads; an index outside 0..context-1 is
+ * reported as CLO_E_INDEX in sync->error_word and the nearest row is read).
+ * ws as for clo_topk_select.
  */
 clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const void* q, void* out,
                            void* ws, size_t ws_bytes, const clo_sync* sync, void* stream);

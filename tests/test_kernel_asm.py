@@ -75,3 +75,11 @@ def test_every_barrier_after_an_lds_write_waits_for_it(asm_text):
 def test_no_packed_fp32_instructions(asm_text):
     found = re.findall(r"^\s*(v_pk_(?:add|mul|fma|mov)_f32)\b", asm_text, re.M)
     assert not found, sorted(set(found))
+
+
+def test_no_scalar_memory_writes(asm_text):
+    # every store and atomic of the kernels goes through the vector memory path:
+    # nothing writes through the scalar data cache (no scalar stores or atomics,
+    # and no write-back or discard of that cache)
+    found = re.findall(r"^\s*(s_(?:buffer_|scratch_)?(?:store|atomic)\w*|s_dcache_(?:wb|discard)\w*)\b", asm_text, re.M)
+    assert not found, sorted(set(found))

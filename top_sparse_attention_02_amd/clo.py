@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libclo.so")
 
 CLO_F32, CLO_BF16 = 0, 1
 CLO_HOST_NATIVE, CLO_HOST_INT8 = 0, 1
-CLO_OK, CLO_E_ARG, CLO_E_UNSUPPORTED, CLO_E_WORKSPACE, CLO_E_HIP, CLO_E_TIMEOUT = range(6)
+CLO_OK, CLO_E_ARG, CLO_E_UNSUPPORTED, CLO_E_WORKSPACE, CLO_E_HIP, CLO_E_TIMEOUT, CLO_E_INDEX = range(7)
 
 # every function include/clo.h declares
 EXPORTS = ("clo_workspace_size", "clo_reuse_test", "clo_topk_select", "clo_reuse_select", "clo_gather_kv",

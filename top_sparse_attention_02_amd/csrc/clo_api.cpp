@@ -508,6 +508,7 @@ clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const u
   }
   Workspace w;
   if ((st = check_layer(layer, &p, NEED_IDX | NEED_HOST | NEED_CACHE))) return st;
+  p.a.err = sync ? sync->error_word : nullptr;
   if (reuse && (st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
   uint32_t* counter = reinterpret_cast<uint32_t*>(w.meta + kMetaGather);
@@ -532,6 +533,7 @@ clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const
   }
   Workspace w;
   if ((st = check_layer(layer, &p, NEED_IDX | NEED_CACHE | NEED_HBM_KV))) return st;
+  p.a.err = sync ? sync->error_word : nullptr;
   if ((st = check_device(q, q_bytes(p), "q"))) return st;
   if ((st = check_device(out, q_bytes(p), "out"))) return st;
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
@@ -638,6 +640,7 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
   }
   Workspace w;
   if ((st = check_layer(layer, &p, NEED_IDX | NEED_SCORE | NEED_HOST | NEED_CACHE | NEED_HBM_KV))) return st;
+  p.a.err = sync ? sync->error_word : nullptr;
   if ((st = check_device(q, q_bytes(p), "q"))) return st;
   if ((st = check_device(q_prev, q_bytes(p), "q_prev"))) return st;
   if ((st = check_device(out, q_bytes(p), "out"))) return st;
@@ -766,6 +769,7 @@ const char* clo_status_string(clo_status status) {
     case CLO_E_WORKSPACE: return "workspace missing or too small";
     case CLO_E_HIP: return "HIP runtime error";
     case CLO_E_TIMEOUT: return "device-side wait timed out";
+    case CLO_E_INDEX: return "selected index out of range";
   }
   return "unknown status";
 }

@@ -72,6 +72,7 @@ struct LayerArgs {
   int32_t host_fmt;      // CLO_HOST_NATIVE or CLO_HOST_INT8
   const int8_t* k_exp;   // CLO_HOST_INT8: [B, H, C] row exponents of k_host / v_host
   const int8_t* v_exp;
+  uint32_t* err;         // device error word for selected indices out of range (may be NULL)
 };
 
 constexpr int kQuantMinExp = -120;  // smallest row exponent of the int8 host format

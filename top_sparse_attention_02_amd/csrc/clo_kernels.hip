@@ -104,6 +104,15 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// A selected index outside [0, N) -- a corrupt caller selection -- is read as
+// the nearest row in range (no access leaves the unit's rows) and reported
+// once in the caller's error word, the first error staying.
+__device__ __forceinline__ int64_t checked_row(int64_t r, int64_t N, uint32_t* err) {
+  if (r >= 0 && r < N) return r;
+  if (err) atomicCAS(err, 0u, (uint32_t)CLO_E_INDEX);
+  return r < 0 ? 0 : N - 1;
+}
+
 // Rank of KV head h among the heads of its kind (persistent or not), in head order.
 __device__ __forceinline__ int head_slot(uint64_t pmask, int h) {
   const uint64_t below = pmask & ((1ull << h) - 1ull);
@@ -1132,7 +1141,7 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
   constexpr int UNR = kGatherUnroll;
   static_assert(kGatherChunk == 256, "one index per thread");
   __shared__ uint32_t s_item;
-  __shared__ int32_t s_src[kGatherChunk];  // the item's source rows, clamped into [0, N)
+  __shared__ int32_t s_src[kGatherChunk];  // the item's source rows (checked_row)
   __shared__ int32_t s_units[kGatherListCap];
   __shared__ uint32_t s_wcnt[4];
   const int nch = (int)((a.k + kGatherChunk - 1) / kGatherChunk);
@@ -1163,10 +1172,7 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
     const int64_t r_end = (r0 + kGatherChunk < a.k) ? r0 + kGatherChunk : a.k;
     // the item's indices in one coalesced load, so that the host reads below
     // do not wait on an index load each time
-    if (r0 + threadIdx.x < r_end) {
-      const int32_t src = ix[r0 + threadIdx.x];
-      s_src[threadIdx.x] = src < 0 ? 0 : (src >= a.N ? (int32_t)(a.N - 1) : src);
-    }
+    if (r0 + threadIdx.x < r_end) s_src[threadIdx.x] = (int32_t)checked_row(ix[r0 + threadIdx.x], a.N, a.err);
     __syncthreads();
     for (int64_t rb = r0; rb < r_end; rb += RPI * UNR) {
       // rows past the end re-read the last row (in bounds) and are not stored
@@ -1269,8 +1275,7 @@ __global__ __launch_bounds__(256) void gather_q8_kernel(LayerArgs a, const uint8
     const int64_t r0 = (int64_t)c * kGatherChunk;
     const int64_t r_end = (r0 + kGatherChunk < a.k) ? r0 + kGatherChunk : a.k;
     if (r0 + threadIdx.x < r_end) {
-      int32_t src = ix[r0 + threadIdx.x];
-      src = src < 0 ? 0 : (src >= a.N ? (int32_t)(a.N - 1) : src);
+      const int32_t src = (int32_t)checked_row(ix[r0 + threadIdx.x], a.N, a.err);
       s_src[threadIdx.x] = src;
       s_sc[0][threadIdx.x] = pow2f(a.k_exp[slot * a.C + src]);
       s_sc[1][threadIdx.x] = pow2f(a.v_exp[slot * a.C + src]);
@@ -1423,11 +1428,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
     vbase = static_cast<const T*>(a.v_cache) + s;
   }
   // row of the source tensor holding selected row i (< nrows) of this chunk
-  auto row_of = [&](int i) -> int64_t {
-    if (!pers) return i;
-    int64_t r = ix[i];
-    return r < 0 ? 0 : (r >= a.N ? a.N - 1 : r);
-  };
+  auto row_of = [&](int i) -> int64_t { return pers ? checked_row(ix[i], a.N, a.err) : (int64_t)i; };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane & 15, rg = lane >> 4;
   const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
