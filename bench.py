@@ -234,23 +234,48 @@ def probe_host_link(torch, nbytes=1 << 30):
     return res
 
 
-def cpu_baseline(p, layers, budget_s, step_kind, one_thread=False):
-    """The CPU oracle, as it is, on a bounded sample of the step's units, scaled to steps/s.
+def host_cpu_info():
+    """CPUs this process may run on, and the CPU model from /proc/cpuinfo."""
+    try:
+        cpus = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        cpus = os.cpu_count() or 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cpus, model
 
-    Inputs are the generated ones only: the oracle classifies units with its own
-    cosine test and, for a reused unit, first makes its own previous selection
-    (untimed) from q_prev.  one_thread: also time a second sample with the BLAS
-    pool limited to one thread (the small workloads)."""
+
+def cpu_baseline(p, layers, budget_s, step_kind, full_step: bool, one_thread=False):
+    """The CPU oracle, as it is, timed on the machine's host cores.
+
+    Units run in parallel on a pool of worker threads (one per core of the
+    process's CPU share, at most 16), each with a one-thread BLAS, so the
+    oracle's matrix products and sorts of different units overlap.  Inputs are
+    the generated ones only: the oracle classifies units with its own cosine
+    test, and for a reused unit first makes its own previous selection from
+    q_prev (untimed, before the timed region).  full_step: the whole step's
+    units, timed three times, median (single-layer workloads); otherwise a
+    bounded sample of miss and reuse units in the step's proportions, scaled
+    to the step.  one_thread: the same with a single worker."""
+    import concurrent.futures as cf
+
     import numpy as np
 
     import oracle
 
     try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    cpus, model = host_cpu_info()
+    workers = max(1, min(cpus, 16))
     g = p.g
     tau = p.tau if step_kind == 1 else math.inf
     miss_u, hit_u = [], []
@@ -263,59 +288,96 @@ def cpu_baseline(p, layers, budget_s, step_kind, one_thread=False):
             for h in range(p.hkv):
                 c = oracle.group_cosine(query[b, h * g:(h + 1) * g], qpf[b, h * g:(h + 1) * g])
                 (hit_u if oracle.reuse_decision(c, tau) else miss_u).append((l, b, h))
-    # sample evenly over the step
-    rng = np.random.default_rng(0)
-    miss_s = [miss_u[i] for i in rng.permutation(len(miss_u))]
-    hit_s = [hit_u[i] for i in rng.permutation(len(hit_u))]
+
+    hit_set = set(hit_u)
+
+    stored = {}  # persistent heads' K/V, generated again before the timed passes
 
     def kv_stored(l, b, h):
         bufs = layers[l]
         if bufs.is_persistent(h):
-            return p.kv("k", l, b, h), p.kv("v", l, b, h)
+            return stored[(l, b, h)]
         return bufs.host_view("k", b, h), bufs.host_view("v", b, h)
 
-    def run(u, reused):
+    def groups(u):
         l, b, h = u
-        K, V = kv_stored(l, b, h)
         query, qpf = qs[l]
-        qg, qpg = query[b, h * g:(h + 1) * g], qpf[b, h * g:(h + 1) * g]
-        prev = None
-        if reused:  # the previous step's selection, made by the oracle itself (untimed)
-            prev = oracle.select_topk(oracle.token_scores(qpg, oracle.as_f64(K, p.dtype)), p.topk)
-        t = time.perf_counter()
+        return query[b, h * g:(h + 1) * g], qpf[b, h * g:(h + 1) * g]
+
+    def prev_selection(u):
+        K, _ = kv_stored(*u)
+        return oracle.select_topk(oracle.token_scores(groups(u)[1], oracle.as_f64(K, p.dtype)), p.topk)
+
+    def unit(u, prev):
+        K, V = kv_stored(*u)
+        qg, qpg = groups(u)
         oracle.decode_unit(qg, qpg, oracle.as_f64(K, p.dtype), oracle.as_f64(V, p.dtype), p.topk, tau, prev)
+
+    def run(units, prevs, nworkers):
+        """Wall seconds of the oracle over `units` on nworkers threads."""
+        t = time.perf_counter()
+        with cf.ThreadPoolExecutor(max_workers=nworkers) as ex:
+            list(ex.map(lambda u: unit(u, prevs.get(u)), units))
         return time.perf_counter() - t
 
-    def sample(budget):
-        t_miss, t_hit = [], []
-        spent = 0.0
-        i = 0
-        while spent < budget and (i < len(miss_s) or i < len(hit_s)):
-            if i < len(miss_s):
-                t_miss.append(run(miss_s[i], False))
-                spent += t_miss[-1]
-            if i < len(hit_s):
-                t_hit.append(run(hit_s[i], True))
-                spent += t_hit[-1]
-            i += 1
-        est = (np.mean(t_miss) if t_miss else 0.0) * len(miss_u) + (np.mean(t_hit) if t_hit else 0.0) * len(hit_u)
-        return est, len(t_miss), len(t_hit), spent
+    def prevs_of(units, nworkers):
+        """Untimed preparation: the inputs of persistent heads (from the generator;
+        non-persistent heads are read in place from pinned memory) and each reuse
+        unit's previous selection."""
+        for u in units:
+            l, b, h = u
+            if layers[l].is_persistent(h) and u not in stored:
+                stored[u] = (p.kv("k", l, b, h), p.kv("v", l, b, h))
+        hits = [u for u in units if u in hit_set]
+        with cf.ThreadPoolExecutor(max_workers=nworkers) as ex:
+            return dict(zip(hits, ex.map(prev_selection, hits)))
 
-    est, n_miss, n_hit, spent = sample(budget_s)
-    out = {"value": round(1.0 / est, 6) if est > 0 else None, "unit": "steps/s", "cores": threads, "kind": "oracle",
-           "sample": f"{n_miss} miss + {n_hit} reuse units of the {len(miss_u) + len(hit_u)}-unit step "
-                     f"({spent:.1f} s of oracle time), fp64 numpy oracle, per-unit mean times scaled to the "
-                     f"step's {len(miss_u)} miss / {len(hit_u)} reuse units",
-           "seconds_per_step_est": round(est, 3)}
-    if one_thread:
-        try:
-            from threadpoolctl import threadpool_limits
-        except ImportError:
-            return out
+    def measure(nworkers, budget):
+        """(seconds per step, miss units timed, reuse units timed)."""
+        if full_step:
+            units = miss_u + hit_u
+            prevs = prevs_of(units, nworkers)
+            return float(np.median([run(units, prevs, nworkers) for _ in range(3)])), len(miss_u), len(hit_u)
+        # per class, a sample sized for about budget / 6 seconds per pass; its
+        # median wall time over 3 passes per unit, times the class's units
+        rng = np.random.default_rng(0)
+        est, counts = 0.0, []
+        for us in (miss_u, hit_u):
+            if not us:
+                counts.append(0)
+                continue
+            one = [us[0]]
+            t1 = run(one, prevs_of(one, 1), 1)
+            n = int(min(len(us), max(nworkers, budget / 6 / max(t1, 1e-4) * nworkers)))
+            sample = [us[i] for i in rng.permutation(len(us))[:n]]
+            prevs = prevs_of(sample, nworkers)
+            wall = float(np.median([run(sample, prevs, nworkers) for _ in range(3)]))
+            est += wall / n * len(us)
+            counts.append(n)
+        return est, counts[0], counts[1]
+
+    def limited(fn, *a):
+        if threadpool_limits is None:
+            return fn(*a)
         with threadpool_limits(limits=1):
-            est1, n_miss1, n_hit1, spent1 = sample(budget_s / 2)
+            return fn(*a)
+
+    est, n_m, n_h = limited(measure, workers, budget_s)
+    total = len(miss_u) + len(hit_u)
+    what = (f"the whole step ({len(miss_u)} miss + {len(hit_u)} reuse units), median of 3" if full_step else
+            f"samples of {n_m} miss and {n_h} reuse units of the {total}-unit step (median of 3 passes each), "
+            f"per-unit wall times scaled to the step's {len(miss_u)} miss / {len(hit_u)} reuse units")
+    out = {"value": round(1.0 / est, 6) if est > 0 else None, "unit": "steps/s", "cores": workers,
+           "kind": "oracle",
+           "sample": f"{what}; fp64 numpy oracle unchanged, units in parallel on {workers} worker threads with "
+                     f"a one-thread BLAS each; each reuse unit's previous selection made by the oracle first, "
+                     f"untimed",
+           "seconds_per_step": round(est, 4), "host_cpus": cpus, "cpu_model": model, "blas_threads_per_worker": 1,
+           "full_step": full_step}
+    if one_thread:
+        est1, _, _ = limited(measure, 1, budget_s / 2)
         out["value_1thread"] = round(1.0 / est1, 6) if est1 > 0 else None
-        out["sample_1thread"] = f"{n_miss1} miss + {n_hit1} reuse units ({spent1:.1f} s), BLAS limited to 1 thread"
+        out["sample_1thread"] = "the same on one worker thread (one-thread BLAS)"
     return out
 
 
@@ -538,7 +600,7 @@ def main():
         return
     overrides = {}
     if args.config in (4, 5):
-        overrides["data_layers"] = args.data_layers or (8 if args.config == 4 else 16)
+        overrides["data_layers"] = args.data_layers or 16
     if args.volatile:
         overrides["volatile_frac"] = args.volatile
     if args.block_size > 1:
@@ -615,8 +677,12 @@ def main():
     for _ in range(args.steps):
         step()
     e1.record()
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    # host time to enqueue one step (validation and launches); the GPU side is
+    # the limit while this stays below ms_per_step
+    enqueue_us = (t_enq - t_wall) / args.steps * 1e6
     # a second pass of K steps with an event after every step, for the per-step
     # median and minimum (kept out of the timed region above: at tens of
     # microseconds per step the extra events would show in it)
@@ -674,6 +740,21 @@ def main():
             roofline["peak_measured"] = round(hbm_probe["read_gbs"], 1)
             roofline["frac_measured"] = round(attn_gbs / hbm_probe["read_gbs"], 4)
 
+    # the step's lower bounds from its algorithmic bytes: the host link at the
+    # rate measured in this run, HBM at the published peak and at the measured
+    # read ceiling; the step can overlap the two, so its bound is the larger
+    host_bound_ms = alg["host_bytes"] / (probe["h_meas_gbs"] * 1e9) * 1e3 if probe else None
+    hbm_bound_ms = alg["hbm_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e3
+    hbm_bound_meas_ms = alg["hbm_bytes"] / (hbm_probe["read_gbs"] * 1e9) * 1e3 if hbm_probe else None
+    step_bound_ms = max(x for x in (host_bound_ms, hbm_bound_meas_ms or hbm_bound_ms) if x is not None)
+    bounds = {"host_bytes": alg["host_bytes"], "hbm_bytes": alg["hbm_bytes"],
+              "host_bound_ms": round(host_bound_ms, 4) if host_bound_ms is not None else None,
+              "hbm_bound_ms_at_peak": round(hbm_bound_ms, 4),
+              "hbm_bound_ms_at_read_ceiling": round(hbm_bound_meas_ms, 4) if hbm_bound_meas_ms else None,
+              "step_bound_ms": round(step_bound_ms, 4),
+              "frac_of_step_bound": round(step_bound_ms / ms_per_step, 4),
+              "host_enqueue_us_per_step": round(enqueue_us, 2)}
+
     result = {
         "metric": METRIC,
         "value": round(1.0 / step_s, 3),
@@ -700,6 +781,9 @@ def main():
                    "data_layers": p.data_layers or p.layers, "host_memory": args.host_memory,
                    **({"graph": True} if args.graph else {}),
                    **({"select_streams": args.select_streams} if multi else {})},
+        "host_bound_ms": bounds["host_bound_ms"],
+        "frac_of_host_bound": round(host_bound_ms / ms_per_step, 4) if host_bound_ms else None,
+        "bounds": bounds,
         "roofline": roofline,
         "persistent_plan": None if plan is None else {k: v for k, v in plan.items() if k != "persistent"},
         "block_size": args.block_size or 1,
@@ -723,8 +807,13 @@ def main():
         result["layer_steps_per_s"] = round(p.layers / step_s, 2)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of units")
-        result["cpu_baseline"] = cpu_baseline(p, layers, args.cpu_sample_seconds, args.step,
-                                              one_thread=args.config in (1, 2))
+        if args.host_kv != "native":
+            # the oracle reads stored rows of the step's dtype; the int8 host copy
+            # holds none, so the native-format baseline is the one to compare with
+            result["cpu_baseline"] = None
+        else:
+            result["cpu_baseline"] = cpu_baseline(p, layers, args.cpu_sample_seconds, args.step,
+                                                  full_step=not multi, one_thread=args.config in (1, 2))
     print(json.dumps(result), flush=True)
 
 

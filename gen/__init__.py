@@ -63,6 +63,7 @@ def lib():
         L.gen_u64_fill.argtypes = [vp, i64, u64, i64]
         L.gen_uniform_f64.argtypes = [vp, i64, u64, i64]
         L.gen_normal_f64.argtypes = [vp, i64, u64, i64]
+        L.gen_normal_rows.argtypes = [vp, vp, vp, i64, i64]
         L.gen_fill_rows.argtypes = [vp, i64, i64, u64, vp, ctypes.c_int, ctypes.c_int]
         L.gen_round.argtypes = [vp, vp, i64, ctypes.c_int]
         L.gen_copy.argtypes = [vp, vp, i64, ctypes.c_int]
@@ -387,9 +388,9 @@ class Problem:
                     one[:] = round_to(vals, self.dtype)
                     ctypes.memmove(out_ptr + row * self.d * eb, one.ctypes.data, self.d * eb)
 
-    def kv(self, which: str, layer: int, b: int, kvh: int) -> np.ndarray:
+    def kv(self, which: str, layer: int, b: int, kvh: int, threads: Optional[int] = None) -> np.ndarray:
         out = np.empty((self.context, self.d), dtype=storage_dtype(self.dtype))
-        self.fill(which, layer, b, kvh, out.ctypes.data)
+        self.fill(which, layer, b, kvh, out.ctypes.data, threads)
         return out
 
     def k_row_draw(self, layer: int, b: int, kvh: int, row: int, rnd: int) -> np.ndarray:
@@ -399,6 +400,22 @@ class Problem:
         scale = self._row_scale(layer, b)
         if scale is not None:
             vals = vals * float(scale[row])
+        return round_to(vals, self.dtype)
+
+    def k_rows_draw(self, layer: int, b: int, kvh: int, rows, rnds) -> np.ndarray:
+        """Stored values [n, d] of key rows rows[i] of a unit as drawn in resample
+        rounds rnds[i] (k_row_draw for many rows and rounds in one call)."""
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        rnds = np.asarray(rnds, dtype=np.int64)
+        dl = self.data_layer(layer)
+        keymap = {int(r): derive_key(self.seed, TAG_K, dl, b, kvh, int(r)) for r in np.unique(rnds)}
+        keys = np.array([keymap[int(r)] for r in rnds], dtype=np.uint64)
+        vals = np.empty((rows.shape[0], self.d))
+        if rows.shape[0]:
+            lib().gen_normal_rows(vals.ctypes.data, keys.ctypes.data, rows.ctypes.data, rows.shape[0], self.d)
+        scale = self._row_scale(layer, b)
+        if scale is not None:
+            vals *= scale[rows].astype(np.float64)[:, None]
         return round_to(vals, self.dtype)
 
     def k_row_round(self, layer: int, b: int, kvh: int, row: int) -> int:

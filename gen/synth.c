@@ -77,6 +77,14 @@ void gen_normal_f64(double* out, int64_t n, uint64_t key, int64_t first) {
   for (int64_t i = 0; i < n; ++i) out[i] = normal_at(key, (uint64_t)(first + i));
 }
 
+/* out[i * cols + c] = N(0,1) element (rows[i] * cols + c) of stream keys[i]:
+ * row rows[i] of a [*, cols] block drawn from stream keys[i]. */
+void gen_normal_rows(double* out, const uint64_t* keys, const int64_t* rows, int64_t n, int64_t cols) {
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t c = 0; c < cols; ++c)
+      out[i * cols + c] = normal_at(keys[i], (uint64_t)(rows[i] * cols + c));
+}
+
 /*
  * Fill a [rows, cols] block: row r, column c takes normal element
  * (r * cols + c) of stream key, times row_scale[r] when row_scale is not

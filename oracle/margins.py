@@ -30,12 +30,28 @@ def gamma(d: int) -> float:
     return d * u / (1 - d * u)
 
 
+def abs_sums(qgs, K: np.ndarray) -> np.ndarray:
+    """Per key row, the largest sum_i |q_i k_ji| over the queries' heads."""
+    Ka = np.abs(K)
+    return np.max(np.stack([(Ka @ np.abs(qg).T).max(axis=1) for qg in qgs]), axis=0)
+
+
+def delta_of(m: float, d: int) -> float:
+    return max(1e-2, 4 * gamma(d) * m)
+
+
 def score_delta(qgs, K: np.ndarray) -> float:
     """delta_u for the queries that score a unit."""
-    m = 0.0
-    for qg in qgs:
-        m = max(m, float((np.abs(K) @ np.abs(qg).T).max()))
-    return max(1e-2, 4 * gamma(qgs[0].shape[1]) * m)
+    return delta_of(float(abs_sums(qgs, K).max()), qgs[0].shape[1])
+
+
+def midpoints(s: np.ndarray, ranks):
+    """Midpoints between the r-th and (r+1)-th largest of the scores s, per rank r."""
+    rs = [r for r in ranks if 1 <= r < s.shape[0]]
+    if not rs:
+        return []
+    part = np.partition(-s, sorted({r - 1 for r in rs} | set(rs)))
+    return [-0.5 * (part[r - 1] + part[r]) for r in rs]
 
 
 def boundaries(qgs, K: np.ndarray, ranks):
@@ -43,9 +59,7 @@ def boundaries(qgs, K: np.ndarray, ranks):
     out = []
     for qg in qgs:
         s = oracle.token_scores(qg, K)
-        order = np.argsort(-s, kind="stable")
-        ts = [0.5 * (s[order[r - 1]] + s[order[r]]) for r in ranks if 1 <= r < s.shape[0]]
-        out.append((s, ts))
+        out.append((s, midpoints(s, ranks)))
     return out
 
 
@@ -84,13 +98,38 @@ def _redraw_keeping_sides(p, layer, b, h, K, qgs, row, bounds, delta, max_tries=
     raise RuntimeError(f"no redraw of key row {row} keeps its side")
 
 
-def enforce_margins(problem, layer: int, units=None, extra_ranks=(), max_rounds: int = 40, tau=None):
+def for_units(fn, units, workers: int = 1):
+    """fn(b, h) for every unit, on `workers` threads (each with a one-thread BLAS);
+    the first exception is raised.  Units touch disjoint resample records."""
+    units = list(units)
+    if workers <= 1 or len(units) <= 1:
+        return [fn(b, h) for b, h in units]
+    import concurrent.futures as cf
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        if ctx:
+            ctx.__enter__()
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(lambda u: fn(*u), units))
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+
+
+def enforce_margins(problem, layer: int, units=None, extra_ranks=(), max_rounds: int = 40, tau=None,
+                    workers: int = 1):
     """Redraw q_prev / key rows of the listed (b, kvh) units until every decision has a margin.
 
     A key within delta_u of a rank boundary is redrawn until it lands on the same
     side of every boundary, at least delta_u away: the number of keys above each
     boundary is unchanged, so the boundaries stay where they are and the band
-    around them empties."""
+    around them empties.  workers > 1 treats the units' keys on that many
+    threads."""
     p = problem
     tau = p.tau if tau is None else tau
     g = p.g
@@ -110,12 +149,16 @@ def enforce_margins(problem, layer: int, units=None, extra_ranks=(), max_rounds:
     else:
         raise RuntimeError("cosine margins not reached")
     ranks = [p.topk, *extra_ranks]
-    for b, h in units:
+
+    def one(b, h):
         qgs = [qp[b, h * g:(h + 1) * g], q[b, h * g:(h + 1) * g]]
-        K = oracle.as_f64(p.kv("k", layer, b, h), p.dtype)
+        K = oracle.as_f64(p.kv("k", layer, b, h, threads=1 if workers > 1 else None), p.dtype)
+        # scores and row bounds are kept up to date for the redrawn rows only
+        A = abs_sums(qgs, K)
+        S = [oracle.token_scores(qg, K) for qg in qgs]
         for _ in range(max_rounds):
-            delta = score_delta(qgs, K)
-            bounds = boundaries(qgs, K, ranks)
+            delta = delta_of(float(A.max()), K.shape[1])
+            bounds = [(s, midpoints(s, ranks)) for s in S]
             bad = set()
             for s, ts in bounds:
                 for t in ts:
@@ -127,11 +170,50 @@ def enforce_margins(problem, layer: int, units=None, extra_ranks=(), max_rounds:
                     bad -= set(np.nonzero((s > lo_t) & (s < hi_t))[0].tolist())
             if not bad:
                 break
-            for row in sorted(bad):
-                _redraw_keeping_sides(p, layer, b, h, K, qgs, row, bounds, delta)
+            rows = np.asarray(sorted(bad), dtype=np.int64)
+            _redraw_rows_keeping_sides(p, layer, b, h, K, qgs, rows, bounds, delta)
+            A[rows] = abs_sums(qgs, K[rows])
+            for s, qg in zip(S, qgs):
+                s[rows] = (K[rows] @ qg.T).max(axis=1)
         else:
             raise RuntimeError(f"score margins not reached for unit {(b, h)}")
+
+    for_units(one, units, workers)
     return p
+
+
+def _redraw_rows_keeping_sides(p, layer, b, h, K, qgs, rows, bounds, delta, batch: int = 32,
+                               max_rounds: int = 4096):
+    """_redraw_keeping_sides for many rows at once: candidate rounds are drawn
+    `batch` at a time for every row still open, and each row takes the first
+    round (above every listed row's current one) that keeps its side of every
+    boundary at least delta away."""
+    rows = np.asarray(sorted(rows), dtype=np.int64)
+    sides = [np.stack([s[rows] > t for t in ts], axis=1) if ts else np.zeros((rows.size, 0), bool)
+             for s, ts in bounds]
+    base = max(p.k_row_round(layer, b, h, int(r)) for r in rows)
+    open_ = np.ones(rows.size, dtype=bool)
+    for start in range(base + 1, base + 1 + max_rounds, batch):
+        idx = np.nonzero(open_)[0]
+        if idx.size == 0:
+            return
+        rr = np.repeat(rows[idx], batch)
+        rnds = np.tile(np.arange(start, start + batch), idx.size)
+        cand = oracle.as_f64(p.k_rows_draw(layer, b, h, rr, rnds), p.dtype).reshape(idx.size, batch, -1)
+        ok = np.ones((idx.size, batch), dtype=bool)
+        for qg, (s, ts), sd in zip(qgs, bounds, sides):
+            sc = (cand @ qg.T).max(axis=2)  # [rows, batch]
+            for j, t in enumerate(ts):
+                above = sd[idx, j][:, None]
+                ok &= np.where(above, sc > t + delta, sc < t - delta)
+        for n, i in enumerate(idx):
+            hit = np.nonzero(ok[n])[0]
+            if hit.size:
+                j = int(hit[0])
+                p.set_k_row_round(layer, b, h, int(rows[i]), start + j)
+                K[rows[i]] = cand[n, j]
+                open_[i] = False
+    raise RuntimeError(f"no redraw keeps the side of key rows {rows[open_][:5].tolist()}")
 
 
 def _redraw_keeping_sides_pairs(p, layer, b, h, K, pairs, row, bounds, delta, max_tries=2000):
@@ -229,7 +311,8 @@ def enforce_walk_margins(problem, layer: int, steps: int, tau=None, max_rounds: 
     return p
 
 
-def enforce_block_margins(problem, layer: int, block_size: int, units=None, max_rounds: int = 40):
+def enforce_block_margins(problem, layer: int, block_size: int, units=None, max_rounds: int = 40,
+                          workers: int = 1):
     """Margins for block selection: for each query that scores a unit (q_prev at
     step 0, q_t at step 1), t = the midpoint between the (k/B)-th and (k/B+1)-th
     largest block maxima (full blocks of B tokens); every token of the full blocks
@@ -243,12 +326,13 @@ def enforce_block_margins(problem, layer: int, block_size: int, units=None, max_
     q = oracle.as_f64(p.q(layer), p.dtype)
     qp = oracle.as_f64(p.q_prev(layer), p.dtype)
     kb = p.topk // block_size
-    for b, h in units:
+
+    def one(b, h):
         qgs = [qp[b, h * g:(h + 1) * g], q[b, h * g:(h + 1) * g]]
-        K = oracle.as_f64(p.kv("k", layer, b, h), p.dtype)
+        K = oracle.as_f64(p.kv("k", layer, b, h, threads=1 if workers > 1 else None), p.dtype)
         nb = K.shape[0] // block_size
         if nb <= kb:
-            continue
+            return
         for _ in range(max_rounds):
             delta = score_delta(qgs, K)
             bounds, bad = [], set()
@@ -264,4 +348,6 @@ def enforce_block_margins(problem, layer: int, block_size: int, units=None, max_
                 _redraw_keeping_sides(p, layer, b, h, K, qgs, row, bounds, delta)
         else:
             raise RuntimeError(f"block margins not reached for unit {(b, h)}")
+
+    for_units(one, units, workers)
     return p

@@ -77,15 +77,18 @@ def compare(p: gen.Problem, bufs, got, ref, kv, step: str, units=None, check_cos
     """Assert GPU outputs of one step equal the oracle's (decisions and indices bit-exact).
 
     cache_of(b, kvh): the float64 rows a miss unit's cache must hold (default: the
-    stored K and V, bit for bit)."""
+    stored K and V, bit for bit).  Returns the largest normwise output error and
+    cosine difference met (the headroom under the tolerances)."""
     g = p.g
     check_cos = (step == "step1") if check_cos is None else check_cos
     tol = TOL[p.dtype]
+    worst = {"out_err": 0.0, "cos_err": 0.0, "units": 0}
     for (b, h), r in ref.items():
         where = f"{step} unit (b={b}, kvh={h})"
         assert bool(got["reuse"][b, h]) == r["reuse"], f"{where}: reuse {got['reuse'][b, h]} vs {r['reuse']}"
         if check_cos:
             assert abs(got["cos"][b, h] - r["cos"]) <= 1e-5, f"{where}: cos {got['cos'][b, h]} vs {r['cos']}"
+            worst["cos_err"] = max(worst["cos_err"], abs(got["cos"][b, h] - r["cos"]))
         gi = got["idx"][b, h]
         if not np.array_equal(gi, r["idx"]):
             missing = sorted(set(r["idx"].tolist()) - set(gi.tolist()))[:5]
@@ -107,6 +110,26 @@ def compare(p: gen.Problem, bufs, got, ref, kv, step: str, units=None, check_cos
         ro = r["out"]
         err = np.abs(o - ro).max(axis=1) / np.maximum(np.abs(ro).max(axis=1), 1e-30)
         assert err.max() <= tol, f"{where}: output error {err.max():.3e} > {tol}"
+        worst["out_err"] = max(worst["out_err"], float(err.max()))
+        worst["units"] += 1
+    return worst
+
+
+def merge_worst(results):
+    """Largest errors over many compare() results."""
+    out = {"out_err": 0.0, "cos_err": 0.0, "units": 0}
+    for r in results:
+        out["out_err"] = max(out["out_err"], r["out_err"])
+        out["cos_err"] = max(out["cos_err"], r["cos_err"])
+        out["units"] += r["units"]
+    return out
+
+
+def log_worst(case: str, step: str, worst, dtype: str):
+    tol = TOL[dtype]
+    log(f"[{case}] {step}: {worst['units']} units, max normwise output error {worst['out_err']:.3e} "
+        f"(tolerance {tol:g}, headroom {tol / max(worst['out_err'], 1e-30):.1f}x), max cosine difference "
+        f"{worst['cos_err']:.2e} (tolerance 1e-5)")
 
 
 def run_and_check(p: gen.Problem, layer: int = 0, units=None, bufs=None):
@@ -121,8 +144,8 @@ def run_and_check(p: gen.Problem, layer: int = 0, units=None, bufs=None):
     bufs.step1()
     got1 = snapshot(bufs)
     r0, r1, kv = oracle_steps(p, layer, units)
-    compare(p, bufs, got0, r0, kv, "step0")
-    compare(p, bufs, got1, r1, kv, "step1")
+    log_worst(p.name, "step0", compare(p, bufs, got0, r0, kv, "step0"), p.dtype)
+    log_worst(p.name, "step1", compare(p, bufs, got1, r1, kv, "step1"), p.dtype)
     # hit units keep step 0's selection and cache rows
     for (b, h), r in r1.items():
         if r["reuse"]:

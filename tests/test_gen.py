@@ -63,3 +63,17 @@ def test_resample_changes_only_listed_rows():
     after = p.kv("k", 0, 0, 0)
     diff = np.nonzero((before != after).any(axis=1))[0].tolist()
     assert diff == [5, 700]
+
+
+def test_rows_draw_matches_single_row_draws():
+    # the vectorized redraw used by the margins gives the same stored values as
+    # drawing each row on its own, heavy-hitter scale included
+    p = gen.config(2, batch=1, context=4096, topk=410)
+    rows = np.array([0, 5, 4095, 77, 5], dtype=np.int64)
+    rnds = np.array([1, 1, 3, 7, 2], dtype=np.int64)
+    got = p.k_rows_draw(0, 0, 3, rows, rnds)
+    want = np.stack([p.k_row_draw(0, 0, 3, int(r), int(n)) for r, n in zip(rows, rnds)])
+    assert np.array_equal(got, want)
+    # and a row set to a round through the resample record comes out of fill so
+    p.set_k_row_round(0, 0, 3, 77, 7)
+    assert np.array_equal(p.kv("k", 0, 0, 3)[77], want[3])
