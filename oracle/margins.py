@@ -183,11 +183,15 @@ def enforce_margins(problem, layer: int, units=None, extra_ranks=(), max_rounds:
 
 
 def _redraw_rows_keeping_sides(p, layer, b, h, K, qgs, rows, bounds, delta, batch: int = 32,
-                               max_rounds: int = 4096):
+                               max_rounds: int = 4096, keep_rounds=None):
     """_redraw_keeping_sides for many rows at once: candidate rounds are drawn
     `batch` at a time for every row still open, and each row takes the first
     round (above every listed row's current one) that keeps its side of every
-    boundary at least delta away."""
+    boundary at least delta away.  With keep_rounds, a row still open after that
+    many rounds takes the first draw at least delta away from every boundary on
+    either side (a side that is rare for every query at once, such as above
+    the block-maximum boundary near the top percent of the scores, is then left):
+    the boundaries may move by a rank, and the caller checks again."""
     rows = np.asarray(sorted(rows), dtype=np.int64)
     sides = [np.stack([s[rows] > t for t in ts], axis=1) if ts else np.zeros((rows.size, 0), bool)
              for s, ts in bounds]
@@ -197,6 +201,7 @@ def _redraw_rows_keeping_sides(p, layer, b, h, K, qgs, rows, bounds, delta, batc
         idx = np.nonzero(open_)[0]
         if idx.size == 0:
             return
+        either = keep_rounds is not None and start - base > keep_rounds
         rr = np.repeat(rows[idx], batch)
         rnds = np.tile(np.arange(start, start + batch), idx.size)
         cand = oracle.as_f64(p.k_rows_draw(layer, b, h, rr, rnds), p.dtype).reshape(idx.size, batch, -1)
@@ -204,8 +209,11 @@ def _redraw_rows_keeping_sides(p, layer, b, h, K, qgs, rows, bounds, delta, batc
         for qg, (s, ts), sd in zip(qgs, bounds, sides):
             sc = (cand @ qg.T).max(axis=2)  # [rows, batch]
             for j, t in enumerate(ts):
-                above = sd[idx, j][:, None]
-                ok &= np.where(above, sc > t + delta, sc < t - delta)
+                if either:
+                    ok &= np.abs(sc - t) >= delta
+                else:
+                    above = sd[idx, j][:, None]
+                    ok &= np.where(above, sc > t + delta, sc < t - delta)
         for n, i in enumerate(idx):
             hit = np.nonzero(ok[n])[0]
             if hit.size:
@@ -344,8 +352,7 @@ def enforce_block_margins(problem, layer: int, block_size: int, units=None, max_
                 bad |= set(np.nonzero(np.abs(s[:nb * block_size] - t) < delta)[0].tolist())
             if not bad:
                 break
-            for row in sorted(bad):
-                _redraw_keeping_sides(p, layer, b, h, K, qgs, row, bounds, delta)
+            _redraw_rows_keeping_sides(p, layer, b, h, K, qgs, sorted(bad), bounds, delta, keep_rounds=1024)
         else:
             raise RuntimeError(f"block margins not reached for unit {(b, h)}")
 
