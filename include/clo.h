@@ -261,6 +261,26 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
                            void* ws, size_t ws_bytes, const clo_sync* sync, void* stream);
 
 /*
+ * clo_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, semantics and outputs
+ * as clo_decode_step, bit for bit.  Its workspace is the library's static
+ * device scratch of CLO_STATIC_SCRATCH_BYTES per device (part of the library's
+ * code object, held until the process ends); the call allocates, frees and
+ * creates nothing, and runs every kernel in order on `stream` (no helper
+ * streams, so the host gather does not overlap the scoring here).  A shape whose
+ * clo_workspace_size() exceeds CLO_STATIC_SCRATCH_BYTES is rejected with
+ * CLO_E_WORKSPACE before anything is launched.  Every call on one device uses
+ * the same scratch, which keeps the last call's contents (the step clears what
+ * must start at zero itself): calls that overlap on one device -- on different
+ * streams, or from different threads -- race and must not be made.
+ */
+#define CLO_STATIC_SCRATCH_BYTES (32u << 20)
+clo_status clo_decode_step_static(const clo_shape* shape, const clo_layer* layer, const void* q,
+                                  const void* q_prev, void* out, uint8_t* reuse, float* cos, const clo_sync* sync,
+                                  void* stream);
+
+/*
  * Multi-step decoding with a growing context -- appending the decoded token
  * (synthesis section 5.7 on incremental offloading: new KV goes to host memory
  * as it is produced; abstract feature (3): the GPU moves KV without CPU work).

@@ -19,7 +19,7 @@ CLO_OK, CLO_E_ARG, CLO_E_UNSUPPORTED, CLO_E_WORKSPACE, CLO_E_HIP, CLO_E_TIMEOUT,
 
 # every function include/clo.h declares
 EXPORTS = ("clo_workspace_size", "clo_reuse_test", "clo_topk_select", "clo_reuse_select", "clo_gather_kv",
-           "clo_sparse_attn", "clo_decode_step", "clo_append_kv", "clo_update_reference", "clo_plan_persistent", "clo_quantize_rows",
+           "clo_sparse_attn", "clo_decode_step", "clo_decode_step_static", "clo_append_kv", "clo_update_reference", "clo_plan_persistent", "clo_quantize_rows",
            "clo_stream_read", "clo_status_string", "clo_last_error")
 
 
@@ -75,6 +75,8 @@ def load():
         L.clo_sparse_attn.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, sz, P(clo_sync), vp]
         L.clo_decode_step.restype = st
         L.clo_decode_step.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, vp, vp, vp, sz, P(clo_sync), vp]
+        L.clo_decode_step_static.restype = st
+        L.clo_decode_step_static.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, vp, vp, P(clo_sync), vp]
         L.clo_append_kv.restype = st
         L.clo_append_kv.argtypes = [P(clo_shape), P(clo_layer), vp, vp, ctypes.c_int64, P(clo_sync), vp]
         L.clo_update_reference.restype = st
@@ -251,6 +253,16 @@ def clo_decode_step(shape: Shape, layer: Layer, q, q_prev, out, reuse, cos, ws, 
     _check(load().clo_decode_step(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(q), ptr(q_prev), ptr(out),
                                   ptr(reuse), ptr(cos), ptr(ws), nbytes(ws, ws_bytes), _sync(sync),
                                   stream_handle(stream)), "clo_decode_step")
+
+
+def clo_decode_step_static(shape: Shape, layer: Layer, q, q_prev, out, reuse, cos, sync: Optional[Sync] = None,
+                           stream=None):
+    _check(load().clo_decode_step_static(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(q), ptr(q_prev),
+                                         ptr(out), ptr(reuse), ptr(cos), _sync(sync), stream_handle(stream)),
+           "clo_decode_step_static")
+
+
+CLO_STATIC_SCRATCH_BYTES = 32 << 20
 
 
 def clo_append_kv(shape: Shape, layer: Layer, k_new, v_new, position: int, sync: Optional[Sync] = None,

@@ -212,12 +212,14 @@ WsLayout ws_layout(const Plan& p) {
   return w;
 }
 
-clo_status bind_ws(const Plan& p, void* ws, size_t ws_bytes, Workspace* w) {
+// Carves the workspace into its parts.  trusted: ws is the library's own
+// static scratch, whose extent is known, so the runtime is not asked about it.
+clo_status bind_ws(const Plan& p, void* ws, size_t ws_bytes, Workspace* w, bool trusted = false) {
   const WsLayout L = ws_layout(p);
   if (!ws) return fail(CLO_E_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(CLO_E_WORKSPACE, "workspace is not 256-byte aligned");
   if (ws_bytes < L.total) return fail(CLO_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, L.total);
-  if (check_device(ws, L.total, "workspace")) {
+  if (!trusted && check_device(ws, L.total, "workspace")) {
     char why[sizeof g_last_msg];
     memcpy(why, g_last_msg, sizeof why);
     return fail(CLO_E_WORKSPACE, "%s", why);
@@ -545,7 +547,9 @@ clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const
 
 namespace {
 
-// Decode step for layers without offloaded heads: one stream, nothing to overlap.
+// Decode step with every kernel in order on the caller's stream: layers without
+// offloaded heads (nothing to overlap), and clo_decode_step_static, which
+// creates no helper streams.  The gather of offloaded heads follows the top-k.
 clo_status step_in_order(const Plan& p, const Workspace& w, const void* q, const void* q_prev, void* out,
                          uint8_t* reuse, float* cos, hipStream_t s) {
   clo_status st;
@@ -560,6 +564,15 @@ clo_status step_in_order(const Plan& p, const Workspace& w, const void* q, const
   }
   if ((st = hip_status(launch_score(p.a, q, span_all_misses(w), p.U, w, score_counter(w, 0), cu, s), "score launch"))) return st;
   if ((st = hip_status(launch_select(p.a, span_all_misses(w), p.U, w, s), "top-k launch"))) return st;
+  if (p.a.H > 0) {
+    // the unit lists hold one range; its offloaded misses, and the work counter
+    // the list kernel cleared
+    if ((st = hip_status(launch_gather(p.a, reuse, span_host_range(w, 0), p.U,
+                                       p.U >= kGatherWideUnits ? kGatherBlocksAloneWide : kGatherBlocksAlone,
+                                       reinterpret_cast<uint32_t*>(w.meta + kMetaGather), s),
+                         "gather launch")))
+      return st;
+  }
   if ((st = hip_status(launch_attn_partial(p.a, q, w.part, kAllUnits, p.U, s), "attention launch"))) return st;
   return hip_status(launch_attn_combine(p.a, w.part, out, kAllUnits, p.U, s), "attention combine launch");
 }
@@ -651,6 +664,38 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
   st = p.a.H > 0 ? step_overlapped(p, w, q, q_prev, out, reuse, cos, s)
                  : step_in_order(p, w, q, q_prev, out, reuse, cos, s);
   if (st) return st;
+  return post_signal(sync, s);
+}
+
+clo_status clo_decode_step_static(const clo_shape* shape, const clo_layer* layer, const void* q,
+                                  const void* q_prev, void* out, uint8_t* reuse, float* cos, const clo_sync* sync,
+                                  void* stream) {
+  Plan p;
+  clo_status st;
+  if ((st = make_plan(shape, layer ? layer->persistent_mask : 0, &p))) return st;
+  if ((st = check_sync_flags(sync))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.U == 0) {
+    if ((st = pre_wait(sync, s))) return st;
+    return post_signal(sync, s);
+  }
+  const size_t need = ws_layout(p).total;
+  if (need > kStaticScratchBytes)
+    return fail(CLO_E_WORKSPACE, "the step needs %zu bytes of scratch; the static scratch holds %zu (use clo_decode_step)",
+                need, (size_t)kStaticScratchBytes);
+  Workspace w;
+  if ((st = check_layer(layer, &p, NEED_IDX | NEED_SCORE | NEED_HOST | NEED_CACHE | NEED_HBM_KV))) return st;
+  p.a.err = sync ? sync->error_word : nullptr;
+  if ((st = check_device(q, q_bytes(p), "q"))) return st;
+  if ((st = check_device(q_prev, q_bytes(p), "q_prev"))) return st;
+  if ((st = check_device(out, q_bytes(p), "out"))) return st;
+  if ((st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
+  if (cos && (st = check_device(cos, (size_t)p.U * 4, "cos"))) return st;
+  void* scratch = nullptr;
+  if ((st = hip_status(static_scratch(&scratch), "static scratch lookup"))) return st;
+  if ((st = bind_ws(p, scratch, kStaticScratchBytes, &w, true))) return st;
+  if ((st = pre_wait(sync, s))) return st;
+  if ((st = step_in_order(p, w, q, q_prev, out, reuse, cos, s))) return st;
   return post_signal(sync, s);
 }
 

@@ -144,6 +144,13 @@ struct Span {
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// Device scratch of clo_decode_step_static: a file-scope array in the kernels'
+// code object (each device holds its own copy until the process ends).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+// Device address of the current device's scratch array (looked up once per
+// device with hipGetSymbolAddress and kept).
+hipError_t static_scratch(void** ptr);
+
 // Launchers: enqueue on `s`; return the HIP error of the launch.
 hipError_t launch_reuse(const LayerArgs& a, const void* q, const void* q_prev, uint8_t* reuse, float* cos,
                         hipStream_t s);

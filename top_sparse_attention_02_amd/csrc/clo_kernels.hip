@@ -18,12 +18,38 @@
 // arithmetic is fp32.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/clo.h"
 #include "clo_internal.h"
 
 namespace clo {
+
+// Workspace of clo_decode_step_static, for callers that cannot allocate.  In
+// host code this name stands for the array and is no device address: the host
+// side uses only the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
