@@ -221,10 +221,58 @@ clo_status clo_reuse_select(const clo_shape* shape, const clo_layer* layer, cons
  * sync->error_word and the row nearest to it is copied.  Persistent heads need no transfer: attention
  * reads their rows in place.  reuse NULL = all units miss.  ws: device workspace
  * as for clo_topk_select (the gather's blocks take work from a counter in it;
- * calls that share one workspace must not overlap).  sync may be NULL.
+ * calls that share one workspace must not overlap).  sync may be NULL.  With
+ * sync->wait_flag the wait and the signal happen inside the gather kernel (its
+ * blocks poll the flag, the last block to finish stores the signal), so the
+ * call is one launch; it then needs the workspace's two gather counters at zero,
+ * as every call on a workspace leaves them and every selection call
+ * (clo_topk_select, clo_reuse_select, clo_decode_step) sets them: a workspace
+ * whose first use is such a call must be zero-filled once.
  */
 clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const uint8_t* reuse,
                          void* ws, size_t ws_bytes, const clo_sync* sync, void* stream);
+
+/*
+ * A4 for many layers in one launch (a resident gather: the KV-cache offloading
+ * article, pillar 3, on a long-running kernel that decides on the GPU when to
+ * move data; synthesis section 5.6, one-layer-ahead prefetch; abstract feature
+ * (3), GPU-centric synchronization).  Layer by layer, in plan order, the
+ * kernel's blocks wait until the layer's wait_flag reaches the step's
+ * wait_value (its selection is done), gather the layer exactly as
+ * clo_gather_kv does, and the last block to finish stores the step's
+ * signal_value to the layer's signal_flag (release, agent scope); a block
+ * that runs out of a layer's work goes straight on to the next layer.
+ *
+ * clo_gather_plan validates every layer as clo_gather_kv would, writes their
+ * descriptors into `plan` (device memory of clo_gather_plan_size(n_layers)
+ * bytes, caller-owned) with a blocking copy, clears each layer's gather
+ * counters in its workspace, and returns in *blocks the grid size to pass to
+ * clo_gather_layers.  The plan stays valid while the layers' buffers, reuse
+ * flags, workspaces and flags stay where they were.  Layers may differ in shape,
+ * dtype and host format.  n_layers in 1..4096.
+ *
+ * clo_gather_layers enqueues one launch on `stream`.  Every layer's wait_flag
+ * must be signalled by work enqueued (in host order) before this call.  Waits
+ * are bounded by spin_limit polls per block and layer (0 = about a second); a
+ * time-out or a selected index out of range is reported in error_word (device,
+ * may be NULL) as for clo_sync.  A layer's workspace must not be used by
+ * other calls while the launch runs.
+ */
+typedef struct {
+  const clo_shape* shape;
+  const clo_layer* layer;
+  const uint8_t* reuse;       /* device [B, Hkv] reuse flags (NULL = every unit misses) */
+  void* ws;                   /* the layer's workspace, as for clo_gather_kv */
+  size_t ws_bytes;
+  const uint32_t* wait_flag;  /* device: the layer's selection is done once *wait_flag >= wait_value */
+  uint32_t* signal_flag;      /* device: set to signal_value once the layer's rows are in its cache */
+} clo_gather_layer;
+
+size_t clo_gather_plan_size(int32_t n_layers);
+clo_status clo_gather_plan(const clo_gather_layer* layers, int32_t n_layers, void* plan, size_t plan_bytes,
+                           int32_t* blocks);
+clo_status clo_gather_layers(const void* plan, int32_t n_layers, int32_t blocks, uint32_t wait_value,
+                             uint32_t signal_value, uint32_t* error_word, uint32_t spin_limit, void* stream);
 
 /*
  * A5 -- sparse attention over the selected rows, every unit (synthesis 2.3

@@ -3,9 +3,10 @@
 Every unit of configs 1, 2 and 3 is compared with the oracle at both steps of
 the two-step protocol (reuse decision and selection bit-exact, cache rows bit
 for bit, outputs within tolerance).  Configs 4 and 5 run all 48 layers through
-the three-stream layer loop with the bench's 16 distinct data layers; 8 layers
-with 8 different data layers are compared (config 5: all their units; config
-4: every miss unit and some reuse units of each), and every unit of those
+the three-stream layer loop with the bench's distinct data layers (8 for
+config 4, 16 for config 5); 8 layers with 8 different data layers are
+compared (config 5: all their units; config 4: every miss unit and some reuse
+units of each), and every unit of those
 layers is checked for its reuse decision and a valid selection.  Config 3's
 shape is also run with int8 host KV and with 16-token blocks on sampled units.
 Each case logs its largest normwise output error against the tolerance.
@@ -191,8 +192,10 @@ def test_config3_shape_variants(need_gpu, variant):
     _release()
 
 
-# 8 layers over 8 different data layers (16 data layers, layer l holds data layer l % 16)
-LAYERS_CHECKED = [0, 17, 34, 3, 20, 37, 6, 47]
+# the bench's distinct data layers (layer l holds data layer l % D), and 8 layers
+# over 8 different data layers
+DATA_LAYERS = {4: 8, 5: 16}
+LAYERS_CHECKED = {4: [0, 9, 18, 27, 36, 45, 6, 15], 5: [0, 17, 34, 3, 20, 37, 6, 47]}
 
 
 @pytest.mark.timeout(1200)
@@ -202,11 +205,12 @@ def test_layer_loop_configs_full_size(need_gpu, cfg):
 
     from top_sparse_attention_02_amd import workload
 
-    p = gen.config(cfg, data_layers=16)
-    assert len({p.data_layer(l) for l in LAYERS_CHECKED}) == len(LAYERS_CHECKED)
+    p = gen.config(cfg, data_layers=DATA_LAYERS[cfg])
+    checked = LAYERS_CHECKED[cfg]
+    assert len({p.data_layer(l) for l in checked}) == len(checked)
     tag = f"full config {cfg}"
     samples = {}
-    for l in LAYERS_CHECKED:
+    for l in checked:
         enforce_cos_all(p, l)
         if cfg == 5:
             samples[l] = [(b, h) for b in range(p.batch) for h in range(p.hkv)]
@@ -214,7 +218,7 @@ def test_layer_loop_configs_full_size(need_gpu, cfg):
             miss, hit = unit_classes(p, l)
             samples[l] = miss + sample_units(p, l, n_miss=0, n_hit=4, seed=l)
         enforce_margins(p, l, units=samples[l], workers=WORKERS)
-    mixes = [(bool(p.persistent[l].any()), bool((~p.persistent[l]).any())) for l in LAYERS_CHECKED]
+    mixes = [(bool(p.persistent[l].any()), bool((~p.persistent[l]).any())) for l in checked]
     assert any(a for a, _ in mixes) and any(b for _, b in mixes), "persistent and offloaded heads both covered"
     log(f"[{tag}] generating and loading 48 layers ({p.data_layers} data layers)")
     layers = workload.load_layers(p)
@@ -222,12 +226,12 @@ def test_layer_loop_configs_full_size(need_gpu, cfg):
     loop.step(cold=True)
     torch.cuda.synchronize()
     loop.check()
-    got0 = {l: snapshot(layers[l]) for l in LAYERS_CHECKED}
+    got0 = {l: snapshot(layers[l]) for l in checked}
     loop.step()
     torch.cuda.synchronize()
     loop.check()
-    got1 = {l: snapshot(layers[l]) for l in LAYERS_CHECKED}
-    for l in LAYERS_CHECKED:
+    got1 = {l: snapshot(layers[l]) for l in checked}
+    for l in checked:
         n_p = sum(1 for b, h in samples[l] if layers[l].is_persistent(h))
         log(f"[{tag}] oracle, layer {l}: {len(samples[l])} units ({n_p} of persistent heads)")
         check_units(p, l, layers[l], got0[l], got1[l], samples[l], f"{tag} layer {l}")

@@ -30,16 +30,17 @@ def enforce_all_layers(p):
     raise RuntimeError("margins did not settle")
 
 
-@pytest.mark.parametrize("select_streams", [1, 2, 3])
-def test_layer_loop_matches_sequential_and_oracle(need_gpu, select_streams):
+@pytest.mark.parametrize("select_streams,gather", [(1, "resident"), (2, "resident"), (3, "resident"),
+                                                   (1, "per-layer")])
+def test_layer_loop_matches_sequential_and_oracle(need_gpu, select_streams, gather):
     import torch
 
     from top_sparse_attention_02_amd import workload
 
     p = enforce_all_layers(multi_layer_problem())
     layers = workload.load_layers(p)
-    loop = workload.LayerLoop(layers, select_streams=select_streams)
-    log(f"[case layer loop, {select_streams} select streams] cold step")
+    loop = workload.LayerLoop(layers, select_streams=select_streams, gather=gather)
+    log(f"[case layer loop, {select_streams} select streams, {gather} gather] cold step")
     loop.step(cold=True)
     torch.cuda.synchronize()
     loop.check()
@@ -92,6 +93,57 @@ def test_layer_loop_int8_host_kv_matches_sequential(need_gpu):
     for l in range(p.layers):
         for key in a1[l]:
             assert np.array_equal(a1[l][key], b1[l][key]), (l, key)
+
+
+def test_resident_gather_with_a_layer_without_offloaded_heads(need_gpu):
+    """The resident gather walks a layer whose heads are all persistent (nothing to
+    gather: its counters live in the plan) between layers that gather; three steps
+    in a row equal the per-layer gathers bit for bit."""
+    import torch
+
+    from top_sparse_attention_02_amd import workload
+
+    p = gen.Problem(name="layers_pers", layers=4, batch=2, hq=8, hkv=2, d=128, context=2500, topk=250,
+                    dtype="bf16", tau=0.8, seed=0x5EED0201, qprev_model="target_cos", low_frac=0.5,
+                    persistent=np.array([[0, 1], [1, 1], [0, 0], [1, 1]], dtype=bool))
+    p = enforce_all_layers(p)
+    got = {}
+    for mode in ("resident", "per-layer"):
+        layers = workload.load_layers(p)
+        loop = workload.LayerLoop(layers, gather=mode)
+        log(f"[case layers without offloaded heads, {mode}]")
+        loop.step(cold=True)
+        loop.step()
+        loop.step()
+        torch.cuda.synchronize()
+        loop.check()
+        got[mode] = [snapshot(b) for b in layers]
+    for l in range(p.layers):
+        for key in got["resident"][l]:
+            assert np.array_equal(got["resident"][l][key], got["per-layer"][l][key]), (l, key)
+
+
+def test_resident_gather_wait_times_out_without_hanging(need_gpu):
+    """A plan whose selection flags are never set: every block gives up after its
+    bounded wait, CLO_E_TIMEOUT lands in the error word, each layer is still
+    signalled, and the launch ends."""
+    import torch
+
+    from top_sparse_attention_02_amd import clo, workload
+    from tests.gpu_common import small_problem
+
+    p = small_problem("resident_timeout", batch=1, hq=4, hkv=2, context=700, topk=70, dtype="f32",
+                      persistent=[0, 1])
+    bufs = [workload.load_layer(p, 0) for _ in range(2)]
+    flags = torch.zeros(2, 2, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plan = torch.zeros(clo.clo_gather_plan_size(2), dtype=torch.uint8, device="cuda")
+    blocks = clo.clo_gather_plan([(b.shape, b.layer(), b.reuse, b.ws, flags[0, l], flags[1, l])
+                                  for l, b in enumerate(bufs)], plan)
+    clo.clo_gather_layers(plan, 2, blocks, 1, 5, error_word=err, spin_limit=2000)
+    torch.cuda.synchronize()
+    assert int(err.item()) == clo.CLO_E_TIMEOUT
+    assert flags[1].tolist() == [5, 5]
 
 
 def test_consumer_sees_rows_written_before_the_flag(need_gpu):

@@ -20,7 +20,8 @@ CLO_OK, CLO_E_ARG, CLO_E_UNSUPPORTED, CLO_E_WORKSPACE, CLO_E_HIP, CLO_E_TIMEOUT,
 # every function include/clo.h declares
 EXPORTS = ("clo_workspace_size", "clo_reuse_test", "clo_topk_select", "clo_reuse_select", "clo_gather_kv",
            "clo_sparse_attn", "clo_decode_step", "clo_decode_step_static", "clo_append_kv", "clo_update_reference", "clo_plan_persistent", "clo_quantize_rows",
-           "clo_stream_read", "clo_status_string", "clo_last_error")
+           "clo_stream_read", "clo_status_string", "clo_last_error", "clo_gather_plan_size", "clo_gather_plan",
+           "clo_gather_layers")
 
 
 class CloError(RuntimeError):
@@ -47,6 +48,12 @@ class clo_sync(ctypes.Structure):
     _fields_ = [("wait_flag", ctypes.c_void_p), ("wait_value", ctypes.c_uint32),
                 ("signal_flag", ctypes.c_void_p), ("signal_value", ctypes.c_uint32),
                 ("error_word", ctypes.c_void_p), ("spin_limit", ctypes.c_uint32)]
+
+
+class clo_gather_layer(ctypes.Structure):
+    _fields_ = [("shape", ctypes.POINTER(clo_shape)), ("layer", ctypes.POINTER(clo_layer)), ("reuse", ctypes.c_void_p),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("wait_flag", ctypes.c_void_p),
+                ("signal_flag", ctypes.c_void_p)]
 
 
 _lib = None
@@ -87,6 +94,13 @@ def load():
         L.clo_stream_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int32, vp, vp]
         L.clo_plan_persistent.restype = st
         L.clo_plan_persistent.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
+        L.clo_gather_plan_size.restype = sz
+        L.clo_gather_plan_size.argtypes = [ctypes.c_int32]
+        L.clo_gather_plan.restype = st
+        L.clo_gather_plan.argtypes = [P(clo_gather_layer), ctypes.c_int32, vp, sz, P(ctypes.c_int32)]
+        L.clo_gather_layers.restype = st
+        L.clo_gather_layers.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint32, vp,
+                                        ctypes.c_uint32, vp]
         L.clo_status_string.restype = ctypes.c_char_p
         L.clo_status_string.argtypes = [st]
         L.clo_last_error.restype = st
@@ -263,6 +277,33 @@ def clo_decode_step_static(shape: Shape, layer: Layer, q, q_prev, out, reuse, co
 
 
 CLO_STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def clo_gather_plan_size(n_layers: int) -> int:
+    return int(load().clo_gather_plan_size(int(n_layers)))
+
+
+def clo_gather_plan(items, plan, plan_bytes: Optional[int] = None) -> int:
+    """items: (shape, layer, reuse, ws, wait_flag, signal_flag) per layer, in gather order.
+    Writes the plan (device memory) and returns the grid size for clo_gather_layers."""
+    n = len(items)
+    arr = (clo_gather_layer * max(n, 1))()
+    keep = []
+    for i, (shape, layer, reuse, ws, wait_flag, signal_flag) in enumerate(items):
+        cs, cl = shape.c(), layer.c()
+        keep += [cs, cl]
+        arr[i] = clo_gather_layer(ctypes.pointer(cs), ctypes.pointer(cl), ptr(reuse), ptr(ws), nbytes(ws),
+                                  ptr(wait_flag), ptr(signal_flag))
+    blocks = ctypes.c_int32(0)
+    _check(load().clo_gather_plan(arr, n, ptr(plan), nbytes(plan, plan_bytes), ctypes.byref(blocks)),
+           "clo_gather_plan")
+    return int(blocks.value)
+
+
+def clo_gather_layers(plan, n_layers: int, blocks: int, wait_value: int, signal_value: int, error_word=None,
+                      spin_limit: int = 0, stream=None):
+    _check(load().clo_gather_layers(ptr(plan), int(n_layers), int(blocks), int(wait_value), int(signal_value),
+                                    ptr(error_word), int(spin_limit), stream_handle(stream)), "clo_gather_layers")
 
 
 def clo_append_kv(shape: Shape, layer: Layer, k_new, v_new, position: int, sync: Optional[Sync] = None,

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -176,7 +177,7 @@ clo_status make_plan(const clo_shape* s, uint64_t pmask, Plan* p) {
 // Workspace layout: meta | list_all | list_host | list_hit | h0 | h1 | tstate | chist | keys | part,
 // each 256-byte aligned.
 struct WsLayout {
-  size_t meta, list_all, list_host, list_hit, h0, h1, tstate, chist, keys, part, bkeys, h0b, bidx, total;
+  size_t meta, list_all, list_host, list_hit, h0, h1, tstate, chist, keys, part, bkeys, h0b, bidx, fsync, total;
   int64_t npb;
   int cmax;
 };
@@ -197,6 +198,7 @@ WsLayout ws_layout(const Plan& p) {
   w.h0 = take((size_t)p.U * 256 * 4);
   w.h1 = take((size_t)p.U * 256 * 4);
   w.tstate = take((size_t)p.U * sizeof(TopkState));
+  w.fsync = take((size_t)p.U * kFusedSyncWords * 4);
   w.chist = take((size_t)p.U * (size_t)w.cmax * kChunkHist * 4);
   w.keys = take((size_t)p.U * (size_t)p.a.Np * 4);
   w.part = take((size_t)p.U * (size_t)p.nch_attn * (size_t)p.a.G * kPartStride * 4);
@@ -232,6 +234,7 @@ clo_status bind_ws(const Plan& p, void* ws, size_t ws_bytes, Workspace* w, bool 
   w->h0 = reinterpret_cast<uint32_t*>(b + L.h0);
   w->h1 = reinterpret_cast<uint32_t*>(b + L.h1);
   w->tstate = reinterpret_cast<TopkState*>(b + L.tstate);
+  w->fsync = reinterpret_cast<uint32_t*>(b + L.fsync);
   w->chist = reinterpret_cast<uint32_t*>(b + L.chist);
   w->cmax = L.cmax;
   w->keys = reinterpret_cast<uint32_t*>(b + L.keys);
@@ -448,6 +451,7 @@ clo_status clo_topk_select(const clo_shape* shape, const clo_layer* layer, const
   }
   Workspace w;
   if ((st = check_layer(layer, &p, NEED_IDX | NEED_SCORE | NEED_HBM_K))) return st;
+  p.a.err = sync ? sync->error_word : nullptr;
   if ((st = check_device(q, q_bytes(p), "q"))) return st;
   if (reuse && (st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
@@ -473,6 +477,7 @@ clo_status clo_reuse_select(const clo_shape* shape, const clo_layer* layer, cons
   }
   Workspace w;
   if ((st = check_layer(layer, &p, NEED_IDX | NEED_SCORE | NEED_HBM_K))) return st;
+  p.a.err = sync ? sync->error_word : nullptr;
   if ((st = check_device(q, q_bytes(p), "q"))) return st;
   if ((st = check_device(q_prev, q_bytes(p), "q_prev"))) return st;
   if ((st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
@@ -514,12 +519,91 @@ clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const u
   if (reuse && (st = check_device(reuse, (size_t)p.U, "reuse"))) return st;
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
   uint32_t* counter = reinterpret_cast<uint32_t*>(w.meta + kMetaGather);
-  if ((st = pre_wait(sync, s, counter))) return st;
-  if ((st = hip_status(launch_gather(p.a, reuse, kAllUnits, p.U,
-                                     p.U >= kGatherWideUnits ? kGatherBlocksAloneWide : kGatherBlocksAlone,
-                                     counter, s), "gather launch")))
-    return st;
+  uint32_t* done = reinterpret_cast<uint32_t*>(w.meta + kMetaGatherDone);
+  const int blocks = p.U >= kGatherWideUnits ? kGatherBlocksAloneWide : kGatherBlocksAlone;
+  if (sync && sync->wait_flag) {
+    // one launch: the gather's blocks wait for the flag themselves, and the last
+    // one to finish signals; the work counters are zero (every call on the
+    // workspace leaves them so, and every selection call sets them)
+    const GatherSync gs{sync->wait_flag, sync->wait_value, sync->spin_limit ? sync->spin_limit : (1u << 22),
+                        sync->error_word, sync->signal_flag, sync->signal_value, done};
+    return hip_status(launch_gather(p.a, reuse, kAllUnits, p.U, blocks, counter, s, &gs), "gather launch");
+  }
+  // the counters are cleared before (a fresh workspace) and by the kernel's last block
+  const GatherSync gs{nullptr, 0u, 0u, nullptr, nullptr, 0u, done};
+  if ((st = hip_status(launch_zero(counter, s, done), "counter reset launch"))) return st;
+  if ((st = hip_status(launch_gather(p.a, reuse, kAllUnits, p.U, blocks, counter, s, &gs), "gather launch"))) return st;
   return post_signal(sync, s);
+}
+
+size_t clo_gather_plan_size(int32_t n_layers) {
+  if (n_layers < 1 || n_layers > 4096) return 0;
+  return (size_t)round_up((int64_t)n_layers * (int64_t)sizeof(GatherPlanLayer), 256);
+}
+
+clo_status clo_gather_plan(const clo_gather_layer* layers, int32_t n_layers, void* plan, size_t plan_bytes,
+                           int32_t* blocks) {
+  if (!layers || !blocks) return fail(CLO_E_ARG, "layers or blocks is NULL");
+  const size_t need = clo_gather_plan_size(n_layers);
+  if (!need) return fail(CLO_E_ARG, "n_layers %d outside 1..4096", n_layers);
+  if (plan_bytes < need) return fail(CLO_E_ARG, "plan has %zu bytes, %zu needed", plan_bytes, need);
+  clo_status st;
+  if ((st = check_device(plan, need, "plan"))) return st;
+  std::vector<GatherPlanLayer> host((size_t)n_layers);
+  int grid = kGatherBlocksAlone;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const clo_gather_layer& g = layers[l];
+    Plan p;
+    if ((st = make_plan(g.shape, g.layer ? g.layer->persistent_mask : 0, &p))) return st;
+    GatherPlanLayer& d = host[(size_t)l];
+    memset(&d, 0, sizeof d);
+    if ((st = check_flag_ptr(g.wait_flag, "wait_flag")) || (st = check_flag_ptr(g.signal_flag, "signal_flag")))
+      return st;
+    if (!g.wait_flag) return fail(CLO_E_ARG, "layer %d: wait_flag is NULL", l);
+    d.wait_flag = g.wait_flag;
+    d.signal_flag = g.signal_flag;
+    if (p.U > 0 && p.a.H > 0) {
+      Workspace w;
+      if ((st = check_layer(g.layer, &p, NEED_IDX | NEED_HOST | NEED_CACHE))) return st;
+      if (g.reuse && (st = check_device(g.reuse, (size_t)p.U, "reuse"))) return st;
+      if ((st = bind_ws(p, g.ws, g.ws_bytes, &w))) return st;
+      d.a = p.a;
+      d.reuse = g.reuse;
+      d.counter = reinterpret_cast<uint32_t*>(w.meta + kMetaGather);
+      d.done = reinterpret_cast<uint32_t*>(w.meta + kMetaGatherDone);
+      const uint32_t zero = 0;
+      hipError_t e = hipMemcpy(d.counter, &zero, 4, hipMemcpyHostToDevice);
+      if (e == hipSuccess) e = hipMemcpy(d.done, &zero, 4, hipMemcpyHostToDevice);
+      if ((st = hip_status(e, "clearing the gather counters"))) return st;
+      if (p.U >= kGatherWideUnits) grid = kGatherBlocksAloneWide;
+    } else {
+      // nothing to gather: the layer's items are none, its counters live in the plan
+      d.a = p.a;
+      d.a.B = 0;
+      d.counter = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(plan) + (size_t)l * sizeof(GatherPlanLayer) +
+                                              offsetof(GatherPlanLayer, zero_words));
+      d.done = d.counter + 1;
+    }
+  }
+  if ((st = hip_status(hipMemcpy(plan, host.data(), host.size() * sizeof(GatherPlanLayer), hipMemcpyHostToDevice),
+                       "writing the gather plan")))
+    return st;
+  *blocks = grid;
+  return ok();
+}
+
+clo_status clo_gather_layers(const void* plan, int32_t n_layers, int32_t blocks, uint32_t wait_value,
+                             uint32_t signal_value, uint32_t* error_word, uint32_t spin_limit, void* stream) {
+  const size_t need = clo_gather_plan_size(n_layers);
+  if (!need) return fail(CLO_E_ARG, "n_layers %d outside 1..4096", n_layers);
+  if (blocks < 1 || blocks > 1024) return fail(CLO_E_ARG, "blocks %d outside 1..1024", blocks);
+  clo_status st;
+  if ((st = check_device(plan, need, "plan"))) return st;
+  if ((st = check_flag_ptr(error_word, "error_word"))) return st;
+  return hip_status(launch_gather_layers(static_cast<const GatherPlanLayer*>(plan), n_layers, blocks, wait_value,
+                                         signal_value, spin_limit ? spin_limit : (1u << 22), error_word,
+                                         static_cast<hipStream_t>(stream)),
+                    "gather launch");
 }
 
 clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const void* q, void* out, void* ws,

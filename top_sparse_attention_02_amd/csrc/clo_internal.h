@@ -98,7 +98,8 @@ constexpr int kMetaOffAll = 16;    // [R + 1] first position of each range in li
 constexpr int kMetaOffHost = 40;   // [R + 1] first position of each range in list_host
 constexpr int kMetaGather = 64;    // [kMaxRanges] work counters of the range gathers
 constexpr int kMetaScore = 80;     // [kMaxRanges] work counters of the range scorings
-constexpr int kMetaInts = 96;
+constexpr int kMetaGatherDone = 96;  // blocks of the standalone gather that have finished
+constexpr int kMetaInts = 128;
 
 // Multi-block top-k: each unit's keys are split into chunks of kTopkChunk keys,
 // one 256-thread block per chunk.
@@ -113,8 +114,14 @@ struct TopkState {
 };
 
 // Per chunk of the digit-4 pass: 256 bins of the chunk's keys that match the
-// 24-bit prefix, and the count of its keys above that prefix.
+// 24-bit prefix, and the count of its keys above that prefix.  (The one-launch
+// top-k keeps only each chunk's counts of keys above and equal to the k-th key
+// in the first two words.)
 constexpr int kChunkHist = 257;
+
+// Per-unit exchange words of the one-launch top-k: the unit-wide histograms of
+// digits 2, 3 and 4 (256 bins each) and four arrival counts.
+constexpr int kFusedSyncWords = 3 * 256 + 16;
 
 struct Workspace {
   int32_t* meta;       // counts and range offsets (layout above)
@@ -132,6 +139,7 @@ struct Workspace {
   int32_t* bidx;       // block selection: [U][k / bs] selected blocks, ascending
   int64_t npb;         // block selection: padded row stride of bkeys
   float* part;         // [U][nch][G][kPartStride] attention partials
+  uint32_t* fsync;     // [U][kFusedSyncWords] one-launch top-k exchange words
 };
 
 // A device-side list of units: list[*lo .. *hi).  list == nullptr means "all
@@ -175,9 +183,34 @@ hipError_t launch_select(const LayerArgs& a, Span sp, int64_t max_units, const W
 // waves in flight, and a smaller grid leaves the CUs to concurrent kernels.
 // Blocks take work items from *counter (zero at launch) so that blocks that
 // start late, behind other streams' work, simply take fewer items.
+// Ordering done inside the standalone gather kernel: with wait_flag every block
+// polls it before its first read; with done, the last block to finish (done
+// counts them) clears *counter and *done for the next launch on the workspace
+// and then, with signal_flag, stores signal_value there (release).
+struct GatherSync {
+  const uint32_t* wait_flag;
+  uint32_t wait_value;
+  uint32_t limit;
+  uint32_t* error_word;
+  uint32_t* signal_flag;
+  uint32_t signal_value;
+  uint32_t* done;
+};
 hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, Span sp, int64_t max_units, int max_blocks,
-                         uint32_t* counter, hipStream_t s);
-hipError_t launch_zero(uint32_t* word, hipStream_t s);
+                         uint32_t* counter, hipStream_t s, const GatherSync* gs = nullptr);
+// One layer of a multi-layer gather plan (device memory, written by the host).
+struct GatherPlanLayer {
+  LayerArgs a;
+  const uint8_t* reuse;        // NULL = every unit misses
+  uint32_t* counter;           // the layer's gather work counter (in its workspace)
+  uint32_t* done;              // blocks done with the layer (in its workspace)
+  const uint32_t* wait_flag;   // the layer's rows may be read once *wait_flag >= wait_value
+  uint32_t* signal_flag;       // set to signal_value once the layer's rows are in its cache
+  uint32_t zero_words[2];      // counter and done of a layer with nothing to gather
+};
+hipError_t launch_gather_layers(const GatherPlanLayer* plan, int n_layers, int blocks, uint32_t wait_value,
+                                uint32_t signal_value, uint32_t limit, uint32_t* error_word, hipStream_t s);
+hipError_t launch_zero(uint32_t* word, hipStream_t s, uint32_t* word2 = nullptr);
 hipError_t launch_stream_read(const void* src, int64_t n16, int blocks, uint32_t* sink, hipStream_t s);
 hipError_t launch_attn_partial(const LayerArgs& a, const void* q, float* part, Span sp, int64_t max_units,
                                hipStream_t s);

@@ -266,6 +266,7 @@ __device__ void compact_units(MissF is_miss, int U, int Hkv, uint64_t pmask, int
     meta[kMetaGather + tid] = 0;
     meta[kMetaScore + tid] = 0;
   }
+  if (tid == 0) meta[kMetaGatherDone] = 0;
   if (tid == 0) {
     meta[kMetaCountAll] = base[0];
     meta[kMetaCountHost] = base[1];
@@ -351,10 +352,17 @@ __global__ __launch_bounds__(1024) void reuse_compact_kernel(const T* __restrict
 // (nothing reads either before the top-k kernels that follow).
 // Body without barriers: the caller brackets it so that every wave has finished
 // the item before it and no wave counts into s_h again until after it.
+// The one-launch top-k's per-unit exchange words (pass histograms and arrival
+// counts), cleared by 256 threads together with the unit's other radix state.
+__device__ __forceinline__ void clear_fused_sync(uint32_t* __restrict__ fs, int u) {
+  uint32_t* f = fs + (int64_t)u * kFusedSyncWords;
+  for (int i = threadIdx.x; i < kFusedSyncWords; i += 256) f[i] = 0u;
+}
+
 template <int W>
 __device__ __forceinline__ void flush_score_hist(uint32_t (*s_h)[W], int u, int c, int64_t k,
                                                  uint32_t* __restrict__ h0, uint32_t* __restrict__ h1,
-                                                 TopkState* __restrict__ st) {
+                                                 TopkState* __restrict__ st, uint32_t* __restrict__ fs) {
   const int t = threadIdx.x;  // 256 threads, one bin each
   const uint32_t sum = s_h[0][t] + s_h[1][t] + s_h[2][t] + s_h[3][t];
   s_h[0][t] = 0u;
@@ -365,15 +373,16 @@ __device__ __forceinline__ void flush_score_hist(uint32_t (*s_h)[W], int u, int 
   if (c == 0) {
     h1[(int64_t)u * 256 + t] = 0u;
     if (t == 0) st[u] = TopkState{0u, 0u, (uint32_t)k, 0u};
+    clear_fused_sync(fs, u);
   }
 }
 
 template <int W>
 __device__ __forceinline__ void score_item_done(uint32_t (*s_h)[W], int u, int c, int64_t k,
                                                 uint32_t* __restrict__ h0, uint32_t* __restrict__ h1,
-                                                TopkState* __restrict__ st) {
+                                                TopkState* __restrict__ st, uint32_t* __restrict__ fs) {
   __syncthreads();
-  flush_score_hist(s_h, u, c, k, h0, h1, st);
+  flush_score_hist(s_h, u, c, k, h0, h1, st, fs);
   __syncthreads();
 }
 
@@ -387,7 +396,8 @@ __device__ __forceinline__ void clear_score_hist(uint32_t (*s_h)[W]) {
 template <typename T, int G>
 __global__ __launch_bounds__(256) void score_kernel(LayerArgs a, const T* __restrict__ q, Span sp,
                                                     uint32_t* __restrict__ keys, uint32_t* __restrict__ h0,
-                                                    uint32_t* __restrict__ h1, TopkState* __restrict__ st) {
+                                                    uint32_t* __restrict__ h1, TopkState* __restrict__ st,
+                                                    uint32_t* __restrict__ fs) {
   constexpr int UNR = 8;
   __shared__ uint32_t s_h[4][256];
   clear_score_hist(s_h);
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(256) void score_kernel(LayerArgs a, const T* __rest
         }
       }
     }
-    score_item_done(s_h, u, c, a.k, h0, h1, st);
+    score_item_done(s_h, u, c, a.k, h0, h1, st, fs);
   }
 }
 
@@ -464,7 +474,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     LayerArgs a, const uint16_t* __restrict__ q, Span sp,
                                                          uint32_t* __restrict__ keys, uint32_t* __restrict__ counter,
                                                          uint32_t* __restrict__ h0, uint32_t* __restrict__ h1,
-                                                         TopkState* __restrict__ st) {
+                                                         TopkState* __restrict__ st, uint32_t* __restrict__ fs) {
   constexpr int TILES = 8;                         // 16-key tiles per wave iteration (128 keys)
   constexpr int kKeysPerWave = kScoreItem / 4;     // 256
   static_assert(G <= 8, "group of at most 8 query heads");
@@ -484,7 +494,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     __syncthreads();
     const int64_t it = s_item;
     // every wave is past the previous item: add its histogram to the unit's
-    if (cur_u >= 0) flush_score_hist(s_h, cur_u, prev_c, a.k, h0, h1, st);
+    if (cur_u >= 0) flush_score_hist(s_h, cur_u, prev_c, a.k, h0, h1, st, fs);
     __syncthreads();
     if (it >= items) break;  // uniform per block
     const int u = list[it / nch];
@@ -1069,6 +1079,200 @@ __global__ __launch_bounds__(kTopkThreads) void topk_write_kernel(LayerArgs a, S
   }
 }
 
+// ---------------------------------------------------------------- A3 top-k in one launch
+// The same exact select with the chunk blocks of a unit cooperating inside one
+// launch.  Each block reads its chunk of keys from global memory once, into
+// LDS (16384 keys = 64 KiB of gfx950's 160 KiB per CU), and keeps it there for
+// digits 2-4 and the write.  For each digit the blocks add their LDS histograms
+// into the unit's histogram of that digit (device-scope atomics, performed at
+// the device's point of coherence), wait until every chunk block of the unit
+// has arrived, read the unit's histogram back and all pick the same digit.
+// After digit 4 each block publishes its counts of keys above and equal to the
+// k-th key; after one more arrival every block knows where its winners go.  A
+// launch beside the host gather costs each memory round trip many times over;
+// this path has one launch and one read of the keys per unit, where the
+// multi-launch path has four of each.
+//
+// Every chunk block of a unit waits for the others, so all blocks of a launch
+// must be resident at once: a launch has at most kFusedMaxBlocks blocks, in
+// groups of cmax consecutive blocks (one per chunk), and each group takes the
+// span's units g, g + groups, g + 2 groups, ... one after another.  Two blocks
+// fit a CU (66 KiB of LDS each), so four such launches running side by side
+// still fit the GPU.  The waits are bounded all the same (the error word gets
+// CLO_E_TIMEOUT, and every block still runs to its end).
+constexpr int kFusedMaxBlocks = 128;
+
+// Block-wide arrival at one of a unit's exchange counts: the block's device-scope
+// atomics are acknowledged first, then thread 0 arrives and polls until all n
+// chunk blocks have arrived.
+__device__ __forceinline__ void unit_arrive_wait(uint32_t* arrive, uint32_t n, uint32_t limit, uint32_t* err) {
+  wait_vm_acks();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t spins = 0;
+    while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+      if (++spins >= limit) {
+        if (err) atomicCAS(err, 0u, (uint32_t)CLO_E_TIMEOUT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_fused_kernel(LayerArgs a, Span sp,
+                                                                  const uint32_t* __restrict__ keys,
+                                                                  const uint32_t* __restrict__ h0,
+                                                                  uint32_t* __restrict__ fsync,
+                                                                  uint32_t* __restrict__ ccnt, int cmax,
+                                                                  uint32_t limit) {
+  constexpr int kLoads = kTopkChunk / (kTopkThreads * 4);  // 16-byte loads per thread
+  __shared__ u32x4 s_keys[kTopkChunk / 4];
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_prefix, s_mask, s_rem, s_x[4], s_y[4];
+  const int lo = *sp.lo;
+  const int n_units = *sp.hi - lo;
+  const int groups = (int)(gridDim.x / cmax);
+  const int c = (int)(blockIdx.x % cmax);
+  const int tid = threadIdx.x;
+  const int64_t N = a.N;
+  const int64_t c0 = (int64_t)c * kTopkChunk;
+  const int nk = (int)((c0 + kTopkChunk < N) ? kTopkChunk : N - c0);
+  for (int ui = (int)(blockIdx.x / cmax); ui < n_units; ui += groups) {  // the same units for a group's blocks
+    const int u = sp.list[lo + ui];
+    const uint32_t* kk = keys + (int64_t)u * a.Np + c0;
+    uint32_t* fs = fsync + (int64_t)u * kFusedSyncWords;
+    // the chunk's keys into LDS: all loads issued first (the row stride is a
+    // multiple of 64 keys, so a 16-byte load that starts below nk stays in the row)
+    {
+      u32x4 v[kLoads];
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        const int i = (j * kTopkThreads + tid) * 4;
+        v[j] = i < nk ? *reinterpret_cast<const u32x4*>(kk + i) : u32x4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();  // the previous unit's write has read s_keys
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) s_keys[j * kTopkThreads + tid] = v[j];
+    }
+    // digit 1 from the scoring histogram
+    s_hist[tid] = h0[(int64_t)u * 256 + tid];
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t d, above;
+      pick_digit(s_hist, (uint32_t)a.k, d, above);
+      if (tid == 0) {
+        s_prefix = d << 24;
+        s_mask = 0xFF000000u;
+        s_rem = (uint32_t)a.k - above;
+      }
+    }
+    __syncthreads();
+    for (int p = 0; p < 3; ++p) {
+      const int shift = 16 - 8 * p;
+      const uint32_t prefix = s_prefix, mask = s_mask, rem = s_rem;
+      s_hist[tid] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        const int i = (j * kTopkThreads + tid) * 4;
+        const u32x4 w = s_keys[j * kTopkThreads + tid];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (i + e < nk && (w[e] & mask) == prefix) atomicAdd(&s_hist[(w[e] >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (s_hist[tid]) atomicAdd(fs + p * 256 + tid, s_hist[tid]);
+      unit_arrive_wait(fs + 768 + p, (uint32_t)cmax, limit, a.err);
+      s_hist[tid] = __hip_atomic_load(fs + p * 256 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (tid < 64) {
+        uint32_t d, above;
+        pick_digit(s_hist, rem, d, above);
+        if (tid == 0) {
+          s_prefix = prefix | (d << shift);
+          s_mask = mask | (255u << shift);
+          s_rem = rem - above;
+        }
+      }
+      __syncthreads();
+    }
+    // T = the k-th largest key; `need` of the keys equal to T are taken, the first by index
+    const uint32_t T = s_prefix, need = s_rem;
+    uint32_t cg = 0, ce = 0;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int i = (j * kTopkThreads + tid) * 4;
+      const u32x4 w = s_keys[j * kTopkThreads + tid];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cg += (i + e < nk) && w[e] > T;
+        ce += (i + e < nk) && w[e] == T;
+      }
+    }
+    uint32_t tg, te;
+    block_sum2(cg, ce, s_x, s_y, tg, te);
+    uint32_t* cc = ccnt + (int64_t)u * cmax * kChunkHist;
+    if (tid == 0) {
+      __hip_atomic_store(cc + (int64_t)c * kChunkHist, tg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(cc + (int64_t)c * kChunkHist + 1, te, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    unit_arrive_wait(fs + 768 + 3, (uint32_t)cmax, limit, a.err);
+    // winners in the earlier chunks
+    uint32_t base_g, base_e;
+    {
+      uint32_t g = 0, e = 0;
+      if (tid < c) {
+        g = __hip_atomic_load(cc + (int64_t)tid * kChunkHist, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        e = __hip_atomic_load(cc + (int64_t)tid * kChunkHist + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      block_sum2(g, e, s_x, s_y, base_g, base_e);
+    }
+    // the winners of this chunk in ascending index order: tiles of kTopkThreads x
+    // kTopkPerThread consecutive keys, a block-wide scan per tile
+    int32_t* out = a.idx + (int64_t)u * a.k;
+    constexpr int kTile = kTopkThreads * kTopkPerThread;
+    for (int t0 = 0; t0 < nk; t0 += kTile) {  // uniform per block
+      const int i0 = t0 + tid * kTopkPerThread;
+      u32x4 v[kTopkPerThread / 4];
+#pragma unroll
+      for (int j = 0; j < kTopkPerThread / 4; ++j) v[j] = s_keys[(i0 >> 2) + j];
+      uint32_t xg = 0, xe = 0;
+#pragma unroll
+      for (int j = 0; j < kTopkPerThread / 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool valid = i0 + 4 * j + e < nk;
+          xg += valid && v[j][e] > T;
+          xe += valid && v[j][e] == T;
+        }
+      uint32_t eg, ee, sg, se;
+      scan2(xg, xe, s_x, s_y, eg, ee, sg, se);
+      uint32_t pg = base_g + eg, pe = base_e + ee;
+#pragma unroll
+      for (int j = 0; j < kTopkPerThread / 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + 4 * j + e;
+          if (i >= nk) continue;
+          const uint32_t kv = v[j][e];
+          if (kv > T) {
+            const uint32_t pos = pg + (pe < need ? pe : need);
+            if (pos < (uint32_t)a.k) out[pos] = (int32_t)(c0 + i);
+            ++pg;
+          } else if (kv == T) {
+            if (pe < need && pg + pe < (uint32_t)a.k) out[pg + pe] = (int32_t)(c0 + i);
+            ++pe;
+          }
+        }
+      base_g += sg;
+      base_e += se;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- A3 top-k over token blocks
 // Block b of a unit covers tokens b*bs .. b*bs+bs-1 (full blocks only); its key is
 // the largest of its tokens' keys (= the key of its best score).  Each CTA takes
@@ -1082,7 +1286,7 @@ __global__ __launch_bounds__(256) void block_keys_kernel(LayerArgs a, Span sp, c
                                                          uint32_t* __restrict__ bkeys, int64_t nb, int64_t npb,
                                                          int cmaxb, uint32_t* __restrict__ h0b,
                                                          uint32_t* __restrict__ h1, TopkState* __restrict__ st,
-                                                         int64_t kb) {
+                                                         int64_t kb, uint32_t* __restrict__ fs) {
   __shared__ uint32_t s_h[4][256];
   const UnitChunk uc = unit_chunk(sp, cmaxb);
   if (!uc.valid) return;
@@ -1113,6 +1317,7 @@ __global__ __launch_bounds__(256) void block_keys_kernel(LayerArgs a, Span sp, c
   if (uc.c == 0) {
     h1[(int64_t)uc.u * 256 + tid] = 0u;
     if (tid == 0) st[uc.u] = TopkState{0u, 0u, (uint32_t)kb, 0u};
+    clear_fused_sync(fs, uc.u);
   }
 }
 
@@ -1155,12 +1360,49 @@ __device__ __forceinline__ int list_gather_units(const LayerArgs& a, const uint8
   return total;
 }
 
+// The standalone gather's own wait: thread 0 of every block polls the flag
+// (acquire, agent scope, bounded as wait_kernel), the block waits at a barrier.
+__device__ __forceinline__ void gather_wait(const GatherSync& gs) {
+  if (!gs.wait_flag) return;
+  if (threadIdx.x == 0) {
+    uint32_t n = 0;
+    while (__hip_atomic_load(gs.wait_flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gs.wait_value) {
+      if (++n >= gs.limit) {
+        if (gs.error_word)
+          __hip_atomic_store(gs.error_word, (uint32_t)CLO_E_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  __syncthreads();
+}
+
+// End of a standalone gather: each wave releases its cache rows at agent scope
+// (written back past its XCD's L2), then the block counts itself done; the last
+// block clears the work counters for the next launch on the workspace and, with
+// a signal flag, publishes the layer with a release store.
+__device__ __forceinline__ void gather_finish(const GatherSync& gs, uint32_t* counter) {
+  if (!gs.done) return;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(gs.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == gridDim.x - 1) {
+      __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gs.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (gs.signal_flag)
+        __hip_atomic_store(gs.signal_flag, gs.signal_value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Rows of d elements are moved as 16-byte pieces: LPR lanes per row.  The
 // loads from pinned host memory are issued UNR rows deep per lane before any
 // store; grid x UNR sets the bytes in flight on the host link.
 template <typename T>
-__global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp,
-                                                     uint32_t* __restrict__ counter) {
+__device__ __forceinline__ void gather_native_rows(const LayerArgs& a, const uint8_t* __restrict__ reuse, Span sp,
+                                                   uint32_t* __restrict__ counter, uint32_t* err) {
   constexpr int RB = kHeadDim * (int)sizeof(T);  // row bytes
   constexpr int LPR = RB / 16;
   constexpr int RPI = 256 / LPR;
@@ -1198,7 +1440,7 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
     const int64_t r_end = (r0 + kGatherChunk < a.k) ? r0 + kGatherChunk : a.k;
     // the item's indices in one coalesced load, so that the host reads below
     // do not wait on an index load each time
-    if (r0 + threadIdx.x < r_end) s_src[threadIdx.x] = (int32_t)checked_row(ix[r0 + threadIdx.x], a.N, a.err);
+    if (r0 + threadIdx.x < r_end) s_src[threadIdx.x] = (int32_t)checked_row(ix[r0 + threadIdx.x], a.N, err);
     __syncthreads();
     for (int64_t rb = r0; rb < r_end; rb += RPI * UNR) {
       // rows past the end re-read the last row (in bounds) and are not stored
@@ -1221,6 +1463,14 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
       }
     }
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp,
+                                                     uint32_t* __restrict__ counter, GatherSync gs) {
+  gather_wait(gs);
+  gather_native_rows<T>(a, reuse, sp, counter, a.err);
+  gather_finish(gs, counter);
 }
 
 // Int8 host rows (CLO_HOST_INT8): 128 bytes per row, 8 lanes of 16 values each;
@@ -1262,8 +1512,8 @@ __device__ __forceinline__ void store_deq16<float>(float* dst, u32x4 w, float sc
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void gather_q8_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp,
-                                                        uint32_t* __restrict__ counter) {
+__device__ __forceinline__ void gather_q8_rows(const LayerArgs& a, const uint8_t* __restrict__ reuse, Span sp,
+                                               uint32_t* __restrict__ counter, uint32_t* err) {
   // one 256-byte record per token: lanes 0-7 of a row group read its K values,
   // lanes 8-15 its V values, in a single 16-lane load
   constexpr int kRec = 2 * kHeadDim;  // record bytes
@@ -1301,7 +1551,7 @@ __global__ __launch_bounds__(256) void gather_q8_kernel(LayerArgs a, const uint8
     const int64_t r0 = (int64_t)c * kGatherChunk;
     const int64_t r_end = (r0 + kGatherChunk < a.k) ? r0 + kGatherChunk : a.k;
     if (r0 + threadIdx.x < r_end) {
-      const int32_t src = (int32_t)checked_row(ix[r0 + threadIdx.x], a.N, a.err);
+      const int32_t src = (int32_t)checked_row(ix[r0 + threadIdx.x], a.N, err);
       s_src[threadIdx.x] = src;
       s_sc[0][threadIdx.x] = pow2f(a.k_exp[slot * a.C + src]);
       s_sc[1][threadIdx.x] = pow2f(a.v_exp[slot * a.C + src]);
@@ -1321,6 +1571,44 @@ __global__ __launch_bounds__(256) void gather_q8_kernel(LayerArgs a, const uint8
         if (row < r_end) store_deq16<T>(dst + row * kHeadDim + piece * 16, x[j], s_sc[half][row - r0]);
       }
     }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gather_q8_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp,
+                                                        uint32_t* __restrict__ counter, GatherSync gs) {
+  gather_wait(gs);
+  gather_q8_rows<T>(a, reuse, sp, counter, a.err);
+  gather_finish(gs, counter);
+}
+
+// The gathers of many layers in one launch (a resident kernel).  Layer by
+// layer the blocks wait for the layer's selection flag, take its items from the
+// layer's work counter, and count themselves done; the last block of a layer
+// clears its counters and publishes the layer.  A block that runs out of a
+// layer's items goes straight on to the next layer, so the layers' tails
+// overlap and no launch separates them.
+__global__ __launch_bounds__(256) void gather_layers_kernel(const GatherPlanLayer* __restrict__ plan, int n_layers,
+                                                            uint32_t wait_value, uint32_t signal_value,
+                                                            uint32_t limit, uint32_t* err) {
+  for (int l = 0; l < n_layers; ++l) {
+    const GatherPlanLayer& g = plan[l];
+    const GatherSync gs{g.wait_flag, wait_value, limit, err, g.signal_flag, signal_value, g.done};
+    gather_wait(gs);
+    const LayerArgs& a = g.a;
+    const Span all{nullptr, nullptr, nullptr};
+    if (a.host_fmt == CLO_HOST_INT8) {
+      if (a.dtype == CLO_F32)
+        gather_q8_rows<float>(a, g.reuse, all, g.counter, err);
+      else
+        gather_q8_rows<uint16_t>(a, g.reuse, all, g.counter, err);
+    } else if (a.dtype == CLO_F32) {
+      gather_native_rows<float>(a, g.reuse, all, g.counter, err);
+    } else {
+      gather_native_rows<uint16_t>(a, g.reuse, all, g.counter, err);
+    }
+    gather_finish(gs, g.counter);
+    __syncthreads();  // the next layer reuses the block's LDS
   }
 }
 
@@ -1378,8 +1666,11 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict_
   quantize_row_wave<T>(src + row * kHeadDim, dst + row * stride, dst_exp + row);
 }
 
-__global__ void zero_kernel(uint32_t* word) {
-  if (threadIdx.x == 0) *word = 0u;
+__global__ void zero_kernel(uint32_t* word, uint32_t* word2) {
+  if (threadIdx.x == 0) {
+    *word = 0u;
+    if (word2) *word2 = 0u;
+  }
 }
 
 // ---------------------------------------------------------------- A5 attention
@@ -1857,14 +2148,15 @@ hipError_t launch_score(const LayerArgs& a, const void* q, Span sp, int64_t max_
     if (a.dtype == CLO_F32) {
       const int64_t nch = (a.N + kScoreChunk - 1) / kScoreChunk;
       const int grid = grid_cap(max_units * nch, (int64_t)num_cu * 32);
-      score_kernel<float, G><<<grid, 256, 0, s>>>(a, static_cast<const float*>(q), sp, keys, w.h0, w.h1, w.tstate);
+      score_kernel<float, G><<<grid, 256, 0, s>>>(a, static_cast<const float*>(q), sp, keys, w.h0, w.h1, w.tstate,
+                                                  w.fsync);
     } else {
       // persistent: two blocks (eight waves) per CU keep enough 16-byte loads in
       // flight to stream K; more blocks only add contention
       const int64_t nch = (a.N + kScoreItem - 1) / kScoreItem;
       const int grid = grid_cap(max_units * nch, (int64_t)num_cu * 2);
       score_mfma_kernel<G><<<grid, 256, 0, s>>>(a, static_cast<const uint16_t*>(q), sp, keys, counter, w.h0, w.h1,
-                                                 w.tstate);
+                                                 w.tstate, w.fsync);
     }
     return hipGetLastError();
   });
@@ -1876,6 +2168,15 @@ hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uin
   if (cmax < kTopkMultiMin) {
     const int grid = grid_cap(max_units, 4096);
     topk_unit_kernel<<<grid, kUnitThreads, 0, s>>>(a, sp, keys, w.h0);
+    return hipGetLastError();
+  }
+  if (cmax <= kFusedMaxBlocks) {
+    // one launch: groups of cmax blocks, as many groups as the units need and
+    // kFusedMaxBlocks allows
+    const int64_t units = max_units > 0 ? max_units : 1;
+    const int64_t groups = units < kFusedMaxBlocks / cmax ? units : kFusedMaxBlocks / cmax;
+    topk_fused_kernel<<<(unsigned)(groups * cmax), kTopkThreads, 0, s>>>(a, sp, keys, w.h0, w.fsync, w.chist, cmax,
+                                                                        1u << 20);
     return hipGetLastError();
   }
   const int64_t grid = max_units * cmax;
@@ -1901,7 +2202,8 @@ hipError_t launch_select(const LayerArgs& a, Span sp, int64_t max_units, const W
   wb.cmax = (int32_t)((nb + kTopkChunk - 1) / kTopkChunk);
   const int cmaxb = (int)((nb + kBlockKeysPerCta - 1) / kBlockKeysPerCta);
   const unsigned g1 = (unsigned)(max_units * cmaxb > 0 ? max_units * cmaxb : 1);
-  block_keys_kernel<<<g1, 256, 0, s>>>(a, sp, w.keys, w.bkeys, nb, w.npb, cmaxb, w.h0b, w.h1, w.tstate, kb);
+  block_keys_kernel<<<g1, 256, 0, s>>>(a, sp, w.keys, w.bkeys, nb, w.npb, cmaxb, w.h0b, w.h1, w.tstate, kb,
+                                       w.fsync);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = launch_topk(ab, sp, max_units, w.bkeys, wb, s)) != hipSuccess) return e;
@@ -1912,19 +2214,29 @@ hipError_t launch_select(const LayerArgs& a, Span sp, int64_t max_units, const W
 }
 
 hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, Span sp, int64_t max_units, int max_blocks,
-                         uint32_t* counter, hipStream_t s) {
+                         uint32_t* counter, hipStream_t s, const GatherSync* gsp) {
   const int64_t nch = (a.k + kGatherChunk - 1) / kGatherChunk;
-  const int grid = grid_cap(max_units * nch, (int64_t)max_blocks);
+  // with its own wait the grid is fixed (every block arrives at the done count);
+  // otherwise it shrinks to the work when that is smaller
+  const int grid = gsp && gsp->wait_flag ? max_blocks : grid_cap(max_units * nch, (int64_t)max_blocks);
+  GatherSync gs{};
+  if (gsp) gs = *gsp;
   if (a.host_fmt == CLO_HOST_INT8) {
     if (a.dtype == CLO_F32)
-      gather_q8_kernel<float><<<grid, 256, 0, s>>>(a, reuse, sp, counter);
+      gather_q8_kernel<float><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
     else
-      gather_q8_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse, sp, counter);
+      gather_q8_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
   } else if (a.dtype == CLO_F32) {
-    gather_kernel<float><<<grid, 256, 0, s>>>(a, reuse, sp, counter);
+    gather_kernel<float><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
   } else {
-    gather_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse, sp, counter);
+    gather_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_layers(const GatherPlanLayer* plan, int n_layers, int blocks, uint32_t wait_value,
+                                uint32_t signal_value, uint32_t limit, uint32_t* error_word, hipStream_t s) {
+  gather_layers_kernel<<<blocks, 256, 0, s>>>(plan, n_layers, wait_value, signal_value, limit, error_word);
   return hipGetLastError();
 }
 
@@ -1946,8 +2258,8 @@ hipError_t launch_stream_read(const void* src, int64_t n16, int blocks, uint32_t
   return hipGetLastError();
 }
 
-hipError_t launch_zero(uint32_t* word, hipStream_t s) {
-  zero_kernel<<<1, 64, 0, s>>>(word);
+hipError_t launch_zero(uint32_t* word, hipStream_t s, uint32_t* word2) {
+  zero_kernel<<<1, 64, 0, s>>>(word, word2);
   return hipGetLastError();
 }
 

@@ -85,14 +85,14 @@ class LayerBuffers:
             self.v_cache = torch.zeros_like(self.k_cache)
         self.shape = clo.Shape(batch, hq, hkv, context, topk, tau, clo_dtype(dtype))
         ws = clo.clo_workspace_size(self.shape)
-        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
 
     def set_block_size(self, block_size: int):
         """Select token blocks of this size (0/1 = tokens); grows the workspace when needed."""
         self.shape.block_size = block_size
         need = clo.clo_workspace_size(self.shape)
         if need > self.ws.numel():
-            self.ws = torch.empty(need, dtype=torch.uint8, device=self.ws.device)
+            self.ws = torch.zeros(need, dtype=torch.uint8, device=self.ws.device)
 
     # ----------------------------------------------------------------- views
     def layer(self) -> clo.Layer:
@@ -260,7 +260,10 @@ class LayerLoop:
             concurrent scorings and top-k passes slowing each other and the
             gather more than the overlap gains);
     gather: waits for sel[l], reads layer l's selected rows from host memory,
-            then flag gat[l] = epoch;
+            then flag gat[l] = epoch -- by default one resident launch per step
+            over all layers (clo_gather_layers), whose blocks run from one
+            layer's tail straight into the next layer; gather="per-layer" uses
+            one clo_gather_kv launch per layer instead;
     attend: waits for gat[l], attention of layer l, then flag att[l] = epoch.
     The selection of layer l in the next step waits for att[l] of this step
     before overwriting layer l's selections.  Selection and gathering of layer
@@ -270,7 +273,9 @@ class LayerLoop:
     only read-only inputs.
     """
 
-    def __init__(self, layers, spin_limit: int = 0, select_streams: int = 1):
+    def __init__(self, layers, spin_limit: int = 0, select_streams: int = 1, gather: str = "resident"):
+        if gather not in ("resident", "per-layer"):
+            raise ValueError(gather)
         self.layers = layers
         L = len(layers)
         dev = layers[0].q.device
@@ -281,6 +286,13 @@ class LayerLoop:
         self.s_attend = torch.cuda.Stream(device=dev)
         self.epoch = 0
         self.spin_limit = spin_limit
+        self.gather = gather
+        self.plan = None
+        if gather == "resident":
+            self.plan = torch.zeros(clo.clo_gather_plan_size(L), dtype=torch.uint8, device=dev)
+            items = [(b.shape, b.layer(), b.reuse, b.ws, self._flag(0, l), self._flag(1, l))
+                     for l, b in enumerate(layers)]
+            self.plan_blocks = clo.clo_gather_plan(items, self.plan)
 
     def _flag(self, kind: int, l: int):
         return self.flags[kind, l]
@@ -294,6 +306,8 @@ class LayerLoop:
         self.epoch += 1
         e = self.epoch
         sp = self.spin_limit
+        resident = self.gather == "resident"
+        calls = []
         for l, b in enumerate(self.layers):
             tau = math.inf if cold else b.tau
             q = b.q_prev if cold else b.q
@@ -305,16 +319,29 @@ class LayerLoop:
                                     spin_limit=sp, signal_flag=self._flag(0, l), signal_value=e)
             s_sel = self.s_selects[l % len(self.s_selects)]
             clo.clo_reuse_select(shape, layer, q, b.q_prev, b.reuse, b.cos, b.ws, sync=sel_sync, stream=s_sel)
-            clo.clo_gather_kv(shape, layer, b.reuse, b.ws,
-                              sync=clo.Sync(wait_flag=self._flag(0, l), wait_value=e, signal_flag=self._flag(1, l),
-                                            signal_value=e, error_word=self.error, spin_limit=sp),
-                              stream=self.s_gather)
-            clo.clo_sparse_attn(shape, layer, q, b.out, b.ws,
-                                sync=clo.Sync(wait_flag=self._flag(1, l), wait_value=e, signal_flag=self._flag(2, l),
-                                              signal_value=e, error_word=self.error, spin_limit=sp),
-                                stream=self.s_attend)
+            if not resident:
+                clo.clo_gather_kv(shape, layer, b.reuse, b.ws,
+                                  sync=clo.Sync(wait_flag=self._flag(0, l), wait_value=e,
+                                                signal_flag=self._flag(1, l), signal_value=e,
+                                                error_word=self.error, spin_limit=sp),
+                                  stream=self.s_gather)
+                self._attend(b, shape, layer, q, l, e)
+            else:
+                calls.append((b, shape, layer, q, l))
+        if resident:
+            # every selection is enqueued before the gather that waits for it
+            clo.clo_gather_layers(self.plan, len(self.layers), self.plan_blocks, e, e, error_word=self.error,
+                                  spin_limit=sp, stream=self.s_gather)
+            for b, shape, layer, q, l in calls:
+                self._attend(b, shape, layer, q, l, e)
         # the caller's stream continues after the last attention
         cur.wait_stream(self.s_attend)
+
+    def _attend(self, b, shape, layer, q, l, e):
+        clo.clo_sparse_attn(shape, layer, q, b.out, b.ws,
+                            sync=clo.Sync(wait_flag=self._flag(1, l), wait_value=e, signal_flag=self._flag(2, l),
+                                          signal_value=e, error_word=self.error, spin_limit=self.spin_limit),
+                            stream=self.s_attend)
 
     def check(self):
         """Raise if any device-side wait timed out (call after a synchronize)."""
