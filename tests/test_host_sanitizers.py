@@ -28,8 +28,10 @@ def _run(cmd, **kw):
 def test_host_abi_under_address_and_undefined_sanitizers(tmp_path):
     from top_sparse_attention_02_amd import build
 
-    kobj = tmp_path / "kernels.o"
-    _run([build.hipcc(), *build.HIPCC_FLAGS, "-c", os.path.join(CSRC, "clo_kernels.hip"), "-o", str(kobj)])
+    kobjs = []
+    for src in sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")):
+        kobjs.append(str(tmp_path / (src + ".o")))
+        _run([build.hipcc(), *build.HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", kobjs[-1]])
     san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g", "-O1"]
     common = ["-std=c++17", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", f"-I{os.path.join(ROOT, 'include')}"]
     aobj, dobj = tmp_path / "api.o", tmp_path / "driver.o"
@@ -37,7 +39,7 @@ def test_host_abi_under_address_and_undefined_sanitizers(tmp_path):
     _run(["g++", *common, *san, "-c", os.path.join(ROOT, "tests", "host_sanitize", "abi_host_driver.cpp"), "-o",
           str(dobj)])
     exe = tmp_path / "abi_host_driver"
-    _run(["g++", *san, str(dobj), str(aobj), str(kobj), f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,{ROCM}/lib",
+    _run(["g++", *san, str(dobj), str(aobj), *kobjs, f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,{ROCM}/lib",
           "-o", str(exe)])
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
     r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)

@@ -28,12 +28,16 @@ def asm_text(tmp_path_factory):
     cc = B.hipcc()
     if not (os.path.isabs(cc) and os.path.exists(cc)) and shutil.which(cc) is None:
         pytest.skip("hipcc not found")
-    out = tmp_path_factory.mktemp("asm") / "clo_kernels.s"
-    src = os.path.join(B.CSRC, "clo_kernels.hip")
+    d = tmp_path_factory.mktemp("asm")
     flags = [f for f in B.HIPCC_FLAGS if f != "-fPIC"]
-    r = subprocess.run([cc, *flags, "--cuda-device-only", "-S", src, "-o", str(out)], capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    return out.read_text()
+    texts = []
+    for name in sorted(f for f in os.listdir(B.CSRC) if f.endswith(".hip")):
+        out = d / (name + ".s")
+        r = subprocess.run([cc, *flags, "--cuda-device-only", "-S", os.path.join(B.CSRC, name), "-o", str(out)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        texts.append(out.read_text())
+    return "\n".join(texts)
 
 
 def barriers_without_lds_wait(text):

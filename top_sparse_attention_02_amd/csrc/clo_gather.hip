@@ -1,0 +1,325 @@
+// HIP kernels of the gather (gfx950), A4: the selected K/V rows of offloaded
+// heads read by the GPU straight from pinned host memory into the HBM cache,
+// per layer or for many layers in one resident launch (CLO abstract, features
+// (2) and (3); "CLO (2511.14510) -- L3 Per-Paper Synthesis", section 2.1 item 3).
+#include <math.h>
+
+#include <type_traits>
+
+#include "../../include/clo.h"
+#include "clo_device.h"
+#include "clo_internal.h"
+
+namespace clo {
+namespace {
+
+// ---------------------------------------------------------------- A4 gather
+// Without a unit list (the standalone gather) every block first lists the units
+// it serves -- offloaded heads that miss, ascending -- in LDS, so that the work
+// counter runs over their items only instead of handing out (and skipping) the
+// items of reuse and persistent units one claim at a time.  Layers of more than
+// kGatherListCap units keep the skipping scheme.
+constexpr int kGatherListCap = 2048;
+
+__device__ __forceinline__ int list_gather_units(const LayerArgs& a, const uint8_t* __restrict__ reuse, int U,
+                                                 int32_t* s_units, uint32_t* s_wcnt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int total = 0;
+  for (int base = 0; base < U; base += 256) {
+    const int u = base + (int)threadIdx.x;
+    bool f = false;
+    if (u < U) f = !((a.pmask >> (u % a.Hkv)) & 1ull) && !(reuse && reuse[u]);
+    const uint64_t m = __ballot(f);
+    if (lane == 0) s_wcnt[wave] = (uint32_t)__popcll(m);
+    __syncthreads();
+    int off = total;
+    for (int w = 0; w < wave; ++w) off += (int)s_wcnt[w];
+    if (f) s_units[off + __popcll(m & ((1ull << lane) - 1ull))] = u;
+    total += (int)(s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3]);
+    __syncthreads();
+  }
+  return total;
+}
+
+// The standalone gather's own wait: thread 0 of every block polls the flag
+// (acquire, agent scope, bounded as wait_kernel), the block waits at a barrier.
+__device__ __forceinline__ void gather_wait(const GatherSync& gs) {
+  if (!gs.wait_flag) return;
+  if (threadIdx.x == 0) {
+    uint32_t n = 0;
+    while (__hip_atomic_load(gs.wait_flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gs.wait_value) {
+      if (++n >= gs.limit) {
+        if (gs.error_word)
+          __hip_atomic_store(gs.error_word, (uint32_t)CLO_E_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  __syncthreads();
+}
+
+// End of a standalone gather: each wave releases its cache rows at agent scope
+// (written back past its XCD's L2), then the block counts itself done; the last
+// block clears the work counters for the next launch on the workspace and, with
+// a signal flag, publishes the layer with a release store.
+__device__ __forceinline__ void gather_finish(const GatherSync& gs, uint32_t* counter) {
+  if (!gs.done) return;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(gs.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == gridDim.x - 1) {
+      __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gs.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (gs.signal_flag)
+        __hip_atomic_store(gs.signal_flag, gs.signal_value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Rows of d elements are moved as 16-byte pieces: LPR lanes per row.  The
+// loads from pinned host memory are issued UNR rows deep per lane before any
+// store; grid x UNR sets the bytes in flight on the host link.
+template <typename T>
+__device__ __forceinline__ void gather_native_rows(const LayerArgs& a, const uint8_t* __restrict__ reuse, Span sp,
+                                                   uint32_t* __restrict__ counter, uint32_t* err) {
+  constexpr int RB = kHeadDim * (int)sizeof(T);  // row bytes
+  constexpr int LPR = RB / 16;
+  constexpr int RPI = 256 / LPR;
+  constexpr int UNR = kGatherUnroll;
+  static_assert(kGatherChunk == 256, "one index per thread");
+  __shared__ uint32_t s_item;
+  __shared__ int32_t s_src[kGatherChunk];  // the item's source rows (checked_row)
+  __shared__ int32_t s_units[kGatherListCap];
+  __shared__ uint32_t s_wcnt[4];
+  const int nch = (int)((a.k + kGatherChunk - 1) / kGatherChunk);
+  const int lo = sp.list ? *sp.lo : 0;
+  const int U = a.B * a.Hkv;
+  const bool listed = !sp.list && U <= kGatherListCap;
+  const int64_t n_units = sp.list ? (int64_t)(*sp.hi - lo)
+                                  : (listed ? (int64_t)list_gather_units(a, reuse, U, s_units, s_wcnt) : (int64_t)U);
+  const int64_t items = n_units * nch;
+  const int sub = threadIdx.x % LPR, rl = threadIdx.x / LPR;
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(counter, 1u);
+    __syncthreads();
+    const int64_t it = s_item;
+    __syncthreads();
+    if (it >= items) break;  // uniform per block
+    const int u = sp.list ? sp.list[lo + it / nch] : (listed ? s_units[it / nch] : (int)(it / nch));
+    const int c = (int)(it % nch);
+    const int b = u / a.Hkv, h = u % a.Hkv;
+    if (!sp.list && !listed && (((a.pmask >> h) & 1ull) || (reuse && reuse[u]))) continue;
+    const int64_t slot = (int64_t)b * a.H + head_slot(a.pmask, h);
+    const char* ks = static_cast<const char*>(a.k_host) + slot * a.C * RB;
+    const char* vs = static_cast<const char*>(a.v_host) + slot * a.C * RB;
+    char* kd = static_cast<char*>(a.k_cache) + slot * a.k * RB;
+    char* vd = static_cast<char*>(a.v_cache) + slot * a.k * RB;
+    const int32_t* ix = a.idx + (int64_t)u * a.k;
+    const int64_t r0 = (int64_t)c * kGatherChunk;
+    const int64_t r_end = (r0 + kGatherChunk < a.k) ? r0 + kGatherChunk : a.k;
+    // the item's indices in one coalesced load, so that the host reads below
+    // do not wait on an index load each time
+    if (r0 + threadIdx.x < r_end) s_src[threadIdx.x] = (int32_t)checked_row(ix[r0 + threadIdx.x], a.N, err);
+    __syncthreads();
+    for (int64_t rb = r0; rb < r_end; rb += RPI * UNR) {
+      // rows past the end re-read the last row (in bounds) and are not stored
+      u32x4 kx[UNR], vx[UNR];
+#pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        int64_t row = rb + j * RPI + rl;
+        row = row < r_end ? row : r_end - 1;
+        const int64_t src = s_src[row - r0];
+        kx[j] = *reinterpret_cast<const u32x4*>(ks + src * RB + sub * 16);
+        vx[j] = *reinterpret_cast<const u32x4*>(vs + src * RB + sub * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        const int64_t row = rb + j * RPI + rl;
+        if (row < r_end) {
+          *reinterpret_cast<u32x4*>(kd + row * RB + sub * 16) = kx[j];
+          *reinterpret_cast<u32x4*>(vd + row * RB + sub * 16) = vx[j];
+        }
+      }
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp,
+                                                     uint32_t* __restrict__ counter, GatherSync gs) {
+  gather_wait(gs);
+  gather_native_rows<T>(a, reuse, sp, counter, a.err);
+  gather_finish(gs, counter);
+}
+
+// Int8 host rows (CLO_HOST_INT8): 128 bytes per row, 8 lanes of 16 values each;
+// the row's exponent e (device memory) turns q into q * 2^e, exact in T.  The
+// rest is the native kernel's scheme: items of 256 rows from a counter, the
+// item's source rows and exponents preloaded into LDS, 2 rows of K and V deep
+// per lane.
+__device__ __forceinline__ float pow2f(int e) { return __int_as_float((e + 127) << 23); }  // -126 <= e <= 127
+
+template <typename T>
+__device__ __forceinline__ void store_deq16(T* dst, u32x4 w, float scale);
+template <>
+__device__ __forceinline__ void store_deq16<uint16_t>(uint16_t* dst, u32x4 w, float scale) {
+  u32x4 o[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = w[i];
+    // four signed bytes -> exact products q * 2^e -> bf16 (exact: q has 7 bits)
+    const float f0 = (float)(int8_t)(x & 0xFFu) * scale, f1 = (float)(int8_t)((x >> 8) & 0xFFu) * scale;
+    const float f2 = (float)(int8_t)((x >> 16) & 0xFFu) * scale, f3 = (float)(int8_t)(x >> 24) * scale;
+    o[i / 2][(i % 2) * 2] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+    o[i / 2][(i % 2) * 2 + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
+  }
+  reinterpret_cast<u32x4*>(dst)[0] = o[0];
+  reinterpret_cast<u32x4*>(dst)[1] = o[1];
+}
+template <>
+__device__ __forceinline__ void store_deq16<float>(float* dst, u32x4 w, float scale) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = w[i];
+    u32x4 o;
+    o[0] = __float_as_uint((float)(int8_t)(x & 0xFFu) * scale);
+    o[1] = __float_as_uint((float)(int8_t)((x >> 8) & 0xFFu) * scale);
+    o[2] = __float_as_uint((float)(int8_t)((x >> 16) & 0xFFu) * scale);
+    o[3] = __float_as_uint((float)(int8_t)(x >> 24) * scale);
+    reinterpret_cast<u32x4*>(dst)[i] = o;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void gather_q8_rows(const LayerArgs& a, const uint8_t* __restrict__ reuse, Span sp,
+                                               uint32_t* __restrict__ counter, uint32_t* err) {
+  // one 256-byte record per token: lanes 0-7 of a row group read its K values,
+  // lanes 8-15 its V values, in a single 16-lane load
+  constexpr int kRec = 2 * kHeadDim;  // record bytes
+  constexpr int LPR = kRec / 16;      // 16 lanes per token
+  constexpr int RPI = 256 / LPR;
+  constexpr int UNR = 2 * kGatherUnroll;  // same bytes in flight as the native kernel
+  __shared__ uint32_t s_item;
+  __shared__ int32_t s_src[kGatherChunk];
+  __shared__ float s_sc[2][kGatherChunk];  // 2^e of the item's K and V rows
+  __shared__ int32_t s_units[kGatherListCap];
+  __shared__ uint32_t s_wcnt[4];
+  const int nch = (int)((a.k + kGatherChunk - 1) / kGatherChunk);
+  const int lo = sp.list ? *sp.lo : 0;
+  const int U = a.B * a.Hkv;
+  const bool listed = !sp.list && U <= kGatherListCap;
+  const int64_t n_units = sp.list ? (int64_t)(*sp.hi - lo)
+                                  : (listed ? (int64_t)list_gather_units(a, reuse, U, s_units, s_wcnt) : (int64_t)U);
+  const int64_t items = n_units * nch;
+  const int sub = threadIdx.x % LPR, rl = threadIdx.x / LPR;
+  const int half = sub >> 3, piece = sub & 7;  // 0 = K, 1 = V; 16-value piece of the row
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(counter, 1u);
+    __syncthreads();
+    const int64_t it = s_item;
+    __syncthreads();
+    if (it >= items) break;  // uniform per block
+    const int u = sp.list ? sp.list[lo + it / nch] : (listed ? s_units[it / nch] : (int)(it / nch));
+    const int c = (int)(it % nch);
+    const int b = u / a.Hkv, h = u % a.Hkv;
+    if (!sp.list && !listed && (((a.pmask >> h) & 1ull) || (reuse && reuse[u]))) continue;
+    const int64_t slot = (int64_t)b * a.H + head_slot(a.pmask, h);
+    const char* rec = static_cast<const char*>(a.k_host) + slot * a.C * kRec;
+    T* dst = static_cast<T*>(half ? a.v_cache : a.k_cache) + slot * a.k * kHeadDim;
+    const int32_t* ix = a.idx + (int64_t)u * a.k;
+    const int64_t r0 = (int64_t)c * kGatherChunk;
+    const int64_t r_end = (r0 + kGatherChunk < a.k) ? r0 + kGatherChunk : a.k;
+    if (r0 + threadIdx.x < r_end) {
+      const int32_t src = (int32_t)checked_row(ix[r0 + threadIdx.x], a.N, err);
+      s_src[threadIdx.x] = src;
+      s_sc[0][threadIdx.x] = pow2f(a.k_exp[slot * a.C + src]);
+      s_sc[1][threadIdx.x] = pow2f(a.v_exp[slot * a.C + src]);
+    }
+    __syncthreads();
+    for (int64_t rb = r0; rb < r_end; rb += RPI * UNR) {
+      u32x4 x[UNR];
+#pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        int64_t row = rb + j * RPI + rl;
+        row = row < r_end ? row : r_end - 1;
+        x[j] = *reinterpret_cast<const u32x4*>(rec + (int64_t)s_src[row - r0] * kRec + sub * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        const int64_t row = rb + j * RPI + rl;
+        if (row < r_end) store_deq16<T>(dst + row * kHeadDim + piece * 16, x[j], s_sc[half][row - r0]);
+      }
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gather_q8_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp,
+                                                        uint32_t* __restrict__ counter, GatherSync gs) {
+  gather_wait(gs);
+  gather_q8_rows<T>(a, reuse, sp, counter, a.err);
+  gather_finish(gs, counter);
+}
+
+// The gathers of many layers in one launch (a resident kernel).  Layer by
+// layer the blocks wait for the layer's selection flag, take its items from the
+// layer's work counter, and count themselves done; the last block of a layer
+// clears its counters and publishes the layer.  A block that runs out of a
+// layer's items goes straight on to the next layer, so the layers' tails
+// overlap and no launch separates them.
+__global__ __launch_bounds__(256) void gather_layers_kernel(const GatherPlanLayer* __restrict__ plan, int n_layers,
+                                                            uint32_t wait_value, uint32_t signal_value,
+                                                            uint32_t limit, uint32_t* err) {
+  for (int l = 0; l < n_layers; ++l) {
+    const GatherPlanLayer& g = plan[l];
+    const GatherSync gs{g.wait_flag, wait_value, limit, err, g.signal_flag, signal_value, g.done};
+    gather_wait(gs);
+    const LayerArgs& a = g.a;
+    const Span all{nullptr, nullptr, nullptr};
+    if (a.host_fmt == CLO_HOST_INT8) {
+      if (a.dtype == CLO_F32)
+        gather_q8_rows<float>(a, g.reuse, all, g.counter, err);
+      else
+        gather_q8_rows<uint16_t>(a, g.reuse, all, g.counter, err);
+    } else if (a.dtype == CLO_F32) {
+      gather_native_rows<float>(a, g.reuse, all, g.counter, err);
+    } else {
+      gather_native_rows<uint16_t>(a, g.reuse, all, g.counter, err);
+    }
+    gather_finish(gs, g.counter);
+    __syncthreads();  // the next layer reuses the block's LDS
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, Span sp, int64_t max_units, int max_blocks,
+                         uint32_t* counter, hipStream_t s, const GatherSync* gsp) {
+  const int64_t nch = (a.k + kGatherChunk - 1) / kGatherChunk;
+  // with its own wait the grid is fixed (every block arrives at the done count);
+  // otherwise it shrinks to the work when that is smaller
+  const int grid = gsp && gsp->wait_flag ? max_blocks : grid_cap(max_units * nch, (int64_t)max_blocks);
+  GatherSync gs{};
+  if (gsp) gs = *gsp;
+  if (a.host_fmt == CLO_HOST_INT8) {
+    if (a.dtype == CLO_F32)
+      gather_q8_kernel<float><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
+    else
+      gather_q8_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
+  } else if (a.dtype == CLO_F32) {
+    gather_kernel<float><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
+  } else {
+    gather_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_layers(const GatherPlanLayer* plan, int n_layers, int blocks, uint32_t wait_value,
+                                uint32_t signal_value, uint32_t limit, uint32_t* error_word, hipStream_t s) {
+  gather_layers_kernel<<<blocks, 256, 0, s>>>(plan, n_layers, wait_value, signal_value, limit, error_word);
+  return hipGetLastError();
+}
+
+}  // namespace clo

@@ -1,4 +1,5 @@
-// Internal launch interface between the C ABI (clo_api.cpp) and the HIP kernels (clo_kernels.hip).
+// Internal launch interface between the C ABI (clo_api.cpp) and the HIP kernel
+// sources (clo_select.hip, clo_gather.hip, clo_attn.hip, clo_kernels.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
