@@ -7,7 +7,9 @@ from .clo_oracle import (  # noqa: F401
     dequantize_row,
     decode_unit,
     group_cosine,
+    pack_int4,
     plan_persistent,
+    quant_max,
     quantize_row,
     quantized_rows,
     reuse_decision,

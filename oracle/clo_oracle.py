@@ -42,11 +42,12 @@ Synthesis"; CLO abstract page on fugumt):
     稀疏" (recall whole blocks so that each recall is one transfer).  The block
     score (max of its tokens' scores) and the full-blocks-only rule are this
     implementation's reading.
-  * Quantized host KV (quantize_row, dequantize_row, quantized_rows): the same
-    article, pillar 3, subsection "量化卸载" (quantize the offloaded KV, move
-    fewer bytes, dequantize on the GPU).  The format (int8 values, one
-    power-of-two scale per row) is this implementation's choice, written out
-    at quantize_row.  Scoring keeps the exact keys; attention of offloaded
+  * Quantized host KV (quantize_row, dequantize_row, quantized_rows,
+    pack_int4): the same article, pillar 3, subsection "量化卸载" (quantize the
+    offloaded KV, move fewer bytes, dequantize on the GPU; its examples go down
+    to 2 and 3 bits).  The formats (8- or 4-bit values, one power-of-two scale
+    per row; 4-bit values two to a byte) are this implementation's choice,
+    written out at quantize_row and pack_int4.  Scoring keeps the exact keys; attention of offloaded
     heads reads the dequantized rows (decode_unit's K_attn / V_attn).
   * Multi-step decoding (decode_steps_unit): synthesis section 2.1 item 2 --
     the similarity is between adjacent decode steps; section 5.7 -- a KV cache
@@ -239,21 +240,35 @@ def plan_persistent(s_hat, n_persist: int):
 
 
 QUANT_MIN_EXP = -120
+QUANT_BITS = (8, 4)
 
 
-def quantize_row(x):
-    """Int8 host format of one row: (q, e) with x ~ q * 2^e.
+def quant_max(bits: int) -> int:
+    """Largest |q| of the signed `bits`-bit format: 2^(bits-1) - 1 (127 or 7).
+    The most negative code (-128, -8) is left unused so that the range is
+    symmetric."""
+    if bits not in QUANT_BITS:
+        raise ValueError(f"bits must be one of {QUANT_BITS}")
+    return 2 ** (bits - 1) - 1
 
-    m = max |x_i|; e = the smallest integer with m <= 127 * 2^e (0 for a zero
-    row), raised to -120 if smaller; q_i = x_i * 2^-e rounded to the nearest
-    integer, ties to even (|q_i| <= 127 by the choice of e).
+
+def quantize_row(x, bits: int = 8):
+    """Host format of one row with `bits`-bit values: (q, e) with x ~ q * 2^e.
+
+    M = quant_max(bits); m = max |x_i|; e = the smallest integer with
+    m <= M * 2^e (0 for a zero row), raised to -120 if smaller; q_i = x_i * 2^-e
+    rounded to the nearest integer, ties to even (|q_i| <= M by the choice of e).
     """
+    M = quant_max(bits)
     x = np.asarray(x, dtype=np.float64)
     m = float(np.max(np.abs(x))) if x.size else 0.0
     if m == 0.0:
         return np.zeros(x.shape, dtype=np.int64), 0
-    e = math.frexp(m)[1] - 1 - 6  # floor(log2 m) - 6
-    if m > 127.0 * 2.0 ** e:
+    # 2^f <= M < 2^(f+1) with f = floor(log2 M); floor(log2 m) - f is the
+    # smallest exponent that can hold m, or one below it
+    f = math.frexp(M)[1] - 1
+    e = math.frexp(m)[1] - 1 - f
+    if m > M * 2.0 ** e:
         e += 1
     e = max(e, QUANT_MIN_EXP)
     q = np.rint(x * 2.0 ** -e).astype(np.int64)
@@ -265,13 +280,22 @@ def dequantize_row(q, e: int) -> np.ndarray:
     return np.asarray(q, dtype=np.float64) * 2.0 ** e
 
 
-def quantized_rows(X) -> np.ndarray:
+def quantized_rows(X, bits: int = 8) -> np.ndarray:
     """Every row of X [n, d] through quantize_row and dequantize_row."""
     X = np.asarray(X, dtype=np.float64)
     out = np.empty_like(X)
     for i in range(X.shape[0]):
-        out[i] = dequantize_row(*quantize_row(X[i]))
+        out[i] = dequantize_row(*quantize_row(X[i], bits))
     return out
+
+
+def pack_int4(q) -> bytes:
+    """Bytes of a row of 4-bit values: value 2j in the low half of byte j and
+    value 2j+1 in the high half, each as a 4-bit two's complement code."""
+    q = [int(v) for v in q]
+    if len(q) % 2 or any(not -8 <= v <= 7 for v in q):
+        raise ValueError("an even number of values in [-8, 7]")
+    return bytes((q[2 * j] & 0xF) | ((q[2 * j + 1] & 0xF) << 4) for j in range(len(q) // 2))
 
 
 def select_blocks(s: np.ndarray, k: int, block_size: int) -> np.ndarray:

@@ -395,7 +395,15 @@ def pin_plan_persistent(O):
         assert chosen == list(best)
 
 
-# ---------------------------------------------------------------- int8 host format
+# ---------------------------------------------------------------- quantized host formats
+def raises(exc, fn, *args) -> bool:
+    try:
+        fn(*args)
+    except exc:
+        return True
+    return False
+
+
 def pin_quantize_closed_forms(O):
     # m = 1: 127 * 2^-7 = 0.99 < 1 <= 127 * 2^-6 = 1.98, so e = -6 and q = x * 64
     q, e = O.quantize_row([1.0, -0.5, 0.25, 0.0])
@@ -448,6 +456,66 @@ def pin_quantized_rows_closed_form(O):
     # flush 2^-10 to 0 next to 64
     Y = np.array([[64.0, -32.0, 16.0], [2.0 ** -10, 0.0, -(2.0 ** -12)]])
     assert np.array_equal(O.quantized_rows(Y), Y)
+
+
+def pin_quantize4_closed_forms(O):
+    # 4-bit values, M = 7: m = 1 has 7 * 2^-3 = 0.875 < 1 <= 7 * 2^-2 = 1.75, so
+    # e = -2 and q = x * 4
+    assert O.quant_max(4) == 7 and O.quant_max(8) == 127
+    q, e = O.quantize_row([1.0, -0.5, 0.25, 0.0], 4)
+    assert e == -2 and list(q) == [4, -2, 1, 0]
+    # m exactly 7 * 2^-2 keeps e = -2 (q = 7); the next float up needs e = -1,
+    # where 1.75+ / 0.5 = 3.5+ rounds up to 4
+    q, e = O.quantize_row([1.75, 1.0], 4)
+    assert e == -2 and list(q) == [7, 4]
+    q, e = O.quantize_row([np.nextafter(1.75, 2.0), 1.0], 4)
+    assert e == -1 and list(q) == [4, 2]
+    # ties to even at e = -1 (m = 3.5): 0.75 -> 1.5 -> 2, 1.25 -> 2.5 -> 2, -0.25 -> -0.5 -> 0
+    q, e = O.quantize_row([3.5, 0.75, 1.25, -0.25], 4)
+    assert e == -1 and list(q) == [7, 2, 2, 0]
+    # m = 300: 7 * 32 = 224 < 300 <= 448 = 7 * 64, so e = 6; 300 / 64 = 4.6875 -> 5
+    q, e = O.quantize_row([300.0, -1.0, 0.5], 4)
+    assert e == 6 and list(q) == [5, 0, 0]
+    # zero rows and the smallest exponent
+    q, e = O.quantize_row([0.0, 0.0], 4)
+    assert e == 0 and list(q) == [0, 0]
+    q, e = O.quantize_row([2.0 ** -130, -(2.0 ** -125)], 4)
+    assert e == -120 and list(q) == [0, 0]
+    for bad in (0, 2, 16):
+        assert raises(ValueError, O.quantize_row, [1.0], bad)
+
+
+def pin_quantize4_invariants(O):
+    rng = np.random.default_rng(14)
+    for _ in range(200):
+        x = rng.standard_normal(128) * 2.0 ** rng.integers(-20, 20)
+        q, e = O.quantize_row(x, 4)
+        m = np.max(np.abs(x))
+        assert np.max(np.abs(q)) <= 7 and m <= 7 * 2.0 ** e and not m <= 7 * 2.0 ** (e - 1)
+        assert np.max(np.abs(O.dequantize_row(q, e) - x)) <= 2.0 ** (e - 1)
+        # the 8-bit exponent of the same row is 4 lower (127 / 7 lies between 2^4 and 2^5)
+        # or 5 lower, and the 4-bit grid is a subset of the 8-bit one
+        q8, e8 = O.quantize_row(x, 8)
+        assert e - e8 in (4, 5)
+        q2, e2 = O.quantize_row(x * 0.25, 4)
+        assert e2 == e - 2 and list(q2) == list(q)
+    # quantized_rows takes the width along: 0.3 next to 1 becomes 1/4 with 4 bits
+    assert np.array_equal(O.quantized_rows(np.array([[1.0, 0.3]]), 4), np.array([[1.0, 0.25]]))
+
+
+def pin_pack_int4(O):
+    # value 2j in the low half of byte j, value 2j+1 in the high half, two's complement
+    assert O.pack_int4([1, -1, 7, -7]) == bytes([0xF1, 0x97])
+    assert O.pack_int4([4, -2, 1, 0]) == bytes([0xE4, 0x01])
+    assert O.pack_int4([-8, 0, 0, -8]) == bytes([0x08, 0x80])
+    # every pair of codes round-trips through the nibbles
+    for a in range(-8, 8):
+        for b in range(-8, 8):
+            byte = O.pack_int4([a, b])[0]
+            lo, hi = byte & 0xF, byte >> 4
+            assert (lo - 16 if lo >= 8 else lo, hi - 16 if hi >= 8 else hi) == (a, b)
+    for bad in ([1], [8, 0], [0, -9]):
+        assert raises(ValueError, O.pack_int4, bad)
 
 
 # ---------------------------------------------------------------- block selection
@@ -672,6 +740,14 @@ def pin_golden_int8_rows(O):
         assert list(O.dequantize_row(q, e)) == [v * 2.0 ** c["e"] for v in c["q"]], c
 
 
+def pin_golden_int4_rows(O):
+    for c in golden("int4_rows.json")["cases"]:
+        x = golden_array(c["x"])
+        q, e = O.quantize_row(x, 4)
+        assert e == c["e"] and list(q) == c["q"], c
+        assert O.pack_int4(q).hex() == c["bytes"], c
+
+
 ALL_PINS = [
     pin_cosine_closed_forms,
     pin_cosine_group_concatenated,
@@ -696,6 +772,9 @@ ALL_PINS = [
     pin_quantize_closed_forms,
     pin_quantize_invariants,
     pin_quantized_rows_closed_form,
+    pin_quantize4_closed_forms,
+    pin_quantize4_invariants,
+    pin_pack_int4,
     pin_select_blocks_closed_form,
     pin_select_blocks_invariants,
     pin_decode_unit_attn_rows,
@@ -708,4 +787,5 @@ ALL_PINS = [
     pin_golden_decode_step,
     pin_golden_growing_context,
     pin_golden_int8_rows,
+    pin_golden_int4_rows,
 ]

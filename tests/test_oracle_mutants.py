@@ -93,8 +93,18 @@ MUTANTS = {
                          "q = (np.sign(x) * np.floor(np.abs(x * 2.0 ** -e) + 0.5)).astype(np.int64)"),
     "dequant_wrong_sign_exponent": E("return np.asarray(q, dtype=np.float64) * 2.0 ** e",
                                      "return np.asarray(q, dtype=np.float64) * 2.0 ** -e"),
-    "quantized_rows_by_column": E("    for i in range(X.shape[0]):\n        out[i] = dequantize_row(*quantize_row(X[i]))",
-                                  "    for i in range(X.shape[1]):\n        out[:, i] = dequantize_row(*quantize_row(X[:, i]))"),
+    "quantized_rows_by_column": E("    for i in range(X.shape[0]):\n        out[i] = dequantize_row(*quantize_row(X[i], bits))",
+                                  "    for i in range(X.shape[1]):\n        out[:, i] = dequantize_row(*quantize_row(X[:, i], bits))"),
+    # 4-bit rows: the range's exponent off by one, 8 levels, the width dropped
+    # on the way through quantized_rows, the nibbles swapped or unsigned
+    "quant_range_exponent_high": E("f = math.frexp(M)[1] - 1", "f = math.frexp(M)[1]"),
+    "quant4_eight_levels": E("return 2 ** (bits - 1) - 1", "return 2 ** (bits - 1) - (1 if bits == 8 else 0)"),
+    "quantized_rows_drops_width": E("out[i] = dequantize_row(*quantize_row(X[i], bits))",
+                                    "out[i] = dequantize_row(*quantize_row(X[i]))"),
+    "pack_nibbles_swapped": E("(q[2 * j] & 0xF) | ((q[2 * j + 1] & 0xF) << 4)",
+                              "((q[2 * j] & 0xF) << 4) | (q[2 * j + 1] & 0xF)"),
+    "pack_offset_binary": E("(q[2 * j] & 0xF) | ((q[2 * j + 1] & 0xF) << 4)",
+                            "((q[2 * j] + 8) & 0xF) | (((q[2 * j + 1] + 8) & 0xF) << 4)"),
     # block selection
     "blocks_scored_by_sum": E("bscore = s[:nb * block_size].reshape(nb, block_size).max(axis=1)",
                               "bscore = s[:nb * block_size].reshape(nb, block_size).sum(axis=1)"),
