@@ -57,15 +57,15 @@ def parse():
                     help="choose the persistent heads from profiling (mean reuse-test cosine per slot on "
                          "separately seeded instances, lowest first) instead of the seeded draw; same count")
     ap.add_argument("--profile-instances", type=int, default=8)
-    ap.add_argument("--host-kv", choices=["native", "int8"], default="native",
-                    help="format of the offloaded K/V in host memory: the step's dtype, or int8 rows with one "
-                         "power-of-two scale per row (half the host-link bytes of bf16; dequantized exactly "
-                         "by the gather)")
+    ap.add_argument("--host-kv", choices=["native", "int8", "int4"], default="native",
+                    help="format of the offloaded K/V in host memory: the step's dtype, or int8 / int4 rows with "
+                         "one power-of-two scale per row (a half / a quarter of the host-link bytes of bf16; "
+                         "dequantized exactly by the gather)")
     ap.add_argument("--block-size", type=int, default=0, metavar="B",
                     help="select blocks of B consecutive tokens instead of tokens (top-k a multiple of B: "
                          "k is rounded down to one)")
     ap.add_argument("--no-compare-native", action="store_true",
-                    help="int8 host KV, configs 1-3: skip the output comparison against the native format")
+                    help="quantized host KV, configs 1-3: skip the output comparison against the native format")
     ap.add_argument("--select-streams", type=int, default=1, metavar="S",
                     help="48-layer loop: streams the layers' selections alternate between")
     ap.add_argument("--graph", action="store_true",
@@ -84,8 +84,8 @@ def algorithmic_bytes(layers):
 
     HBM: M * N * d * b (scoring) + M_p * k * 2 d b (persistent miss rows)
          + M_np * k * 2 d b (cache writes) + H * k * 2 d b (rows of reuse units)
-    host: M_np * k * 2 d b_host (b_host = 1 for the int8 host format, whose row
-          exponents come from HBM: + M_np * k * 2 bytes there)
+    host: M_np * k * 2 d b_host (b_host = 1 for the int8 host format and 1/2 for
+          int4, whose row exponents come from HBM: + M_np * k * 2 bytes there)
     """
     import numpy as np
 
@@ -108,8 +108,9 @@ def algorithmic_bytes(layers):
         tot["misses_host"] += M_np
         tot["hits"] += H
         tot["score_bytes"] += score
-        q8 = getattr(bufs, "host_format", 0) == 1
-        host_row2 = bufs.k * 2 * HEAD_DIM * (1 if q8 else b)
+        fmt = getattr(bufs, "host_format", 0)
+        q8 = fmt != 0  # a quantized host format
+        host_row2 = bufs.k * 2 * {0: HEAD_DIM * b, 1: HEAD_DIM, 2: HEAD_DIM // 2}[fmt]
         tot["hbm_bytes"] += score + M_p * row2 + M_np * row2 + H * row2 + (M_np * bufs.k * 2 if q8 else 0)
         tot["host_bytes"] += M_np * host_row2
         tot["attn_bytes"] += bufs.B * bufs.Hkv * row2
@@ -552,7 +553,7 @@ def compare_tokens(torch, bufs, step_kind: int) -> dict:
 
 
 def compare_native(torch, workload, p, q8_layer, step_kind: int, flags) -> dict:
-    """Output of the int8-host-KV step against the same step with native host
+    """Output of the quantized-host-KV step against the same step with native host
     rows (the same inputs loaded a second time): normwise relative deviation per
     (sequence, query head), max_i |o_i - n_i| / max_i |n_i|, and how many
     selections differ (none can: scoring reads the exact keys in both)."""
@@ -622,7 +623,8 @@ def main():
              "coherent": hip_host.hipHostMallocMapped | hip_host.hipHostMallocCoherent,
              "noncoherent": hip_host.hipHostMallocMapped | hip_host.hipHostMallocNonCoherent}[args.host_memory]
     t0 = time.time()
-    host_format = clo.CLO_HOST_INT8 if args.host_kv == "int8" else clo.CLO_HOST_NATIVE
+    host_format = {"native": clo.CLO_HOST_NATIVE, "int8": clo.CLO_HOST_INT8,
+                   "int4": clo.CLO_HOST_INT4}[args.host_kv]
     if multi:
         layers = workload.load_layers(p, log=log, host_flags=flags, host_format=host_format)
     else:
@@ -713,9 +715,9 @@ def main():
         log(f"blocks of {args.block_size} vs tokens: output deviation mean {blocks['out_dev_mean']:.3f}, "
             f"selection overlap {blocks['selection_overlap']:.3f}")
     quant = None
-    if host_format == clo.CLO_HOST_INT8 and not multi and not args.no_compare_native:
+    if host_format != clo.CLO_HOST_NATIVE and not multi and not args.no_compare_native:
         quant = compare_native(torch, workload, p, layers[0], args.step, flags)
-        log(f"int8 host KV vs native: output deviation mean {quant['out_dev_mean']:.2e}, "
+        log(f"{args.host_kv} host KV vs native: output deviation mean {quant['out_dev_mean']:.2e}, "
             f"max {quant['out_dev_max']:.2e}")
     phases = phase_times(torch, clo, layers, args.step, passes=args.steps if not multi else 2)
     gather_s = phases["gather"] / 1e3
@@ -783,7 +785,7 @@ def main():
                    (", steady step (80/20 reuse)" if args.step == 1 else ", cold step (all miss)") +
                    (f", {args.volatile:.0%} volatile (layer, KV head) slots" if args.volatile else "") +
                    (", persistent heads from profiling" if plan else "") +
-                   (", int8 host KV (power-of-two row scales)" if args.host_kv == "int8" else "") +
+                   (f", {args.host_kv} host KV (power-of-two row scales)" if args.host_kv != "native" else "") +
                    (f", selection in blocks of {args.block_size} tokens, k={p.topk}" if args.block_size > 1 else ""),
                    "layers": p.layers, "batch": p.batch, "q_heads": p.hq, "kv_heads": p.hkv, "head_dim": HEAD_DIM,
                    "context": p.context, "topk": p.topk, "tau": p.tau, "step": args.step,
@@ -817,7 +819,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of units")
         if args.host_kv != "native":
-            # the oracle reads stored rows of the step's dtype; the int8 host copy
+            # the oracle reads stored rows of the step's dtype; the quantized host copy
             # holds none, so the native-format baseline is the one to compare with
             result["cpu_baseline"] = None
         else:

@@ -49,7 +49,9 @@
  *   k_hbm, v_hbm     [B, P, C, d]   device   full K/V of persistent heads (rows < N used)
  *   k_host, v_host   [B, H, C, d]   pinned   full K/V of non-persistent heads; with
  *                                            CLO_HOST_INT8: k_host [B, H, C, 2, d] int8
- *                                            (K row, V row per token), v_host unused
+ *                                            (K row, V row per token), v_host unused;
+ *                                            CLO_HOST_INT4: k_host [B, H, C, 2, d/2] uint8
+ *                                            (4-bit K row, V row per token), v_host unused
  *   k_score          [B, H, C, d]   device   copy of k_host read by scoring
  *   k_cache, v_cache [B, H, k, d]   device   rows k_host[idx], v_host[idx]
  *   idx              [B, Hkv, k]    int32    selected token indices, ascending
@@ -79,8 +81,17 @@ typedef enum { CLO_F32 = 0, CLO_BF16 = 1 } clo_dtype;
  *                    e = the smallest integer with m <= 127 * 2^e (e = 0 when m = 0),
  *                    raised to -120 if smaller; q_i = x_i * 2^-e rounded to the
  *                    nearest integer, ties to even.  q_i * 2^e is exact in bf16 and
- *                    fp32, so dequantized rows are exact. */
-typedef enum { CLO_HOST_NATIVE = 0, CLO_HOST_INT8 = 1 } clo_host_format;
+ *                    fp32, so dequantized rows are exact.
+ *   CLO_HOST_INT4    the same with 4-bit values: q_i in [-7, 7], e the smallest
+ *                    integer with m <= 7 * 2^e (0 when m = 0), at least -120, q_i =
+ *                    x_i * 2^-e rounded to nearest even.  A row is 64 bytes, value 2j
+ *                    in the low 4 bits of byte j and value 2j+1 in the high 4 bits,
+ *                    each as a 4-bit two's complement code; a token is one 128-byte
+ *                    record (K row, then V row) in k_host; exponents as for
+ *                    CLO_HOST_INT8.  The same article's quantized offloading
+ *                    passage gives 2- and 3-bit schemes as examples; the format here
+ *                    is this library's. */
+typedef enum { CLO_HOST_NATIVE = 0, CLO_HOST_INT8 = 1, CLO_HOST_INT4 = 2 } clo_host_format;
 
 typedef enum {
   CLO_OK = 0,
@@ -135,7 +146,7 @@ typedef struct {
   void* v_cache;
   int32_t* idx;              /* [B, Hkv, k] device, written for miss units, read for all units */
   int32_t host_format;       /* clo_host_format of k_host / v_host (0 = the shape's dtype) */
-  const int8_t* k_host_exp;  /* CLO_HOST_INT8: [B, H, C] device, row scale exponents of k_host */
+  const int8_t* k_host_exp;  /* CLO_HOST_INT8/INT4: [B, H, C] device, row scale exponents of k_host */
   const int8_t* v_host_exp;  /*                [B, H, C] device, of v_host */
 } clo_layer;
 
@@ -336,7 +347,8 @@ clo_status clo_decode_step_static(const clo_shape* shape, const clo_layer* layer
  * as row `position` of every (sequence, KV head): into k_hbm/v_hbm for
  * persistent heads; for the others into k_host/v_host, stored by the GPU
  * straight into pinned host memory (quantized first when the layer's
- * host_format is CLO_HOST_INT8, its exponents into k_host_exp/v_host_exp), and
+ * host_format is CLO_HOST_INT8 or CLO_HOST_INT4, its exponents into
+ * k_host_exp/v_host_exp), and
  * into the k_score copy.  Requires
  * 0 <= position < capacity (CLO_E_ARG otherwise); shape->context is not used
  * beyond validation and the row is visible to later calls on the same stream
@@ -374,18 +386,20 @@ clo_status clo_plan_persistent(const float* s_hat, int32_t n_layers, int32_t n_k
                                uint64_t* masks);
 
 /*
- * Quantize rows for an int8 host copy (CLO_HOST_INT8; quantized offloaded KV,
- * KV-cache offloading article, pillar 3, quantized offloading: fewer bytes cross
- * the host link and the GPU dequantizes).
+ * Quantize rows for a quantized host copy (CLO_HOST_INT8 or CLO_HOST_INT4;
+ * quantized offloaded KV, KV-cache offloading article, pillar 3, quantized
+ * offloading: fewer bytes cross the host link and the GPU dequantizes).
  * Reads n_rows rows of 128 elements of `dtype` from src (device), writes their
- * int8 values to dst (device or pinned host memory; row r at dst + r *
- * dst_stride bytes, dst_stride >= 128 and a multiple of 16: 256 fills the K or V
- * half of CLO_HOST_INT8 records) and their scale exponents to dst_exp (device,
- * [n_rows]), by the rule documented at clo_host_format.  Finite inputs only.
+ * quantized values (host_format CLO_HOST_INT8: 128 bytes per row; CLO_HOST_INT4:
+ * 64 bytes) to dst (device or pinned host memory; row r at dst + r * dst_stride
+ * bytes, dst_stride at least the row's bytes and a multiple of 16: twice the
+ * row's bytes fills the K or V half of the format's records) and their scale
+ * exponents to dst_exp (device, [n_rows]), by the rules documented at
+ * clo_host_format.  CLO_E_ARG for another host_format.  Finite inputs only.
  * sync may be NULL.
  */
-clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int64_t dst_stride,
-                             int8_t* dst_exp, const clo_sync* sync, void* stream);
+clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int32_t host_format, void* dst,
+                             int64_t dst_stride, int8_t* dst_exp, const clo_sync* sync, void* stream);
 
 /*
  * Measurement helper (no step of the method): reads `bytes` (a multiple of 16)

@@ -99,8 +99,14 @@ int main() {
     CHECK(clo_stream_read(nullptr, 17, 1, nullptr, nullptr) == CLO_E_ARG);
     CHECK(clo_stream_read(nullptr, 16, 0, nullptr, nullptr) == CLO_E_ARG);
     CHECK(clo_stream_read(nullptr, 0, 1, nullptr, nullptr) == CLO_OK);
-    CHECK(clo_quantize_rows(nullptr, 0, 5, nullptr, 128, nullptr, nullptr, nullptr) == CLO_E_UNSUPPORTED);
-    CHECK(clo_quantize_rows(nullptr, -1, CLO_BF16, nullptr, 128, nullptr, nullptr, nullptr) == CLO_E_ARG);
+    CHECK(clo_quantize_rows(nullptr, 0, 5, CLO_HOST_INT8, nullptr, 128, nullptr, nullptr, nullptr) ==
+          CLO_E_UNSUPPORTED);
+    CHECK(clo_quantize_rows(nullptr, -1, CLO_BF16, CLO_HOST_INT8, nullptr, 128, nullptr, nullptr, nullptr) == CLO_E_ARG);
+    CHECK(clo_quantize_rows(nullptr, 0, CLO_BF16, CLO_HOST_NATIVE, nullptr, 128, nullptr, nullptr, nullptr) ==
+          CLO_E_ARG);
+    CHECK(clo_quantize_rows(nullptr, 0, CLO_BF16, CLO_HOST_INT8, nullptr, 64, nullptr, nullptr, nullptr) == CLO_E_ARG);
+    CHECK(clo_quantize_rows(nullptr, 0, CLO_BF16, CLO_HOST_INT4, nullptr, 64, nullptr, nullptr, nullptr) == CLO_OK);
+    CHECK(clo_quantize_rows(nullptr, 0, CLO_BF16, CLO_HOST_INT4, nullptr, 56, nullptr, nullptr, nullptr) == CLO_E_ARG);
   }
 
   // the last-error buffer at every length, including 0 and 1

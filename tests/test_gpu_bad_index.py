@@ -21,7 +21,7 @@ def _bf16_bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("host_format", [0, 1])
+@pytest.mark.parametrize("host_format", [0, 1, 2])
 def test_gather_reports_out_of_range_index(need_gpu, host_format):
     import torch
 
@@ -53,14 +53,21 @@ def test_gather_reports_out_of_range_index(need_gpu, host_format):
         vh[:] = rng.integers(0, 1 << 16, size=vh.shape, dtype=np.uint16)
         layer = clo.Layer(0, None, None, kh_buf.ptr, vh_buf.ptr, None, k_cache, v_cache, idx_d)
     else:
-        rec = HostBuffer(B * hkv * N * 2 * D)
+        # quantized records: K values then V values per token (int8: one byte per
+        # value; int4: value 2j in the low half of byte j)
+        rb = D if host_format == 1 else D // 2
+        rec = HostBuffer(B * hkv * N * 2 * rb)
         bufs = [rec]
-        r = rec.numpy("i1", (B, hkv, N, 2, D))
-        r[:] = rng.integers(-127, 128, size=r.shape, dtype=np.int8)
+        lim = 127 if host_format == 1 else 7
+        vals = rng.integers(-lim, lim + 1, size=(B, hkv, N, 2, D))
+        r = rec.numpy("u1", (B, hkv, N, 2, rb))
+        if host_format == 1:
+            r[:] = vals.astype(np.int8).view(np.uint8)
+        else:
+            r[:] = ((vals[..., 0::2] & 0xF) | ((vals[..., 1::2] & 0xF) << 4)).astype(np.uint8)
         k_exp = torch.from_numpy(rng.integers(-10, 2, size=(B, hkv, N), dtype=np.int8)).cuda()
         v_exp = torch.from_numpy(rng.integers(-10, 2, size=(B, hkv, N), dtype=np.int8)).cuda()
-        layer = clo.Layer(0, None, None, rec.ptr, None, None, k_cache, v_cache, idx_d, clo.CLO_HOST_INT8,
-                          k_exp, v_exp)
+        layer = clo.Layer(0, None, None, rec.ptr, None, None, k_cache, v_cache, idx_d, host_format, k_exp, v_exp)
     # no error word: the call finishes and reports nothing
     clo.clo_gather_kv(shape, layer, None, ws)
     torch.cuda.synchronize()
@@ -77,7 +84,7 @@ def test_gather_reports_out_of_range_index(need_gpu, host_format):
                 assert np.array_equal(gv[b, h], vh[b, h, clamped[b, h]])
             else:
                 ke = k_exp.cpu().numpy()[b, h, clamped[b, h]].astype(np.float64)
-                want = r[b, h, clamped[b, h], 0].astype(np.float64) * 2.0 ** ke[:, None]
+                want = vals[b, h, clamped[b, h], 0].astype(np.float64) * 2.0 ** ke[:, None]
                 got = (gk[b, h].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
                 assert np.array_equal(got, want)
     # a valid selection leaves a cleared word at zero

@@ -8,7 +8,8 @@ config 4, 16 for config 5); 8 layers with 8 different data layers are
 compared (config 5: all their units; config 4: every miss unit and some reuse
 units of each), and every unit of those
 layers is checked for its reuse decision and a valid selection.  Config 3's
-shape is also run with int8 host KV and with 16-token blocks on sampled units.
+shape is also run with int8 and int4 host KV and with 16-token blocks on sampled
+units.
 Each case logs its largest normwise output error against the tolerance.
 
 The oracle and the margin work run per unit on a pool of threads (each with a
@@ -44,15 +45,15 @@ class _Prev:
         return self.idx
 
 
-def check_unit(p, layer, bufs, got0, got1, b, h, q, qp, block_size=1, int8=False, tag=""):
+def check_unit(p, layer, bufs, got0, got1, b, h, q, qp, block_size=1, quant_bits=0, tag=""):
     """Both steps of one unit against the oracle; returns the two compare() results."""
     K = p.kv("k", layer, b, h, threads=1)
     V = p.kv("v", layer, b, h, threads=1)
     kv = lambda bb, hh: (K, V)  # noqa: E731
     attn = cache_of = None
-    if int8 and not bufs.is_persistent(h):
-        Kq = oracle.quantized_rows(oracle.as_f64(K, p.dtype))
-        Vq = oracle.quantized_rows(oracle.as_f64(V, p.dtype))
+    if quant_bits and not bufs.is_persistent(h):
+        Kq = oracle.quantized_rows(oracle.as_f64(K, p.dtype), quant_bits)
+        Vq = oracle.quantized_rows(oracle.as_f64(V, p.dtype), quant_bits)
         attn = lambda bb, hh: (Kq, Vq)  # noqa: E731
         cache_of = attn
     u = [(b, h)]
@@ -168,12 +169,17 @@ def test_single_layer_configs_every_unit(need_gpu, cfg):
     _release()
 
 
+QUANT = {"int8_host_kv": 8, "int4_host_kv": 4}
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("variant", ["int8_host_kv", "blocks_16"])
+@pytest.mark.parametrize("variant", ["int8_host_kv", "int4_host_kv", "blocks_16"])
 def test_config3_shape_variants(need_gpu, variant):
     from top_sparse_attention_02_amd import clo
 
     bs = 16 if variant == "blocks_16" else 1
+    bits = QUANT.get(variant, 0)
+    host_format = {8: clo.CLO_HOST_INT8, 4: clo.CLO_HOST_INT4}.get(bits, clo.CLO_HOST_NATIVE)
     p = gen.config(3) if bs == 1 else gen.config(3, topk=gen.config(3).topk // bs * bs)
     tag = f"config 3 {variant}"
     enforce_cos_all(p, 0)
@@ -183,9 +189,9 @@ def test_config3_shape_variants(need_gpu, variant):
         enforce_block_margins(p, 0, bs, units=units, workers=WORKERS)
     else:
         enforce_margins(p, 0, units=units, workers=WORKERS)
-    bufs, got0, got1 = _run_single_layer(p, host_format=clo.CLO_HOST_INT8 if bs == 1 else 0, block_size=bs)
+    bufs, got0, got1 = _run_single_layer(p, host_format=host_format, block_size=bs)
     log(f"[{tag}] oracle")
-    check_units(p, 0, bufs, got0, got1, units, tag, block_size=bs, int8=bs == 1)
+    check_units(p, 0, bufs, got0, got1, units, tag, block_size=bs, quant_bits=bits)
     check_all_units(p, 0, got0, 0, block_size=bs)
     check_all_units(p, 0, got1, 1, block_size=bs)
     del bufs, got0, got1

@@ -68,18 +68,21 @@ def test_layer_loop_matches_sequential_and_oracle(need_gpu, select_streams, gath
         compare(p, layers[l], a1[l], r1, kv, f"layer {l} step1")
 
 
-def test_layer_loop_int8_host_kv_matches_sequential(need_gpu):
-    """The three-stream loop over layers whose offloaded KV is int8 in host memory (the
-    dequantizing gather, its in-LDS unit list and the fused reuse-select launch) equals
-    the fused step run layer after layer on one stream, bit for bit."""
+@pytest.mark.parametrize("host_kv", ["int8", "int4"])
+def test_layer_loop_quantized_host_kv_matches_sequential(need_gpu, host_kv):
+    """The three-stream loop over layers whose offloaded KV is quantized in host memory
+    (the dequantizing gather inside the resident launch, its in-LDS unit list and the
+    fused reuse-select launch) equals the fused step run layer after layer on one
+    stream, bit for bit."""
     import torch
 
     from top_sparse_attention_02_amd import clo, workload
 
     p = enforce_all_layers(multi_layer_problem())
-    layers = workload.load_layers(p, host_format=clo.CLO_HOST_INT8)
+    fmt = clo.CLO_HOST_INT8 if host_kv == "int8" else clo.CLO_HOST_INT4
+    layers = workload.load_layers(p, host_format=fmt)
     loop = workload.LayerLoop(layers)
-    log("[case layer loop, int8 host KV] cold + steady step")
+    log(f"[case layer loop, {host_kv} host KV] cold + steady step")
     loop.step(cold=True)
     loop.step()
     torch.cuda.synchronize()

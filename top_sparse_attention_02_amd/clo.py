@@ -14,7 +14,7 @@ from typing import Optional, Sequence
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libclo.so")
 
 CLO_F32, CLO_BF16 = 0, 1
-CLO_HOST_NATIVE, CLO_HOST_INT8 = 0, 1
+CLO_HOST_NATIVE, CLO_HOST_INT8, CLO_HOST_INT4 = 0, 1, 2
 CLO_OK, CLO_E_ARG, CLO_E_UNSUPPORTED, CLO_E_WORKSPACE, CLO_E_HIP, CLO_E_TIMEOUT, CLO_E_INDEX = range(7)
 
 # every function include/clo.h declares
@@ -89,7 +89,8 @@ def load():
         L.clo_update_reference.restype = st
         L.clo_update_reference.argtypes = [P(clo_shape), vp, vp, vp, P(clo_sync), vp]
         L.clo_quantize_rows.restype = st
-        L.clo_quantize_rows.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int64, vp, P(clo_sync), vp]
+        L.clo_quantize_rows.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int64, vp,
+                                        P(clo_sync), vp]
         L.clo_stream_read.restype = st
         L.clo_stream_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int32, vp, vp]
         L.clo_plan_persistent.restype = st
@@ -199,7 +200,7 @@ class Layer:
     k_cache: object = None
     v_cache: object = None
     idx: object = None
-    host_format: int = 0  # CLO_HOST_NATIVE or CLO_HOST_INT8
+    host_format: int = 0  # CLO_HOST_NATIVE, CLO_HOST_INT8 or CLO_HOST_INT4
     k_host_exp: object = None
     v_host_exp: object = None
 
@@ -317,10 +318,10 @@ def clo_update_reference(shape: Shape, q, reuse, q_ref, sync: Optional[Sync] = N
                                        stream_handle(stream)), "clo_update_reference")
 
 
-def clo_quantize_rows(src, n_rows: int, dtype: int, dst, dst_exp, dst_stride: int = 128, sync: Optional[Sync] = None,
-                      stream=None):
-    _check(load().clo_quantize_rows(ptr(src), int(n_rows), int(dtype), ptr(dst), int(dst_stride), ptr(dst_exp),
-                                    _sync(sync), stream_handle(stream)), "clo_quantize_rows")
+def clo_quantize_rows(src, n_rows: int, dtype: int, dst, dst_exp, dst_stride: int = 128,
+                      host_format: int = CLO_HOST_INT8, sync: Optional[Sync] = None, stream=None):
+    _check(load().clo_quantize_rows(ptr(src), int(n_rows), int(dtype), int(host_format), ptr(dst), int(dst_stride),
+                                    ptr(dst_exp), _sync(sync), stream_handle(stream)), "clo_quantize_rows")
 
 
 def clo_stream_read(src, nbytes_: int, blocks: int, sink, stream=None):

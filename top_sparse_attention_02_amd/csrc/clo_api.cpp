@@ -335,20 +335,21 @@ clo_status check_layer(const clo_layer* l, Plan* p, unsigned need) {
     if (need & NEED_HOST) {
       const void* dk = nullptr;
       const void* dv = nullptr;
-      if (l->host_format != CLO_HOST_NATIVE && l->host_format != CLO_HOST_INT8)
+      if (l->host_format != CLO_HOST_NATIVE && l->host_format != CLO_HOST_INT8 && l->host_format != CLO_HOST_INT4)
         return fail(CLO_E_ARG, "layer.host_format %d is not a clo_host_format", l->host_format);
       a.host_fmt = l->host_format;
       const size_t rows = (size_t)a.B * a.H * (size_t)a.C;
-      if (a.host_fmt == CLO_HOST_INT8) {
-        // one 256-byte record (K values, then V values) per token; v_host unused
-        if ((st = check_host(l->k_host, rows * 2 * kHeadDim, "layer.k_host", &dk))) return st;
+      const bool quant = a.host_fmt != CLO_HOST_NATIVE;
+      if (quant) {
+        // one record (K values, then V values) per token; v_host unused
+        if ((st = check_host(l->k_host, rows * 2 * quant_row_bytes(a.host_fmt), "layer.k_host", &dk))) return st;
       } else {
         if ((st = check_host(l->k_host, full_bytes(*p, a.H), "layer.k_host", &dk))) return st;
         if ((st = check_host(l->v_host, full_bytes(*p, a.H), "layer.v_host", &dv))) return st;
       }
       a.k_host = dk;
       a.v_host = dv;
-      if (a.host_fmt == CLO_HOST_INT8) {
+      if (quant) {
         if ((st = check_device(l->k_host_exp, rows, "layer.k_host_exp", 1))) return st;
         if ((st = check_device(l->v_host_exp, rows, "layer.v_host_exp", 1))) return st;
         a.k_exp = l->k_host_exp;
@@ -864,13 +865,17 @@ clo_status clo_stream_read(const void* src, size_t bytes, int32_t blocks, uint32
                     "stream read launch");
 }
 
-clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int64_t dst_stride,
-                             int8_t* dst_exp, const clo_sync* sync, void* stream) {
+clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int32_t host_format, void* dst,
+                             int64_t dst_stride, int8_t* dst_exp, const clo_sync* sync, void* stream) {
   clo_status st;
   if (dtype != CLO_F32 && dtype != CLO_BF16) return fail(CLO_E_UNSUPPORTED, "dtype %d is not fp32 or bf16", dtype);
+  if (host_format != CLO_HOST_INT8 && host_format != CLO_HOST_INT4)
+    return fail(CLO_E_ARG, "host_format %d is not CLO_HOST_INT8 or CLO_HOST_INT4", host_format);
   if (n_rows < 0) return fail(CLO_E_ARG, "n_rows %lld < 0", (long long)n_rows);
-  if (dst_stride < kHeadDim || dst_stride % 16)
-    return fail(CLO_E_ARG, "dst_stride %lld is not a multiple of 16 of at least 128", (long long)dst_stride);
+  const int64_t row_bytes = quant_row_bytes(host_format);
+  if (dst_stride < row_bytes || dst_stride % 16)
+    return fail(CLO_E_ARG, "dst_stride %lld is not a multiple of 16 of at least %lld", (long long)dst_stride,
+                (long long)row_bytes);
   if ((st = check_sync_flags(sync))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (n_rows == 0) {
@@ -880,11 +885,11 @@ clo_status clo_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int
   const size_t e = dtype == CLO_F32 ? 4 : 2;
   if ((st = check_device(src, (size_t)n_rows * kHeadDim * e, "src"))) return st;
   const void* d = nullptr;
-  if ((st = check_host(dst, (size_t)(n_rows - 1) * dst_stride + kHeadDim, "dst", &d))) return st;  // or device
+  if ((st = check_host(dst, (size_t)(n_rows - 1) * dst_stride + row_bytes, "dst", &d))) return st;  // or device
   if ((st = check_device(dst_exp, (size_t)n_rows, "dst_exp", 1))) return st;
   if ((st = pre_wait(sync, s))) return st;
-  if ((st = hip_status(launch_quantize_rows(src, n_rows, dtype, static_cast<int8_t*>(const_cast<void*>(d)), dst_stride,
-                                            dst_exp, s),
+  if ((st = hip_status(launch_quantize_rows(src, n_rows, dtype, host_format,
+                                            static_cast<uint8_t*>(const_cast<void*>(d)), dst_stride, dst_exp, s),
                        "quantize launch")))
     return st;
   return post_signal(sync, s);

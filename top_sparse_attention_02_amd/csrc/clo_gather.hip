@@ -154,53 +154,61 @@ __global__ __launch_bounds__(256) void gather_kernel(LayerArgs a, const uint8_t*
   gather_finish(gs, counter);
 }
 
-// Int8 host rows (CLO_HOST_INT8): 128 bytes per row, 8 lanes of 16 values each;
-// the row's exponent e (device memory) turns q into q * 2^e, exact in T.  The
-// rest is the native kernel's scheme: items of 256 rows from a counter, the
-// item's source rows and exponents preloaded into LDS, 2 rows of K and V deep
-// per lane.
+// Quantized host rows (CLO_HOST_INT8: 128 bytes per row; CLO_HOST_INT4: 64),
+// read as 16-byte pieces of 16 or 32 values; the row's exponent e (device
+// memory) turns q into q * 2^e, exact in T.  The rest is the native kernel's
+// scheme: items of 256 rows from a counter, the item's source rows and
+// exponents preloaded into LDS, several rows of K and V deep per lane.
 __device__ __forceinline__ float pow2f(int e) { return __int_as_float((e + 127) << 23); }  // -126 <= e <= 127
 
-template <typename T>
-__device__ __forceinline__ void store_deq16(T* dst, u32x4 w, float scale);
-template <>
-__device__ __forceinline__ void store_deq16<uint16_t>(uint16_t* dst, u32x4 w, float scale) {
-  u32x4 o[2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t x = w[i];
-    // four signed bytes -> exact products q * 2^e -> bf16 (exact: q has 7 bits)
-    const float f0 = (float)(int8_t)(x & 0xFFu) * scale, f1 = (float)(int8_t)((x >> 8) & 0xFFu) * scale;
-    const float f2 = (float)(int8_t)((x >> 16) & 0xFFu) * scale, f3 = (float)(int8_t)(x >> 24) * scale;
-    o[i / 2][(i % 2) * 2] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-    o[i / 2][(i % 2) * 2 + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
-  }
-  reinterpret_cast<u32x4*>(dst)[0] = o[0];
-  reinterpret_cast<u32x4*>(dst)[1] = o[1];
+// q of element n of a 16-byte piece: a signed byte (8-bit) or a signed nibble,
+// value 2j in the low half of byte j (4-bit)
+template <int BITS>
+__device__ __forceinline__ float quant_at(const u32x4& w, int n) {
+  const uint32_t x = w[n * BITS / 32];
+  const int sh = (n * BITS) % 32;
+  return (float)(((int32_t)(x << (32 - BITS - sh))) >> (32 - BITS));
 }
-template <>
-__device__ __forceinline__ void store_deq16<float>(float* dst, u32x4 w, float scale) {
+
+// 16 * 8 / BITS values of one piece, times 2^e, stored as T; the products have at
+// most 7 significant bits, so the bf16 pattern is the fp32 one's upper half
+template <typename T, int BITS>
+__device__ __forceinline__ void store_deq(T* dst, const u32x4& w, float scale) {
+  constexpr int NV = 128 / BITS;  // values per piece
+  if constexpr (std::is_same<T, uint16_t>::value) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t x = w[i];
-    u32x4 o;
-    o[0] = __float_as_uint((float)(int8_t)(x & 0xFFu) * scale);
-    o[1] = __float_as_uint((float)(int8_t)((x >> 8) & 0xFFu) * scale);
-    o[2] = __float_as_uint((float)(int8_t)((x >> 16) & 0xFFu) * scale);
-    o[3] = __float_as_uint((float)(int8_t)(x >> 24) * scale);
-    reinterpret_cast<u32x4*>(dst)[i] = o;
+    for (int o = 0; o < NV / 8; ++o) {
+      u32x4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f0 = quant_at<BITS>(w, o * 8 + 2 * i) * scale, f1 = quant_at<BITS>(w, o * 8 + 2 * i + 1) * scale;
+        r[i] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+      }
+      reinterpret_cast<u32x4*>(dst)[o] = r;
+    }
+  } else {
+#pragma unroll
+    for (int o = 0; o < NV / 4; ++o) {
+      u32x4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(quant_at<BITS>(w, o * 4 + i) * scale);
+      reinterpret_cast<u32x4*>(dst)[o] = r;
+    }
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void gather_q8_rows(const LayerArgs& a, const uint8_t* __restrict__ reuse, Span sp,
-                                               uint32_t* __restrict__ counter, uint32_t* err) {
-  // one 256-byte record per token: lanes 0-7 of a row group read its K values,
-  // lanes 8-15 its V values, in a single 16-lane load
-  constexpr int kRec = 2 * kHeadDim;  // record bytes
-  constexpr int LPR = kRec / 16;      // 16 lanes per token
+template <typename T, int BITS>
+__device__ __forceinline__ void gather_quant_rows(const LayerArgs& a, const uint8_t* __restrict__ reuse, Span sp,
+                                                  uint32_t* __restrict__ counter, uint32_t* err) {
+  // one record per token (K values, then V values): the first half of a row
+  // group's lanes read its K values, the second half its V values, in a
+  // single load of 16 (8-bit) or 8 (4-bit) lanes
+  constexpr int kRec = 2 * kHeadDim * BITS / 8;  // record bytes
+  constexpr int LPR = kRec / 16;                 // lanes per token
+  constexpr int LPH = LPR / 2;                   // lanes per row
+  constexpr int NV = 128 / BITS;                 // values per lane
   constexpr int RPI = 256 / LPR;
-  constexpr int UNR = 2 * kGatherUnroll;  // same bytes in flight as the native kernel
+  constexpr int UNR = 2 * kGatherUnroll;  // 16-byte loads in flight per lane
   __shared__ uint32_t s_item;
   __shared__ int32_t s_src[kGatherChunk];
   __shared__ float s_sc[2][kGatherChunk];  // 2^e of the item's K and V rows
@@ -214,7 +222,7 @@ __device__ __forceinline__ void gather_q8_rows(const LayerArgs& a, const uint8_t
                                   : (listed ? (int64_t)list_gather_units(a, reuse, U, s_units, s_wcnt) : (int64_t)U);
   const int64_t items = n_units * nch;
   const int sub = threadIdx.x % LPR, rl = threadIdx.x / LPR;
-  const int half = sub >> 3, piece = sub & 7;  // 0 = K, 1 = V; 16-value piece of the row
+  const int half = sub / LPH, piece = sub % LPH;  // 0 = K, 1 = V; piece of the row
   for (;;) {
     if (threadIdx.x == 0) s_item = atomicAdd(counter, 1u);
     __syncthreads();
@@ -249,18 +257,40 @@ __device__ __forceinline__ void gather_q8_rows(const LayerArgs& a, const uint8_t
 #pragma unroll
       for (int j = 0; j < UNR; ++j) {
         const int64_t row = rb + j * RPI + rl;
-        if (row < r_end) store_deq16<T>(dst + row * kHeadDim + piece * 16, x[j], s_sc[half][row - r0]);
+        if (row < r_end) store_deq<T, BITS>(dst + row * kHeadDim + piece * NV, x[j], s_sc[half][row - r0]);
       }
     }
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void gather_q8_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp,
-                                                        uint32_t* __restrict__ counter, GatherSync gs) {
+template <typename T, int BITS>
+__global__ __launch_bounds__(256) void gather_quant_kernel(LayerArgs a, const uint8_t* __restrict__ reuse, Span sp,
+                                                           uint32_t* __restrict__ counter, GatherSync gs) {
   gather_wait(gs);
-  gather_q8_rows<T>(a, reuse, sp, counter, a.err);
+  gather_quant_rows<T, BITS>(a, reuse, sp, counter, a.err);
   gather_finish(gs, counter);
+}
+
+// One layer's rows in the layer's host format and dtype.
+__device__ __forceinline__ void gather_rows_any(const LayerArgs& a, const uint8_t* __restrict__ reuse,
+                                                uint32_t* __restrict__ counter, uint32_t* err) {
+  const Span all{nullptr, nullptr, nullptr};
+  const bool f32 = a.dtype == CLO_F32;
+  if (a.host_fmt == CLO_HOST_INT8) {
+    if (f32)
+      gather_quant_rows<float, 8>(a, reuse, all, counter, err);
+    else
+      gather_quant_rows<uint16_t, 8>(a, reuse, all, counter, err);
+  } else if (a.host_fmt == CLO_HOST_INT4) {
+    if (f32)
+      gather_quant_rows<float, 4>(a, reuse, all, counter, err);
+    else
+      gather_quant_rows<uint16_t, 4>(a, reuse, all, counter, err);
+  } else if (f32) {
+    gather_native_rows<float>(a, reuse, all, counter, err);
+  } else {
+    gather_native_rows<uint16_t>(a, reuse, all, counter, err);
+  }
 }
 
 // The gathers of many layers in one launch (a resident kernel).  Layer by
@@ -276,18 +306,7 @@ __global__ __launch_bounds__(256) void gather_layers_kernel(const GatherPlanLaye
     const GatherPlanLayer& g = plan[l];
     const GatherSync gs{g.wait_flag, wait_value, limit, err, g.signal_flag, signal_value, g.done};
     gather_wait(gs);
-    const LayerArgs& a = g.a;
-    const Span all{nullptr, nullptr, nullptr};
-    if (a.host_fmt == CLO_HOST_INT8) {
-      if (a.dtype == CLO_F32)
-        gather_q8_rows<float>(a, g.reuse, all, g.counter, err);
-      else
-        gather_q8_rows<uint16_t>(a, g.reuse, all, g.counter, err);
-    } else if (a.dtype == CLO_F32) {
-      gather_native_rows<float>(a, g.reuse, all, g.counter, err);
-    } else {
-      gather_native_rows<uint16_t>(a, g.reuse, all, g.counter, err);
-    }
+    gather_rows_any(g.a, g.reuse, g.counter, err);
     gather_finish(gs, g.counter);
     __syncthreads();  // the next layer reuses the block's LDS
   }
@@ -305,9 +324,14 @@ hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, Span sp, int6
   if (gsp) gs = *gsp;
   if (a.host_fmt == CLO_HOST_INT8) {
     if (a.dtype == CLO_F32)
-      gather_q8_kernel<float><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
+      gather_quant_kernel<float, 8><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
     else
-      gather_q8_kernel<uint16_t><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
+      gather_quant_kernel<uint16_t, 8><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
+  } else if (a.host_fmt == CLO_HOST_INT4) {
+    if (a.dtype == CLO_F32)
+      gather_quant_kernel<float, 4><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
+    else
+      gather_quant_kernel<uint16_t, 4><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
   } else if (a.dtype == CLO_F32) {
     gather_kernel<float><<<grid, 256, 0, s>>>(a, reuse, sp, counter, gs);
   } else {

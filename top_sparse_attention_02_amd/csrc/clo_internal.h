@@ -70,13 +70,15 @@ struct LayerArgs {
   void* v_cache;
   int32_t* idx;
   int32_t bs;            // selection block size (1 = tokens)
-  int32_t host_fmt;      // CLO_HOST_NATIVE or CLO_HOST_INT8
-  const int8_t* k_exp;   // CLO_HOST_INT8: [B, H, C] row exponents of k_host / v_host
+  int32_t host_fmt;      // CLO_HOST_NATIVE, CLO_HOST_INT8 or CLO_HOST_INT4
+  const int8_t* k_exp;   // CLO_HOST_INT8/INT4: [B, H, C] row exponents of k_host / v_host
   const int8_t* v_exp;
   uint32_t* err;         // device error word for selected indices out of range (may be NULL)
 };
 
-constexpr int kQuantMinExp = -120;  // smallest row exponent of the int8 host format
+constexpr int kQuantMinExp = -120;  // smallest row exponent of the quantized host formats
+// bytes of one quantized row of kHeadDim values (a record holds a K and a V row)
+constexpr int64_t quant_row_bytes(int32_t host_fmt) { return host_fmt == CLO_HOST_INT4 ? kHeadDim / 2 : kHeadDim; }
 
 // Unit ranges of one decode step: units are split into R contiguous ranges
 // [first[r], first[r + 1]) so that the gather of one range can run while the
@@ -222,8 +224,8 @@ hipError_t launch_append(const LayerArgs& a, const void* k_new, const void* v_ne
                          void* k_hbm, void* v_hbm, void* k_host, void* v_host, void* k_score, hipStream_t s);
 hipError_t launch_update_reference(const LayerArgs& a, const void* q, const uint8_t* reuse, void* q_ref,
                                    hipStream_t s);
-hipError_t launch_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int64_t stride,
-                                int8_t* dst_exp, hipStream_t s);
+hipError_t launch_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int32_t host_fmt, uint8_t* dst,
+                                int64_t stride, int8_t* dst_exp, hipStream_t s);
 hipError_t launch_wait(const uint32_t* flag, uint32_t value, uint32_t spin_limit, uint32_t* error_word,
                        uint32_t* zero_word, hipStream_t s);
 hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s);

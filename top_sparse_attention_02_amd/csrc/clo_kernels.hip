@@ -1,5 +1,5 @@
 // HIP kernels of the CLO decode step for gfx950 (MI355X) outside the five steps'
-// own sources: quantization of rows for the int8 host copy, appending a decoded
+// own sources: quantization of rows for the quantized host copies, appending a decoded
 // token (growing context), reference queries, the device-side wait and signal
 // kernels that order work between streams, the HBM read probe, and the static
 // scratch of clo_decode_step_static.  The steps themselves: clo_select.hip (A1
@@ -44,23 +44,27 @@ hipError_t static_scratch(void** ptr) {
 
 namespace {
 
-// ---------------------------------------------------------------- int8 quantization
-// Row quantization of the int8 host format by one wave: lane l holds elements
-// 2l and 2l+1.  m = max|x|; e = the smallest integer with m <= 127 * 2^e (0 for a
-// zero row), at least kQuantMinExp; q = x * 2^-e rounded to nearest even.
+// ---------------------------------------------------------------- quantization
+// Row quantization of the quantized host formats by one wave: lane l holds
+// elements 2l and 2l+1.  With M = 127 (8-bit values) or 7 (4-bit): m = max|x|;
+// e = the smallest integer with m <= M * 2^e (0 for a zero row), at least
+// kQuantMinExp; q = x * 2^-e rounded to nearest even.
+template <int BITS>
 __device__ __forceinline__ int quant_exponent(float m) {
+  constexpr float M = BITS == 8 ? 127.f : 7.f;
+  constexpr int F = BITS == 8 ? 6 : 2;  // 2^F <= M < 2^(F+1)
   if (m == 0.f) return 0;
   int E;
   frexpf(m, &E);  // m = f * 2^E, 0.5 <= f < 1
-  int e = E - 1 - 6;
-  if (m > ldexpf(127.f, e)) e += 1;
+  int e = E - 1 - F;
+  if (m > ldexpf(M, e)) e += 1;
   return e < kQuantMinExp ? kQuantMinExp : e;
 }
 
-__device__ __forceinline__ uint32_t quant_pair(float x0, float x1, int e) {
+__device__ __forceinline__ void quant_pair(float x0, float x1, int e, int& q0, int& q1) {
   const float inv = ldexpf(1.f, -e);  // exact power of two
-  const int q0 = (int)rintf(x0 * inv), q1 = (int)rintf(x1 * inv);
-  return (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8);
+  q0 = (int)rintf(x0 * inv);
+  q1 = (int)rintf(x1 * inv);
 }
 
 template <typename T>
@@ -78,24 +82,30 @@ __device__ __forceinline__ void load_pair<float>(const float* row, int lane, flo
   x1 = v.y;
 }
 
-// Quantizes one row held by a wave and stores 2 bytes per lane plus the exponent.
-template <typename T>
-__device__ __forceinline__ void quantize_row_wave(const T* row, int8_t* dst, int8_t* dst_exp) {
+// Quantizes one row held by a wave and stores its values (8-bit: 2 bytes per
+// lane; 4-bit: 1 byte, value 2l in the low half) plus the exponent.
+template <typename T, int BITS>
+__device__ __forceinline__ void quantize_row_wave(const T* row, uint8_t* dst, int8_t* dst_exp) {
   const int lane = threadIdx.x & 63;
   float x0, x1;
   load_pair<T>(row, lane, x0, x1);
   const float m = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-  const int e = quant_exponent(m);
-  reinterpret_cast<uint16_t*>(dst)[lane] = (uint16_t)quant_pair(x0, x1, e);
+  const int e = quant_exponent<BITS>(m);
+  int q0, q1;
+  quant_pair(x0, x1, e, q0, q1);
+  if (BITS == 8)
+    reinterpret_cast<uint16_t*>(dst)[lane] = (uint16_t)((uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8));
+  else
+    dst[lane] = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
   if (lane == 0) *dst_exp = (int8_t)e;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict__ src, int64_t n_rows, int8_t* dst,
+template <typename T, int BITS>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict__ src, int64_t n_rows, uint8_t* dst,
                                                             int64_t stride, int8_t* __restrict__ dst_exp) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n_rows) return;  // whole wave
-  quantize_row_wave<T>(src + row * kHeadDim, dst + row * stride, dst_exp + row);
+  quantize_row_wave<T, BITS>(src + row * kHeadDim, dst + row * stride, dst_exp + row);
 }
 
 __global__ void zero_kernel(uint32_t* word, uint32_t* word2) {
@@ -121,12 +131,20 @@ __global__ __launch_bounds__(64) void append_kernel(LayerArgs a, const T* __rest
   const int64_t rows = pers ? a.P : a.H;
   const int64_t dst = (((int64_t)b * rows + head_slot(a.pmask, h)) * a.C + position) * kHeadDim;
   const int64_t src = (int64_t)u * kHeadDim;
-  if (!pers && a.host_fmt == CLO_HOST_INT8) {
-    // the int8 host copy gets the quantized row, the score copy the exact one
-    const int64_t er = dst / kHeadDim;                          // the token's row index
-    int8_t* record = reinterpret_cast<int8_t*>(k_host) + er * 2 * kHeadDim;  // K values, then V values
-    quantize_row_wave<T>(k_new + src, record, const_cast<int8_t*>(a.k_exp) + er);
-    quantize_row_wave<T>(v_new + src, record + kHeadDim, const_cast<int8_t*>(a.v_exp) + er);
+  if (!pers && a.host_fmt != CLO_HOST_NATIVE) {
+    // the quantized host copy gets the quantized row, the score copy the exact one
+    const int64_t er = dst / kHeadDim;  // the token's row index
+    const int64_t rb = quant_row_bytes(a.host_fmt);
+    uint8_t* record = reinterpret_cast<uint8_t*>(k_host) + er * 2 * rb;  // K values, then V values
+    int8_t* ke = const_cast<int8_t*>(a.k_exp) + er;
+    int8_t* ve = const_cast<int8_t*>(a.v_exp) + er;
+    if (a.host_fmt == CLO_HOST_INT8) {
+      quantize_row_wave<T, 8>(k_new + src, record, ke);
+      quantize_row_wave<T, 8>(v_new + src, record + rb, ve);
+    } else {
+      quantize_row_wave<T, 4>(k_new + src, record, ke);
+      quantize_row_wave<T, 4>(v_new + src, record + rb, ve);
+    }
     for (int i = threadIdx.x; i < kPieces; i += 64)
       reinterpret_cast<u32x4*>(k_score + dst)[i] = reinterpret_cast<const u32x4*>(k_new + src)[i];
     return;
@@ -205,16 +223,24 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 
 }  // namespace
 
-hipError_t launch_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int8_t* dst, int64_t stride,
-                                int8_t* dst_exp, hipStream_t s) {
+hipError_t launch_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, int32_t host_fmt, uint8_t* dst,
+                                int64_t stride, int8_t* dst_exp, hipStream_t s) {
   const int64_t blocks = (n_rows + 3) / 4;
   if (blocks <= 0) return hipSuccess;
   const unsigned grid = (unsigned)blocks;
-  if (dtype == CLO_F32)
-    quantize_rows_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(src), n_rows, dst, stride, dst_exp);
-  else
-    quantize_rows_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), n_rows, dst, stride,
-                                                        dst_exp);
+  const float* sf = static_cast<const float*>(src);
+  const uint16_t* sb = static_cast<const uint16_t*>(src);
+  if (host_fmt == CLO_HOST_INT8) {
+    if (dtype == CLO_F32)
+      quantize_rows_kernel<float, 8><<<grid, 256, 0, s>>>(sf, n_rows, dst, stride, dst_exp);
+    else
+      quantize_rows_kernel<uint16_t, 8><<<grid, 256, 0, s>>>(sb, n_rows, dst, stride, dst_exp);
+  } else {
+    if (dtype == CLO_F32)
+      quantize_rows_kernel<float, 4><<<grid, 256, 0, s>>>(sf, n_rows, dst, stride, dst_exp);
+    else
+      quantize_rows_kernel<uint16_t, 4><<<grid, 256, 0, s>>>(sb, n_rows, dst, stride, dst_exp);
+  }
   return hipGetLastError();
 }
 

@@ -28,6 +28,11 @@ def clo_dtype(dtype: str) -> int:
     return clo.CLO_F32 if dtype == "f32" else clo.CLO_BF16
 
 
+def quant_row_bytes(host_format: int) -> int:
+    """Bytes of one quantized row of HEAD_DIM values (a record holds a K and a V row)."""
+    return HEAD_DIM // 2 if host_format == clo.CLO_HOST_INT4 else HEAD_DIM
+
+
 def elem_bytes(dtype: str) -> int:
     return 4 if dtype == "f32" else 2
 
@@ -67,15 +72,15 @@ class LayerBuffers:
                 self.v_hbm = torch.empty_like(self.k_hbm)
             self.k_host = self.v_host = self.k_score = None
             if self.H:
-                if host_format == clo.CLO_HOST_INT8:
-                    # one 256-byte record per token: int8 K values, then int8 V values
-                    self.k_host = HostBuffer(batch * self.H * context * 2 * d, host_flags)
+                if host_format != clo.CLO_HOST_NATIVE:
+                    # one record per token (256 bytes with int8, 128 with int4): K values, then V values
+                    self.k_host = HostBuffer(batch * self.H * context * 2 * quant_row_bytes(host_format), host_flags)
                 else:
                     nb = batch * self.H * context * d * elem_bytes(dtype)
                     self.k_host = HostBuffer(nb, host_flags)
                     self.v_host = HostBuffer(nb, host_flags)
                 self.k_score = torch.empty(batch, self.H, context, d, dtype=tdt, device=dev)
-                if host_format == clo.CLO_HOST_INT8:
+                if host_format != clo.CLO_HOST_NATIVE:
                     self.k_exp = torch.zeros(batch, self.H, context, dtype=torch.int8, device=dev)
                     self.v_exp = torch.zeros_like(self.k_exp)
         # outputs and per-layer state
@@ -117,11 +122,14 @@ class LayerBuffers:
         return bool((self.mask >> kvh) & 1)
 
     def host_view(self, which: str, b: int, kvh: int) -> np.ndarray:
-        """numpy view [N, d] of a non-persistent unit's pinned K or V (int8 for the int8 host format)."""
-        if self.host_format == clo.CLO_HOST_INT8:
-            unit = self.N * 2 * HEAD_DIM
+        """numpy view of a non-persistent unit's pinned K or V: [N, d] rows, or the
+        quantized values ([N, d] int8; [N, d/2] uint8 bytes of two 4-bit values)."""
+        if self.host_format != clo.CLO_HOST_NATIVE:
+            rb = quant_row_bytes(self.host_format)
+            unit = self.N * 2 * rb
             off = (b * self.H + self.slot(kvh)) * unit
-            rec = self.k_host.numpy(np.int8, (self.N, 2, HEAD_DIM), offset=off)
+            npdt = np.int8 if self.host_format == clo.CLO_HOST_INT8 else np.uint8
+            rec = self.k_host.numpy(npdt, (self.N, 2, rb), offset=off)
             return rec[:, 0 if which == "k" else 1, :]
         buf = self.k_host if which == "k" else self.v_host
         npdt, eb = (np.float32 if self.dtype == "f32" else np.uint16), elem_bytes(self.dtype)
@@ -178,8 +186,9 @@ def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads
     """Allocate (unless given) and fill the buffers of one layer of `problem`.
 
     With `share`, the layer reuses that layer's K/V buffers (aliased data) and
-    only its queries are loaded.  With the int8 host format the offloaded rows
-    are quantized by clo_quantize_rows on the GPU straight into pinned memory."""
+    only its queries are loaded.  With a quantized host format the offloaded
+    rows are quantized by clo_quantize_rows on the GPU straight into pinned
+    memory."""
     p = problem
     mask = p.persistent_mask_bits(layer)
     if bufs is None:
@@ -193,7 +202,8 @@ def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads
     eb = elem_bytes(p.dtype)
     unit_bytes = p.context * HEAD_DIM * eb
     staging = None
-    q8 = bufs.host_format == clo.CLO_HOST_INT8
+    q8 = bufs.host_format != clo.CLO_HOST_NATIVE  # a quantized host format
+    rb = quant_row_bytes(bufs.host_format) if q8 else 0
     dev_stage = torch.empty(p.context, HEAD_DIM, dtype=torch_dtype(p.dtype), device=bufs.q.device) if q8 else None
     for b in range(p.batch):
         for kvh in range(p.hkv):
@@ -201,14 +211,14 @@ def load_layer(problem, layer: int, bufs: Optional[LayerBuffers] = None, threads
                 if staging is None:
                     staging = HostBuffer(unit_bytes)
                 s = bufs.slot(kvh)
-                rec = bufs.k_host.ptr + (b * bufs.H + s) * p.context * 2 * HEAD_DIM  # the unit's records
-                for which, exp, half in (("k", bufs.k_exp, 0), ("v", bufs.v_exp, HEAD_DIM)):
+                rec = bufs.k_host.ptr + (b * bufs.H + s) * p.context * 2 * rb  # the unit's records
+                for which, exp, half in (("k", bufs.k_exp, 0), ("v", bufs.v_exp, rb)):
                     p.fill(which, layer, b, kvh, staging.ptr, threads)
                     copy_h2d(dev_stage.data_ptr(), staging.ptr, unit_bytes)
                     if which == "k":
                         bufs.k_score[b, s].copy_(dev_stage)
                     clo.clo_quantize_rows(dev_stage, p.context, clo_dtype(p.dtype), rec + half, exp[b, s],
-                                          dst_stride=2 * HEAD_DIM)
+                                          dst_stride=2 * rb, host_format=bufs.host_format)
                 torch.cuda.synchronize()
                 continue
             if bufs.is_persistent(kvh):
