@@ -66,6 +66,15 @@ def parse():
                          "k is rounded down to one)")
     ap.add_argument("--no-compare-native", action="store_true",
                     help="quantized host KV, configs 1-3: skip the output comparison against the native format")
+    ap.add_argument("--layer", type=int, default=None, metavar="L",
+                    help="configs 4-5: layer L alone through the single-layer fused step (clo_decode_step) "
+                         "instead of the 48-layer loop: one layer's latency and phases, and a launch sequence "
+                         "that rocprofv3 --pmc can run one kernel at a time (the loop's kernels wait on flags "
+                         "that kernels on other streams set, which a serialized run cannot satisfy)")
+    ap.add_argument("--sync-probe", action="store_true",
+                    help="measure the cross-stream hand-off instead of a decode step: HIP events, the command "
+                         "processor's stream memory operations (hipStreamWaitValue32) and the library's device "
+                         "flags, each between small calls on two streams")
     ap.add_argument("--select-streams", type=int, default=1, metavar="S",
                     help="48-layer loop: streams the layers' selections alternate between")
     ap.add_argument("--graph", action="store_true",
@@ -571,6 +580,96 @@ def compare_native(torch, workload, p, q8_layer, step_kind: int, flags) -> dict:
     return res
 
 
+def sync_probe(torch, clo, rounds: int = 500, trials: int = 3) -> dict:
+    """Cross-stream hand-off latency.  Two streams take turns, 2 x rounds turns in
+    all; each turn is one small library call (the reuse test of one sequence with
+    2 KV heads, fp32: one short kernel) that may start only after the other
+    stream's previous call.  The hand-off is made (a) with HIP events
+    (hipStreamWaitEvent), (b) with the command processor's stream memory
+    operations (hipStreamWriteValue32 after a call, hipStreamWaitValue32 before
+    the next, on a word of signal memory), and (c) with the library's device
+    flags (the clo_sync signal store after a call and the polling wait before
+    the next, one kernel each).  The same calls back to back on one stream give
+    the work alone; a turn's time minus that is the hand-off's cost.  Every
+    producer is enqueued before its consumer, so every wait ends."""
+    from top_sparse_attention_02_amd import hip_host
+
+    shape = clo.Shape(1, 8, 2, 64, 7, 0.8, clo.CLO_F32)
+    q = torch.randn(1, 8, HEAD_DIM, device="cuda")
+    qp = torch.randn_like(q)
+    reuse = torch.zeros(1, 2, dtype=torch.uint8, device="cuda")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    streams = (sa, sb)
+    turns = 2 * rounds
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cp_ok = hip_host.can_wait_value()
+    sig = hip_host.signal_word() if cp_ok else None
+    events = [torch.cuda.Event() for _ in range(turns)]
+    base = [0]
+
+    def work(s, sync=None):
+        clo.clo_reuse_test(shape, q, qp, reuse, sync=sync, stream=s)
+
+    def one_stream():
+        for _ in range(turns):
+            work(sa)
+
+    def by_events():
+        for t in range(turns):
+            s = streams[t % 2]
+            if t:
+                s.wait_event(events[t - 1])
+            work(s)
+            events[t].record(s)
+
+    def by_stream_ops():
+        b = base[0]
+        for t in range(turns):
+            s = streams[t % 2]
+            if t:
+                hip_host.stream_wait_value32(s.cuda_stream, sig, b + t)
+            work(s)
+            hip_host.stream_write_value32(s.cuda_stream, sig, b + t + 1)
+        base[0] = b + turns + 1
+
+    def by_flags():
+        b = base[0]
+        for t in range(turns):
+            s = streams[t % 2]
+            work(s, clo.Sync(wait_flag=flag if t else None, wait_value=b + t, signal_flag=flag,
+                             signal_value=b + t + 1))
+        base[0] = b + turns + 1
+
+    def timed(fn) -> float:
+        best = math.inf
+        for _ in range(trials):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(sa)
+            sb.wait_stream(sa)
+            fn()
+            sa.wait_stream(sb)
+            e1.record(sa)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / turns)
+        return best
+
+    if cp_ok:
+        hip_host.stream_write_value32(sa.cuda_stream, sig, 0)
+    torch.cuda.synchronize()
+    alone = timed(one_stream)
+    res = {"work_alone_us": round(alone, 2)}
+    for name, fn in (("events", by_events), ("stream_wait_value", by_stream_ops if cp_ok else None),
+                     ("device_flags", by_flags)):
+        if fn is None:
+            res[name] = None
+            continue
+        us = timed(fn)
+        res[name] = {"us_per_turn": round(us, 2), "handoff_us": round(us - alone, 2)}
+    res["turns"] = turns
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -599,6 +698,16 @@ def main():
                        f", {args.growing} decode steps with one appended token each, reference = previous query"},
             "growing": g}), flush=True)
         return
+    if args.sync_probe:
+        r = sync_probe(torch, clo)
+        log(f"hand-off per turn: {r}")
+        print(json.dumps({
+            "metric": "cross-stream hand-off latency on the GPU (library device flags), us per turn",
+            "value": r["device_flags"]["handoff_us"], "unit": "us", "n_gpus": 1, "steps": r["turns"],
+            "warmup": 0, "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic", "config": {"workload": "two streams taking turns, one small call per turn"},
+            "sync_probe": r}), flush=True)
+        return
     overrides = {}
     if args.config in (4, 5):
         # distinct K/V layer buffers: 8 for B=8 (36 GB of offloaded K/V in pinned host
@@ -614,7 +723,11 @@ def main():
         plan = profile_and_plan(torch, clo, gen, args.config, overrides, args.profile_instances)
         overrides["persistent"] = plan["persistent"]
     p = gen.config(args.config, **overrides)
-    multi = p.layers > 1
+    if args.layer is not None and not (args.config in (4, 5) and 0 <= args.layer < p.layers):
+        print(f"--layer takes a layer 0..{p.layers - 1} of config 4 or 5", file=sys.stderr)
+        sys.exit(2)
+    multi = p.layers > 1 and args.layer is None
+    n_layers = p.layers if multi else 1
     log(f"config {args.config}: L={p.layers} B={p.batch} Hq={p.hq} Hkv={p.hkv} N={p.context} k={p.topk} "
         f"{p.dtype} data layers={p.data_layers or p.layers}")
     from top_sparse_attention_02_amd import hip_host
@@ -628,7 +741,7 @@ def main():
     if multi:
         layers = workload.load_layers(p, log=log, host_flags=flags, host_format=host_format)
     else:
-        layers = [workload.load_layer(p, 0, log=log if p.batch >= 16 else None, host_flags=flags,
+        layers = [workload.load_layer(p, args.layer or 0, log=log if p.batch >= 16 else None, host_flags=flags,
                                       host_format=host_format)]
     log(f"inputs generated and resident ({time.time() - t0:.1f} s)")
 
@@ -786,8 +899,9 @@ def main():
                    (f", {args.volatile:.0%} volatile (layer, KV head) slots" if args.volatile else "") +
                    (", persistent heads from profiling" if plan else "") +
                    (f", {args.host_kv} host KV (power-of-two row scales)" if args.host_kv != "native" else "") +
-                   (f", selection in blocks of {args.block_size} tokens, k={p.topk}" if args.block_size > 1 else ""),
-                   "layers": p.layers, "batch": p.batch, "q_heads": p.hq, "kv_heads": p.hkv, "head_dim": HEAD_DIM,
+                   (f", selection in blocks of {args.block_size} tokens, k={p.topk}" if args.block_size > 1 else "") +
+                   (f", layer {args.layer} alone (single-layer fused step)" if args.layer is not None else ""),
+                   "layers": n_layers, "batch": p.batch, "q_heads": p.hq, "kv_heads": p.hkv, "head_dim": HEAD_DIM,
                    "context": p.context, "topk": p.topk, "tau": p.tau, "step": args.step,
                    "data_layers": p.data_layers or p.layers, "host_memory": args.host_memory,
                    **({"graph": True} if args.graph else {}),
@@ -818,9 +932,10 @@ def main():
         result["layer_steps_per_s"] = round(p.layers / step_s, 2)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of units")
-        if args.host_kv != "native":
-            # the oracle reads stored rows of the step's dtype; the quantized host copy
-            # holds none, so the native-format baseline is the one to compare with
+        if args.host_kv != "native" or args.layer is not None:
+            # the oracle reads stored rows of the step's dtype (the quantized host copy
+            # holds none, so the native-format baseline is the one to compare with); a
+            # single layer of a 48-layer workload is compared with in the full run
             result["cpu_baseline"] = None
         else:
             result["cpu_baseline"] = cpu_baseline(p, layers, args.cpu_sample_seconds, args.step,

@@ -17,8 +17,11 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("name,kw", [
     # fp32, every head persistent: one stream, the single-block reuse test + lists
     ("graph_f32_persistent", dict(batch=1, hq=32, hkv=8, context=4096, topk=410, dtype="f32", persistent=[1] * 8)),
-    # bf16 with offloaded heads: the overlapped step, helper streams joined by events
+    # bf16 with offloaded heads, 8 units: the step in order on one stream, gather included
     ("graph_bf16_mixed", dict(batch=2, hq=8, hkv=4, context=3000, topk=300, dtype="bf16", persistent=[1, 0, 0, 1])),
+    # 20 units: the overlapped step, helper streams joined by events
+    ("graph_bf16_overlapped", dict(batch=5, hq=8, hkv=4, context=3000, topk=300, dtype="bf16",
+                                   persistent=[1, 0, 0, 1])),
 ])
 def test_graph_replays_equal_eager_step(need_gpu, name, kw):
     import torch

@@ -43,6 +43,11 @@ CASES = {
                                      persistent=[0, 1]),
     "bf16_g4_multi_at_switch": dict(batch=1, hq=8, hkv=2, context=114689, topk=11469, dtype="bf16",
                                     persistent=[1, 0]),
+    # 20 and 18 units with offloaded heads: the step overlapped over 8 unit ranges
+    # of 2-3 units on the helper streams (smaller layers run in order)
+    "bf16_g4_overlapped": dict(batch=5, hq=16, hkv=4, context=3001, topk=301, dtype="bf16",
+                               persistent=[0, 1, 0, 0], heavy_frac=0.01),
+    "f32_g2_overlapped": dict(batch=9, hq=4, hkv=2, context=2000, topk=200, dtype="f32", persistent=[0, 0]),
 }
 
 
@@ -125,13 +130,15 @@ def test_ties_go_to_the_smaller_index(need_gpu, context):
         assert np.array_equal(got["idx"][0, h], ref["idx"])
 
 
-def test_standalone_entry_points_equal_fused_step(need_gpu):
-    """clo_reuse_test + clo_topk_select + clo_gather_kv + clo_sparse_attn == clo_decode_step, bit for bit."""
-    import torch
-
+@pytest.mark.parametrize("batch", [2, 5])
+def test_standalone_entry_points_equal_fused_step(need_gpu, batch):
+    """clo_reuse_test + clo_topk_select + clo_gather_kv + clo_sparse_attn == clo_decode_step, bit for bit,
+    for a layer of 8 units (the step in order on one stream) and of 20 units (overlapped over unit
+    ranges on helper streams)."""
     from top_sparse_attention_02_amd import clo, workload
 
-    p = small_problem("split", batch=2, hq=8, hkv=4, context=3000, topk=300, dtype="bf16", persistent=[0, 1, 0, 1])
+    p = small_problem(f"split{batch}", batch=batch, hq=8, hkv=4, context=3000, topk=300, dtype="bf16",
+                      persistent=[0, 1, 0, 1])
     enforce_margins(p, 0)
     bufs = workload.load_layer(p, 0)
     bufs.step0()

@@ -633,8 +633,11 @@ clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const
 namespace {
 
 // Decode step with every kernel in order on the caller's stream: layers without
-// offloaded heads (nothing to overlap), and clo_decode_step_static, which
-// creates no helper streams.  The gather of offloaded heads follows the top-k.
+// offloaded heads (nothing to overlap), layers of fewer than kOverlapUnits units
+// (a range per unit would leave most ranges empty and make the call's ~70
+// launches and stream waits cost more host time than the overlap saves), and
+// clo_decode_step_static, which creates no helper streams.  The gather of
+// offloaded heads follows the top-k.
 clo_status step_in_order(const Plan& p, const Workspace& w, const void* q, const void* q_prev, void* out,
                          uint8_t* reuse, float* cos, hipStream_t s) {
   clo_status st;
@@ -746,8 +749,8 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
   if (cos && (st = check_device(cos, (size_t)p.U * 4, "cos"))) return st;
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
   if ((st = pre_wait(sync, s))) return st;
-  st = p.a.H > 0 ? step_overlapped(p, w, q, q_prev, out, reuse, cos, s)
-                 : step_in_order(p, w, q, q_prev, out, reuse, cos, s);
+  st = p.a.H > 0 && p.U >= kOverlapUnits ? step_overlapped(p, w, q, q_prev, out, reuse, cos, s)
+                                         : step_in_order(p, w, q, q_prev, out, reuse, cos, s);
   if (st) return st;
   return post_signal(sync, s);
 }

@@ -87,6 +87,10 @@ constexpr int64_t quant_row_bytes(int32_t host_fmt) { return host_fmt == CLO_HOS
 // one single-block launch (16 waves, at most 4 units each; wider layers keep a
 // wave per unit in a launch of its own).
 constexpr int kFusedReuseUnits = 64;
+// clo_decode_step overlaps selection, gather and attention over unit ranges on
+// helper streams for layers of at least this many units, and runs smaller
+// layers in order on the caller's stream
+constexpr int kOverlapUnits = 16;
 constexpr int kMaxRanges = 16;
 struct RangeBounds {
   int32_t first[kMaxRanges + 1];  // first unit of each range; first[R] = U

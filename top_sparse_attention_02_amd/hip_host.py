@@ -21,6 +21,10 @@ hipHostMallocNumaUser = 0x20000000
 hipHostMallocCoherent = 0x40000000
 hipHostMallocNonCoherent = 0x80000000
 
+hipMallocSignalMemory = 0x2  # hipExtMallocWithFlags: memory hipStreamWaitValue32 can wait on
+hipStreamWaitValueGte = 0x0
+hipDeviceAttributeCanUseStreamWaitValue = 10013
+
 hipMemcpyHostToDevice = 1
 hipMemcpyDeviceToHost = 2
 hipMemcpyDefault = 4
@@ -45,6 +49,10 @@ def hip():
         _hip.hipGetErrorString.restype = ctypes.c_char_p
         _hip.hipGetErrorString.argtypes = [ctypes.c_int]
         _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(vp), vp, u]
+        _hip.hipExtMallocWithFlags.argtypes = [ctypes.POINTER(vp), sz, u]
+        _hip.hipStreamWriteValue32.argtypes = [vp, vp, ctypes.c_uint32, u]
+        _hip.hipStreamWaitValue32.argtypes = [vp, vp, ctypes.c_uint32, u, ctypes.c_uint32]
+        _hip.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
     return _hip
 
 
@@ -98,3 +106,37 @@ def copy_d2h(dst_host_ptr: int, src_dev_ptr: int, nbytes: int):
 
 def copy_async(dst: int, src: int, nbytes: int, stream_handle: int):
     check(hip().hipMemcpyAsync(dst, src, nbytes, hipMemcpyDefault, stream_handle), "hipMemcpyAsync")
+
+
+# ---------------------------------------------------------------- stream memory operations
+# Signal-memory words are never freed: they stay allocated until the process ends.
+_signal_words = []
+
+
+def can_wait_value(device: int = 0) -> bool:
+    """Whether the device supports hipStreamWaitValue32."""
+    v = ctypes.c_int(0)
+    check(hip().hipDeviceGetAttribute(ctypes.byref(v), hipDeviceAttributeCanUseStreamWaitValue, device),
+          "hipDeviceGetAttribute")
+    return bool(v.value)
+
+
+def signal_word() -> int:
+    """Address of an 8-byte word of signal memory (hipExtMallocWithFlags with
+    hipMallocSignalMemory), the memory hipStreamWaitValue32 waits on; kept until
+    the process ends."""
+    p = ctypes.c_void_p()
+    check(hip().hipExtMallocWithFlags(ctypes.byref(p), 8, hipMallocSignalMemory), "hipExtMallocWithFlags(signal)")
+    _signal_words.append(p.value)
+    return p.value
+
+
+def stream_write_value32(stream_handle: int, ptr: int, value: int):
+    """After the stream's earlier work, the command processor writes `value` to *ptr."""
+    check(hip().hipStreamWriteValue32(stream_handle, ptr, value, 0), "hipStreamWriteValue32")
+
+
+def stream_wait_value32(stream_handle: int, ptr: int, value: int):
+    """The stream's later work waits until *ptr >= value (signal memory)."""
+    check(hip().hipStreamWaitValue32(stream_handle, ptr, value, hipStreamWaitValueGte, 0xFFFFFFFF),
+          "hipStreamWaitValue32")
