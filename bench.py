@@ -127,7 +127,7 @@ def algorithmic_bytes(layers):
     return tot
 
 
-def profiled_traffic(kernel: str, cfg: int):
+def profiled_traffic(kernel: str, cfg: int, layer=None):
     """HBM/host traffic of a kernel from a committed rocprofv3 counter record, or None.
 
     The record (profiles/<kernel>_traffic__*.json) stores the sha256 of the kernel
@@ -142,6 +142,8 @@ def profiled_traffic(kernel: str, cfg: int):
         except (OSError, ValueError):
             continue
         if rec.get("kernel") != kernel or not rec.get("workload", "").startswith(f"config {cfg} "):
+            continue
+        if rec.get("layer") != layer:  # a record of one layer of a 48-layer workload names it
             continue
         src = os.path.join(ROOT, rec["source"])
         if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
@@ -158,7 +160,7 @@ def score_roofline(score_gbs: float, alg: dict, args, multi: bool, hbm_probe=Non
     alone (rocprofv3 durations of the same launch)."""
     out = {"bound": "hbm", "kernel": "compact+score+topk", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS,
            "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": alg["score_bytes"]}
-    rec = profiled_traffic("score_mfma_kernel", args.config) if not multi and args.step == 1 else None
+    rec = profiled_traffic("score_mfma_kernel", args.config, args.layer) if not multi and args.step == 1 else None
     if rec:
         gbs = rec["algorithmic_bytes_per_launch"] / (rec["mean_us"] * 1e3)
         out["kernel_only"] = {"kernel": "score_mfma_kernel", "achieved": round(gbs, 1),
@@ -846,7 +848,7 @@ def main():
                     "launch_ms": round(phases["gather"] / len(layers), 4)}
         # the committed record covers the native-format token gather of the steady step only
         same_launch = not multi and args.step == 1 and args.host_kv == "native" and args.block_size <= 1
-        rec = profiled_traffic("gather_kernel", args.config) if same_launch else None
+        rec = profiled_traffic("gather_kernel", args.config, args.layer) if same_launch else None
         if rec:
             roofline["traffic"] = rec["traffic_bytes_per_launch"]
             roofline["traffic_detail"] = {"read_bytes": rec["read_bytes_per_launch"],
