@@ -39,7 +39,15 @@
  *    allocation's extent, a tensor that would run past it is rejected.
  *  - Inputs must be finite; results for NaN/Inf inputs are unspecified (no
  *    out-of-bounds access happens either way).
- *  - Calls on distinct buffers and streams may run concurrently.
+ *  - Calls on distinct buffers and streams may run concurrently, with two
+ *    limits.  Concurrent clo_decode_step calls on one device share that
+ *    device's helper streams: a lock serializes their enqueueing and their
+ *    GPU work runs one after another.  The top-k of a layer of 8 or more
+ *    chunks of 16384 keys runs as one launch of at most 128 blocks that wait
+ *    for one another, so all of them must be resident at once: four such
+ *    launches side by side fit an MI355X (two blocks per CU); beyond that a
+ *    launch's waits can run out (CLO_E_TIMEOUT in the error word, every
+ *    kernel still finishes) instead of hanging.
  *
  * Tensor layouts (row-major, element type = shape->dtype unless noted), with
  * P = number of persistent KV heads (bits set in persistent_mask), H = n_kv_heads - P,
