@@ -75,6 +75,9 @@ def parse():
                     help="measure the cross-stream hand-off instead of a decode step: HIP events, the command "
                          "processor's stream memory operations (hipStreamWaitValue32) and the library's device "
                          "flags, each between small calls on two streams")
+    ap.add_argument("--select", choices=["batched", "per-layer"], default="batched",
+                    help="48-layer loop: selections in multi-layer batches (clo_select_layers) or one "
+                         "clo_reuse_select per layer")
     ap.add_argument("--select-streams", type=int, default=1, metavar="S",
                     help="48-layer loop: streams the layers' selections alternate between")
     ap.add_argument("--graph", action="store_true",
@@ -435,6 +438,27 @@ def phase_times(torch, clo, layers, step_kind, passes):
     return {n: float(np.mean(v)) for n, v in acc.items()}
 
 
+def select_phase_ms(torch, clo, loop, step_kind, passes) -> float:
+    """ms per step of the loop's multi-layer selections alone (every layer, in the
+    loop's batches, on one stream, nothing else running)."""
+    plan = loop.sel_plans[step_kind == 0]
+    e = loop.epoch  # flags keep their values: waits for e - 1 pass, signals store e again
+    times = []
+    for _ in range(passes):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        first = 0
+        for n in loop.batches:
+            clo.clo_select_layers(loop.layers[0].shape, plan, first, n, e - 1, e, error_word=loop.error)
+            first += n
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    loop.check()
+    return float(sorted(times)[len(times) // 2])
+
+
 def growing_bench(torch, clo, workload, gen, cfg: int, steps: int) -> dict:
     """T steps over a growing context (the workload's context plus one appended
     token per step; k fixed at the workload's top-k), per reference policy.
@@ -771,7 +795,7 @@ def main():
         for bufs in layers:
             bufs.set_block_size(args.block_size)
     if multi:
-        loop = workload.LayerLoop(layers, select_streams=args.select_streams)
+        loop = workload.LayerLoop(layers, select_streams=args.select_streams, select=args.select)
         loop.step(cold=True)
         step = (lambda: loop.step()) if args.step == 1 else (lambda: loop.step(cold=True))
     else:
@@ -835,6 +859,8 @@ def main():
         log(f"{args.host_kv} host KV vs native: output deviation mean {quant['out_dev_mean']:.2e}, "
             f"max {quant['out_dev_max']:.2e}")
     phases = phase_times(torch, clo, layers, args.step, passes=args.steps if not multi else 2)
+    if multi and loop.select == "batched":
+        phases["select_batched"] = select_phase_ms(torch, clo, loop, args.step, passes=3)
     gather_s = phases["gather"] / 1e3
     host_gbs = alg["host_bytes"] / gather_s / 1e9 if alg["host_bytes"] else 0.0
     score_s = phases["score_topk"] / 1e3
@@ -907,7 +933,7 @@ def main():
                    "context": p.context, "topk": p.topk, "tau": p.tau, "step": args.step,
                    "data_layers": p.data_layers or p.layers, "host_memory": args.host_memory,
                    **({"graph": True} if args.graph else {}),
-                   **({"select_streams": args.select_streams} if multi else {})},
+                   **({"select_streams": args.select_streams, "select": loop.select} if multi else {})},
         "host_bound_ms": bounds["host_bound_ms"],
         "frac_of_host_bound": round(host_bound_ms / ms_per_step, 4) if host_bound_ms else None,
         "bounds": bounds,
@@ -919,6 +945,9 @@ def main():
         "host_kv_vs_native": quant,
         "volatile_frac": args.volatile,
         "roofline_score": score_roofline(score_gbs, alg, args, multi, hbm_probe),
+        # the loop's multi-layer selections alone: the same scoring bytes over their time
+        "select_batched_gbs": (round(alg["score_bytes"] / (phases["select_batched"] / 1e3) / 1e9, 1)
+                               if "select_batched" in phases else None),
         "attention_hbm_gbs": round(attn_gbs, 1),
         "attention_frac_measured": round(attn_gbs / hbm_probe["read_gbs"], 4) if hbm_probe else None,
         "step_hbm_gbs": round(alg["hbm_bytes"] / step_s / 1e9, 1),

@@ -294,6 +294,58 @@ clo_status clo_gather_layers(const void* plan, int32_t n_layers, int32_t blocks,
                              uint32_t signal_value, uint32_t* error_word, uint32_t spin_limit, void* stream);
 
 /*
+ * Selection of many layers in three launches -- for each layer what
+ * clo_reuse_select does (A1 reuse test, then A2 scoring and A3 top-k of its
+ * miss units), with the layers' launches merged: the reuse test and unit lists
+ * of every layer in one launch (one block per layer, each after the layer's
+ * own wait), the scoring of all the layers' miss units in one launch, and
+ * their top-k in one more, whose last block then signals every layer.  For
+ * decode steps whose layers are small (a few sequences: each layer's own
+ * scoring and top-k launches are short, their ramp-up, tail and launch gaps
+ * cost more than their keys), with the selections running ahead of the
+ * layers' attention as the pages' prefetch does (synthesis section 5.6;
+ * abstract feature (3), GPU-centric synchronization).
+ *
+ * clo_select_plan writes, into `plan` (device, clo_select_plan_size bytes),
+ * everything the launches need for each layer: its shape (thresholds
+ * included), buffers, workspace, and flags.  All layers of a plan must have
+ * the same batch, heads, context and top-k, bf16 data, batch * n_kv_heads <=
+ * 64, token top-k (block_size <= 1) and a context of at most 128 chunks of
+ * 16384 keys (CLO_E_UNSUPPORTED otherwise; the per-layer calls take the other
+ * shapes).  A plan stays valid while its buffers, workspaces and flags stay
+ * where they were; it is written once, with hipMemcpy (the call synchronizes).
+ *
+ * clo_select_layers enqueues the selection of plan layers first .. first +
+ * count - 1 (count <= 64) on `stream`: each layer waits until *wait_flag >=
+ * wait_value (bounded by spin_limit polls, 0 = about a second; a time-out
+ * writes CLO_E_TIMEOUT to error_word and the layer goes on), and once every
+ * layer of the call is selected, signal_value is stored to each layer's
+ * signal_flag (release, agent scope).  `shape` is the shape the plan's layers
+ * share (its tau and tau_heads are not used: each layer keeps its own); a
+ * layer that does not match it is skipped and CLO_E_ARG written to
+ * error_word.  Outputs are bit for bit those of clo_reuse_select on each layer.
+ * Calls on one plan must not overlap (they share its counters).
+ */
+typedef struct {
+  const clo_shape* shape;
+  const clo_layer* layer;     /* persistent_mask, k_hbm, k_score and idx are used */
+  const void* q;              /* [B, Hq, d] device: the query the layer selects with */
+  const void* q_prev;         /* [B, Hq, d] device: the reuse test's reference */
+  uint8_t* reuse;             /* [B, Hkv] device */
+  float* cos;                 /* [B, Hkv] device, may be NULL */
+  void* ws;                   /* the layer's workspace (clo_workspace_size) */
+  size_t ws_bytes;
+  const uint32_t* wait_flag;  /* device, may be NULL */
+  uint32_t* signal_flag;      /* device, may be NULL */
+} clo_select_layer;
+
+size_t clo_select_plan_size(int32_t n_layers);
+clo_status clo_select_plan(const clo_select_layer* layers, int32_t n_layers, void* plan, size_t plan_bytes);
+clo_status clo_select_layers(const clo_shape* shape, const void* plan, int32_t first, int32_t count,
+                             uint32_t wait_value, uint32_t signal_value, uint32_t* error_word, uint32_t spin_limit,
+                             void* stream);
+
+/*
  * A5 -- sparse attention over the selected rows, every unit (synthesis 2.3
  * table).  For query head h of unit u: l_i = q_h . K_sel_i / sqrt(d),
  * p = softmax(l), out_h = sum_i p_i V_sel_i, accumulated in fp32 and rounded

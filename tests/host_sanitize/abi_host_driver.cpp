@@ -107,6 +107,30 @@ int main() {
     CHECK(clo_quantize_rows(nullptr, 0, CLO_BF16, CLO_HOST_INT8, nullptr, 64, nullptr, nullptr, nullptr) == CLO_E_ARG);
     CHECK(clo_quantize_rows(nullptr, 0, CLO_BF16, CLO_HOST_INT4, nullptr, 64, nullptr, nullptr, nullptr) == CLO_OK);
     CHECK(clo_quantize_rows(nullptr, 0, CLO_BF16, CLO_HOST_INT4, nullptr, 56, nullptr, nullptr, nullptr) == CLO_E_ARG);
+    // the gather and selection plans: sizes and argument checks made before any HIP call
+    CHECK(clo_gather_plan_size(0) == 0 && clo_gather_plan_size(4097) == 0 && clo_gather_plan_size(48) > 0);
+    CHECK(clo_select_plan_size(0) == 0 && clo_select_plan_size(4097) == 0);
+    CHECK(clo_select_plan_size(48) >= 48 * 64 && clo_select_plan_size(48) % 256 == 0);
+    CHECK(clo_select_plan(nullptr, 4, nullptr, 1 << 20) == CLO_E_ARG);
+    clo_select_layer sl;
+    std::memset(&sl, 0, sizeof sl);
+    CHECK(clo_select_plan(&sl, 0, nullptr, 1 << 20) == CLO_E_ARG);
+    CHECK(clo_select_plan(&sl, 1, nullptr, 16) == CLO_E_ARG);  // plan smaller than clo_select_plan_size(1)
+    {
+      clo_shape ok_shape = shape(1, 8, 2, 128, 524288, 52429, 0.8f, CLO_BF16);
+      CHECK(clo_select_layers(&ok_shape, nullptr, 0, 0, 0, 1, nullptr, 0, nullptr) == CLO_E_ARG);
+      CHECK(clo_select_layers(&ok_shape, nullptr, 0, 65, 0, 1, nullptr, 0, nullptr) == CLO_E_ARG);
+      CHECK(clo_select_layers(&ok_shape, nullptr, -1, 4, 0, 1, nullptr, 0, nullptr) == CLO_E_ARG);
+      clo_shape f32 = shape(1, 8, 2, 128, 524288, 52429, 0.8f, CLO_F32);
+      CHECK(clo_select_layers(&f32, nullptr, 0, 4, 0, 1, nullptr, 0, nullptr) == CLO_E_UNSUPPORTED);
+      clo_shape wide = shape(64, 32, 8, 128, 131072, 13108, 0.8f, CLO_BF16);  // 512 units per layer
+      CHECK(clo_select_layers(&wide, nullptr, 0, 4, 0, 1, nullptr, 0, nullptr) == CLO_E_UNSUPPORTED);
+      clo_shape blocks = shape(1, 8, 2, 128, 524288, 52432, 0.8f, CLO_BF16);
+      blocks.block_size = 16;
+      CHECK(clo_select_layers(&blocks, nullptr, 0, 4, 0, 1, nullptr, 0, nullptr) == CLO_E_UNSUPPORTED);
+      clo_shape longer = shape(1, 8, 2, 128, 128 * 16384 + 1, 209716, 0.8f, CLO_BF16);  // 129 chunks
+      CHECK(clo_select_layers(&longer, nullptr, 0, 4, 0, 1, nullptr, 0, nullptr) == CLO_E_UNSUPPORTED);
+    }
   }
 
   // the last-error buffer at every length, including 0 and 1

@@ -30,17 +30,18 @@ def enforce_all_layers(p):
     raise RuntimeError("margins did not settle")
 
 
-@pytest.mark.parametrize("select_streams,gather", [(1, "resident"), (2, "resident"), (3, "resident"),
-                                                   (1, "per-layer")])
-def test_layer_loop_matches_sequential_and_oracle(need_gpu, select_streams, gather):
+@pytest.mark.parametrize("select_streams,gather,select", [(1, "resident", "per-layer"), (2, "resident", "per-layer"),
+                                                          (3, "resident", "per-layer"), (1, "per-layer", "per-layer"),
+                                                          (1, "resident", "batched"), (1, "per-layer", "batched")])
+def test_layer_loop_matches_sequential_and_oracle(need_gpu, select_streams, gather, select):
     import torch
 
     from top_sparse_attention_02_amd import workload
 
     p = enforce_all_layers(multi_layer_problem())
     layers = workload.load_layers(p)
-    loop = workload.LayerLoop(layers, select_streams=select_streams, gather=gather)
-    log(f"[case layer loop, {select_streams} select streams, {gather} gather] cold step")
+    loop = workload.LayerLoop(layers, select_streams=select_streams, gather=gather, select=select)
+    log(f"[case layer loop, {select_streams} select streams, {gather} gather, {select} selection] cold step")
     loop.step(cold=True)
     torch.cuda.synchronize()
     loop.check()

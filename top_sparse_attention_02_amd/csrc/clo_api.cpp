@@ -607,6 +607,102 @@ clo_status clo_gather_layers(const void* plan, int32_t n_layers, int32_t blocks,
                     "gather launch");
 }
 
+size_t clo_select_plan_size(int32_t n_layers) {
+  if (n_layers < 1 || n_layers > 4096) return 0;
+  return (size_t)round_up((int64_t)sizeof(SelectPlanHeader) + (int64_t)n_layers * (int64_t)sizeof(SelectPlanLayer),
+                          256);
+}
+
+namespace {
+
+// What the multi-layer selection supports: bf16 layers of at most
+// kFusedReuseUnits units, token top-k, and at most kFusedMaxBlocks chunks.
+clo_status check_select_shape(const Plan& p, const char* what) {
+  if (p.a.dtype != CLO_BF16) return fail(CLO_E_UNSUPPORTED, "%s: multi-layer selection takes bf16 layers", what);
+  if (p.U < 1 || p.U > kFusedReuseUnits)
+    return fail(CLO_E_UNSUPPORTED, "%s: batch * n_kv_heads = %lld outside 1..%d", what, (long long)p.U,
+                kFusedReuseUnits);
+  if (p.a.bs > 1) return fail(CLO_E_UNSUPPORTED, "%s: multi-layer selection takes token top-k (block_size <= 1)", what);
+  if ((p.a.N + kTopkChunk - 1) / kTopkChunk > kFusedMaxBlocks)
+    return fail(CLO_E_UNSUPPORTED, "%s: context %lld beyond %lld", what, (long long)p.a.N,
+                (long long)kFusedMaxBlocks * kTopkChunk);
+  return ok();
+}
+
+}  // namespace
+
+clo_status clo_select_plan(const clo_select_layer* layers, int32_t n_layers, void* plan, size_t plan_bytes) {
+  if (!layers) return fail(CLO_E_ARG, "layers is NULL");
+  const size_t need = clo_select_plan_size(n_layers);
+  if (!need) return fail(CLO_E_ARG, "n_layers %d outside 1..4096", n_layers);
+  if (plan_bytes < need) return fail(CLO_E_ARG, "plan has %zu bytes, %zu needed", plan_bytes, need);
+  clo_status st;
+  if ((st = check_device(plan, need, "plan"))) return st;
+  std::vector<SelectPlanLayer> host((size_t)n_layers);
+  Plan p0;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const clo_select_layer& g = layers[l];
+    Plan p;
+    if ((st = make_plan(g.shape, g.layer ? g.layer->persistent_mask : 0, &p))) return st;
+    if ((st = check_select_shape(p, "layer"))) return st;
+    if (l == 0) {
+      p0 = p;
+    } else if (p.a.B != p0.a.B || p.a.Hq != p0.a.Hq || p.a.Hkv != p0.a.Hkv || p.a.N != p0.a.N ||
+               p.a.k != p0.a.k) {
+      return fail(CLO_E_ARG, "layer %d: batch, heads, context and top-k must equal layer 0's", l);
+    }
+    if ((st = check_flag_ptr(g.wait_flag, "wait_flag")) || (st = check_flag_ptr(g.signal_flag, "signal_flag")))
+      return st;
+    if ((st = check_layer(g.layer, &p, NEED_IDX | NEED_SCORE | NEED_HBM_K))) return st;
+    if ((st = check_device(g.q, q_bytes(p), "q"))) return st;
+    if ((st = check_device(g.q_prev, q_bytes(p), "q_prev"))) return st;
+    if ((st = check_device(g.reuse, (size_t)p.U, "reuse"))) return st;
+    if (g.cos && (st = check_device(g.cos, (size_t)p.U * 4, "cos"))) return st;
+    Workspace w;
+    if ((st = bind_ws(p, g.ws, g.ws_bytes, &w))) return st;
+    SelectPlanLayer& d = host[(size_t)l];
+    memset(&d, 0, sizeof d);
+    d.a = p.a;
+    d.a.err = nullptr;
+    d.q = g.q;
+    d.q_prev = g.q_prev;
+    d.reuse = g.reuse;
+    d.cos = g.cos;
+    d.w = w;
+    d.wait_flag = g.wait_flag;
+    d.signal_flag = g.signal_flag;
+  }
+  SelectPlanHeader hdr;
+  memset(&hdr, 0, sizeof hdr);
+  hdr.n_layers = (uint32_t)n_layers;
+  hipError_t e = hipMemcpy(plan, &hdr, sizeof hdr, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(static_cast<char*>(plan) + sizeof(SelectPlanHeader), host.data(),
+                  host.size() * sizeof(SelectPlanLayer), hipMemcpyHostToDevice);
+  return hip_status(e, "writing the selection plan");
+}
+
+clo_status clo_select_layers(const clo_shape* shape, const void* plan, int32_t first, int32_t count,
+                             uint32_t wait_value, uint32_t signal_value, uint32_t* error_word, uint32_t spin_limit,
+                             void* stream) {
+  Plan p;
+  clo_status st;
+  if ((st = make_plan(shape, 0, &p))) return st;
+  if ((st = check_select_shape(p, "shape"))) return st;
+  if (count < 1 || count > kMaxSelectBatch) return fail(CLO_E_ARG, "count %d outside 1..%d", count, kMaxSelectBatch);
+  if (first < 0 || first > 4096 - count) return fail(CLO_E_ARG, "first %d outside the plan's 4096 layers", first);
+  const size_t need = clo_select_plan_size(first + count);
+  if ((st = check_device(plan, need, "plan"))) return st;
+  if ((st = check_flag_ptr(error_word, "error_word"))) return st;
+  auto* hdr = static_cast<SelectPlanHeader*>(const_cast<void*>(plan));
+  auto* entries = reinterpret_cast<const SelectPlanLayer*>(static_cast<const char*>(plan) + sizeof(SelectPlanHeader));
+  const int cmax = (int)((p.a.N + kTopkChunk - 1) / kTopkChunk);
+  return hip_status(launch_select_layers(entries, hdr, first, count, p.a, cmax, wait_value, signal_value,
+                                         spin_limit ? spin_limit : (1u << 22), error_word, num_cus(),
+                                         static_cast<hipStream_t>(stream)),
+                    "selection launch");
+}
+
 clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const void* q, void* out, void* ws,
                            size_t ws_bytes, const clo_sync* sync, void* stream) {
   Plan p;

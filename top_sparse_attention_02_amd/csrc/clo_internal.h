@@ -217,6 +217,34 @@ struct GatherPlanLayer {
 };
 hipError_t launch_gather_layers(const GatherPlanLayer* plan, int n_layers, int blocks, uint32_t wait_value,
                                 uint32_t signal_value, uint32_t limit, uint32_t* error_word, hipStream_t s);
+// One layer of a multi-layer selection plan (device memory, written by the host):
+// what clo_reuse_select needs for the layer, its workspace views and its flags.
+struct SelectPlanLayer {
+  LayerArgs a;
+  const void* q;
+  const void* q_prev;
+  uint8_t* reuse;
+  float* cos;
+  Workspace w;
+  const uint32_t* wait_flag;   // the layer's selection starts once *wait_flag >= wait_value (may be NULL)
+  uint32_t* signal_flag;       // set to signal_value once the layer's selection is done (may be NULL)
+};
+// Counters of a selection launch sequence, at the start of the plan.
+struct SelectPlanHeader {
+  uint32_t score_counter;  // scoring work items taken
+  uint32_t topk_done;      // top-k blocks finished
+  uint32_t n_layers;       // layers the plan holds (launches past them are refused on the GPU)
+  uint32_t pad[61];
+};
+constexpr int kMaxSelectBatch = 64;  // layers per multi-layer selection
+// Blocks of a one-launch top-k, all resident at once (so chunks per unit at most).
+constexpr int kFusedMaxBlocks = 128;
+// Reuse test and unit lists (one block per layer, after the layer's wait),
+// scoring and top-k of plan layers first .. first + count - 1; the top-k's
+// last block stores signal_value to every layer's signal flag.
+hipError_t launch_select_layers(const SelectPlanLayer* plan, SelectPlanHeader* hdr, int first, int count,
+                                const LayerArgs& shape, int cmax, uint32_t wait_value, uint32_t signal_value,
+                                uint32_t limit, uint32_t* error_word, int num_cu, hipStream_t s);
 hipError_t launch_zero(uint32_t* word, hipStream_t s, uint32_t* word2 = nullptr);
 hipError_t launch_stream_read(const void* src, int64_t n16, int blocks, uint32_t* sink, hipStream_t s);
 hipError_t launch_attn_partial(const LayerArgs& a, const void* q, float* part, Span sp, int64_t max_units,

@@ -164,16 +164,14 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
 // on a select stream whose every launch waits behind other streams' memory
 // traffic.
 template <typename T>
-__global__ __launch_bounds__(1024) void reuse_compact_kernel(const T* __restrict__ q, const T* __restrict__ qp,
-                                                             uint8_t* __restrict__ reuse, float* __restrict__ cosv,
-                                                             int Hkv, int Hq, int G, HeadTau tau, int U,
-                                                             uint64_t pmask, int32_t* __restrict__ meta,
-                                                             int32_t* __restrict__ list_all,
-                                                             int32_t* __restrict__ list_host,
-                                                             int32_t* __restrict__ list_hit,
-                                                             uint32_t* __restrict__ h0, uint32_t* __restrict__ h0b,
-                                                             const uint32_t* wait_flag, uint32_t wait_value,
-                                                             uint32_t limit, uint32_t* error_word) {
+__device__ __forceinline__ void reuse_compact_body(const T* __restrict__ q, const T* __restrict__ qp,
+                                                   uint8_t* __restrict__ reuse, float* __restrict__ cosv, int Hkv,
+                                                   int Hq, int G, const float* tau_h, int U, uint64_t pmask,
+                                                   int32_t* __restrict__ meta, int32_t* __restrict__ list_all,
+                                                   int32_t* __restrict__ list_host, int32_t* __restrict__ list_hit,
+                                                   uint32_t* __restrict__ h0, uint32_t* __restrict__ h0b,
+                                                   const uint32_t* wait_flag, uint32_t wait_value, uint32_t limit,
+                                                   uint32_t* error_word) {
   __shared__ uint8_t s_reuse[kFusedReuseUnits];
   static_assert(kFusedReuseUnits <= 1024, "one unit per thread in the compaction");
   if (wait_flag && threadIdx.x == 0) {
@@ -192,7 +190,7 @@ __global__ __launch_bounds__(1024) void reuse_compact_kernel(const T* __restrict
   for (int u = wave; u < U; u += 16) {
     const float c = group_cosine(q, qp, u, Hkv, Hq, G);
     if (lane == 0) {
-      const uint8_t r = (c >= tau.t[u % Hkv]) ? 1 : 0;
+      const uint8_t r = (c >= tau_h[u % Hkv]) ? 1 : 0;
       if (cosv) cosv[u] = c;
       reuse[u] = r;
       s_reuse[u] = r;
@@ -203,6 +201,90 @@ __global__ __launch_bounds__(1024) void reuse_compact_kernel(const T* __restrict
   rb.first[1] = U;
   compact_units([&](int u) { return s_reuse[u] == 0; }, U, Hkv, pmask, 1, rb, meta, list_all, list_host, list_hit,
                 h0, h0b);
+}
+
+template <typename T>
+__global__ __launch_bounds__(1024) void reuse_compact_kernel(const T* __restrict__ q, const T* __restrict__ qp,
+                                                             uint8_t* __restrict__ reuse, float* __restrict__ cosv,
+                                                             int Hkv, int Hq, int G, HeadTau tau, int U,
+                                                             uint64_t pmask, int32_t* __restrict__ meta,
+                                                             int32_t* __restrict__ list_all,
+                                                             int32_t* __restrict__ list_host,
+                                                             int32_t* __restrict__ list_hit,
+                                                             uint32_t* __restrict__ h0, uint32_t* __restrict__ h0b,
+                                                             const uint32_t* wait_flag, uint32_t wait_value,
+                                                             uint32_t limit, uint32_t* error_word) {
+  reuse_compact_body<T>(q, qp, reuse, cosv, Hkv, Hq, G, tau.t, U, pmask, meta, list_all, list_host, list_hit, h0,
+                        h0b, wait_flag, wait_value, limit, error_word);
+}
+
+// The same for the layers of a multi-layer selection, one block per layer (each
+// after its own wait); block 0 also clears the launch sequence's counters.
+template <typename T>
+__global__ __launch_bounds__(1024) void reuse_compact_layers_kernel(const SelectPlanLayer* __restrict__ plan,
+                                                                    SelectPlanHeader* __restrict__ hdr, int first,
+                                                                    uint32_t wait_value, uint32_t limit,
+                                                                    uint32_t* error_word) {
+  if ((uint32_t)first + gridDim.x > hdr->n_layers) {  // layers the plan does not hold: refused
+    if (error_word && blockIdx.x == 0 && threadIdx.x == 0) atomicCAS(error_word, 0u, (uint32_t)CLO_E_ARG);
+    return;
+  }
+  const SelectPlanLayer& L = plan[first + (int)blockIdx.x];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    hdr->score_counter = 0u;
+    hdr->topk_done = 0u;
+  }
+  reuse_compact_body<T>(static_cast<const T*>(L.q), static_cast<const T*>(L.q_prev), L.reuse, L.cos, L.a.Hkv, L.a.Hq,
+                        L.a.G, L.a.tau_h, L.a.B * L.a.Hkv, L.a.pmask, L.w.meta, L.w.list_all, L.w.list_host,
+                        L.w.list_hit, L.w.h0, nullptr, L.wait_flag, wait_value, limit, error_word);
+}
+
+// Miss units of the layers first .. first + count - 1 of a plan before each
+// layer (pref[j]) and in all (pref[count]), from the counts the unit lists
+// left in each layer's workspace; every thread of the block reads them after
+// the barrier.
+__device__ __forceinline__ void load_miss_prefix(const SelectPlanLayer* __restrict__ plan,
+                                                 const SelectPlanHeader* __restrict__ hdr, int first, int count,
+                                                 int32_t* pref) {
+  if (threadIdx.x == 0) {
+    // a launch past the plan's layers does no work (the reuse launch reported it)
+    const bool held = (uint32_t)(first + count) <= hdr->n_layers;
+    int32_t acc = 0;
+    pref[0] = 0;
+    for (int j = 0; j < count; ++j) {
+      if (held) acc += plan[first + j].w.meta[kMetaCountAll];
+      pref[j + 1] = acc;
+    }
+  }
+  __syncthreads();
+}
+
+// The layer j (0 .. count - 1) whose miss units hold unit gu of the batch.
+__device__ __forceinline__ int layer_of(const int32_t* pref, int gu) {
+  int j = 0;
+  while (pref[j + 1] <= gu) ++j;
+  return j;
+}
+
+// End of a multi-layer selection: each block releases its writes at agent scope
+// and counts itself done; the last one clears the count and stores
+// signal_value to every layer's signal flag (release).
+__device__ __forceinline__ void select_layers_done(const SelectPlanLayer* __restrict__ plan,
+                                                   SelectPlanHeader* __restrict__ hdr, int first, int count,
+                                                   uint32_t signal_value) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&hdr->topk_done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == gridDim.x - 1) {
+      __hip_atomic_store(&hdr->topk_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int held = (uint32_t)(first + count) <= hdr->n_layers ? count : 0;
+      for (int j = 0; j < held; ++j) {
+        uint32_t* f = plan[first + j].signal_flag;
+        if (f) __hip_atomic_store(f, signal_value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- A2 scoring
@@ -330,15 +412,129 @@ constexpr int kScoreItem = 1024;
 // compiler so lets it keep all of an iteration's 16-byte key loads in flight
 // instead of rationing registers for a higher occupancy (632 vs 650 us for
 // 3.4 GB on MI355X).
+// One work item of the MFMA scoring: keys c * kScoreItem .. of unit u, scored
+// into keys[u], their digit 1 counted into s_h.  Thread 0 takes the next item
+// from *counter once the item's last key loads are issued and leaves it in
+// *s_item.
 template <int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void score_mfma_kernel(
-    LayerArgs a, const uint16_t* __restrict__ q, Span sp,
-                                                         uint32_t* __restrict__ keys, uint32_t* __restrict__ counter,
-                                                         uint32_t* __restrict__ h0, uint32_t* __restrict__ h1,
-                                                         TopkState* __restrict__ st, uint32_t* __restrict__ fs) {
+__device__ __forceinline__ void score_mfma_item(const LayerArgs& a, const uint16_t* __restrict__ q,
+                                                uint32_t* __restrict__ keys, int u, int c,
+                                                uint32_t* __restrict__ counter, uint32_t (*s_h)[257],
+                                                uint32_t* s_item) {
   constexpr int TILES = 8;                         // 16-key tiles per wave iteration (128 keys)
   constexpr int kKeysPerWave = kScoreItem / 4;     // 256
   static_assert(G <= 8, "group of at most 8 query heads");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, ks = lane >> 4;       // tile column / k-slice of this lane
+  bf16x8 qa[4];
+  const int b = u / a.Hkv, h = u % a.Hkv;
+  const uint16_t* kb = unit_keys<uint16_t>(a, b, h);
+  {
+    // the query operand of the item's unit (64 bytes per lane, an L2 hit after
+    // the first item of the unit), loaded without a branch so that the item's
+    // key loads are not held behind it
+    const int head = col;  // row of Qpad
+    const uint16_t* qh = q + ((int64_t)b * a.Hq + (int64_t)h * G + (head < G ? head : 0)) * kHeadDim;
+    const uint32_t keep = head < G ? ~0u : 0u;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(qh + s * 32 + ks * 8);
+      qa[s] = __builtin_bit_cast(bf16x8, w & keep);
+    }
+  }
+  uint32_t* kout = keys + (int64_t)u * a.Np;
+  const int64_t w_begin = (int64_t)c * kScoreItem + (int64_t)wave * kKeysPerWave;
+  // digit-1 bins of the previous iteration's keys, counted only after this
+  // iteration's loads are issued: an LDS atomic placed before them keeps the
+  // compiler from issuing them early
+  uint32_t pend[TILES / 4];
+  bool have_pend = false;
+  // the next item is claimed once the last key loads of this one are issued:
+  // the counter's round trip then overlaps the item's tail, while a claim at
+  // the item's start would hold work back from blocks that run out earlier
+  uint32_t next_item = 0;
+  bool claimed = false;
+#pragma unroll
+  for (int t0 = 0; t0 < kKeysPerWave; t0 += 16 * TILES) {
+    if (w_begin + t0 >= a.N) break;  // uniform per wave
+    u32x4 kbuf[TILES][4];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      int64_t row = w_begin + t0 + t * 16 + col;
+      row = row < a.N ? row : a.N - 1;
+      const uint16_t* kr = kb + row * kHeadDim + ks * 8;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kbuf[t][s] = *reinterpret_cast<const u32x4*>(kr + s * 32);
+    }
+    if (t0 + 16 * TILES >= kKeysPerWave && threadIdx.x == 0) {
+      next_item = atomicAdd(counter, 1u);
+      claimed = true;
+    }
+    if (have_pend) {
+#pragma unroll
+      for (int i = 0; i < TILES / 4; ++i) atomicAdd(&s_h[wave][pend[i]], 1u);
+    }
+    float mt[TILES];  // tile maxima, valid in lanes 0..15 (lane = key within the tile)
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8, kbuf[t][s]), acc, 0, 0, 0);
+      // max over the unit's heads: rows 0..min(G,4)-1 here, rows 4..G-1 in lane + 16
+      float m = acc[0];
+      if (G > 1) m = fmaxf(m, acc[1]);
+      if (G > 2) m = fmaxf(m, acc[2]);
+      if (G > 3) m = fmaxf(m, acc[3]);
+      if (G > 4) {
+        float m2 = acc[0];
+        if (G > 5) m2 = fmaxf(m2, acc[1]);
+        if (G > 6) m2 = fmaxf(m2, acc[2]);
+        if (G > 7) m2 = fmaxf(m2, acc[3]);
+        m = fmaxf(m, __shfl_down(m2, 16, 64));
+      }
+      mt[t] = m;
+    }
+    // lane L of the wave takes key L of each 4-tile group: one 256-byte store
+    // per group instead of four 64-byte ones
+#pragma unroll
+    for (int t4 = 0; t4 < TILES; t4 += 4) {
+      float v = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float x = __shfl(mt[t4 + t], col, 64);
+        if (ks == t) v = x;
+      }
+      const int64_t key = w_begin + t0 + t4 * 16 + lane;
+      const uint32_t sk = score_key(v);
+      if (key < a.N) kout[key] = sk;
+      pend[t4 / 4] = key < a.N ? sk >> 24 : 256u;
+    }
+    have_pend = true;
+  }
+  if (have_pend) {
+#pragma unroll
+    for (int i = 0; i < TILES / 4; ++i) atomicAdd(&s_h[wave][pend[i]], 1u);
+  }
+  // read at the top of the next iteration, after the barrier there; every
+  // wave read the current value before the barrier that follows the flush
+  if (threadIdx.x == 0) *s_item = claimed ? next_item : atomicAdd(counter, 1u);
+  // the LDS writes of this item (s_item, the digit counts) complete before the
+  // barrier at the loop top: hipcc (ROCm 7.2, gfx950) emits that barrier on
+  // this back edge without the LDS wait its fence implies, and other waves
+  // then read the previous item number
+  wait_lds();
+}
+
+// The grid holds two blocks per CU, i.e. two waves per SIMD; telling the
+// compiler so lets it keep all of an iteration's 16-byte key loads in flight
+// instead of rationing registers for a higher occupancy (632 vs 650 us for
+// 3.4 GB on MI355X).
+template <int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void score_mfma_kernel(
+    LayerArgs a, const uint16_t* __restrict__ q, Span sp, uint32_t* __restrict__ keys,
+    uint32_t* __restrict__ counter, uint32_t* __restrict__ h0, uint32_t* __restrict__ h1,
+    TopkState* __restrict__ st, uint32_t* __restrict__ fs) {
   __shared__ uint32_t s_item;
   __shared__ uint32_t s_h[4][257];  // bin 256 takes keys past the end (not flushed)
   clear_score_hist(s_h);
@@ -346,10 +542,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int lo = *sp.lo;
   const int64_t items = (int64_t)(*sp.hi - lo) * nch;
   const int32_t* list = sp.list + lo;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, ks = lane >> 4;       // tile column / k-slice of this lane
   int cur_u = -1, prev_c = 0;
-  bf16x8 qa[4];
   if (threadIdx.x == 0) s_item = atomicAdd(counter, 1u);
   for (;;) {
     __syncthreads();
@@ -362,103 +555,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const int c = (int)(it % nch);
     prev_c = c;
     cur_u = u;
-    const int b = u / a.Hkv, h = u % a.Hkv;
-    const uint16_t* kb = unit_keys<uint16_t>(a, b, h);
-    {
-      // the query operand of the item's unit (64 bytes per lane, an L2 hit after
-      // the first item of the unit), loaded without a branch so that the item's
-      // key loads are not held behind it
-      const int head = col;  // row of Qpad
-      const uint16_t* qh = q + ((int64_t)b * a.Hq + (int64_t)h * G + (head < G ? head : 0)) * kHeadDim;
-      const uint32_t keep = head < G ? ~0u : 0u;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(qh + s * 32 + ks * 8);
-        qa[s] = __builtin_bit_cast(bf16x8, w & keep);
-      }
+    score_mfma_item<G>(a, q, keys, u, c, counter, s_h, &s_item);
+  }
+}
+
+// The scoring of a multi-layer selection: the same persistent blocks take items
+// from one counter over the miss units of all the batch's layers, layer after
+// layer, so that the short scorings of small layers share one launch and one
+// ramp-up and tail.
+template <int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void score_mfma_layers_kernel(
+    const SelectPlanLayer* __restrict__ plan, SelectPlanHeader* __restrict__ hdr, int first, int count,
+    uint32_t* err) {
+  __shared__ uint32_t s_item;
+  __shared__ uint32_t s_h[4][257];
+  __shared__ int32_t s_pref[kMaxSelectBatch + 1];
+  clear_score_hist(s_h);
+  load_miss_prefix(plan, hdr, first, count, s_pref);
+  const int64_t nch = (plan[first].a.N + kScoreItem - 1) / kScoreItem;
+  const int64_t items = (int64_t)s_pref[count] * nch;
+  uint32_t* counter = &hdr->score_counter;
+  int cur_u = -1, prev_c = 0, cur_j = 0;
+  if (threadIdx.x == 0) s_item = atomicAdd(counter, 1u);
+  for (;;) {
+    __syncthreads();
+    const int64_t it = s_item;
+    if (cur_u >= 0) {
+      const SelectPlanLayer& P = plan[first + cur_j];
+      flush_score_hist(s_h, cur_u, prev_c, P.a.k, P.w.h0, P.w.h1, P.w.tstate, P.w.fsync);
     }
-    uint32_t* kout = keys + (int64_t)u * a.Np;
-    const int64_t w_begin = (int64_t)c * kScoreItem + (int64_t)wave * kKeysPerWave;
-    // digit-1 bins of the previous iteration's keys, counted only after this
-    // iteration's loads are issued: an LDS atomic placed before them keeps the
-    // compiler from issuing them early
-    uint32_t pend[TILES / 4];
-    bool have_pend = false;
-    // the next item is claimed once the last key loads of this one are issued:
-    // the counter's round trip then overlaps the item's tail, while a claim at
-    // the item's start would hold work back from blocks that run out earlier
-    uint32_t next_item = 0;
-    bool claimed = false;
-#pragma unroll
-    for (int t0 = 0; t0 < kKeysPerWave; t0 += 16 * TILES) {
-      if (w_begin + t0 >= a.N) break;  // uniform per wave
-      u32x4 kbuf[TILES][4];
-#pragma unroll
-      for (int t = 0; t < TILES; ++t) {
-        int64_t row = w_begin + t0 + t * 16 + col;
-        row = row < a.N ? row : a.N - 1;
-        const uint16_t* kr = kb + row * kHeadDim + ks * 8;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kbuf[t][s] = *reinterpret_cast<const u32x4*>(kr + s * 32);
+    __syncthreads();
+    if (it >= items) break;  // uniform per block
+    const int gu = (int)(it / nch);
+    const int j = layer_of(s_pref, gu);
+    const SelectPlanLayer& L = plan[first + j];
+    if (L.a.G != G || L.a.N != plan[first].a.N) {  // a layer the launch was not shaped for: reported, skipped
+      if (threadIdx.x == 0) {
+        if (err) atomicCAS(err, 0u, (uint32_t)CLO_E_ARG);
+        s_item = atomicAdd(counter, 1u);
       }
-      if (t0 + 16 * TILES >= kKeysPerWave && threadIdx.x == 0) {
-        next_item = atomicAdd(counter, 1u);
-        claimed = true;
-      }
-      if (have_pend) {
-#pragma unroll
-        for (int i = 0; i < TILES / 4; ++i) atomicAdd(&s_h[wave][pend[i]], 1u);
-      }
-      float mt[TILES];  // tile maxima, valid in lanes 0..15 (lane = key within the tile)
-#pragma unroll
-      for (int t = 0; t < TILES; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8, kbuf[t][s]), acc, 0, 0, 0);
-        // max over the unit's heads: rows 0..min(G,4)-1 here, rows 4..G-1 in lane + 16
-        float m = acc[0];
-        if (G > 1) m = fmaxf(m, acc[1]);
-        if (G > 2) m = fmaxf(m, acc[2]);
-        if (G > 3) m = fmaxf(m, acc[3]);
-        if (G > 4) {
-          float m2 = acc[0];
-          if (G > 5) m2 = fmaxf(m2, acc[1]);
-          if (G > 6) m2 = fmaxf(m2, acc[2]);
-          if (G > 7) m2 = fmaxf(m2, acc[3]);
-          m = fmaxf(m, __shfl_down(m2, 16, 64));
-        }
-        mt[t] = m;
-      }
-      // lane L of the wave takes key L of each 4-tile group: one 256-byte store
-      // per group instead of four 64-byte ones
-#pragma unroll
-      for (int t4 = 0; t4 < TILES; t4 += 4) {
-        float v = 0.f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float x = __shfl(mt[t4 + t], col, 64);
-          if (ks == t) v = x;
-        }
-        const int64_t key = w_begin + t0 + t4 * 16 + lane;
-        const uint32_t sk = score_key(v);
-        if (key < a.N) kout[key] = sk;
-        pend[t4 / 4] = key < a.N ? sk >> 24 : 256u;
-      }
-      have_pend = true;
+      cur_u = -1;
+      wait_lds();  // s_item is in LDS before the loop-top barrier (see score_mfma_item)
+      continue;
     }
-    if (have_pend) {
-#pragma unroll
-      for (int i = 0; i < TILES / 4; ++i) atomicAdd(&s_h[wave][pend[i]], 1u);
-    }
-    // read at the top of the next iteration, after the barrier there; every
-    // wave read the current value before the barrier that follows the flush
-    if (threadIdx.x == 0) s_item = claimed ? next_item : atomicAdd(counter, 1u);
-    // the LDS writes of this item (s_item, the digit counts) complete before the
-    // barrier at the loop top: hipcc (ROCm 7.2, gfx950) emits that barrier on
-    // this back edge without the LDS wait its fence implies, and other waves
-    // then read the previous item number
-    wait_lds();
+    const int u = L.w.list_all[gu - s_pref[j]];
+    const int c = (int)(it % nch);
+    prev_c = c;
+    cur_u = u;
+    cur_j = j;
+    score_mfma_item<G>(L.a, static_cast<const uint16_t*>(L.q), L.w.keys, u, c, counter, s_h, &s_item);
   }
 }
 
@@ -679,138 +824,156 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pass_kernel(LayerArgs a, Sp
 constexpr int kUnitThreads = 1024;
 constexpr int kUnitPerThread = 16;
 
-__global__ __launch_bounds__(kUnitThreads) void topk_unit_kernel(LayerArgs a, Span sp,
-                                                                 const uint32_t* __restrict__ keys,
-                                                                 const uint32_t* __restrict__ h0) {
+__device__ __forceinline__ void topk_unit_one(const LayerArgs& a, int u, const uint32_t* __restrict__ keys,
+                                              const uint32_t* __restrict__ h0) {
   __shared__ uint32_t hist[16][256];
   __shared__ uint32_t tot[256];
   __shared__ uint32_t s_prefix, s_mask, s_rem, s_base_gt, s_base_eq;
   __shared__ uint32_t s_wgt[16], s_weq[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lo = *sp.lo;
-  const int n_units = *sp.hi - lo;
-  const int32_t* list = sp.list + lo;
   const int64_t N = a.N;
-  for (int it = blockIdx.x; it < n_units; it += gridDim.x) {
-    const int u = list[it];
-    const uint32_t* kk = keys + (int64_t)u * a.Np;
-    int32_t* out = a.idx + (int64_t)u * a.k;
-    if (tid < 256) tot[tid] = h0[(int64_t)u * 256 + tid];
+  const uint32_t* kk = keys + (int64_t)u * a.Np;
+  int32_t* out = a.idx + (int64_t)u * a.k;
+  if (tid < 256) tot[tid] = h0[(int64_t)u * 256 + tid];
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t d, above;
+    pick_digit(tot, (uint32_t)a.k, d, above);
+    if (tid == 0) {
+      s_prefix = d << 24;
+      s_mask = 0xFF000000u;
+      s_rem = (uint32_t)a.k - above;
+    }
+  }
+  for (int shift = 16; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 16 * 256; i += kUnitThreads) (&hist[0][0])[i] = 0u;
+    __syncthreads();
+    const uint32_t prefix = s_prefix, mask = s_mask;
+    constexpr int kStep = kUnitThreads * 4;
+    for (int64_t base = (int64_t)tid * 4; base < N; base += (int64_t)kStep * kTopkUnroll) {
+      u32x4 v[kTopkUnroll];
+#pragma unroll
+      for (int j = 0; j < kTopkUnroll; ++j) {
+        const int64_t i = base + (int64_t)j * kStep;
+        v[j] = i < N ? *reinterpret_cast<const u32x4*>(kk + i) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < kTopkUnroll; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t kv = v[j][e];
+          if (base + (int64_t)j * kStep + e < N && (kv & mask) == prefix)
+            atomicAdd(&hist[wave][(kv >> shift) & 255u], 1u);
+        }
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t sum = 0;
+      for (int w = 0; w < 16; ++w) sum += hist[w][tid];
+      tot[tid] = sum;
+    }
     __syncthreads();
     if (wave == 0) {
       uint32_t d, above;
-      pick_digit(tot, (uint32_t)a.k, d, above);
+      pick_digit(tot, s_rem, d, above);
       if (tid == 0) {
-        s_prefix = d << 24;
-        s_mask = 0xFF000000u;
-        s_rem = (uint32_t)a.k - above;
+        s_rem -= above;
+        s_prefix = prefix | (d << shift);
+        s_mask = mask | (255u << shift);
       }
-    }
-    for (int shift = 16; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 16 * 256; i += kUnitThreads) (&hist[0][0])[i] = 0u;
-      __syncthreads();
-      const uint32_t prefix = s_prefix, mask = s_mask;
-      constexpr int kStep = kUnitThreads * 4;
-      for (int64_t base = (int64_t)tid * 4; base < N; base += (int64_t)kStep * kTopkUnroll) {
-        u32x4 v[kTopkUnroll];
-#pragma unroll
-        for (int j = 0; j < kTopkUnroll; ++j) {
-          const int64_t i = base + (int64_t)j * kStep;
-          v[j] = i < N ? *reinterpret_cast<const u32x4*>(kk + i) : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int j = 0; j < kTopkUnroll; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t kv = v[j][e];
-            if (base + (int64_t)j * kStep + e < N && (kv & mask) == prefix)
-              atomicAdd(&hist[wave][(kv >> shift) & 255u], 1u);
-          }
-      }
-      __syncthreads();
-      if (tid < 256) {
-        uint32_t sum = 0;
-        for (int w = 0; w < 16; ++w) sum += hist[w][tid];
-        tot[tid] = sum;
-      }
-      __syncthreads();
-      if (wave == 0) {
-        uint32_t d, above;
-        pick_digit(tot, s_rem, d, above);
-        if (tid == 0) {
-          s_rem -= above;
-          s_prefix = prefix | (d << shift);
-          s_mask = mask | (255u << shift);
-        }
-      }
-      __syncthreads();
-    }
-    const uint32_t T = s_prefix, need = s_rem;
-    if (tid == 0) {
-      s_base_gt = 0u;
-      s_base_eq = 0u;
     }
     __syncthreads();
-    constexpr int kTile = kUnitThreads * kUnitPerThread;
-    for (int64_t t0 = 0; t0 < N; t0 += kTile) {
-      const int64_t i0 = t0 + (int64_t)tid * kUnitPerThread;
-      u32x4 v[kUnitPerThread / 4];
-#pragma unroll
-      for (int j = 0; j < kUnitPerThread / 4; ++j)
-        v[j] = (i0 + 4 * j < N) ? *reinterpret_cast<const u32x4*>(kk + i0 + 4 * j) : u32x4{0u, 0u, 0u, 0u};
-      uint32_t cg = 0, ce = 0;
-#pragma unroll
-      for (int j = 0; j < kUnitPerThread / 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool valid = i0 + 4 * j + e < N;
-          cg += (valid && v[j][e] > T);
-          ce += (valid && v[j][e] == T);
-        }
-      uint32_t xg = cg, xe = ce;
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t yg = __shfl_up(xg, off, 64), ye = __shfl_up(xe, off, 64);
-        if (lane >= off) {
-          xg += yg;
-          xe += ye;
-        }
-      }
-      if (lane == 63) {
-        s_wgt[wave] = xg;
-        s_weq[wave] = xe;
-      }
-      __syncthreads();
-      uint32_t pg = s_base_gt + xg - cg, pe = s_base_eq + xe - ce;
-      for (int w = 0; w < wave; ++w) {
-        pg += s_wgt[w];
-        pe += s_weq[w];
-      }
-#pragma unroll
-      for (int j = 0; j < kUnitPerThread / 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t i = i0 + 4 * j + e;
-          if (i >= N) continue;
-          const uint32_t kv = v[j][e];
-          if (kv > T) {
-            const uint32_t pos = pg + (pe < need ? pe : need);
-            if (pos < (uint32_t)a.k) out[pos] = (int32_t)i;
-            ++pg;
-          } else if (kv == T) {
-            if (pe < need && pg + pe < (uint32_t)a.k) out[pg + pe] = (int32_t)i;
-            ++pe;
-          }
-        }
-      __syncthreads();
-      if (tid == 0) {
-        for (int w = 0; w < 16; ++w) {
-          s_base_gt += s_wgt[w];
-          s_base_eq += s_weq[w];
-        }
-      }
-      __syncthreads();
-    }
   }
+  const uint32_t T = s_prefix, need = s_rem;
+  if (tid == 0) {
+    s_base_gt = 0u;
+    s_base_eq = 0u;
+  }
+  __syncthreads();
+  constexpr int kTile = kUnitThreads * kUnitPerThread;
+  for (int64_t t0 = 0; t0 < N; t0 += kTile) {
+    const int64_t i0 = t0 + (int64_t)tid * kUnitPerThread;
+    u32x4 v[kUnitPerThread / 4];
+#pragma unroll
+    for (int j = 0; j < kUnitPerThread / 4; ++j)
+      v[j] = (i0 + 4 * j < N) ? *reinterpret_cast<const u32x4*>(kk + i0 + 4 * j) : u32x4{0u, 0u, 0u, 0u};
+    uint32_t cg = 0, ce = 0;
+#pragma unroll
+    for (int j = 0; j < kUnitPerThread / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = i0 + 4 * j + e < N;
+        cg += (valid && v[j][e] > T);
+        ce += (valid && v[j][e] == T);
+      }
+    uint32_t xg = cg, xe = ce;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t yg = __shfl_up(xg, off, 64), ye = __shfl_up(xe, off, 64);
+      if (lane >= off) {
+        xg += yg;
+        xe += ye;
+      }
+    }
+    if (lane == 63) {
+      s_wgt[wave] = xg;
+      s_weq[wave] = xe;
+    }
+    __syncthreads();
+    uint32_t pg = s_base_gt + xg - cg, pe = s_base_eq + xe - ce;
+    for (int w = 0; w < wave; ++w) {
+      pg += s_wgt[w];
+      pe += s_weq[w];
+    }
+#pragma unroll
+    for (int j = 0; j < kUnitPerThread / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t i = i0 + 4 * j + e;
+        if (i >= N) continue;
+        const uint32_t kv = v[j][e];
+        if (kv > T) {
+          const uint32_t pos = pg + (pe < need ? pe : need);
+          if (pos < (uint32_t)a.k) out[pos] = (int32_t)i;
+          ++pg;
+        } else if (kv == T) {
+          if (pe < need && pg + pe < (uint32_t)a.k) out[pg + pe] = (int32_t)i;
+          ++pe;
+        }
+      }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 0; w < 16; ++w) {
+        s_base_gt += s_wgt[w];
+        s_base_eq += s_weq[w];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kUnitThreads) void topk_unit_kernel(LayerArgs a, Span sp,
+                                                                 const uint32_t* __restrict__ keys,
+                                                                 const uint32_t* __restrict__ h0) {
+  const int lo = *sp.lo;
+  const int n_units = *sp.hi - lo;
+  const int32_t* list = sp.list + lo;
+  for (int it = blockIdx.x; it < n_units; it += gridDim.x) topk_unit_one(a, list[it], keys, h0);
+}
+
+// The single-block top-k of a multi-layer selection: the blocks take the miss
+// units of all the batch's layers; the last block to finish signals every layer.
+__global__ __launch_bounds__(kUnitThreads) void topk_unit_layers_kernel(const SelectPlanLayer* __restrict__ plan,
+                                                                        SelectPlanHeader* __restrict__ hdr, int first,
+                                                                        int count, uint32_t signal_value) {
+  __shared__ int32_t s_pref[kMaxSelectBatch + 1];
+  load_miss_prefix(plan, hdr, first, count, s_pref);
+  const int total = s_pref[count];
+  for (int gu = blockIdx.x; gu < total; gu += gridDim.x) {
+    const int j = layer_of(s_pref, gu);
+    const SelectPlanLayer& L = plan[first + j];
+    topk_unit_one(L.a, L.w.list_all[gu - s_pref[j]], L.w.keys, L.w.h0);
+  }
+  select_layers_done(plan, hdr, first, count, signal_value);
 }
 
 // Block-wide exclusive scan of two counts (keys > T, keys == T) of each thread.
@@ -960,8 +1123,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_write_kernel(LayerArgs a, S
 // span's units g, g + groups, g + 2 groups, ... one after another.  Two blocks
 // fit a CU (66 KiB of LDS each), so four such launches running side by side
 // still fit the GPU.  The waits are bounded all the same (the error word gets
-// CLO_E_TIMEOUT, and every block still runs to its end).
-constexpr int kFusedMaxBlocks = 128;
+// CLO_E_TIMEOUT, and every block still runs to its end).  kFusedMaxBlocks is
+// in clo_internal.h.
 
 // Block-wide arrival at one of a unit's exchange counts: the block's device-scope
 // atomics are acknowledged first, then thread 0 arrives and polls until all n
@@ -983,155 +1146,188 @@ __device__ __forceinline__ void unit_arrive_wait(uint32_t* arrive, uint32_t n, u
   __syncthreads();
 }
 
+// One unit's select by the chunk block c of the unit's group (the block's
+// chunk of keys into LDS, digits 2-4 with the other chunk blocks, the write).
+__device__ __forceinline__ void topk_fused_unit(const LayerArgs& a, int u, int c, int cmax,
+                                                const uint32_t* __restrict__ keys, const uint32_t* __restrict__ h0,
+                                                uint32_t* __restrict__ fsync, uint32_t* __restrict__ ccnt,
+                                                uint32_t limit, uint32_t* err) {
+  constexpr int kLoads = kTopkChunk / (kTopkThreads * 4);  // 16-byte loads per thread
+  __shared__ u32x4 s_keys[kTopkChunk / 4];
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_prefix, s_mask, s_rem, s_x[4], s_y[4];
+  const int tid = threadIdx.x;
+  const int64_t N = a.N;
+  const int64_t c0 = (int64_t)c * kTopkChunk;
+  const int nk = (int)((c0 + kTopkChunk < N) ? kTopkChunk : N - c0);
+  const uint32_t* kk = keys + (int64_t)u * a.Np + c0;
+  uint32_t* fs = fsync + (int64_t)u * kFusedSyncWords;
+  // the chunk's keys into LDS: all loads issued first (the row stride is a
+  // multiple of 64 keys, so a 16-byte load that starts below nk stays in the row)
+  {
+    u32x4 v[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int i = (j * kTopkThreads + tid) * 4;
+      v[j] = i < nk ? *reinterpret_cast<const u32x4*>(kk + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();  // the previous unit's write has read s_keys
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) s_keys[j * kTopkThreads + tid] = v[j];
+  }
+  // digit 1 from the scoring histogram
+  s_hist[tid] = h0[(int64_t)u * 256 + tid];
+  __syncthreads();
+  if (tid < 64) {
+    uint32_t d, above;
+    pick_digit(s_hist, (uint32_t)a.k, d, above);
+    if (tid == 0) {
+      s_prefix = d << 24;
+      s_mask = 0xFF000000u;
+      s_rem = (uint32_t)a.k - above;
+    }
+  }
+  __syncthreads();
+  for (int p = 0; p < 3; ++p) {
+    const int shift = 16 - 8 * p;
+    const uint32_t prefix = s_prefix, mask = s_mask, rem = s_rem;
+    s_hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int i = (j * kTopkThreads + tid) * 4;
+      const u32x4 w = s_keys[j * kTopkThreads + tid];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i + e < nk && (w[e] & mask) == prefix) atomicAdd(&s_hist[(w[e] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (s_hist[tid]) atomicAdd(fs + p * 256 + tid, s_hist[tid]);
+    unit_arrive_wait(fs + 768 + p, (uint32_t)cmax, limit, err);
+    s_hist[tid] = __hip_atomic_load(fs + p * 256 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t d, above;
+      pick_digit(s_hist, rem, d, above);
+      if (tid == 0) {
+        s_prefix = prefix | (d << shift);
+        s_mask = mask | (255u << shift);
+        s_rem = rem - above;
+      }
+    }
+    __syncthreads();
+  }
+  // T = the k-th largest key; `need` of the keys equal to T are taken, the first by index
+  const uint32_t T = s_prefix, need = s_rem;
+  uint32_t cg = 0, ce = 0;
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int i = (j * kTopkThreads + tid) * 4;
+    const u32x4 w = s_keys[j * kTopkThreads + tid];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cg += (i + e < nk) && w[e] > T;
+      ce += (i + e < nk) && w[e] == T;
+    }
+  }
+  uint32_t tg, te;
+  block_sum2(cg, ce, s_x, s_y, tg, te);
+  uint32_t* cc = ccnt + (int64_t)u * cmax * kChunkHist;
+  if (tid == 0) {
+    __hip_atomic_store(cc + (int64_t)c * kChunkHist, tg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(cc + (int64_t)c * kChunkHist + 1, te, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  unit_arrive_wait(fs + 768 + 3, (uint32_t)cmax, limit, err);
+  // winners in the earlier chunks
+  uint32_t base_g, base_e;
+  {
+    uint32_t g = 0, e = 0;
+    if (tid < c) {
+      g = __hip_atomic_load(cc + (int64_t)tid * kChunkHist, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      e = __hip_atomic_load(cc + (int64_t)tid * kChunkHist + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    block_sum2(g, e, s_x, s_y, base_g, base_e);
+  }
+  // the winners of this chunk in ascending index order: tiles of kTopkThreads x
+  // kTopkPerThread consecutive keys, a block-wide scan per tile
+  int32_t* out = a.idx + (int64_t)u * a.k;
+  constexpr int kTile = kTopkThreads * kTopkPerThread;
+  for (int t0 = 0; t0 < nk; t0 += kTile) {  // uniform per block
+    const int i0 = t0 + tid * kTopkPerThread;
+    u32x4 v[kTopkPerThread / 4];
+#pragma unroll
+    for (int j = 0; j < kTopkPerThread / 4; ++j) v[j] = s_keys[(i0 >> 2) + j];
+    uint32_t xg = 0, xe = 0;
+#pragma unroll
+    for (int j = 0; j < kTopkPerThread / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = i0 + 4 * j + e < nk;
+        xg += valid && v[j][e] > T;
+        xe += valid && v[j][e] == T;
+      }
+    uint32_t eg, ee, sg, se;
+    scan2(xg, xe, s_x, s_y, eg, ee, sg, se);
+    uint32_t pg = base_g + eg, pe = base_e + ee;
+#pragma unroll
+    for (int j = 0; j < kTopkPerThread / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + 4 * j + e;
+        if (i >= nk) continue;
+        const uint32_t kv = v[j][e];
+        if (kv > T) {
+          const uint32_t pos = pg + (pe < need ? pe : need);
+          if (pos < (uint32_t)a.k) out[pos] = (int32_t)(c0 + i);
+          ++pg;
+        } else if (kv == T) {
+          if (pe < need && pg + pe < (uint32_t)a.k) out[pg + pe] = (int32_t)(c0 + i);
+          ++pe;
+        }
+      }
+    base_g += sg;
+    base_e += se;
+  }
+}
+
 __global__ __launch_bounds__(kTopkThreads) void topk_fused_kernel(LayerArgs a, Span sp,
                                                                   const uint32_t* __restrict__ keys,
                                                                   const uint32_t* __restrict__ h0,
                                                                   uint32_t* __restrict__ fsync,
                                                                   uint32_t* __restrict__ ccnt, int cmax,
                                                                   uint32_t limit) {
-  constexpr int kLoads = kTopkChunk / (kTopkThreads * 4);  // 16-byte loads per thread
-  __shared__ u32x4 s_keys[kTopkChunk / 4];
-  __shared__ uint32_t s_hist[256];
-  __shared__ uint32_t s_prefix, s_mask, s_rem, s_x[4], s_y[4];
   const int lo = *sp.lo;
   const int n_units = *sp.hi - lo;
   const int groups = (int)(gridDim.x / cmax);
   const int c = (int)(blockIdx.x % cmax);
-  const int tid = threadIdx.x;
-  const int64_t N = a.N;
-  const int64_t c0 = (int64_t)c * kTopkChunk;
-  const int nk = (int)((c0 + kTopkChunk < N) ? kTopkChunk : N - c0);
-  for (int ui = (int)(blockIdx.x / cmax); ui < n_units; ui += groups) {  // the same units for a group's blocks
-    const int u = sp.list[lo + ui];
-    const uint32_t* kk = keys + (int64_t)u * a.Np + c0;
-    uint32_t* fs = fsync + (int64_t)u * kFusedSyncWords;
-    // the chunk's keys into LDS: all loads issued first (the row stride is a
-    // multiple of 64 keys, so a 16-byte load that starts below nk stays in the row)
-    {
-      u32x4 v[kLoads];
-#pragma unroll
-      for (int j = 0; j < kLoads; ++j) {
-        const int i = (j * kTopkThreads + tid) * 4;
-        v[j] = i < nk ? *reinterpret_cast<const u32x4*>(kk + i) : u32x4{0u, 0u, 0u, 0u};
-      }
-      __syncthreads();  // the previous unit's write has read s_keys
-#pragma unroll
-      for (int j = 0; j < kLoads; ++j) s_keys[j * kTopkThreads + tid] = v[j];
+  for (int ui = (int)(blockIdx.x / cmax); ui < n_units; ui += groups)  // the same units for a group's blocks
+    topk_fused_unit(a, sp.list[lo + ui], c, cmax, keys, h0, fsync, ccnt, limit, a.err);
+}
+
+// The one-launch top-k of a multi-layer selection: the groups take the miss
+// units of all the batch's layers in turn; the last block to finish signals
+// every layer.
+__global__ __launch_bounds__(kTopkThreads) void topk_fused_layers_kernel(const SelectPlanLayer* __restrict__ plan,
+                                                                         SelectPlanHeader* __restrict__ hdr,
+                                                                         int first, int count, int cmax,
+                                                                         uint32_t limit, uint32_t* err,
+                                                                         uint32_t signal_value) {
+  __shared__ int32_t s_pref[kMaxSelectBatch + 1];
+  load_miss_prefix(plan, hdr, first, count, s_pref);
+  const int total = s_pref[count];
+  const int groups = (int)(gridDim.x / cmax);
+  const int c = (int)(blockIdx.x % cmax);
+  for (int gu = (int)(blockIdx.x / cmax); gu < total; gu += groups) {
+    const int j = layer_of(s_pref, gu);
+    const SelectPlanLayer& L = plan[first + j];
+    if ((L.a.N + kTopkChunk - 1) / kTopkChunk != cmax) {  // not the launch's chunk count: reported, skipped
+      if (err && threadIdx.x == 0) atomicCAS(err, 0u, (uint32_t)CLO_E_ARG);
+      continue;
     }
-    // digit 1 from the scoring histogram
-    s_hist[tid] = h0[(int64_t)u * 256 + tid];
-    __syncthreads();
-    if (tid < 64) {
-      uint32_t d, above;
-      pick_digit(s_hist, (uint32_t)a.k, d, above);
-      if (tid == 0) {
-        s_prefix = d << 24;
-        s_mask = 0xFF000000u;
-        s_rem = (uint32_t)a.k - above;
-      }
-    }
-    __syncthreads();
-    for (int p = 0; p < 3; ++p) {
-      const int shift = 16 - 8 * p;
-      const uint32_t prefix = s_prefix, mask = s_mask, rem = s_rem;
-      s_hist[tid] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kLoads; ++j) {
-        const int i = (j * kTopkThreads + tid) * 4;
-        const u32x4 w = s_keys[j * kTopkThreads + tid];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (i + e < nk && (w[e] & mask) == prefix) atomicAdd(&s_hist[(w[e] >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (s_hist[tid]) atomicAdd(fs + p * 256 + tid, s_hist[tid]);
-      unit_arrive_wait(fs + 768 + p, (uint32_t)cmax, limit, a.err);
-      s_hist[tid] = __hip_atomic_load(fs + p * 256 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      if (tid < 64) {
-        uint32_t d, above;
-        pick_digit(s_hist, rem, d, above);
-        if (tid == 0) {
-          s_prefix = prefix | (d << shift);
-          s_mask = mask | (255u << shift);
-          s_rem = rem - above;
-        }
-      }
-      __syncthreads();
-    }
-    // T = the k-th largest key; `need` of the keys equal to T are taken, the first by index
-    const uint32_t T = s_prefix, need = s_rem;
-    uint32_t cg = 0, ce = 0;
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int i = (j * kTopkThreads + tid) * 4;
-      const u32x4 w = s_keys[j * kTopkThreads + tid];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        cg += (i + e < nk) && w[e] > T;
-        ce += (i + e < nk) && w[e] == T;
-      }
-    }
-    uint32_t tg, te;
-    block_sum2(cg, ce, s_x, s_y, tg, te);
-    uint32_t* cc = ccnt + (int64_t)u * cmax * kChunkHist;
-    if (tid == 0) {
-      __hip_atomic_store(cc + (int64_t)c * kChunkHist, tg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(cc + (int64_t)c * kChunkHist + 1, te, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    unit_arrive_wait(fs + 768 + 3, (uint32_t)cmax, limit, a.err);
-    // winners in the earlier chunks
-    uint32_t base_g, base_e;
-    {
-      uint32_t g = 0, e = 0;
-      if (tid < c) {
-        g = __hip_atomic_load(cc + (int64_t)tid * kChunkHist, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        e = __hip_atomic_load(cc + (int64_t)tid * kChunkHist + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      block_sum2(g, e, s_x, s_y, base_g, base_e);
-    }
-    // the winners of this chunk in ascending index order: tiles of kTopkThreads x
-    // kTopkPerThread consecutive keys, a block-wide scan per tile
-    int32_t* out = a.idx + (int64_t)u * a.k;
-    constexpr int kTile = kTopkThreads * kTopkPerThread;
-    for (int t0 = 0; t0 < nk; t0 += kTile) {  // uniform per block
-      const int i0 = t0 + tid * kTopkPerThread;
-      u32x4 v[kTopkPerThread / 4];
-#pragma unroll
-      for (int j = 0; j < kTopkPerThread / 4; ++j) v[j] = s_keys[(i0 >> 2) + j];
-      uint32_t xg = 0, xe = 0;
-#pragma unroll
-      for (int j = 0; j < kTopkPerThread / 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool valid = i0 + 4 * j + e < nk;
-          xg += valid && v[j][e] > T;
-          xe += valid && v[j][e] == T;
-        }
-      uint32_t eg, ee, sg, se;
-      scan2(xg, xe, s_x, s_y, eg, ee, sg, se);
-      uint32_t pg = base_g + eg, pe = base_e + ee;
-#pragma unroll
-      for (int j = 0; j < kTopkPerThread / 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i0 + 4 * j + e;
-          if (i >= nk) continue;
-          const uint32_t kv = v[j][e];
-          if (kv > T) {
-            const uint32_t pos = pg + (pe < need ? pe : need);
-            if (pos < (uint32_t)a.k) out[pos] = (int32_t)(c0 + i);
-            ++pg;
-          } else if (kv == T) {
-            if (pe < need && pg + pe < (uint32_t)a.k) out[pg + pe] = (int32_t)(c0 + i);
-            ++pe;
-          }
-        }
-      base_g += sg;
-      base_e += se;
-    }
+    topk_fused_unit(L.a, L.w.list_all[gu - s_pref[j]], c, cmax, L.w.keys, L.w.h0, L.w.fsync, L.w.chist, limit,
+                    err);
   }
+  select_layers_done(plan, hdr, first, count, signal_value);
 }
 
 // ---------------------------------------------------------------- A3 top-k over token blocks
@@ -1282,6 +1478,37 @@ hipError_t launch_topk(const LayerArgs& a, Span sp, int64_t max_units, const uin
   for (int shift = 16; shift >= 0; shift -= 8)
     topk_pass_kernel<<<cg, kTopkThreads, 0, s>>>(a, sp, keys, w.h0, w.h1, w.tstate, w.chist, cmax, shift);
   topk_write_kernel<<<cg, kTopkThreads, 0, s>>>(a, sp, keys, w.tstate, w.chist, cmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_layers(const SelectPlanLayer* plan, SelectPlanHeader* hdr, int first, int count,
+                                const LayerArgs& a, int cmax, uint32_t wait_value, uint32_t signal_value,
+                                uint32_t limit, uint32_t* error_word, int num_cu, hipStream_t s) {
+  if (count < 1 || count > kMaxSelectBatch || a.dtype != CLO_BF16 || a.B * a.Hkv > kFusedReuseUnits ||
+      cmax > kFusedMaxBlocks)
+    return hipErrorInvalidValue;
+  const int64_t U = (int64_t)a.B * a.Hkv;
+  reuse_compact_layers_kernel<uint16_t><<<(unsigned)count, 1024, 0, s>>>(plan, hdr, first, wait_value, limit,
+                                                                         error_word);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = dispatch_group(a.G, [&](auto gc) {
+    constexpr int G = decltype(gc)::value;
+    const int64_t nch = (a.N + kScoreItem - 1) / kScoreItem;
+    const int grid = grid_cap(count * U * nch, (int64_t)num_cu * 2);
+    score_mfma_layers_kernel<G><<<grid, 256, 0, s>>>(plan, hdr, first, count, error_word);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
+  if (cmax < kTopkMultiMin) {
+    const int grid = grid_cap(count * U, 4096);
+    topk_unit_layers_kernel<<<grid, kUnitThreads, 0, s>>>(plan, hdr, first, count, signal_value);
+  } else {
+    const int64_t units = count * U;
+    const int64_t groups = units < kFusedMaxBlocks / cmax ? units : kFusedMaxBlocks / cmax;
+    topk_fused_layers_kernel<<<(unsigned)(groups * cmax), kTopkThreads, 0, s>>>(plan, hdr, first, count, cmax,
+                                                                               1u << 20, error_word, signal_value);
+  }
   return hipGetLastError();
 }
 

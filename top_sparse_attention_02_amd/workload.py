@@ -259,6 +259,15 @@ def load_layers(problem, log=None, threads: Optional[int] = None, host_flags: in
     return layers
 
 
+def batched_select_ok(layers) -> bool:
+    """Whether clo_select_layers takes these layers: bf16, at most 64 units per
+    layer, token top-k, at most 128 chunks of 16384 keys, one shape for all."""
+    b = layers[0]
+    same = all((x.B, x.Hq, x.Hkv, x.N, x.k) == (b.B, b.Hq, b.Hkv, b.N, b.k) for x in layers)
+    return (same and b.dtype == "bf16" and b.B * b.Hkv <= 64 and (b.shape.block_size or 1) <= 1
+            and -(-b.N // 16384) <= 128)
+
+
 class LayerLoop:
     """A multi-layer decode step on streams ordered only by device flags.
 
@@ -275,6 +284,10 @@ class LayerLoop:
             layer's tail straight into the next layer; gather="per-layer" uses
             one clo_gather_kv launch per layer instead;
     attend: waits for gat[l], attention of layer l, then flag att[l] = epoch.
+    With select="batched" the selections run as clo_select_layers calls over
+    consecutive layers (sizes `select_batches`: small first so that the gather
+    starts early, larger after), three launches per call instead of four per
+    layer; each layer still waits for its own att[l] and sets its own sel[l].
     The selection of layer l in the next step waits for att[l] of this step
     before overwriting layer l's selections.  Selection and gathering of layer
     l+1 therefore run while layer l is attended (one-layer-ahead prefetch and
@@ -283,9 +296,14 @@ class LayerLoop:
     only read-only inputs.
     """
 
-    def __init__(self, layers, spin_limit: int = 0, select_streams: int = 1, gather: str = "resident"):
+    def __init__(self, layers, spin_limit: int = 0, select_streams: int = 1, gather: str = "resident",
+                 select: str = "batched", select_batches=(1, 1, 2, 4, 8, 16, 16)):
         if gather not in ("resident", "per-layer"):
             raise ValueError(gather)
+        if select not in ("per-layer", "batched"):
+            raise ValueError(select)
+        if select == "batched" and not batched_select_ok(layers):
+            select = "per-layer"  # shapes the multi-layer selection does not take
         self.layers = layers
         L = len(layers)
         dev = layers[0].q.device
@@ -303,6 +321,32 @@ class LayerLoop:
             items = [(b.shape, b.layer(), b.reuse, b.ws, self._flag(0, l), self._flag(1, l))
                      for l, b in enumerate(layers)]
             self.plan_blocks = clo.clo_gather_plan(items, self.plan)
+        self.select = select
+        self.sel_plans = {}
+        if select == "batched":
+            # consecutive batches covering the layers: the given sizes, the last
+            # cut to fit or repeated until every layer is covered
+            sizes, left = [], L
+            for n in select_batches:
+                if left <= 0:
+                    break
+                sizes.append(min(int(n), left))
+                left -= sizes[-1]
+            while left > 0:
+                sizes.append(min(int(select_batches[-1]), left))
+                left -= sizes[-1]
+            self.batches = sizes
+            # one plan for steady steps (each layer's query and threshold) and one for
+            # cold steps (every unit misses: tau = +inf, q_prev as the query)
+            for cold in (False, True):
+                plan = torch.zeros(clo.clo_select_plan_size(L), dtype=torch.uint8, device=dev)
+                items = []
+                for l, b in enumerate(layers):
+                    shape = b.shape_with(math.inf if cold else b.tau)
+                    items.append((shape, b.layer(), b.q_prev if cold else b.q, b.q_prev, b.reuse, b.cos, b.ws,
+                                  self._flag(2, l), self._flag(0, l)))
+                clo.clo_select_plan(items, plan)
+                self.sel_plans[cold] = plan
 
     def _flag(self, kind: int, l: int):
         return self.flags[kind, l]
@@ -318,6 +362,13 @@ class LayerLoop:
         sp = self.spin_limit
         resident = self.gather == "resident"
         calls = []
+        if self.select == "batched":
+            # each layer waits for its att[l] of the previous step (flags start at 0)
+            plan, first = self.sel_plans[cold], 0
+            for n in self.batches:
+                clo.clo_select_layers(self.layers[0].shape, plan, first, n, e - 1, e, error_word=self.error,
+                                      spin_limit=sp, stream=self.s_selects[0])
+                first += n
         for l, b in enumerate(self.layers):
             tau = math.inf if cold else b.tau
             q = b.q_prev if cold else b.q
@@ -328,7 +379,8 @@ class LayerLoop:
                 sel_sync = clo.Sync(wait_flag=self._flag(2, l), wait_value=e - 1, error_word=self.error,
                                     spin_limit=sp, signal_flag=self._flag(0, l), signal_value=e)
             s_sel = self.s_selects[l % len(self.s_selects)]
-            clo.clo_reuse_select(shape, layer, q, b.q_prev, b.reuse, b.cos, b.ws, sync=sel_sync, stream=s_sel)
+            if self.select != "batched":
+                clo.clo_reuse_select(shape, layer, q, b.q_prev, b.reuse, b.cos, b.ws, sync=sel_sync, stream=s_sel)
             if not resident:
                 clo.clo_gather_kv(shape, layer, b.reuse, b.ws,
                                   sync=clo.Sync(wait_flag=self._flag(0, l), wait_value=e,
