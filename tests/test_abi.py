@@ -126,3 +126,12 @@ def test_update_reference_null_pointers_rejected():
         clo.clo_update_reference(shape(), None, None, None, stream=0)
     assert e.value.status == clo.CLO_E_ARG and "q is NULL" in str(e.value)
     clo.clo_update_reference(shape(batch=0), None, None, None, stream=0)
+
+
+def test_tau_heads_must_name_every_kv_head():
+    # the library reads exactly n_kv_heads thresholds; the binding refuses another length
+    with pytest.raises(ValueError):
+        shape(tau_heads=[0.8]).c()
+    with pytest.raises(ValueError):
+        shape(tau_heads=[0.8, 0.9, 0.7]).c()
+    assert clo.clo_workspace_size(shape(tau_heads=[0.8, 0.9])) > 0
