@@ -294,12 +294,12 @@ clo_status clo_gather_layers(const void* plan, int32_t n_layers, int32_t blocks,
                              uint32_t signal_value, uint32_t* error_word, uint32_t spin_limit, void* stream);
 
 /*
- * Selection of many layers in three launches -- for each layer what
+ * Selection of many layers in four launches -- for each layer what
  * clo_reuse_select does (A1 reuse test, then A2 scoring and A3 top-k of its
  * miss units), with the layers' launches merged: the reuse test and unit lists
  * of every layer in one launch (one block per layer, each after the layer's
- * own wait), the scoring of all the layers' miss units in one launch, and
- * their top-k in one more, whose last block then signals every layer.  For
+ * own wait), the scoring of all the layers' miss units in one launch, their
+ * top-k in one more, and a one-wave launch that signals every layer.  For
  * decode steps whose layers are small (a few sequences: each layer's own
  * scoring and top-k launches are short, their ramp-up, tail and launch gaps
  * cost more than their keys), with the selections running ahead of the

@@ -232,16 +232,15 @@ struct SelectPlanLayer {
 // Counters of a selection launch sequence, at the start of the plan.
 struct SelectPlanHeader {
   uint32_t score_counter;  // scoring work items taken
-  uint32_t topk_done;      // top-k blocks finished
   uint32_t n_layers;       // layers the plan holds (launches past them are refused on the GPU)
-  uint32_t pad[61];
+  uint32_t pad[62];
 };
 constexpr int kMaxSelectBatch = 64;  // layers per multi-layer selection
 // Blocks of a one-launch top-k, all resident at once (so chunks per unit at most).
 constexpr int kFusedMaxBlocks = 128;
 // Reuse test and unit lists (one block per layer, after the layer's wait),
-// scoring and top-k of plan layers first .. first + count - 1; the top-k's
-// last block stores signal_value to every layer's signal flag.
+// scoring and top-k of plan layers first .. first + count - 1, then a one-wave
+// launch storing signal_value to every layer's signal flag.
 hipError_t launch_select_layers(const SelectPlanLayer* plan, SelectPlanHeader* hdr, int first, int count,
                                 const LayerArgs& shape, int cmax, uint32_t wait_value, uint32_t signal_value,
                                 uint32_t limit, uint32_t* error_word, int num_cu, hipStream_t s);

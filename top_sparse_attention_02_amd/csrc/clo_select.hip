@@ -219,7 +219,7 @@ __global__ __launch_bounds__(1024) void reuse_compact_kernel(const T* __restrict
 }
 
 // The same for the layers of a multi-layer selection, one block per layer (each
-// after its own wait); block 0 also clears the launch sequence's counters.
+// after its own wait); block 0 also clears the scoring's work counter.
 template <typename T>
 __global__ __launch_bounds__(1024) void reuse_compact_layers_kernel(const SelectPlanLayer* __restrict__ plan,
                                                                     SelectPlanHeader* __restrict__ hdr, int first,
@@ -230,10 +230,7 @@ __global__ __launch_bounds__(1024) void reuse_compact_layers_kernel(const Select
     return;
   }
   const SelectPlanLayer& L = plan[first + (int)blockIdx.x];
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    hdr->score_counter = 0u;
-    hdr->topk_done = 0u;
-  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) hdr->score_counter = 0u;
   reuse_compact_body<T>(static_cast<const T*>(L.q), static_cast<const T*>(L.q_prev), L.reuse, L.cos, L.a.Hkv, L.a.Hq,
                         L.a.G, L.a.tau_h, L.a.B * L.a.Hkv, L.a.pmask, L.w.meta, L.w.list_all, L.w.list_host,
                         L.w.list_hit, L.w.h0, nullptr, L.wait_flag, wait_value, limit, error_word);
@@ -266,25 +263,19 @@ __device__ __forceinline__ int layer_of(const int32_t* pref, int gu) {
   return j;
 }
 
-// End of a multi-layer selection: each block releases its writes at agent scope
-// and counts itself done; the last one clears the count and stores
-// signal_value to every layer's signal flag (release).
-__device__ __forceinline__ void select_layers_done(const SelectPlanLayer* __restrict__ plan,
-                                                   SelectPlanHeader* __restrict__ hdr, int first, int count,
-                                                   uint32_t signal_value) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&hdr->topk_done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == gridDim.x - 1) {
-      __hip_atomic_store(&hdr->topk_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int held = (uint32_t)(first + count) <= hdr->n_layers ? count : 0;
-      for (int j = 0; j < held; ++j) {
-        uint32_t* f = plan[first + j].signal_flag;
-        if (f) __hip_atomic_store(f, signal_value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
+// End of a multi-layer selection: one wave stores signal_value to every layer's
+// signal flag (release).  It runs as a launch of its own after the top-k: the
+// kernel boundary makes the top-k's writes visible to every XCD with one L2
+// write-back, where an agent-scope release in each top-k block would write back
+// its XCD's whole L2 once per block (that made a 48-layer step 1.5-7% slower
+// when tried on the attention combine).
+__global__ __launch_bounds__(64) void signal_layers_kernel(const SelectPlanLayer* __restrict__ plan,
+                                                           const SelectPlanHeader* __restrict__ hdr, int first,
+                                                           int count, uint32_t signal_value) {
+  const int j = (int)threadIdx.x;
+  if (j >= count || (uint32_t)(first + count) > hdr->n_layers) return;
+  uint32_t* f = plan[first + j].signal_flag;
+  if (f) __hip_atomic_store(f, signal_value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- A2 scoring
@@ -961,10 +952,10 @@ __global__ __launch_bounds__(kUnitThreads) void topk_unit_kernel(LayerArgs a, Sp
 }
 
 // The single-block top-k of a multi-layer selection: the blocks take the miss
-// units of all the batch's layers; the last block to finish signals every layer.
+// units of all the batch's layers.
 __global__ __launch_bounds__(kUnitThreads) void topk_unit_layers_kernel(const SelectPlanLayer* __restrict__ plan,
-                                                                        SelectPlanHeader* __restrict__ hdr, int first,
-                                                                        int count, uint32_t signal_value) {
+                                                                        const SelectPlanHeader* __restrict__ hdr,
+                                                                        int first, int count) {
   __shared__ int32_t s_pref[kMaxSelectBatch + 1];
   load_miss_prefix(plan, hdr, first, count, s_pref);
   const int total = s_pref[count];
@@ -973,7 +964,6 @@ __global__ __launch_bounds__(kUnitThreads) void topk_unit_layers_kernel(const Se
     const SelectPlanLayer& L = plan[first + j];
     topk_unit_one(L.a, L.w.list_all[gu - s_pref[j]], L.w.keys, L.w.h0);
   }
-  select_layers_done(plan, hdr, first, count, signal_value);
 }
 
 // Block-wide exclusive scan of two counts (keys > T, keys == T) of each thread.
@@ -1305,13 +1295,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_fused_kernel(LayerArgs a, S
 }
 
 // The one-launch top-k of a multi-layer selection: the groups take the miss
-// units of all the batch's layers in turn; the last block to finish signals
-// every layer.
+// units of all the batch's layers in turn.
 __global__ __launch_bounds__(kTopkThreads) void topk_fused_layers_kernel(const SelectPlanLayer* __restrict__ plan,
-                                                                         SelectPlanHeader* __restrict__ hdr,
+                                                                         const SelectPlanHeader* __restrict__ hdr,
                                                                          int first, int count, int cmax,
-                                                                         uint32_t limit, uint32_t* err,
-                                                                         uint32_t signal_value) {
+                                                                         uint32_t limit, uint32_t* err) {
   __shared__ int32_t s_pref[kMaxSelectBatch + 1];
   load_miss_prefix(plan, hdr, first, count, s_pref);
   const int total = s_pref[count];
@@ -1327,7 +1315,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_fused_layers_kernel(const S
     topk_fused_unit(L.a, L.w.list_all[gu - s_pref[j]], c, cmax, L.w.keys, L.w.h0, L.w.fsync, L.w.chist, limit,
                     err);
   }
-  select_layers_done(plan, hdr, first, count, signal_value);
 }
 
 // ---------------------------------------------------------------- A3 top-k over token blocks
@@ -1502,13 +1489,15 @@ hipError_t launch_select_layers(const SelectPlanLayer* plan, SelectPlanHeader* h
   if (e != hipSuccess) return e;
   if (cmax < kTopkMultiMin) {
     const int grid = grid_cap(count * U, 4096);
-    topk_unit_layers_kernel<<<grid, kUnitThreads, 0, s>>>(plan, hdr, first, count, signal_value);
+    topk_unit_layers_kernel<<<grid, kUnitThreads, 0, s>>>(plan, hdr, first, count);
   } else {
     const int64_t units = count * U;
     const int64_t groups = units < kFusedMaxBlocks / cmax ? units : kFusedMaxBlocks / cmax;
     topk_fused_layers_kernel<<<(unsigned)(groups * cmax), kTopkThreads, 0, s>>>(plan, hdr, first, count, cmax,
-                                                                               1u << 20, error_word, signal_value);
+                                                                               1u << 20, error_word);
   }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  signal_layers_kernel<<<1, 64, 0, s>>>(plan, hdr, first, count, signal_value);
   return hipGetLastError();
 }
 

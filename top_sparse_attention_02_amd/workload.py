@@ -286,7 +286,7 @@ class LayerLoop:
     attend: waits for gat[l], attention of layer l, then flag att[l] = epoch.
     With select="batched" the selections run as clo_select_layers calls over
     consecutive layers (sizes `select_batches`: small first so that the gather
-    starts early, larger after), three launches per call instead of four per
+    starts early, larger after), four launches per call instead of four per
     layer; each layer still waits for its own att[l] and sets its own sel[l].
     The selection of layer l in the next step waits for att[l] of this step
     before overwriting layer l's selections.  Selection and gathering of layer
