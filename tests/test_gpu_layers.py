@@ -40,7 +40,9 @@ def test_layer_loop_matches_sequential_and_oracle(need_gpu, select_streams, gath
 
     p = enforce_all_layers(multi_layer_problem())
     layers = workload.load_layers(p)
-    loop = workload.LayerLoop(layers, select_streams=select_streams, gather=gather, select=select)
+    # three batches of selections over the 6 layers (the default sizing takes them in one)
+    loop = workload.LayerLoop(layers, select_streams=select_streams, gather=gather, select=select,
+                              select_batches=(1, 2, 3) if select == "batched" else None)
     log(f"[case layer loop, {select_streams} select streams, {gather} gather, {select} selection] cold step")
     loop.step(cold=True)
     torch.cuda.synchronize()

@@ -40,3 +40,14 @@ def test_plan_rejects_nan():
     with pytest.raises(clo.CloError) as e:
         clo.clo_plan_persistent(s, 3)
     assert e.value.status == clo.CLO_E_ARG and "NaN" in str(e.value)
+
+
+def test_default_selection_batches_cover_the_layers():
+    from top_sparse_attention_02_amd.workload import default_select_batches
+
+    assert default_select_batches(8, 48) == (3, 3, 6, 12, 24)   # B=1, 8 KV heads
+    assert default_select_batches(64, 48)[:6] == (1, 1, 2, 4, 8, 16)
+    for units in (1, 4, 8, 16, 64, 512):
+        for n in (1, 6, 48, 200):
+            sizes = default_select_batches(units, n)
+            assert sum(sizes) >= n and all(1 <= x <= 64 for x in sizes)

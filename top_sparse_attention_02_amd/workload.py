@@ -259,6 +259,21 @@ def load_layers(problem, log=None, threads: Optional[int] = None, host_flags: in
     return layers
 
 
+def default_select_batches(units: int, n_layers: int):
+    """Selection batch sizes of the 48-layer loop: a first batch of about 24
+    units (at least one layer), the same again, then doubling, at most 64 layers
+    per call.  Measured on MI355X (ms per 48-layer step): B=1, N=524288 (8 units
+    per layer) 17.89 with 3, 3, 6, 12, 24 against 18.09 with 1, 1, 2, 4, 8, 16, 16
+    (int4 rows: 8.10 against 8.15); B=8, N=262144 (64 units) 76.2 with 1, 1, 2, 4,
+    8, 16, 16 against 76.6 with 3, 3, 6, 12, 24."""
+    f = max(1, -(-24 // max(1, units)))
+    sizes, n = [f, f], f
+    while sum(sizes) < n_layers:
+        n = min(2 * n, 64)
+        sizes.append(n)
+    return tuple(sizes)
+
+
 def batched_select_ok(layers) -> bool:
     """Whether clo_select_layers takes these layers: bf16, at most 64 units per
     layer, token top-k, at most 128 chunks of 16384 keys, one shape for all."""
@@ -285,9 +300,10 @@ class LayerLoop:
             one clo_gather_kv launch per layer instead;
     attend: waits for gat[l], attention of layer l, then flag att[l] = epoch.
     With select="batched" the selections run as clo_select_layers calls over
-    consecutive layers (sizes `select_batches`: small first so that the gather
-    starts early, larger after), four launches per call instead of four per
-    layer; each layer still waits for its own att[l] and sets its own sel[l].
+    consecutive layers (sizes `select_batches`, by default
+    default_select_batches: small first so that the gather starts early, larger
+    after), four launches per call instead of four per layer; each layer still
+    waits for its own att[l] and sets its own sel[l].
     The selection of layer l in the next step waits for att[l] of this step
     before overwriting layer l's selections.  Selection and gathering of layer
     l+1 therefore run while layer l is attended (one-layer-ahead prefetch and
@@ -297,7 +313,7 @@ class LayerLoop:
     """
 
     def __init__(self, layers, spin_limit: int = 0, select_streams: int = 1, gather: str = "resident",
-                 select: str = "batched", select_batches=(1, 1, 2, 4, 8, 16, 16)):
+                 select: str = "batched", select_batches=None):
         if gather not in ("resident", "per-layer"):
             raise ValueError(gather)
         if select not in ("per-layer", "batched"):
@@ -324,6 +340,8 @@ class LayerLoop:
         self.select = select
         self.sel_plans = {}
         if select == "batched":
+            if select_batches is None:
+                select_batches = default_select_batches(layers[0].B * layers[0].Hkv, L)
             # consecutive batches covering the layers: the given sizes, the last
             # cut to fit or repeated until every layer is covered
             sizes, left = [], L
