@@ -363,17 +363,23 @@ clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const
  * buffers and semantics as the calls above; the reuse decisions never leave
  * the GPU.  cos may be NULL; reuse must not be NULL.
  *
- * When the layer has offloaded heads, the step overlaps its HBM work with the
- * host gather: units are split into ranges; `stream` scores and selects range
- * after range, two helper streams gather the even and the odd ranges, each
- * once its top-k is done, and a third attends the reuse units and then each
- * gathered range.  The helper streams (default priority, non-blocking) and
- * their events are
+ * When the layer has offloaded heads (and at least 16 units) and `stream` is
+ * not capturing a graph, the step overlaps its HBM work with the host gather
+ * (otherwise every kernel runs in order on `stream`): units are split into ranges;
+ * `stream` scores and selects range after range, helper streams read each
+ * range's host rows once its top-k is done (a gather launch per range on two
+ * streams in turn, or, from 256 units on, one resident gather launch for all
+ * ranges), and another helper stream attends the reuse units and then each
+ * gathered range.
+ * The helper streams (default priority, non-blocking) and their events are
  * created by the library on first use per device and kept until the process
- * ends; they hold no user data.  All ordering is done on the GPU with events;
- * the call is ordered after earlier work on `stream`, and later work on
- * `stream` is ordered after all of the step.  Concurrent calls on one device
- * share the helper streams (their work then runs one after another).
+ * ends; they hold no user data.  All ordering is done on the GPU, with events
+ * and with flags in the workspace that the consumers poll (bounded by
+ * sync->spin_limit, 0 = about a second; a time-out writes CLO_E_TIMEOUT to
+ * sync->error_word and the consumer goes on); the call is ordered after
+ * earlier work on `stream`, and later work on `stream` is ordered after all of
+ * the step.  Concurrent calls on one device share the helper streams (their
+ * work then runs one after another).
  */
 clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const void* q,
                            const void* q_prev, void* out, uint8_t* reuse, float* cos,

@@ -19,7 +19,8 @@ pytestmark = pytest.mark.gpu
     ("graph_f32_persistent", dict(batch=1, hq=32, hkv=8, context=4096, topk=410, dtype="f32", persistent=[1] * 8)),
     # bf16 with offloaded heads, 8 units: the step in order on one stream, gather included
     ("graph_bf16_mixed", dict(batch=2, hq=8, hkv=4, context=3000, topk=300, dtype="bf16", persistent=[1, 0, 0, 1])),
-    # 20 units: the overlapped step, helper streams joined by events
+    # 20 units, which run overlapped on helper streams when launched eagerly: under
+    # capture the step runs in order (the eager reference is the overlapped step)
     ("graph_bf16_overlapped", dict(batch=5, hq=8, hkv=4, context=3000, topk=300, dtype="bf16",
                                    persistent=[1, 0, 0, 1])),
 ])

@@ -48,6 +48,10 @@ CASES = {
     "bf16_g4_overlapped": dict(batch=5, hq=16, hkv=4, context=3001, topk=301, dtype="bf16",
                                persistent=[0, 1, 0, 0], heavy_frac=0.01),
     "f32_g2_overlapped": dict(batch=9, hq=4, hkv=2, context=2000, topk=200, dtype="f32", persistent=[0, 0]),
+    # 256 units: one resident gather launch for the 8 ranges, selected in groups of 1, 1, 2 and 4 ranges
+    "bf16_g4_resident": dict(batch=64, hq=16, hkv=4, context=2000, topk=200, dtype="bf16",
+                             persistent=[0, 1, 0, 0], heavy_frac=0.01),
+    "f32_g2_resident": dict(batch=130, hq=4, hkv=2, context=1500, topk=150, dtype="f32", persistent=[0, 0]),
 }
 
 
@@ -130,11 +134,11 @@ def test_ties_go_to_the_smaller_index(need_gpu, context):
         assert np.array_equal(got["idx"][0, h], ref["idx"])
 
 
-@pytest.mark.parametrize("batch", [2, 5])
+@pytest.mark.parametrize("batch", [2, 5, 64])
 def test_standalone_entry_points_equal_fused_step(need_gpu, batch):
     """clo_reuse_test + clo_topk_select + clo_gather_kv + clo_sparse_attn == clo_decode_step, bit for bit,
-    for a layer of 8 units (the step in order on one stream) and of 20 units (overlapped over unit
-    ranges on helper streams)."""
+    for a layer of 8 units (the step in order on one stream), of 20 units (overlapped over unit
+    ranges, a gather launch per range) and of 256 units (one resident gather launch)."""
     from top_sparse_attention_02_amd import clo, workload
 
     p = small_problem(f"split{batch}", batch=batch, hq=8, hkv=4, context=3000, topk=300, dtype="bf16",

@@ -92,6 +92,9 @@ CASES = {
     "bf16_g4_mixed": dict(batch=2, hq=8, hkv=2, context=3000, topk=300, dtype="bf16", persistent=[1, 0],
                           heavy_frac=0.005),
     "f32_g5_host": dict(batch=2, hq=10, hkv=2, context=2500, topk=250, dtype="f32", persistent=[0, 0]),
+    # 24 units: overlapped, a gather launch per range; 256 units: one resident gather launch
+    "bf16_g4_overlapped": dict(batch=6, hq=16, hkv=4, context=2000, topk=200, dtype="bf16", persistent=[0, 1, 0, 0]),
+    "bf16_g4_resident": dict(batch=64, hq=16, hkv=4, context=1200, topk=120, dtype="bf16", persistent=[0, 0, 1, 0]),
 }
 
 

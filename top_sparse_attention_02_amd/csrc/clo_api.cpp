@@ -268,10 +268,12 @@ uint32_t* score_counter(const Workspace& w, int r) { return reinterpret_cast<uin
 struct DeviceQueues {
   std::mutex mu;  // one decode step enqueues at a time per device
   bool ready = false;
-  hipStream_t gather = nullptr;   // host gathers of the even unit ranges
-  hipStream_t gather2 = nullptr;  // and of the odd ones
-  hipStream_t attend = nullptr;  // attention: reuse units first, then each range's misses
-  hipEvent_t ev_attn = nullptr;
+  hipStream_t gather = nullptr;   // the gathers of the even unit ranges, or the resident gather
+  hipStream_t gather2 = nullptr;  // the gathers of the odd unit ranges
+  hipStream_t attend = nullptr;   // attention: reuse units first, then each range's misses
+  hipEvent_t ev_lists = nullptr;     // unit lists and range flags ready (resident gather)
+  hipEvent_t ev_gathered = nullptr;  // the resident gather ended
+  hipEvent_t ev_attn = nullptr;      // the attention stream's work ended
   hipEvent_t ev_topk[kMaxRanges] = {}, ev_gather[kMaxRanges] = {};
 };
 
@@ -290,7 +292,8 @@ clo_status device_queues(DeviceQueues** out) {
     hipError_t e = hipStreamCreateWithFlags(&q.gather, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&q.gather2, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&q.attend, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&q.ev_attn, hipEventDisableTiming);
+    for (hipEvent_t* ev : {&q.ev_lists, &q.ev_gathered, &q.ev_attn})
+      if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
     for (int r = 0; r < kMaxRanges && e == hipSuccess; ++r) {
       e = hipEventCreateWithFlags(&q.ev_topk[r], hipEventDisableTiming);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&q.ev_gather[r], hipEventDisableTiming);
@@ -400,7 +403,7 @@ clo_status hip_status(hipError_t e, const char* what) {
 clo_status pre_wait(const clo_sync* sy, hipStream_t s, uint32_t* zero_word = nullptr) {
   if (!sy || !sy->wait_flag)
     return zero_word ? hip_status(launch_zero(zero_word, s), "counter reset launch") : CLO_OK;
-  const uint32_t limit = sy->spin_limit ? sy->spin_limit : (1u << 22);
+  const uint32_t limit = sy->spin_limit ? sy->spin_limit : kDefaultSpinLimit;
   return hip_status(launch_wait(sy->wait_flag, sy->wait_value, limit, sy->error_word, zero_word, s), "wait launch");
 }
 
@@ -487,7 +490,7 @@ clo_status clo_reuse_select(const clo_shape* shape, const clo_layer* layer, cons
   const int cu = num_cus();
   if (p.U <= kFusedReuseUnits) {
     const bool wait = sync && sync->wait_flag;
-    const uint32_t limit = wait && sync->spin_limit ? sync->spin_limit : (1u << 22);
+    const uint32_t limit = wait && sync->spin_limit ? sync->spin_limit : kDefaultSpinLimit;
     if ((st = hip_status(launch_reuse_compact(p.a, q, q_prev, reuse, cos, w, wait ? sync->wait_flag : nullptr,
                                               wait ? sync->wait_value : 0u, limit,
                                               wait ? sync->error_word : nullptr, s),
@@ -526,7 +529,7 @@ clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const u
     // one launch: the gather's blocks wait for the flag themselves, and the last
     // one to finish signals; the work counters are zero (every call on the
     // workspace leaves them so, and every selection call sets them)
-    const GatherSync gs{sync->wait_flag, sync->wait_value, sync->spin_limit ? sync->spin_limit : (1u << 22),
+    const GatherSync gs{sync->wait_flag, sync->wait_value, sync->spin_limit ? sync->spin_limit : kDefaultSpinLimit,
                         sync->error_word, sync->signal_flag, sync->signal_value, done};
     return hip_status(launch_gather(p.a, reuse, kAllUnits, p.U, blocks, counter, s, &gs), "gather launch");
   }
@@ -602,7 +605,7 @@ clo_status clo_gather_layers(const void* plan, int32_t n_layers, int32_t blocks,
   if ((st = check_device(plan, need, "plan"))) return st;
   if ((st = check_flag_ptr(error_word, "error_word"))) return st;
   return hip_status(launch_gather_layers(static_cast<const GatherPlanLayer*>(plan), n_layers, blocks, wait_value,
-                                         signal_value, spin_limit ? spin_limit : (1u << 22), error_word,
+                                         signal_value, spin_limit ? spin_limit : kDefaultSpinLimit, error_word,
                                          static_cast<hipStream_t>(stream)),
                     "gather launch");
 }
@@ -698,7 +701,7 @@ clo_status clo_select_layers(const clo_shape* shape, const void* plan, int32_t f
   auto* entries = reinterpret_cast<const SelectPlanLayer*>(static_cast<const char*>(plan) + sizeof(SelectPlanHeader));
   const int cmax = (int)((p.a.N + kTopkChunk - 1) / kTopkChunk);
   return hip_status(launch_select_layers(entries, hdr, first, count, p.a, cmax, wait_value, signal_value,
-                                         spin_limit ? spin_limit : (1u << 22), error_word, num_cus(),
+                                         spin_limit ? spin_limit : kDefaultSpinLimit, error_word, num_cus(),
                                          static_cast<hipStream_t>(stream)),
                     "selection launch");
 }
@@ -731,8 +734,9 @@ namespace {
 // Decode step with every kernel in order on the caller's stream: layers without
 // offloaded heads (nothing to overlap), layers of fewer than kOverlapUnits units
 // (a range per unit would leave most ranges empty and make the call's ~70
-// launches and stream waits cost more host time than the overlap saves), and
-// clo_decode_step_static, which creates no helper streams.  The gather of
+// launches and stream waits cost more host time than the overlap saves), steps
+// enqueued under graph capture, and clo_decode_step_static, which creates no
+// helper streams.  The gather of
 // offloaded heads follows the top-k.
 clo_status step_in_order(const Plan& p, const Workspace& w, const void* q, const void* q_prev, void* out,
                          uint8_t* reuse, float* cos, hipStream_t s) {
@@ -761,46 +765,68 @@ clo_status step_in_order(const Plan& p, const Workspace& w, const void* q, const
   return hip_status(launch_attn_combine(p.a, w.part, out, kAllUnits, p.U, s), "attention combine launch");
 }
 
-// Decode step with offloaded heads.  Units are split into R ranges.  The
-// caller's stream scores and selects range after range; the gather stream
-// starts each range's host reads as soon as its top-k is done; the attention
-// stream first attends the reuse units (which need nothing new) and then each
-// range's miss units once their rows have arrived, combining the chunk
-// partials range by range so that only the last range's remain at the end.  Events order the streams
-// on the GPU; the host never waits.  The caller's stream finally waits for the
-// attention stream, so the call is ordered like a single-stream call.
-clo_status step_overlapped(const Plan& p, const Workspace& w, const void* q, const void* q_prev, void* out,
-                           uint8_t* reuse, float* cos, hipStream_t s) {
-  DeviceQueues* dq = nullptr;
-  clo_status st;
-  if ((st = device_queues(&dq))) return st;
-  std::lock_guard<std::mutex> lk(dq->mu);
-  const int cu = num_cus();
-  // Up to 8 ranges of equal unit counts.  Measured at B=64, N=131072 (102 miss
-  // units): ranges growing from 1/64 of the units (so that the first gather
-  // starts sooner) and a small last range lost 0.7% against equal ranges: the
-  // larger middle ranges are selected beside the gather, whose host reads
-  // slow the selection's latency-bound top-k kernels several times over
-  const int R = (int)(p.U < 8 ? p.U : 8);
-  RangeBounds rb{};
-  for (int r = 0; r <= R; ++r) rb.first[r] = (int32_t)(p.U * r / R);
-  int64_t per = 1;  // the most units in one range: sizes the per-range grids
-  for (int r = 0; r < R; ++r) per = std::max<int64_t>(per, rb.first[r + 1] - rb.first[r]);
-  hipStream_t gs = dq->gather, as = dq->attend;
+// Decode step with offloaded heads, overlapped on the helper streams.  Units
+// are split into R ranges of equal unit counts; the caller's stream scores and
+// selects them in order, the gather reads each range's host rows once its
+// top-k is done, and the attention stream first attends the reuse units (which
+// need nothing new) and then each range's miss units once their rows have
+// arrived, combining the chunk partials range by range so that only the last
+// range's remain at the end.  Everything is ordered on the GPU (events and
+// device flags); the host never waits.  The caller's stream finally waits for
+// the helper streams, so the call is ordered like a single-stream call.
+//
+// Two schedules of the gather.  Layers of fewer than kResidentGatherUnits
+// units launch a gather per range, on two gather streams in turn (so that one
+// range's host reads start while the previous range's last items finish
+// instead of after a launch gap), each behind an event after the range's
+// top-k, and attention waits on events.  Larger layers keep one gather launch
+// resident for the whole step: it reads range after range, each once the
+// range's flag is up, and raises a flag per gathered range that attention
+// waits for; their ranges are selected in groups of 1, 1, 2, 4 ranges, since
+// beside the host reads every launch takes several times its time alone.
+// Steps/s measured side by side on one box, streams / resident:
+//   B=64, N=131072 (512 units)  native 80.9-81.1 / 81.8-81.9, int4 rows
+//                               224-225 / 227-230, int4 16-token blocks 257 / 263-266
+//   B=16, N=32768 (128 units)   native 330.6-332.4 / 328.7-330.4, int4 rows
+//                               839-849 / 797-801
+// (Up to 8 ranges.  At B=64, N=131072, ranges growing from 1/64 of the units so
+// that the first gather starts sooner, and a small last range, lost 0.7%
+// against equal ranges: the larger middle ranges are selected beside the
+// gather, whose host reads slow the selection's latency-bound top-k kernels
+// several times over.)
+struct Ranges {
+  int R;
+  RangeBounds rb;
+  int64_t per;  // the most units in one range: sizes the per-range grids
+};
+
+Ranges split_ranges(const Plan& p) {
+  Ranges x{};
+  x.R = (int)(p.U < 8 ? p.U : 8);
+  for (int r = 0; r <= x.R; ++r) x.rb.first[r] = (int32_t)(p.U * r / x.R);
+  x.per = 1;
+  for (int r = 0; r < x.R; ++r) x.per = std::max<int64_t>(x.per, x.rb.first[r + 1] - x.rb.first[r]);
+  return x;
+}
+
 #define CLO_TRY(expr, what) \
   if ((st = hip_status((expr), (what)))) return st
+
+clo_status step_overlapped_streams(const Plan& p, const Workspace& w, const void* q, const void* q_prev, void* out,
+                                   uint8_t* reuse, float* cos, DeviceQueues* dq, hipStream_t s) {
+  clo_status st;
+  const int cu = num_cus();
+  const Ranges x = split_ranges(p);
+  hipStream_t as = dq->attend;
   CLO_TRY(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch");
-  CLO_TRY(launch_compact(p.a, reuse, w, R, rb, s), "compact launch");
-  for (int r = 0; r < R; ++r) {
-    CLO_TRY(launch_score(p.a, q, span_range(w, r), per, w, score_counter(w, r), cu, s), "score launch");
-    CLO_TRY(launch_select(p.a, span_range(w, r), per, w, s), "top-k launch");
+  CLO_TRY(launch_compact(p.a, reuse, w, x.R, x.rb, s), "compact launch");
+  for (int r = 0; r < x.R; ++r) {
+    CLO_TRY(launch_score(p.a, q, span_range(w, r), x.per, w, score_counter(w, r), cu, s), "score launch");
+    CLO_TRY(launch_select(p.a, span_range(w, r), x.per, w, s), "top-k launch");
     CLO_TRY(hipEventRecord(dq->ev_topk[r], s), "event record");
-    // ranges alternate between two gather streams, so that one range's host
-    // reads start while the previous range's last items finish instead of
-    // after a launch gap (~12 us each)
-    hipStream_t gsr = (r & 1) ? dq->gather2 : gs;
+    hipStream_t gsr = (r & 1) ? dq->gather2 : dq->gather;
     CLO_TRY(hipStreamWaitEvent(gsr, dq->ev_topk[r], 0), "stream wait");
-    CLO_TRY(launch_gather(p.a, reuse, span_host_range(w, r), per, kGatherBlocksOverlapped,
+    CLO_TRY(launch_gather(p.a, reuse, span_host_range(w, r), x.per, kGatherBlocksOverlapped,
                           reinterpret_cast<uint32_t*>(w.meta + kMetaGather + r), gsr),
             "gather launch");
     CLO_TRY(hipEventRecord(dq->ev_gather[r], gsr), "event record");
@@ -810,15 +836,69 @@ clo_status step_overlapped(const Plan& p, const Workspace& w, const void* q, con
   CLO_TRY(hipStreamWaitEvent(as, dq->ev_topk[0], 0), "stream wait");
   CLO_TRY(launch_attn_partial(p.a, q, w.part, span_hits(w), p.U, as), "attention launch");
   CLO_TRY(launch_attn_combine(p.a, w.part, out, span_hits(w), p.U, as), "attention combine launch");
-  for (int r = 0; r < R; ++r) {
+  for (int r = 0; r < x.R; ++r) {
     CLO_TRY(hipStreamWaitEvent(as, dq->ev_gather[r], 0), "stream wait");
-    CLO_TRY(launch_attn_partial(p.a, q, w.part, span_range(w, r), per, as), "attention launch");
-    CLO_TRY(launch_attn_combine(p.a, w.part, out, span_range(w, r), per, as), "attention combine launch");
+    CLO_TRY(launch_attn_partial(p.a, q, w.part, span_range(w, r), x.per, as), "attention launch");
+    CLO_TRY(launch_attn_combine(p.a, w.part, out, span_range(w, r), x.per, as), "attention combine launch");
   }
   CLO_TRY(hipEventRecord(dq->ev_attn, as), "event record");
   CLO_TRY(hipStreamWaitEvent(s, dq->ev_attn, 0), "stream wait");
-#undef CLO_TRY
   return ok();
+}
+
+clo_status step_overlapped_resident(const Plan& p, const Workspace& w, const void* q, const void* q_prev,
+                                    void* out, uint8_t* reuse, float* cos, uint32_t limit, DeviceQueues* dq,
+                                    hipStream_t s) {
+  clo_status st;
+  const int cu = num_cus();
+  const Ranges x = split_ranges(p);
+  hipStream_t gs = dq->gather, as = dq->attend;
+  uint32_t* meta = reinterpret_cast<uint32_t*>(w.meta);
+  CLO_TRY(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch");
+  // the unit lists; the range flags, counters and done counts at zero
+  CLO_TRY(launch_compact(p.a, reuse, w, x.R, x.rb, s), "compact launch");
+  CLO_TRY(hipEventRecord(dq->ev_lists, s), "event record");
+  // groups of 1, 1, 2, 4, ... ranges
+  for (int r0 = 0, n = 1, g = 0; r0 < x.R; r0 += n, n = g >= 1 ? 2 * n : n, ++g) {
+    n = std::min(n, x.R - r0);
+    const Span sp{w.list_all, w.meta + kMetaOffAll + r0, w.meta + kMetaOffAll + r0 + n};
+    CLO_TRY(launch_score(p.a, q, sp, x.per * n, w, score_counter(w, g), cu, s), "score launch");
+    CLO_TRY(launch_select(p.a, sp, x.per * n, w, s), "top-k launch");
+    // the kernel boundary makes the ranges' indices visible to the gather
+    CLO_TRY(launch_signal(meta + kMetaSelFlag + r0, 1u, s, n), "signal launch");
+    if (r0 == 0) {
+      CLO_TRY(hipEventRecord(dq->ev_topk[0], s), "event record");
+      // enqueued once the first group's selection is, so that a failed launch
+      // above leaves no gather waiting for it
+      CLO_TRY(hipStreamWaitEvent(gs, dq->ev_lists, 0), "stream wait");
+      CLO_TRY(launch_gather_ranges(p.a, w, x.R, kGatherBlocksRanges, limit, gs), "gather launch");
+      CLO_TRY(hipEventRecord(dq->ev_gathered, gs), "event record");
+    }
+  }
+  CLO_TRY(hipStreamWaitEvent(as, dq->ev_topk[0], 0), "stream wait");
+  CLO_TRY(launch_attn_partial(p.a, q, w.part, span_hits(w), p.U, as), "attention launch");
+  CLO_TRY(launch_attn_combine(p.a, w.part, out, span_hits(w), p.U, as), "attention combine launch");
+  for (int r = 0; r < x.R; ++r) {
+    CLO_TRY(launch_wait(meta + kMetaGatherFlag + r, 1u, limit, p.a.err, nullptr, as), "wait launch");
+    CLO_TRY(launch_attn_partial(p.a, q, w.part, span_range(w, r), x.per, as), "attention launch");
+    CLO_TRY(launch_attn_combine(p.a, w.part, out, span_range(w, r), x.per, as), "attention combine launch");
+  }
+  CLO_TRY(hipEventRecord(dq->ev_attn, as), "event record");
+  CLO_TRY(hipStreamWaitEvent(s, dq->ev_attn, 0), "stream wait");
+  CLO_TRY(hipStreamWaitEvent(s, dq->ev_gathered, 0), "stream wait");
+  return ok();
+}
+
+#undef CLO_TRY
+
+clo_status step_overlapped(const Plan& p, const Workspace& w, const void* q, const void* q_prev, void* out,
+                           uint8_t* reuse, float* cos, uint32_t limit, hipStream_t s) {
+  DeviceQueues* dq = nullptr;
+  clo_status st;
+  if ((st = device_queues(&dq))) return st;
+  std::lock_guard<std::mutex> lk(dq->mu);
+  return p.U >= kResidentGatherUnits ? step_overlapped_resident(p, w, q, q_prev, out, reuse, cos, limit, dq, s)
+                                     : step_overlapped_streams(p, w, q, q_prev, out, reuse, cos, dq, s);
 }
 
 }  // namespace
@@ -845,8 +925,19 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
   if (cos && (st = check_device(cos, (size_t)p.U * 4, "cos"))) return st;
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
   if ((st = pre_wait(sync, s))) return st;
-  st = p.a.H > 0 && p.U >= kOverlapUnits ? step_overlapped(p, w, q, q_prev, out, reuse, cos, s)
-                                         : step_in_order(p, w, q, q_prev, out, reuse, cos, s);
+  // Under stream capture the step runs in order on `stream`: a graph may run
+  // independent branches one after another, and the overlapped step's gather
+  // and attention poll flags that kernels on another branch raise.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    cap = hipStreamCaptureStatusActive;
+  }
+  // the bound of the overlapped step's own waits (its streams' hand-offs)
+  const uint32_t limit = sync && sync->spin_limit ? sync->spin_limit : kDefaultSpinLimit;
+  st = p.a.H > 0 && p.U >= kOverlapUnits && cap == hipStreamCaptureStatusNone
+           ? step_overlapped(p, w, q, q_prev, out, reuse, cos, limit, s)
+           : step_in_order(p, w, q, q_prev, out, reuse, cos, s);
   if (st) return st;
   return post_signal(sync, s);
 }

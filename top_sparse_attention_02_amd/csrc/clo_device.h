@@ -8,6 +8,7 @@
 
 #include <type_traits>
 
+#include "../../include/clo.h"
 #include "clo_internal.h"
 
 namespace clo {
@@ -70,6 +71,27 @@ __device__ __forceinline__ void wait_vm_acks() { __builtin_amdgcn_s_waitcnt(0x0F
 // Wait until this wave's LDS operations have completed: s_waitcnt lgkmcnt(0),
 // vmcnt and expcnt left at their maxima (63 and 7).
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Bounded wait of one thread until *flag >= value: at most limit polls with a
+// short sleep between them; on time-out CLO_E_TIMEOUT goes to *error_word (when
+// not NULL) and the wait ends.  The polls are relaxed device-scope loads (read
+// where the writes of every XCD meet); one acquire fence follows the last, so
+// that what the flag's writer released before raising it is visible to the
+// caller's later reads.  An acquire load per poll would add a cache
+// invalidation to every poll of a wait that can last milliseconds beside other
+// kernels.
+__device__ __forceinline__ void poll_flag(const uint32_t* flag, uint32_t value, uint32_t limit,
+                                          uint32_t* error_word) {
+  uint32_t n = 0;
+  while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < value) {
+    if (++n >= limit) {
+      if (error_word) __hip_atomic_store(error_word, (uint32_t)CLO_E_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
 
 // Sum over the 16 lanes of a row group; the xor butterfly leaves the same
 // bits in every lane of the group.

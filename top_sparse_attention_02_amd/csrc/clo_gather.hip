@@ -42,20 +42,10 @@ __device__ __forceinline__ int list_gather_units(const LayerArgs& a, const uint8
 }
 
 // The standalone gather's own wait: thread 0 of every block polls the flag
-// (acquire, agent scope, bounded as wait_kernel), the block waits at a barrier.
+// (bounded, acquire once it is up), the block waits at a barrier.
 __device__ __forceinline__ void gather_wait(const GatherSync& gs) {
   if (!gs.wait_flag) return;
-  if (threadIdx.x == 0) {
-    uint32_t n = 0;
-    while (__hip_atomic_load(gs.wait_flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gs.wait_value) {
-      if (++n >= gs.limit) {
-        if (gs.error_word)
-          __hip_atomic_store(gs.error_word, (uint32_t)CLO_E_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(8);
-    }
-  }
+  if (threadIdx.x == 0) poll_flag(gs.wait_flag, gs.wait_value, gs.limit, gs.error_word);
   __syncthreads();
 }
 
@@ -312,7 +302,52 @@ __global__ __launch_bounds__(256) void gather_layers_kernel(const GatherPlanLaye
   }
 }
 
+// The host gathers of one decode step's unit ranges in one resident launch
+// (BITS = 0: native rows).  Range by range the blocks wait until the range's
+// top-k is done, take the range's items from its work counter and count
+// themselves done; the last block of a range publishes it for attention.  A
+// block that runs out of a range's items goes straight on to the next range,
+// so that no launch gap or tail of one range leaves the host link idle.
+template <typename T, int BITS>
+__global__ __launch_bounds__(256) void gather_ranges_kernel(LayerArgs a, int32_t* __restrict__ meta,
+                                                            const int32_t* __restrict__ list_host, int R,
+                                                            uint32_t limit) {
+  uint32_t* m = reinterpret_cast<uint32_t*>(meta);
+  for (int r = 0; r < R; ++r) {
+    const GatherSync gs{m + kMetaSelFlag + r, 1u, limit, a.err, m + kMetaGatherFlag + r, 1u, m + kMetaRangeDone + r};
+    gather_wait(gs);
+    const Span sp{list_host, meta + kMetaOffHost + r, meta + kMetaOffHost + r + 1};
+    if constexpr (BITS == 0)
+      gather_native_rows<T>(a, nullptr, sp, m + kMetaGather + r, a.err);
+    else
+      gather_quant_rows<T, BITS>(a, nullptr, sp, m + kMetaGather + r, a.err);
+    gather_finish(gs, m + kMetaGather + r);
+    __syncthreads();  // the next range reuses the block's LDS
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gather_ranges(const LayerArgs& a, const Workspace& w, int ranges, int blocks, uint32_t limit,
+                                hipStream_t s) {
+  const bool f32 = a.dtype == CLO_F32;
+  if (a.host_fmt == CLO_HOST_INT8) {
+    if (f32)
+      gather_ranges_kernel<float, 8><<<blocks, 256, 0, s>>>(a, w.meta, w.list_host, ranges, limit);
+    else
+      gather_ranges_kernel<uint16_t, 8><<<blocks, 256, 0, s>>>(a, w.meta, w.list_host, ranges, limit);
+  } else if (a.host_fmt == CLO_HOST_INT4) {
+    if (f32)
+      gather_ranges_kernel<float, 4><<<blocks, 256, 0, s>>>(a, w.meta, w.list_host, ranges, limit);
+    else
+      gather_ranges_kernel<uint16_t, 4><<<blocks, 256, 0, s>>>(a, w.meta, w.list_host, ranges, limit);
+  } else if (f32) {
+    gather_ranges_kernel<float, 0><<<blocks, 256, 0, s>>>(a, w.meta, w.list_host, ranges, limit);
+  } else {
+    gather_ranges_kernel<uint16_t, 0><<<blocks, 256, 0, s>>>(a, w.meta, w.list_host, ranges, limit);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_gather(const LayerArgs& a, const uint8_t* reuse, Span sp, int64_t max_units, int max_blocks,
                          uint32_t* counter, hipStream_t s, const GatherSync* gsp) {

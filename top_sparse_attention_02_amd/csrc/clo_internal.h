@@ -48,6 +48,7 @@ constexpr int kPartStride = kHeadDim + 2;  // floats per (chunk, head) partial: 
 // host read, and its rows carry half the host bytes.
 constexpr int kGatherUnroll = 2;
 constexpr int kGatherBlocksOverlapped = 20;  // per gather stream
+constexpr int kGatherBlocksRanges = 40;      // the resident range gather of clo_decode_step
 constexpr int kGatherBlocksAlone = 24;
 constexpr int kGatherBlocksAloneWide = 40;  // layers of at least kGatherWideUnits units
 constexpr int kGatherWideUnits = 64;
@@ -91,7 +92,12 @@ constexpr int kFusedReuseUnits = 64;
 // helper streams for layers of at least this many units, and runs smaller
 // layers in order on the caller's stream
 constexpr int kOverlapUnits = 16;
+// ... and from this many units on, with one resident gather launch for all the
+// ranges instead of a gather launch per range
+constexpr int kResidentGatherUnits = 256;
 constexpr int kMaxRanges = 16;
+// polls of a device-side wait when the caller gives no bound (about a second)
+constexpr uint32_t kDefaultSpinLimit = 1u << 22;
 struct RangeBounds {
   int32_t first[kMaxRanges + 1];  // first unit of each range; first[R] = U
 };
@@ -106,7 +112,11 @@ constexpr int kMetaOffHost = 40;   // [R + 1] first position of each range in li
 constexpr int kMetaGather = 64;    // [kMaxRanges] work counters of the range gathers
 constexpr int kMetaScore = 80;     // [kMaxRanges] work counters of the range scorings
 constexpr int kMetaGatherDone = 96;  // blocks of the standalone gather that have finished
-constexpr int kMetaInts = 128;
+// clo_decode_step's resident range gather (cleared by the compact kernel):
+constexpr int kMetaSelFlag = 128;     // [kMaxRanges] 1 once the range's top-k is done
+constexpr int kMetaGatherFlag = 144;  // [kMaxRanges] 1 once the range's host rows are in the cache
+constexpr int kMetaRangeDone = 160;   // [kMaxRanges] blocks done with the range
+constexpr int kMetaInts = 192;
 
 // Multi-block top-k: each unit's keys are split into chunks of kTopkChunk keys,
 // one 256-thread block per chunk.
@@ -215,6 +225,13 @@ struct GatherPlanLayer {
   uint32_t* signal_flag;       // set to signal_value once the layer's rows are in its cache
   uint32_t zero_words[2];      // counter and done of a layer with nothing to gather
 };
+// The host gathers of a decode step's R unit ranges in one resident launch of
+// `blocks` blocks: range by range every block waits (bounded by limit; a
+// time-out is written to a.err) until meta[kMetaSelFlag + r] is 1, takes the
+// range's items of list_host from meta[kMetaGather + r], and the last block
+// done with the range sets meta[kMetaGatherFlag + r] to 1 (release).
+hipError_t launch_gather_ranges(const LayerArgs& a, const Workspace& w, int ranges, int blocks, uint32_t limit,
+                                hipStream_t s);
 hipError_t launch_gather_layers(const GatherPlanLayer* plan, int n_layers, int blocks, uint32_t wait_value,
                                 uint32_t signal_value, uint32_t limit, uint32_t* error_word, hipStream_t s);
 // One layer of a multi-layer selection plan (device memory, written by the host):
@@ -259,6 +276,7 @@ hipError_t launch_quantize_rows(const void* src, int64_t n_rows, int32_t dtype, 
                                 int64_t stride, int8_t* dst_exp, hipStream_t s);
 hipError_t launch_wait(const uint32_t* flag, uint32_t value, uint32_t spin_limit, uint32_t* error_word,
                        uint32_t* zero_word, hipStream_t s);
-hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s);
+// flag[0 .. n) = value (release, agent scope), n <= 64
+hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s, int n = 1);
 
 }  // namespace clo

@@ -182,20 +182,15 @@ __global__ __launch_bounds__(64) void update_reference_kernel(const T* __restric
 __global__ __launch_bounds__(64) void wait_kernel(const uint32_t* flag, uint32_t value, uint32_t limit,
                                                   uint32_t* error_word, uint32_t* zero_word) {
   if (threadIdx.x != 0) return;
-  uint32_t n = 0;
-  while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < value) {
-    if (++n >= limit) {
-      if (error_word) __hip_atomic_store(error_word, (uint32_t)CLO_E_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(8);
-  }
+  poll_flag(flag, value, limit, error_word);
   if (zero_word) *zero_word = 0u;
 }
 
-__global__ __launch_bounds__(64) void signal_kernel(uint32_t* flag, uint32_t value) {
-  if (threadIdx.x == 0) __hip_atomic_store(flag, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+// flag[0 .. n) = value (release), one lane per flag (n <= 64)
+__global__ __launch_bounds__(64) void signal_kernel(uint32_t* flag, uint32_t value, int n) {
+  if ((int)threadIdx.x < n) __hip_atomic_store(flag + threadIdx.x, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
+
 
 // ---------------------------------------------------------------- measurement
 // Streaming read of n16 16-byte words: the HBM read ceiling that the scoring
@@ -288,8 +283,8 @@ hipError_t launch_wait(const uint32_t* flag, uint32_t value, uint32_t spin_limit
   return hipGetLastError();
 }
 
-hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s) {
-  signal_kernel<<<1, 64, 0, s>>>(flag, value);
+hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s, int n) {
+  signal_kernel<<<1, 64, 0, s>>>(flag, value, n);
   return hipGetLastError();
 }
 

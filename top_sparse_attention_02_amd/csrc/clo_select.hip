@@ -126,6 +126,9 @@ __device__ void compact_units(MissF is_miss, int U, int Hkv, uint64_t pmask, int
   if (tid < kMaxRanges) {
     meta[kMetaGather + tid] = 0;
     meta[kMetaScore + tid] = 0;
+    meta[kMetaSelFlag + tid] = 0;
+    meta[kMetaGatherFlag + tid] = 0;
+    meta[kMetaRangeDone + tid] = 0;
   }
   if (tid == 0) meta[kMetaGatherDone] = 0;
   if (tid == 0) {
@@ -174,17 +177,7 @@ __device__ __forceinline__ void reuse_compact_body(const T* __restrict__ q, cons
                                                    uint32_t* error_word) {
   __shared__ uint8_t s_reuse[kFusedReuseUnits];
   static_assert(kFusedReuseUnits <= 1024, "one unit per thread in the compaction");
-  if (wait_flag && threadIdx.x == 0) {
-    uint32_t n = 0;
-    while (__hip_atomic_load(wait_flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < wait_value) {
-      if (++n >= limit) {
-        if (error_word)
-          __hip_atomic_store(error_word, (uint32_t)CLO_E_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(8);
-    }
-  }
+  if (wait_flag && threadIdx.x == 0) poll_flag(wait_flag, wait_value, limit, error_word);
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int u = wave; u < U; u += 16) {

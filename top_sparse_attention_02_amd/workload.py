@@ -155,9 +155,9 @@ def capture_step(step) -> "torch.cuda.CUDAGraph":
     """Capture one call of `step` (a function that enqueues a whole decode step on
     the current stream, e.g. LayerBuffers.step1) into a HIP graph; replay() then
     launches all of its kernels at once.  The library records no memset or copy,
-    synchronizes nothing and orders its helper streams with events, so the step
-    captures whole; validation runs on the host at capture time only, and the
-    buffers must stay where they were when captured."""
+    synchronizes nothing and, under capture, runs the step in order on the
+    capturing stream, so the step captures whole; validation runs on the host at
+    capture time only, and the buffers must stay where they were when captured."""
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
