@@ -71,6 +71,11 @@ def parse():
                          "instead of the 48-layer loop: one layer's latency and phases, and a launch sequence "
                          "that rocprofv3 --pmc can run one kernel at a time (the loop's kernels wait on flags "
                          "that kernels on other streams set, which a serialized run cannot satisfy)")
+    ap.add_argument("--counters", action="store_true",
+                    help="for runs under rocprofv3 --pmc, which runs one kernel at a time: decode steps run in "
+                         "order on one stream (CLO_STEP_IN_ORDER=1), since the overlapped step's gather and "
+                         "attention wait for flags that kernels queued behind them raise; the 48-layer loop "
+                         "is refused (use --layer)")
     ap.add_argument("--sync-probe", action="store_true",
                     help="measure the cross-stream hand-off instead of a decode step: HIP events, the command "
                          "processor's stream memory operations (hipStreamWaitValue32) and the library's device "
@@ -702,6 +707,12 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
               f"multi-GPU exchange: units shard by sequence or KV head, one process per GPU).", file=sys.stderr)
         sys.exit(2)
+    if args.counters:
+        if args.config in (4, 5) and args.layer is None:
+            print("--counters: the 48-layer loop's streams wait on each other's flags; pass --layer L",
+                  file=sys.stderr)
+            sys.exit(2)
+        os.environ["CLO_STEP_IN_ORDER"] = "1"  # read by the library at its first decode step
     import torch
 
     import gen
@@ -933,6 +944,7 @@ def main():
                    "context": p.context, "topk": p.topk, "tau": p.tau, "step": args.step,
                    "data_layers": p.data_layers or p.layers, "host_memory": args.host_memory,
                    **({"graph": True} if args.graph else {}),
+                   **({"step_schedule": "in order on one stream (--counters)"} if args.counters else {}),
                    **({"select_streams": args.select_streams, "select": loop.select} if multi else {})},
         "host_bound_ms": bounds["host_bound_ms"],
         "frac_of_host_bound": round(host_bound_ms / ms_per_step, 4) if host_bound_ms else None,

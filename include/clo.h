@@ -363,9 +363,11 @@ clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const
  * buffers and semantics as the calls above; the reuse decisions never leave
  * the GPU.  cos may be NULL; reuse must not be NULL.
  *
- * When the layer has offloaded heads (and at least 16 units) and `stream` is
- * not capturing a graph, the step overlaps its HBM work with the host gather
- * (otherwise every kernel runs in order on `stream`): units are split into ranges;
+ * When the layer has offloaded heads (and at least 16 units), `stream` is not
+ * capturing a graph and the environment variable CLO_STEP_IN_ORDER is not "1"
+ * (set it for tools that run one kernel at a time, such as hardware counter
+ * collection), the step overlaps its HBM work with the host gather (otherwise
+ * every kernel runs in order on `stream`): units are split into ranges;
  * `stream` scores and selects range after range, helper streams read each
  * range's host rows once its top-k is done (a gather launch per range on two
  * streams in turn, or, from 256 units on, one resident gather launch for all

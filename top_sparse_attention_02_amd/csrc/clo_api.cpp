@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cstdlib>
 #include <mutex>
 
 #include "../../include/clo.h"
@@ -891,6 +892,19 @@ clo_status step_overlapped_resident(const Plan& p, const Workspace& w, const voi
 
 #undef CLO_TRY
 
+// CLO_STEP_IN_ORDER=1 in the environment runs every decode step in order on the
+// caller's stream, as under graph capture: for tools that run one kernel at a
+// time (hardware counter collection), under which the overlapped step's
+// gather and attention would wait for flags that kernels queued behind them
+// raise, until their bounds.
+bool step_in_order_forced() {
+  static const bool forced = [] {
+    const char* e = std::getenv("CLO_STEP_IN_ORDER");
+    return e != nullptr && e[0] == '1';
+  }();
+  return forced;
+}
+
 clo_status step_overlapped(const Plan& p, const Workspace& w, const void* q, const void* q_prev, void* out,
                            uint8_t* reuse, float* cos, uint32_t limit, hipStream_t s) {
   DeviceQueues* dq = nullptr;
@@ -935,7 +949,7 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
   }
   // the bound of the overlapped step's own waits (its streams' hand-offs)
   const uint32_t limit = sync && sync->spin_limit ? sync->spin_limit : kDefaultSpinLimit;
-  st = p.a.H > 0 && p.U >= kOverlapUnits && cap == hipStreamCaptureStatusNone
+  st = p.a.H > 0 && p.U >= kOverlapUnits && cap == hipStreamCaptureStatusNone && !step_in_order_forced()
            ? step_overlapped(p, w, q, q_prev, out, reuse, cos, limit, s)
            : step_in_order(p, w, q, q_prev, out, reuse, cos, s);
   if (st) return st;
