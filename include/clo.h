@@ -376,9 +376,10 @@ clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const
  * The helper streams (default priority, non-blocking) and their events are
  * created by the library on first use per device and kept until the process
  * ends; they hold no user data.  All ordering is done on the GPU, with events
- * and with flags in the workspace that the consumers poll (bounded by
- * sync->spin_limit, 0 = about a second; a time-out writes CLO_E_TIMEOUT to
- * sync->error_word and the consumer goes on); the call is ordered after
+ * and with flags in the workspace that the consumers poll (bounded at about a
+ * second whatever sync->spin_limit says, which bounds the caller's own wait
+ * only; a time-out writes CLO_E_TIMEOUT to sync->error_word and the consumer
+ * goes on); the call is ordered after
  * earlier work on `stream`, and later work on `stream` is ordered after all of
  * the step.  Concurrent calls on one device share the helper streams (their
  * work then runs one after another).

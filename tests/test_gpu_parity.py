@@ -161,6 +161,33 @@ def test_standalone_entry_points_equal_fused_step(need_gpu, batch):
         assert np.array_equal(fused[key], split[key]), key
 
 
+@pytest.mark.parametrize("batch", [5, 64])
+def test_caller_spin_limit_bounds_only_the_callers_wait(need_gpu, batch):
+    """A tiny sync.spin_limit on a flag that is already up bounds the caller's own wait
+    only: the overlapped step's internal waits (the resident gather's and the attention
+    stream's, 256 units) keep the library's bound, so the step reports no time-out and
+    equals the step without sync bit for bit."""
+    import torch
+
+    from top_sparse_attention_02_amd import clo, workload
+
+    p = small_problem(f"spin{batch}", batch=batch, hq=16, hkv=4, context=1500, topk=150, dtype="bf16",
+                      persistent=[0, 1, 0, 0])
+    bufs = workload.load_layer(p, 0)
+    bufs.step0()
+    bufs.step1()
+    ref = snapshot(bufs)
+    flag = torch.ones(1, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bufs.step0()
+    bufs.decode_step(bufs.q, bufs.q_prev, bufs.tau,
+                     sync=clo.Sync(wait_flag=flag[0], wait_value=1, error_word=err, spin_limit=1))
+    got = snapshot(bufs)
+    assert int(err.item()) == 0
+    for key in ref:
+        assert np.array_equal(ref[key], got[key]), key
+
+
 @pytest.mark.parametrize("name,kw", [
     # config-1 shape: 8 units, 2 attention chunks
     ("inorder_f32", dict(batch=1, hq=32, hkv=8, context=4096, topk=410, dtype="f32", persistent=[1] * 8)),

@@ -947,10 +947,11 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
     (void)hipGetLastError();
     cap = hipStreamCaptureStatusActive;
   }
-  // the bound of the overlapped step's own waits (its streams' hand-offs)
-  const uint32_t limit = sync && sync->spin_limit ? sync->spin_limit : kDefaultSpinLimit;
+  // The overlapped step's own waits (its streams' hand-offs) are bounded by the
+  // library's default, not by sync->spin_limit: a bound the caller chose for its
+  // own flag could end them before the kernels they wait for have run.
   st = p.a.H > 0 && p.U >= kOverlapUnits && cap == hipStreamCaptureStatusNone && !step_in_order_forced()
-           ? step_overlapped(p, w, q, q_prev, out, reuse, cos, limit, s)
+           ? step_overlapped(p, w, q, q_prev, out, reuse, cos, kDefaultSpinLimit, s)
            : step_in_order(p, w, q, q_prev, out, reuse, cos, s);
   if (st) return st;
   return post_signal(sync, s);
