@@ -83,6 +83,11 @@ def parse():
     ap.add_argument("--select", choices=["batched", "per-layer"], default="batched",
                     help="48-layer loop: selections in multi-layer batches (clo_select_layers) or one "
                          "clo_reuse_select per layer")
+    ap.add_argument("--attend", choices=["batched", "per-layer"], default="batched",
+                    help="48-layer loop: attention in multi-layer batches (clo_attend_layers) or one "
+                         "clo_sparse_attn per layer")
+    ap.add_argument("--attend-batches", default="", metavar="N,N,...",
+                    help="48-layer loop: attention batch sizes (default: workload.default_attend_batches)")
     ap.add_argument("--select-streams", type=int, default=1, metavar="S",
                     help="48-layer loop: streams the layers' selections alternate between")
     ap.add_argument("--graph", action="store_true",
@@ -806,7 +811,9 @@ def main():
         for bufs in layers:
             bufs.set_block_size(args.block_size)
     if multi:
-        loop = workload.LayerLoop(layers, select_streams=args.select_streams, select=args.select)
+        att_batches = tuple(int(x) for x in args.attend_batches.split(",")) if args.attend_batches else None
+        loop = workload.LayerLoop(layers, select_streams=args.select_streams, select=args.select,
+                                  attend=args.attend, attend_batches=att_batches)
         loop.step(cold=True)
         step = (lambda: loop.step()) if args.step == 1 else (lambda: loop.step(cold=True))
     else:
@@ -945,7 +952,9 @@ def main():
                    "data_layers": p.data_layers or p.layers, "host_memory": args.host_memory,
                    **({"graph": True} if args.graph else {}),
                    **({"step_schedule": "in order on one stream (--counters)"} if args.counters else {}),
-                   **({"select_streams": args.select_streams, "select": loop.select} if multi else {})},
+                   **({"select_streams": args.select_streams, "select": loop.select, "attend": loop.attend,
+                       **({"attend_batches": list(loop.att_batches)} if loop.attend == "batched" else {})}
+                      if multi else {})},
         "host_bound_ms": bounds["host_bound_ms"],
         "frac_of_host_bound": round(host_bound_ms / ms_per_step, 4) if host_bound_ms else None,
         "bounds": bounds,

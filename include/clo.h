@@ -358,6 +358,52 @@ clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const
                            void* ws, size_t ws_bytes, const clo_sync* sync, void* stream);
 
 /*
+ * A5 over many layers -- the attention of a batch of layers in four launches
+ * instead of four per layer (clo_sparse_attn with a wait and a signal), for a
+ * layer loop whose attention stream follows a gather layer by layer (synthesis
+ * section 5.6 prefetch; abstract feature (3), GPU-centric synchronization):
+ * beside the host reads of a running gather every launch takes several times
+ * its work alone.
+ *
+ * clo_attend_plan writes, into `plan` (device, clo_attend_plan_size bytes),
+ * what the launches need for each layer: its shape, buffers (k_cache, v_cache,
+ * k_hbm, v_hbm, idx and persistent_mask of `layer`), query, output, workspace
+ * (whose chunk partials it uses) and flags.  All layers of a plan must have the
+ * same batch, heads, top-k and dtype.  A plan stays valid while those buffers
+ * stay where they were; it is written once, with hipMemcpy (the call
+ * synchronizes).
+ *
+ * clo_attend_layers enqueues on `stream` the attention of plan layers first ..
+ * first + count - 1 (count <= 64): a wait until every layer's *wait_flag >=
+ * wait_value (bounded by spin_limit polls, 0 = about a second; a time-out
+ * writes CLO_E_TIMEOUT to error_word and the attention goes on), the outputs
+ * of every unit of every layer, bit for bit those of clo_sparse_attn on each
+ * layer, and then signal_value stored to each layer's signal_flag (release,
+ * agent scope).  `shape` is the shape the plan's layers share; a layer that
+ * does not match it is skipped and CLO_E_ARG written to error_word, as is a
+ * call reaching past the plan's layers (which then does nothing).  Selected
+ * indices out of range on persistent heads are reported as CLO_E_INDEX in
+ * error_word, as by clo_sparse_attn.  Calls whose layers share a workspace
+ * must not overlap.
+ */
+typedef struct {
+  const clo_shape* shape;
+  const clo_layer* layer;
+  const void* q;               /* [B, Hq, d] device: the query the layer attends with */
+  void* out;                   /* [B, Hq, d] device */
+  void* ws;                    /* the layer's workspace */
+  size_t ws_bytes;
+  const uint32_t* wait_flag;   /* device, may be NULL */
+  uint32_t* signal_flag;       /* device, may be NULL */
+} clo_attend_layer;
+
+size_t clo_attend_plan_size(int32_t n_layers);
+clo_status clo_attend_plan(const clo_attend_layer* layers, int32_t n_layers, void* plan, size_t plan_bytes);
+clo_status clo_attend_layers(const clo_shape* shape, const void* plan, int32_t first, int32_t count,
+                             uint32_t wait_value, uint32_t signal_value, uint32_t* error_word, uint32_t spin_limit,
+                             void* stream);
+
+/*
  * A1..A5 -- one whole decode step of one layer: reuse test, then scoring,
  * top-k and gather for the miss units, then attention for all units.  Same
  * buffers and semantics as the calls above; the reuse decisions never leave

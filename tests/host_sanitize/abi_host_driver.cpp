@@ -131,6 +131,23 @@ int main() {
       clo_shape longer = shape(1, 8, 2, 128, 128 * 16384 + 1, 209716, 0.8f, CLO_BF16);  // 129 chunks
       CHECK(clo_select_layers(&longer, nullptr, 0, 4, 0, 1, nullptr, 0, nullptr) == CLO_E_UNSUPPORTED);
     }
+    // the multi-layer attention plan
+    CHECK(clo_attend_plan_size(0) == 0 && clo_attend_plan_size(4097) == 0);
+    CHECK(clo_attend_plan_size(48) >= 48 * 64 && clo_attend_plan_size(48) % 256 == 0);
+    CHECK(clo_attend_plan(nullptr, 4, nullptr, 1 << 20) == CLO_E_ARG);
+    {
+      clo_attend_layer al;
+      std::memset(&al, 0, sizeof al);
+      CHECK(clo_attend_plan(&al, 0, nullptr, 1 << 20) == CLO_E_ARG);
+      CHECK(clo_attend_plan(&al, 1, nullptr, 16) == CLO_E_ARG);  // plan smaller than clo_attend_plan_size(1)
+      clo_shape ok_shape = shape(1, 8, 2, 128, 524288, 52429, 0.8f, CLO_BF16);
+      CHECK(clo_attend_layers(&ok_shape, nullptr, 0, 0, 0, 1, nullptr, 0, nullptr) == CLO_E_ARG);
+      CHECK(clo_attend_layers(&ok_shape, nullptr, 0, 65, 0, 1, nullptr, 0, nullptr) == CLO_E_ARG);
+      CHECK(clo_attend_layers(&ok_shape, nullptr, -1, 4, 0, 1, nullptr, 0, nullptr) == CLO_E_ARG);
+      CHECK(clo_attend_layers(&ok_shape, nullptr, 4093, 4, 0, 1, nullptr, 0, nullptr) == CLO_E_ARG);
+      clo_shape empty = shape(0, 8, 2, 128, 524288, 52429, 0.8f, CLO_BF16);
+      CHECK(clo_attend_layers(&empty, nullptr, 0, 4, 0, 1, nullptr, 0, nullptr) == CLO_E_ARG);
+    }
   }
 
   // the last-error buffer at every length, including 0 and 1

@@ -30,20 +30,26 @@ def enforce_all_layers(p):
     raise RuntimeError("margins did not settle")
 
 
-@pytest.mark.parametrize("select_streams,gather,select", [(1, "resident", "per-layer"), (2, "resident", "per-layer"),
-                                                          (3, "resident", "per-layer"), (1, "per-layer", "per-layer"),
-                                                          (1, "resident", "batched"), (1, "per-layer", "batched")])
-def test_layer_loop_matches_sequential_and_oracle(need_gpu, select_streams, gather, select):
+@pytest.mark.parametrize("select_streams,gather,select,attend", [
+    (1, "resident", "per-layer", "per-layer"), (2, "resident", "per-layer", "per-layer"),
+    (3, "resident", "per-layer", "batched"), (1, "per-layer", "per-layer", "per-layer"),
+    (1, "resident", "batched", "per-layer"), (1, "per-layer", "batched", "per-layer"),
+    (1, "resident", "batched", "batched")])
+def test_layer_loop_matches_sequential_and_oracle(need_gpu, select_streams, gather, select, attend):
     import torch
 
     from top_sparse_attention_02_amd import workload
 
     p = enforce_all_layers(multi_layer_problem())
     layers = workload.load_layers(p)
-    # three batches of selections over the 6 layers (the default sizing takes them in one)
+    # three batches of selections over the 6 layers (the default sizing takes them in one),
+    # attention in batches of 3, 2 and 1 layers
     loop = workload.LayerLoop(layers, select_streams=select_streams, gather=gather, select=select,
-                              select_batches=(1, 2, 3) if select == "batched" else None)
-    log(f"[case layer loop, {select_streams} select streams, {gather} gather, {select} selection] cold step")
+                              select_batches=(1, 2, 3) if select == "batched" else None, attend=attend,
+                              attend_batches=(3, 2, 1))
+    assert loop.attend == (attend if gather == "resident" else "per-layer")
+    log(f"[case layer loop, {select_streams} select streams, {gather} gather, {select} selection, "
+        f"{attend} attention] cold step")
     loop.step(cold=True)
     torch.cuda.synchronize()
     loop.check()

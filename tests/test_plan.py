@@ -51,3 +51,15 @@ def test_default_selection_batches_cover_the_layers():
         for n in (1, 6, 48, 200):
             sizes = default_select_batches(units, n)
             assert sum(sizes) >= n and all(1 <= x <= 64 for x in sizes)
+
+
+def test_default_attend_batches_cover_the_layers():
+    """The loop's attention batches: 8 layers each, the last layers 4, 2, 1 and 1;
+    every size within 1..64 (the multi-layer attention's limit) and, once cut to
+    the layer count, covering every layer exactly once."""
+    from top_sparse_attention_02_amd.workload import _cover, default_attend_batches
+
+    assert default_attend_batches(48) == (8, 8, 8, 8, 8, 4, 2, 1, 1)
+    for n in (1, 2, 3, 6, 8, 9, 48, 200):
+        sizes = _cover(default_attend_batches(n), n)
+        assert sum(sizes) == n and all(1 <= x <= 64 for x in sizes), (n, sizes)

@@ -21,7 +21,8 @@ CLO_OK, CLO_E_ARG, CLO_E_UNSUPPORTED, CLO_E_WORKSPACE, CLO_E_HIP, CLO_E_TIMEOUT,
 EXPORTS = ("clo_workspace_size", "clo_reuse_test", "clo_topk_select", "clo_reuse_select", "clo_gather_kv",
            "clo_sparse_attn", "clo_decode_step", "clo_decode_step_static", "clo_append_kv", "clo_update_reference", "clo_plan_persistent", "clo_quantize_rows",
            "clo_stream_read", "clo_status_string", "clo_last_error", "clo_gather_plan_size", "clo_gather_plan",
-           "clo_gather_layers", "clo_select_plan_size", "clo_select_plan", "clo_select_layers")
+           "clo_gather_layers", "clo_select_plan_size", "clo_select_plan", "clo_select_layers",
+           "clo_attend_plan_size", "clo_attend_plan", "clo_attend_layers")
 
 
 class CloError(RuntimeError):
@@ -61,6 +62,12 @@ class clo_select_layer(ctypes.Structure):
                 ("q_prev", ctypes.c_void_p), ("reuse", ctypes.c_void_p), ("cos", ctypes.c_void_p),
                 ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("wait_flag", ctypes.c_void_p),
                 ("signal_flag", ctypes.c_void_p)]
+
+
+class clo_attend_layer(ctypes.Structure):
+    _fields_ = [("shape", ctypes.POINTER(clo_shape)), ("layer", ctypes.POINTER(clo_layer)), ("q", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+                ("wait_flag", ctypes.c_void_p), ("signal_flag", ctypes.c_void_p)]
 
 
 _lib = None
@@ -112,6 +119,13 @@ def load():
         L.clo_select_plan.argtypes = [P(clo_select_layer), ctypes.c_int32, vp, sz]
         L.clo_select_layers.restype = st
         L.clo_select_layers.argtypes = [P(clo_shape), vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
+                                        ctypes.c_uint32, vp, ctypes.c_uint32, vp]
+        L.clo_attend_plan_size.restype = sz
+        L.clo_attend_plan_size.argtypes = [ctypes.c_int32]
+        L.clo_attend_plan.restype = st
+        L.clo_attend_plan.argtypes = [P(clo_attend_layer), ctypes.c_int32, vp, sz]
+        L.clo_attend_layers.restype = st
+        L.clo_attend_layers.argtypes = [P(clo_shape), vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
                                         ctypes.c_uint32, vp, ctypes.c_uint32, vp]
         L.clo_gather_layers.restype = st
         L.clo_gather_layers.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint32, vp,
@@ -344,6 +358,31 @@ def clo_select_layers(shape: Shape, plan, first: int, count: int, wait_value: in
     _check(load().clo_select_layers(ctypes.byref(shape.c()), ptr(plan), int(first), int(count), int(wait_value),
                                     int(signal_value), ptr(error_word), int(spin_limit), stream_handle(stream)),
            "clo_select_layers")
+
+
+def clo_attend_plan_size(n_layers: int) -> int:
+    return int(load().clo_attend_plan_size(int(n_layers)))
+
+
+def clo_attend_plan(items, plan, plan_bytes: Optional[int] = None):
+    """items: (shape, layer, q, out, ws, wait_flag, signal_flag) per layer.
+    Writes the plan (device memory)."""
+    n = len(items)
+    arr = (clo_attend_layer * max(n, 1))()
+    keep = []
+    for i, (shape, layer, q, out, ws, wait_flag, signal_flag) in enumerate(items):
+        cs, cl = shape.c(), layer.c()
+        keep += [cs, cl]
+        arr[i] = clo_attend_layer(ctypes.pointer(cs), ctypes.pointer(cl), ptr(q), ptr(out), ptr(ws), nbytes(ws),
+                                  ptr(wait_flag), ptr(signal_flag))
+    _check(load().clo_attend_plan(arr, n, ptr(plan), nbytes(plan, plan_bytes)), "clo_attend_plan")
+
+
+def clo_attend_layers(shape: Shape, plan, first: int, count: int, wait_value: int, signal_value: int,
+                      error_word=None, spin_limit: int = 0, stream=None):
+    _check(load().clo_attend_layers(ctypes.byref(shape.c()), ptr(plan), int(first), int(count), int(wait_value),
+                                    int(signal_value), ptr(error_word), int(spin_limit), stream_handle(stream)),
+           "clo_attend_layers")
 
 
 def clo_append_kv(shape: Shape, layer: Layer, k_new, v_new, position: int, sync: Optional[Sync] = None,

@@ -707,6 +707,80 @@ clo_status clo_select_layers(const clo_shape* shape, const void* plan, int32_t f
                     "selection launch");
 }
 
+size_t clo_attend_plan_size(int32_t n_layers) {
+  if (n_layers < 1 || n_layers > 4096) return 0;
+  return (size_t)round_up((int64_t)sizeof(AttendPlanHeader) + (int64_t)n_layers * (int64_t)sizeof(AttendPlanLayer),
+                          256);
+}
+
+clo_status clo_attend_plan(const clo_attend_layer* layers, int32_t n_layers, void* plan, size_t plan_bytes) {
+  if (!layers) return fail(CLO_E_ARG, "layers is NULL");
+  const size_t need = clo_attend_plan_size(n_layers);
+  if (!need) return fail(CLO_E_ARG, "n_layers %d outside 1..4096", n_layers);
+  if (plan_bytes < need) return fail(CLO_E_ARG, "plan has %zu bytes, %zu needed", plan_bytes, need);
+  clo_status st;
+  if ((st = check_device(plan, need, "plan"))) return st;
+  std::vector<AttendPlanLayer> host((size_t)n_layers);
+  Plan p0;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const clo_attend_layer& g = layers[l];
+    Plan p;
+    if ((st = make_plan(g.shape, g.layer ? g.layer->persistent_mask : 0, &p))) return st;
+    if (p.U < 1) return fail(CLO_E_ARG, "layer %d has no units", l);
+    if (l == 0) {
+      p0 = p;
+    } else if (p.a.B != p0.a.B || p.a.Hq != p0.a.Hq || p.a.Hkv != p0.a.Hkv || p.a.k != p0.a.k ||
+               p.a.dtype != p0.a.dtype) {
+      return fail(CLO_E_ARG, "layer %d: batch, heads, top-k and dtype must equal layer 0's", l);
+    }
+    if ((st = check_flag_ptr(g.wait_flag, "wait_flag")) || (st = check_flag_ptr(g.signal_flag, "signal_flag")))
+      return st;
+    if ((st = check_layer(g.layer, &p, NEED_IDX | NEED_CACHE | NEED_HBM_KV))) return st;
+    if ((st = check_device(g.q, q_bytes(p), "q"))) return st;
+    if ((st = check_device(g.out, q_bytes(p), "out"))) return st;
+    Workspace w;
+    if ((st = bind_ws(p, g.ws, g.ws_bytes, &w))) return st;
+    AttendPlanLayer& d = host[(size_t)l];
+    memset(&d, 0, sizeof d);
+    d.a = p.a;
+    d.a.err = nullptr;
+    d.q = g.q;
+    d.part = w.part;
+    d.out = g.out;
+    d.wait_flag = g.wait_flag;
+    d.signal_flag = g.signal_flag;
+  }
+  AttendPlanHeader hdr;
+  memset(&hdr, 0, sizeof hdr);
+  hdr.n_layers = (uint32_t)n_layers;
+  hipError_t e = hipMemcpy(plan, &hdr, sizeof hdr, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(static_cast<char*>(plan) + sizeof(AttendPlanHeader), host.data(),
+                  host.size() * sizeof(AttendPlanLayer), hipMemcpyHostToDevice);
+  return hip_status(e, "writing the attention plan");
+}
+
+clo_status clo_attend_layers(const clo_shape* shape, const void* plan, int32_t first, int32_t count,
+                             uint32_t wait_value, uint32_t signal_value, uint32_t* error_word, uint32_t spin_limit,
+                             void* stream) {
+  Plan p;
+  clo_status st;
+  if ((st = make_plan(shape, 0, &p))) return st;
+  if (p.U < 1) return fail(CLO_E_ARG, "shape has no units");
+  if (count < 1 || count > kMaxAttendBatch) return fail(CLO_E_ARG, "count %d outside 1..%d", count, kMaxAttendBatch);
+  if (first < 0 || first > 4096 - count) return fail(CLO_E_ARG, "first %d outside the plan's 4096 layers", first);
+  const size_t need = clo_attend_plan_size(first + count);
+  if ((st = check_device(plan, need, "plan"))) return st;
+  if ((st = check_flag_ptr(error_word, "error_word"))) return st;
+  const auto* hdr = static_cast<const AttendPlanHeader*>(plan);
+  const auto* entries =
+      reinterpret_cast<const AttendPlanLayer*>(static_cast<const char*>(plan) + sizeof(AttendPlanHeader));
+  return hip_status(launch_attend_layers(entries, hdr, first, count, p.a, wait_value, signal_value,
+                                         spin_limit ? spin_limit : kDefaultSpinLimit, error_word,
+                                         static_cast<hipStream_t>(stream)),
+                    "attention launch");
+}
+
 clo_status clo_sparse_attn(const clo_shape* shape, const clo_layer* layer, const void* q, void* out, void* ws,
                            size_t ws_bytes, const clo_sync* sync, void* stream) {
   Plan p;

@@ -52,21 +52,14 @@ struct Row8<float> {
   }
 };
 
+// The partial of unit u's chunk c, by one 256-thread block (an index out of
+// range is reported in *err).
 template <typename T, int G>
-__global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T* __restrict__ q,
-                                                           float* __restrict__ part, int nch, Span sp) {
+__device__ __forceinline__ void attn_partial_item(const LayerArgs& a, const T* __restrict__ q,
+                                                  float* __restrict__ part, int nch, int u, int c, uint32_t* err) {
   __shared__ float lg[G][kAttnChunk];
   __shared__ float red[4][G][kHeadDim];
   __shared__ float sm[G], sl[G];
-  int u;
-  if (sp.list) {
-    const int lo = *sp.lo;
-    if ((int64_t)blockIdx.x >= (int64_t)(*sp.hi - lo) * nch) return;  // whole block
-    u = sp.list[lo + blockIdx.x / nch];
-  } else {
-    u = blockIdx.x / nch;
-  }
-  const int c = blockIdx.x % nch;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const bool pers = (a.pmask >> h) & 1ull;
   const int64_t r0 = (int64_t)c * kAttnChunk;
@@ -84,7 +77,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
     vbase = static_cast<const T*>(a.v_cache) + s;
   }
   // row of the source tensor holding selected row i (< nrows) of this chunk
-  auto row_of = [&](int i) -> int64_t { return pers ? checked_row(ix[i], a.N, a.err) : (int64_t)i; };
+  auto row_of = [&](int i) -> int64_t { return pers ? checked_row(ix[i], a.N, err) : (int64_t)i; };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane & 15, rg = lane >> 4;
   const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
@@ -250,6 +243,20 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
   }
 }
 
+template <typename T, int G>
+__global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T* __restrict__ q,
+                                                           float* __restrict__ part, int nch, Span sp) {
+  int u;
+  if (sp.list) {
+    const int lo = *sp.lo;
+    if ((int64_t)blockIdx.x >= (int64_t)(*sp.hi - lo) * nch) return;  // whole block
+    u = sp.list[lo + blockIdx.x / nch];
+  } else {
+    u = blockIdx.x / nch;
+  }
+  attn_partial_item<T, G>(a, q, part, nch, u, (int)(blockIdx.x % nch), a.err);
+}
+
 // Merge the chunk partials of one (unit, head) with the usual max/sum
 // rescaling.  S groups of 128 threads (one per output column) each merge a
 // contiguous run of the chunks, kAttnBatch chunks' partials loaded before any is
@@ -257,17 +264,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(LayerArgs a, const T*
 // (many chunks, few units) take S up to 8, so that no single thread walks
 // hundreds of chunks one load latency after another.
 template <typename T, int S>
-__global__ __launch_bounds__(128 * S) void attn_combine_kernel(LayerArgs a, const float* __restrict__ part, int nch,
-                                                               Span sp, T* __restrict__ out) {
+__device__ __forceinline__ void attn_combine_item(const LayerArgs& a, const float* __restrict__ part, int nch,
+                                                  T* __restrict__ out, int u, int g) {
   __shared__ float sM[S], sL[S], sO[S][kHeadDim];
   const int G = a.G;
-  const int i = blockIdx.x / G, g = blockIdx.x % G;
-  int u = i;
-  if (sp.list) {
-    const int lo = *sp.lo;
-    if (i >= *sp.hi - lo) return;  // uniform per block
-    u = sp.list[lo + i];
-  }
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int grp = threadIdx.x / kHeadDim, col = threadIdx.x % kHeadDim;
   const int per = (nch + S - 1) / S;
@@ -319,6 +319,83 @@ __global__ __launch_bounds__(128 * S) void attn_combine_kernel(LayerArgs a, cons
   store_out(out + ((int64_t)b * a.Hq + (int64_t)h * G + g) * kHeadDim + col, Ot / Lt);
 }
 
+template <typename T, int S>
+__global__ __launch_bounds__(128 * S) void attn_combine_kernel(LayerArgs a, const float* __restrict__ part, int nch,
+                                                               Span sp, T* __restrict__ out) {
+  const int i = blockIdx.x / a.G, g = blockIdx.x % a.G;
+  int u = i;
+  if (sp.list) {
+    const int lo = *sp.lo;
+    if (i >= *sp.hi - lo) return;  // uniform per block
+    u = sp.list[lo + i];
+  }
+  attn_combine_item<T, S>(a, part, nch, out, u, g);
+}
+
+// ---------------------------------------------------------------- many layers
+// The attention of plan layers first .. first + count - 1 (every unit of each)
+// in four launches: a one-wave wait for every layer's rows (lane j polls layer
+// j's flag), the partials of all the layers' (unit, chunk) items, their
+// combines, and a one-wave launch storing the signal value to every layer's
+// flag.  The per-item bodies are the single-layer kernels'.  A launch past the
+// plan's layers, or a layer whose shape is not the launch's, is reported
+// (CLO_E_ARG) and does nothing.
+__device__ __forceinline__ bool attend_layer_ok(const AttendPlanLayer& L, const AttendPlanHeader* hdr, int first,
+                                                int count, const LayerArgs& shape, uint32_t* err) {
+  const bool ok = (uint32_t)(first + count) <= hdr->n_layers && L.a.B == shape.B && L.a.Hq == shape.Hq &&
+                  L.a.Hkv == shape.Hkv && L.a.k == shape.k && L.a.dtype == shape.dtype;
+  if (!ok && threadIdx.x == 0 && err) atomicCAS(err, 0u, (uint32_t)CLO_E_ARG);
+  return ok;
+}
+
+__global__ __launch_bounds__(64) void attend_wait_layers_kernel(const AttendPlanLayer* __restrict__ plan,
+                                                                const AttendPlanHeader* __restrict__ hdr, int first,
+                                                                int count, uint32_t wait_value, uint32_t limit,
+                                                                uint32_t* err) {
+  const int j = (int)threadIdx.x;
+  if (j >= count || (uint32_t)(first + count) > hdr->n_layers) return;
+  const uint32_t* f = plan[first + j].wait_flag;
+  if (f) poll_flag(f, wait_value, limit, err);
+}
+
+template <typename T, int G>
+__global__ __launch_bounds__(256) void attn_partial_layers_kernel(const AttendPlanLayer* __restrict__ plan,
+                                                                  const AttendPlanHeader* __restrict__ hdr,
+                                                                  int first, int count, LayerArgs shape, int nch,
+                                                                  uint32_t* err) {
+  const int64_t per = (int64_t)shape.B * shape.Hkv * nch;  // items of one layer
+  const int j = (int)(blockIdx.x / per);
+  const int it = (int)(blockIdx.x % per);
+  const AttendPlanLayer& L = plan[first + j];
+  if (!attend_layer_ok(L, hdr, first, count, shape, err)) return;
+  attn_partial_item<T, G>(L.a, static_cast<const T*>(L.q), L.part, nch, it / nch, it % nch, err);
+}
+
+template <typename T, int S>
+__global__ __launch_bounds__(128 * S) void attn_combine_layers_kernel(const AttendPlanLayer* __restrict__ plan,
+                                                                      const AttendPlanHeader* __restrict__ hdr,
+                                                                      int first, int count, LayerArgs shape, int nch,
+                                                                      uint32_t* err) {
+  const int64_t per = (int64_t)shape.B * shape.Hkv * shape.G;  // (unit, head) pairs of one layer
+  const int j = (int)(blockIdx.x / per);
+  const int it = (int)(blockIdx.x % per);
+  const AttendPlanLayer& L = plan[first + j];
+  if (!attend_layer_ok(L, hdr, first, count, shape, err)) return;
+  attn_combine_item<T, S>(L.a, L.part, nch, static_cast<T*>(L.out), it / shape.G, it % shape.G);
+}
+
+__global__ __launch_bounds__(64) void attend_signal_layers_kernel(const AttendPlanLayer* __restrict__ plan,
+                                                                  const AttendPlanHeader* __restrict__ hdr,
+                                                                  int first, int count, uint32_t signal_value) {
+  const int j = (int)threadIdx.x;
+  if (j >= count || (uint32_t)(first + count) > hdr->n_layers) return;
+  uint32_t* f = plan[first + j].signal_flag;
+  if (f) __hip_atomic_store(f, signal_value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// chunk groups of the combine: about 16 or more chunks each
+int combine_groups(int nch) { return nch > 64 ? 8 : nch > 32 ? 4 : nch > 16 ? 2 : 1; }
+
 }  // namespace
 
 hipError_t launch_attn_partial(const LayerArgs& a, const void* q, float* part, Span sp, int64_t max_units,
@@ -341,8 +418,7 @@ hipError_t launch_attn_combine(const LayerArgs& a, const float* part, void* out,
   const int64_t units = sp.list ? max_units : (int64_t)a.B * a.Hkv;
   if (units <= 0) return hipSuccess;
   const unsigned grid = (unsigned)(units * a.G);
-  // chunk groups: about 16 or more chunks each
-  const int S = nch > 64 ? 8 : nch > 32 ? 4 : nch > 16 ? 2 : 1;
+  const int S = combine_groups(nch);
   auto go = [&](auto sc) {
     constexpr int SG = decltype(sc)::value;
     if (a.dtype == CLO_F32)
@@ -356,6 +432,44 @@ hipError_t launch_attn_combine(const LayerArgs& a, const float* part, void* out,
     case 4: go(std::integral_constant<int, 4>{}); break;
     default: go(std::integral_constant<int, 8>{}); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_layers(const AttendPlanLayer* plan, const AttendPlanHeader* hdr, int first, int count,
+                                const LayerArgs& shape, uint32_t wait_value, uint32_t signal_value, uint32_t limit,
+                                uint32_t* err, hipStream_t s) {
+  const int nch = (int)((shape.k + kAttnChunk - 1) / kAttnChunk);
+  const int64_t U = (int64_t)shape.B * shape.Hkv;
+  attend_wait_layers_kernel<<<1, 64, 0, s>>>(plan, hdr, first, count, wait_value, limit, err);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned pgrid = (unsigned)(count * U * nch);
+  e = dispatch_group(shape.G, [&](auto gc) {
+    constexpr int G = decltype(gc)::value;
+    if (shape.dtype == CLO_F32)
+      attn_partial_layers_kernel<float, G><<<pgrid, 256, 0, s>>>(plan, hdr, first, count, shape, nch, err);
+    else
+      attn_partial_layers_kernel<uint16_t, G><<<pgrid, 256, 0, s>>>(plan, hdr, first, count, shape, nch, err);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
+  const unsigned cgrid = (unsigned)(count * U * shape.G);
+  auto go = [&](auto sc) {
+    constexpr int SG = decltype(sc)::value;
+    if (shape.dtype == CLO_F32)
+      attn_combine_layers_kernel<float, SG><<<cgrid, 128 * SG, 0, s>>>(plan, hdr, first, count, shape, nch, err);
+    else
+      attn_combine_layers_kernel<uint16_t, SG><<<cgrid, 128 * SG, 0, s>>>(plan, hdr, first, count, shape, nch, err);
+  };
+  switch (combine_groups(nch)) {
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    default: go(std::integral_constant<int, 8>{}); break;
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  attend_signal_layers_kernel<<<1, 64, 0, s>>>(plan, hdr, first, count, signal_value);
   return hipGetLastError();
 }
 

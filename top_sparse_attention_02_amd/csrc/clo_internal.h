@@ -253,6 +253,27 @@ struct SelectPlanHeader {
   uint32_t pad[62];
 };
 constexpr int kMaxSelectBatch = 64;  // layers per multi-layer selection
+// One layer of a multi-layer attention plan (device memory, written by the host).
+struct AttendPlanLayer {
+  LayerArgs a;
+  const void* q;               // the query the layer attends with
+  float* part;                 // the layer's chunk partials (its workspace)
+  void* out;
+  const uint32_t* wait_flag;   // the layer's rows are ready once *wait_flag >= wait_value (may be NULL)
+  uint32_t* signal_flag;       // set to signal_value once the layer's outputs are written (may be NULL)
+};
+struct AttendPlanHeader {
+  uint32_t n_layers;  // layers the plan holds (launches past them are refused on the GPU)
+  uint32_t pad[63];
+};
+constexpr int kMaxAttendBatch = 64;  // layers per multi-layer attention
+// The attention of plan layers first .. first + count - 1 (shape: the layers'
+// common shape) in four launches: a one-wave wait for every layer's flag
+// (bounded by limit), the partials, the combines, and a one-wave launch
+// storing signal_value to every layer's signal flag (release).
+hipError_t launch_attend_layers(const AttendPlanLayer* plan, const AttendPlanHeader* hdr, int first, int count,
+                                const LayerArgs& shape, uint32_t wait_value, uint32_t signal_value, uint32_t limit,
+                                uint32_t* err, hipStream_t s);
 // Blocks of a one-launch top-k, all resident at once (so chunks per unit at most).
 constexpr int kFusedMaxBlocks = 128;
 // Reuse test and unit lists (one block per layer, after the layer's wait),

@@ -274,6 +274,25 @@ def default_select_batches(units: int, n_layers: int):
     return tuple(sizes)
 
 
+def default_attend_batches(n_layers: int):
+    """Attention batch sizes of the 48-layer loop (clo_attend_layers): batches of
+    8 layers, the last layers in batches of 4, 2, 1 and 1 so that little
+    attention is left once the gather has read the last layer."""
+    sizes, left = [], n_layers
+    tail = [n for n in (4, 2, 1, 1) if n <= n_layers]
+    body = n_layers - sum(tail)
+    while body > 0:
+        sizes.append(min(8, body))
+        body -= sizes[-1]
+    return tuple(sizes + tail)
+
+
+def batched_attend_ok(layers) -> bool:
+    """Whether clo_attend_layers takes these layers: one batch, head and top-k shape."""
+    b = layers[0]
+    return all((x.B, x.Hq, x.Hkv, x.k, x.dtype) == (b.B, b.Hq, b.Hkv, b.k, b.dtype) for x in layers)
+
+
 def batched_select_ok(layers) -> bool:
     """Whether clo_select_layers takes these layers: bf16, at most 64 units per
     layer, token top-k, at most 128 chunks of 16384 keys, one shape for all."""
@@ -281,6 +300,21 @@ def batched_select_ok(layers) -> bool:
     same = all((x.B, x.Hq, x.Hkv, x.N, x.k) == (b.B, b.Hq, b.Hkv, b.N, b.k) for x in layers)
     return (same and b.dtype == "bf16" and b.B * b.Hkv <= 64 and (b.shape.block_size or 1) <= 1
             and -(-b.N // 16384) <= 128)
+
+
+def _cover(sizes, n_layers: int):
+    """Consecutive batches covering n_layers: the given sizes, the last cut to
+    fit or repeated until every layer is covered."""
+    out, left = [], n_layers
+    for n in sizes:
+        if left <= 0:
+            break
+        out.append(min(int(n), left))
+        left -= out[-1]
+    while left > 0:
+        out.append(min(int(sizes[-1]), left))
+        left -= out[-1]
+    return out
 
 
 class LayerLoop:
@@ -298,7 +332,12 @@ class LayerLoop:
             over all layers (clo_gather_layers), whose blocks run from one
             layer's tail straight into the next layer; gather="per-layer" uses
             one clo_gather_kv launch per layer instead;
-    attend: waits for gat[l], attention of layer l, then flag att[l] = epoch.
+    attend: waits for gat[l], attention of layer l, then flag att[l] = epoch;
+            with attend="batched" (the default) consecutive layers are attended
+            by one clo_attend_layers call each (sizes `attend_batches`, by
+            default default_attend_batches), which waits for every gat[l] of
+            its layers and sets their att[l], four launches per call instead
+            of four per layer.
     With select="batched" the selections run as clo_select_layers calls over
     consecutive layers (sizes `select_batches`, by default
     default_select_batches: small first so that the gather starts early, larger
@@ -313,13 +352,17 @@ class LayerLoop:
     """
 
     def __init__(self, layers, spin_limit: int = 0, select_streams: int = 1, gather: str = "resident",
-                 select: str = "batched", select_batches=None):
+                 select: str = "batched", select_batches=None, attend: str = "batched", attend_batches=None):
         if gather not in ("resident", "per-layer"):
             raise ValueError(gather)
         if select not in ("per-layer", "batched"):
             raise ValueError(select)
+        if attend not in ("per-layer", "batched"):
+            raise ValueError(attend)
         if select == "batched" and not batched_select_ok(layers):
             select = "per-layer"  # shapes the multi-layer selection does not take
+        if attend == "batched" and (gather != "resident" or not batched_attend_ok(layers)):
+            attend = "per-layer"  # the per-layer gathers each hand their layer to its attention
         self.layers = layers
         L = len(layers)
         dev = layers[0].q.device
@@ -342,18 +385,7 @@ class LayerLoop:
         if select == "batched":
             if select_batches is None:
                 select_batches = default_select_batches(layers[0].B * layers[0].Hkv, L)
-            # consecutive batches covering the layers: the given sizes, the last
-            # cut to fit or repeated until every layer is covered
-            sizes, left = [], L
-            for n in select_batches:
-                if left <= 0:
-                    break
-                sizes.append(min(int(n), left))
-                left -= sizes[-1]
-            while left > 0:
-                sizes.append(min(int(select_batches[-1]), left))
-                left -= sizes[-1]
-            self.batches = sizes
+            self.batches = _cover(select_batches, L)
             # one plan for steady steps (each layer's query and threshold) and one for
             # cold steps (every unit misses: tau = +inf, q_prev as the query)
             for cold in (False, True):
@@ -365,6 +397,17 @@ class LayerLoop:
                                   self._flag(2, l), self._flag(0, l)))
                 clo.clo_select_plan(items, plan)
                 self.sel_plans[cold] = plan
+        self.attend = attend
+        self.att_plans = {}
+        if attend == "batched":
+            self.att_batches = _cover(attend_batches or default_attend_batches(L), L)
+            # steady steps attend with each layer's query, cold steps with q_prev
+            for cold in (False, True):
+                plan = torch.zeros(clo.clo_attend_plan_size(L), dtype=torch.uint8, device=dev)
+                items = [(b.shape, b.layer(), b.q_prev if cold else b.q, b.out, b.ws, self._flag(1, l),
+                          self._flag(2, l)) for l, b in enumerate(layers)]
+                clo.clo_attend_plan(items, plan)
+                self.att_plans[cold] = plan
 
     def _flag(self, kind: int, l: int):
         return self.flags[kind, l]
@@ -412,8 +455,15 @@ class LayerLoop:
             # every selection is enqueued before the gather that waits for it
             clo.clo_gather_layers(self.plan, len(self.layers), self.plan_blocks, e, e, error_word=self.error,
                                   spin_limit=sp, stream=self.s_gather)
-            for b, shape, layer, q, l in calls:
-                self._attend(b, shape, layer, q, l, e)
+            if self.attend == "batched":
+                plan, first = self.att_plans[cold], 0
+                for n in self.att_batches:
+                    clo.clo_attend_layers(self.layers[0].shape, plan, first, n, e, e, error_word=self.error,
+                                          spin_limit=sp, stream=self.s_attend)
+                    first += n
+            else:
+                for b, shape, layer, q, l in calls:
+                    self._attend(b, shape, layer, q, l, e)
         # the caller's stream continues after the last attention
         cur.wait_stream(self.s_attend)
 
