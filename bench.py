@@ -910,6 +910,21 @@ def main():
             roofline["peak_measured"] = round(hbm_probe["read_gbs"], 1)
             roofline["frac_measured"] = round(attn_gbs / hbm_probe["read_gbs"], 4)
 
+    # how the gather runs: its grid and the host bytes its loads keep in flight
+    # (the gather grids sit near measured cliffs, so a change shows here)
+    per_block = clo.clo_decode_step_schedule(layers[0].shape, layers[0].mask)["host_bytes_per_gather_block"]
+    if multi:
+        gb = loop.plan_blocks if loop.gather == "resident" else None
+        gather_schedule = {"mode": "48-layer loop, " + ("one resident gather launch per step" if gb else
+                                                          "a gather launch per layer"),
+                           "gather_blocks": gb, "host_bytes_in_flight": gb * per_block if gb else None}
+    else:
+        gather_schedule = clo.clo_decode_step_schedule(layers[0].shape, layers[0].mask)
+        if args.graph:
+            gather_schedule["mode"] = "in order (graph capture)"
+        if args.counters:
+            gather_schedule["mode"] = "in order (--counters)"
+
     # the step's lower bounds from its algorithmic bytes: the host link at the
     # rate measured in this run, HBM at the published peak and at the measured
     # read ceiling; the step can overlap the two, so its bound is the larger
@@ -959,6 +974,7 @@ def main():
         "frac_of_host_bound": round(host_bound_ms / ms_per_step, 4) if host_bound_ms else None,
         "bounds": bounds,
         "roofline": roofline,
+        "gather_schedule": gather_schedule,
         "persistent_plan": None if plan is None else {k: v for k, v in plan.items() if k != "persistent"},
         "block_size": args.block_size or 1,
         "blocks_vs_tokens": blocks,

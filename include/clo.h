@@ -435,6 +435,32 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
                            void* ws, size_t ws_bytes, const clo_sync* sync, void* stream);
 
 /*
+ * How clo_decode_step runs a layer of this shape (persistent_mask as in
+ * clo_layer), on a stream that is not capturing a graph: every kernel in order
+ * on the stream, a gather launch per unit range on two helper streams in turn,
+ * or one resident gather launch for all ranges; the ranges, the gather's grid
+ * and the host bytes its loads keep in flight (the quantity the gather grids
+ * are sized by: a few hundred KiB saturate the host link, and more slows every
+ * HBM kernel beside it).  Host-only; writes *out.
+ */
+typedef enum {
+  CLO_STEP_IN_ORDER = 0,
+  CLO_STEP_RANGE_GATHERS = 1,
+  CLO_STEP_RESIDENT_GATHER = 2
+} clo_step_mode;
+
+typedef struct {
+  int32_t mode;                         /* clo_step_mode */
+  int32_t ranges;                       /* unit ranges (1 in order) */
+  int32_t gather_blocks;                /* blocks of one gather launch (0: nothing to gather) */
+  int32_t gather_blocks_in_flight;      /* gather blocks running at once at most */
+  int64_t host_bytes_per_gather_block;  /* host reads one gather block keeps in flight */
+  int64_t host_bytes_in_flight;         /* gather_blocks_in_flight x host_bytes_per_gather_block */
+} clo_step_schedule;
+
+clo_status clo_decode_step_schedule(const clo_shape* shape, uint64_t persistent_mask, clo_step_schedule* out);
+
+/*
  * clo_decode_step without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, semantics and outputs

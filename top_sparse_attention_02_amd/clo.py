@@ -22,7 +22,11 @@ EXPORTS = ("clo_workspace_size", "clo_reuse_test", "clo_topk_select", "clo_reuse
            "clo_sparse_attn", "clo_decode_step", "clo_decode_step_static", "clo_append_kv", "clo_update_reference", "clo_plan_persistent", "clo_quantize_rows",
            "clo_stream_read", "clo_status_string", "clo_last_error", "clo_gather_plan_size", "clo_gather_plan",
            "clo_gather_layers", "clo_select_plan_size", "clo_select_plan", "clo_select_layers",
-           "clo_attend_plan_size", "clo_attend_plan", "clo_attend_layers")
+           "clo_attend_plan_size", "clo_attend_plan", "clo_attend_layers", "clo_decode_step_schedule")
+
+CLO_STEP_IN_ORDER, CLO_STEP_RANGE_GATHERS, CLO_STEP_RESIDENT_GATHER = range(3)
+STEP_MODES = {CLO_STEP_IN_ORDER: "in order", CLO_STEP_RANGE_GATHERS: "a gather launch per unit range",
+              CLO_STEP_RESIDENT_GATHER: "one resident gather launch"}
 
 
 class CloError(RuntimeError):
@@ -64,6 +68,12 @@ class clo_select_layer(ctypes.Structure):
                 ("signal_flag", ctypes.c_void_p)]
 
 
+class clo_step_schedule(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("ranges", ctypes.c_int32), ("gather_blocks", ctypes.c_int32),
+                ("gather_blocks_in_flight", ctypes.c_int32), ("host_bytes_per_gather_block", ctypes.c_int64),
+                ("host_bytes_in_flight", ctypes.c_int64)]
+
+
 class clo_attend_layer(ctypes.Structure):
     _fields_ = [("shape", ctypes.POINTER(clo_shape)), ("layer", ctypes.POINTER(clo_layer)), ("q", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
@@ -96,6 +106,8 @@ def load():
         L.clo_sparse_attn.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, sz, P(clo_sync), vp]
         L.clo_decode_step.restype = st
         L.clo_decode_step.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, vp, vp, vp, sz, P(clo_sync), vp]
+        L.clo_decode_step_schedule.restype = st
+        L.clo_decode_step_schedule.argtypes = [P(clo_shape), ctypes.c_uint64, P(clo_step_schedule)]
         L.clo_decode_step_static.restype = st
         L.clo_decode_step_static.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, vp, vp, P(clo_sync), vp]
         L.clo_append_kv.restype = st
@@ -289,6 +301,17 @@ def clo_sparse_attn(shape: Shape, layer: Layer, q, out, ws, sync: Optional[Sync]
     _check(load().clo_sparse_attn(ctypes.byref(shape.c()), ctypes.byref(layer.c()), ptr(q), ptr(out), ptr(ws),
                                   nbytes(ws, ws_bytes), _sync(sync), stream_handle(stream)),
            "clo_sparse_attn")
+
+
+def clo_decode_step_schedule(shape: Shape, persistent_mask: int = 0) -> dict:
+    """How clo_decode_step runs a layer of this shape (host-only)."""
+    out = clo_step_schedule()
+    _check(load().clo_decode_step_schedule(ctypes.byref(shape.c()), int(persistent_mask), ctypes.byref(out)),
+           "clo_decode_step_schedule")
+    return {"mode": STEP_MODES[out.mode], "ranges": out.ranges, "gather_blocks": out.gather_blocks,
+            "gather_blocks_in_flight": out.gather_blocks_in_flight,
+            "host_bytes_per_gather_block": out.host_bytes_per_gather_block,
+            "host_bytes_in_flight": out.host_bytes_in_flight}
 
 
 def clo_decode_step(shape: Shape, layer: Layer, q, q_prev, out, reuse, cos, ws, sync: Optional[Sync] = None,

@@ -979,14 +979,21 @@ bool step_in_order_forced() {
   return forced;
 }
 
+// How clo_decode_step runs a layer (clo_decode_step_schedule reports it).
+clo_step_mode step_mode(const Plan& p, bool capturing) {
+  if (p.a.H == 0 || p.U < kOverlapUnits || capturing || step_in_order_forced()) return CLO_STEP_IN_ORDER;
+  return p.U >= kResidentGatherUnits ? CLO_STEP_RESIDENT_GATHER : CLO_STEP_RANGE_GATHERS;
+}
+
 clo_status step_overlapped(const Plan& p, const Workspace& w, const void* q, const void* q_prev, void* out,
-                           uint8_t* reuse, float* cos, uint32_t limit, hipStream_t s) {
+                           uint8_t* reuse, float* cos, uint32_t limit, clo_step_mode mode, hipStream_t s) {
   DeviceQueues* dq = nullptr;
   clo_status st;
   if ((st = device_queues(&dq))) return st;
   std::lock_guard<std::mutex> lk(dq->mu);
-  return p.U >= kResidentGatherUnits ? step_overlapped_resident(p, w, q, q_prev, out, reuse, cos, limit, dq, s)
-                                     : step_overlapped_streams(p, w, q, q_prev, out, reuse, cos, dq, s);
+  return mode == CLO_STEP_RESIDENT_GATHER
+             ? step_overlapped_resident(p, w, q, q_prev, out, reuse, cos, limit, dq, s)
+             : step_overlapped_streams(p, w, q, q_prev, out, reuse, cos, dq, s);
 }
 
 }  // namespace
@@ -1024,11 +1031,36 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
   // The overlapped step's own waits (its streams' hand-offs) are bounded by the
   // library's default, not by sync->spin_limit: a bound the caller chose for its
   // own flag could end them before the kernels they wait for have run.
-  st = p.a.H > 0 && p.U >= kOverlapUnits && cap == hipStreamCaptureStatusNone && !step_in_order_forced()
-           ? step_overlapped(p, w, q, q_prev, out, reuse, cos, kDefaultSpinLimit, s)
-           : step_in_order(p, w, q, q_prev, out, reuse, cos, s);
+  const clo_step_mode mode = step_mode(p, cap != hipStreamCaptureStatusNone);
+  st = mode != CLO_STEP_IN_ORDER ? step_overlapped(p, w, q, q_prev, out, reuse, cos, kDefaultSpinLimit, mode, s)
+                                 : step_in_order(p, w, q, q_prev, out, reuse, cos, s);
   if (st) return st;
   return post_signal(sync, s);
+}
+
+clo_status clo_decode_step_schedule(const clo_shape* shape, uint64_t persistent_mask, clo_step_schedule* out) {
+  Plan p;
+  clo_status st;
+  if (!out) return fail(CLO_E_ARG, "out is NULL");
+  if ((st = make_plan(shape, persistent_mask, &p))) return st;
+  clo_step_schedule x;
+  memset(&x, 0, sizeof x);
+  x.mode = step_mode(p, false);
+  x.host_bytes_per_gather_block = kGatherBytesPerBlock;
+  if (x.mode == CLO_STEP_IN_ORDER) {
+    x.ranges = 1;
+    x.gather_blocks = p.a.H > 0 && p.U > 0 ? (p.U >= kGatherWideUnits ? kGatherBlocksAloneWide : kGatherBlocksAlone)
+                                           : 0;
+    x.gather_blocks_in_flight = x.gather_blocks;
+  } else {
+    x.ranges = split_ranges(p).R;
+    const bool resident = x.mode == CLO_STEP_RESIDENT_GATHER;
+    x.gather_blocks = resident ? kGatherBlocksRanges : kGatherBlocksOverlapped;
+    x.gather_blocks_in_flight = resident ? kGatherBlocksRanges : 2 * kGatherBlocksOverlapped;  // two streams
+  }
+  x.host_bytes_in_flight = (int64_t)x.gather_blocks_in_flight * kGatherBytesPerBlock;
+  *out = x;
+  return ok();
 }
 
 clo_status clo_decode_step_static(const clo_shape* shape, const clo_layer* layer, const void* q,

@@ -49,6 +49,9 @@ constexpr int kPartStride = kHeadDim + 2;  // floats per (chunk, head) partial: 
 constexpr int kGatherUnroll = 2;
 constexpr int kGatherBlocksOverlapped = 20;  // per gather stream
 constexpr int kGatherBlocksRanges = 40;      // the resident range gather of clo_decode_step
+// host bytes one gather block keeps in flight: 256 lanes x 4 loads of 16 bytes
+// (kGatherUnroll rows of K and of V, or 2 x kGatherUnroll quantized records)
+constexpr int64_t kGatherBytesPerBlock = 256 * 2 * kGatherUnroll * 16;
 constexpr int kGatherBlocksAlone = 24;
 constexpr int kGatherBlocksAloneWide = 40;  // layers of at least kGatherWideUnits units
 constexpr int kGatherWideUnits = 64;
