@@ -88,6 +88,8 @@ def parse():
                          "clo_sparse_attn per layer")
     ap.add_argument("--attend-batches", default="", metavar="N,N,...",
                     help="48-layer loop: attention batch sizes (default: workload.default_attend_batches)")
+    ap.add_argument("--gather-blocks", type=int, default=0, metavar="G",
+                    help="48-layer loop: blocks of the resident gather launch (default: clo_gather_plan's)")
     ap.add_argument("--select-streams", type=int, default=1, metavar="S",
                     help="48-layer loop: streams the layers' selections alternate between")
     ap.add_argument("--graph", action="store_true",
@@ -813,7 +815,7 @@ def main():
     if multi:
         att_batches = tuple(int(x) for x in args.attend_batches.split(",")) if args.attend_batches else None
         loop = workload.LayerLoop(layers, select_streams=args.select_streams, select=args.select,
-                                  attend=args.attend, attend_batches=att_batches)
+                                  attend=args.attend, attend_batches=att_batches, gather_blocks=args.gather_blocks)
         loop.step(cold=True)
         step = (lambda: loop.step()) if args.step == 1 else (lambda: loop.step(cold=True))
     else:
@@ -912,14 +914,15 @@ def main():
 
     # how the gather runs: its grid and the host bytes its loads keep in flight
     # (the gather grids sit near measured cliffs, so a change shows here)
-    per_block = clo.clo_decode_step_schedule(layers[0].shape, layers[0].mask)["host_bytes_per_gather_block"]
+    per_block = clo.clo_decode_step_schedule(layers[0].shape, layers[0].mask,
+                                             host_format)["host_bytes_per_gather_block"]
     if multi:
         gb = loop.plan_blocks if loop.gather == "resident" else None
         gather_schedule = {"mode": "48-layer loop, " + ("one resident gather launch per step" if gb else
                                                           "a gather launch per layer"),
                            "gather_blocks": gb, "host_bytes_in_flight": gb * per_block if gb else None}
     else:
-        gather_schedule = clo.clo_decode_step_schedule(layers[0].shape, layers[0].mask)
+        gather_schedule = clo.clo_decode_step_schedule(layers[0].shape, layers[0].mask, host_format)
         if args.graph:
             gather_schedule["mode"] = "in order (graph capture)"
         if args.counters:

@@ -435,8 +435,8 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
                            void* ws, size_t ws_bytes, const clo_sync* sync, void* stream);
 
 /*
- * How clo_decode_step runs a layer of this shape (persistent_mask as in
- * clo_layer), on a stream that is not capturing a graph: every kernel in order
+ * How clo_decode_step runs a layer of this shape (persistent_mask and
+ * host_format as in clo_layer), on a stream that is not capturing a graph: every kernel in order
  * on the stream, a gather launch per unit range on two helper streams in turn,
  * or one resident gather launch for all ranges; the ranges, the gather's grid
  * and the host bytes its loads keep in flight (the quantity the gather grids
@@ -458,7 +458,8 @@ typedef struct {
   int64_t host_bytes_in_flight;         /* gather_blocks_in_flight x host_bytes_per_gather_block */
 } clo_step_schedule;
 
-clo_status clo_decode_step_schedule(const clo_shape* shape, uint64_t persistent_mask, clo_step_schedule* out);
+clo_status clo_decode_step_schedule(const clo_shape* shape, uint64_t persistent_mask, int32_t host_format,
+                                    clo_step_schedule* out);
 
 /*
  * clo_decode_step without a workspace argument, for callers that cannot

@@ -153,9 +153,15 @@ def test_decode_step_schedule_reports_how_a_layer_runs():
     one = clo.clo_decode_step_schedule(S(batch=1, n_q_heads=40, n_kv_heads=8, context=524288, topk=52429, tau=0.8,
                                          dtype=clo.CLO_BF16), persistent_mask=0b1)
     assert one["mode"] == "in order" and one["ranges"] == 1 and one["gather_blocks"] > 0
+    one_q = clo.clo_decode_step_schedule(S(batch=1, n_q_heads=40, n_kv_heads=8, context=524288, topk=52429, tau=0.8,
+                                           dtype=clo.CLO_BF16), persistent_mask=0b1, host_format=clo.CLO_HOST_INT4)
+    assert one_q["gather_blocks"] > one["gather_blocks"]  # quantized items keep fewer bytes in flight per block
     allp = clo.clo_decode_step_schedule(S(batch=1, n_q_heads=32, n_kv_heads=8, context=4096, topk=410, tau=0.8,
                                           dtype=clo.CLO_F32), persistent_mask=0xFF)
     assert allp["mode"] == "in order" and allp["gather_blocks"] == 0 and allp["host_bytes_in_flight"] == 0
     with pytest.raises(clo.CloError):
         clo.clo_decode_step_schedule(S(batch=1, n_q_heads=30, n_kv_heads=8, context=4096, topk=410, tau=0.8,
                                        dtype=clo.CLO_F32))
+    with pytest.raises(clo.CloError):
+        clo.clo_decode_step_schedule(S(batch=1, n_q_heads=32, n_kv_heads=8, context=4096, topk=410, tau=0.8,
+                                       dtype=clo.CLO_F32), host_format=7)

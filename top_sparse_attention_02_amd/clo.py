@@ -107,7 +107,7 @@ def load():
         L.clo_decode_step.restype = st
         L.clo_decode_step.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, vp, vp, vp, sz, P(clo_sync), vp]
         L.clo_decode_step_schedule.restype = st
-        L.clo_decode_step_schedule.argtypes = [P(clo_shape), ctypes.c_uint64, P(clo_step_schedule)]
+        L.clo_decode_step_schedule.argtypes = [P(clo_shape), ctypes.c_uint64, ctypes.c_int32, P(clo_step_schedule)]
         L.clo_decode_step_static.restype = st
         L.clo_decode_step_static.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, vp, vp, P(clo_sync), vp]
         L.clo_append_kv.restype = st
@@ -303,11 +303,11 @@ def clo_sparse_attn(shape: Shape, layer: Layer, q, out, ws, sync: Optional[Sync]
            "clo_sparse_attn")
 
 
-def clo_decode_step_schedule(shape: Shape, persistent_mask: int = 0) -> dict:
+def clo_decode_step_schedule(shape: Shape, persistent_mask: int = 0, host_format: int = CLO_HOST_NATIVE) -> dict:
     """How clo_decode_step runs a layer of this shape (host-only)."""
     out = clo_step_schedule()
-    _check(load().clo_decode_step_schedule(ctypes.byref(shape.c()), int(persistent_mask), ctypes.byref(out)),
-           "clo_decode_step_schedule")
+    _check(load().clo_decode_step_schedule(ctypes.byref(shape.c()), int(persistent_mask), int(host_format),
+                                           ctypes.byref(out)), "clo_decode_step_schedule")
     return {"mode": STEP_MODES[out.mode], "ranges": out.ranges, "gather_blocks": out.gather_blocks,
             "gather_blocks_in_flight": out.gather_blocks_in_flight,
             "host_bytes_per_gather_block": out.host_bytes_per_gather_block,

@@ -525,7 +525,7 @@ clo_status clo_gather_kv(const clo_shape* shape, const clo_layer* layer, const u
   if ((st = bind_ws(p, ws, ws_bytes, &w))) return st;
   uint32_t* counter = reinterpret_cast<uint32_t*>(w.meta + kMetaGather);
   uint32_t* done = reinterpret_cast<uint32_t*>(w.meta + kMetaGatherDone);
-  const int blocks = p.U >= kGatherWideUnits ? kGatherBlocksAloneWide : kGatherBlocksAlone;
+  const int blocks = alone_gather_blocks(p.U, p.a.host_fmt);
   if (sync && sync->wait_flag) {
     // one launch: the gather's blocks wait for the flag themselves, and the last
     // one to finish signals; the work counters are zero (every call on the
@@ -580,7 +580,7 @@ clo_status clo_gather_plan(const clo_gather_layer* layers, int32_t n_layers, voi
       hipError_t e = hipMemcpy(d.counter, &zero, 4, hipMemcpyHostToDevice);
       if (e == hipSuccess) e = hipMemcpy(d.done, &zero, 4, hipMemcpyHostToDevice);
       if ((st = hip_status(e, "clearing the gather counters"))) return st;
-      if (p.U >= kGatherWideUnits) grid = kGatherBlocksAloneWide;
+      grid = std::max(grid, alone_gather_blocks(p.U, p.a.host_fmt));
     } else {
       // nothing to gather: the layer's items are none, its counters live in the plan
       d.a = p.a;
@@ -831,7 +831,7 @@ clo_status step_in_order(const Plan& p, const Workspace& w, const void* q, const
     // the unit lists hold one range; its offloaded misses, and the work counter
     // the list kernel cleared
     if ((st = hip_status(launch_gather(p.a, reuse, span_host_range(w, 0), p.U,
-                                       p.U >= kGatherWideUnits ? kGatherBlocksAloneWide : kGatherBlocksAlone,
+                                       alone_gather_blocks(p.U, p.a.host_fmt),
                                        reinterpret_cast<uint32_t*>(w.meta + kMetaGather), s),
                          "gather launch")))
       return st;
@@ -1038,19 +1038,22 @@ clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const
   return post_signal(sync, s);
 }
 
-clo_status clo_decode_step_schedule(const clo_shape* shape, uint64_t persistent_mask, clo_step_schedule* out) {
+clo_status clo_decode_step_schedule(const clo_shape* shape, uint64_t persistent_mask, int32_t host_format,
+                                    clo_step_schedule* out) {
   Plan p;
   clo_status st;
   if (!out) return fail(CLO_E_ARG, "out is NULL");
   if ((st = make_plan(shape, persistent_mask, &p))) return st;
+  if (host_format != CLO_HOST_NATIVE && host_format != CLO_HOST_INT8 && host_format != CLO_HOST_INT4)
+    return fail(CLO_E_ARG, "host_format %d is not a clo_host_format", host_format);
+  p.a.host_fmt = host_format;
   clo_step_schedule x;
   memset(&x, 0, sizeof x);
   x.mode = step_mode(p, false);
   x.host_bytes_per_gather_block = kGatherBytesPerBlock;
   if (x.mode == CLO_STEP_IN_ORDER) {
     x.ranges = 1;
-    x.gather_blocks = p.a.H > 0 && p.U > 0 ? (p.U >= kGatherWideUnits ? kGatherBlocksAloneWide : kGatherBlocksAlone)
-                                           : 0;
+    x.gather_blocks = p.a.H > 0 && p.U > 0 ? alone_gather_blocks(p.U, p.a.host_fmt) : 0;
     x.gather_blocks_in_flight = x.gather_blocks;
   } else {
     x.ranges = split_ranges(p).R;

@@ -53,8 +53,21 @@ constexpr int kGatherBlocksRanges = 40;      // the resident range gather of clo
 // (kGatherUnroll rows of K and of V, or 2 x kGatherUnroll quantized records)
 constexpr int64_t kGatherBytesPerBlock = 256 * 2 * kGatherUnroll * 16;
 constexpr int kGatherBlocksAlone = 24;
+constexpr int kGatherBlocksAloneQuant = 32;  // int8 / int4 host rows
 constexpr int kGatherBlocksAloneWide = 40;  // layers of at least kGatherWideUnits units
 constexpr int kGatherWideUnits = 64;
+// Grid of a gather that runs alone on its stream (clo_gather_kv, the in-order
+// step, the resident multi-layer gather).  ms per 48-layer step at B=1,
+// N=524288 (8 units per layer) with 24 / 32 / 40 blocks: native rows 17.84 /
+// 17.91-17.98 / 18.00-18.02, int8 rows 9.84-9.85 / 9.55, int4 rows 7.27-7.34 /
+// 7.02-7.08 / 7.41-7.43 (28 and 36: 7.07 and 7.17); at B=8, N=262144 (64
+// units) flat within 0.2% over 24-40 (int4 rows 27.87 / 27.81 with 32 / 40,
+// 28.45 with 48).  Quantized items wait on index and exponent loads before any
+// host read, so they keep fewer bytes in flight per block.
+inline int alone_gather_blocks(int64_t units, int32_t host_fmt) {
+  if (units >= kGatherWideUnits) return kGatherBlocksAloneWide;
+  return host_fmt == CLO_HOST_NATIVE ? kGatherBlocksAlone : kGatherBlocksAloneQuant;
+}
 
 // Everything a kernel needs to address one layer's buffers.
 struct LayerArgs {

@@ -352,7 +352,8 @@ class LayerLoop:
     """
 
     def __init__(self, layers, spin_limit: int = 0, select_streams: int = 1, gather: str = "resident",
-                 select: str = "batched", select_batches=None, attend: str = "batched", attend_batches=None):
+                 select: str = "batched", select_batches=None, attend: str = "batched", attend_batches=None,
+                 gather_blocks: int = 0):
         if gather not in ("resident", "per-layer"):
             raise ValueError(gather)
         if select not in ("per-layer", "batched"):
@@ -380,6 +381,8 @@ class LayerLoop:
             items = [(b.shape, b.layer(), b.reuse, b.ws, self._flag(0, l), self._flag(1, l))
                      for l, b in enumerate(layers)]
             self.plan_blocks = clo.clo_gather_plan(items, self.plan)
+            if gather_blocks:  # the resident gather's grid instead of the plan's suggestion
+                self.plan_blocks = int(gather_blocks)
         self.select = select
         self.sel_plans = {}
         if select == "batched":
