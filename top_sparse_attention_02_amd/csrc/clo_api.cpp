@@ -264,6 +264,17 @@ RangeBounds one_range(const Plan& p) {
 }
 uint32_t* score_counter(const Workspace& w, int r) { return reinterpret_cast<uint32_t*>(w.meta + kMetaScore + r); }
 
+// CUs the scoring of the ranges (or batches of layers) from `first` on is
+// spread over (two persistent blocks each).  The first range's scoring runs
+// alone and takes every CU; the later ones run beside the gather and the
+// attention of earlier ranges, whose blocks find no registers left on a CU
+// holding two scoring blocks.  At half the CUs, steps/s: B=16, N=32768
+// 332.3-332.5 -> 333.2 (int4 rows 837-838 -> 862-865); B=64, N=131072
+// unchanged at 81.9 (int4 rows 226-227 -> 229-230); the 48-layer loop at B=1,
+// N=524288 unchanged at 56.0 (int8 rows 104.6-104.7 -> 105.2, int4 140.8-140.9
+// -> 141.3-141.4).
+int score_cus(int first, int cu) { return first == 0 ? cu : std::max(1, cu / 2); }
+
 // Per-device helper streams and events of the overlapped decode step, created
 // on first use and kept for the life of the process.  They hold no user data.
 struct DeviceQueues {
@@ -702,8 +713,8 @@ clo_status clo_select_layers(const clo_shape* shape, const void* plan, int32_t f
   auto* entries = reinterpret_cast<const SelectPlanLayer*>(static_cast<const char*>(plan) + sizeof(SelectPlanHeader));
   const int cmax = (int)((p.a.N + kTopkChunk - 1) / kTopkChunk);
   return hip_status(launch_select_layers(entries, hdr, first, count, p.a, cmax, wait_value, signal_value,
-                                         spin_limit ? spin_limit : kDefaultSpinLimit, error_word, num_cus(),
-                                         static_cast<hipStream_t>(stream)),
+                                         spin_limit ? spin_limit : kDefaultSpinLimit, error_word,
+                                         score_cus(first, num_cus()), static_cast<hipStream_t>(stream)),
                     "selection launch");
 }
 
@@ -896,7 +907,8 @@ clo_status step_overlapped_streams(const Plan& p, const Workspace& w, const void
   CLO_TRY(launch_reuse(p.a, q, q_prev, reuse, cos, s), "reuse launch");
   CLO_TRY(launch_compact(p.a, reuse, w, x.R, x.rb, s), "compact launch");
   for (int r = 0; r < x.R; ++r) {
-    CLO_TRY(launch_score(p.a, q, span_range(w, r), x.per, w, score_counter(w, r), cu, s), "score launch");
+    CLO_TRY(launch_score(p.a, q, span_range(w, r), x.per, w, score_counter(w, r), score_cus(r, cu), s),
+            "score launch");
     CLO_TRY(launch_select(p.a, span_range(w, r), x.per, w, s), "top-k launch");
     CLO_TRY(hipEventRecord(dq->ev_topk[r], s), "event record");
     hipStream_t gsr = (r & 1) ? dq->gather2 : dq->gather;
@@ -937,7 +949,7 @@ clo_status step_overlapped_resident(const Plan& p, const Workspace& w, const voi
   for (int r0 = 0, n = 1, g = 0; r0 < x.R; r0 += n, n = g >= 1 ? 2 * n : n, ++g) {
     n = std::min(n, x.R - r0);
     const Span sp{w.list_all, w.meta + kMetaOffAll + r0, w.meta + kMetaOffAll + r0 + n};
-    CLO_TRY(launch_score(p.a, q, sp, x.per * n, w, score_counter(w, g), cu, s), "score launch");
+    CLO_TRY(launch_score(p.a, q, sp, x.per * n, w, score_counter(w, g), score_cus(r0, cu), s), "score launch");
     CLO_TRY(launch_select(p.a, sp, x.per * n, w, s), "top-k launch");
     // the kernel boundary makes the ranges' indices visible to the gather
     CLO_TRY(launch_signal(meta + kMetaSelFlag + r0, 1u, s, n), "signal launch");
