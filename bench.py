@@ -88,6 +88,8 @@ def parse():
                          "clo_sparse_attn per layer")
     ap.add_argument("--attend-batches", default="", metavar="N,N,...",
                     help="48-layer loop: attention batch sizes (default: workload.default_attend_batches)")
+    ap.add_argument("--select-batches", default="", metavar="N,N,...",
+                    help="48-layer loop: selection batch sizes (default: workload.default_select_batches)")
     ap.add_argument("--gather-blocks", type=int, default=0, metavar="G",
                     help="48-layer loop: blocks of the resident gather launch (default: clo_gather_plan's)")
     ap.add_argument("--select-streams", type=int, default=1, metavar="S",
@@ -814,8 +816,10 @@ def main():
             bufs.set_block_size(args.block_size)
     if multi:
         att_batches = tuple(int(x) for x in args.attend_batches.split(",")) if args.attend_batches else None
+        sel_batches = tuple(int(x) for x in args.select_batches.split(",")) if args.select_batches else None
         loop = workload.LayerLoop(layers, select_streams=args.select_streams, select=args.select,
-                                  attend=args.attend, attend_batches=att_batches, gather_blocks=args.gather_blocks)
+                                  attend=args.attend, attend_batches=att_batches, gather_blocks=args.gather_blocks,
+                                  select_batches=sel_batches)
         loop.step(cold=True)
         step = (lambda: loop.step()) if args.step == 1 else (lambda: loop.step(cold=True))
     else:
@@ -970,7 +974,9 @@ def main():
                    "data_layers": p.data_layers or p.layers, "host_memory": args.host_memory,
                    **({"graph": True} if args.graph else {}),
                    **({"step_schedule": "in order on one stream (--counters)"} if args.counters else {}),
-                   **({"select_streams": args.select_streams, "select": loop.select, "attend": loop.attend,
+                   **({"select_streams": args.select_streams, "select": loop.select,
+                       **({"select_batches": list(loop.batches)} if loop.select == "batched" else {}),
+                       "attend": loop.attend,
                        **({"attend_batches": list(loop.att_batches)} if loop.attend == "batched" else {})}
                       if multi else {})},
         "host_bound_ms": bounds["host_bound_ms"],

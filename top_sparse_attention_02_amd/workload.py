@@ -265,7 +265,10 @@ def default_select_batches(units: int, n_layers: int):
     per call.  Measured on MI355X (ms per 48-layer step): B=1, N=524288 (8 units
     per layer) 17.89 with 3, 3, 6, 12, 24 against 18.09 with 1, 1, 2, 4, 8, 16, 16
     (int4 rows: 8.10 against 8.15); B=8, N=262144 (64 units) 76.2 with 1, 1, 2, 4,
-    8, 16, 16 against 76.6 with 3, 3, 6, 12, 24."""
+    8, 16, 16 against 76.6 with 3, 3, 6, 12, 24.  With the attention batched too, at
+    B=1: 17.84 (int4 rows 7.02) with 3, 3, 6, 12, 24 against 17.90-17.91 (7.40-7.44)
+    with 2, 2, 4, 8, 16, 16 or 4, 4, 8, 16, 16, 18.04 (7.09) with 6, 6, 12, 24 and
+    17.95 (7.62) with 3, 6, 12, 27."""
     f = max(1, -(-24 // max(1, units)))
     sizes, n = [f, f], f
     while sum(sizes) < n_layers:
