@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_common import log, run_and_check, small_problem, snapshot, compare, oracle_steps
+from tests.gpu_common import log, log_worst, run_and_check, small_problem, snapshot, compare, oracle_steps
 from oracle.margins import enforce_margins
 
 pytestmark = pytest.mark.gpu
@@ -159,6 +159,36 @@ def test_standalone_entry_points_equal_fused_step(need_gpu, batch):
     split = snapshot(bufs)
     for key in fused:
         assert np.array_equal(fused[key], split[key]), key
+
+
+@pytest.mark.parametrize("batch", [5, 64])
+def test_every_unit_reusing_gathers_nothing(need_gpu, batch):
+    """A steady step whose every unit reuses (q = q_prev): the overlapped step (20 units: a
+    gather launch per range; 256 units: the resident gather, every range with nothing to
+    gather but its flags still raised) keeps the cold step's selections and cache rows and
+    attends them, equal to the oracle's reuse step."""
+    import torch
+
+    from top_sparse_attention_02_amd import clo, workload
+
+    p = small_problem(f"allhit{batch}", batch=batch, hq=16, hkv=4, context=1500, topk=150, dtype="bf16",
+                      persistent=[0, 1, 0, 0])
+    enforce_margins(p, 0)
+    bufs = workload.load_layer(p, 0)
+    bufs.step0()
+    cold = snapshot(bufs)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bufs.decode_step(bufs.q_prev, bufs.q_prev, bufs.tau, sync=clo.Sync(error_word=err))
+    got = snapshot(bufs)
+    assert int(err.item()) == 0
+    assert got["reuse"].all()
+    for key in ("idx", "k_cache", "v_cache", "out"):
+        assert np.array_equal(got[key], cold[key]), key
+    qp = p.q_prev(0)
+    kv = lambda b, h: (p.kv("k", 0, b, h), p.kv("v", 0, b, h))  # noqa: E731
+    ref = oracle.decode_layer(qp, qp, kv, p.hkv, p.topk, p.tau, p.dtype, idx_prev=cold["idx"])
+    assert all(r["reuse"] for r in ref.values())
+    log_worst(p.name, "all reuse", compare(p, bufs, got, ref, kv, "all reuse", check_cos=False), p.dtype)
 
 
 @pytest.mark.parametrize("batch", [5, 64])
