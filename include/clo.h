@@ -462,6 +462,18 @@ clo_status clo_decode_step_schedule(const clo_shape* shape, uint64_t persistent_
                                     clo_step_schedule* out);
 
 /*
+ * GPU time, in ms, of the gather inside the last overlapped clo_decode_step on
+ * the current device (clo_step_mode 1 or 2): from the start of its first
+ * gather launch to the end of its last, measured with events on the helper
+ * streams the gathers run on.  For measurement: the caller's events cannot
+ * bracket work on the library's streams.  Call once that step has completed
+ * (CLO_E_ARG while it runs, or when no overlapped step has gathered on this
+ * device).  The resident launch's time includes its wait for the first
+ * range's selection.
+ */
+clo_status clo_last_step_gather_ms(float* ms);
+
+/*
  * clo_decode_step without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, semantics and outputs

@@ -192,6 +192,29 @@ def test_every_unit_reusing_gathers_nothing(need_gpu, batch):
 
 
 @pytest.mark.parametrize("batch", [5, 64])
+def test_last_step_gather_time_is_reported(need_gpu, batch):
+    """clo_last_step_gather_ms after an overlapped step (20 units: range gathers on two
+    streams; 256 units: the resident gather) is a positive GPU time no longer than the step
+    itself, as timed with events on the caller's stream around it."""
+    import torch
+
+    from top_sparse_attention_02_amd import clo, workload
+
+    p = small_problem(f"gtime{batch}", batch=batch, hq=16, hkv=4, context=3000, topk=300, dtype="bf16",
+                      persistent=[0, 1, 0, 0])
+    bufs = workload.load_layer(p, 0)
+    bufs.step0()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    bufs.step1()
+    e1.record()
+    torch.cuda.synchronize()
+    g = clo.clo_last_step_gather_ms()
+    log(f"[case gather time, {batch * 4} units] gather {g:.4f} ms of a {e0.elapsed_time(e1):.4f} ms step")
+    assert 0.0 < g <= e0.elapsed_time(e1) + 1e-3
+
+
+@pytest.mark.parametrize("batch", [5, 64])
 def test_caller_spin_limit_bounds_only_the_callers_wait(need_gpu, batch):
     """A tiny sync.spin_limit on a flag that is already up bounds the caller's own wait
     only: the overlapped step's internal waits (the resident gather's and the attention

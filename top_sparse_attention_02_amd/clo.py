@@ -22,7 +22,8 @@ EXPORTS = ("clo_workspace_size", "clo_reuse_test", "clo_topk_select", "clo_reuse
            "clo_sparse_attn", "clo_decode_step", "clo_decode_step_static", "clo_append_kv", "clo_update_reference", "clo_plan_persistent", "clo_quantize_rows",
            "clo_stream_read", "clo_status_string", "clo_last_error", "clo_gather_plan_size", "clo_gather_plan",
            "clo_gather_layers", "clo_select_plan_size", "clo_select_plan", "clo_select_layers",
-           "clo_attend_plan_size", "clo_attend_plan", "clo_attend_layers", "clo_decode_step_schedule")
+           "clo_attend_plan_size", "clo_attend_plan", "clo_attend_layers", "clo_decode_step_schedule",
+           "clo_last_step_gather_ms")
 
 CLO_STEP_IN_ORDER, CLO_STEP_RANGE_GATHERS, CLO_STEP_RESIDENT_GATHER = range(3)
 STEP_MODES = {CLO_STEP_IN_ORDER: "in order", CLO_STEP_RANGE_GATHERS: "a gather launch per unit range",
@@ -108,6 +109,8 @@ def load():
         L.clo_decode_step.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, vp, vp, vp, sz, P(clo_sync), vp]
         L.clo_decode_step_schedule.restype = st
         L.clo_decode_step_schedule.argtypes = [P(clo_shape), ctypes.c_uint64, ctypes.c_int32, P(clo_step_schedule)]
+        L.clo_last_step_gather_ms.restype = st
+        L.clo_last_step_gather_ms.argtypes = [P(ctypes.c_float)]
         L.clo_decode_step_static.restype = st
         L.clo_decode_step_static.argtypes = [P(clo_shape), P(clo_layer), vp, vp, vp, vp, vp, P(clo_sync), vp]
         L.clo_append_kv.restype = st
@@ -312,6 +315,13 @@ def clo_decode_step_schedule(shape: Shape, persistent_mask: int = 0, host_format
             "gather_blocks_in_flight": out.gather_blocks_in_flight,
             "host_bytes_per_gather_block": out.host_bytes_per_gather_block,
             "host_bytes_in_flight": out.host_bytes_in_flight}
+
+
+def clo_last_step_gather_ms() -> float:
+    """GPU ms of the gather inside the last overlapped clo_decode_step on this device."""
+    v = ctypes.c_float()
+    _check(load().clo_last_step_gather_ms(ctypes.byref(v)), "clo_last_step_gather_ms")
+    return float(v.value)
 
 
 def clo_decode_step(shape: Shape, layer: Layer, q, q_prev, out, reuse, cos, ws, sync: Optional[Sync] = None,

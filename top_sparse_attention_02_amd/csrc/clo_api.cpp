@@ -287,6 +287,10 @@ struct DeviceQueues {
   hipEvent_t ev_gathered = nullptr;  // the resident gather ended
   hipEvent_t ev_attn = nullptr;      // the attention stream's work ended
   hipEvent_t ev_topk[kMaxRanges] = {}, ev_gather[kMaxRanges] = {};
+  // timing events around the last overlapped step's gather launches (start; end
+  // on each gather stream) and how many end events that step recorded
+  hipEvent_t ev_g_start = nullptr, ev_g_end[2] = {};
+  int g_ends = 0;
 };
 
 DeviceQueues g_queues[64];
@@ -310,6 +314,8 @@ clo_status device_queues(DeviceQueues** out) {
       e = hipEventCreateWithFlags(&q.ev_topk[r], hipEventDisableTiming);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&q.ev_gather[r], hipEventDisableTiming);
     }
+    for (hipEvent_t* ev : {&q.ev_g_start, &q.ev_g_end[0], &q.ev_g_end[1]})
+      if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDefault);
     if (e != hipSuccess) return fail(CLO_E_HIP, "creating helper streams/events: %s", hipGetErrorString(e));
     q.ready = true;
   }
@@ -913,10 +919,17 @@ clo_status step_overlapped_streams(const Plan& p, const Workspace& w, const void
     CLO_TRY(hipEventRecord(dq->ev_topk[r], s), "event record");
     hipStream_t gsr = (r & 1) ? dq->gather2 : dq->gather;
     CLO_TRY(hipStreamWaitEvent(gsr, dq->ev_topk[r], 0), "stream wait");
+    if (r == 0) CLO_TRY(hipEventRecord(dq->ev_g_start, gsr), "event record");
     CLO_TRY(launch_gather(p.a, reuse, span_host_range(w, r), x.per, kGatherBlocksOverlapped,
                           reinterpret_cast<uint32_t*>(w.meta + kMetaGather + r), gsr),
             "gather launch");
     CLO_TRY(hipEventRecord(dq->ev_gather[r], gsr), "event record");
+  }
+  CLO_TRY(hipEventRecord(dq->ev_g_end[0], dq->gather), "event record");
+  dq->g_ends = 1;
+  if (x.R > 1) {
+    CLO_TRY(hipEventRecord(dq->ev_g_end[1], dq->gather2), "event record");
+    dq->g_ends = 2;
   }
   // reuse units need no new rows; they are attended once the first range is
   // selected, so that their many short blocks do not delay the first top-k
@@ -958,7 +971,10 @@ clo_status step_overlapped_resident(const Plan& p, const Workspace& w, const voi
       // enqueued once the first group's selection is, so that a failed launch
       // above leaves no gather waiting for it
       CLO_TRY(hipStreamWaitEvent(gs, dq->ev_lists, 0), "stream wait");
+      CLO_TRY(hipEventRecord(dq->ev_g_start, gs), "event record");
       CLO_TRY(launch_gather_ranges(p.a, w, x.R, kGatherBlocksRanges, limit, gs), "gather launch");
+      CLO_TRY(hipEventRecord(dq->ev_g_end[0], gs), "event record");
+      dq->g_ends = 1;
       CLO_TRY(hipEventRecord(dq->ev_gathered, gs), "event record");
     }
   }
@@ -1003,6 +1019,7 @@ clo_status step_overlapped(const Plan& p, const Workspace& w, const void* q, con
   clo_status st;
   if ((st = device_queues(&dq))) return st;
   std::lock_guard<std::mutex> lk(dq->mu);
+  dq->g_ends = 0;
   return mode == CLO_STEP_RESIDENT_GATHER
              ? step_overlapped_resident(p, w, q, q_prev, out, reuse, cos, limit, dq, s)
              : step_overlapped_streams(p, w, q, q_prev, out, reuse, cos, dq, s);
@@ -1075,6 +1092,28 @@ clo_status clo_decode_step_schedule(const clo_shape* shape, uint64_t persistent_
   }
   x.host_bytes_in_flight = (int64_t)x.gather_blocks_in_flight * kGatherBytesPerBlock;
   *out = x;
+  return ok();
+}
+
+clo_status clo_last_step_gather_ms(float* ms) {
+  if (!ms) return fail(CLO_E_ARG, "ms is NULL");
+  DeviceQueues* dq = nullptr;
+  clo_status st;
+  if ((st = device_queues(&dq))) return st;
+  std::lock_guard<std::mutex> lk(dq->mu);
+  if (dq->g_ends == 0) return fail(CLO_E_ARG, "no overlapped decode step has gathered on this device");
+  float best = 0.f;
+  for (int i = 0; i < dq->g_ends; ++i) {
+    float t = 0.f;
+    const hipError_t e = hipEventElapsedTime(&t, dq->ev_g_start, dq->ev_g_end[i]);
+    if (e == hipErrorNotReady) {
+      (void)hipGetLastError();
+      return fail(CLO_E_ARG, "the last decode step has not finished");
+    }
+    if ((st = hip_status(e, "gather timing"))) return st;
+    best = std::max(best, t);
+  }
+  *ms = best;
   return ok();
 }
 
