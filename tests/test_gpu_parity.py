@@ -214,6 +214,51 @@ def test_last_step_gather_time_is_reported(need_gpu, batch):
     assert 0.0 < g <= e0.elapsed_time(e1) + 1e-3
 
 
+def test_concurrent_steps_on_two_streams_equal_sequential_steps(need_gpu):
+    """Two host threads, each on its own stream, run overlapped steps of their own layer at
+    the same time (256 units: the resident gather; 20 units: a gather launch per range): the
+    calls share the device's helper streams under its lock and keep their flags in their own
+    workspaces, so every step's outputs equal the same steps run one after another."""
+    import threading
+
+    import torch
+
+    from top_sparse_attention_02_amd import workload
+
+    probs = [small_problem("conc64", batch=64, hq=16, hkv=4, context=1500, topk=150, dtype="bf16",
+                           persistent=[0, 1, 0, 0]),
+             small_problem("conc5", batch=5, hq=16, hkv=4, context=2000, topk=200, dtype="bf16",
+                           persistent=[0, 0, 1, 0])]
+    bufs = [workload.load_layer(p, 0) for p in probs]
+    for b in bufs:
+        b.step0()
+        b.step1()
+    ref = [snapshot(b) for b in bufs]
+    streams = [torch.cuda.Stream() for _ in bufs]
+    errors = []
+
+    def run(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for _ in range(6):
+                    bufs[i].step0(stream=streams[i])
+                    bufs[i].step1(stream=streams[i])
+            streams[i].synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads) and not errors, errors
+    for i, b in enumerate(bufs):
+        got = snapshot(b)
+        for key in ref[i]:
+            assert np.array_equal(ref[i][key], got[key]), (probs[i].name, key)
+
+
 @pytest.mark.parametrize("batch", [5, 64])
 def test_caller_spin_limit_bounds_only_the_callers_wait(need_gpu, batch):
     """A tiny sync.spin_limit on a flag that is already up bounds the caller's own wait
