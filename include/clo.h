@@ -164,7 +164,10 @@ typedef struct {
  * polling" instead of coarse CPU-centric synchronization).  Every entry point
  * takes one (NULL = none).  All pointers are device memory and may be NULL
  * (then that half is skipped).  A producer's signal must be enqueued (in host
- * order) before the consumer's wait, as with events.
+ * order) before the consumer's wait, as with events: streams beyond the
+ * device's hardware queues (GPU_MAX_HW_QUEUES) share one, which starts kernels
+ * in the order they were enqueued, so there a wait enqueued ahead of its
+ * signal runs out its bound.
  *   wait_flag/wait_value      before its first kernel, the call waits on the
  *                             GPU until *wait_flag >= wait_value (acquire,
  *                             agent scope), polling at most spin_limit times
@@ -427,8 +430,11 @@ clo_status clo_attend_layers(const clo_shape* shape, const void* plan, int32_t f
  * only; a time-out writes CLO_E_TIMEOUT to sync->error_word and the consumer
  * goes on); the call is ordered after
  * earlier work on `stream`, and later work on `stream` is ordered after all of
- * the step.  Concurrent calls on one device share the helper streams (their
- * work then runs one after another).
+ * the step.  Every kernel that polls a flag is enqueued after the kernels that
+ * raise it, so the step also completes where its streams share hardware
+ * queues (then its parts run partly or wholly one after another).  Concurrent
+ * calls on one device share the helper streams (their work then runs one
+ * after another).
  */
 clo_status clo_decode_step(const clo_shape* shape, const clo_layer* layer, const void* q,
                            const void* q_prev, void* out, uint8_t* reuse, float* cos,

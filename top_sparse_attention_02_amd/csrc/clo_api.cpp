@@ -966,18 +966,21 @@ clo_status step_overlapped_resident(const Plan& p, const Workspace& w, const voi
     CLO_TRY(launch_select(p.a, sp, x.per * n, w, s), "top-k launch");
     // the kernel boundary makes the ranges' indices visible to the gather
     CLO_TRY(launch_signal(meta + kMetaSelFlag + r0, 1u, s, n), "signal launch");
-    if (r0 == 0) {
-      CLO_TRY(hipEventRecord(dq->ev_topk[0], s), "event record");
-      // enqueued once the first group's selection is, so that a failed launch
-      // above leaves no gather waiting for it
-      CLO_TRY(hipStreamWaitEvent(gs, dq->ev_lists, 0), "stream wait");
-      CLO_TRY(hipEventRecord(dq->ev_g_start, gs), "event record");
-      CLO_TRY(launch_gather_ranges(p.a, w, x.R, kGatherBlocksRanges, limit, gs), "gather launch");
-      CLO_TRY(hipEventRecord(dq->ev_g_end[0], gs), "event record");
-      dq->g_ends = 1;
-      CLO_TRY(hipEventRecord(dq->ev_gathered, gs), "event record");
-    }
+    if (r0 == 0) CLO_TRY(hipEventRecord(dq->ev_topk[0], s), "event record");
   }
+  // The gather polls every group's flag, so it is enqueued after the last
+  // group's selection: streams beyond the device's hardware queues share one,
+  // whose kernels start in the order they were enqueued, and a gather queued
+  // ahead of a selection it polls for would wait out its bound.  It still
+  // starts reading with the first group (the host has enqueued the whole step
+  // long before that group's top-k ends), and a failed launch above leaves no
+  // gather waiting.
+  CLO_TRY(hipStreamWaitEvent(gs, dq->ev_lists, 0), "stream wait");
+  CLO_TRY(hipEventRecord(dq->ev_g_start, gs), "event record");
+  CLO_TRY(launch_gather_ranges(p.a, w, x.R, kGatherBlocksRanges, limit, gs), "gather launch");
+  CLO_TRY(hipEventRecord(dq->ev_g_end[0], gs), "event record");
+  dq->g_ends = 1;
+  CLO_TRY(hipEventRecord(dq->ev_gathered, gs), "event record");
   CLO_TRY(hipStreamWaitEvent(as, dq->ev_topk[0], 0), "stream wait");
   CLO_TRY(launch_attn_partial(p.a, q, w.part, span_hits(w), p.U, as), "attention launch");
   CLO_TRY(launch_attn_combine(p.a, w.part, out, span_hits(w), p.U, as), "attention combine launch");
