@@ -964,14 +964,17 @@ def main():
             gather_schedule["mode"] = "in order (--counters)"
 
     # the step's lower bounds from its algorithmic bytes: the host link at the
-    # rate measured in this run, HBM at the published peak and at the measured
-    # read ceiling; the step can overlap the two, so its bound is the larger
+    # rate measured in this run (without the probe, at the link's published
+    # peak), HBM at the published peak and at the measured read ceiling; the
+    # step can overlap the two, so its bound is the larger
     host_bound_ms = alg["host_bytes"] / (probe["h_meas_gbs"] * 1e9) * 1e3 if probe else None
+    host_bound_peak_ms = alg["host_bytes"] / (HOST_LINK_PEAK_GBS * 1e9) * 1e3
     hbm_bound_ms = alg["hbm_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e3
     hbm_bound_meas_ms = alg["hbm_bytes"] / (hbm_probe["read_gbs"] * 1e9) * 1e3 if hbm_probe else None
-    step_bound_ms = max(x for x in (host_bound_ms, hbm_bound_meas_ms or hbm_bound_ms) if x is not None)
+    step_bound_ms = max(host_bound_ms or host_bound_peak_ms, hbm_bound_meas_ms or hbm_bound_ms)
     bounds = {"host_bytes": alg["host_bytes"], "hbm_bytes": alg["hbm_bytes"],
               "host_bound_ms": round(host_bound_ms, 4) if host_bound_ms is not None else None,
+              "host_bound_ms_at_peak": round(host_bound_peak_ms, 4),
               "hbm_bound_ms_at_peak": round(hbm_bound_ms, 4),
               "hbm_bound_ms_at_read_ceiling": round(hbm_bound_meas_ms, 4) if hbm_bound_meas_ms else None,
               "step_bound_ms": round(step_bound_ms, 4),

@@ -268,7 +268,9 @@ def default_select_batches(units: int, n_layers: int):
     8, 16, 16 against 76.6 with 3, 3, 6, 12, 24.  With the attention batched too, at
     B=1: 17.84 (int4 rows 7.02) with 3, 3, 6, 12, 24 against 17.90-17.91 (7.40-7.44)
     with 2, 2, 4, 8, 16, 16 or 4, 4, 8, 16, 16, 18.04 (7.09) with 6, 6, 12, 24 and
-    17.95 (7.62) with 3, 6, 12, 27."""
+    17.95 (7.62) with 3, 6, 12, 27; re-measured side by side, 17.83-17.84 with 3, 3,
+    6, 12, 24 against 17.88-17.89 with 1, 2, 3, 6, 12, 24, 17.92-17.94 with 1, 2,
+    4, 8, 16, 17 and 18.02 with 2, 3, 6, 12, 25."""
     f = max(1, -(-24 // max(1, units)))
     sizes, n = [f, f], f
     while sum(sizes) < n_layers:
