@@ -1,12 +1,15 @@
 """Decode steps of every overlapped schedule, run with error words, for
 tests/test_gpu_shared_queue.py.  The test runs them in its own process and, as
-`python -m tests.shared_queue_steps OUT.npz`, in a child process whose streams
-all share one hardware queue (GPU_MAX_HW_QUEUES=1 in its environment): there
-kernels start in the order they were enqueued, so a kernel that polls a flag
-finishes only if it was enqueued after the kernels that raise it."""
+`python -m tests.shared_queue_steps OUT.npz`, in child processes: one whose
+streams all share one hardware queue (GPU_MAX_HW_QUEUES=1 in its environment),
+where kernels start in the order they were enqueued, so a kernel that polls a
+flag finishes only if it was enqueued after the kernels that raise it; and one
+with CLO_STEP_IN_ORDER=1, where clo_decode_step runs every kernel in order on
+the caller's stream."""
 from __future__ import annotations
 
 import math
+import os
 import sys
 import time
 
@@ -36,7 +39,8 @@ LAYER_CASES = (("resident", 64), ("ranges", 5))
 def run_steps(log=print) -> dict:
     """A cold and a steady step of each single-layer case and of a 4-layer loop
     (batched selection, resident gather, batched attention).  Returns
-    {case: {output: array, "err": error word, "seconds": wall time}}."""
+    {case: {output: array, "err": error word, "seconds": wall time, "mode": the
+    schedule clo_decode_step_schedule reports (single-layer cases)}}."""
     import torch
 
     from top_sparse_attention_02_amd import clo, workload
@@ -51,8 +55,9 @@ def run_steps(log=print) -> dict:
             b.decode_step(b.q_prev if cold else b.q, b.q_prev, math.inf if cold else b.tau,
                           sync=clo.Sync(error_word=err))
         torch.cuda.synchronize()
-        res[name] = dict(snapshot(b), err=int(err.item()), seconds=time.perf_counter() - t0)
-        log(f"  {name}: error word {res[name]['err']}, {res[name]['seconds']:.3f} s")
+        res[name] = dict(snapshot(b), err=int(err.item()), seconds=time.perf_counter() - t0,
+                         mode=clo.clo_decode_step_schedule(b.shape, b.mask)["mode"])
+        log(f"  {name}: {res[name]['mode']}, error word {res[name]['err']}, {res[name]['seconds']:.3f} s")
     layers = workload.load_layers(loop_problem())
     loop = workload.LayerLoop(layers, gather="resident", select="batched", select_batches=(1, 3),
                               attend="batched", attend_batches=(2, 2))
@@ -70,7 +75,8 @@ def run_steps(log=print) -> dict:
 
 
 def main(path: str):
-    print("steps with every stream on one hardware queue", flush=True)
+    env = {k: os.environ[k] for k in ("GPU_MAX_HW_QUEUES", "CLO_STEP_IN_ORDER") if k in os.environ}
+    print(f"steps with {env}", flush=True)
     res = run_steps(log=lambda m: print(m, flush=True))
     np.savez(path, **{f"{c}__{k}": np.asarray(v) for c, d in res.items() for k, v in d.items()})
 
