@@ -34,6 +34,35 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+class Markers:
+    """roctx ranges around the benchmark's phases, so that a trace taken with
+    `rocprofv3 --marker-trace` names them beside the kernels.  Each range is
+    closed after its phase's closing synchronize, so the kernels that run inside
+    it are that phase's.  A no-op where the roctx library is not installed."""
+
+    def __init__(self):
+        import ctypes
+
+        self.lib = None
+        for name in ("librocprofiler-sdk-roctx.so.1", "/opt/rocm/lib/librocprofiler-sdk-roctx.so.1"):
+            try:
+                lib = ctypes.CDLL(name)
+            except OSError:
+                continue
+            lib.roctxRangePushA.argtypes, lib.roctxRangePushA.restype = [ctypes.c_char_p], ctypes.c_int
+            lib.roctxRangePop.argtypes, lib.roctxRangePop.restype = [], ctypes.c_int
+            self.lib = lib
+            break
+
+    def push(self, name: str):
+        if self.lib is not None:
+            self.lib.roctxRangePushA(name.encode())
+
+    def pop(self):
+        if self.lib is not None:
+            self.lib.roctxRangePop()
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -791,7 +820,9 @@ def main():
                                       host_format=host_format)]
     log(f"inputs generated and resident ({time.time() - t0:.1f} s)")
 
+    mk = Markers()
     probe = None
+    mk.push("probes")
     if not args.no_probe:
         probe = probe_host_link(torch)
         log(f"host link: memcpy {probe['memcpy_h2d_gbs']:.1f} GB/s, zero-copy stream "
@@ -801,6 +832,7 @@ def main():
     if not args.no_probe:
         hbm_probe = probe_hbm_read(torch)
         log(f"HBM read ceiling: {hbm_probe['read_gbs']:.0f} GB/s ({hbm_probe['blocks']} blocks)")
+    mk.pop()
 
     if args.calibrate_copy:
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
@@ -814,6 +846,7 @@ def main():
     if args.block_size > 1:
         for bufs in layers:
             bufs.set_block_size(args.block_size)
+    mk.push("cold step and warmup")
     if multi:
         att_batches = tuple(int(x) for x in args.attend_batches.split(",")) if args.attend_batches else None
         sel_batches = tuple(int(x) for x in args.select_batches.split(",")) if args.select_batches else None
@@ -836,10 +869,12 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    mk.pop()
 
     # timed region: K whole decode steps (all layers)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    mk.push("timed steps")
     t_wall = time.perf_counter()
     e0.record()
     for _ in range(args.steps):
@@ -847,15 +882,18 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    mk.pop()
     # a second pass of K steps with an event after every step, for the per-step
     # median and minimum (kept out of the timed region above: at tens of
     # microseconds per step the extra events would show in it)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    mk.push("per-step pass")
     ev[0].record()
     for i in range(args.steps):
         step()
         ev[i + 1].record()
     torch.cuda.synchronize()
+    mk.pop()
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     # host time to enqueue one step (argument checks and launches) onto an idle
     # GPU, median of K: while it stays below ms_per_step the GPU side is the limit
@@ -864,6 +902,7 @@ def main():
     sched = None if multi else clo.clo_decode_step_schedule(layers[0].shape, layers[0].mask, host_format)
     in_step = sched is not None and sched["mode"] != "in order" and not args.graph and not args.counters
     enq, gather_in_step = [], []
+    mk.push("enqueue pass")
     for _ in range(args.steps):
         torch.cuda.synchronize()
         if in_step and enq:
@@ -874,6 +913,7 @@ def main():
     torch.cuda.synchronize()
     if in_step:
         gather_in_step.append(clo.clo_last_step_gather_ms())
+    mk.pop()
     enqueue_us = sorted(enq)[len(enq) // 2] * 1e6
     if multi:
         loop.check()
@@ -890,9 +930,12 @@ def main():
         quant = compare_native(torch, workload, p, layers[0], args.step, flags)
         log(f"{args.host_kv} host KV vs native: output deviation mean {quant['out_dev_mean']:.2e}, "
             f"max {quant['out_dev_max']:.2e}")
+    mk.push("phase passes")
     phases = phase_times(torch, clo, layers, args.step, passes=args.steps if not multi else 2)
     if multi and loop.select == "batched":
         phases["select_batched"] = select_phase_ms(torch, clo, loop, args.step, passes=3)
+    torch.cuda.synchronize()
+    mk.pop()
     gather_s = phases["gather"] / 1e3
     host_gbs = alg["host_bytes"] / gather_s / 1e9 if alg["host_bytes"] else 0.0
     score_s = phases["score_topk"] / 1e3
@@ -1049,8 +1092,10 @@ def main():
             # single layer of a 48-layer workload is compared with in the full run
             result["cpu_baseline"] = None
         else:
+            mk.push("cpu baseline")
             result["cpu_baseline"] = cpu_baseline(p, layers, args.cpu_sample_seconds, args.step,
                                                   full_step=not multi, one_thread=args.config in (1, 2))
+            mk.pop()
     print(json.dumps(result), flush=True)
 
 
