@@ -9,7 +9,7 @@ compared (config 5: all their units; config 4: every miss unit and some reuse
 units of each), and every unit of those
 layers is checked for its reuse decision and a valid selection.  Config 3's
 shape is also run with int8 and int4 host KV and with 16-token blocks on sampled
-units.
+units, and config 5's loop with int4 host KV on 3 of those layers.
 Each case logs its largest normwise output error against the tolerance.
 
 The oracle and the margin work run per unit on a pool of threads (each with a
@@ -202,19 +202,23 @@ def test_config3_shape_variants(need_gpu, variant):
 # over 8 different data layers
 DATA_LAYERS = {4: 8, 5: 16}
 LAYERS_CHECKED = {4: [0, 9, 18, 27, 36, 45, 6, 15], 5: [0, 17, 34, 3, 20, 37, 6, 47]}
+# with int4 host KV, three of them, those with the most offloaded heads (the
+# oracle dequantizes every row of an offloaded unit, one row at a time)
+LAYERS_CHECKED_QUANT = {5: [34, 3, 47]}
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("cfg", [4, 5])
-def test_layer_loop_configs_full_size(need_gpu, cfg):
+@pytest.mark.parametrize("cfg,bits", [(4, 0), (5, 0), (5, 4)], ids=["config4", "config5", "config5_int4_host_kv"])
+def test_layer_loop_configs_full_size(need_gpu, cfg, bits):
     import torch
 
-    from top_sparse_attention_02_amd import workload
+    from top_sparse_attention_02_amd import clo, workload
 
+    host_format = {8: clo.CLO_HOST_INT8, 4: clo.CLO_HOST_INT4}.get(bits, clo.CLO_HOST_NATIVE)
     p = gen.config(cfg, data_layers=DATA_LAYERS[cfg])
-    checked = LAYERS_CHECKED[cfg]
+    checked = LAYERS_CHECKED_QUANT[cfg] if bits else LAYERS_CHECKED[cfg]
     assert len({p.data_layer(l) for l in checked}) == len(checked)
-    tag = f"full config {cfg}"
+    tag = f"full config {cfg}" + (f" int{bits} host KV" if bits else "")
     samples = {}
     for l in checked:
         enforce_cos_all(p, l)
@@ -227,7 +231,7 @@ def test_layer_loop_configs_full_size(need_gpu, cfg):
     mixes = [(bool(p.persistent[l].any()), bool((~p.persistent[l]).any())) for l in checked]
     assert any(a for a, _ in mixes) and any(b for _, b in mixes), "persistent and offloaded heads both covered"
     log(f"[{tag}] generating and loading 48 layers ({p.data_layers} data layers)")
-    layers = workload.load_layers(p)
+    layers = workload.load_layers(p, host_format=host_format)
     loop = workload.LayerLoop(layers)
     loop.step(cold=True)
     torch.cuda.synchronize()
@@ -240,7 +244,7 @@ def test_layer_loop_configs_full_size(need_gpu, cfg):
     for l in checked:
         n_p = sum(1 for b, h in samples[l] if layers[l].is_persistent(h))
         log(f"[{tag}] oracle, layer {l}: {len(samples[l])} units ({n_p} of persistent heads)")
-        check_units(p, l, layers[l], got0[l], got1[l], samples[l], f"{tag} layer {l}")
+        check_units(p, l, layers[l], got0[l], got1[l], samples[l], f"{tag} layer {l}", quant_bits=bits)
         check_all_units(p, l, got0[l], 0)
         check_all_units(p, l, got1[l], 1)
     del layers, loop, got0, got1
