@@ -165,3 +165,23 @@ def test_decode_step_schedule_reports_how_a_layer_runs():
     with pytest.raises(clo.CloError):
         clo.clo_decode_step_schedule(S(batch=1, n_q_heads=32, n_kv_heads=8, context=4096, topk=410, tau=0.8,
                                        dtype=clo.CLO_F32), host_format=7)
+
+
+def test_step_in_order_switch_sets_the_schedule():
+    """CLO_STEP_IN_ORDER=1 (read once per process) makes clo_decode_step, and the
+    schedule it reports, run every kernel in order on the caller's stream; any
+    other value leaves the overlapped schedules."""
+    import subprocess
+    import sys
+
+    code = ("from top_sparse_attention_02_amd import clo; "
+            "print(clo.clo_decode_step_schedule(clo.Shape(batch=64, n_q_heads=32, n_kv_heads=8, context=131072, "
+            "topk=13108, tau=0.8, dtype=clo.CLO_BF16))['mode'])")
+    modes = {}
+    for value in ("1", "0"):
+        env = dict(os.environ, CLO_STEP_IN_ORDER=value)
+        r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                           timeout=120)
+        assert r.returncode == 0, r.stderr[-2000:]
+        modes[value] = r.stdout.strip().splitlines()[-1]
+    assert modes == {"1": "in order", "0": "one resident gather launch"}
