@@ -112,7 +112,8 @@ constexpr int kOverlapUnits = 16;
 // ranges instead of a gather launch per range
 constexpr int kResidentGatherUnits = 256;
 constexpr int kMaxRanges = 16;
-// polls of a device-side wait when the caller gives no bound (about a second)
+// polls of a device-side wait when the caller gives no bound (about a second:
+// 1.35 s measured on an idle MI355X, 0.32 us per poll)
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
 struct RangeBounds {
   int32_t first[kMaxRanges + 1];  // first unit of each range; first[R] = U
