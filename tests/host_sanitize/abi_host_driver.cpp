@@ -148,6 +148,23 @@ int main() {
       clo_shape empty = shape(0, 8, 2, 128, 524288, 52429, 0.8f, CLO_BF16);
       CHECK(clo_attend_layers(&empty, nullptr, 0, 4, 0, 1, nullptr, 0, nullptr) == CLO_E_ARG);
     }
+    // how a step runs (host-only) and the gather timer before any overlapped step
+    {
+      clo_shape b64 = shape(64, 32, 8, 128, 131072, 13108, 0.8f, CLO_BF16);
+      clo_step_schedule sc;
+      std::memset(&sc, 0xAB, sizeof sc);
+      CHECK(clo_decode_step_schedule(nullptr, 0, CLO_HOST_NATIVE, &sc) == CLO_E_ARG);
+      CHECK(clo_decode_step_schedule(&b64, 0, CLO_HOST_NATIVE, nullptr) == CLO_E_ARG);
+      CHECK(clo_decode_step_schedule(&b64, 0, 7, &sc) == CLO_E_ARG);
+      CHECK(clo_decode_step_schedule(&b64, 0, CLO_HOST_NATIVE, &sc) == CLO_OK);
+      CHECK(sc.mode == CLO_STEP_RESIDENT_GATHER && sc.ranges == 8 && sc.gather_blocks > 0);
+      CHECK(sc.host_bytes_in_flight == (int64_t)sc.gather_blocks_in_flight * sc.host_bytes_per_gather_block);
+      CHECK(clo_decode_step_schedule(&b64, 0xFF, CLO_HOST_NATIVE, &sc) == CLO_OK);  // every head persistent
+      CHECK(sc.mode == CLO_STEP_IN_ORDER && sc.gather_blocks == 0 && sc.host_bytes_in_flight == 0);
+      float ms = -1.f;
+      CHECK(clo_last_step_gather_ms(nullptr) == CLO_E_ARG);
+      CHECK(clo_last_step_gather_ms(&ms) != CLO_OK && ms == -1.f);
+    }
   }
 
   // the last-error buffer at every length, including 0 and 1
