@@ -30,8 +30,12 @@
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  Buffers must stay alive until the stream work completes.
  *  - Arguments are validated on the host before anything is launched; a
- *    non-OK status means nothing was enqueued.  clo_last_error() gives the
- *    reason (thread-local).  No exception crosses the ABI and nothing aborts.
+ *    non-OK status from validation means nothing was enqueued.  CLO_E_HIP (a
+ *    launch the runtime refused) can follow kernels of the same call that
+ *    were already enqueued: the call's outputs are then undefined, and none of
+ *    its enqueued kernels waits for a flag of the call that no enqueued kernel
+ *    raises.  clo_last_error() gives the reason (thread-local).  No exception
+ *    crosses the ABI and nothing aborts.
  *  - Device buffers must be device memory of the current device; host K/V
  *    buffers must be pinned host memory that the device can address (e.g.
  *    hipHostMalloc); pageable host memory is rejected with CLO_E_ARG.  Every
