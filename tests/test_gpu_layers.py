@@ -77,21 +77,34 @@ def test_layer_loop_matches_sequential_and_oracle(need_gpu, select_streams, gath
         compare(p, layers[l], a1[l], r1, kv, f"layer {l} step1")
 
 
-@pytest.mark.parametrize("host_kv", ["int8", "int4"])
-def test_layer_loop_quantized_host_kv_matches_sequential(need_gpu, host_kv):
+def wide_layer_problem():
+    # 64 units per layer (16 sequences x 4 KV heads): the most a batched selection
+    # takes, and the resident gather's grid for layers of 64 units or more
+    return gen.Problem(name="layers_wide", layers=3, batch=16, hq=16, hkv=4, d=128, context=1500, topk=150,
+                       dtype="bf16", tau=0.8, seed=0x5EED0202, qprev_model="target_cos", low_frac=0.5,
+                       heavy_frac=0.005,
+                       persistent=np.array([[0, 1, 0, 0], [0, 0, 0, 0], [1, 0, 0, 1]], dtype=bool))
+
+
+@pytest.mark.parametrize("host_kv,units,blocks", [("int8", 4, 32), ("int4", 4, 32), ("int8", 64, 40),
+                                                  ("int4", 64, 40)])
+def test_layer_loop_quantized_host_kv_matches_sequential(need_gpu, host_kv, units, blocks):
     """The three-stream loop over layers whose offloaded KV is quantized in host memory
     (the dequantizing gather inside the resident launch, its in-LDS unit list and the
     fused reuse-select launch) equals the fused step run layer after layer on one
-    stream, bit for bit."""
+    stream, bit for bit, for layers of 4 units and of 64 (the resident gather's grid
+    of 32 and of 40 blocks)."""
     import torch
 
     from top_sparse_attention_02_amd import clo, workload
 
-    p = enforce_all_layers(multi_layer_problem())
+    p = enforce_all_layers(multi_layer_problem() if units == 4 else wide_layer_problem())
+    assert p.batch * p.hkv == units
     fmt = clo.CLO_HOST_INT8 if host_kv == "int8" else clo.CLO_HOST_INT4
     layers = workload.load_layers(p, host_format=fmt)
     loop = workload.LayerLoop(layers)
-    log(f"[case layer loop, {host_kv} host KV] cold + steady step")
+    assert loop.plan_blocks == blocks and loop.select == "batched"
+    log(f"[case layer loop, {host_kv} host KV, {units} units per layer] cold + steady step")
     loop.step(cold=True)
     loop.step()
     torch.cuda.synchronize()
