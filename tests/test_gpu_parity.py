@@ -43,6 +43,12 @@ CASES = {
                                      persistent=[0, 1]),
     "bf16_g4_multi_at_switch": dict(batch=1, hq=8, hkv=2, context=114689, topk=11469, dtype="bf16",
                                     persistent=[1, 0]),
+    # either side of the one-launch top-k's limit (128 chunks of 16384 keys; 128 chunks and
+    # one key: the top-k then runs its three radix passes and the write launch by launch)
+    "bf16_g4_fused_at_limit": dict(batch=2, hq=4, hkv=1, context=128 * 16384, topk=209716, dtype="bf16",
+                                   persistent=[0]),
+    "bf16_g4_passes_past_limit": dict(batch=2, hq=4, hkv=1, context=128 * 16384 + 1, topk=209716,
+                                      dtype="bf16", persistent=[1]),
     # 20 and 18 units with offloaded heads: the step overlapped over 8 unit ranges
     # of 2-3 units on the helper streams (smaller layers run in order)
     "bf16_g4_overlapped": dict(batch=5, hq=16, hkv=4, context=3001, topk=301, dtype="bf16",
