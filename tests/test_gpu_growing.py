@@ -22,6 +22,11 @@ CASES = {
                           heavy_frac=0.005, low_frac=0.2),
     "f32_g5_host": dict(batch=1, hq=10, hkv=2, context=2500 + STEPS, topk=251, dtype="f32", persistent=[0, 0],
                         low_frac=0.2),
+    # from 114686 to 114692 keys: at step 3 the context passes 7 chunks of 16384 keys
+    # and the top-k moves from the single-block to the multi-block kernel (the path
+    # depends on the context only; a small k keeps the score margins cheap to set)
+    "bf16_g4_across_topk_switch": dict(batch=2, hq=8, hkv=2, context=7 * 16384 - 2 + STEPS, topk=300,
+                                       dtype="bf16", persistent=[0, 1], low_frac=0.2),
 }
 
 
